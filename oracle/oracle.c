@@ -1,0 +1,532 @@
+/*
+ * Plain, slow CPU oracle for the block-scaled GEMM family.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark load this library.  It shares no code,
+ * header, table or helper with the HIP path, and the HIP path never loads it.
+ *
+ * Everything is decoded exactly and accumulated in fp64; epilogues run in
+ * fp64.  The one exception is the MX output quantiser, whose integer
+ * decisions (scale byte, code) are taken in fp32 because that is the
+ * precision the GPU kernels decide them in (documented per function).
+ *
+ * Sources (cuDNN frontend "GEMM fusions" documentation pages):
+ *   [GA]  "GEMM + Amax (SM100)": Equations; Shapes; Input/Output tensors.
+ *   [GS]  "Grouped GEMM + sReLU (SM100)": Equations; Tanh soft clamp;
+ *         Shapes (SFD_row / SFD_col atom shapes).
+ *   [GD]  "Grouped GEMM + dSwiGLU (SM100)": Step 3, output quantisation.
+ *   [GB]  "Grouped GEMM (SM100 BF16)": Operation; Tensors and layouts.
+ *   [PR]  "GEMM + RoPE + MXFP8 Projection (SM100)": Equations; Shapes.
+ * Number formats follow the OCP Microscaling (MX) v1.0 definitions of
+ * E4M3 ("fn", no infinities), E2M1 and E8M0.
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC oracle.c -o liboracle.so -lm
+ */
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* Number formats                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* E4M3 (fn flavour): 1 sign, 4 exponent bits (bias 7), 3 mantissa bits.
+ * Exponent field 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN; no Inf. */
+double orc_dec_e4m3(uint32_t code)
+{
+    uint32_t s = (code >> 7) & 1u, e = (code >> 3) & 15u, m = code & 7u;
+    double v;
+    if (e == 15u && m == 7u) return NAN;
+    if (e == 0u) v = ldexp((double)m / 8.0, -6);
+    else v = ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+    return s ? -v : v;
+}
+
+/* E2M1: 1 sign, 2 exponent bits (bias 1), 1 mantissa bit; exponent field 0
+ * is subnormal (m * 0.5).  Magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}. */
+double orc_dec_e2m1(uint32_t nib)
+{
+    uint32_t s = (nib >> 3) & 1u, e = (nib >> 1) & 3u, m = nib & 1u;
+    double v;
+    if (e == 0u) v = 0.5 * (double)m;
+    else v = ldexp(1.0 + (double)m / 2.0, (int)e - 1);
+    return s ? -v : v;
+}
+
+/* E8M0: unsigned biased exponent 2^(b-127); 0xFF is NaN. */
+double orc_dec_e8m0(uint32_t b)
+{
+    if ((b & 255u) == 255u) return NAN;
+    return ldexp(1.0, (int)(b & 255u) - 127);
+}
+
+/* bf16 is the upper half of an IEEE binary32. */
+double orc_dec_bf16(uint32_t h)
+{
+    uint32_t w = (h & 0xFFFFu) << 16;
+    float f;
+    memcpy(&f, &w, 4);
+    return (double)f;
+}
+
+/* Round x to the nearest multiple of `step` (a power of two), ties to even. */
+static double rne_to_step(double x, double step)
+{
+    double q = x / step;            /* exact: power-of-two division */
+    double fl = floor(q);
+    double r = q - fl;
+    if (r > 0.5 || (r == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;
+    return fl * step;
+}
+
+/* fp64 -> E4M3 code: round to nearest, ties to even; magnitudes at or above
+ * the largest finite value (448) saturate to it; never returns the NaN code.
+ * Negative values that round to zero keep the sign bit (0x80). */
+uint32_t orc_enc_e4m3(double x)
+{
+    uint32_t s = signbit(x) ? 0x80u : 0u;
+    double a = fabs(x), q;
+    int e2;
+    if (isnan(x)) return 0x7Fu;
+    if (a >= 448.0) return s | 0x7Eu;
+    if (a == 0.0) return s;
+    frexp(a, &e2);                         /* a in [2^(e2-1), 2^e2) */
+    {
+        int ulp_exp = e2 - 1 - 3;          /* 3 stored mantissa bits */
+        if (ulp_exp < -9) ulp_exp = -9;    /* subnormal spacing 2^-9 */
+        q = rne_to_step(a, ldexp(1.0, ulp_exp));
+    }
+    if (q >= 448.0) return s | 0x7Eu;
+    if (q == 0.0) return s;
+    if (q < ldexp(1.0, -6)) {              /* subnormal: m * 2^-9 */
+        return s | (uint32_t)(q / ldexp(1.0, -9));
+    }
+    frexp(q, &e2);
+    {
+        int E = e2 - 1;                    /* q in [2^E, 2^(E+1)) */
+        uint32_t m = (uint32_t)((q / ldexp(1.0, E) - 1.0) * 8.0);
+        return s | ((uint32_t)(E + 7) << 3) | m;
+    }
+}
+
+/* fp64 -> bf16 bits with a single round-to-nearest-even step. */
+uint32_t orc_rne_bf16(double x)
+{
+    double a = fabs(x), q;
+    int e2, ulp_exp;
+    float f;
+    uint32_t w;
+    if (isnan(x)) return 0x7FC0u;
+    if (a == 0.0) q = 0.0;
+    else {
+        frexp(a, &e2);
+        ulp_exp = e2 - 1 - 7;              /* 7 stored mantissa bits */
+        if (ulp_exp < -133) ulp_exp = -133;
+        q = rne_to_step(a, ldexp(1.0, ulp_exp));
+    }
+    if (q >= ldexp(1.0, 128)) q = INFINITY;
+    f = (float)(signbit(x) ? -q : q);      /* exact: q has <= 8 significant bits */
+    memcpy(&w, &f, 4);
+    return w >> 16;
+}
+
+/* E8M0 byte of the smallest power of two >= sigma, clamped to [0, 254];
+ * sigma <= 0 gives 0.  (Rounding of a computed scale: see the quantiser.) */
+uint32_t orc_e8m0_ceil(double sigma)
+{
+    int e2, E;
+    double f;
+    if (!(sigma > 0.0)) return 0u;
+    f = frexp(sigma, &e2);                 /* sigma = f * 2^e2, f in [0.5,1) */
+    E = (f == 0.5) ? e2 - 1 : e2;
+    E += 127;
+    if (E < 0) E = 0;
+    if (E > 254) E = 254;
+    return (uint32_t)E;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Scale-factor atom addressing                                             */
+/* ------------------------------------------------------------------------ */
+/* [GA] Shapes / "Using JAX arrays": the logical scale tensor has shape
+ * (32, 4, ceil(MN/128), 4, ceil(K/(4*sf)), L) and is the C-contiguous
+ * physical buffer (L, ceil(MN/128), ceil(K/(4*sf)), 32, 4, 4) permuted by
+ * (3,4,1,5,2,0).  Reading the hierarchical row mode (32,4,MN') first-mode
+ * fastest, row r = 128*mt + 32*r4 + r32 and k-block kb = 4*kt + k4, so the
+ * byte sits at physical index (l, mt, kt, r32, r4, k4). */
+int64_t orc_sf_offset(int64_t r, int64_t kb, int64_t l, int64_t mn, int64_t kblocks)
+{
+    int64_t mt_n = (mn + 127) / 128;
+    int64_t kt_n = (kblocks + 3) / 4;
+    int64_t mt = r / 128, r4 = (r % 128) / 32, r32 = r % 32;
+    int64_t kt = kb / 4, k4 = kb % 4;
+    return ((((l * mt_n + mt) * kt_n + kt) * 32 + r32) * 4 + r4) * 4 + k4;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dequantisation ([GA] Equations: A_hat = dequantize(A, SFA, sf_vec_size)) */
+/* ------------------------------------------------------------------------ */
+/* fmt 0: one E4M3 code per byte.  fmt 1: E2M1, two per byte, element 2j in
+ * the low nibble and 2j+1 in the high nibble. */
+static double code_value(const uint8_t *row, int fmt, int64_t kk)
+{
+    if (fmt == 0) return orc_dec_e4m3(row[kk]);
+    {
+        uint8_t byte = row[kk >> 1];
+        return orc_dec_e2m1((kk & 1) ? (byte >> 4) : (byte & 15u));
+    }
+}
+
+/* Row r of matrix `l` of an (MN, K) operand, dequantised into out[0..K). */
+static void dequant_row(const uint8_t *codes, const uint8_t *sf, int fmt,
+                        int64_t r, int64_t l, int64_t mn, int64_t k, double *out)
+{
+    int64_t rowbytes = fmt == 0 ? k : k / 2;
+    int64_t kblocks = (k + 31) / 32;
+    const uint8_t *row = codes + (l * mn + r) * rowbytes;
+    for (int64_t kk = 0; kk < k; ++kk) {
+        double scale = orc_dec_e8m0(sf[orc_sf_offset(r, kk / 32, l, mn, kblocks)]);
+        out[kk] = code_value(row, fmt, kk) * scale;
+    }
+}
+
+/* acc = sum_k a[k]*b[k]; sabs = sum_k |a[k]*b[k]| */
+static void dot(const double *a, const double *b, int64_t k, double *acc, double *sabs)
+{
+    double s = 0.0, t = 0.0;
+    for (int64_t kk = 0; kk < k; ++kk) {
+        double p = a[kk] * b[kk];
+        s += p;
+        t += fabs(p);
+    }
+    *acc = s;
+    *sabs = t;
+}
+
+/* Dequantise all N rows of B for batch/expert l: out is (N, K). */
+static void dequant_matrix(const uint8_t *codes, const uint8_t *sf, int fmt,
+                           int64_t l, int64_t rows, int64_t k, double *out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        dequant_row(codes, sf, fmt, r, l, rows, k, out + r * k);
+}
+
+/* ------------------------------------------------------------------------ */
+/* [GA] C[m,n,l] = sum_k A_hat[m,k,l] * B_hat[n,k,l]                        */
+/* ------------------------------------------------------------------------ */
+/* Rows [r0, r1) of batch `batch`.  c and sabs (nullable) are (r1-r0, n). */
+int orc_gemm_amax(const uint8_t *a, const uint8_t *b, const uint8_t *sfa, const uint8_t *sfb,
+                  int64_t m, int64_t n, int64_t k, int64_t l, int fmt,
+                  int64_t batch, int64_t r0, int64_t r1, double *c, double *sabs)
+{
+    double *bh, *ah;
+    if (batch < 0 || batch >= l || r0 < 0 || r1 > m || r0 > r1) return 1;
+    if (fmt == 1 && (k % 2)) return 2;
+    bh = (double *)malloc(sizeof(double) * (size_t)(n * k));
+    ah = (double *)malloc(sizeof(double) * (size_t)((r1 - r0) * k));
+    if (!bh || !ah) { free(bh); free(ah); return 3; }
+    dequant_matrix(b, sfb, fmt, batch, n, k, bh);
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = r0; i < r1; ++i)
+        dequant_row(a, sfa, fmt, i, batch, m, k, ah + (i - r0) * k);
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = r0; i < r1; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            double acc, t;
+            dot(ah + (i - r0) * k, bh + j * k, k, &acc, &t);
+            c[(i - r0) * n + j] = acc;
+            if (sabs) sabs[(i - r0) * n + j] = t;
+        }
+    free(bh);
+    free(ah);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Expert routing ([GB] Operation: rows [begin_g, padded_offsets[g]) with   */
+/* begin_0 = 0 and begin_g = padded_offsets[g-1])                           */
+/* ------------------------------------------------------------------------ */
+/* The unique g whose range holds row r, or -1 when r >= padded_offsets[L-1].
+ * Empty ranges (begin_g == end_g) hold no row. */
+int32_t orc_expert_of_row(const int32_t *offsets, int64_t L, int64_t r)
+{
+    int64_t begin = 0;
+    for (int64_t g = 0; g < L; ++g) {
+        int64_t end = offsets[g];
+        if (begin <= r && r < end) return (int32_t)g;
+        begin = end;
+    }
+    return -1;
+}
+
+/* ------------------------------------------------------------------------ */
+/* [GS] Equations and "Tanh soft clamp":                                    */
+/*   C = alpha_g * sum_k A_hat * B_hat_g                                    */
+/*   D = prob[m] * relu(C)^2                       (s <= 0: no clamp)       */
+/*   D = prob[m] * (s * min(1, tanh(relu(C)/s)))^2 (s > 0; t capped at 1)   */
+/* ------------------------------------------------------------------------ */
+int orc_grouped_srelu(const uint8_t *a, const uint8_t *b, const uint8_t *sfa, const uint8_t *sfb,
+                      const int32_t *offsets, const float *alpha, const float *prob,
+                      int64_t m, int64_t n, int64_t k, int64_t L, int fmt, double s,
+                      int64_t r0, int64_t r1,
+                      double *c_out, double *d_out, double *sabs_out, int32_t *group_out)
+{
+    double *bh = NULL, *ah;
+    int64_t rows = r1 - r0, have = -1;
+    if (r0 < 0 || r1 > m || r0 > r1) return 1;
+    if (fmt == 1 && (k % 2)) return 2;
+    ah = (double *)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1) * (size_t)(rows > 0 ? rows : 1));
+    bh = (double *)malloc(sizeof(double) * (size_t)(n * k > 0 ? n * k : 1));
+    if (!ah || !bh) { free(ah); free(bh); return 3; }
+    for (int64_t i = r0; i < r1; ++i) group_out[i - r0] = orc_expert_of_row(offsets, L, i);
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = r0; i < r1; ++i)
+        dequant_row(a, sfa, fmt, i, 0, m, k, ah + (i - r0) * k);
+    for (int64_t i = r0; i < r1; ++i) {
+        int64_t g = group_out[i - r0];
+        if (g < 0) {
+            for (int64_t j = 0; j < n; ++j) {
+                c_out[(i - r0) * n + j] = NAN;
+                d_out[(i - r0) * n + j] = NAN;
+                if (sabs_out) sabs_out[(i - r0) * n + j] = NAN;
+            }
+            continue;
+        }
+        if (g != have) { dequant_matrix(b, sfb, fmt, g, n, k, bh); have = g; }
+        #pragma omp parallel for schedule(static)
+        for (int64_t j = 0; j < n; ++j) {
+            double acc, t, cval, x;
+            dot(ah + (i - r0) * k, bh + j * k, k, &acc, &t);
+            cval = (double)alpha[g] * acc;
+            x = cval > 0.0 ? cval : 0.0;
+            if (s > 0.0) {
+                double th = tanh(x / s);
+                if (th > 1.0) th = 1.0;
+                x = s * th;
+            }
+            c_out[(i - r0) * n + j] = cval;
+            d_out[(i - r0) * n + j] = (double)prob[i] * x * x;
+            if (sabs_out) sabs_out[(i - r0) * n + j] = fabs((double)alpha[g]) * t;
+        }
+    }
+    free(ah);
+    free(bh);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* [GB] Operation:                                                          */
+/*   G = alpha[g] * A_g @ B_g^T                                             */
+/*   with bias:    C = G + prob * bias[:, g],  D = C                        */
+/*   without bias: C = G,                      D = prob * G                 */
+/* A (M,K) bf16; B stored [L][N][K] bf16; bias (N,L) stride (1,N) given     */
+/* here already widened to fp64, memory [L][N].                             */
+/* ------------------------------------------------------------------------ */
+int orc_grouped_bf16(const uint16_t *a, const uint16_t *b, const int32_t *offsets,
+                     const float *alpha, const float *prob, const double *bias,
+                     int64_t m, int64_t n, int64_t k, int64_t L, int64_t r0, int64_t r1,
+                     double *c_out, double *d_out, double *sabs_out, int32_t *group_out)
+{
+    double *bh, *ah;
+    int64_t have = -1, rows = r1 - r0;
+    if (r0 < 0 || r1 > m || r0 > r1) return 1;
+    ah = (double *)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1) * (size_t)(rows > 0 ? rows : 1));
+    bh = (double *)malloc(sizeof(double) * (size_t)(n * k > 0 ? n * k : 1));
+    if (!ah || !bh) { free(ah); free(bh); return 3; }
+    for (int64_t i = r0; i < r1; ++i) {
+        group_out[i - r0] = orc_expert_of_row(offsets, L, i);
+        for (int64_t kk = 0; kk < k; ++kk)
+            ah[(i - r0) * k + kk] = orc_dec_bf16(a[i * k + kk]);
+    }
+    for (int64_t i = r0; i < r1; ++i) {
+        int64_t g = group_out[i - r0];
+        if (g < 0) {
+            for (int64_t j = 0; j < n; ++j) {
+                c_out[(i - r0) * n + j] = NAN;
+                d_out[(i - r0) * n + j] = NAN;
+                if (sabs_out) sabs_out[(i - r0) * n + j] = NAN;
+            }
+            continue;
+        }
+        if (g != have) {
+            #pragma omp parallel for schedule(static)
+            for (int64_t j = 0; j < n; ++j)
+                for (int64_t kk = 0; kk < k; ++kk)
+                    bh[j * k + kk] = orc_dec_bf16(b[(g * n + j) * k + kk]);
+            have = g;
+        }
+        #pragma omp parallel for schedule(static)
+        for (int64_t j = 0; j < n; ++j) {
+            double acc, t, G;
+            dot(ah + (i - r0) * k, bh + j * k, k, &acc, &t);
+            G = (double)alpha[g] * acc;
+            if (bias) {
+                double cval = G + (double)prob[i] * bias[g * n + j];
+                c_out[(i - r0) * n + j] = cval;
+                d_out[(i - r0) * n + j] = cval;
+            } else {
+                c_out[(i - r0) * n + j] = G;
+                d_out[(i - r0) * n + j] = (double)prob[i] * G;
+            }
+            if (sabs_out) sabs_out[(i - r0) * n + j] = fabs((double)alpha[g]) * t;
+        }
+    }
+    free(ah);
+    free(bh);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* [PR] Equations: Y = x W reshaped to [tokens, heads, head_dim]; the        */
+/* trailing qk_rope features of each head get the interleaved-in /          */
+/* halves-out rotary embedding:                                             */
+/*   a_j = Y[.., nope + 2j],  b_j = Y[.., nope + 2j + 1],  j < qk_rope/2      */
+/*   out[nope + j]        = a_j cos[t, j]        - b_j sin[t, j]            */
+/*   out[nope + half + j] = b_j cos[t, half + j] + a_j sin[t, half + j]     */
+/* w_out_in = 1: w is [out, in]; 0: w is [in, out].                         */
+/* Rows [t0, t1); y_out and sabs_out (nullable) are (t1-t0, heads*head_dim). */
+/* ------------------------------------------------------------------------ */
+int orc_proj_rope(const uint16_t *x, const uint16_t *w, const uint16_t *cosv, const uint16_t *sinv,
+                  int64_t tokens, int64_t q_lora, int64_t heads, int64_t head_dim,
+                  int64_t qk_rope, int w_out_in, int64_t t0, int64_t t1,
+                  double *y_out, double *sabs_out)
+{
+    int64_t nout = heads * head_dim, nope = head_dim - qk_rope, half = qk_rope / 2;
+    int64_t rows = t1 - t0;
+    double *wt, *xr, *yr, *sr;
+    if (t0 < 0 || t1 > tokens || t0 > t1 || qk_rope % 2 || qk_rope > head_dim) return 1;
+    wt = (double *)malloc(sizeof(double) * (size_t)(nout * q_lora));
+    xr = (double *)malloc(sizeof(double) * (size_t)(q_lora * (rows > 0 ? rows : 1)));
+    yr = (double *)malloc(sizeof(double) * (size_t)(nout * (rows > 0 ? rows : 1)));
+    sr = (double *)malloc(sizeof(double) * (size_t)(nout * (rows > 0 ? rows : 1)));
+    if (!wt || !xr || !yr || !sr) { free(wt); free(xr); free(yr); free(sr); return 3; }
+    /* weight as [out][in] */
+    #pragma omp parallel for schedule(static)
+    for (int64_t o = 0; o < nout; ++o)
+        for (int64_t i = 0; i < q_lora; ++i)
+            wt[o * q_lora + i] = orc_dec_bf16(w_out_in ? w[o * q_lora + i] : w[i * nout + o]);
+    for (int64_t t = t0; t < t1; ++t)
+        for (int64_t i = 0; i < q_lora; ++i)
+            xr[(t - t0) * q_lora + i] = orc_dec_bf16(x[t * q_lora + i]);
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t t = t0; t < t1; ++t)
+        for (int64_t o = 0; o < nout; ++o) {
+            double acc, s;
+            dot(xr + (t - t0) * q_lora, wt + o * q_lora, q_lora, &acc, &s);
+            yr[(t - t0) * nout + o] = acc;
+            sr[(t - t0) * nout + o] = s;
+        }
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t t = t0; t < t1; ++t)
+        for (int64_t h = 0; h < heads; ++h) {
+            const double *y = yr + (t - t0) * nout + h * head_dim;
+            const double *sy = sr + (t - t0) * nout + h * head_dim;
+            double *out = y_out + (t - t0) * nout + h * head_dim;
+            double *so = sabs_out ? sabs_out + (t - t0) * nout + h * head_dim : NULL;
+            for (int64_t d = 0; d < nope; ++d) {
+                out[d] = y[d];
+                if (so) so[d] = sy[d];
+            }
+            for (int64_t j = 0; j < half; ++j) {
+                double av = y[nope + 2 * j], bv = y[nope + 2 * j + 1];
+                double c0 = orc_dec_bf16(cosv[t * qk_rope + j]);
+                double s0 = orc_dec_bf16(sinv[t * qk_rope + j]);
+                double c1 = orc_dec_bf16(cosv[t * qk_rope + half + j]);
+                double s1 = orc_dec_bf16(sinv[t * qk_rope + half + j]);
+                out[nope + j] = av * c0 - bv * s0;
+                out[nope + half + j] = bv * c1 + av * s1;
+                if (so) {
+                    double sa = sy[nope + 2 * j], sb = sy[nope + 2 * j + 1];
+                    so[nope + j] = sa * fabs(c0) + sb * fabs(s0);
+                    so[nope + half + j] = sb * fabs(c1) + sa * fabs(s1);
+                }
+            }
+        }
+    free(wt);
+    free(xr);
+    free(yr);
+    free(sr);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* MX output quantiser ([GD] Step 3):                                       */
+/*   SFD = norm_const * max_{k in block} |D| * rcp_max                      */
+/*   D_q = D * norm_const / SFD                                             */
+/* with rcp_max = 1/448 for E4M3 and blocks of 32 consecutive elements.     */
+/* SFD is stored as E8M0: the smallest power of two >= the computed value   */
+/* (so |D_q| <= 448 needs no clipping); codes are E4M3 by round to nearest  */
+/* even, saturating.  The decisions are taken in binary32, in this order:   */
+/*   v     = fp32(D)                                                         */
+/*   amax  = max |v|                                                         */
+/*   sigma = fp32(fp32(norm_const * amax) * fp32(1/448))                    */
+/*   byte  = e8m0_ceil(sigma)                                               */
+/*   inv   = min(norm_const * 2^(127 - byte), FLT_MAX)  (power-of-two step) */
+/*   code  = e4m3_rne_sat(fp32(v * inv))                                    */
+/* ------------------------------------------------------------------------ */
+static void quant_block(const double *d, int64_t cnt, int64_t stride, float norm_const,
+                        uint8_t *codes, int64_t cstride, uint8_t *scale)
+{
+    float amax = 0.0f, sigma, inv;
+    uint32_t byte;
+    const float rcp_max = 1.0f / 448.0f;
+    for (int64_t i = 0; i < cnt; ++i) {
+        float v = fabsf((float)d[i * stride]);
+        if (v > amax) amax = v;
+    }
+    sigma = (norm_const * amax) * rcp_max;
+    byte = orc_e8m0_ceil((double)sigma);
+    inv = ldexpf(norm_const, 127 - (int)byte);
+    if (inv > FLT_MAX) inv = FLT_MAX;     /* tiny blocks with a large norm_const */
+    for (int64_t i = 0; i < cnt; ++i) {
+        float v = (float)d[i * stride];
+        float y = v * inv;
+        codes[i * cstride] = (uint8_t)orc_enc_e4m3((double)y);
+    }
+    *scale = (uint8_t)byte;
+}
+
+/* Row direction: blocks of 32 along each row.  d is (rows, cols) with
+ * leading dimension ld; codes (rows, cols); scales (rows, ceil(cols/32)). */
+void orc_mx_quant_rows(const double *d, int64_t rows, int64_t cols, int64_t ld,
+                       float norm_const, uint8_t *codes, uint8_t *scales)
+{
+    int64_t nb = (cols + 31) / 32;
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            int64_t c0 = b * 32, cnt = cols - c0 < 32 ? cols - c0 : 32;
+            quant_block(d + r * ld + c0, cnt, 1, norm_const, codes + r * cols + c0, 1,
+                        scales + r * nb + b);
+        }
+}
+
+/* Column direction: blocks of 32 consecutive rows in each column.
+ * codes (rows, cols); scales (ceil(rows/32), cols). */
+void orc_mx_quant_cols(const double *d, int64_t rows, int64_t cols, int64_t ld,
+                       float norm_const, uint8_t *codes, uint8_t *scales)
+{
+    int64_t nb = (rows + 31) / 32;
+    #pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < cols; ++c)
+        for (int64_t b = 0; b < nb; ++b) {
+            int64_t r0 = b * 32, cnt = rows - r0 < 32 ? rows - r0 : 32;
+            quant_block(d + r0 * ld + c, cnt, ld, norm_const, codes + r0 * cols + c, cols,
+                        scales + b * cols + c);
+        }
+}
+
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,183 @@
+"""Pins of the oracle's fused epilogues and MX output quantiser.
+
+  * sReLU / tanh clamp ("Grouped GEMM + sReLU (SM100)", Equations and Tanh
+    soft clamp): relu zeroes C <= 0, prob = 0 zeroes D, D <= s^2 prob, the
+    unclamped limit, and the closed form tanh(ln(2)/2) = 1/3.
+  * BF16 grouped ("Grouped GEMM (SM100 BF16)", Operation): numpy float64
+    matmul per expert, and the literal bias / no-bias asymmetry.
+  * RoPE ("GEMM + RoPE + MXFP8 Projection (SM100)", Equations): cos=1/sin=0
+    is the pure de-interleave, cos=0/sin=1 gives [-b, a], features before the
+    rotary part equal the plain projection, both weight layouts agree.
+  * Quantiser ("Grouped GEMM + dSwiGLU (SM100)", Step 3): closed forms for
+    powers of two, code range [224, 448], norm_const shifts, zero blocks and
+    half-step reconstruction.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+
+
+def _srelu_case(m=256, n=64, k=128, s=32.0, seed=0, L=2, sizes=(256, 0)):
+    off = np.cumsum(sizes).astype(np.int32)
+    p = W.grouped_srelu_problem(0, L, n, k, "e4m3", seed=seed, offsets=off)
+    r = O.grouped_srelu(p.t["a"], p.t["b"], p.t["sfa"], p.t["sfb"], p.t["offsets"],
+                        p.t["alpha"], p.t["prob"], p.sizes["m"], n, k, L, "e4m3", s)
+    return p, r
+
+
+def test_srelu_relu_and_prob_zeroes():
+    p, r = _srelu_case(s=0.0)
+    c, d = r["c"], r["d"]
+    assert np.all(d[c <= 0] == 0.0)
+    prob = p.t["prob"].double().numpy()
+    pos = c > 0
+    np.testing.assert_allclose(d[pos], (prob[:, None] * c ** 2)[pos], rtol=4e-16, atol=0)
+    assert np.all(d[prob == 0.0] == 0.0)
+
+
+def test_srelu_clamp_bound_and_unclamped_limit():
+    p, r = _srelu_case(s=0.5)           # tight clamp: many saturate
+    prob = p.t["prob"].double().numpy()[:, None]
+    assert np.all(r["d"] <= 0.25 * prob * (1 + 1e-15))
+    _, r_big = _srelu_case(s=1e30)
+    _, r_none = _srelu_case(s=0.0)
+    np.testing.assert_allclose(r_big["d"], r_none["d"], rtol=1e-14, atol=0)
+
+
+def test_srelu_tanh_closed_form_and_saturation():
+    # one-hot A, unit scales, B codes chosen so C = alpha * v; pick alpha so
+    # relu(C)/s = ln(2)/2 -> tanh = 1/3 exactly in reals -> D = prob * (s/3)^2.
+    n, k, s = 8, 32, 4.0
+    A = torch.zeros(256, k, dtype=torch.uint8); A[:, 0] = 0x38          # 1.0
+    B = torch.zeros(1, n, k, dtype=torch.uint8); B[0, :, 0] = 0x38
+    sfa = torch.full((W.sf_atom_bytes(256, k, 1),), 127, dtype=torch.uint8)
+    sfb = torch.full((W.sf_atom_bytes(n, k, 1),), 127, dtype=torch.uint8)
+    off = np.array([256], np.int32)
+    prob = np.full(256, 0.75, np.float32)
+    alpha = np.array([np.float32(s * math.log(2) / 2)], np.float32)
+    r = O.grouped_srelu(A, B, sfa, sfb, off, alpha, prob, 256, n, k, 1, "e4m3", s)
+    x = float(alpha[0]) / s                       # alpha rounded to fp32
+    want = 0.75 * (s * (math.exp(2 * x) - 1) / (math.exp(2 * x) + 1)) ** 2
+    np.testing.assert_allclose(r["d"], want, rtol=1e-14)
+    np.testing.assert_allclose(want, 0.75 * (s / 3) ** 2, rtol=1e-6)
+    # saturation: C >> s gives D == s^2 prob
+    alpha = np.array([1e4], np.float32)
+    r = O.grouped_srelu(A, B, sfa, sfb, off, alpha, prob, 256, n, k, 1, "e4m3", s)
+    assert np.all(r["d"] == 0.75 * s * s)
+
+
+def test_bf16_grouped_matches_numpy_per_expert_and_bias_branches():
+    sizes = np.array([256, 0, 512, 256])
+    off = np.cumsum(sizes).astype(np.int32)
+    n, k, L = 48, 96, 4
+    p = W.grouped_bf16_problem(0, L, n, k, seed=1, offsets=off, extra_rows=32)
+    m = p.sizes["m"]
+    a_bits, b_bits = O.bits16(p.t["a"]), O.bits16(p.t["b"])
+    a = p.t["a"].double().numpy(); b = p.t["b"].double().numpy()
+    alpha = p.t["alpha"].numpy(); prob = p.t["prob"].double().numpy()
+    bias = p.t["bias"].double().numpy()                     # (L, N)
+    rb = O.grouped_bf16(a_bits, b_bits, off, alpha, p.t["prob"], bias, m, n, k, L)
+    rn = O.grouped_bf16(a_bits, b_bits, off, alpha, p.t["prob"], None, m, n, k, L)
+    rz = O.grouped_bf16(a_bits, b_bits, off, alpha, p.t["prob"], np.zeros_like(bias), m, n, k, L)
+    begin = 0
+    for g in range(L):
+        rows = slice(begin, off[g]); begin = off[g]
+        G = float(alpha[g]) * (a[rows] @ b[g].T)
+        np.testing.assert_allclose(rn["c"][rows], G, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(rn["d"][rows], prob[rows, None] * G, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(rb["c"][rows], G + prob[rows, None] * bias[g][None, :],
+                                   rtol=1e-12, atol=1e-12)
+    assert np.array_equal(rb["c"], rb["d"], equal_nan=True)
+    # literal asymmetry: zero bias -> D == C == G; no bias -> D == prob * G
+    assert np.array_equal(rz["d"], rn["c"], equal_nan=True)
+    assert np.all(np.isnan(rn["c"][off[-1]:]))
+
+
+def _rope_case(cos_val=None, sin_val=None, tokens=8, q_lora=64, heads=3, w_out_in=True):
+    p = W.proj_rope_problem(tokens, q_lora, heads, 192, 64, seed=2, w_out_in=w_out_in)
+    if cos_val is not None:
+        p.t["cos"] = torch.full_like(p.t["cos"], cos_val)
+        p.t["sin"] = torch.full_like(p.t["sin"], sin_val)
+    y, s = O.proj_rope(O.bits16(p.t["x"]), O.bits16(p.t["w"]), O.bits16(p.t["cos"]),
+                       O.bits16(p.t["sin"]), tokens, q_lora, heads, 192, 64, int(w_out_in))
+    w = p.t["w"].double().numpy()
+    plain = p.t["x"].double().numpy() @ (w.T if w_out_in else w)
+    return y, plain
+
+
+def test_rope_identity_is_deinterleave():
+    y, plain = _rope_case(1.0, 0.0)
+    y = y.reshape(8, 3, 192); plain = plain.reshape(8, 3, 192)
+    np.testing.assert_allclose(y[..., :128], plain[..., :128], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(y[..., 128:160], plain[..., 128::2], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(y[..., 160:], plain[..., 129::2], rtol=1e-13, atol=1e-13)
+
+
+def test_rope_quarter_turn():
+    y, plain = _rope_case(0.0, 1.0)
+    y = y.reshape(8, 3, 192); plain = plain.reshape(8, 3, 192)
+    np.testing.assert_allclose(y[..., 128:160], -plain[..., 129::2], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(y[..., 160:], plain[..., 128::2], rtol=1e-13, atol=1e-13)
+
+
+def test_rope_weight_layouts_agree_and_norm_preserved_at_angle0():
+    y1, _ = _rope_case(w_out_in=True)
+    y0, _ = _rope_case(w_out_in=False)
+    assert np.array_equal(y1, y0)
+    # position 0 has angle 0 in the generated tables: cos = 1, sin = 0
+    cos, sin = W.rope_tables(4)
+    assert torch.all(cos[0] == 1) and torch.all(sin[0] == 0)
+
+
+def test_quantiser_power_of_two_closed_forms():
+    # block max exactly 448 * 2^j -> scale byte 127 + j and codes = RNE(D / 2^j)
+    rng = np.random.default_rng(5)
+    for j in (-20, -3, 0, 4, 30):
+        blk = rng.uniform(-1, 1, 32) * 448 * 2.0 ** j
+        blk[7] = 448 * 2.0 ** j
+        codes, scales = O.mx_quant_rows(blk[None, :])
+        assert scales[0, 0] == 127 + j
+        assert codes[0, 7] == 0x7E
+        for i in range(32):
+            v = float(np.float32(blk[i])) / 2.0 ** j
+            assert codes[0, i] == O.enc_e4m3(v)
+    # one step above a power of two rounds the scale up
+    blk = np.full(32, 448.0); blk[0] = 449.0
+    _, sc = O.mx_quant_rows(blk[None, :])
+    assert sc[0, 0] == 128
+
+
+def test_quantiser_code_range_norm_const_and_zero_blocks():
+    rng = np.random.default_rng(6)
+    d = rng.standard_normal((64, 96)) * np.exp(rng.uniform(-8, 8, (64, 1)))
+    d[3, 32:64] = 0.0
+    codes, scales = O.mx_quant_rows(d)
+    vals = np.vectorize(O.dec_e4m3)(codes.astype(np.uint32))
+    blkmax = np.abs(vals).reshape(64, 3, 32).max(-1)
+    nz = np.abs(d).reshape(64, 3, 32).max(-1) > 0
+    assert np.all((blkmax[nz] >= 224) & (blkmax[nz] <= 448))
+    assert scales[3, 1] == 0 and np.all(codes[3, 32:64] == 0)
+    # half-step reconstruction: |dec(code) * 2^(byte-127) - D| <= half an E4M3 step
+    deq = vals * np.exp2(np.repeat(scales.astype(np.float64), 32, axis=1) - 127)
+    f = np.abs(vals)
+    step = np.where(f < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(f, 1e-300))) - 3))
+    step *= np.exp2(np.repeat(scales.astype(np.float64), 32, axis=1) - 127)
+    assert np.all(np.abs(deq - d.astype(np.float32)) <= 0.5 * step * (1 + 1e-6) + 1e-300)
+    # norm_const = 2^j shifts every nonzero block's byte by j, codes unchanged
+    for j in (-3, 5):
+        c2, s2 = O.mx_quant_rows(d, norm_const=2.0 ** j)
+        assert np.array_equal(c2, codes)
+        assert np.array_equal(s2[nz].astype(int), scales[nz].astype(int) + j)
+
+
+def test_quantiser_columns_equal_rows_of_transpose():
+    rng = np.random.default_rng(8)
+    d = rng.standard_normal((96, 40)) * 3
+    cc, cs = O.mx_quant_cols(d)
+    rc, rs = O.mx_quant_rows(np.ascontiguousarray(d.T))
+    assert np.array_equal(cc, rc.T) and np.array_equal(cs, rs.T)
