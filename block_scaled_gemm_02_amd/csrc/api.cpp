@@ -1,0 +1,318 @@
+// C ABI of the block-scaled GEMM library: argument validation (the pages'
+// check_support()), status reporting and dispatch to the gfx950 kernels.
+//
+// Every host-detectable error is returned before anything is enqueued, as
+// the "Grouped GEMM (SM100 BF16)" page requires of its launches
+// (Scheduling, caching, and errors).  Device-resident values are not read.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/bsg.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(int dt)
+{
+    switch (dt) {
+    case BSG_F32: return 4;
+    case BSG_F16:
+    case BSG_BF16: return 2;
+    default: return 1;
+    }
+}
+
+bool is_float_out(int dt) { return dt == BSG_F32 || dt == BSG_F16 || dt == BSG_BF16; }
+
+// Device check: the kernels are built for gfx950 only.
+int check_device()
+{
+    static int cached[64];   // 0 unknown, 1 ok, 2 bad
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(BSG_ERR_DEVICE, "hipGetDevice failed");
+    if (dev >= 0 && dev < 64 && cached[dev] == 1) return BSG_OK;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return fail(BSG_ERR_DEVICE, "hipGetDeviceProperties failed");
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+        if (dev >= 0 && dev < 64) cached[dev] = 2;
+        return fail(BSG_ERR_DEVICE, "device %d is %s; this library is built for gfx950", dev,
+                    prop.gcnArchName);
+    }
+    if (dev >= 0 && dev < 64) cached[dev] = 1;
+    return BSG_OK;
+}
+
+int launch_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return BSG_OK;
+    if (e == hipErrorNotSupported) return fail(BSG_ERR_UNSUPPORTED, "%s: not supported", what);
+    return fail(BSG_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+}
+
+int check_ab_sf(int ab_dtype, int sf_vec_size)
+{
+    if (ab_dtype != BSG_E4M3 && ab_dtype != BSG_E2M1X2) {
+        if (ab_dtype == BSG_E5M2)
+            return fail(BSG_ERR_UNSUPPORTED, "ab_dtype E5M2 is not built (E4M3 and E2M1X2 are)");
+        return fail(BSG_ERR_DTYPE, "ab_dtype %d is not a block-scaled operand dtype", ab_dtype);
+    }
+    if (sf_vec_size != 32) {
+        if (sf_vec_size == 16)
+            return fail(BSG_ERR_UNSUPPORTED, "sf_vec_size 16 is not built (32 is)");
+        return fail(BSG_ERR_SHAPE, "sf_vec_size must be 32 (got %d)", sf_vec_size);
+    }
+    return BSG_OK;
+}
+
+int row_bytes(int ab_dtype, int64_t k) { return (int)(ab_dtype == BSG_E2M1X2 ? k / 2 : k); }
+
+}  // namespace
+
+extern "C" {
+
+const char *bsg_status_string(int status)
+{
+    switch (status) {
+    case BSG_OK: return "ok";
+    case BSG_ERR_NULLPTR: return "required pointer is NULL";
+    case BSG_ERR_SHAPE: return "invalid or inconsistent shape";
+    case BSG_ERR_DTYPE: return "invalid dtype";
+    case BSG_ERR_ALIGN: return "16-byte alignment violated";
+    case BSG_ERR_UNSUPPORTED: return "combination not supported by this build";
+    case BSG_ERR_DEVICE: return "device error (not gfx950 or HIP failure)";
+    case BSG_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+const char *bsg_last_error(void) { return g_err; }
+
+int bsg_version(void) { return 100; }
+
+// ---------------------------------------------------------------------------
+// gemm_amax
+// ---------------------------------------------------------------------------
+int bsg_validate_gemm_amax(const void *a, const void *b, const uint8_t *sfa, const uint8_t *sfb,
+                           void *c, float *amax, int64_t m, int64_t n, int64_t k, int64_t l,
+                           int ab_dtype, int c_dtype, int sf_vec_size)
+{
+    (void)amax;
+    int st = check_ab_sf(ab_dtype, sf_vec_size);
+    if (st) return st;
+    if (m < 0 || n < 0 || k < 0 || l < 0) return fail(BSG_ERR_SHAPE, "negative size");
+    if (k % 32) return fail(BSG_ERR_SHAPE, "K=%lld must be a multiple of sf_vec_size 32", (long long)k);
+    if (!is_float_out(c_dtype)) {
+        if (c_dtype == BSG_E4M3 || c_dtype == BSG_E5M2 || c_dtype == BSG_E2M1X2)
+            return fail(BSG_ERR_UNSUPPORTED, "low-precision C dtype %d is not built", c_dtype);
+        return fail(BSG_ERR_DTYPE, "c_dtype %d is not an output dtype", c_dtype);
+    }
+    if (m * n * l == 0) return BSG_OK;   // nothing to read or write but amax
+    if (!a || !b || !sfa || !sfb || !c) return fail(BSG_ERR_NULLPTR, "a, b, sfa, sfb and c are required");
+    if (k > 0 && (!aligned16(a) || !aligned16(b))) return fail(BSG_ERR_ALIGN, "A and B must be 16-byte aligned");
+    if (!aligned16(c) || (n * elem_bytes(c_dtype)) % 16)
+        return fail(BSG_ERR_ALIGN, "C must be 16-byte aligned with N*sizeof(C) a multiple of 16");
+    if ((int64_t)row_bytes(ab_dtype, k) * 256 >= (1ll << 31))
+        return fail(BSG_ERR_UNSUPPORTED, "K too large for 32-bit tile offsets");
+    return BSG_OK;
+}
+
+int gemm_amax(const void *a, const void *b, const uint8_t *sfa, const uint8_t *sfb, void *c,
+              float *amax, int64_t m, int64_t n, int64_t k, int64_t l, int ab_dtype, int c_dtype,
+              int sf_vec_size, void *stream)
+{
+    int st = bsg_validate_gemm_amax(a, b, sfa, sfb, c, amax, m, n, k, l, ab_dtype, c_dtype, sf_vec_size);
+    if (st) return st;
+    if ((st = check_device())) return st;
+    bsg::GemmAmaxArgs args{static_cast<const uint8_t *>(a), static_cast<const uint8_t *>(b), sfa, sfb,
+                           c, amax, m, n, k, l, ab_dtype == BSG_E2M1X2 ? 1 : 0, c_dtype};
+    return launch_status(bsg::launch_gemm_amax(args, static_cast<hipStream_t>(stream)), "gemm_amax");
+}
+
+// ---------------------------------------------------------------------------
+// Grouped: shared checks
+// ---------------------------------------------------------------------------
+static int check_grouped_common(const void *a, const void *b, const int32_t *offsets,
+                                const float *alpha, const float *prob, void *d, int64_t m, int64_t n,
+                                int64_t k, int64_t num_experts)
+{
+    if (m < 0 || n < 0 || k < 0) return fail(BSG_ERR_SHAPE, "negative size");
+    if (num_experts < 1 || num_experts > 1024)
+        return fail(BSG_ERR_SHAPE, "expert count L=%lld must be in [1, 1024]", (long long)num_experts);
+    if (m % 256) return fail(BSG_ERR_SHAPE, "M=%lld must be a multiple of 256", (long long)m);
+    if (!offsets || !alpha) return fail(BSG_ERR_NULLPTR, "padded_offsets and alpha are required");
+    if (!prob) return fail(BSG_ERR_NULLPTR, "prob is required");
+    if (m * n == 0) return BSG_OK;
+    if (!a || !b || !d) return fail(BSG_ERR_NULLPTR, "a, b and d are required");
+    if (k > 0 && (!aligned16(a) || !aligned16(b))) return fail(BSG_ERR_ALIGN, "A and B must be 16-byte aligned");
+    return BSG_OK;
+}
+
+// ---------------------------------------------------------------------------
+// grouped_gemm (BF16)
+// ---------------------------------------------------------------------------
+int bsg_validate_grouped_gemm(const void *a, const void *b, const int32_t *padded_offsets,
+                              const float *alpha, const float *prob, const void *bias, void *c,
+                              void *d, int64_t m, int64_t n, int64_t k, int64_t num_experts,
+                              int bias_dtype, int c_dtype, int d_dtype)
+{
+    int st = check_grouped_common(a, b, padded_offsets, alpha, prob, d, m, n, k, num_experts);
+    if (st) return st;
+    if (k % 8) return fail(BSG_ERR_ALIGN, "K=%lld: rows of bf16 A/B must be 16-byte multiples", (long long)k);
+    if (!is_float_out(c_dtype) || !is_float_out(d_dtype))
+        return fail(BSG_ERR_DTYPE, "C and D dtypes must be F32, F16 or BF16");
+    if (bias && !is_float_out(bias_dtype)) return fail(BSG_ERR_DTYPE, "bias dtype must be F32, F16 or BF16");
+    if (m * n == 0) return BSG_OK;
+    if (!aligned16(d) || (n * elem_bytes(d_dtype)) % 16 || (c && (!aligned16(c) || (n * elem_bytes(c_dtype)) % 16)))
+        return fail(BSG_ERR_ALIGN, "C/D must be 16-byte aligned with N*sizeof a multiple of 16");
+    if ((int64_t)2 * k * 256 >= (1ll << 31)) return fail(BSG_ERR_UNSUPPORTED, "K too large");
+    return BSG_OK;
+}
+
+int grouped_gemm(const void *a, const void *b, const int32_t *padded_offsets, const float *alpha,
+                 const float *prob, const void *bias, void *c, void *d, int64_t m, int64_t n,
+                 int64_t k, int64_t num_experts, int bias_dtype, int c_dtype, int d_dtype,
+                 void *stream)
+{
+    int st = bsg_validate_grouped_gemm(a, b, padded_offsets, alpha, prob, bias, c, d, m, n, k,
+                                       num_experts, bias_dtype, c_dtype, d_dtype);
+    if (st) return st;
+    if ((st = check_device())) return st;
+    bsg::GroupedArgs args{};
+    args.a = static_cast<const uint8_t *>(a); args.b = static_cast<const uint8_t *>(b);
+    args.offsets = padded_offsets; args.alpha = alpha; args.prob = prob; args.bias = bias;
+    args.c = c; args.d = d; args.m = m; args.n = n; args.k = k; args.num_experts = num_experts;
+    args.fmt = 2; args.c_dtype = c_dtype; args.d_dtype = d_dtype; args.bias_dtype = bias_dtype;
+    return launch_status(bsg::launch_grouped_gemm(args, static_cast<hipStream_t>(stream)), "grouped_gemm");
+}
+
+// ---------------------------------------------------------------------------
+// grouped_gemm_srelu
+// ---------------------------------------------------------------------------
+int bsg_validate_grouped_gemm_srelu(const void *a, const void *b, const uint8_t *sfa,
+                                    const uint8_t *sfb, const int32_t *padded_offsets,
+                                    const float *alpha, const float *prob, const float *norm_const,
+                                    void *c, void *d, void *d_col, uint8_t *sfd_row,
+                                    uint8_t *sfd_col, float *amax, int64_t m, int64_t n, int64_t k,
+                                    int64_t num_experts, int ab_dtype, int c_dtype, int d_dtype,
+                                    int sf_vec_size, float tanh_clamp_scale)
+{
+    (void)amax;
+    int st = check_ab_sf(ab_dtype, sf_vec_size);
+    if (st) return st;
+    if ((st = check_grouped_common(a, b, padded_offsets, alpha, prob, d, m, n, k, num_experts))) return st;
+    if (k % 32) return fail(BSG_ERR_SHAPE, "K=%lld must be a multiple of sf_vec_size 32", (long long)k);
+    if (n % 32) return fail(BSG_ERR_SHAPE, "N=%lld must be a multiple of 32", (long long)n);
+    if (!(tanh_clamp_scale == tanh_clamp_scale)) return fail(BSG_ERR_SHAPE, "tanh_clamp_scale is NaN");
+    if (c && !is_float_out(c_dtype)) return fail(BSG_ERR_DTYPE, "C dtype must be F32, F16 or BF16");
+    const bool fp8_out = d_dtype == BSG_E4M3;
+    if (!fp8_out && !is_float_out(d_dtype)) {
+        if (d_dtype == BSG_E5M2 || d_dtype == BSG_E2M1X2)
+            return fail(BSG_ERR_UNSUPPORTED, "D dtype %d is not built", d_dtype);
+        return fail(BSG_ERR_DTYPE, "D dtype %d invalid", d_dtype);
+    }
+    if (fp8_out) {
+        if (ab_dtype != BSG_E4M3)
+            return fail(BSG_ERR_DTYPE, "FP8 D requires FP8 A/B (FP4 inputs take fp16/bf16/fp32 D)");
+        if (!norm_const || !sfd_row || !sfd_col || !d_col)
+            return fail(BSG_ERR_NULLPTR, "FP8 D needs norm_const, d_col, sfd_row and sfd_col");
+    }
+    if (m * n == 0) return BSG_OK;
+    if (!sfa || !sfb) return fail(BSG_ERR_NULLPTR, "sfa and sfb are required");
+    const int db = fp8_out ? 1 : elem_bytes(d_dtype);
+    if (!aligned16(d) || (n * db) % 16 || (d_col && !aligned16(d_col)) ||
+        (c && (!aligned16(c) || (n * elem_bytes(c_dtype)) % 16)))
+        return fail(BSG_ERR_ALIGN, "C/D/D_col must be 16-byte aligned with 16-byte rows");
+    if ((int64_t)row_bytes(ab_dtype, k) * 256 >= (1ll << 31)) return fail(BSG_ERR_UNSUPPORTED, "K too large");
+    return BSG_OK;
+}
+
+int grouped_gemm_srelu(const void *a, const void *b, const uint8_t *sfa, const uint8_t *sfb,
+                       const int32_t *padded_offsets, const float *alpha, const float *prob,
+                       const float *norm_const, void *c, void *d, void *d_col, uint8_t *sfd_row,
+                       uint8_t *sfd_col, float *amax, int64_t m, int64_t n, int64_t k,
+                       int64_t num_experts, int ab_dtype, int c_dtype, int d_dtype, int sf_vec_size,
+                       float tanh_clamp_scale, void *stream)
+{
+    int st = bsg_validate_grouped_gemm_srelu(a, b, sfa, sfb, padded_offsets, alpha, prob, norm_const,
+                                             c, d, d_col, sfd_row, sfd_col, amax, m, n, k,
+                                             num_experts, ab_dtype, c_dtype, d_dtype, sf_vec_size,
+                                             tanh_clamp_scale);
+    if (st) return st;
+    if ((st = check_device())) return st;
+    bsg::GroupedArgs args{};
+    args.a = static_cast<const uint8_t *>(a); args.b = static_cast<const uint8_t *>(b);
+    args.sfa = sfa; args.sfb = sfb; args.offsets = padded_offsets; args.alpha = alpha;
+    args.prob = prob; args.norm_const = norm_const; args.c = c; args.d = d; args.d_col = d_col;
+    args.sfd_row = sfd_row; args.sfd_col = sfd_col;
+    args.amax = d_dtype == BSG_E4M3 ? nullptr : amax;
+    args.m = m; args.n = n; args.k = k; args.num_experts = num_experts;
+    args.fmt = ab_dtype == BSG_E2M1X2 ? 1 : 0; args.c_dtype = c_dtype; args.d_dtype = d_dtype;
+    args.tanh_s = tanh_clamp_scale > 0.0f ? tanh_clamp_scale : 0.0f;
+    return launch_status(bsg::launch_grouped_srelu(args, static_cast<hipStream_t>(stream)),
+                         "grouped_gemm_srelu");
+}
+
+// ---------------------------------------------------------------------------
+// gemm_proj_rope_mxfp8
+// ---------------------------------------------------------------------------
+int bsg_validate_gemm_proj_rope_mxfp8(const void *x, const void *w, const uint8_t *x_scale,
+                                      const uint8_t *w_scale, const void *cos, const void *sin,
+                                      uint8_t *out_fp8_row, uint8_t *out_scales_row,
+                                      uint8_t *out_fp8_col, uint8_t *out_scales_col,
+                                      int64_t tokens, int64_t q_lora, int64_t num_heads,
+                                      int64_t head_dim, int64_t qk_rope, int in_dtype, int w_out_in)
+{
+    if (in_dtype == BSG_E4M3) return fail(BSG_ERR_UNSUPPORTED, "MXFP8-input projection is not built");
+    if (in_dtype != BSG_BF16) return fail(BSG_ERR_DTYPE, "x/w dtype must be BF16");
+    if (x_scale || w_scale) return fail(BSG_ERR_SHAPE, "x_scale/w_scale must be NULL for BF16 inputs");
+    if (tokens < 0 || q_lora < 0 || num_heads < 0) return fail(BSG_ERR_SHAPE, "negative size");
+    if (tokens % 128) return fail(BSG_ERR_SHAPE, "tokens=%lld must be a multiple of 128", (long long)tokens);
+    if (q_lora % 32) return fail(BSG_ERR_SHAPE, "q_lora must be a multiple of 32");
+    if (head_dim != 192 || qk_rope != 64)
+        return fail(BSG_ERR_UNSUPPORTED, "only head_dim 192 with qk_rope 64 is built");
+    if (w_out_in != 0 && w_out_in != 1) return fail(BSG_ERR_SHAPE, "w_out_in must be 0 or 1");
+    if (tokens * num_heads == 0) return BSG_OK;
+    if (!x || !w || !cos || !sin || !out_fp8_row || !out_scales_row || !out_fp8_col || !out_scales_col)
+        return fail(BSG_ERR_NULLPTR, "all tensors are required");
+    if (!aligned16(x) || !aligned16(w) || !aligned16(out_fp8_row) || !aligned16(out_fp8_col))
+        return fail(BSG_ERR_ALIGN, "x, w and the fp8 outputs must be 16-byte aligned");
+    return BSG_OK;
+}
+
+int gemm_proj_rope_mxfp8(const void *x, const void *w, const uint8_t *x_scale, const uint8_t *w_scale,
+                         const void *cos, const void *sin, uint8_t *out_fp8_row,
+                         uint8_t *out_scales_row, uint8_t *out_fp8_col, uint8_t *out_scales_col,
+                         int64_t tokens, int64_t q_lora, int64_t num_heads, int64_t head_dim,
+                         int64_t qk_rope, int in_dtype, int w_out_in, void *stream)
+{
+    int st = bsg_validate_gemm_proj_rope_mxfp8(x, w, x_scale, w_scale, cos, sin, out_fp8_row,
+                                               out_scales_row, out_fp8_col, out_scales_col, tokens,
+                                               q_lora, num_heads, head_dim, qk_rope, in_dtype, w_out_in);
+    if (st) return st;
+    if ((st = check_device())) return st;
+    bsg::ProjRopeArgs args{static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w),
+                           static_cast<const uint16_t *>(cos), static_cast<const uint16_t *>(sin),
+                           out_fp8_row, out_scales_row, out_fp8_col, out_scales_col,
+                           tokens, q_lora, num_heads, head_dim, qk_rope, w_out_in};
+    return launch_status(bsg::launch_proj_rope(args, static_cast<hipStream_t>(stream)),
+                         "gemm_proj_rope_mxfp8");
+}
+
+}  // extern "C"

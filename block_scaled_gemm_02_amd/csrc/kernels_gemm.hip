@@ -1,0 +1,256 @@
+// Dense and grouped block-scaled GEMM kernels for gfx950.
+//
+//   k_gemm_amax      "GEMM + Amax (SM100)": C = sum_k A_hat B_hat per batch,
+//                    Amax = max |C| (one atomicMax per workgroup).
+//   k_grouped        "Grouped GEMM (SM100 BF16)" and "Grouped GEMM + sReLU
+//                    (SM100)": tiles of 256 rows never straddle an expert
+//                    because every padded_offsets entry is a multiple of 256.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace bsg {
+
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_E4M3 = 3 };
+
+__device__ __forceinline__ void store_elem(void *base, int64_t idx, float v, int dtype)
+{
+    if (dtype == DT_F32) {
+        static_cast<float *>(base)[idx] = v;
+    } else if (dtype == DT_BF16) {
+        static_cast<uint16_t *>(base)[idx] = f32_to_bf16_rne(v);
+    } else {
+        static_cast<uint16_t *>(base)[idx] = f32_to_f16_rne(v);
+    }
+}
+
+__device__ __forceinline__ float load_elem(const void *base, int64_t idx, int dtype)
+{
+    if (dtype == DT_F32) return static_cast<const float *>(base)[idx];
+    uint16_t h = static_cast<const uint16_t *>(base)[idx];
+    if (dtype == DT_BF16) return __uint_as_float((uint32_t)h << 16);
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+__global__ void k_fill_zero(float *p, int64_t n)
+{
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+}
+
+static hipError_t zero_floats(float *p, int64_t n, hipStream_t s)
+{
+    if (!p || n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
+static inline uint32_t row_bytes_of(int fmt, int64_t k)
+{
+    return (uint32_t)(fmt == FMT_E2M1 ? k / 2 : (fmt == FMT_BF16 ? 2 * k : k));
+}
+
+// ---------------------------------------------------------------------------
+// Dense batched GEMM + global amax
+// ---------------------------------------------------------------------------
+struct GemmAmaxParams {
+    const uint8_t *a, *b, *sfa, *sfb;
+    void *c;
+    float *amax;
+    int64_t m, n, k;
+    int64_t m_t, n_t, k_t;   // ceil(M/128), ceil(N/128), ceil(K/128)
+    uint32_t row_bytes;
+    int c_dtype;
+};
+
+template <int F>
+__global__ void __launch_bounds__(256) k_gemm_amax(GemmAmaxParams p)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kStageBytes];
+    __shared__ float red[4];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
+    const int64_t batch = blockIdx.z;
+    const int64_t m0 = (int64_t)blockIdx.y * kTileM, n0 = (int64_t)blockIdx.x * kTileN;
+    const int64_t rows_a = p.m - m0 < kTileM ? p.m - m0 : kTileM;
+    const int64_t rows_b = p.n - n0 < kTileN ? p.n - n0 : kTileN;
+
+    OperandDesc A{p.a + (batch * p.m + m0) * p.row_bytes, (uint32_t)(rows_a * p.row_bytes),
+                  p.row_bytes, p.sfa, batch, p.m_t, p.k_t, m0 / 128, p.m_t - 1};
+    OperandDesc B{p.b + (batch * p.n + n0) * p.row_bytes, (uint32_t)(rows_b * p.row_bytes),
+                  p.row_bytes, p.sfb, batch, p.n_t, p.k_t, n0 / 128, p.n_t - 1};
+    f32x16 acc[4][4];
+    mainloop<F>(acc, lds, A, B, p.k);
+
+    float lmax = 0.0f;
+    const int64_t cbase = batch * p.m * p.n;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t row = m0 + acc_row(wm, i, v, lane);
+            if (row >= p.m) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t col = n0 + acc_col(wn, j, lane);
+                if (col >= p.n) continue;
+                const float x = acc[i][j][v];
+                store_elem(p.c, cbase + row * p.n + col, x, p.c_dtype);
+                lmax = fmaxf(lmax, fabsf(x));
+            }
+        }
+    if (p.amax) block_amax_atomic(lmax, p.amax, red);
+}
+
+hipError_t launch_gemm_amax(const GemmAmaxArgs &a, hipStream_t s)
+{
+    hipError_t e = zero_floats(a.amax, 1, s);
+    if (e != hipSuccess) return e;
+    if (a.m == 0 || a.n == 0 || a.l == 0) return hipSuccess;
+    GemmAmaxParams p;
+    p.a = a.a; p.b = a.b; p.sfa = a.sfa; p.sfb = a.sfb; p.c = a.c; p.amax = a.amax;
+    p.m = a.m; p.n = a.n; p.k = a.k;
+    p.m_t = (a.m + 127) / 128; p.n_t = (a.n + 127) / 128; p.k_t = (a.k + 127) / 128;
+    p.row_bytes = row_bytes_of(a.fmt, a.k);
+    p.c_dtype = a.c_dtype;
+    dim3 grid((unsigned)((a.n + kTileN - 1) / kTileN), (unsigned)((a.m + kTileM - 1) / kTileM),
+              (unsigned)a.l);
+    if (a.fmt == FMT_E4M3)
+        hipLaunchKernelGGL(k_gemm_amax<FMT_E4M3>, grid, dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL(k_gemm_amax<FMT_E2M1>, grid, dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM over padded_offsets expert ranges
+// ---------------------------------------------------------------------------
+enum : int { EPI_BF16_BIAS = 0, EPI_SRELU = 1 };
+
+struct GroupedParams {
+    const uint8_t *a, *b, *sfa, *sfb;
+    const int32_t *offsets;
+    const float *alpha, *prob;
+    const void *bias;
+    void *c, *d, *d_col;
+    float *amax;
+    int64_t m, n, k, num_experts;
+    int64_t m_t, n_t, k_t;
+    uint32_t row_bytes;
+    int c_dtype, d_dtype, bias_dtype;
+    float tanh_s, tanh_inv_s;
+};
+
+// Index of the expert whose range [offsets[g-1], offsets[g]) holds row r:
+// the number of offsets <= r (offsets are nondecreasing).
+__device__ __forceinline__ int expert_of(const int32_t *offsets, int num, int64_t r)
+{
+    int lo = 0, hi = num;   // first g with offsets[g] > r
+    while (lo < hi) {
+        int mid = (lo + hi) >> 1;
+        if ((int64_t)offsets[mid] > r) hi = mid;
+        else lo = mid + 1;
+    }
+    return lo;
+}
+
+template <int F, int EPI>
+__global__ void __launch_bounds__(256) k_grouped(GroupedParams p)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kStageBytes];
+    __shared__ float red[4];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
+    const int64_t m0 = (int64_t)blockIdx.y * kTileM, n0 = (int64_t)blockIdx.x * kTileN;
+    const int64_t valid_m = p.offsets[p.num_experts - 1];
+    if (m0 >= valid_m) return;                      // uniform per workgroup
+    const int g = expert_of(p.offsets, (int)p.num_experts, m0);
+    const int64_t rows_b = p.n - n0 < kTileN ? p.n - n0 : kTileN;
+
+    OperandDesc A{p.a + m0 * p.row_bytes, (uint32_t)(kTileM * p.row_bytes), p.row_bytes, p.sfa,
+                  0, p.m_t, p.k_t, m0 / 128, p.m_t - 1};
+    OperandDesc B{p.b + ((int64_t)g * p.n + n0) * p.row_bytes, (uint32_t)(rows_b * p.row_bytes),
+                  p.row_bytes, p.sfb, g, p.n_t, p.k_t, n0 / 128, p.n_t - 1};
+    f32x16 acc[4][4];
+    mainloop<F>(acc, lds, A, B, p.k);
+
+    const float alpha = p.alpha[g];
+    float lmax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t row = m0 + acc_row(wm, i, v, lane);
+            const float pr = p.prob[row];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t col = n0 + acc_col(wn, j, lane);
+                if (col >= p.n) continue;
+                const int64_t idx = row * p.n + col;
+                const float gval = alpha * acc[i][j][v];
+                if constexpr (EPI == EPI_BF16_BIAS) {
+                    float cval, dval;
+                    if (p.bias) {
+                        cval = gval + pr * load_elem(p.bias, (int64_t)g * p.n + col, p.bias_dtype);
+                        dval = cval;
+                    } else {
+                        cval = gval;
+                        dval = pr * gval;
+                    }
+                    if (p.c) store_elem(p.c, idx, cval, p.c_dtype);
+                    store_elem(p.d, idx, dval, p.d_dtype);
+                } else {
+                    float x = fmaxf(gval, 0.0f);
+                    if (p.tanh_s > 0.0f) x = p.tanh_s * fminf(1.0f, tanh_pos(x * p.tanh_inv_s));
+                    const float dval = pr * x * x;
+                    if (p.c) store_elem(p.c, idx, gval, p.c_dtype);
+                    store_elem(p.d, idx, dval, p.d_dtype);
+                    if (p.d_col) store_elem(p.d_col, idx, dval, p.d_dtype);
+                    lmax = fmaxf(lmax, fabsf(dval));
+                }
+            }
+        }
+    if constexpr (EPI == EPI_SRELU) {
+        if (p.amax) block_amax_atomic(lmax, p.amax + g, red);
+    }
+}
+
+static GroupedParams grouped_params(const GroupedArgs &a)
+{
+    GroupedParams p;
+    p.a = a.a; p.b = a.b; p.sfa = a.sfa; p.sfb = a.sfb; p.offsets = a.offsets;
+    p.alpha = a.alpha; p.prob = a.prob; p.bias = a.bias;
+    p.c = a.c; p.d = a.d; p.d_col = a.d_col; p.amax = a.amax;
+    p.m = a.m; p.n = a.n; p.k = a.k; p.num_experts = a.num_experts;
+    p.m_t = (a.m + 127) / 128; p.n_t = (a.n + 127) / 128; p.k_t = (a.k + 127) / 128;
+    p.row_bytes = row_bytes_of(a.fmt, a.k);
+    p.c_dtype = a.c_dtype; p.d_dtype = a.d_dtype; p.bias_dtype = a.bias_dtype;
+    p.tanh_s = a.tanh_s;
+    p.tanh_inv_s = a.tanh_s > 0.0f ? 1.0f / a.tanh_s : 0.0f;
+    return p;
+}
+
+hipError_t launch_grouped_gemm(const GroupedArgs &a, hipStream_t s)
+{
+    if (a.m == 0 || a.n == 0) return hipSuccess;
+    GroupedParams p = grouped_params(a);
+    dim3 grid((unsigned)((a.n + kTileN - 1) / kTileN), (unsigned)(a.m / kTileM));
+    hipLaunchKernelGGL((k_grouped<FMT_BF16, EPI_BF16_BIAS>), grid, dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped_srelu(const GroupedArgs &a, hipStream_t s)
+{
+    hipError_t e = zero_floats(a.amax, a.num_experts, s);
+    if (e != hipSuccess) return e;
+    if (a.m == 0 || a.n == 0) return hipSuccess;
+    if (a.d_dtype == DT_E4M3) return hipErrorNotSupported;
+    GroupedParams p = grouped_params(a);
+    dim3 grid((unsigned)((a.n + kTileN - 1) / kTileN), (unsigned)(a.m / kTileM));
+    if (a.fmt == FMT_E4M3)
+        hipLaunchKernelGGL((k_grouped<FMT_E4M3, EPI_SRELU>), grid, dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((k_grouped<FMT_E2M1, EPI_SRELU>), grid, dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_proj_rope(const ProjRopeArgs &, hipStream_t) { return hipErrorNotSupported; }
+
+}  // namespace bsg

@@ -1,0 +1,44 @@
+// Host-side launch interface between the C ABI (api.cpp) and the kernels.
+// Arguments have already been validated when these are called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsg {
+
+struct GemmAmaxArgs {
+    const uint8_t *a, *b, *sfa, *sfb;
+    void *c;
+    float *amax;
+    int64_t m, n, k, l;
+    int fmt;       // 0 = E4M3, 1 = E2M1
+    int c_dtype;   // bsg_dtype
+};
+
+struct GroupedArgs {
+    const uint8_t *a, *b, *sfa, *sfb;   // sfa/sfb null for BF16
+    const int32_t *offsets;
+    const float *alpha, *prob, *norm_const;
+    const void *bias;
+    void *c, *d, *d_col;
+    uint8_t *sfd_row, *sfd_col;
+    float *amax;
+    int64_t m, n, k, num_experts;
+    int fmt;        // 0 = E4M3, 1 = E2M1, 2 = BF16
+    int c_dtype, d_dtype, bias_dtype;
+    float tanh_s;   // <= 0: no clamp
+};
+
+struct ProjRopeArgs {
+    const uint16_t *x, *w, *cos, *sin;
+    uint8_t *q_row, *s_row, *q_col, *s_col;
+    int64_t tokens, q_lora, heads, head_dim, qk_rope;
+    int w_out_in;
+};
+
+hipError_t launch_gemm_amax(const GemmAmaxArgs &a, hipStream_t s);
+hipError_t launch_grouped_gemm(const GroupedArgs &a, hipStream_t s);
+hipError_t launch_grouped_srelu(const GroupedArgs &a, hipStream_t s);
+hipError_t launch_proj_rope(const ProjRopeArgs &a, hipStream_t s);
+
+}  // namespace bsg

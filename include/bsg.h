@@ -1,0 +1,227 @@
+/*
+ * bsg.h -- block-scaled GEMM family for AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  Four operations, each the
+ * problem statement of one cuDNN frontend "GEMM fusions" documentation page:
+ *
+ *   gemm_amax             "GEMM + Amax (SM100)"
+ *   grouped_gemm          "Grouped GEMM (SM100 BF16)"
+ *   grouped_gemm_srelu    "Grouped GEMM + sReLU (SM100)"
+ *   gemm_proj_rope_mxfp8  "GEMM + RoPE + MXFP8 Projection (SM100)"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer on the current HIP device;
+ *    `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *  - All calls are asynchronous: arguments are validated on the host, then
+ *    kernels are enqueued on `stream`; there is no host synchronisation.
+ *    Every error the host can detect is returned BEFORE anything is
+ *    enqueued ("Grouped GEMM (SM100 BF16)", Scheduling, caching, and errors).
+ *  - The caller owns every buffer and keeps it alive and unmodified until
+ *    the stream has completed the call ("Grouped GEMM (SM100 BF16)",
+ *    Tensors and layouts).  The library allocates no device memory per call
+ *    (same page, Using JAX arrays: workspaces belong to the caller).
+ *  - Device-resident VALUES (padded_offsets, alpha, prob, ...) are the
+ *    caller's responsibility and are not checked ("Grouped GEMM + dSwiGLU
+ *    (SM100)", JAX execution: offsets are the caller's responsibility).
+ *  - Operand layouts: A (M,K,L) and B (N,K,L) are k-major, i.e. memory
+ *    order [L][rows][K]; C/D are n-major, memory order [L][M][N].  Packed
+ *    FP4 (E2M1X2) stores two codes per byte, element 2j in the low nibble,
+ *    so a row holds K/2 bytes ("GEMM + Amax (SM100)", Layouts and strides).
+ *  - Scale factors: one E8M0 byte per 32 consecutive K elements of a row
+ *    (sf_vec_size = 32), stored in the scale-atom layout of the pages'
+ *    Shapes sections: logical (32, 4, ceil(MN/128), 4, ceil(K/128), L),
+ *    i.e. the C-contiguous physical buffer (L, ceil(MN/128), ceil(K/128),
+ *    32, 4, 4).  The byte for row r, K-block kb = k/32, batch l sits at
+ *        (((l*MN' + r/128)*K' + kb/4)*32 + r%32)*16 + ((r%128)/32)*4 + kb%4
+ *    with MN' = ceil(MN/128), K' = ceil(K/128).  Bytes of padding rows and
+ *    padding K-blocks are ignored.
+ *  - Alignment: base pointers of A, B, C, D, D_col, x, w must be 16-byte
+ *    aligned and so must each row's byte length ("GEMM + Amax (SM100)":
+ *    16-byte alignment along the contiguous dimension).
+ *  - Return value: BSG_OK (0) or a bsg_status; bsg_last_error() returns a
+ *    thread-local message describing the most recent failure.
+ */
+#ifndef BSG_H
+#define BSG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bsg_status {
+    BSG_OK = 0,
+    BSG_ERR_NULLPTR = 1,     /* a required pointer is NULL */
+    BSG_ERR_SHAPE = 2,       /* negative or inconsistent sizes */
+    BSG_ERR_DTYPE = 3,       /* dtype not valid for this argument */
+    BSG_ERR_ALIGN = 4,       /* 16-byte alignment rule broken */
+    BSG_ERR_UNSUPPORTED = 5, /* valid on the pages, not built here */
+    BSG_ERR_DEVICE = 6,      /* current device is not gfx950 / HIP error */
+    BSG_ERR_LAUNCH = 7       /* kernel launch failed */
+} bsg_status;
+
+typedef enum bsg_dtype {
+    BSG_F32 = 0,
+    BSG_F16 = 1,
+    BSG_BF16 = 2,
+    BSG_E4M3 = 3,   /* float8_e4m3fn (OCP) */
+    BSG_E5M2 = 4,   /* float8_e5m2 */
+    BSG_E2M1X2 = 5, /* float4_e2m1fn_x2: two E2M1 codes per byte */
+    BSG_E8M0 = 6    /* float8_e8m0fnu */
+} bsg_dtype;
+
+/*
+ * gemm_amax -- "GEMM + Amax (SM100)", Equations:
+ *     C[m,n,l] = sum_k dequant(A)[m,k,l] * dequant(B)[n,k,l]
+ *     Amax     = max_{m,n,l} |C[m,n,l]|
+ * with dequant(X)[r,k,l] = X[r,k,l] * 2^(SF byte - 127) per 32-wide K block.
+ *
+ *  a     (M,K,L) codes, k-major; E4M3: M*K*L bytes; E2M1X2: M*(K/2)*L bytes
+ *  b     (N,K,L) codes, k-major, same dtype as a
+ *  sfa   scale atoms over (M, K, L);  sfb: scale atoms over (N, K, L)
+ *  c     (M,N,L) output, n-major, c_dtype in {F32, BF16, F16}; RNE cast
+ *        of the fp32 accumulator
+ *  amax  one float32 (nullable): max |C| of the fp32 accumulators (before
+ *        the output cast); the library zero-fills it on `stream` first
+ *  ab_dtype in {E4M3, E2M1X2}; sf_vec_size must be 32.
+ *  Sizes: M, N, L >= 0; K >= 0 with K % 32 == 0.  M or N need not be tile
+ *  multiples.  Accumulation is fp32 (the pages' only accumulator dtype).
+ */
+int gemm_amax(const void *a, const void *b, const uint8_t *sfa, const uint8_t *sfb,
+              void *c, float *amax, int64_t m, int64_t n, int64_t k, int64_t l,
+              int ab_dtype, int c_dtype, int sf_vec_size, void *stream);
+
+/*
+ * grouped_gemm -- "Grouped GEMM (SM100 BF16)", Operation.  For expert g
+ * with rows [begin_g, padded_offsets[g]) (begin_0 = 0, begin_g =
+ * padded_offsets[g-1]):
+ *     G = alpha[g] * A_g @ B_g^T                     (fp32 accumulation)
+ *     with bias:    C = G + prob[m] * bias[n,g],  D = C
+ *     without bias: C = G,                        D = prob[m] * G
+ *
+ *  a               (M,K) bf16, k-major
+ *  b               (N,K,L) bf16, k-major: memory [L][N][K]
+ *  padded_offsets  (L,) int32 cumulative padded ends, nondecreasing
+ *                  multiples of 256 in [0, M]
+ *  alpha (L,) fp32;  prob (M,) fp32
+ *  bias            (N,L) with stride (1,N): memory [L][N]; nullable;
+ *                  bias_dtype in {BF16, F16, F32}
+ *  c               (M,N) n-major, nullable (no C output); c_dtype
+ *  d               (M,N) n-major; d_dtype;  c/d dtypes in {BF16, F16, F32}
+ *  Rows at or past padded_offsets[L-1] are not written.
+ *  Sizes: M % 256 == 0, 1 <= L <= 1024, K % 8 == 0, N % 8 == 0.
+ */
+int grouped_gemm(const void *a, const void *b, const int32_t *padded_offsets,
+                 const float *alpha, const float *prob, const void *bias,
+                 void *c, void *d, int64_t m, int64_t n, int64_t k, int64_t num_experts,
+                 int bias_dtype, int c_dtype, int d_dtype, void *stream);
+
+/*
+ * grouped_gemm_srelu -- "Grouped GEMM + sReLU (SM100)", Equations and
+ * Tanh soft clamp.  For rows m of expert g:
+ *     C[m,n] = alpha[g] * sum_k dequant(A)[m,k] * dequant(B)[n,k,g]
+ *     D[m,n] = prob[m] * relu(C)^2                       (s <= 0)
+ *     D[m,n] = prob[m] * (s * min(1, tanh(relu(C)/s)))^2  (s > 0)
+ * evaluated in fp32 from the accumulator.
+ *
+ *  a, sfa          (M,K) codes, k-major, scale atoms over (M, K, 1)
+ *  b, sfb          (N,K,L) codes [L][N][K]; scale atoms over (N, K, L)
+ *  padded_offsets, alpha, prob   as for grouped_gemm
+ *  c               (M,N) pre-activation alpha*acc, nullable; c_dtype in
+ *                  {BF16, F16, F32}
+ *  d_dtype in {BF16, F16, F32}:
+ *      d      (M,N) D, RNE cast;  d_col: nullable copy of d
+ *      amax   (L,) fp32, nullable: amax[g] = max |D| over expert g's rows
+ *             (fp32 values before the cast); zero-filled by the library;
+ *             an expert with no rows reports 0
+ *  d_dtype == E4M3 (MXFP8 output, "Grouped GEMM + dSwiGLU (SM100)" Step 3
+ *  quantiser with rcp_max = 1/448):
+ *      d        (M,N) E4M3 codes quantised in 32-wide blocks along N
+ *      sfd_row  scale atoms over (M, N, 1)  (MN = M, "K" = N)
+ *      d_col    (M,N) E4M3 codes quantised in 32-tall blocks along M
+ *      sfd_col  scale atoms over (N, M, 1)  (MN = N, "K" = M)
+ *      norm_const (1,) fp32 device scalar, required
+ *  tanh_clamp_scale: s; a value <= 0 means no clamp (the pages' None).
+ *  ab_dtype in {E4M3, E2M1X2}; sf_vec_size == 32.
+ *  Sizes: M % 256 == 0, 1 <= L <= 1024, K % 32 == 0, N % 32 == 0.
+ *  Rows at or past padded_offsets[L-1] are not written.
+ */
+int grouped_gemm_srelu(const void *a, const void *b, const uint8_t *sfa, const uint8_t *sfb,
+                       const int32_t *padded_offsets, const float *alpha, const float *prob,
+                       const float *norm_const, void *c, void *d, void *d_col,
+                       uint8_t *sfd_row, uint8_t *sfd_col, float *amax,
+                       int64_t m, int64_t n, int64_t k, int64_t num_experts,
+                       int ab_dtype, int c_dtype, int d_dtype, int sf_vec_size,
+                       float tanh_clamp_scale, void *stream);
+
+/*
+ * gemm_proj_rope_mxfp8 -- "GEMM + RoPE + MXFP8 Projection (SM100)",
+ * Equations:
+ *     Y[t,h,:] = (x W) reshaped to [tokens, num_heads, head_dim]
+ *     the trailing qk_rope features of each head get the interleaved-in /
+ *     halves-out rotary embedding, pairs (2j, 2j+1) -> outputs j and
+ *     qk_rope/2 + j:
+ *        out[nope+j]      = a_j cos[t,j]        - b_j sin[t,j]
+ *        out[nope+half+j] = b_j cos[t,half+j]   + a_j sin[t,half+j]
+ *     then MXFP8 (E4M3, blocks of 32, E8M0 scales, norm_const 1) along
+ *     head_dim (row) and along tokens (column).
+ *
+ *  x    (tokens, q_lora) bf16 row-major
+ *  w    w_out_in = 1: (num_heads*head_dim, q_lora) [out, in];
+ *       w_out_in = 0: (q_lora, num_heads*head_dim) [in, out]; bf16
+ *  cos, sin  (tokens, qk_rope) bf16
+ *  out_fp8_row, out_fp8_col   (tokens, num_heads, head_dim) E4M3 codes
+ *  out_scales_row             (tokens, num_heads, head_dim/32) E8M0
+ *  out_scales_col             (tokens/32, num_heads, head_dim) E8M0
+ *  x_scale, w_scale           MXFP8-input path only (in_dtype == E4M3):
+ *                             not built here, must be NULL
+ *  in_dtype == BF16.  Sizes: tokens % 128 == 0, q_lora % 32 == 0,
+ *  head_dim == 192, qk_rope == 64.
+ */
+int gemm_proj_rope_mxfp8(const void *x, const void *w, const uint8_t *x_scale,
+                         const uint8_t *w_scale, const void *cos, const void *sin,
+                         uint8_t *out_fp8_row, uint8_t *out_scales_row,
+                         uint8_t *out_fp8_col, uint8_t *out_scales_col,
+                         int64_t tokens, int64_t q_lora, int64_t num_heads,
+                         int64_t head_dim, int64_t qk_rope, int in_dtype, int w_out_in,
+                         void *stream);
+
+/* Host-only argument checks (the pages' check_support()): the same
+ * arguments minus the stream; touch no device memory; return the status
+ * the launch call would return before enqueueing anything. */
+int bsg_validate_gemm_amax(const void *a, const void *b, const uint8_t *sfa,
+                           const uint8_t *sfb, void *c, float *amax, int64_t m, int64_t n,
+                           int64_t k, int64_t l, int ab_dtype, int c_dtype, int sf_vec_size);
+int bsg_validate_grouped_gemm(const void *a, const void *b, const int32_t *padded_offsets,
+                              const float *alpha, const float *prob, const void *bias,
+                              void *c, void *d, int64_t m, int64_t n, int64_t k,
+                              int64_t num_experts, int bias_dtype, int c_dtype, int d_dtype);
+int bsg_validate_grouped_gemm_srelu(const void *a, const void *b, const uint8_t *sfa,
+                                    const uint8_t *sfb, const int32_t *padded_offsets,
+                                    const float *alpha, const float *prob,
+                                    const float *norm_const, void *c, void *d, void *d_col,
+                                    uint8_t *sfd_row, uint8_t *sfd_col, float *amax,
+                                    int64_t m, int64_t n, int64_t k, int64_t num_experts,
+                                    int ab_dtype, int c_dtype, int d_dtype, int sf_vec_size,
+                                    float tanh_clamp_scale);
+int bsg_validate_gemm_proj_rope_mxfp8(const void *x, const void *w, const uint8_t *x_scale,
+                                      const uint8_t *w_scale, const void *cos, const void *sin,
+                                      uint8_t *out_fp8_row, uint8_t *out_scales_row,
+                                      uint8_t *out_fp8_col, uint8_t *out_scales_col,
+                                      int64_t tokens, int64_t q_lora, int64_t num_heads,
+                                      int64_t head_dim, int64_t qk_rope, int in_dtype,
+                                      int w_out_in);
+
+/* Static text for a status code. */
+const char *bsg_status_string(int status);
+/* Thread-local message for the most recent non-zero return on this thread. */
+const char *bsg_last_error(void);
+/* Library version: major*10000 + minor*100 + patch. */
+int bsg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BSG_H */

@@ -55,13 +55,14 @@ def lib():
         L.orc_enc_e4m3.restype = u32; L.orc_enc_e4m3.argtypes = [d]
         L.orc_rne_bf16.restype = u32; L.orc_rne_bf16.argtypes = [d]
         L.orc_e8m0_ceil.restype = u32; L.orc_e8m0_ceil.argtypes = [d]
+        L.orc_rne_bf16_array.restype = None; L.orc_rne_bf16_array.argtypes = [p, p, i64]
         L.orc_sf_offset.restype = i64; L.orc_sf_offset.argtypes = [i64] * 5
         L.orc_expert_of_row.restype = ctypes.c_int32
         L.orc_expert_of_row.argtypes = [p, i64, i64]
         L.orc_gemm_amax.restype = i32
-        L.orc_gemm_amax.argtypes = [p, p, p, p, i64, i64, i64, i64, i32, i64, i64, i64, p, p]
+        L.orc_gemm_amax.argtypes = [p, p, p, p, i64, i64, i64, i64, i32, i64, i64, i64, p, p, p]
         L.orc_grouped_srelu.restype = i32
-        L.orc_grouped_srelu.argtypes = [p] * 7 + [i64] * 4 + [i32, d, i64, i64, p, p, p, p]
+        L.orc_grouped_srelu.argtypes = [p] * 7 + [i64] * 4 + [i32, d, i64, i64, p, p, p, p, p]
         L.orc_grouped_bf16.restype = i32
         L.orc_grouped_bf16.argtypes = [p] * 6 + [i64] * 6 + [p, p, p, p]
         L.orc_proj_rope.restype = i32
@@ -130,41 +131,50 @@ def sf_offsets(rows: np.ndarray, kbs: np.ndarray, l: int, mn: int, kblocks: int)
 
 
 def rne_bf16_array(x: np.ndarray) -> np.ndarray:
-    f = lib().orc_rne_bf16
+    """Elementwise fp64 -> bf16 bit patterns, one round-to-nearest-even step."""
     flat = np.ascontiguousarray(x, dtype=np.float64).ravel()
-    return np.fromiter((f(float(v)) for v in flat), dtype=np.uint16,
-                       count=flat.size).reshape(np.shape(x))
+    out = np.empty(flat.size, dtype=np.uint16)
+    lib().orc_rne_bf16_array(_ptr(flat), _ptr(out), flat.size)
+    return out.reshape(np.shape(x))
 
 
 # ---------------------------------------------------------------------------
 # [GA] gemm_amax
 # ---------------------------------------------------------------------------
-def gemm_amax(a, b, sfa, sfb, m, n, k, l, fmt, batch=0, r0=0, r1=None, want_sabs=True):
+def gemm_amax(a, b, sfa, sfb, m, n, k, l, fmt, batch=0, r0=0, r1=None, want_sabs=True,
+              want_bmax=False):
     """Rows [r0, r1) of batch `batch`: C = sum_k A_hat * B_hat in fp64.
 
-    Returns (C, Sabs) where Sabs = sum_k |A_hat * B_hat| (for error bounds).
-    Amax over a full problem is `max |C|` over every batch and row.
+    Returns (C, Sabs) where Sabs = sum_k |A_hat * B_hat| (for error bounds),
+    plus Bmax = sum over 32-wide K blocks of max |A_hat * B_hat| when
+    want_bmax.  Amax over a full problem is `max |C|` over every batch and row.
     """
     L = lib()
     r1 = m if r1 is None else r1
     a, b, sfa, sfb = (_np(x, np.uint8) for x in (a, b, sfa, sfb))
     c = np.empty((r1 - r0, n), dtype=np.float64)
     s = np.empty_like(c) if want_sabs else None
+    bm = np.empty_like(c) if want_bmax else None
     rc = L.orc_gemm_amax(_ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), m, n, k, l, _FMT[fmt],
-                         batch, r0, r1, _ptr(c), _ptr(s))
+                         batch, r0, r1, _ptr(c), _ptr(s), _ptr(bm))
     if rc:
         raise ValueError(f"orc_gemm_amax failed ({rc})")
-    return c, s
+    return (c, s, bm) if want_bmax else (c, s)
 
 
-def gemm_amax_full(a, b, sfa, sfb, m, n, k, l, fmt):
-    """Whole problem: C (L, M, N) fp64, Sabs, and Amax = max |C| ([GA] Equations)."""
-    cs, ss = [], []
+def gemm_amax_full(a, b, sfa, sfb, m, n, k, l, fmt, want_bmax=False):
+    """Whole problem: C (L, M, N) fp64, Sabs, and Amax = max |C| ([GA] Equations)
+    (plus Bmax, see gemm_amax, when want_bmax)."""
+    cs, ss, bs = [], [], []
     for bi in range(l):
-        c, s = gemm_amax(a, b, sfa, sfb, m, n, k, l, fmt, batch=bi)
-        cs.append(c); ss.append(s)
+        r = gemm_amax(a, b, sfa, sfb, m, n, k, l, fmt, batch=bi, want_bmax=want_bmax)
+        cs.append(r[0]); ss.append(r[1])
+        if want_bmax:
+            bs.append(r[2])
     c = np.stack(cs); s = np.stack(ss)
     amax = float(np.abs(c).max()) if c.size else 0.0
+    if want_bmax:
+        return c, s, amax, np.stack(bs)
     return c, s, amax
 
 
@@ -172,7 +182,8 @@ def gemm_amax_full(a, b, sfa, sfb, m, n, k, l, fmt):
 # [GS] grouped_gemm_srelu
 # ---------------------------------------------------------------------------
 def grouped_srelu(a, b, sfa, sfb, offsets, alpha, prob, m, n, k, L_, fmt, s, r0=0, r1=None):
-    """Rows [r0, r1): returns dict(c, d, sabs, group) in fp64.
+    """Rows [r0, r1): returns dict(c, d, sabs, group, bmax) in fp64 (bmax and
+    sabs include |alpha_g|).
 
     Rows at or past padded_offsets[L-1] carry group -1 and NaN outputs.
     s <= 0 means no tanh clamp.
@@ -183,13 +194,14 @@ def grouped_srelu(a, b, sfa, sfb, offsets, alpha, prob, m, n, k, L_, fmt, s, r0=
     off = _np(offsets, np.int32); al = _np(alpha, np.float32); pr = _np(prob, np.float32)
     rows = r1 - r0
     c = np.empty((rows, n)); d = np.empty((rows, n)); sab = np.empty((rows, n))
+    bm = np.empty((rows, n))
     grp = np.empty(rows, dtype=np.int32)
     rc = L.orc_grouped_srelu(_ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), _ptr(off), _ptr(al),
                              _ptr(pr), m, n, k, L_, _FMT[fmt], float(s), r0, r1,
-                             _ptr(c), _ptr(d), _ptr(sab), _ptr(grp))
+                             _ptr(c), _ptr(d), _ptr(sab), _ptr(grp), _ptr(bm))
     if rc:
         raise ValueError(f"orc_grouped_srelu failed ({rc})")
-    return dict(c=c, d=d, sabs=sab, group=grp)
+    return dict(c=c, d=d, sabs=sab, group=grp, bmax=bm)
 
 
 def expert_amax(d: np.ndarray, group: np.ndarray, L_: int) -> np.ndarray:

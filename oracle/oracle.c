@@ -135,6 +135,12 @@ uint32_t orc_rne_bf16(double x)
     return w >> 16;
 }
 
+void orc_rne_bf16_array(const double *x, uint16_t *out, int64_t n)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = (uint16_t)orc_rne_bf16(x[i]);
+}
+
 /* E8M0 byte of the smallest power of two >= sigma, clamped to [0, 254];
  * sigma <= 0 gives 0.  (Rounding of a computed scale: see the quantiser.) */
 uint32_t orc_e8m0_ceil(double sigma)
@@ -208,6 +214,22 @@ static void dot(const double *a, const double *b, int64_t k, double *acc, double
     *sabs = t;
 }
 
+/* Error-bound statistic (not part of the result): sum over 32-wide K blocks
+ * of the block's largest |a[k]*b[k]|. */
+static double block_max_sum(const double *a, const double *b, int64_t k)
+{
+    double t = 0.0;
+    for (int64_t k0 = 0; k0 < k; k0 += 32) {
+        double mx = 0.0;
+        for (int64_t kk = k0; kk < k0 + 32 && kk < k; ++kk) {
+            double p = fabs(a[kk] * b[kk]);
+            if (p > mx) mx = p;
+        }
+        t += mx;
+    }
+    return t;
+}
+
 /* Dequantise all N rows of B for batch/expert l: out is (N, K). */
 static void dequant_matrix(const uint8_t *codes, const uint8_t *sf, int fmt,
                            int64_t l, int64_t rows, int64_t k, double *out)
@@ -223,7 +245,7 @@ static void dequant_matrix(const uint8_t *codes, const uint8_t *sf, int fmt,
 /* Rows [r0, r1) of batch `batch`.  c and sabs (nullable) are (r1-r0, n). */
 int orc_gemm_amax(const uint8_t *a, const uint8_t *b, const uint8_t *sfa, const uint8_t *sfb,
                   int64_t m, int64_t n, int64_t k, int64_t l, int fmt,
-                  int64_t batch, int64_t r0, int64_t r1, double *c, double *sabs)
+                  int64_t batch, int64_t r0, int64_t r1, double *c, double *sabs, double *bmax)
 {
     double *bh, *ah;
     if (batch < 0 || batch >= l || r0 < 0 || r1 > m || r0 > r1) return 1;
@@ -242,6 +264,7 @@ int orc_gemm_amax(const uint8_t *a, const uint8_t *b, const uint8_t *sfa, const 
             dot(ah + (i - r0) * k, bh + j * k, k, &acc, &t);
             c[(i - r0) * n + j] = acc;
             if (sabs) sabs[(i - r0) * n + j] = t;
+            if (bmax) bmax[(i - r0) * n + j] = block_max_sum(ah + (i - r0) * k, bh + j * k, k);
         }
     free(bh);
     free(ah);
@@ -275,7 +298,8 @@ int orc_grouped_srelu(const uint8_t *a, const uint8_t *b, const uint8_t *sfa, co
                       const int32_t *offsets, const float *alpha, const float *prob,
                       int64_t m, int64_t n, int64_t k, int64_t L, int fmt, double s,
                       int64_t r0, int64_t r1,
-                      double *c_out, double *d_out, double *sabs_out, int32_t *group_out)
+                      double *c_out, double *d_out, double *sabs_out, int32_t *group_out,
+                      double *bmax_out)
 {
     double *bh = NULL, *ah;
     int64_t rows = r1 - r0, have = -1;
@@ -295,6 +319,7 @@ int orc_grouped_srelu(const uint8_t *a, const uint8_t *b, const uint8_t *sfa, co
                 c_out[(i - r0) * n + j] = NAN;
                 d_out[(i - r0) * n + j] = NAN;
                 if (sabs_out) sabs_out[(i - r0) * n + j] = NAN;
+                if (bmax_out) bmax_out[(i - r0) * n + j] = NAN;
             }
             continue;
         }
@@ -313,6 +338,9 @@ int orc_grouped_srelu(const uint8_t *a, const uint8_t *b, const uint8_t *sfa, co
             c_out[(i - r0) * n + j] = cval;
             d_out[(i - r0) * n + j] = (double)prob[i] * x * x;
             if (sabs_out) sabs_out[(i - r0) * n + j] = fabs((double)alpha[g]) * t;
+            if (bmax_out)
+                bmax_out[(i - r0) * n + j] =
+                    fabs((double)alpha[g]) * block_max_sum(ah + (i - r0) * k, bh + j * k, k);
         }
     }
     free(ah);

@@ -1,0 +1,112 @@
+"""CPU tests of the C ABI boundary: the library loads, exports every entry
+point that include/bsg.h declares, and its host-only validation rejects the
+inputs the pages' constraint lists forbid, before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_gemm_02_amd as bsg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULLPTR, SHAPE, DTYPE, ALIGN, UNSUP = 0, 1, 2, 3, 4, 5
+P = 0x10000   # a 16-byte aligned fake device address (validation never dereferences)
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "bsg.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) -
+                  {"if", "sizeof", "defined"})
+
+
+def test_library_exports_every_declared_symbol():
+    L = bsg.lib()
+    declared = header_functions()
+    assert set(bsg.symbols()) == set(declared), declared
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.bsg_version() >= 100
+    assert L.bsg_status_string(4) == b"16-byte alignment violated"
+
+
+def va(**kw):
+    base = dict(a=P, b=P, sfa=P, sfb=P, c=P, amax=P, m=256, n=256, k=256, l=1,
+                ab_dtype="e4m3", c_dtype=bsg.F32, sf_vec_size=32)
+    base.update(kw)
+    return bsg.gemm_amax(**base, validate_only=True)
+
+
+def test_gemm_amax_validation():
+    assert va() == OK
+    assert va(ab_dtype=bsg.E5M2) == UNSUP              # E5M2 not built
+    assert va(sf_vec_size=16) == UNSUP                   # NVFP4-style sf 16 not built
+    assert va(sf_vec_size=8) == SHAPE
+    assert va(k=48) == SHAPE                             # K % 32
+    assert va(c_dtype=bsg.E4M3) == UNSUP                 # FP8 C disabled on the page too
+    assert va(a=0) == NULLPTR
+    assert va(a=P + 8) == ALIGN                          # 16-byte alignment
+    assert va(n=250) == ALIGN                            # fp32 C row of 1000 bytes
+    assert va(m=-1) == SHAPE
+    assert va(m=0, a=0, b=0, c=0) == OK                  # empty problem: only amax is written
+    msg = bsg.lib().bsg_last_error().decode()
+    assert isinstance(msg, str)
+
+
+def vs(**kw):
+    base = dict(a=P, b=P, sfa=P, sfb=P, padded_offsets=P, alpha=P, prob=P, norm_const=None,
+                c=P, d=P, d_col=None, sfd_row=None, sfd_col=None, amax=P, m=512, n=256, k=256,
+                num_experts=4, ab_dtype="e4m3", c_dtype=bsg.BF16, d_dtype=bsg.BF16,
+                sf_vec_size=32, tanh_clamp_scale=32.0)
+    base.update(kw)
+    return bsg.grouped_gemm_srelu(**base, validate_only=True)
+
+
+def test_grouped_srelu_validation():
+    assert vs() == OK
+    assert vs(prob=None) == NULLPTR                      # prob is required
+    assert vs(m=300) == SHAPE                            # M % 256 (m_aligned)
+    assert vs(num_experts=1025) == SHAPE                 # L <= 1024
+    assert vs(num_experts=0) == SHAPE
+    assert vs(d_dtype=bsg.E4M3) == NULLPTR               # FP8 D needs norm_const / SFD / D_col
+    assert vs(d_dtype=bsg.E4M3, norm_const=P, d_col=P, sfd_row=P, sfd_col=P) == OK
+    assert vs(d_dtype=bsg.E4M3, norm_const=P, d_col=P, sfd_row=P, sfd_col=P, ab_dtype="e2m1") == DTYPE
+    assert vs(n=80) == SHAPE                             # N % 32
+    assert vs(tanh_clamp_scale=float("nan")) == SHAPE
+    assert vs(tanh_clamp_scale=0.0) == OK                # None
+    assert vs(d=P + 4) == ALIGN
+
+
+def vg(**kw):
+    base = dict(a=P, b=P, padded_offsets=P, alpha=P, prob=P, bias=P, c=P, d=P, m=512, n=256,
+                k=256, num_experts=8, bias_dtype=bsg.BF16, c_dtype=bsg.BF16, d_dtype=bsg.BF16)
+    base.update(kw)
+    return bsg.grouped_gemm(**base, validate_only=True)
+
+
+def test_grouped_bf16_validation():
+    assert vg() == OK
+    assert vg(bias=None) == OK and vg(c=None) == OK
+    assert vg(m=255) == SHAPE
+    assert vg(k=12) == ALIGN
+    assert vg(padded_offsets=None) == NULLPTR
+    assert vg(d_dtype=bsg.E4M3) == DTYPE
+
+
+def vp(**kw):
+    base = dict(x=P, w=P, x_scale=None, w_scale=None, cos=P, sin=P, out_fp8_row=P,
+                out_scales_row=P, out_fp8_col=P, out_scales_col=P, tokens=256, q_lora=1536,
+                num_heads=128, head_dim=192, qk_rope=64, in_dtype=bsg.BF16, w_out_in=1)
+    base.update(kw)
+    return bsg.gemm_proj_rope_mxfp8(**base, validate_only=True)
+
+
+def test_proj_rope_validation():
+    assert vp() == OK
+    assert vp(tokens=200) == SHAPE                       # tokens % TILE_M (128)
+    assert vp(in_dtype=bsg.E4M3) == UNSUP                # MXFP8-input path not built
+    assert vp(x_scale=P) == SHAPE                        # scales only on the MXFP8 path
+    assert vp(head_dim=128) == UNSUP
+    assert vp(q_lora=100) == SHAPE
+    assert vp(w_out_in=0) == OK

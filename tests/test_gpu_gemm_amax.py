@@ -1,0 +1,143 @@
+"""GPU parity of gemm_amax ("GEMM + Amax (SM100)") against the CPU oracle.
+
+All calls go through the C ABI (libbsg.so) via the thin Python binding.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_gemm_02_amd as bsg
+import oracle as O
+import workloads as W
+from parity import check_amax, check_float, ceil_div, sf_slice, sum_bound
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def run_gemm(p, c_dtype=torch.float32):
+    s = p.sizes
+    t = {k: v.cuda() for k, v in p.t.items()}
+    c = torch.empty(s["l"], s["m"], s["n"], dtype=c_dtype, device="cuda")
+    amax = torch.full((1,), -7.0, device="cuda")
+    bsg.gemm_amax(t["a"], t["b"], t["sfa"], t["sfb"], c, amax, s["m"], s["n"], s["k"], s["l"],
+                  s["fmt"])
+    torch.cuda.synchronize()
+    return c, amax, t
+
+
+@pytest.mark.parametrize("case", [
+    dict(m=256, n=256, k=256, l=1, fmt="e4m3", c=torch.float32, plain=True),   # small workload
+    dict(m=300, n=200, k=96, l=2, fmt="e4m3", c=torch.float32, plain=False),   # ragged M/N/K
+    dict(m=520, n=264, k=640, l=1, fmt="e4m3", c=torch.bfloat16, plain=False),
+    dict(m=260, n=136, k=352, l=2, fmt="e2m1", c=torch.float32, plain=False),
+    dict(m=512, n=512, k=1024, l=1, fmt="e2m1", c=torch.bfloat16, plain=False),
+    dict(m=33, n=40, k=32, l=3, fmt="e4m3", c=torch.float16, plain=False),
+])
+def test_gemm_amax_matches_oracle(case):
+    say(f"gemm_amax parity {case}")
+    p = W.gemm_amax_problem(case["m"], case["n"], case["k"], case["l"], case["fmt"], seed=1,
+                            plain_round=case["plain"], sf_spread=3 if case["plain"] else 1)
+    c, amax, _ = run_gemm(p, case["c"])
+    s = p.sizes
+    oc, os_, oamax, obm = O.gemm_amax_full(p.t["a"], p.t["b"], p.t["sfa"], p.t["sfb"], s["m"],
+                                           s["n"], s["k"], s["l"], s["fmt"], want_bmax=True)
+    bound = sum_bound(os_, s["k"], bmax=obm)
+    r = check_float(c.cpu(), oc, bound, what=str(case))
+    say(f"  escapes {r}")
+    check_amax(float(amax.item()), oamax, float(bound.ravel()[np.argmax(np.abs(oc))]))
+    if case["c"] == torch.float32:
+        assert amax.item() == c.abs().max().item()      # amax of the fp32 values, bit-exact
+
+
+def test_gemm_amax_small_workload_argmax_location():
+    say("gemm_amax 256^3 argmax")
+    p = W.dense_256()
+    c, amax, _ = run_gemm(p)
+    oc, os_, oamax, obm = O.gemm_amax_full(p.t["a"], p.t["b"], p.t["sfa"], p.t["sfb"], 256, 256, 256, 1,
+                                           "e4m3", want_bmax=True)
+    g = c.cpu().double().numpy()
+    flat_o = np.abs(oc).ravel()
+    top2 = np.sort(flat_o)[-2:]
+    bound = sum_bound(os_, 256, bmax=obm).ravel()[np.argsort(flat_o)[-2:]].sum()
+    if top2[1] - top2[0] > bound:
+        say("  arg-max location is decided: checking it")
+        assert np.argmax(np.abs(g).ravel()) == np.argmax(flat_o)
+    assert amax.item() == np.abs(g).max()
+
+
+def test_gemm_amax_pow2_rescale_and_determinism():
+    say("gemm_amax pow2 rescale")
+    p = W.gemm_amax_problem(384, 320, 512, 2, "e4m3", seed=3)
+    c0, a0, t = run_gemm(p)
+    c1, a1, _ = run_gemm(p)
+    assert torch.equal(c0, c1) and torch.equal(a0, a1)
+    for ja, jb in [(2, 0), (-3, 1)]:
+        p2 = W.gemm_amax_problem(384, 320, 512, 2, "e4m3", seed=3)
+        p2.t["sfa"] = (p2.t["sfa"].int() + ja).to(torch.uint8)
+        p2.t["sfb"] = (p2.t["sfb"].int() + jb).to(torch.uint8)
+        c2, a2, _ = run_gemm(p2)
+        assert torch.equal(c2, c0 * 2.0 ** (ja + jb))
+        assert a2.item() == a0.item() * 2.0 ** (ja + jb)
+
+
+def test_gemm_amax_unit_scales_exact():
+    # unit scales and small integer-valued codes make every fp32 partial sum exact
+    say("gemm_amax unit scales exact")
+    g = torch.Generator().manual_seed(4)
+    ints = torch.tensor([-3.0, -2, -1, 0, 1, 2, 3]).to(torch.float8_e4m3fn).view(torch.uint8)
+    a = ints[torch.randint(0, 7, (1, 256, 512), generator=g)]
+    b = ints[torch.randint(0, 7, (1, 256, 512), generator=g)]
+    sf = torch.full((W.sf_atom_bytes(256, 512, 1),), 127, dtype=torch.uint8)
+    p = W.Problem("gemm_amax", dict(m=256, n=256, k=512, l=1, fmt="e4m3"), dict(a=a, b=b, sfa=sf, sfb=sf))
+    c, amax, _ = run_gemm(p)
+    ref = a[0].view(torch.float8_e4m3fn).double() @ b[0].view(torch.float8_e4m3fn).double().T
+    assert torch.equal(c[0].cpu().double(), ref)
+
+
+def test_gemm_amax_empty_and_k_zero():
+    say("gemm_amax empty")
+    amax = torch.full((1,), 5.0, device="cuda")
+    bsg.gemm_amax(None, None, None, None, None, amax, 0, 64, 64, 1, "e4m3", c_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert amax.item() == 0.0
+    c = torch.full((1, 64, 64), 3.0, device="cuda")
+    sf = torch.zeros(W.sf_atom_bytes(64, 32, 1), dtype=torch.uint8, device="cuda")
+    a = torch.zeros(64, 32, dtype=torch.uint8, device="cuda")
+    bsg.gemm_amax(a, a, sf, sf, c, amax, 64, 64, 0, 1, "e4m3")
+    torch.cuda.synchronize()
+    assert torch.all(c == 0) and amax.item() == 0.0
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_gemm_amax_full_size_sampled(fmt):
+    """M=N=K=8192, L=4 at the benchmarked launch: sampled 128-row panels vs the oracle."""
+    say(f"gemm_amax 8192^3 x4 {fmt}")
+    p = W.dense_8192(fmt, device="cuda")
+    s = p.sizes
+    c = torch.empty(s["l"], s["m"], s["n"], dtype=torch.bfloat16, device="cuda")
+    amax = torch.zeros(1, device="cuda")
+    bsg.gemm_amax(p.t["a"], p.t["b"], p.t["sfa"], p.t["sfb"], c, amax, s["m"], s["n"], s["k"],
+                  s["l"], fmt)
+    torch.cuda.synchronize()
+    m_t, k_t = ceil_div(s["m"], 128), ceil_div(s["k"], 128)
+    rng = np.random.default_rng(0)
+    for batch in (0, 3):
+        mt = int(rng.integers(m_t))
+        say(f"  oracle batch {batch} rows {mt * 128}..{mt * 128 + 127}")
+        a_sub = p.t["a"][batch, mt * 128:(mt + 1) * 128].cpu()
+        b_sub = p.t["b"][batch].cpu()
+        sfa_sub = sf_slice(p.t["sfa"], batch, m_t, k_t, mt, mt + 1).cpu()
+        sfb_sub = sf_slice(p.t["sfb"], batch, m_t, k_t, 0, m_t).cpu()
+        oc, os_, obm = O.gemm_amax(a_sub, b_sub, sfa_sub, sfb_sub, 128, s["n"], s["k"], 1, fmt,
+                                   want_bmax=True)
+        r = check_float(c[batch, mt * 128:(mt + 1) * 128].cpu(), oc, sum_bound(os_, s["k"], bmax=obm),
+                        what=f"{fmt} b{batch}")
+        say(f"  {r}")
+        assert amax.item() >= (np.abs(oc) - sum_bound(os_, s["k"], bmax=obm)).max() * (1 - 1e-5)
+    # amax is the max of the fp32 values whose bf16 roundings are in C
+    cmax = c.float().abs().max().item()
+    assert abs(amax.item() - cmax) <= cmax * 2.0 ** -8

@@ -1,0 +1,221 @@
+"""GPU parity of grouped_gemm ("Grouped GEMM (SM100 BF16)") and
+grouped_gemm_srelu ("Grouped GEMM + sReLU (SM100)") against the CPU oracle,
+through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_gemm_02_amd as bsg
+import oracle as O
+import workloads as W
+from parity import check_amax, check_float, ceil_div, sf_slice, sum_bound
+
+pytestmark = pytest.mark.gpu
+SENT = -1536.0    # exactly representable in bf16, fp16 and fp32
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def d_bound(o_c, bc, prob, s):
+    """Escape bound for D = prob * f(C) given C's bound bc: |f'| <= 2|C| + bc,
+    plus the clamp's tanh error (absolute 1e-6 on t, i.e. 2 s^2 1e-6 on f)."""
+    b = prob[:, None] * (2 * np.abs(o_c) + bc) * bc
+    if s > 0:
+        b = b + prob[:, None] * 2 * s * s * 1e-6
+    return b
+
+
+def run_srelu(p, c_dtype=torch.bfloat16, d_dtype=torch.bfloat16, with_c=True, with_dcol=True):
+    s = p.sizes
+    t = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in p.t.items()}
+    m, n = s["m"], s["n"]
+    c = torch.full((m, n), SENT, dtype=c_dtype, device="cuda") if with_c else None
+    d = torch.full((m, n), SENT, dtype=d_dtype, device="cuda")
+    d_col = torch.full((m, n), SENT, dtype=d_dtype, device="cuda") if with_dcol else None
+    amax = torch.full((s["l"],), -1.0, device="cuda")
+    bsg.grouped_gemm_srelu(t["a"], t["b"], t["sfa"], t["sfb"], t["offsets"], t["alpha"], t["prob"],
+                           None, c, d, d_col, None, None, amax, m, n, s["k"], s["l"], s["fmt"],
+                           c_dtype=c_dtype, d_dtype=d_dtype, tanh_clamp_scale=s["tanh_clamp"])
+    torch.cuda.synchronize()
+    return c, d, d_col, amax
+
+
+SRELU_CASES = [
+    dict(sizes=[256, 0, 512, 256], n=320, k=192, fmt="e4m3", s=32.0, c=torch.bfloat16, d=torch.bfloat16),
+    dict(sizes=[512, 256, 0, 0, 256], n=256, k=256, fmt="e4m3", s=0.0, c=torch.float32, d=torch.float32),
+    dict(sizes=[256, 768], n=96, k=512, fmt="e4m3", s=0.5, c=torch.float16, d=torch.float16),
+    dict(sizes=[0, 256, 256], n=288, k=256, fmt="e2m1", s=32.0, c=torch.bfloat16, d=torch.bfloat16),
+    dict(sizes=[256], n=512, k=1024, fmt="e2m1", s=0.0, c=torch.float32, d=torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("case", SRELU_CASES)
+def test_grouped_srelu_matches_oracle(case):
+    say(f"grouped_srelu parity {case}")
+    off = np.cumsum(case["sizes"]).astype(np.int32)
+    L = len(case["sizes"])
+    p = W.grouped_srelu_problem(0, L, case["n"], case["k"], case["fmt"], seed=2, offsets=off,
+                                tanh_clamp=case["s"], extra_rows=256)
+    s = p.sizes
+    c, d, d_col, amax = run_srelu(p, case["c"], case["d"])
+    r = O.grouped_srelu(p.t["a"], p.t["b"], p.t["sfa"], p.t["sfb"], off, p.t["alpha"], p.t["prob"],
+                        s["m"], s["n"], s["k"], L, s["fmt"], s["tanh_clamp"])
+    valid = s["valid_m"]
+    prob = p.t["prob"].double().numpy()
+    bc = sum_bound(r["sabs"], s["k"], bmax=r["bmax"])
+    rc = check_float(c[:valid].cpu(), r["c"][:valid], bc[:valid], what="C")
+    bd = d_bound(r["c"], bc, prob, s["tanh_clamp"])
+    rd = check_float(d[:valid].cpu(), r["d"][:valid], bd[:valid], what="D")
+    say(f"  C {rc}  D {rd}")
+    assert torch.equal(d_col, d)
+    # rows past padded_offsets[-1] untouched
+    assert torch.all(c[valid:].float() == SENT) and torch.all(d[valid:].float() == SENT)
+    oam = O.expert_amax(r["d"], r["group"], L)
+    for g in range(L):
+        rows = np.where(r["group"] == g)[0]
+        bnd = float(bd[rows].max()) if rows.size else 0.0
+        check_amax(float(amax[g].item()), oam[g], bnd, what=f"amax[{g}]")
+    # structural bound D <= s^2 prob
+    if s["tanh_clamp"] > 0:
+        dd = d[:valid].float().cpu().double().numpy()
+        lim = s["tanh_clamp"] ** 2 * prob[:valid, None]
+        assert np.all(dd <= lim * (1 + 2 ** -7))
+
+
+def test_grouped_srelu_routing_bit_exact():
+    """Unit scales, one-hot A, expert g's B codes = integer g%8+1: C = alpha_g (g%8+1)."""
+    say("grouped_srelu routing")
+    sizes = [256, 0, 512, 256, 0, 768, 256]
+    off = np.cumsum(sizes).astype(np.int32)
+    L, n, k = len(sizes), 256, 128
+    m = int(off[-1])
+    A = torch.zeros(m, k, dtype=torch.uint8); A[:, 5] = 0x38
+    ints = torch.tensor([1.0, 2, 3, 4, 5, 6, 7, 8]).to(torch.float8_e4m3fn).view(torch.uint8)
+    B = torch.stack([torch.full((n, k), int(ints[g % 8]), dtype=torch.uint8) for g in range(L)])
+    sfa = torch.full((W.sf_atom_bytes(m, k, 1),), 127, dtype=torch.uint8)
+    sfb = torch.full((W.sf_atom_bytes(n, k, L),), 127, dtype=torch.uint8)
+    alpha = torch.linspace(0.5, 1.5, L)
+    prob = torch.ones(m)
+    p = W.Problem("grouped_gemm_srelu", dict(m=m, n=n, k=k, l=L, fmt="e4m3", tanh_clamp=0.0, valid_m=m),
+                  dict(a=A, b=B, sfa=sfa, sfb=sfb, offsets=torch.from_numpy(off), alpha=alpha, prob=prob))
+    c, d, _, amax = run_srelu(p, torch.float32, torch.float32)
+    g = np.array([O.expert_of_row(off, L, r) for r in range(m)])
+    want = (alpha.numpy()[g].astype(np.float32) * (g % 8 + 1).astype(np.float32))
+    assert np.array_equal(c.cpu().numpy(), np.broadcast_to(want[:, None], (m, n)))
+
+
+def test_grouped_srelu_full_size_sampled():
+    """32 experts, N=4096, K=7168, valid_m ~ 32768, s = 32: sampled row panels."""
+    say("grouped_srelu full size")
+    p = W.moe_mxfp8_srelu(device="cuda")
+    s = p.sizes
+    m, n, k, L = s["m"], s["n"], s["k"], s["l"]
+    c = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    d = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    amax = torch.empty(L, device="cuda")
+    t = p.t
+    bsg.grouped_gemm_srelu(t["a"], t["b"], t["sfa"], t["sfb"], t["offsets"], t["alpha"], t["prob"],
+                           None, c, d, None, None, None, amax, m, n, k, L, "e4m3",
+                           c_dtype=torch.bfloat16, d_dtype=torch.bfloat16, tanh_clamp_scale=32.0)
+    torch.cuda.synchronize()
+    off = t["offsets"].cpu().numpy()
+    m_t, n_t, k_t = ceil_div(m, 128), ceil_div(n, 128), ceil_div(k, 128)
+    begins = np.concatenate([[0], off[:-1]])
+    nonempty = [g for g in range(L) if off[g] > begins[g]]
+    for g in (nonempty[0], nonempty[len(nonempty) // 2], nonempty[-1]):
+        r0 = int(off[g]) - 128                     # last 128-row group of expert g
+        assert O.expert_of_row(off, L, r0) == g
+        say(f"  oracle expert {g} rows {r0}..{r0 + 127}")
+        sub = O.grouped_srelu(t["a"][r0:r0 + 128].cpu(), t["b"][g:g + 1].cpu(),
+                              sf_slice(t["sfa"], 0, m_t, k_t, r0 // 128, r0 // 128 + 1).cpu(),
+                              sf_slice(t["sfb"], g, n_t, k_t, 0, n_t).cpu(),
+                              np.array([128], np.int32), t["alpha"][g:g + 1].cpu(),
+                              t["prob"][r0:r0 + 128].cpu(), 128, n, k, 1, "e4m3", 32.0)
+        prob = t["prob"][r0:r0 + 128].double().cpu().numpy()
+        bc = sum_bound(sub["sabs"], k, bmax=sub["bmax"])
+        rc = check_float(c[r0:r0 + 128].cpu(), sub["c"], bc, what=f"C e{g}")
+        rd = check_float(d[r0:r0 + 128].cpu(), sub["d"], d_bound(sub["c"], bc, prob, 32.0),
+                         what=f"D e{g}")
+        say(f"  C {rc} D {rd}")
+        bd = d_bound(sub["c"], bc, prob, 32.0)
+        assert amax[g].item() >= (np.abs(sub["d"]) - bd).max() * (1 - 1e-5)
+    # amax[g] is the max of D over expert g: compare with the GPU's own D
+    for g in range(L):
+        rows = slice(int(begins[g]), int(off[g]))
+        if off[g] == begins[g]:
+            assert amax[g].item() == 0.0
+        else:
+            dm = d[rows].float().abs().max().item()
+            assert abs(amax[g].item() - dm) <= dm * 2 ** -8
+
+
+# ---------------------------------------------------------------------------
+# BF16 grouped GEMM
+# ---------------------------------------------------------------------------
+BF16_CASES = [
+    dict(sizes=[256, 0, 512, 256], n=264, k=200, bias=torch.bfloat16, c=torch.bfloat16, d=torch.bfloat16),
+    dict(sizes=[256, 256], n=128, k=64, bias=None, c=torch.float32, d=torch.bfloat16),
+    dict(sizes=[0, 512], n=512, k=1024, bias=torch.float32, c=None, d=torch.float32),
+    dict(sizes=[768], n=96, k=136, bias=torch.float16, c=torch.float16, d=torch.float16),
+]
+
+
+@pytest.mark.parametrize("case", BF16_CASES)
+def test_grouped_bf16_matches_oracle(case):
+    say(f"grouped_gemm parity {case}")
+    off = np.cumsum(case["sizes"]).astype(np.int32)
+    L = len(case["sizes"])
+    p = W.grouped_bf16_problem(0, L, case["n"], case["k"], seed=3, offsets=off, extra_rows=256,
+                               with_bias=case["bias"] is not None)
+    s = p.sizes
+    m, n, k = s["m"], s["n"], s["k"]
+    t = {kk: (v.cuda() if isinstance(v, torch.Tensor) else v) for kk, v in p.t.items()}
+    bias = t["bias"].to(case["bias"]) if case["bias"] is not None else None
+    c = torch.full((m, n), SENT, dtype=case["c"], device="cuda") if case["c"] is not None else None
+    d = torch.full((m, n), SENT, dtype=case["d"], device="cuda")
+    bsg.grouped_gemm(t["a"], t["b"], t["offsets"], t["alpha"], t["prob"], bias, c, d, m, n, k, L,
+                     bias_dtype=case["bias"] or torch.bfloat16, c_dtype=case["c"] or torch.bfloat16,
+                     d_dtype=case["d"])
+    torch.cuda.synchronize()
+    bias_v = None if bias is None else bias.double().cpu().numpy()
+    r = O.grouped_bf16(O.bits16(p.t["a"]), O.bits16(p.t["b"]), off, p.t["alpha"], p.t["prob"],
+                       bias_v, m, n, k, L)
+    valid = s["valid_m"]
+    bnd = sum_bound(r["sabs"], k) + 1e-7 * np.abs(r["c"])
+    if c is not None:
+        say(f"  C {check_float(c[:valid].cpu(), r['c'][:valid], bnd[:valid], what='C')}")
+        assert torch.all(c[valid:].float() == SENT)
+    prob = p.t["prob"].double().numpy()[:, None]
+    dbnd = bnd * (1 if bias is not None else prob)
+    say(f"  D {check_float(d[:valid].cpu(), r['d'][:valid], dbnd[:valid], what='D')}")
+    assert torch.all(d[valid:].float() == SENT)
+
+
+def test_grouped_bf16_full_size_sampled():
+    """16384 tokens x top-8 over 64 experts, N=2048, K=7168: sampled row panels."""
+    say("grouped_gemm full size")
+    p = W.moe_bf16(device="cuda")
+    s = p.sizes
+    m, n, k, L = s["m"], s["n"], s["k"], s["l"]
+    t = p.t
+    c = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    d = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    bsg.grouped_gemm(t["a"], t["b"], t["offsets"], t["alpha"], t["prob"], t["bias"], c, d, m, n, k, L,
+                     bias_dtype=torch.bfloat16, c_dtype=torch.bfloat16, d_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    off = t["offsets"].cpu().numpy()
+    begins = np.concatenate([[0], off[:-1]])
+    nonempty = [g for g in range(L) if off[g] > begins[g]]
+    for g in (nonempty[0], nonempty[len(nonempty) // 2], nonempty[-1]):
+        r0 = int(off[g]) - 64
+        assert O.expert_of_row(off, L, r0) == g
+        say(f"  oracle expert {g} rows {r0}..{r0 + 63}")
+        sub = O.grouped_bf16(O.bits16(t["a"][r0:r0 + 64]), O.bits16(t["b"][g:g + 1]),
+                             np.array([64], np.int32), t["alpha"][g:g + 1].cpu(),
+                             t["prob"][r0:r0 + 64].cpu(), t["bias"][g:g + 1].double().cpu().numpy(),
+                             64, n, k, 1)
+        bnd = sum_bound(sub["sabs"], k) + 1e-7 * np.abs(sub["c"])
+        say(f"  C {check_float(c[r0:r0 + 64].cpu(), sub['c'], bnd, what=f'C e{g}')}")
+        say(f"  D {check_float(d[r0:r0 + 64].cpu(), sub['d'], bnd, what=f'D e{g}')}")

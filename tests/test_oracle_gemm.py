@@ -212,3 +212,13 @@ def test_grouped_single_expert_reduces_to_dense():
     assert np.array_equal(r["c"], dense)
     assert np.array_equal(r["d"], np.maximum(dense, 0) ** 2)
     assert np.array_equal(r["sabs"], sab)
+
+
+def test_block_max_statistic_matches_numpy():
+    # Bmax (error-bound statistic) = sum over 32-wide K blocks of max |A_hat B_hat|
+    p = unit_scale_problem(64, 40, 96, 1, seed=8)
+    a = torch_dec_e4m3(p.t["a"])[0]; b = torch_dec_e4m3(p.t["b"])[0]
+    c, s, bm = O.gemm_amax(p.t["a"], p.t["b"], p.t["sfa"], p.t["sfb"], 64, 40, 96, 1, "e4m3",
+                           want_bmax=True)
+    prod = np.abs(a[:, None, :] * b[None, :, :]).reshape(64, 40, 3, 32)
+    assert np.array_equal(bm, prod.max(-1).sum(-1))
