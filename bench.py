@@ -1,0 +1,261 @@
+"""Throughput of the block-scaled GEMM family on one MI355X.
+
+Default workload (the headline metric): grouped MXFP8 GEMM + prob-gated
+squared ReLU with tanh soft clamp s = 32, 32 experts, N = 4096, K = 7168,
+Zipf(1.1)-routed expert rows padded to 256 (valid_m ~ 32768), bf16 C and D
+plus per-expert amax.  One step = one grouped_gemm_srelu call on inputs
+already resident in HBM.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--report PATH]
+
+Prints one JSON line: throughput in TFLOP/s (algorithmic flops, padded rows
+included), a roofline object for the dominant kernel timed with HIP events
+on the launch stream, and the CPU oracle timed on a bounded sample of the
+same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
+PEAK = {"e4m3": 5000.0, "e2m1": 10100.0, "bf16": 2500.0}
+HBM_GBS = 8000.0
+
+
+def ceil_div(a, b):
+    return -(-a // b)
+
+
+# ---------------------------------------------------------------------------
+# Workloads: each returns (step_fn, info) with inputs resident on the GPU.
+# ---------------------------------------------------------------------------
+def wl_moe_mxfp8_srelu(fp8_out=False):
+    import torch
+    import block_scaled_gemm_02_amd as bsg
+    import workloads as W
+    p = W.moe_mxfp8_srelu(device="cuda")
+    s, t = p.sizes, p.t
+    m, n, k, L = s["m"], s["n"], s["k"], s["l"]
+    c = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    if fp8_out:
+        d = torch.empty(m, n, dtype=torch.uint8, device="cuda")
+        d_col = torch.empty(m, n, dtype=torch.uint8, device="cuda")
+        sfd_row = torch.empty(W.sf_atom_bytes(m, n, 1), dtype=torch.uint8, device="cuda")
+        sfd_col = torch.empty(W.sf_atom_bytes(n, m, 1), dtype=torch.uint8, device="cuda")
+        amax = None
+        dd = "e4m3"
+    else:
+        d = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+        d_col = sfd_row = sfd_col = None
+        amax = torch.empty(L, device="cuda")
+        dd = torch.bfloat16
+
+    def step():
+        bsg.grouped_gemm_srelu(t["a"], t["b"], t["sfa"], t["sfb"], t["offsets"], t["alpha"],
+                               t["prob"], t["norm_const"], c, d, d_col, sfd_row, sfd_col, amax,
+                               m, n, k, L, "e4m3", c_dtype=torch.bfloat16, d_dtype=dd,
+                               tanh_clamp_scale=32.0)
+
+    valid_m = s["valid_m"]
+    flops = 2.0 * valid_m * n * k
+    sf_bytes = t["sfa"].numel() + t["sfb"].numel()
+    out_bytes = valid_m * n * (2 + (2 if not fp8_out else 2) + 0)
+    alg_bytes = valid_m * k + L * n * k + sf_bytes + out_bytes
+    name = "moe_mxfp8_srelu" + ("_fp8d" if fp8_out else "")
+    info = dict(
+        name=name, fmt="e4m3", flops=flops, alg_bytes=alg_bytes, kernel="k_grouped",
+        config={"workload": "grouped MXFP8 (E4M3, E8M0 per 32 K) GEMM + prob-gated sReLU, "
+                            "tanh clamp s=32",
+                "experts": L, "n": n, "k": k, "valid_m": valid_m, "routed_rows": 28672,
+                "routing": "multinomial Zipf(1.1), padded to 256",
+                "outputs": "C bf16, D " + ("E4M3 + SFD_row/SFD_col" if fp8_out else "bf16 + amax(L)")},
+        cpu=lambda: cpu_sample_srelu(p))
+    return step, info
+
+
+def cpu_sample_srelu(p, rows=1024):
+    """Oracle on `rows` rows of the most popular expert (bounded CPU sample)."""
+    import numpy as np
+    import oracle as O
+    s, t = p.sizes, p.t
+
+    def sf_slice(sf, l, mn_t, k_t, mt0, mt1):
+        # atom row-groups [mt0, mt1) of batch l in the (L, MN', K', 32, 4, 4) buffer
+        start = ((l * mn_t + mt0) * k_t) * 512
+        return sf[start:start + (mt1 - mt0) * k_t * 512]
+
+    m, n, k = s["m"], s["n"], s["k"]
+    off = t["offsets"].cpu().numpy()
+    g = 0
+    r0 = 0
+    rows = min(rows, int(off[0]))
+    m_t, n_t, k_t = ceil_div(m, 128), ceil_div(n, 128), ceil_div(k, 128)
+    a = t["a"][r0:r0 + rows].cpu()
+    b = t["b"][g:g + 1].cpu()
+    sfa = sf_slice(t["sfa"], 0, m_t, k_t, 0, ceil_div(rows, 128)).cpu()
+    sfb = sf_slice(t["sfb"], g, n_t, k_t, 0, n_t).cpu()
+    alpha = t["alpha"][g:g + 1].cpu()
+    prob = t["prob"][:rows].cpu()
+    t0 = time.perf_counter()
+    O.grouped_srelu(a, b, sfa, sfb, np.array([rows], np.int32), alpha, prob, rows, n, k, 1,
+                    "e4m3", 32.0)
+    dt = time.perf_counter() - t0
+    return dict(value=2.0 * rows * n * k / dt / 1e12, unit="TFLOP/s", cores=O.threads(),
+                kind="oracle", seconds=dt,
+                sample=f"{rows} rows of expert 0 (x N={n}, K={k}), fp64 oracle incl. B dequantisation")
+
+
+def wl_dense_8192(fmt):
+    import torch
+    import block_scaled_gemm_02_amd as bsg
+    import workloads as W
+    p = W.dense_8192(fmt, device="cuda")
+    s, t = p.sizes, p.t
+    c = torch.empty(s["l"], s["m"], s["n"], dtype=torch.bfloat16, device="cuda")
+    amax = torch.empty(1, device="cuda")
+
+    def step():
+        bsg.gemm_amax(t["a"], t["b"], t["sfa"], t["sfb"], c, amax, s["m"], s["n"], s["k"], s["l"], fmt)
+
+    flops = 2.0 * s["l"] * s["m"] * s["n"] * s["k"]
+    ab = t["a"].numel() + t["b"].numel() + t["sfa"].numel() + t["sfb"].numel()
+    info = dict(name=f"dense_8192_{fmt}", fmt=fmt, flops=flops, alg_bytes=ab + c.numel() * 2,
+                kernel="k_gemm_amax",
+                config={"workload": f"batched dense MX{'FP8' if fmt == 'e4m3' else 'FP4'} GEMM + amax",
+                        "m": 8192, "n": 8192, "k": 8192, "l": 4, "c": "bf16"},
+                cpu=None)
+    return step, info
+
+
+def wl_dense_256():
+    import torch
+    import block_scaled_gemm_02_amd as bsg
+    import workloads as W
+    p = W.dense_256()
+    t = {k: v.cuda() for k, v in p.t.items()}
+    c = torch.empty(1, 256, 256, device="cuda")
+    amax = torch.empty(1, device="cuda")
+
+    def step():
+        bsg.gemm_amax(t["a"], t["b"], t["sfa"], t["sfb"], c, amax, 256, 256, 256, 1, "e4m3")
+
+    info = dict(name="dense_256", fmt="e4m3", flops=2.0 * 256 ** 3, alg_bytes=2 * 65536 + 4096 + 262144,
+                kernel="k_gemm_amax", config={"workload": "dense MXFP8 GEMM + amax, 256^3, C fp32"},
+                cpu=None)
+    return step, info
+
+
+def wl_moe_bf16():
+    import torch
+    import block_scaled_gemm_02_amd as bsg
+    import workloads as W
+    p = W.moe_bf16(device="cuda")
+    s, t = p.sizes, p.t
+    m, n, k, L = s["m"], s["n"], s["k"], s["l"]
+    c = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    d = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        bsg.grouped_gemm(t["a"], t["b"], t["offsets"], t["alpha"], t["prob"], t["bias"], c, d,
+                         m, n, k, L, bias_dtype=torch.bfloat16, c_dtype=torch.bfloat16,
+                         d_dtype=torch.bfloat16)
+
+    vm = s["valid_m"]
+    info = dict(name="moe_bf16", fmt="bf16", flops=2.0 * vm * n * k,
+                alg_bytes=2 * (vm * k + L * n * k + 2 * vm * n), kernel="k_grouped",
+                config={"workload": "BF16 MoE grouped GEMM, bias/prob epilogue", "experts": L,
+                        "n": n, "k": k, "valid_m": vm}, cpu=None)
+    return step, info
+
+
+WORKLOADS = {
+    "moe_mxfp8_srelu": lambda: wl_moe_mxfp8_srelu(False),
+    "moe_mxfp8_srelu_fp8d": lambda: wl_moe_mxfp8_srelu(True),
+    "dense_8192_e4m3": lambda: wl_dense_8192("e4m3"),
+    "dense_8192_e2m1": lambda: wl_dense_8192("e2m1"),
+    "dense_256": wl_dense_256,
+    "moe_bf16": wl_moe_bf16,
+}
+
+
+def measure(step, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps
+    return wall / steps * 1e3, per_launch_ms
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="moe_mxfp8_srelu", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--report", default=None, help="also append the JSON line to this file")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    step, info = WORKLOADS[args.workload]()
+    ms_step, ms_launch = measure(step, args.steps, args.warmup)
+    tflops = info["flops"] / (ms_step * 1e-3) / 1e12
+    achieved = info["flops"] / (ms_launch * 1e-3) / 1e12
+    peak = PEAK[info["fmt"]]
+    out = {
+        "metric": "TFLOP/s and % of MXFP8 MFMA peak, grouped MoE block-scaled GEMM + sReLU"
+        if info["name"].startswith("moe_mxfp8") else f"TFLOP/s, {info['name']}",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"e4m3": "mxfp8-e4m3 (fp32 accumulate)", "e2m1": "mxfp4-e2m1 (fp32 accumulate)",
+                  "bf16": "bf16 (fp32 accumulate)"}[info["fmt"]],
+        "data": "synthetic",
+        "config": info["config"],
+        "pct_of_peak": round(100.0 * tflops / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": info["kernel"], "launch_ms": round(ms_launch, 5),
+                     "alg_gbs": round(info["alg_bytes"] / (ms_launch * 1e-3) / 1e9, 1)},
+    }
+    if info.get("cpu") and not args.no_cpu:
+        out["cpu_baseline"] = info["cpu"]()
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.report:
+        with open(args.report, "a") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

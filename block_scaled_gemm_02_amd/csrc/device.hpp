@@ -29,7 +29,21 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace bsg {
+
+// Compile-time loop: f(std::integral_constant<int, 0>) ... f(<N-1>).  Used
+// wherever an accumulator block is selected, so that no index into the
+// accumulator array is ever a run-time value (which would move it to scratch).
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (N > 0) {
+        static_for<N - 1>(f);
+        f(std::integral_constant<int, N - 1>{});
+    }
+}
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -43,7 +57,7 @@ constexpr int kTileN = 256;
 constexpr int kRowBytes = 128;                  // bytes of one K step per row
 constexpr int kThreads = 256;
 constexpr int kStageBytes = kTileM * kRowBytes; // one operand, one stage
-constexpr uint32_t kOOB = 0x7FFFFFF0u;          // offset that reads zeros
+constexpr uint32_t kOOB = 0x80000000u;          // added to an offset: reads zeros
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
@@ -162,12 +176,13 @@ __device__ __forceinline__ void g2r(i32x4 (&r)[8], const OperandDesc &d, __amdgp
 {
     const uint32_t c = t & 7;
     const uint32_t kb = (uint32_t)ks * kRowBytes + 16u * c;
-    const bool kvalid = kb < d.row_bytes;
+    // chunks past the end of a row read zeros: push them past num_records
+    // (rows * row_bytes < 2^31 is checked on the host, so this cannot wrap)
+    const uint32_t koff = kb + (kb < d.row_bytes ? 0u : kOOB);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         uint32_t row = (uint32_t)(t >> 3) + 32u * i;
-        uint32_t off = kvalid ? row * d.row_bytes + kb : kOOB;
-        r[i] = buf_load16(rs, off);
+        r[i] = buf_load16(rs, row * d.row_bytes + koff);
     }
 }
 

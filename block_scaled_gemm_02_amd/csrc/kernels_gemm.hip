@@ -82,21 +82,21 @@ __global__ void __launch_bounds__(256) k_gemm_amax(GemmAmaxParams p)
 
     float lmax = 0.0f;
     const int64_t cbase = batch * p.m * p.n;
+    static_for<16>([&](auto ij) {
+        constexpr int i = decltype(ij)::value / 4, j = decltype(ij)::value % 4;
+        const f32x16 a = acc[i][j];
+        const int64_t col = n0 + acc_col(wn, j, lane);
+        if (col < p.n) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int64_t row = m0 + acc_row(wm, i, v, lane);
-            if (row >= p.m) continue;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t col = n0 + acc_col(wn, j, lane);
-                if (col >= p.n) continue;
-                const float x = acc[i][j][v];
-                store_elem(p.c, cbase + row * p.n + col, x, p.c_dtype);
-                lmax = fmaxf(lmax, fabsf(x));
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = m0 + acc_row(wm, i, v, lane);
+                if (row < p.m) {
+                    store_elem(p.c, cbase + row * p.n + col, a[v], p.c_dtype);
+                    lmax = fmaxf(lmax, fabsf(a[v]));
+                }
             }
         }
+    });
     if (p.amax) block_amax_atomic(lmax, p.amax, red);
 }
 
@@ -173,22 +173,26 @@ __global__ void __launch_bounds__(256) k_grouped(GroupedParams p)
 
     const float alpha = p.alpha[g];
     float lmax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
+    static_for<16>([&](auto ij) {
+        constexpr int i = decltype(ij)::value / 4, j = decltype(ij)::value % 4;
+        const f32x16 a = acc[i][j];
+        const int64_t col = n0 + acc_col(wn, j, lane);
+        if (col >= p.n) return;
+        float bv = 0.0f;
+        if constexpr (EPI == EPI_BF16_BIAS) {
+            if (p.bias) bv = load_elem(p.bias, (int64_t)g * p.n + col, p.bias_dtype);
+        }
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int64_t row = m0 + acc_row(wm, i, v, lane);
             const float pr = p.prob[row];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t col = n0 + acc_col(wn, j, lane);
-                if (col >= p.n) continue;
+            {
                 const int64_t idx = row * p.n + col;
-                const float gval = alpha * acc[i][j][v];
+                const float gval = alpha * a[v];
                 if constexpr (EPI == EPI_BF16_BIAS) {
                     float cval, dval;
                     if (p.bias) {
-                        cval = gval + pr * load_elem(p.bias, (int64_t)g * p.n + col, p.bias_dtype);
+                        cval = gval + pr * bv;
                         dval = cval;
                     } else {
                         cval = gval;
@@ -207,6 +211,7 @@ __global__ void __launch_bounds__(256) k_grouped(GroupedParams p)
                 }
             }
         }
+    });
     if constexpr (EPI == EPI_SRELU) {
         if (p.amax) block_amax_atomic(lmax, p.amax + g, red);
     }
