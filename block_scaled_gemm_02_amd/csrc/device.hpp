@@ -170,8 +170,10 @@ struct FmtTraits<FMT_BF16> {
     static constexpr int kCode = -1;
 };
 
-// Global -> registers: thread t fetches chunk (t % 8) of rows t/8 + 32i.
-__device__ __forceinline__ void g2r(i32x4 (&r)[8], const OperandDesc &d, __amdgpu_buffer_rsrc_t rs,
+// Global -> registers: thread t fetches chunk (t % 8) of rows t/8 + 32i,
+// for a panel of 32*R rows.
+template <int R>
+__device__ __forceinline__ void g2r(i32x4 (&r)[R], const OperandDesc &d, __amdgpu_buffer_rsrc_t rs,
                                     int ks, int t)
 {
     const uint32_t c = t & 7;
@@ -180,18 +182,19 @@ __device__ __forceinline__ void g2r(i32x4 (&r)[8], const OperandDesc &d, __amdgp
     // (rows * row_bytes < 2^31 is checked on the host, so this cannot wrap)
     const uint32_t koff = kb + (kb < d.row_bytes ? 0u : kOOB);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < R; ++i) {
         uint32_t row = (uint32_t)(t >> 3) + 32u * i;
         r[i] = buf_load16(rs, row * d.row_bytes + koff);
     }
 }
 
-__device__ __forceinline__ void r2lds(uint8_t *lds, const i32x4 (&r)[8], int t)
+template <int R>
+__device__ __forceinline__ void r2lds(uint8_t *lds, const i32x4 (&r)[R], int t)
 {
     const uint32_t c = t & 7, rr = t >> 3;
     const uint32_t pc = c ^ (rr & 7);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < R; ++i) {
         uint32_t row = rr + 32u * i;
         *reinterpret_cast<i32x4 *>(lds + row * kRowBytes + 16u * pc) = r[i];
     }
@@ -222,70 +225,80 @@ __device__ __forceinline__ i32x4 load_scale_words(const OperandDesc &d, int wq, 
     return w;
 }
 
-template <int F, int S>
-__device__ __forceinline__ void mma_substep(f32x16 (&acc)[4][4], const uint8_t *la, const uint8_t *lb,
+template <int F, int S, int NB>
+__device__ __forceinline__ void mma_substep(f32x16 (&acc)[4][NB], const uint8_t *la, const uint8_t *lb,
                                             uint32_t arow, uint32_t brow, int g,
                                             const i32x4 (&sa)[2], const i32x4 (&sb)[2])
 {
     if constexpr (F == FMT_E4M3) {
-        i32x8 af[4], bf[4];
+        i32x8 af[4], bf[NB];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             i32x4 lo = lds_chunk(la, arow + 32u * i, 4 * S + g);
             i32x4 hi = lds_chunk(la, arow + 32u * i, 4 * S + 2 + g);
             af[i] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            i32x4 blo = lds_chunk(lb, brow + 32u * i, 4 * S + g);
-            i32x4 bhi = lds_chunk(lb, brow + 32u * i, 4 * S + 2 + g);
-            bf[i] = i32x8{blo.x, blo.y, blo.z, blo.w, bhi.x, bhi.y, bhi.z, bhi.w};
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            i32x4 blo = lds_chunk(lb, brow + 32u * j, 4 * S + g);
+            i32x4 bhi = lds_chunk(lb, brow + 32u * j, 4 * S + 2 + g);
+            bf[j] = i32x8{blo.x, blo.y, blo.z, blo.w, bhi.x, bhi.y, bhi.z, bhi.w};
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < NB; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                     af[i], bf[j], acc[i][j], 0, 0, 2 * S, sa[0][i], 2 * S, sb[0][j]);
     } else if constexpr (F == FMT_E2M1) {
-        i32x8 af[4], bf[4];
+        i32x8 af[4], bf[NB];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             i32x4 a = lds_chunk(la, arow + 32u * i, 2 * S + g);
-            i32x4 b = lds_chunk(lb, brow + 32u * i, 2 * S + g);
             af[i] = i32x8{a.x, a.y, a.z, a.w, 0, 0, 0, 0};
-            bf[i] = i32x8{b.x, b.y, b.z, b.w, 0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            i32x4 b = lds_chunk(lb, brow + 32u * j, 2 * S + g);
+            bf[j] = i32x8{b.x, b.y, b.z, b.w, 0, 0, 0, 0};
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < NB; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                     af[i], bf[j], acc[i][j], 4, 4, 2 * (S & 1), sa[S >> 1][i], 2 * (S & 1),
                     sb[S >> 1][j]);
     } else {
-        bf16x8 af[4], bf[4];
+        bf16x8 af[4], bf[NB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i)
             af[i] = __builtin_bit_cast(bf16x8, lds_chunk(la, arow + 32u * i, 2 * S + g));
-            bf[i] = __builtin_bit_cast(bf16x8, lds_chunk(lb, brow + 32u * i, 2 * S + g));
-        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            bf[j] = __builtin_bit_cast(bf16x8, lds_chunk(lb, brow + 32u * j, 2 * S + g));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < NB; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
 }
 
-// Full K loop for one 256x256 tile.  `lds` holds 2 stages x (A, B) x 32 KB.
+// Full K loop for one 256 x (64*NB) tile: 4 waves as 2 x 2, each wave owning
+// 128 x (32*NB).  `lds` holds 2 stages x (A, B) x 32 KB.  NB = 4 for the
+// block-scaled formats (a wave's columns must be one 128-row scale atom).
 // On return every wave has passed a final barrier, so `lds` may be reused.
-template <int F>
-__device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], uint8_t *lds, const OperandDesc &A,
+template <int F, int NB = 4>
+__device__ __forceinline__ void mainloop(f32x16 (&acc)[4][NB], uint8_t *lds, const OperandDesc &A,
                                          const OperandDesc &B, int64_t k)
 {
+    static_assert(NB == 4 || F == FMT_BF16, "scaled formats need 128-column wave tiles");
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1, g = lane >> 5;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NB; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
@@ -294,10 +307,10 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], uint8_t *lds, cons
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(A.base, A.bytes);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(B.base, B.bytes);
     const uint32_t arow = 128u * wm + (lane & 31);
-    const uint32_t brow = 128u * wn + (lane & 31);
+    const uint32_t brow = 32u * NB * wn + (lane & 31);
     constexpr int NA = FmtTraits<F>::kAtoms;
 
-    i32x4 pa[8], pb[8];
+    i32x4 pa[8], pb[2 * NB];
     i32x4 sa[2] = {}, sb[2] = {}, na[2] = {}, nb[2] = {};
     if (nks > 0) {
         g2r(pa, A, ra, 0, t);
@@ -329,11 +342,11 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[4][4], uint8_t *lds, cons
                 }
             }
         }
-        mma_substep<F, 0>(acc, cur, cur + kStageBytes, arow, brow, g, sa, sb);
-        mma_substep<F, 1>(acc, cur, cur + kStageBytes, arow, brow, g, sa, sb);
+        mma_substep<F, 0, NB>(acc, cur, cur + kStageBytes, arow, brow, g, sa, sb);
+        mma_substep<F, 1, NB>(acc, cur, cur + kStageBytes, arow, brow, g, sa, sb);
         if constexpr (FmtTraits<F>::kSub == 4) {
-            mma_substep<F, 2>(acc, cur, cur + kStageBytes, arow, brow, g, sa, sb);
-            mma_substep<F, 3>(acc, cur, cur + kStageBytes, arow, brow, g, sa, sb);
+            mma_substep<F, 2, NB>(acc, cur, cur + kStageBytes, arow, brow, g, sa, sb);
+            mma_substep<F, 3, NB>(acc, cur, cur + kStageBytes, arow, brow, g, sa, sb);
         }
         if (more) {
             r2lds(nxt, pa, t);
@@ -354,6 +367,38 @@ __device__ __forceinline__ int acc_row(int wm, int i, int v, int lane)
     return 128 * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
 }
 __device__ __forceinline__ int acc_col(int wn, int j, int lane) { return 128 * wn + 32 * j + (lane & 31); }
+
+// Max over the 32 lanes of each half-wave (lanes 0-31 and 32-63 separately):
+// quad and row DPP steps reduce 16 lanes, a swizzle folds the two rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max_c(float x)
+{
+    const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false);
+    return fmaxf(x, __int_as_float(y));
+}
+__device__ __forceinline__ float half_wave_max(float x)
+{
+    x = dpp_max_c<0xB1>(x);    // quad_perm [1,0,3,2]
+    x = dpp_max_c<0x4E>(x);    // quad_perm [2,3,0,1]
+    x = dpp_max_c<0x141>(x);   // row_half_mirror
+    x = dpp_max_c<0x140>(x);   // row_mirror
+    const int y = __builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F);   // lane ^ 16
+    return fmaxf(x, __int_as_float(y));
+}
+
+// E4M3 code of one value (round to nearest even, saturating to +-448).
+__device__ __forceinline__ uint32_t e4m3_code(float x) { return pack2_e4m3(x, 0.0f) & 0xFFu; }
+
+// The MX output quantiser's scale step for a block with max |D| = amax:
+// SF = smallest power of two >= norm_const * amax / 448 (E8M0 byte), and
+// the factor norm_const / SF that maps the block into E4M3 range.
+__device__ __forceinline__ uint32_t mx_scale_byte(float amax, float norm_const, float &inv)
+{
+    const float sigma = (norm_const * amax) * (1.0f / 448.0f);
+    const uint32_t byte = e8m0_ceil(sigma);
+    inv = fminf(ldexpf(norm_const, 127 - (int)byte), 3.402823466e38f);
+    return byte;
+}
 
 __device__ __forceinline__ float wave_max(float x)
 {

@@ -123,14 +123,15 @@ hipError_t launch_gemm_amax(const GemmAmaxArgs &a, hipStream_t s)
 // ---------------------------------------------------------------------------
 // Grouped GEMM over padded_offsets expert ranges
 // ---------------------------------------------------------------------------
-enum : int { EPI_BF16_BIAS = 0, EPI_SRELU = 1 };
+enum : int { EPI_BF16_BIAS = 0, EPI_SRELU = 1, EPI_SRELU_FP8 = 2 };
 
 struct GroupedParams {
     const uint8_t *a, *b, *sfa, *sfb;
     const int32_t *offsets;
-    const float *alpha, *prob;
+    const float *alpha, *prob, *norm_const;
     const void *bias;
     void *c, *d, *d_col;
+    uint8_t *sfd_row, *sfd_col;
     float *amax;
     int64_t m, n, k, num_experts;
     int64_t m_t, n_t, k_t;
@@ -150,6 +151,89 @@ __device__ __forceinline__ int expert_of(const int32_t *offsets, int num, int64_
         else lo = mid + 1;
     }
     return lo;
+}
+
+// sReLU value of one accumulator: alpha*acc -> relu -> optional tanh clamp
+// -> prob * x^2 (fp32, "Grouped GEMM + sReLU (SM100)" Equations).
+__device__ __forceinline__ float srelu_value(float gval, float pr, float s, float inv_s)
+{
+    float x = fmaxf(gval, 0.0f);
+    if (s > 0.0f) x = s * fminf(1.0f, tanh_pos(x * inv_s));
+    return pr * x * x;
+}
+
+// MXFP8 output: D quantised in 32-wide blocks along N (codes to d, scales to
+// the SFD_row atoms over (M, N)) and in 32-tall blocks along M (codes to
+// d_col, scales to the SFD_col atoms over (N, M)), with the quantiser of
+// "Grouped GEMM + dSwiGLU (SM100)", Step 3 (rcp_max = 1/448).
+//
+// In the 32x32 accumulator layout a row's 32 columns sit in the 32 lanes of
+// one half-wave (reduced with DPP), and a column's 32 rows sit in lane c
+// (16 rows) and lane c+32 (the other 16).
+__device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, const f32x16 (&acc)[4][4],
+                                                   int64_t m0, int64_t n0, int g, float alpha,
+                                                   int wm, int wn, int lane)
+{
+    const float nc = *p.norm_const;
+    const int64_t n = p.n;
+    const int64_t row_kt = (n / 32 + 3) / 4;          // SFD_row: K' over N
+    const int64_t col_kt = (p.m / 32 + 3) / 4;        // SFD_col: K' over M
+    uint8_t *dq = static_cast<uint8_t *>(p.d);
+    uint8_t *dc = static_cast<uint8_t *>(p.d_col);
+    const int c32 = lane & 31, gh = lane >> 5;
+    static_for<16>([&](auto ij) {
+        constexpr int i = decltype(ij)::value / 4, j = decltype(ij)::value % 4;
+        const int64_t col = n0 + acc_col(wn, j, lane);
+        const bool col_ok = col < n;
+        f32x16 dv;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t row = m0 + acc_row(wm, i, v, lane);
+            const float gval = alpha * acc[i][j][v];
+            if (p.c && col_ok) store_elem(p.c, row * n + col, gval, p.c_dtype);
+            dv[v] = srelu_value(gval, p.prob[row], p.tanh_s, p.tanh_inv_s);
+        }
+        // ---- column direction: rows 32i..32i+31 of this quadrant, column col
+        float cm = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) cm = fmaxf(cm, fabsf(dv[v]));
+        cm = fmaxf(cm, __shfl_xor(cm, 32));
+        float cinv;
+        const uint32_t cbyte = mx_scale_byte(cm, nc, cinv);
+        if (col_ok) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = m0 + acc_row(wm, i, v, lane);
+                dc[row * n + col] = (uint8_t)e4m3_code(dv[v] * cinv);
+            }
+            if (gh == 0) {
+                const int64_t mt = (m0 + 128 * wm) / 128;       // 4 row blocks = one atom K group
+                const int64_t off = (((col / 128) * col_kt + mt) * 32 + (col % 32)) * 16 +
+                                    ((col % 128) / 32) * 4 + i;
+                p.sfd_col[off] = (uint8_t)cbyte;
+            }
+        }
+        // ---- row direction: row r of the block, columns 32j..32j+31
+        uint32_t my_byte = 0;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const float rm = half_wave_max(fabsf(dv[v]));
+            float rinv;
+            const uint32_t rbyte = mx_scale_byte(rm, nc, rinv);
+            if (c32 == v) my_byte = rbyte;
+            if (col_ok) {
+                const int64_t row = m0 + acc_row(wm, i, v, lane);
+                dq[row * n + col] = (uint8_t)e4m3_code(dv[v] * rinv);
+            }
+        }
+        if (c32 < 16 && n0 + 128 * wn + 32 * j < n) {
+            const int64_t row = m0 + acc_row(wm, i, c32, lane);
+            const int64_t nb = (n0 + 128 * wn) / 32 + j;
+            const int64_t off = (((row / 128) * row_kt + nb / 4) * 32 + (row % 32)) * 16 +
+                                ((row % 128) / 32) * 4 + (nb % 4);
+            p.sfd_row[off] = (uint8_t)my_byte;
+        }
+    });
 }
 
 template <int F, int EPI>
@@ -172,48 +256,44 @@ __global__ void __launch_bounds__(256) k_grouped(GroupedParams p)
     mainloop<F>(acc, lds, A, B, p.k);
 
     const float alpha = p.alpha[g];
-    float lmax = 0.0f;
-    static_for<16>([&](auto ij) {
-        constexpr int i = decltype(ij)::value / 4, j = decltype(ij)::value % 4;
-        const f32x16 a = acc[i][j];
-        const int64_t col = n0 + acc_col(wn, j, lane);
-        if (col >= p.n) return;
-        float bv = 0.0f;
-        if constexpr (EPI == EPI_BF16_BIAS) {
-            if (p.bias) bv = load_elem(p.bias, (int64_t)g * p.n + col, p.bias_dtype);
-        }
+    if constexpr (EPI == EPI_SRELU_FP8) {
+        epilogue_srelu_fp8(p, acc, m0, n0, g, alpha, wm, wn, lane);
+    } else {
+        float lmax = 0.0f;
+        static_for<16>([&](auto ij) {
+            constexpr int i = decltype(ij)::value / 4, j = decltype(ij)::value % 4;
+            const f32x16 a = acc[i][j];
+            const int64_t col = n0 + acc_col(wn, j, lane);
+            if (col >= p.n) return;
+            float bv = 0.0f;
+            if constexpr (EPI == EPI_BF16_BIAS) {
+                if (p.bias) bv = load_elem(p.bias, (int64_t)g * p.n + col, p.bias_dtype);
+            }
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int64_t row = m0 + acc_row(wm, i, v, lane);
-            const float pr = p.prob[row];
-            {
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = m0 + acc_row(wm, i, v, lane);
+                const float pr = p.prob[row];
                 const int64_t idx = row * p.n + col;
                 const float gval = alpha * a[v];
                 if constexpr (EPI == EPI_BF16_BIAS) {
-                    float cval, dval;
-                    if (p.bias) {
-                        cval = gval + pr * bv;
-                        dval = cval;
-                    } else {
-                        cval = gval;
-                        dval = pr * gval;
-                    }
+                    // "Grouped GEMM (SM100 BF16)", Operation: with bias C = G + prob*bias,
+                    // D = C; without bias C = G, D = prob*G.
+                    const float cval = p.bias ? gval + pr * bv : gval;
+                    const float dval = p.bias ? cval : pr * gval;
                     if (p.c) store_elem(p.c, idx, cval, p.c_dtype);
                     store_elem(p.d, idx, dval, p.d_dtype);
                 } else {
-                    float x = fmaxf(gval, 0.0f);
-                    if (p.tanh_s > 0.0f) x = p.tanh_s * fminf(1.0f, tanh_pos(x * p.tanh_inv_s));
-                    const float dval = pr * x * x;
+                    const float dval = srelu_value(gval, pr, p.tanh_s, p.tanh_inv_s);
                     if (p.c) store_elem(p.c, idx, gval, p.c_dtype);
                     store_elem(p.d, idx, dval, p.d_dtype);
                     if (p.d_col) store_elem(p.d_col, idx, dval, p.d_dtype);
                     lmax = fmaxf(lmax, fabsf(dval));
                 }
             }
+        });
+        if constexpr (EPI == EPI_SRELU) {
+            if (p.amax) block_amax_atomic(lmax, p.amax + g, red);
         }
-    });
-    if constexpr (EPI == EPI_SRELU) {
-        if (p.amax) block_amax_atomic(lmax, p.amax + g, red);
     }
 }
 
@@ -221,8 +301,9 @@ static GroupedParams grouped_params(const GroupedArgs &a)
 {
     GroupedParams p;
     p.a = a.a; p.b = a.b; p.sfa = a.sfa; p.sfb = a.sfb; p.offsets = a.offsets;
-    p.alpha = a.alpha; p.prob = a.prob; p.bias = a.bias;
+    p.alpha = a.alpha; p.prob = a.prob; p.norm_const = a.norm_const; p.bias = a.bias;
     p.c = a.c; p.d = a.d; p.d_col = a.d_col; p.amax = a.amax;
+    p.sfd_row = a.sfd_row; p.sfd_col = a.sfd_col;
     p.m = a.m; p.n = a.n; p.k = a.k; p.num_experts = a.num_experts;
     p.m_t = (a.m + 127) / 128; p.n_t = (a.n + 127) / 128; p.k_t = (a.k + 127) / 128;
     p.row_bytes = row_bytes_of(a.fmt, a.k);
@@ -246,16 +327,16 @@ hipError_t launch_grouped_srelu(const GroupedArgs &a, hipStream_t s)
     hipError_t e = zero_floats(a.amax, a.num_experts, s);
     if (e != hipSuccess) return e;
     if (a.m == 0 || a.n == 0) return hipSuccess;
-    if (a.d_dtype == DT_E4M3) return hipErrorNotSupported;
     GroupedParams p = grouped_params(a);
     dim3 grid((unsigned)((a.n + kTileN - 1) / kTileN), (unsigned)(a.m / kTileM));
-    if (a.fmt == FMT_E4M3)
+    if (a.d_dtype == DT_E4M3) {
+        if (a.fmt != FMT_E4M3) return hipErrorNotSupported;
+        hipLaunchKernelGGL((k_grouped<FMT_E4M3, EPI_SRELU_FP8>), grid, dim3(kThreads), 0, s, p);
+    } else if (a.fmt == FMT_E4M3)
         hipLaunchKernelGGL((k_grouped<FMT_E4M3, EPI_SRELU>), grid, dim3(kThreads), 0, s, p);
     else
         hipLaunchKernelGGL((k_grouped<FMT_E2M1, EPI_SRELU>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
-
-hipError_t launch_proj_rope(const ProjRopeArgs &, hipStream_t) { return hipErrorNotSupported; }
 
 }  // namespace bsg

@@ -57,6 +57,7 @@ def lib():
         L.orc_e8m0_ceil.restype = u32; L.orc_e8m0_ceil.argtypes = [d]
         L.orc_rne_bf16_array.restype = None; L.orc_rne_bf16_array.argtypes = [p, p, i64]
         L.orc_sf_offset.restype = i64; L.orc_sf_offset.argtypes = [i64] * 5
+        L.orc_sf_offset_grid.restype = None; L.orc_sf_offset_grid.argtypes = [i64] * 6 + [p]
         L.orc_expert_of_row.restype = ctypes.c_int32
         L.orc_expert_of_row.argtypes = [p, i64, i64]
         L.orc_gemm_amax.restype = i32
@@ -120,13 +121,10 @@ def sf_offset(r: int, kb: int, l: int, mn: int, kblocks: int) -> int:
     return lib().orc_sf_offset(r, kb, l, mn, kblocks)
 
 
-def sf_offsets(rows: np.ndarray, kbs: np.ndarray, l: int, mn: int, kblocks: int) -> np.ndarray:
-    """Vector form of sf_offset, evaluated one element at a time in C."""
-    f = lib().orc_sf_offset
-    out = np.empty(np.broadcast(rows, kbs).shape, dtype=np.int64)
-    for idx, (r, kb) in enumerate(zip(*[np.broadcast_to(v, out.shape).ravel()
-                                         for v in (rows, kbs)])):
-        out.ravel()[idx] = f(int(r), int(kb), l, mn, kblocks)
+def sf_offset_grid(r0: int, r1: int, nkb: int, l: int, mn: int, kblocks: int) -> np.ndarray:
+    """Offsets of rows [r0, r1) x k-blocks [0, nkb) of batch l: (r1-r0, nkb) int64."""
+    out = np.empty((r1 - r0, nkb), dtype=np.int64)
+    lib().orc_sf_offset_grid(r0, r1, nkb, l, mn, kblocks, _ptr(out))
     return out
 
 

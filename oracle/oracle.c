@@ -174,6 +174,15 @@ int64_t orc_sf_offset(int64_t r, int64_t kb, int64_t l, int64_t mn, int64_t kblo
     return ((((l * mt_n + mt) * kt_n + kt) * 32 + r32) * 4 + r4) * 4 + k4;
 }
 
+/* Offsets of rows [r0, r1) x k-blocks [0, nkb) of batch l, row-major. */
+void orc_sf_offset_grid(int64_t r0, int64_t r1, int64_t nkb, int64_t l, int64_t mn,
+                        int64_t kblocks, int64_t *out)
+{
+    for (int64_t r = r0; r < r1; ++r)
+        for (int64_t kb = 0; kb < nkb; ++kb)
+            out[(r - r0) * nkb + kb] = orc_sf_offset(r, kb, l, mn, kblocks);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Dequantisation ([GA] Equations: A_hat = dequantize(A, SFA, sf_vec_size)) */
 /* ------------------------------------------------------------------------ */

@@ -130,3 +130,40 @@ def sf_slice(sf: torch.Tensor, l: int, mn_t: int, k_t: int, mt0: int, mt1: int) 
 
 def ceil_div(a, b):
     return -(-a // b)
+
+
+def near_pow2_boundary(amax: np.ndarray, bound: np.ndarray, norm_const: float = 1.0) -> np.ndarray:
+    """True where the E8M0 scale of a block whose true max is `amax` could
+    legitimately differ: [amax - bound, amax + bound] straddles a threshold
+    448 * 2^k / norm_const of the quantiser's round-up."""
+    lo = np.maximum(amax - bound, 0.0) * norm_const / 448.0
+    hi = (amax + bound) * norm_const / 448.0
+    with np.errstate(divide="ignore"):
+        return (np.ceil(np.log2(np.maximum(lo, 1e-300))) != np.ceil(np.log2(np.maximum(hi, 1e-300)))) | (lo == 0)
+
+
+def check_mx_outputs(d_o: np.ndarray, bound: np.ndarray, gpu_row_codes, gpu_row_scales,
+                     gpu_col_codes, gpu_col_scales, norm_const=1.0, what=""):
+    """Dual-direction MX quantisation of oracle D (rows x cols, rows % 32 == 0)
+    vs the GPU's codes / scales given in logical (row, block) order."""
+    rc, rs = O.mx_quant_rows(d_o, norm_const)
+    cc, cs = O.mx_quant_cols(d_o, norm_const)
+    R, C = d_o.shape
+    d32 = d_o.astype(np.float32).astype(np.float64)
+    rmax = np.abs(d32).reshape(R, C // 32, 32).max(-1)
+    rb = bound.reshape(R, C // 32, 32).max(-1)
+    cmax = np.abs(d32).reshape(R // 32, 32, C).max(1)
+    cb = bound.reshape(R // 32, 32, C).max(1)
+    r_near = near_pow2_boundary(rmax, rb, norm_const)
+    c_near = near_pow2_boundary(cmax, cb, norm_const)
+    out = {}
+    # row direction: compare codes where the block's scale agrees
+    same_r = np.repeat(gpu_row_scales == rs, 32, axis=1)
+    out["row"] = check_quant(np.where(same_r, gpu_row_codes, rc), gpu_row_scales, rc, rs,
+                             r_near, what=what + " row")
+    same_c = np.repeat(gpu_col_scales == cs, 32, axis=0)
+    out["col"] = check_quant(np.where(same_c, gpu_col_codes, cc), gpu_col_scales, cc, cs,
+                             c_near, what=what + " col")
+    out["row_scale_mismatch_near_pow2"] = int((gpu_row_scales != rs).sum())
+    out["col_scale_mismatch_near_pow2"] = int((gpu_col_scales != cs).sum())
+    return out

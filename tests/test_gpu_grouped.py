@@ -8,7 +8,7 @@ import torch
 import block_scaled_gemm_02_amd as bsg
 import oracle as O
 import workloads as W
-from parity import check_amax, check_float, ceil_div, sf_slice, sum_bound
+from parity import check_amax, check_float, check_mx_outputs, ceil_div, sf_slice, sum_bound
 
 pytestmark = pytest.mark.gpu
 SENT = -1536.0    # exactly representable in bf16, fp16 and fp32
@@ -149,6 +149,96 @@ def test_grouped_srelu_full_size_sampled():
         else:
             dm = d[rows].float().abs().max().item()
             assert abs(amax[g].item() - dm) <= dm * 2 ** -8
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 output (d_dtype = E4M3): dual-direction quantisation
+# ---------------------------------------------------------------------------
+def run_srelu_fp8(p, with_c=True):
+    s = p.sizes
+    t = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in p.t.items()}
+    m, n = s["m"], s["n"]
+    c = torch.full((m, n), SENT, dtype=torch.bfloat16, device="cuda") if with_c else None
+    d = torch.full((m, n), 0xEE, dtype=torch.uint8, device="cuda")
+    d_col = torch.full((m, n), 0xEE, dtype=torch.uint8, device="cuda")
+    sfd_row = torch.full((W.sf_atom_bytes(m, n, 1),), 0xEE, dtype=torch.uint8, device="cuda")
+    sfd_col = torch.full((W.sf_atom_bytes(n, m, 1),), 0xEE, dtype=torch.uint8, device="cuda")
+    bsg.grouped_gemm_srelu(t["a"], t["b"], t["sfa"], t["sfb"], t["offsets"], t["alpha"], t["prob"],
+                           t["norm_const"], c, d, d_col, sfd_row, sfd_col, None, m, n, s["k"], s["l"],
+                           s["fmt"], c_dtype=torch.bfloat16, d_dtype="e4m3",
+                           tanh_clamp_scale=s["tanh_clamp"])
+    torch.cuda.synchronize()
+    return c, d, d_col, sfd_row, sfd_col
+
+
+def gather_scales(sfd_row, sfd_col, r0, r1, m, n):
+    """Logical (row, N/32) and (rows/32, N) scale arrays for rows [r0, r1)."""
+    row_idx = O.sf_offset_grid(r0, r1, n // 32, 0, m, n // 32)
+    col_idx = O.sf_offset_grid(0, n, ceil_div(r1, 32), 0, n, m // 32)[:, r0 // 32:]
+    rs = sfd_row.cpu().numpy()[row_idx]
+    cs = sfd_col.cpu().numpy()[col_idx].T
+    return rs, cs
+
+
+FP8_CASES = [
+    dict(sizes=[256, 0, 512, 256], n=320, k=192, s=32.0, nc=1.0),
+    dict(sizes=[512, 256], n=256, k=512, s=0.0, nc=1.0),
+    dict(sizes=[0, 256, 256], n=128, k=256, s=0.5, nc=4.0),
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES)
+def test_grouped_srelu_fp8_out_matches_oracle(case):
+    say(f"grouped_srelu fp8 out {case}")
+    off = np.cumsum(case["sizes"]).astype(np.int32)
+    L = len(case["sizes"])
+    p = W.grouped_srelu_problem(0, L, case["n"], case["k"], "e4m3", seed=4, offsets=off,
+                                tanh_clamp=case["s"], extra_rows=256, d_dtype="e4m3")
+    p.t["norm_const"] = torch.tensor([case["nc"]])
+    s = p.sizes
+    m, n, k = s["m"], s["n"], s["k"]
+    c, d, d_col, sfd_row, sfd_col = run_srelu_fp8(p)
+    r = O.grouped_srelu(p.t["a"], p.t["b"], p.t["sfa"], p.t["sfb"], off, p.t["alpha"], p.t["prob"],
+                        m, n, k, L, "e4m3", s["tanh_clamp"])
+    valid = s["valid_m"]
+    prob = p.t["prob"].double().numpy()
+    bc = sum_bound(r["sabs"], k, bmax=r["bmax"])
+    check_float(c[:valid].cpu(), r["c"][:valid], bc[:valid], what="C")
+    bd = d_bound(r["c"], bc, prob, s["tanh_clamp"])[:valid]
+    rs, cs = gather_scales(sfd_row, sfd_col, 0, valid, m, n)
+    res = check_mx_outputs(r["d"][:valid], bd, d[:valid].cpu().numpy(), rs, d_col[:valid].cpu().numpy(),
+                           cs, case["nc"], what="D")
+    say(f"  {res}")
+    assert torch.all(d[valid:] == 0xEE) and torch.all(d_col[valid:] == 0xEE)
+
+
+def test_grouped_srelu_fp8_out_full_size_sampled():
+    """Full grouped MXFP8 + sReLU workload with FP8 D: sampled 128-row panels."""
+    say("grouped_srelu fp8 out full size")
+    p = W.moe_mxfp8_srelu(device="cuda", d_dtype="e4m3")
+    s = p.sizes
+    m, n, k, L = s["m"], s["n"], s["k"], s["l"]
+    c, d, d_col, sfd_row, sfd_col = run_srelu_fp8(p, with_c=False)
+    t = p.t
+    off = t["offsets"].cpu().numpy()
+    m_t, n_t, k_t = ceil_div(m, 128), ceil_div(n, 128), ceil_div(k, 128)
+    begins = np.concatenate([[0], off[:-1]])
+    nonempty = [g for g in range(L) if off[g] > begins[g]]
+    for g in (nonempty[0], nonempty[-1]):
+        r0 = int(off[g]) - 128
+        say(f"  oracle expert {g} rows {r0}..{r0 + 127}")
+        sub = O.grouped_srelu(t["a"][r0:r0 + 128].cpu(), t["b"][g:g + 1].cpu(),
+                              sf_slice(t["sfa"], 0, m_t, k_t, r0 // 128, r0 // 128 + 1).cpu(),
+                              sf_slice(t["sfb"], g, n_t, k_t, 0, n_t).cpu(),
+                              np.array([128], np.int32), t["alpha"][g:g + 1].cpu(),
+                              t["prob"][r0:r0 + 128].cpu(), 128, n, k, 1, "e4m3", 32.0)
+        prob = t["prob"][r0:r0 + 128].double().cpu().numpy()
+        bc = sum_bound(sub["sabs"], k, bmax=sub["bmax"])
+        bd = d_bound(sub["c"], bc, prob, 32.0)
+        rs, cs = gather_scales(sfd_row, sfd_col, r0, r0 + 128, m, n)
+        res = check_mx_outputs(sub["d"], bd, d[r0:r0 + 128].cpu().numpy(), rs,
+                               d_col[r0:r0 + 128].cpu().numpy(), cs, 1.0, what=f"e{g}")
+        say(f"  {res}")
 
 
 # ---------------------------------------------------------------------------
