@@ -175,7 +175,34 @@ def wl_moe_bf16():
     return step, info
 
 
+def wl_proj_rope():
+    import torch
+    import block_scaled_gemm_02_amd as bsg
+    import workloads as W
+    p = W.proj_rope_dsv3(device="cuda")
+    s, t = p.sizes, p.t
+    T, H, D = s["tokens"], s["heads"], s["head_dim"]
+    qr = torch.empty(T, H, D, dtype=torch.uint8, device="cuda")
+    qc = torch.empty(T, H, D, dtype=torch.uint8, device="cuda")
+    sr = torch.empty(T, H, D // 32, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(T // 32, H, D, dtype=torch.uint8, device="cuda")
+
+    def step():
+        bsg.gemm_proj_rope_mxfp8(t["x"], t["w"], None, None, t["cos"], t["sin"], qr, sr, qc, sc,
+                                 T, s["q_lora"], H, D, s["qk_rope"], w_out_in=1)
+
+    n = H * D
+    info = dict(name="proj_rope", fmt="bf16", flops=2.0 * T * n * s["q_lora"],
+                alg_bytes=2 * (T * s["q_lora"] + n * s["q_lora"] + 2 * T * 64) + 2 * T * n + T * n // 16,
+                kernel="k_proj_rope",
+                config={"workload": "projection GEMM + per-head RoPE + dual MXFP8, DeepSeek-V3 Q up-proj",
+                        "tokens": T, "q_lora": s["q_lora"], "heads": H, "head_dim": D, "qk_rope": 64},
+                cpu=None)
+    return step, info
+
+
 WORKLOADS = {
+    "proj_rope": wl_proj_rope,
     "moe_mxfp8_srelu": lambda: wl_moe_mxfp8_srelu(False),
     "moe_mxfp8_srelu_fp8d": lambda: wl_moe_mxfp8_srelu(True),
     "dense_8192_e4m3": lambda: wl_dense_8192("e4m3"),

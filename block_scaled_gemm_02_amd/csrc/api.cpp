@@ -239,6 +239,8 @@ int bsg_validate_grouped_gemm_srelu(const void *a, const void *b, const uint8_t 
     if (!aligned16(d) || (n * db) % 16 || (d_col && !aligned16(d_col)) ||
         (c && (!aligned16(c) || (n * elem_bytes(c_dtype)) % 16)))
         return fail(BSG_ERR_ALIGN, "C/D/D_col must be 16-byte aligned with 16-byte rows");
+    if (fp8_out && ((reinterpret_cast<uintptr_t>(sfd_row) | reinterpret_cast<uintptr_t>(sfd_col)) & 3u))
+        return fail(BSG_ERR_ALIGN, "sfd_row and sfd_col must be 4-byte aligned");
     if ((int64_t)row_bytes(ab_dtype, k) * 256 >= (1ll << 31)) return fail(BSG_ERR_UNSUPPORTED, "K too large");
     return BSG_OK;
 }
@@ -291,8 +293,9 @@ int bsg_validate_gemm_proj_rope_mxfp8(const void *x, const void *w, const uint8_
     if (tokens * num_heads == 0) return BSG_OK;
     if (!x || !w || !cos || !sin || !out_fp8_row || !out_scales_row || !out_fp8_col || !out_scales_col)
         return fail(BSG_ERR_NULLPTR, "all tensors are required");
-    if (!aligned16(x) || !aligned16(w) || !aligned16(out_fp8_row) || !aligned16(out_fp8_col))
-        return fail(BSG_ERR_ALIGN, "x, w and the fp8 outputs must be 16-byte aligned");
+    if (!aligned16(x) || !aligned16(w) || !aligned16(out_fp8_row) || !aligned16(out_fp8_col) ||
+        !aligned16(cos) || !aligned16(sin))
+        return fail(BSG_ERR_ALIGN, "x, w, cos, sin and the fp8 outputs must be 16-byte aligned");
     return BSG_OK;
 }
 

@@ -65,7 +65,7 @@ struct GemmAmaxParams {
 template <int F>
 __global__ void __launch_bounds__(256) k_gemm_amax(GemmAmaxParams p)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kStageBytes];
+    BSG_DECLARE_RING(F, ring);
     __shared__ float red[4];
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
     const int64_t batch = blockIdx.z;
@@ -78,23 +78,15 @@ __global__ void __launch_bounds__(256) k_gemm_amax(GemmAmaxParams p)
     OperandDesc B{p.b + (batch * p.n + n0) * p.row_bytes, (uint32_t)(rows_b * p.row_bytes),
                   p.row_bytes, p.sfb, batch, p.n_t, p.k_t, n0 / 128, p.n_t - 1};
     f32x16 acc[4][4];
-    mainloop<F>(acc, lds, A, B, p.k);
+    mainloop_pipe<F>(acc, ring, A, B, p.k);
 
     float lmax = 0.0f;
     const int64_t cbase = batch * p.m * p.n;
-    static_for<16>([&](auto ij) {
-        constexpr int i = decltype(ij)::value / 4, j = decltype(ij)::value % 4;
-        const f32x16 a = acc[i][j];
-        const int64_t col = n0 + acc_col(wn, j, lane);
-        if (col < p.n) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t row = m0 + acc_row(wm, i, v, lane);
-                if (row < p.m) {
-                    store_elem(p.c, cbase + row * p.n + col, a[v], p.c_dtype);
-                    lmax = fmaxf(lmax, fabsf(a[v]));
-                }
-            }
+    for_each_row_quad<4>(acc, wm, wn, lane, [&](auto, auto, auto, int row, int col0, float (&x)[4]) {
+        const int64_t r = m0 + row, c = n0 + col0;
+        if (r < p.m && c < p.n) {       // N is a multiple of 4: a quad is all in or all out
+            store4(p.c, cbase + r * p.n + c, x, p.c_dtype);
+            lmax = fmaxf(lmax, fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
         }
     });
     if (p.amax) block_amax_atomic(lmax, p.amax, red);
@@ -167,12 +159,13 @@ __device__ __forceinline__ float srelu_value(float gval, float pr, float s, floa
 // d_col, scales to the SFD_col atoms over (N, M)), with the quantiser of
 // "Grouped GEMM + dSwiGLU (SM100)", Step 3 (rcp_max = 1/448).
 //
-// In the 32x32 accumulator layout a row's 32 columns sit in the 32 lanes of
-// one half-wave (reduced with DPP), and a column's 32 rows sit in lane c
-// (16 rows) and lane c+32 (the other 16).
-__device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, const f32x16 (&acc)[4][4],
-                                                   int64_t m0, int64_t n0, int g, float alpha,
-                                                   int wm, int wn, int lane)
+// Works in the transposed accumulator layout, where a 32x32 block (i, j) of
+// the wave holds, per lane, 4 columns of 4 rows: a column's 32 values sit in
+// one quad of each half-wave, a row's 32 values in 8 lanes of one half-wave.
+// C (pre-activation) is written first when requested.
+__device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x16 (&acc)[4][4],
+                                                   int64_t m0, int64_t n0, float alpha, int wm,
+                                                   int wn, int lane)
 {
     const float nc = *p.norm_const;
     const int64_t n = p.n;
@@ -180,66 +173,87 @@ __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, const
     const int64_t col_kt = (p.m / 32 + 3) / 4;        // SFD_col: K' over M
     uint8_t *dq = static_cast<uint8_t *>(p.d);
     uint8_t *dc = static_cast<uint8_t *>(p.d_col);
-    const int c32 = lane & 31, gh = lane >> 5;
-    static_for<16>([&](auto ij) {
-        constexpr int i = decltype(ij)::value / 4, j = decltype(ij)::value % 4;
-        const int64_t col = n0 + acc_col(wn, j, lane);
-        const bool col_ok = col < n;
-        f32x16 dv;
+    const int t = lane & 3, c32 = lane & 31, gh = lane >> 5;
+
+    transpose_acc<4>(acc, lane);
+    static_for<4>([&](auto ii) {
+        constexpr int i = decltype(ii)::value;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int64_t row = m0 + acc_row(wm, i, v, lane);
-            const float gval = alpha * acc[i][j][v];
-            if (p.c && col_ok) store_elem(p.c, row * n + col, gval, p.c_dtype);
-            dv[v] = srelu_value(gval, p.prob[row], p.tanh_s, p.tanh_inv_s);
-        }
-        // ---- column direction: rows 32i..32i+31 of this quadrant, column col
-        float cm = 0.0f;
+        for (int q = 0; q < 4; ++q) {
+            const int64_t r = m0 + tr_row(wm, i, q, lane);
+            const float pr = p.prob[r];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) cm = fmaxf(cm, fabsf(dv[v]));
-        cm = fmaxf(cm, __shfl_xor(cm, 32));
-        float cinv;
-        const uint32_t cbyte = mx_scale_byte(cm, nc, cinv);
-        if (col_ok) {
+            for (int j = 0; j < 4; ++j) {
+                const int64_t c = n0 + tr_col<4>(wn, j, lane);
+                float x[4];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t row = m0 + acc_row(wm, i, v, lane);
-                dc[row * n + col] = (uint8_t)e4m3_code(dv[v] * cinv);
+                for (int u = 0; u < 4; ++u) x[u] = alpha * acc[i][j][4 * q + u];
+                if (p.c && c < n) store4(p.c, r * n + c, x, p.c_dtype);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    acc[i][j][4 * q + u] = srelu_value(x[u], pr, p.tanh_s, p.tanh_inv_s);
             }
-            if (gh == 0) {
-                const int64_t mt = (m0 + 128 * wm) / 128;       // 4 row blocks = one atom K group
-                const int64_t off = (((col / 128) * col_kt + mt) * 32 + (col % 32)) * 16 +
-                                    ((col % 128) / 32) * 4 + i;
-                p.sfd_col[off] = (uint8_t)cbyte;
-            }
-        }
-        // ---- row direction: row r of the block, columns 32j..32j+31
-        uint32_t my_byte = 0;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const float rm = half_wave_max(fabsf(dv[v]));
-            float rinv;
-            const uint32_t rbyte = mx_scale_byte(rm, nc, rinv);
-            if (c32 == v) my_byte = rbyte;
-            if (col_ok) {
-                const int64_t row = m0 + acc_row(wm, i, v, lane);
-                dq[row * n + col] = (uint8_t)e4m3_code(dv[v] * rinv);
-            }
-        }
-        if (c32 < 16 && n0 + 128 * wn + 32 * j < n) {
-            const int64_t row = m0 + acc_row(wm, i, c32, lane);
-            const int64_t nb = (n0 + 128 * wn) / 32 + j;
-            const int64_t off = (((row / 128) * row_kt + nb / 4) * 32 + (row % 32)) * 16 +
-                                ((row % 128) / 32) * 4 + (nb % 4);
-            p.sfd_row[off] = (uint8_t)my_byte;
         }
     });
+
+    uint32_t rword[4][4] = {};                        // SFD_row bytes j = 0..3 of each row
+    static_for<4>([&](auto jj) {
+        constexpr int j = decltype(jj)::value;
+        const int64_t c = n0 + tr_col<4>(wn, j, lane);
+        uint32_t cword = 0;                           // SFD_col bytes i = 0..3 of column c + t
+        static_for<4>([&](auto ii) {
+            constexpr int i = decltype(ii)::value;
+            float cm[4], cinv[4];
+            tr_col_absmax(acc[i][j], cm);
+            uint32_t cb[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) cb[u] = mx_scale_byte(cm[u], nc, cinv[u]);
+            cword |= (t == 0 ? cb[0] : t == 1 ? cb[1] : t == 2 ? cb[2] : cb[3]) << (8 * i);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float x[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                    acc[i][j][4 * q + 3]};
+                float rm = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+                rm = row8_max(rm);
+                float rinv;
+                const uint32_t rb = mx_scale_byte(rm, nc, rinv);
+                rword[i][q] |= rb << (8 * j);
+                if (c < n) {
+                    const int64_t r = m0 + tr_row(wm, i, q, lane);
+                    *reinterpret_cast<uint32_t *>(dq + r * n + c) =
+                        pack4_e4m3(x[0] * rinv, x[1] * rinv, x[2] * rinv, x[3] * rinv);
+                    *reinterpret_cast<uint32_t *>(dc + r * n + c) =
+                        pack4_e4m3(x[0] * cinv[0], x[1] * cinv[1], x[2] * cinv[2], x[3] * cinv[3]);
+                }
+            }
+        });
+        if (gh == 0 && c < n) {
+            // column c + t, the wave's four 32-row blocks = one K' group of SFD_col
+            const int64_t col = c + t;
+            const int64_t mt = (m0 + 128 * wm) / 128;
+            const int64_t off = (((col / 128) * col_kt + mt) * 32 + (col % 32)) * 16 + ((col % 128) / 32) * 4;
+            *reinterpret_cast<uint32_t *>(p.sfd_col + off) = cword;
+        }
+    });
+    if (c32 < 4 && n0 + 128 * wn < n) {
+        // row r, the wave's four 32-column blocks = one K' group of SFD_row
+        const int64_t kt = (n0 + 128 * wn) / 128;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t r = m0 + tr_row(wm, i, q, lane);
+                const int64_t off = (((r / 128) * row_kt + kt) * 32 + (r % 32)) * 16 + ((r % 128) / 32) * 4;
+                *reinterpret_cast<uint32_t *>(p.sfd_row + off) = rword[i][q];
+            }
+        }
+    }
 }
 
 template <int F, int EPI>
 __global__ void __launch_bounds__(256) k_grouped(GroupedParams p)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kStageBytes];
+    BSG_DECLARE_RING(F, ring);
     __shared__ float red[4];
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
     const int64_t m0 = (int64_t)blockIdx.y * kTileM, n0 = (int64_t)blockIdx.x * kTileN;
@@ -253,41 +267,53 @@ __global__ void __launch_bounds__(256) k_grouped(GroupedParams p)
     OperandDesc B{p.b + ((int64_t)g * p.n + n0) * p.row_bytes, (uint32_t)(rows_b * p.row_bytes),
                   p.row_bytes, p.sfb, g, p.n_t, p.k_t, n0 / 128, p.n_t - 1};
     f32x16 acc[4][4];
-    mainloop<F>(acc, lds, A, B, p.k);
+    mainloop_pipe<F>(acc, ring, A, B, p.k);
 
     const float alpha = p.alpha[g];
     if constexpr (EPI == EPI_SRELU_FP8) {
-        epilogue_srelu_fp8(p, acc, m0, n0, g, alpha, wm, wn, lane);
+        epilogue_srelu_fp8(p, acc, m0, n0, alpha, wm, wn, lane);
     } else {
         float lmax = 0.0f;
-        static_for<16>([&](auto ij) {
-            constexpr int i = decltype(ij)::value / 4, j = decltype(ij)::value % 4;
-            const f32x16 a = acc[i][j];
-            const int64_t col = n0 + acc_col(wn, j, lane);
-            if (col >= p.n) return;
-            float bv = 0.0f;
-            if constexpr (EPI == EPI_BF16_BIAS) {
-                if (p.bias) bv = load_elem(p.bias, (int64_t)g * p.n + col, p.bias_dtype);
-            }
+        transpose_acc<4>(acc, lane);
+        static_for<4>([&](auto ii) {
+            constexpr int i = decltype(ii)::value;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t row = m0 + acc_row(wm, i, v, lane);
-                const float pr = p.prob[row];
-                const int64_t idx = row * p.n + col;
-                const float gval = alpha * a[v];
-                if constexpr (EPI == EPI_BF16_BIAS) {
-                    // "Grouped GEMM (SM100 BF16)", Operation: with bias C = G + prob*bias,
-                    // D = C; without bias C = G, D = prob*G.
-                    const float cval = p.bias ? gval + pr * bv : gval;
-                    const float dval = p.bias ? cval : pr * gval;
-                    if (p.c) store_elem(p.c, idx, cval, p.c_dtype);
-                    store_elem(p.d, idx, dval, p.d_dtype);
-                } else {
-                    const float dval = srelu_value(gval, pr, p.tanh_s, p.tanh_inv_s);
-                    if (p.c) store_elem(p.c, idx, gval, p.c_dtype);
-                    store_elem(p.d, idx, dval, p.d_dtype);
-                    if (p.d_col) store_elem(p.d_col, idx, dval, p.d_dtype);
-                    lmax = fmaxf(lmax, fabsf(dval));
+            for (int q = 0; q < 4; ++q) {
+                const int64_t r = m0 + tr_row(wm, i, q, lane);
+                const float pr = p.prob[r];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t c = n0 + tr_col<4>(wn, j, lane);
+                    if (c >= p.n) continue;         // N is a multiple of 8: runs of 4 are whole
+                    const int64_t idx = r * p.n + c;
+                    float cv[4], dv[4];
+                    if constexpr (EPI == EPI_BF16_BIAS) {
+                        // "Grouped GEMM (SM100 BF16)", Operation: with bias C = G + prob*bias,
+                        // D = C; without bias C = G, D = prob*G.
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const float gval = alpha * acc[i][j][4 * q + u];
+                            if (p.bias) {
+                                cv[u] = gval + pr * load_elem(p.bias, (int64_t)g * p.n + c + u, p.bias_dtype);
+                                dv[u] = cv[u];
+                            } else {
+                                cv[u] = gval;
+                                dv[u] = pr * gval;
+                            }
+                        }
+                        if (p.c) store4(p.c, idx, cv, p.c_dtype);
+                        store4(p.d, idx, dv, p.d_dtype);
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            cv[u] = alpha * acc[i][j][4 * q + u];
+                            dv[u] = srelu_value(cv[u], pr, p.tanh_s, p.tanh_inv_s);
+                            lmax = fmaxf(lmax, fabsf(dv[u]));
+                        }
+                        if (p.c) store4(p.c, idx, cv, p.c_dtype);
+                        store4(p.d, idx, dv, p.d_dtype);
+                        if (p.d_col) store4(p.d_col, idx, dv, p.d_dtype);
+                    }
                 }
             }
         });

@@ -36,9 +36,10 @@
  *        (((l*MN' + r/128)*K' + kb/4)*32 + r%32)*16 + ((r%128)/32)*4 + kb%4
  *    with MN' = ceil(MN/128), K' = ceil(K/128).  Bytes of padding rows and
  *    padding K-blocks are ignored.
- *  - Alignment: base pointers of A, B, C, D, D_col, x, w must be 16-byte
- *    aligned and so must each row's byte length ("GEMM + Amax (SM100)":
- *    16-byte alignment along the contiguous dimension).
+ *  - Alignment: base pointers of A, B, C, D, D_col, x, w, cos, sin and the
+ *    fp8 outputs must be 16-byte aligned and so must each row's byte length
+ *    ("GEMM + Amax (SM100)": 16-byte alignment along the contiguous
+ *    dimension); the sfd_row / sfd_col scale buffers must be 4-byte aligned.
  *  - Return value: BSG_OK (0) or a bsg_status; bsg_last_error() returns a
  *    thread-local message describing the most recent failure.
  */
