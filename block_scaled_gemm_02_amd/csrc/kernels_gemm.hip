@@ -5,23 +5,16 @@
 //   k_grouped        "Grouped GEMM (SM100 BF16)" and "Grouped GEMM + sReLU
 //                    (SM100)": tiles of 256 rows never straddle an expert
 //                    because every padded_offsets entry is a multiple of 256.
+//
+// Epilogues work on the accumulator layout of mma_one: lane (c, g) of block
+// (i, j) owns row 32i + c and the column runs 32j + 8q + 4g + [0, 4).  Every
+// value a store depends on (prob, bias) is loaded before the first store:
+// loads and stores share one counter, so a load issued after stores would
+// wait for all of them.
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace bsg {
-
-enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_E4M3 = 3 };
-
-__device__ __forceinline__ void store_elem(void *base, int64_t idx, float v, int dtype)
-{
-    if (dtype == DT_F32) {
-        static_cast<float *>(base)[idx] = v;
-    } else if (dtype == DT_BF16) {
-        static_cast<uint16_t *>(base)[idx] = f32_to_bf16_rne(v);
-    } else {
-        static_cast<uint16_t *>(base)[idx] = f32_to_f16_rne(v);
-    }
-}
 
 __device__ __forceinline__ float load_elem(const void *base, int64_t idx, int dtype)
 {
@@ -48,6 +41,55 @@ static inline uint32_t row_bytes_of(int fmt, int64_t k)
 {
     return (uint32_t)(fmt == FMT_E2M1 ? k / 2 : (fmt == FMT_BF16 ? 2 * k : k));
 }
+
+// Stores one 256 x 256 output tile from the accumulators: value(i, j, v, acc)
+// gives the output for register v of block (i, j).  Addresses are a uniform
+// tile base plus a 32-bit per-lane row offset (so 256 rows of the output
+// span less than 4 GiB); the block/run part is an immediate.  Runs past N
+// (a multiple of 4) and rows at or past `rows` are skipped.
+template <int DT, class Fn>
+__device__ __forceinline__ void store_tile(void *base, void *base2, int64_t n, int64_t m0, int64_t n0, int wm,
+                                           int wn, int lane, const f32x16 (&acc)[4][4], int64_t rows,
+                                           Fn &&value)
+{
+    constexpr int ES = DT == DT_F32 ? 4 : 2;
+    char *tile = static_cast<char *>(base) + (m0 * n + n0) * ES;
+    char *tile2 = base2 ? static_cast<char *>(base2) + (m0 * n + n0) * ES : nullptr;
+    static_for<4>([&](auto ii) {
+        constexpr int i = decltype(ii)::value;
+        const int rl = acc_row(wm, i, lane);
+        if (rl >= rows) return;
+        const uint32_t roff = (uint32_t)rl * (uint32_t)n * ES;
+        static_for<4>([&](auto jj) {
+            constexpr int j = decltype(jj)::value;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int cl = acc_col<4>(wn, j, q, lane);
+                if (n0 + cl >= n) continue;
+                float x[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) x[u] = value(i, j, 4 * q + u, acc[i][j][4 * q + u]);
+                const uint32_t off = roff + (uint32_t)cl * ES;
+                store4<DT>(tile + off, 0, x[0], x[1], x[2], x[3]);
+                if (tile2) store4<DT>(tile2 + off, 0, x[0], x[1], x[2], x[3]);
+            }
+        });
+    });
+}
+
+template <class Fn>
+__device__ __forceinline__ void store_tile_rt(int dt, void *base, void *base2, int64_t n, int64_t m0, int64_t n0,
+                                              int wm, int wn, int lane, const f32x16 (&acc)[4][4], int64_t rows,
+                                              Fn &&value)
+{
+    if (dt == DT_F32) store_tile<DT_F32>(base, base2, n, m0, n0, wm, wn, lane, acc, rows, value);
+    else if (dt == DT_BF16) store_tile<DT_BF16>(base, base2, n, m0, n0, wm, wn, lane, acc, rows, value);
+    else store_tile<DT_F16>(base, base2, n, m0, n0, wm, wn, lane, acc, rows, value);
+}
+
+// Waits for every outstanding vector-memory load before the epilogue's first
+// store (see the file comment).
+__device__ __forceinline__ void wait_loads() { s_wait_vm<0>(); }
 
 // ---------------------------------------------------------------------------
 // Dense batched GEMM + global amax
@@ -80,15 +122,13 @@ __global__ void __launch_bounds__(256) k_gemm_amax(GemmAmaxParams p)
     f32x16 acc[4][4];
     mainloop_pipe<F>(acc, ring, A, B, p.k);
 
+    // rows past M (ragged last tile): computed from zero rows of A, not stored
     float lmax = 0.0f;
-    const int64_t cbase = batch * p.m * p.n;
-    for_each_row_quad<4>(acc, wm, wn, lane, [&](auto, auto, auto, int row, int col0, float (&x)[4]) {
-        const int64_t r = m0 + row, c = n0 + col0;
-        if (r < p.m && c < p.n) {       // N is a multiple of 4: a quad is all in or all out
-            store4(p.c, cbase + r * p.n + c, x, p.c_dtype);
-            lmax = fmaxf(lmax, fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
-        }
-    });
+    store_tile_rt(p.c_dtype, static_cast<char *>(p.c) + batch * p.m * p.n * (p.c_dtype == DT_F32 ? 4 : 2),
+                  nullptr, p.n, m0, n0, wm, wn, lane, acc, rows_a, [&](int, int, int, float a) {
+                      lmax = fmaxf(lmax, fabsf(a));
+                      return a;
+                  });
     if (p.amax) block_amax_atomic(lmax, p.amax, red);
 }
 
@@ -145,13 +185,69 @@ __device__ __forceinline__ int expert_of(const int32_t *offsets, int num, int64_
     return lo;
 }
 
-// sReLU value of one accumulator: alpha*acc -> relu -> optional tanh clamp
-// -> prob * x^2 (fp32, "Grouped GEMM + sReLU (SM100)" Equations).
+// sReLU value of one pre-activation value g = alpha*acc: relu, optional tanh
+// clamp, times prob ("Grouped GEMM + sReLU (SM100)" Equations):
+// D = prob * (s * tanh(relu(g) / s))^2, or prob * relu(g)^2 without clamp.
+template <bool CLAMP>
 __device__ __forceinline__ float srelu_value(float gval, float pr, float s, float inv_s)
 {
-    float x = fmaxf(gval, 0.0f);
-    if (s > 0.0f) x = s * fminf(1.0f, tanh_pos(x * inv_s));
+    const float r = fmaxf(gval, 0.0f);
+    const float x = CLAMP ? s * tanh_pos(r * inv_s) : r;
     return pr * x * x;
+}
+
+// BF16 bias epilogue and sReLU epilogue with 16/32-bit outputs: C, then D
+// (and D_col, which equals D for unquantised outputs), each pass with its
+// own compile-time store type.
+template <int EPI, bool CLAMP>
+__device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, const f32x16 (&acc)[4][4],
+                                                 int64_t m0, int64_t n0, int g, float alpha, int wm,
+                                                 int wn, int lane, float *red)
+{
+    const int64_t n = p.n;
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = p.prob[m0 + acc_row(wm, i, lane)];
+    // bias of this lane's 16 columns of each block
+    float bv[4][16];
+    const bool has_bias = EPI == EPI_BF16_BIAS && p.bias != nullptr;
+    if constexpr (EPI == EPI_BF16_BIAS) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t c = n0 + acc_col<4>(wn, j, q, lane);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    bv[j][4 * q + u] = (has_bias && c < n) ? load_elem(p.bias, (int64_t)g * n + c + u, p.bias_dtype)
+                                                           : 0.0f;
+            }
+    }
+    wait_loads();
+    // "Grouped GEMM (SM100 BF16)", Operation: with bias C = G + prob*bias,
+    // D = C; without bias C = G, D = prob*G.  sReLU: C = G, D = sReLU(G).
+    if (p.c) {
+        store_tile_rt(p.c_dtype, p.c, nullptr, n, m0, n0, wm, wn, lane, acc, kTileM, [&](int i, int j, int v, float a) {
+            const float gval = alpha * a;
+            if constexpr (EPI == EPI_BF16_BIAS) return has_bias ? gval + pr[i] * bv[j][v] : gval;
+            else return gval;
+        });
+    }
+    float lmax = 0.0f;
+    store_tile_rt(p.d_dtype, p.d, EPI == EPI_BF16_BIAS ? nullptr : p.d_col, n, m0, n0, wm, wn, lane, acc,
+                  kTileM, [&](int i, int j, int v, float a) {
+        const float gval = alpha * a;
+        if constexpr (EPI == EPI_BF16_BIAS) {
+            return has_bias ? gval + pr[i] * bv[j][v] : pr[i] * gval;
+        } else {
+            const float d = srelu_value<CLAMP>(gval, pr[i], p.tanh_s, p.tanh_inv_s);
+            lmax = fmaxf(lmax, fabsf(d));
+            return d;
+        }
+    });
+    if constexpr (EPI == EPI_SRELU) {
+        if (p.amax) block_amax_atomic(lmax, p.amax + g, red);
+    }
 }
 
 // MXFP8 output: D quantised in 32-wide blocks along N (codes to d, scales to
@@ -159,10 +255,11 @@ __device__ __forceinline__ float srelu_value(float gval, float pr, float s, floa
 // d_col, scales to the SFD_col atoms over (N, M)), with the quantiser of
 // "Grouped GEMM + dSwiGLU (SM100)", Step 3 (rcp_max = 1/448).
 //
-// Works in the transposed accumulator layout, where a 32x32 block (i, j) of
-// the wave holds, per lane, 4 columns of 4 rows: a column's 32 values sit in
-// one quad of each half-wave, a row's 32 values in 8 lanes of one half-wave.
-// C (pre-activation) is written first when requested.
+// A row's 32 values of block j sit in this lane (16) and lane ^ 32 (16); a
+// column's 32 values of block i sit in one register of the 32 lanes of a
+// half-wave.  C (pre-activation) is written first when requested; D then
+// replaces the accumulators.
+template <bool CLAMP>
 __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x16 (&acc)[4][4],
                                                    int64_t m0, int64_t n0, float alpha, int wm,
                                                    int wn, int lane)
@@ -173,84 +270,94 @@ __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x1
     const int64_t col_kt = (p.m / 32 + 3) / 4;        // SFD_col: K' over M
     uint8_t *dq = static_cast<uint8_t *>(p.d);
     uint8_t *dc = static_cast<uint8_t *>(p.d_col);
-    const int t = lane & 3, c32 = lane & 31, gh = lane >> 5;
+    const int c32 = lane & 31, gh = lane >> 5;
 
-    transpose_acc<4>(acc, lane);
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = p.prob[m0 + acc_row(wm, i, lane)];
+    wait_loads();
     static_for<4>([&](auto ii) {
         constexpr int i = decltype(ii)::value;
+        const int64_t r = m0 + acc_row(wm, i, lane);
+        static_for<4>([&](auto jj) {
+            constexpr int j = decltype(jj)::value;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int64_t r = m0 + tr_row(wm, i, q, lane);
-            const float pr = p.prob[r];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t c = n0 + tr_col<4>(wn, j, lane);
+            for (int q = 0; q < 4; ++q) {
                 float x[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) x[u] = alpha * acc[i][j][4 * q + u];
-                if (p.c && c < n) store4(p.c, r * n + c, x, p.c_dtype);
+                const int64_t c = n0 + acc_col<4>(wn, j, q, lane);
+                if (p.c && c < n) store4_rt(p.c, r * n + c, x[0], x[1], x[2], x[3], p.c_dtype);
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    acc[i][j][4 * q + u] = srelu_value(x[u], pr, p.tanh_s, p.tanh_inv_s);
+                    acc[i][j][4 * q + u] = srelu_value<CLAMP>(x[u], pr[i], p.tanh_s, p.tanh_inv_s);
             }
-        }
+        });
     });
 
-    uint32_t rword[4][4] = {};                        // SFD_row bytes j = 0..3 of each row
+    uint32_t rword[4] = {0u, 0u, 0u, 0u};            // SFD_row bytes j = 0..3 of row i*32 + c
     static_for<4>([&](auto jj) {
         constexpr int j = decltype(jj)::value;
-        const int64_t c = n0 + tr_col<4>(wn, j, lane);
-        uint32_t cword = 0;                           // SFD_col bytes i = 0..3 of column c + t
+        uint32_t cword[16];                           // SFD_col bytes i = 0..3 of each column
+#pragma unroll
+        for (int v = 0; v < 16; ++v) cword[v] = 0u;
         static_for<4>([&](auto ii) {
             constexpr int i = decltype(ii)::value;
-            float cm[4], cinv[4];
-            tr_col_absmax(acc[i][j], cm);
-            uint32_t cb[4];
+            const f32x16 &a = acc[i][j];
+            // row block: this lane's 16 columns and the partner half's 16
+            float rm = 0.0f;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) cb[u] = mx_scale_byte(cm[u], nc, cinv[u]);
-            cword |= (t == 0 ? cb[0] : t == 1 ? cb[1] : t == 2 ? cb[2] : cb[3]) << (8 * i);
+            for (int v = 0; v < 16; ++v) rm = fmaxf(rm, fabsf(a[v]));
+            rm = fmaxf(rm, xor32(rm));
+            float rinv;
+            rword[i] |= mx_scale_byte(rm, nc, rinv) << (8 * j);
+            // column blocks: 32 rows of each column over the half-wave
+            float cinv[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float cm = half_wave_max(fabsf(a[v]));
+                cword[v] |= mx_scale_byte(cm, nc, cinv[v]) << (8 * i);
+            }
+            const int64_t r = m0 + acc_row(wm, i, lane);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float x[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                    acc[i][j][4 * q + 3]};
-                float rm = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
-                rm = row8_max(rm);
-                float rinv;
-                const uint32_t rb = mx_scale_byte(rm, nc, rinv);
-                rword[i][q] |= rb << (8 * j);
+                const int64_t c = n0 + acc_col<4>(wn, j, q, lane);
                 if (c < n) {
-                    const int64_t r = m0 + tr_row(wm, i, q, lane);
                     *reinterpret_cast<uint32_t *>(dq + r * n + c) =
-                        pack4_e4m3(x[0] * rinv, x[1] * rinv, x[2] * rinv, x[3] * rinv);
+                        pack4_e4m3(a[4 * q] * rinv, a[4 * q + 1] * rinv, a[4 * q + 2] * rinv, a[4 * q + 3] * rinv);
                     *reinterpret_cast<uint32_t *>(dc + r * n + c) =
-                        pack4_e4m3(x[0] * cinv[0], x[1] * cinv[1], x[2] * cinv[2], x[3] * cinv[3]);
+                        pack4_e4m3(a[4 * q] * cinv[4 * q], a[4 * q + 1] * cinv[4 * q + 1],
+                                   a[4 * q + 2] * cinv[4 * q + 2], a[4 * q + 3] * cinv[4 * q + 3]);
                 }
             }
         });
-        if (gh == 0 && c < n) {
-            // column c + t, the wave's four 32-row blocks = one K' group of SFD_col
-            const int64_t col = c + t;
+        // SFD_col: lane c < 16 of each half writes the word of its register c,
+        // column 32j + 8(c/4) + 4g + c%4: the wave's four 32-row blocks form one
+        // K' group of the (N, M) atoms
+        uint32_t word = cword[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) word = c32 == v ? cword[v] : word;
+        const int64_t col = n0 + acc_col<4>(wn, j, 0, lane) + 8 * (c32 >> 2) + (c32 & 3);
+        if (c32 < 16 && col < n) {
             const int64_t mt = (m0 + 128 * wm) / 128;
             const int64_t off = (((col / 128) * col_kt + mt) * 32 + (col % 32)) * 16 + ((col % 128) / 32) * 4;
-            *reinterpret_cast<uint32_t *>(p.sfd_col + off) = cword;
+            *reinterpret_cast<uint32_t *>(p.sfd_col + off) = word;
         }
     });
-    if (c32 < 4 && n0 + 128 * wn < n) {
-        // row r, the wave's four 32-column blocks = one K' group of SFD_row
+    // SFD_row: row r, the wave's four 32-column blocks = one K' group of the
+    // (M, N) atoms; blocks past N carry the scale of an all-zero block
+    if (gh == 0 && n0 + 128 * wn < n) {
         const int64_t kt = (n0 + 128 * wn) / 128;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t r = m0 + tr_row(wm, i, q, lane);
-                const int64_t off = (((r / 128) * row_kt + kt) * 32 + (r % 32)) * 16 + ((r % 128) / 32) * 4;
-                *reinterpret_cast<uint32_t *>(p.sfd_row + off) = rword[i][q];
-            }
+            const int64_t r = m0 + acc_row(wm, i, lane);
+            const int64_t off = (((r / 128) * row_kt + kt) * 32 + (r % 32)) * 16 + ((r % 128) / 32) * 4;
+            *reinterpret_cast<uint32_t *>(p.sfd_row + off) = rword[i];
         }
     }
 }
 
-template <int F, int EPI>
+template <int F, int EPI, bool CLAMP>
 __global__ void __launch_bounds__(256) k_grouped(GroupedParams p)
 {
     BSG_DECLARE_RING(F, ring);
@@ -271,55 +378,9 @@ __global__ void __launch_bounds__(256) k_grouped(GroupedParams p)
 
     const float alpha = p.alpha[g];
     if constexpr (EPI == EPI_SRELU_FP8) {
-        epilogue_srelu_fp8(p, acc, m0, n0, alpha, wm, wn, lane);
+        epilogue_srelu_fp8<CLAMP>(p, acc, m0, n0, alpha, wm, wn, lane);
     } else {
-        float lmax = 0.0f;
-        transpose_acc<4>(acc, lane);
-        static_for<4>([&](auto ii) {
-            constexpr int i = decltype(ii)::value;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t r = m0 + tr_row(wm, i, q, lane);
-                const float pr = p.prob[r];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int64_t c = n0 + tr_col<4>(wn, j, lane);
-                    if (c >= p.n) continue;         // N is a multiple of 8: runs of 4 are whole
-                    const int64_t idx = r * p.n + c;
-                    float cv[4], dv[4];
-                    if constexpr (EPI == EPI_BF16_BIAS) {
-                        // "Grouped GEMM (SM100 BF16)", Operation: with bias C = G + prob*bias,
-                        // D = C; without bias C = G, D = prob*G.
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const float gval = alpha * acc[i][j][4 * q + u];
-                            if (p.bias) {
-                                cv[u] = gval + pr * load_elem(p.bias, (int64_t)g * p.n + c + u, p.bias_dtype);
-                                dv[u] = cv[u];
-                            } else {
-                                cv[u] = gval;
-                                dv[u] = pr * gval;
-                            }
-                        }
-                        if (p.c) store4(p.c, idx, cv, p.c_dtype);
-                        store4(p.d, idx, dv, p.d_dtype);
-                    } else {
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            cv[u] = alpha * acc[i][j][4 * q + u];
-                            dv[u] = srelu_value(cv[u], pr, p.tanh_s, p.tanh_inv_s);
-                            lmax = fmaxf(lmax, fabsf(dv[u]));
-                        }
-                        if (p.c) store4(p.c, idx, cv, p.c_dtype);
-                        store4(p.d, idx, dv, p.d_dtype);
-                        if (p.d_col) store4(p.d_col, idx, dv, p.d_dtype);
-                    }
-                }
-            }
-        });
-        if constexpr (EPI == EPI_SRELU) {
-            if (p.amax) block_amax_atomic(lmax, p.amax + g, red);
-        }
+        epilogue_grouped<EPI, CLAMP>(p, acc, m0, n0, g, alpha, wm, wn, lane, red);
     }
 }
 
@@ -344,8 +405,17 @@ hipError_t launch_grouped_gemm(const GroupedArgs &a, hipStream_t s)
     if (a.m == 0 || a.n == 0) return hipSuccess;
     GroupedParams p = grouped_params(a);
     dim3 grid((unsigned)((a.n + kTileN - 1) / kTileN), (unsigned)(a.m / kTileM));
-    hipLaunchKernelGGL((k_grouped<FMT_BF16, EPI_BF16_BIAS>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((k_grouped<FMT_BF16, EPI_BF16_BIAS, false>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
+}
+
+template <int F, int EPI>
+static void launch_srelu_variant(const GroupedParams &p, dim3 grid, hipStream_t s)
+{
+    if (p.tanh_s > 0.0f)
+        hipLaunchKernelGGL((k_grouped<F, EPI, true>), grid, dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((k_grouped<F, EPI, false>), grid, dim3(kThreads), 0, s, p);
 }
 
 hipError_t launch_grouped_srelu(const GroupedArgs &a, hipStream_t s)
@@ -357,11 +427,12 @@ hipError_t launch_grouped_srelu(const GroupedArgs &a, hipStream_t s)
     dim3 grid((unsigned)((a.n + kTileN - 1) / kTileN), (unsigned)(a.m / kTileM));
     if (a.d_dtype == DT_E4M3) {
         if (a.fmt != FMT_E4M3) return hipErrorNotSupported;
-        hipLaunchKernelGGL((k_grouped<FMT_E4M3, EPI_SRELU_FP8>), grid, dim3(kThreads), 0, s, p);
-    } else if (a.fmt == FMT_E4M3)
-        hipLaunchKernelGGL((k_grouped<FMT_E4M3, EPI_SRELU>), grid, dim3(kThreads), 0, s, p);
-    else
-        hipLaunchKernelGGL((k_grouped<FMT_E2M1, EPI_SRELU>), grid, dim3(kThreads), 0, s, p);
+        launch_srelu_variant<FMT_E4M3, EPI_SRELU_FP8>(p, grid, s);
+    } else if (a.fmt == FMT_E4M3) {
+        launch_srelu_variant<FMT_E4M3, EPI_SRELU>(p, grid, s);
+    } else {
+        launch_srelu_variant<FMT_E2M1, EPI_SRELU>(p, grid, s);
+    }
     return hipGetLastError();
 }
 

@@ -5,10 +5,11 @@
 // Y = x W^T with the BF16 32x32x16 MFMA (fp32 accumulation); the waves are
 // 2 (tokens) x 2 (features: 0..95 and 96..191).  The second feature wave
 // holds the rotary part (features 128..191) in two 32-column accumulator
-// blocks, applies the interleaved-in / halves-out rotation in registers
-// (pair (2j, 2j+1) -> outputs j and 32+j, exchanged across lanes), then
-// every wave quantises its blocks to E4M3 with E8M0 scales: 32-wide blocks
-// along the head dimension (row) and 32-tall blocks along tokens (column).
+// blocks and applies the interleaved-in / halves-out rotation in registers
+// (pair (2j, 2j+1) -> outputs j and 32+j), then every wave quantises its
+// blocks to E4M3 with E8M0 scales: 32-wide blocks along the head dimension
+// (row) and 32-tall blocks along tokens (column).  All cos/sin loads happen
+// before the first store.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -27,7 +28,7 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
 {
-    constexpr int HD = 192, NOPE = 128, HALF = 32, ROPE = 64, NBLK = HD / 32;
+    constexpr int HD = 192, HALF = 32, ROPE = 64, NBLK = HD / 32;
     BSG_DECLARE_RING(FMT_BF16, ring);
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
     const int c32 = lane & 31, gh = lane >> 5;
@@ -42,89 +43,109 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
                   0, 0, 0, 0, 0};
     f32x16 acc[4][3];
     mainloop_pipe<FMT_BF16, 3>(acc, ring, A, B, p.q_lora);
-
-    transpose_acc<3>(acc, lane);
-    // Transposed layout: element 4q+u of block (i, j) in lane (k, t, g) is token
-    // 32i + 8q + 4g + t of the wave's rows, feature 96wn + 32j + 4k + u.
-    const int k4 = 4 * (c32 >> 2);
+    // Block (i, j) lane (c, g) register 4q+u: token 32i + c of the wave's rows,
+    // head feature 96wn + 32j + 8q + 4g + u.
 
     // ---- RoPE on features 128..191 (wave wn = 1, blocks j = 1 and 2) ----
-    // Output feature c of the rotated half pairs rope inputs 2c and 2c+1;
-    // for output run 4k..4k+3 those are inputs 8k..8k+7 (mod 32), held by
-    // lanes 2k and 2k+1 (mod 8) of the same row, in block 1 for k < 4 and
-    // block 2 otherwise.
+    // Rotary position P of a token is held by block 1 + P/32, register group
+    // (P%32)/8, half ((P%8)/4), element P%4.  Output position q8 = 8q + 4g + u
+    // pairs inputs 2*q8 and 2*q8 + 1: block 1 + q/2, register group
+    // 2(q%2) + g, half u/2, elements 2(u%2) and 2(u%2) + 1.  Each lane fetches
+    // the other half's registers of both blocks, then picks pairs in-lane.
     if (wn == 1) {
-        const int kk = c32 >> 2;
-        const int src0 = 4 * ((2 * kk) & 7) + (lane & 3) + 32 * gh, src1 = src0 + 4;
-        const bool lo = kk < 4;
+        const bool hi = gh == 1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            const int64_t row = m0 + acc_row(wm, i, lane);
+            const int64_t tr = row < p.tokens ? row : 0;
+            float cs0[16], sn0[16], cs1[16], sn1[16];      // cos/sin at q8 and 32 + q8
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                float e[8];                               // rope inputs 8k'..8k'+7 of this row
+                const int q8 = 8 * q + 4 * gh;
+                const uint2 c0 = *reinterpret_cast<const uint2 *>(p.cos + tr * ROPE + q8);
+                const uint2 s0 = *reinterpret_cast<const uint2 *>(p.sin + tr * ROPE + q8);
+                const uint2 c1 = *reinterpret_cast<const uint2 *>(p.cos + tr * ROPE + HALF + q8);
+                const uint2 s1 = *reinterpret_cast<const uint2 *>(p.sin + tr * ROPE + HALF + q8);
+                cs0[4 * q] = bf16_lo(c0.x); cs0[4 * q + 1] = bf16_hi(c0.x); cs0[4 * q + 2] = bf16_lo(c0.y); cs0[4 * q + 3] = bf16_hi(c0.y);
+                sn0[4 * q] = bf16_lo(s0.x); sn0[4 * q + 1] = bf16_hi(s0.x); sn0[4 * q + 2] = bf16_lo(s0.y); sn0[4 * q + 3] = bf16_hi(s0.y);
+                cs1[4 * q] = bf16_lo(c1.x); cs1[4 * q + 1] = bf16_hi(c1.x); cs1[4 * q + 2] = bf16_lo(c1.y); cs1[4 * q + 3] = bf16_hi(c1.y);
+                sn1[4 * q] = bf16_lo(s1.x); sn1[4 * q + 1] = bf16_hi(s1.x); sn1[4 * q + 2] = bf16_lo(s1.y); sn1[4 * q + 3] = bf16_hi(s1.y);
+            }
+            float own[2][16], oth[2][16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                own[0][v] = acc[i][1][v];
+                own[1][v] = acc[i][2][v];
+                oth[0][v] = xor32(own[0][v]);
+                oth[1][v] = xor32(own[1][v]);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const float x1 = __shfl(acc[i][1][4 * q + u], src0), x2 = __shfl(acc[i][2][4 * q + u], src0);
-                    const float y1 = __shfl(acc[i][1][4 * q + u], src1), y2 = __shfl(acc[i][2][4 * q + u], src1);
-                    e[u] = lo ? x1 : x2;
-                    e[4 + u] = lo ? y1 : y2;
-                }
-                const int64_t row = m0 + tr_row(wm, i, q, lane);
-                const int64_t tr = row < p.tokens ? row : 0;
-                const uint2 cw0 = *reinterpret_cast<const uint2 *>(p.cos + tr * ROPE + k4);
-                const uint2 sw0 = *reinterpret_cast<const uint2 *>(p.sin + tr * ROPE + k4);
-                const uint2 cw1 = *reinterpret_cast<const uint2 *>(p.cos + tr * ROPE + HALF + k4);
-                const uint2 sw1 = *reinterpret_cast<const uint2 *>(p.sin + tr * ROPE + HALF + k4);
-                const float c0[4] = {bf16_lo(cw0.x), bf16_hi(cw0.x), bf16_lo(cw0.y), bf16_hi(cw0.y)};
-                const float s0[4] = {bf16_lo(sw0.x), bf16_hi(sw0.x), bf16_lo(sw0.y), bf16_hi(sw0.y)};
-                const float c1[4] = {bf16_lo(cw1.x), bf16_hi(cw1.x), bf16_lo(cw1.y), bf16_hi(cw1.y)};
-                const float s1[4] = {bf16_lo(sw1.x), bf16_hi(sw1.x), bf16_lo(sw1.y), bf16_hi(sw1.y)};
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float a = e[2 * u], b = e[2 * u + 1];
-                    acc[i][1][4 * q + u] = a * c0[u] - b * s0[u];
-                    acc[i][2][4 * q + u] = b * c1[u] + a * s1[u];
+                    const int b = q / 2, qb = 2 * (q % 2), ue = 2 * (u % 2);
+                    // register of the pair in the holding half: group qb + g (this lane's g)
+                    const float lo0 = own[b][4 * qb + ue], lo1 = own[b][4 * qb + ue + 1];
+                    const float hi0 = own[b][4 * (qb + 1) + ue], hi1 = own[b][4 * (qb + 1) + ue + 1];
+                    const float olo0 = oth[b][4 * qb + ue], olo1 = oth[b][4 * qb + ue + 1];
+                    const float ohi0 = oth[b][4 * (qb + 1) + ue], ohi1 = oth[b][4 * (qb + 1) + ue + 1];
+                    // holder half is u/2: this lane when u/2 == g, else the other half
+                    float ea, eb;
+                    if (u / 2 == 0) {
+                        ea = hi ? ohi0 : lo0;
+                        eb = hi ? ohi1 : lo1;
+                    } else {
+                        ea = hi ? hi0 : olo0;
+                        eb = hi ? hi1 : olo1;
+                    }
+                    const int v = 4 * q + u;
+                    acc[i][1][v] = ea * cs0[v] - eb * sn0[v];
+                    acc[i][2][v] = eb * cs1[v] + ea * sn1[v];
                 }
             }
         }
     }
-    (void)NOPE;
 
     // ---- dual MXFP8 quantisation (norm_const 1) ----
     static_for<3>([&](auto jj) {
         constexpr int j = decltype(jj)::value;
         const int blk = 3 * wn + j;                      // 32-feature block within the head
-        const int64_t col = h * HD + 32 * blk + k4;      // first of this lane's 4 feature columns
         static_for<4>([&](auto ii) {
             constexpr int i = decltype(ii)::value;
+            const f32x16 &a = acc[i][j];
             const int64_t rbase = m0 + 128 * wm + 32 * i;   // first token of this 32-token block
             const bool blk_ok = rbase < p.tokens;            // tokens % 128 == 0: blocks are whole
-            // column direction: 32 tokens of one feature
-            float cm[4], cinv[4];
-            tr_col_absmax(acc[i][j], cm);
-            uint32_t cb[4];
+            const int64_t row = m0 + acc_row(wm, i, lane);
+            // row direction: 32 features of one token (this lane and lane ^ 32)
+            float rm = 0.0f;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) cb[u] = mx_scale_byte(cm[u], 1.0f, cinv[u]);
-            const int t = lane & 3;
-            if (blk_ok && gh == 0)
-                p.s_col[(rbase / 32) * n_out + col + t] =
-                    (uint8_t)(t == 0 ? cb[0] : t == 1 ? cb[1] : t == 2 ? cb[2] : cb[3]);
-            // row direction: 32 features of one token
+            for (int v = 0; v < 16; ++v) rm = fmaxf(rm, fabsf(a[v]));
+            rm = fmaxf(rm, xor32(rm));
+            float rinv;
+            const uint32_t rb = mx_scale_byte(rm, 1.0f, rinv);
+            // column direction: 32 tokens of one feature (a register over the half-wave)
+            float cinv[16];
+            uint32_t cb[16];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float x[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                    acc[i][j][4 * q + 3]};
-                float rm = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
-                rm = row8_max(rm);
-                float rinv;
-                const uint32_t rb = mx_scale_byte(rm, 1.0f, rinv);
-                if (blk_ok) {
-                    const int64_t row = m0 + tr_row(wm, i, q, lane);
+            for (int v = 0; v < 16; ++v) cb[v] = mx_scale_byte(half_wave_max(fabsf(a[v])), 1.0f, cinv[v]);
+            if (blk_ok) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t col = h * HD + 32 * blk + 8 * q + 4 * gh;
                     *reinterpret_cast<uint32_t *>(p.q_row + row * n_out + col) =
-                        pack4_e4m3(x[0] * rinv, x[1] * rinv, x[2] * rinv, x[3] * rinv);
+                        pack4_e4m3(a[4 * q] * rinv, a[4 * q + 1] * rinv, a[4 * q + 2] * rinv, a[4 * q + 3] * rinv);
                     *reinterpret_cast<uint32_t *>(p.q_col + row * n_out + col) =
-                        pack4_e4m3(x[0] * cinv[0], x[1] * cinv[1], x[2] * cinv[2], x[3] * cinv[3]);
-                    if (c32 < 4) p.s_row[(row * p.heads + h) * NBLK + blk] = (uint8_t)rb;
+                        pack4_e4m3(a[4 * q] * cinv[4 * q], a[4 * q + 1] * cinv[4 * q + 1],
+                                   a[4 * q + 2] * cinv[4 * q + 2], a[4 * q + 3] * cinv[4 * q + 3]);
+                }
+                if (gh == 0) p.s_row[(row * p.heads + h) * NBLK + blk] = (uint8_t)rb;
+                // lane c < 16 of each half writes the scale of its register c
+                uint32_t byte = cb[0];
+#pragma unroll
+                for (int v = 1; v < 16; ++v) byte = c32 == v ? cb[v] : byte;
+                if (c32 < 16) {
+                    const int64_t col = h * HD + 32 * blk + 8 * (c32 >> 2) + 4 * gh + (c32 & 3);
+                    p.s_col[(rbase / 32) * n_out + col] = (uint8_t)byte;
                 }
             }
         });
