@@ -109,6 +109,17 @@ int bsg_version(void) { return 100; }
 // ---------------------------------------------------------------------------
 // gemm_amax
 // ---------------------------------------------------------------------------
+// Launch-shape limits shared by every GEMM: one workgroup per 256x256 tile in
+// a 1-D grid (under 2^24 workgroups of 256 threads), 32 output rows of at
+// most 4 bytes per element addressable with 32-bit offsets.
+static int check_tiles(int64_t m_tiles, int64_t n, int64_t l)
+{
+    const int64_t tiles = m_tiles * ((n + 255) / 256) * l;
+    if (tiles >= (1ll << 24)) return fail(BSG_ERR_UNSUPPORTED, "%lld output tiles exceed the launch limit", (long long)tiles);
+    if (n * 4 * 32 >= (1ll << 31)) return fail(BSG_ERR_UNSUPPORTED, "N=%lld too large for 32-bit row offsets", (long long)n);
+    return BSG_OK;
+}
+
 int bsg_validate_gemm_amax(const void *a, const void *b, const uint8_t *sfa, const uint8_t *sfb,
                            void *c, float *amax, int64_t m, int64_t n, int64_t k, int64_t l,
                            int ab_dtype, int c_dtype, int sf_vec_size)
@@ -130,7 +141,7 @@ int bsg_validate_gemm_amax(const void *a, const void *b, const uint8_t *sfa, con
         return fail(BSG_ERR_ALIGN, "C must be 16-byte aligned with N*sizeof(C) a multiple of 16");
     if ((int64_t)row_bytes(ab_dtype, k) * 256 >= (1ll << 31))
         return fail(BSG_ERR_UNSUPPORTED, "K too large for 32-bit tile offsets");
-    return BSG_OK;
+    return check_tiles((m + 255) / 256, n, l);
 }
 
 int gemm_amax(const void *a, const void *b, const uint8_t *sfa, const uint8_t *sfb, void *c,
@@ -161,7 +172,7 @@ static int check_grouped_common(const void *a, const void *b, const int32_t *off
     if (m * n == 0) return BSG_OK;
     if (!a || !b || !d) return fail(BSG_ERR_NULLPTR, "a, b and d are required");
     if (k > 0 && (!aligned16(a) || !aligned16(b))) return fail(BSG_ERR_ALIGN, "A and B must be 16-byte aligned");
-    return BSG_OK;
+    return check_tiles(m / 256, n, 1);
 }
 
 // ---------------------------------------------------------------------------

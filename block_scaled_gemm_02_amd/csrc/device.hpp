@@ -117,6 +117,41 @@ __device__ __forceinline__ i32x4 sanitize_scales(i32x4 w, int kt, int kblocks)
 }
 
 // ---------------------------------------------------------------------------
+// Tile order: XCD-aware
+// ---------------------------------------------------------------------------
+// MI355X has 8 XCDs of 32 CUs, each with its own L2; workgroup b of a launch
+// goes to XCD b % 8, and (one 147 KB-LDS workgroup per CU) each XCD runs 32
+// tiles at a time.  Launch index b is mapped to a tile sequence number s so
+// that every XCD works through runs of 32 consecutive s, and s walks the
+// tiles in groups of 8 m-tiles, column by column: an XCD's 32 concurrent
+// tiles are then 8 m-tiles x 4 n-tiles and share 8 A panels and 4 B panels
+// in its L2 (a row-major order gave each XCD 16 m-tiles x 2 n-tiles, with
+// every A panel fetched by all 8 XCDs).  The last partial round keeps b.
+constexpr int kXcds = 8, kCusPerXcd = 32, kGroupM = 8;
+
+struct TileCoord {
+    int64_t l, mt, nt;
+};
+__device__ __forceinline__ TileCoord tile_of(int64_t b, int64_t m_t, int64_t n_t, int64_t tiles)
+{
+    constexpr int64_t R = kXcds * kCusPerXcd;
+    int64_t s = b;
+    if (b < tiles - tiles % R) {
+        const int64_t x = b % kXcds, li = b / kXcds;
+        s = (li / kCusPerXcd) * R + x * kCusPerXcd + li % kCusPerXcd;
+    }
+    TileCoord t;
+    const int64_t per_l = m_t * n_t;
+    t.l = s / per_l;
+    const int64_t sl = s % per_l;
+    const int64_t grp = sl / (kGroupM * n_t), r = sl % (kGroupM * n_t);
+    const int64_t gm = m_t - grp * kGroupM < kGroupM ? m_t - grp * kGroupM : kGroupM;
+    t.mt = grp * kGroupM + r % gm;
+    t.nt = r / gm;
+    return t;
+}
+
+// ---------------------------------------------------------------------------
 // K loop: a 4-stage LDS ring filled by direct-to-LDS buffer loads
 // ---------------------------------------------------------------------------
 // Scale-atom addressing ("Block-scaled GEMM + amax", scale factor layout):
@@ -532,6 +567,105 @@ __device__ __forceinline__ float half_wave_max(float x)
     x = fmaxf(x, dpp_mov<0x141>(x));   // row_half_mirror
     x = fmaxf(x, dpp_mov<0x140>(x));   // row_mirror
     return fmaxf(x, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F)));  // lane ^ 16
+}
+
+// ---------------------------------------------------------------------------
+// Output staging through LDS
+// ---------------------------------------------------------------------------
+// After the K loop the ring is free.  Each wave stages one 32-row block of
+// its 128 x (32*NB) quadrant at a time in its own ring slot, in the
+// accumulator layout, then reads it back row-major, 16 bytes per lane, and
+// stores whole row segments: every 128-byte line of the output is written by
+// one instruction.  Storing straight from the accumulator layout writes 8- or
+// 16-byte pieces of 32 rows per instruction, and those partial lines raised
+// the HBM write traffic by half again.  ES is the output element size (1, 2
+// or 4 bytes); staged rows are 16 bytes longer than the data so that the 32
+// rows one write instruction touches start on different banks.
+template <int ES, int NB>
+struct StageGeom {
+    static constexpr int RB = 32 * NB * ES;          // data bytes per row
+    static constexpr int RBP = RB + 16;              // staged row stride
+    static constexpr int LPR = RB / 16;              // lanes per row when reading back
+    static constexpr int RPI = 64 / LPR;             // rows per read instruction
+    static constexpr int NK = (32 + RPI - 1) / RPI;  // read instructions per 32 rows
+    static_assert(RB % 16 == 0 && LPR <= 64, "rows are whole 16-byte chunks");
+};
+
+// Four consecutive output elements (columns 4k..4k+3 of a row) as stored.
+template <int ES> struct Quad;
+template <> struct Quad<1> { typedef uint32_t T; };
+template <> struct Quad<2> { typedef uint2 T; };
+template <> struct Quad<4> { typedef float4 T; };
+
+// Packs four output values for output type DT.
+template <int DT>
+__device__ __forceinline__ typename Quad<DT == DT_F32 ? 4 : 2>::T pack_quad(float x0, float x1, float x2,
+                                                                             float x3)
+{
+    if constexpr (DT == DT_F32) return make_float4(x0, x1, x2, x3);
+    else if constexpr (DT == DT_BF16) return make_uint2(pack2_bf16(x0, x1), pack2_bf16(x2, x3));
+    else return make_uint2(pack2_f16(x0, x1), pack2_f16(x2, x3));
+}
+
+// Stores the staged 32 rows: row r goes to dst + r*row_bytes, through a
+// buffer resource over the valid rows (at most 32), so rows past M -- and the
+// rows past 32 that a last partial read instruction covers -- fall outside its
+// range and are dropped; lanes whose 16-byte chunk starts at or past
+// col_bytes, or that hold no row, are pointed out of range as well.  The
+// output rows are multiples of 16 bytes, so a chunk is all in or all out.
+template <int ES, int NB>
+__device__ __forceinline__ void stage_flush(const uint8_t *reg, char *dst, uint32_t row_bytes, int rows,
+                                            int col_bytes, int lane)
+{
+    typedef StageGeom<ES, NB> G;
+    if (rows <= 0) return;
+    const int lr = lane / G::LPR, cb = (lane % G::LPR) * 16;
+    const uint8_t *src = reg + lr * G::RBP + cb;
+    const uint32_t nrec = (uint32_t)(rows < 32 ? rows : 32) * row_bytes;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(dst, (short)0, (int)nrec, 0x00020000);
+    const uint32_t voff = (cb < col_bytes && lr < G::RPI) ? (uint32_t)lr * row_bytes + (uint32_t)cb : kOOB;
+#pragma unroll
+    for (int k = 0; k < G::NK; ++k) {
+        const i32x4 v = *reinterpret_cast<const i32x4 *>(src + k * G::RPI * G::RBP);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, voff + (uint32_t)(k * G::RPI) * row_bytes, 0, 0);
+    }
+}
+
+// Writes one output of a wave's 128 x (32*NB) quadrant through LDS:
+// value(i, j, v, acc) gives the element of register v of block (i, j).  dst
+// (and dst2, if non-null) point at element (0, 0) of the quadrant;
+// rows_valid and cols_valid bound it (ragged M / N).
+template <int DT, int NB, class Fn>
+__device__ __forceinline__ void store_quadrant(uint8_t *reg, char *dst, char *dst2, uint32_t row_bytes,
+                                               int rows_valid, int cols_valid, f32x16 (&acc)[4][NB],
+                                               int lane, Fn &&value)
+{
+    constexpr int ES = DT == DT_F32 ? 4 : 2;
+    typedef StageGeom<ES, NB> G;
+    const int c = lane & 31, g = lane >> 5;
+    uint8_t *wrow = reg + c * G::RBP + 4 * g * ES;
+    static_for<4>([&](auto ii) {
+        constexpr int i = decltype(ii)::value;
+        // keep the scheduler from hoisting later blocks' accumulator reads
+        // and arithmetic into this one (the register pressure spills)
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<NB>([&](auto jj) {
+            constexpr int j = decltype(jj)::value;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float x0 = value(i, j, 4 * q, acc[i][j][4 * q]);
+                const float x1 = value(i, j, 4 * q + 1, acc[i][j][4 * q + 1]);
+                const float x2 = value(i, j, 4 * q + 2, acc[i][j][4 * q + 2]);
+                const float x3 = value(i, j, 4 * q + 3, acc[i][j][4 * q + 3]);
+                *reinterpret_cast<typename Quad<ES>::T *>(wrow + (32 * j + 8 * q) * ES) =
+                    pack_quad<DT>(x0, x1, x2, x3);
+            }
+        });
+        const int rows = rows_valid - 32 * i;
+        stage_flush<ES, NB>(reg, dst + (uint32_t)(32 * i) * row_bytes, row_bytes, rows, cols_valid * ES, lane);
+        if (dst2)
+            stage_flush<ES, NB>(reg, dst2 + (uint32_t)(32 * i) * row_bytes, row_bytes, rows, cols_valid * ES, lane);
+    });
 }
 
 // Value of x in lane l ^ 32.

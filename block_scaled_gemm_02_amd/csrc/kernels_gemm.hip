@@ -42,54 +42,34 @@ static inline uint32_t row_bytes_of(int fmt, int64_t k)
     return (uint32_t)(fmt == FMT_E2M1 ? k / 2 : (fmt == FMT_BF16 ? 2 * k : k));
 }
 
-// Stores one 256 x 256 output tile from the accumulators: value(i, j, v, acc)
-// gives the output for register v of block (i, j).  Addresses are a uniform
-// tile base plus a 32-bit per-lane row offset (so 256 rows of the output
-// span less than 4 GiB); the block/run part is an immediate.  Runs past N
-// (a multiple of 4) and rows at or past `rows` are skipped.
-template <int DT, class Fn>
-__device__ __forceinline__ void store_tile(void *base, void *base2, int64_t n, int64_t m0, int64_t n0, int wm,
-                                           int wn, int lane, const f32x16 (&acc)[4][4], int64_t rows,
-                                           Fn &&value)
+// One output of a wave's 128 x (32*NB) quadrant through the wave's LDS
+// staging region: dispatches on the run-time output type.  (row0, col0) is
+// the quadrant's first element; rows_valid / cols_valid bound it.
+template <int NB, class Fn>
+__device__ __forceinline__ void store_quadrant_rt(int dt, uint8_t *reg, void *base, void *base2, int64_t n,
+                                                  int64_t row0, int64_t col0, int rows_valid, int cols_valid,
+                                                  f32x16 (&acc)[4][NB], int lane, Fn &&value)
 {
-    constexpr int ES = DT == DT_F32 ? 4 : 2;
-    char *tile = static_cast<char *>(base) + (m0 * n + n0) * ES;
-    char *tile2 = base2 ? static_cast<char *>(base2) + (m0 * n + n0) * ES : nullptr;
-    static_for<4>([&](auto ii) {
-        constexpr int i = decltype(ii)::value;
-        const int rl = acc_row(wm, i, lane);
-        if (rl >= rows) return;
-        const uint32_t roff = (uint32_t)rl * (uint32_t)n * ES;
-        static_for<4>([&](auto jj) {
-            constexpr int j = decltype(jj)::value;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int cl = acc_col<4>(wn, j, q, lane);
-                if (n0 + cl >= n) continue;
-                float x[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) x[u] = value(i, j, 4 * q + u, acc[i][j][4 * q + u]);
-                const uint32_t off = roff + (uint32_t)cl * ES;
-                store4<DT>(tile + off, 0, x[0], x[1], x[2], x[3]);
-                if (tile2) store4<DT>(tile2 + off, 0, x[0], x[1], x[2], x[3]);
-            }
-        });
-    });
-}
-
-template <class Fn>
-__device__ __forceinline__ void store_tile_rt(int dt, void *base, void *base2, int64_t n, int64_t m0, int64_t n0,
-                                              int wm, int wn, int lane, const f32x16 (&acc)[4][4], int64_t rows,
-                                              Fn &&value)
-{
-    if (dt == DT_F32) store_tile<DT_F32>(base, base2, n, m0, n0, wm, wn, lane, acc, rows, value);
-    else if (dt == DT_BF16) store_tile<DT_BF16>(base, base2, n, m0, n0, wm, wn, lane, acc, rows, value);
-    else store_tile<DT_F16>(base, base2, n, m0, n0, wm, wn, lane, acc, rows, value);
+    const int es = dt == DT_F32 ? 4 : 2;
+    char *dst = static_cast<char *>(base) + (row0 * n + col0) * es;
+    char *dst2 = base2 ? static_cast<char *>(base2) + (row0 * n + col0) * es : nullptr;
+    const uint32_t rb = (uint32_t)(n * es);
+    if (dt == DT_F32) store_quadrant<DT_F32, NB>(reg, dst, dst2, rb, rows_valid, cols_valid, acc, lane, value);
+    else if (dt == DT_BF16) store_quadrant<DT_BF16, NB>(reg, dst, dst2, rb, rows_valid, cols_valid, acc, lane, value);
+    else store_quadrant<DT_F16, NB>(reg, dst, dst2, rb, rows_valid, cols_valid, acc, lane, value);
 }
 
 // Waits for every outstanding vector-memory load before the epilogue's first
 // store (see the file comment).
 __device__ __forceinline__ void wait_loads() { s_wait_vm<0>(); }
+
+template <int F>
+__device__ __forceinline__ uint8_t *wave_stage(const RingSlots<F> &ring, int w)
+{
+    return w == 0 ? ring.s0 : (w == 1 ? ring.s1 : (w == 2 ? ring.s2 : ring.s3));
+}
+
+__device__ __forceinline__ int clamp_extent(int64_t extent) { return extent < 0 ? 0 : (extent > 128 ? 128 : (int)extent); }
 
 // ---------------------------------------------------------------------------
 // Dense batched GEMM + global amax
@@ -110,8 +90,10 @@ __global__ void __launch_bounds__(256) k_gemm_amax(GemmAmaxParams p)
     BSG_DECLARE_RING(F, ring);
     __shared__ float red[4];
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
-    const int64_t batch = blockIdx.z;
-    const int64_t m0 = (int64_t)blockIdx.y * kTileM, n0 = (int64_t)blockIdx.x * kTileN;
+    const int64_t m_tiles = (p.m + kTileM - 1) / kTileM, n_tiles = (p.n + kTileN - 1) / kTileN;
+    const TileCoord tc = tile_of(blockIdx.x, m_tiles, n_tiles, (int64_t)gridDim.x);
+    const int64_t batch = tc.l;
+    const int64_t m0 = tc.mt * kTileM, n0 = tc.nt * kTileN;
     const int64_t rows_a = p.m - m0 < kTileM ? p.m - m0 : kTileM;
     const int64_t rows_b = p.n - n0 < kTileN ? p.n - n0 : kTileN;
 
@@ -122,13 +104,17 @@ __global__ void __launch_bounds__(256) k_gemm_amax(GemmAmaxParams p)
     f32x16 acc[4][4];
     mainloop_pipe<F>(acc, ring, A, B, p.k);
 
-    // rows past M (ragged last tile): computed from zero rows of A, not stored
+    // rows past M / columns past N (ragged last tiles) are computed from zero
+    // rows of A / B and not stored
     float lmax = 0.0f;
-    store_tile_rt(p.c_dtype, static_cast<char *>(p.c) + batch * p.m * p.n * (p.c_dtype == DT_F32 ? 4 : 2),
-                  nullptr, p.n, m0, n0, wm, wn, lane, acc, rows_a, [&](int, int, int, float a) {
-                      lmax = fmaxf(lmax, fabsf(a));
-                      return a;
-                  });
+    const int64_t qr = m0 + 128 * wm, qc = n0 + 128 * wn;
+    store_quadrant_rt<4>(p.c_dtype, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)),
+                         static_cast<char *>(p.c) + batch * p.m * p.n * (p.c_dtype == DT_F32 ? 4 : 2), nullptr,
+                         p.n, qr, qc, clamp_extent(p.m - qr), clamp_extent(p.n - qc), acc, lane,
+                         [&](int, int, int, float a) {
+                             lmax = fmaxf(lmax, fabsf(a));
+                             return a;
+                         });
     if (p.amax) block_amax_atomic(lmax, p.amax, red);
 }
 
@@ -143,8 +129,7 @@ hipError_t launch_gemm_amax(const GemmAmaxArgs &a, hipStream_t s)
     p.m_t = (a.m + 127) / 128; p.n_t = (a.n + 127) / 128; p.k_t = (a.k + 127) / 128;
     p.row_bytes = row_bytes_of(a.fmt, a.k);
     p.c_dtype = a.c_dtype;
-    dim3 grid((unsigned)((a.n + kTileN - 1) / kTileN), (unsigned)((a.m + kTileM - 1) / kTileM),
-              (unsigned)a.l);
+    dim3 grid((unsigned)(((a.n + kTileN - 1) / kTileN) * ((a.m + kTileM - 1) / kTileM) * a.l));
     if (a.fmt == FMT_E4M3)
         hipLaunchKernelGGL(k_gemm_amax<FMT_E4M3>, grid, dim3(kThreads), 0, s, p);
     else
@@ -197,12 +182,12 @@ __device__ __forceinline__ float srelu_value(float gval, float pr, float s, floa
 }
 
 // BF16 bias epilogue and sReLU epilogue with 16/32-bit outputs: C, then D
-// (and D_col, which equals D for unquantised outputs), each pass with its
-// own compile-time store type.
+// (and D_col, which equals D for unquantised outputs), each staged through
+// the wave's LDS region with its own compile-time store type.
 template <int EPI, bool CLAMP>
-__device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, const f32x16 (&acc)[4][4],
-                                                 int64_t m0, int64_t n0, int g, float alpha, int wm,
-                                                 int wn, int lane, float *red)
+__device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, f32x16 (&acc)[4][4],
+                                                 uint8_t *stage, int64_t m0, int64_t n0, int g, float alpha,
+                                                 int wm, int wn, int lane, float *red)
 {
     const int64_t n = p.n;
     float pr[4];
@@ -226,16 +211,19 @@ __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, const f
     wait_loads();
     // "Grouped GEMM (SM100 BF16)", Operation: with bias C = G + prob*bias,
     // D = C; without bias C = G, D = prob*G.  sReLU: C = G, D = sReLU(G).
+    const int64_t qr = m0 + 128 * wm, qc = n0 + 128 * wn;
+    const int cols = clamp_extent(n - qc);
     if (p.c) {
-        store_tile_rt(p.c_dtype, p.c, nullptr, n, m0, n0, wm, wn, lane, acc, kTileM, [&](int i, int j, int v, float a) {
+        store_quadrant_rt<4>(p.c_dtype, stage, p.c, nullptr, n, qr, qc, 128, cols, acc, lane,
+                             [&](int i, int j, int v, float a) {
             const float gval = alpha * a;
             if constexpr (EPI == EPI_BF16_BIAS) return has_bias ? gval + pr[i] * bv[j][v] : gval;
             else return gval;
         });
     }
     float lmax = 0.0f;
-    store_tile_rt(p.d_dtype, p.d, EPI == EPI_BF16_BIAS ? nullptr : p.d_col, n, m0, n0, wm, wn, lane, acc,
-                  kTileM, [&](int i, int j, int v, float a) {
+    store_quadrant_rt<4>(p.d_dtype, stage, p.d, EPI == EPI_BF16_BIAS ? nullptr : p.d_col, n, qr, qc, 128, cols,
+                         acc, lane, [&](int i, int j, int v, float a) {
         const float gval = alpha * a;
         if constexpr (EPI == EPI_BF16_BIAS) {
             return has_bias ? gval + pr[i] * bv[j][v] : pr[i] * gval;
@@ -257,104 +245,86 @@ __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, const f
 //
 // A row's 32 values of block j sit in this lane (16) and lane ^ 32 (16); a
 // column's 32 values of block i sit in one register of the 32 lanes of a
-// half-wave.  C (pre-activation) is written first when requested; D then
-// replaces the accumulators.
+// half-wave.  C (pre-activation) is written first when requested.  Then, one
+// 32-row block at a time, D is formed in registers, both code arrays are
+// staged in the wave's LDS region and stored as whole rows, and the scale
+// bytes are written: SFD_row as one word per row (the wave's four 32-column
+// blocks are one K' group), SFD_col byte by byte.
 template <bool CLAMP>
 __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x16 (&acc)[4][4],
-                                                   int64_t m0, int64_t n0, float alpha, int wm,
-                                                   int wn, int lane)
+                                                   uint8_t *stage, int64_t m0, int64_t n0, float alpha,
+                                                   int wm, int wn, int lane)
 {
+    typedef StageGeom<1, 4> G;
     const float nc = *p.norm_const;
     const int64_t n = p.n;
     const int64_t row_kt = (n / 32 + 3) / 4;          // SFD_row: K' over N
     const int64_t col_kt = (p.m / 32 + 3) / 4;        // SFD_col: K' over M
-    uint8_t *dq = static_cast<uint8_t *>(p.d);
-    uint8_t *dc = static_cast<uint8_t *>(p.d_col);
     const int c32 = lane & 31, gh = lane >> 5;
+    const int64_t qr = m0 + 128 * wm, qc = n0 + 128 * wn;
+    const int cols = clamp_extent(n - qc);
 
     float pr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) pr[i] = p.prob[m0 + acc_row(wm, i, lane)];
     wait_loads();
+    if (p.c) {
+        store_quadrant_rt<4>(p.c_dtype, stage, p.c, nullptr, n, qr, qc, 128, cols, acc, lane,
+                             [&](int, int, int, float a) { return alpha * a; });
+    }
+
+    uint8_t *sd = stage, *sdc = stage + 32 * G::RBP;
+    uint8_t *wd = sd + c32 * G::RBP + 4 * gh, *wdc = sdc + c32 * G::RBP + 4 * gh;
+    const int64_t mt = qr / 128;
     static_for<4>([&](auto ii) {
         constexpr int i = decltype(ii)::value;
-        const int64_t r = m0 + acc_row(wm, i, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t rword = 0u;                          // SFD_row bytes j = 0..3 of row 32i + c
         static_for<4>([&](auto jj) {
             constexpr int j = decltype(jj)::value;
+            float d[16];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float x[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) x[u] = alpha * acc[i][j][4 * q + u];
-                const int64_t c = n0 + acc_col<4>(wn, j, q, lane);
-                if (p.c && c < n) store4_rt(p.c, r * n + c, x[0], x[1], x[2], x[3], p.c_dtype);
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    acc[i][j][4 * q + u] = srelu_value<CLAMP>(x[u], pr[i], p.tanh_s, p.tanh_inv_s);
-            }
-        });
-    });
-
-    uint32_t rword[4] = {0u, 0u, 0u, 0u};            // SFD_row bytes j = 0..3 of row i*32 + c
-    static_for<4>([&](auto jj) {
-        constexpr int j = decltype(jj)::value;
-        uint32_t cword[16];                           // SFD_col bytes i = 0..3 of each column
-#pragma unroll
-        for (int v = 0; v < 16; ++v) cword[v] = 0u;
-        static_for<4>([&](auto ii) {
-            constexpr int i = decltype(ii)::value;
-            const f32x16 &a = acc[i][j];
+            for (int v = 0; v < 16; ++v) d[v] = srelu_value<CLAMP>(alpha * acc[i][j][v], pr[i], p.tanh_s, p.tanh_inv_s);
             // row block: this lane's 16 columns and the partner half's 16
             float rm = 0.0f;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) rm = fmaxf(rm, fabsf(a[v]));
+            for (int v = 0; v < 16; ++v) rm = fmaxf(rm, fabsf(d[v]));
             rm = fmaxf(rm, xor32(rm));
             float rinv;
-            rword[i] |= mx_scale_byte(rm, nc, rinv) << (8 * j);
+            rword |= mx_scale_byte(rm, nc, rinv) << (8 * j);
             // column blocks: 32 rows of each column over the half-wave
             float cinv[16];
+            uint32_t cb[16];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float cm = half_wave_max(fabsf(a[v]));
-                cword[v] |= mx_scale_byte(cm, nc, cinv[v]) << (8 * i);
-            }
-            const int64_t r = m0 + acc_row(wm, i, lane);
+            for (int v = 0; v < 16; ++v) cb[v] = mx_scale_byte(half_wave_max(fabsf(d[v])), nc, cinv[v]);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int64_t c = n0 + acc_col<4>(wn, j, q, lane);
-                if (c < n) {
-                    *reinterpret_cast<uint32_t *>(dq + r * n + c) =
-                        pack4_e4m3(a[4 * q] * rinv, a[4 * q + 1] * rinv, a[4 * q + 2] * rinv, a[4 * q + 3] * rinv);
-                    *reinterpret_cast<uint32_t *>(dc + r * n + c) =
-                        pack4_e4m3(a[4 * q] * cinv[4 * q], a[4 * q + 1] * cinv[4 * q + 1],
-                                   a[4 * q + 2] * cinv[4 * q + 2], a[4 * q + 3] * cinv[4 * q + 3]);
-                }
+                *reinterpret_cast<uint32_t *>(wd + 32 * j + 8 * q) =
+                    pack4_e4m3(d[4 * q] * rinv, d[4 * q + 1] * rinv, d[4 * q + 2] * rinv, d[4 * q + 3] * rinv);
+                *reinterpret_cast<uint32_t *>(wdc + 32 * j + 8 * q) =
+                    pack4_e4m3(d[4 * q] * cinv[4 * q], d[4 * q + 1] * cinv[4 * q + 1],
+                               d[4 * q + 2] * cinv[4 * q + 2], d[4 * q + 3] * cinv[4 * q + 3]);
+            }
+            // SFD_col byte i of column 32j + 8(c/4) + 4g + c%4 (lane c < 16: register c)
+            uint32_t byte = cb[0];
+#pragma unroll
+            for (int v = 1; v < 16; ++v) byte = c32 == v ? cb[v] : byte;
+            const int64_t col = qc + 32 * j + 8 * (c32 >> 2) + 4 * gh + (c32 & 3);
+            if (c32 < 16 && col < n) {
+                const int64_t off = (((col / 128) * col_kt + mt) * 32 + (col % 32)) * 16 + ((col % 128) / 32) * 4;
+                p.sfd_col[off + i] = (uint8_t)byte;
             }
         });
-        // SFD_col: lane c < 16 of each half writes the word of its register c,
-        // column 32j + 8(c/4) + 4g + c%4: the wave's four 32-row blocks form one
-        // K' group of the (N, M) atoms
-        uint32_t word = cword[0];
-#pragma unroll
-        for (int v = 1; v < 16; ++v) word = c32 == v ? cword[v] : word;
-        const int64_t col = n0 + acc_col<4>(wn, j, 0, lane) + 8 * (c32 >> 2) + (c32 & 3);
-        if (c32 < 16 && col < n) {
-            const int64_t mt = (m0 + 128 * wm) / 128;
-            const int64_t off = (((col / 128) * col_kt + mt) * 32 + (col % 32)) * 16 + ((col % 128) / 32) * 4;
-            *reinterpret_cast<uint32_t *>(p.sfd_col + off) = word;
+        const uint32_t rb = (uint32_t)n;
+        stage_flush<1, 4>(sd, static_cast<char *>(p.d) + (qr + 32 * i) * n + qc, rb, 32, cols, lane);
+        stage_flush<1, 4>(sdc, static_cast<char *>(p.d_col) + (qr + 32 * i) * n + qc, rb, 32, cols, lane);
+        // SFD_row word of row r; columns past N carry the scale of an all-zero block
+        if (gh == 0 && cols > 0) {
+            const int64_t r = m0 + acc_row(wm, i, lane);
+            const int64_t off = (((r / 128) * row_kt + qc / 128) * 32 + (r % 32)) * 16 + ((r % 128) / 32) * 4;
+            *reinterpret_cast<uint32_t *>(p.sfd_row + off) = rword;
         }
     });
-    // SFD_row: row r, the wave's four 32-column blocks = one K' group of the
-    // (M, N) atoms; blocks past N carry the scale of an all-zero block
-    if (gh == 0 && n0 + 128 * wn < n) {
-        const int64_t kt = (n0 + 128 * wn) / 128;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t r = m0 + acc_row(wm, i, lane);
-            const int64_t off = (((r / 128) * row_kt + kt) * 32 + (r % 32)) * 16 + ((r % 128) / 32) * 4;
-            *reinterpret_cast<uint32_t *>(p.sfd_row + off) = rword[i];
-        }
-    }
 }
 
 template <int F, int EPI, bool CLAMP>
@@ -363,7 +333,8 @@ __global__ void __launch_bounds__(256) k_grouped(GroupedParams p)
     BSG_DECLARE_RING(F, ring);
     __shared__ float red[4];
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
-    const int64_t m0 = (int64_t)blockIdx.y * kTileM, n0 = (int64_t)blockIdx.x * kTileN;
+    const TileCoord tc = tile_of(blockIdx.x, p.m / kTileM, (p.n + kTileN - 1) / kTileN, (int64_t)gridDim.x);
+    const int64_t m0 = tc.mt * kTileM, n0 = tc.nt * kTileN;
     const int64_t valid_m = p.offsets[p.num_experts - 1];
     if (m0 >= valid_m) return;                      // uniform per workgroup
     const int g = expert_of(p.offsets, (int)p.num_experts, m0);
@@ -378,9 +349,11 @@ __global__ void __launch_bounds__(256) k_grouped(GroupedParams p)
 
     const float alpha = p.alpha[g];
     if constexpr (EPI == EPI_SRELU_FP8) {
-        epilogue_srelu_fp8<CLAMP>(p, acc, m0, n0, alpha, wm, wn, lane);
+        epilogue_srelu_fp8<CLAMP>(p, acc, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), m0, n0, alpha,
+                                  wm, wn, lane);
     } else {
-        epilogue_grouped<EPI, CLAMP>(p, acc, m0, n0, g, alpha, wm, wn, lane, red);
+        epilogue_grouped<EPI, CLAMP>(p, acc, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), m0, n0, g,
+                                     alpha, wm, wn, lane, red);
     }
 }
 
@@ -404,7 +377,7 @@ hipError_t launch_grouped_gemm(const GroupedArgs &a, hipStream_t s)
 {
     if (a.m == 0 || a.n == 0) return hipSuccess;
     GroupedParams p = grouped_params(a);
-    dim3 grid((unsigned)((a.n + kTileN - 1) / kTileN), (unsigned)(a.m / kTileM));
+    dim3 grid((unsigned)(((a.n + kTileN - 1) / kTileN) * (a.m / kTileM)));
     hipLaunchKernelGGL((k_grouped<FMT_BF16, EPI_BF16_BIAS, false>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
@@ -424,7 +397,7 @@ hipError_t launch_grouped_srelu(const GroupedArgs &a, hipStream_t s)
     if (e != hipSuccess) return e;
     if (a.m == 0 || a.n == 0) return hipSuccess;
     GroupedParams p = grouped_params(a);
-    dim3 grid((unsigned)((a.n + kTileN - 1) / kTileN), (unsigned)(a.m / kTileM));
+    dim3 grid((unsigned)(((a.n + kTileN - 1) / kTileN) * (a.m / kTileM)));
     if (a.d_dtype == DT_E4M3) {
         if (a.fmt != FMT_E4M3) return hipErrorNotSupported;
         launch_srelu_variant<FMT_E4M3, EPI_SRELU_FP8>(p, grid, s);

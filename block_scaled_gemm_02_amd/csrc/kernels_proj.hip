@@ -107,15 +107,24 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
     }
 
     // ---- dual MXFP8 quantisation (norm_const 1) ----
-    static_for<3>([&](auto jj) {
-        constexpr int j = decltype(jj)::value;
-        const int blk = 3 * wn + j;                      // 32-feature block within the head
-        static_for<4>([&](auto ii) {
-            constexpr int i = decltype(ii)::value;
+    // One 32-token block at a time: both code arrays are staged in the wave's
+    // LDS region (its ring slot; the K loop is over) and stored as whole
+    // 96-byte row segments; scale bytes are written directly.
+    typedef StageGeom<1, 3> G;
+    uint8_t *stage = w == 0 ? ring.s0 : (w == 1 ? ring.s1 : (w == 2 ? ring.s2 : ring.s3));
+    uint8_t *sr = stage, *sc = stage + 32 * G::RBP;
+    uint8_t *wr = sr + c32 * G::RBP + 4 * gh, *wc = sc + c32 * G::RBP + 4 * gh;
+    const int64_t col0 = h * HD + 96 * wn;              // the wave's first feature column
+    static_for<4>([&](auto ii) {
+        constexpr int i = decltype(ii)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        const int64_t rbase = m0 + 128 * wm + 32 * i;   // first token of this 32-token block
+        const bool blk_ok = rbase < p.tokens;            // tokens % 128 == 0: blocks are whole
+        const int64_t row = m0 + acc_row(wm, i, lane);
+        static_for<3>([&](auto jj) {
+            constexpr int j = decltype(jj)::value;
+            const int blk = 3 * wn + j;                  // 32-feature block within the head
             const f32x16 &a = acc[i][j];
-            const int64_t rbase = m0 + 128 * wm + 32 * i;   // first token of this 32-token block
-            const bool blk_ok = rbase < p.tokens;            // tokens % 128 == 0: blocks are whole
-            const int64_t row = m0 + acc_row(wm, i, lane);
             // row direction: 32 features of one token (this lane and lane ^ 32)
             float rm = 0.0f;
 #pragma unroll
@@ -128,16 +137,15 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
             uint32_t cb[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v) cb[v] = mx_scale_byte(half_wave_max(fabsf(a[v])), 1.0f, cinv[v]);
-            if (blk_ok) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int64_t col = h * HD + 32 * blk + 8 * q + 4 * gh;
-                    *reinterpret_cast<uint32_t *>(p.q_row + row * n_out + col) =
-                        pack4_e4m3(a[4 * q] * rinv, a[4 * q + 1] * rinv, a[4 * q + 2] * rinv, a[4 * q + 3] * rinv);
-                    *reinterpret_cast<uint32_t *>(p.q_col + row * n_out + col) =
-                        pack4_e4m3(a[4 * q] * cinv[4 * q], a[4 * q + 1] * cinv[4 * q + 1],
-                                   a[4 * q + 2] * cinv[4 * q + 2], a[4 * q + 3] * cinv[4 * q + 3]);
-                }
+            for (int q = 0; q < 4; ++q) {
+                *reinterpret_cast<uint32_t *>(wr + 32 * j + 8 * q) =
+                    pack4_e4m3(a[4 * q] * rinv, a[4 * q + 1] * rinv, a[4 * q + 2] * rinv, a[4 * q + 3] * rinv);
+                *reinterpret_cast<uint32_t *>(wc + 32 * j + 8 * q) =
+                    pack4_e4m3(a[4 * q] * cinv[4 * q], a[4 * q + 1] * cinv[4 * q + 1],
+                               a[4 * q + 2] * cinv[4 * q + 2], a[4 * q + 3] * cinv[4 * q + 3]);
+            }
+            if (blk_ok) {
                 if (gh == 0) p.s_row[(row * p.heads + h) * NBLK + blk] = (uint8_t)rb;
                 // lane c < 16 of each half writes the scale of its register c
                 uint32_t byte = cb[0];
@@ -149,6 +157,9 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
                 }
             }
         });
+        const int rows = blk_ok ? 32 : 0;
+        stage_flush<1, 3>(sr, reinterpret_cast<char *>(p.q_row) + rbase * n_out + col0, (uint32_t)n_out, rows, 96, lane);
+        stage_flush<1, 3>(sc, reinterpret_cast<char *>(p.q_col) + rbase * n_out + col0, (uint32_t)n_out, rows, 96, lane);
     });
 }
 
