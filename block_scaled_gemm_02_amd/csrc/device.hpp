@@ -89,16 +89,19 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float x0, float x1, float x2, flo
 }
 
 // E8M0 byte of the smallest power of two >= sigma (sigma >= 0), clamped to
-// [0, 254]; sigma == 0 gives 0.
+// [0, 254]; sigma == 0 (or NaN) gives 0.  Branch-free: it runs once per
+// quantisation block inside unrolled epilogues.
 __device__ __forceinline__ uint32_t e8m0_ceil(float sigma)
 {
-    uint32_t u = __float_as_uint(sigma);
-    if (!(sigma > 0.0f)) return 0u;
-    uint32_t e = u >> 23;                 // biased exponent (sigma > 0, finite)
-    uint32_t mant = u & 0x7FFFFFu;
-    if (e == 0u) return mant > 0x400000u ? 1u : 0u;   // subnormal: 2^-126 or 2^-127
-    if (mant != 0u) e += 1u;
-    return e > 254u ? 254u : e;
+    const uint32_t u = __float_as_uint(sigma);
+    const uint32_t e = u >> 23, mant = u & 0x7FFFFFu;   // sign bit is 0 when sigma > 0
+    // subnormal: 2^-127 (byte 0) or 2^-126 (byte 1); normal: exponent, + 1 if not a power of two.
+    // Selected with masks: the compiler turns a select here into a branch.
+    const uint32_t sub = (uint32_t)(mant > 0x400000u);
+    const uint32_t nrm = e + (uint32_t)(mant != 0u);
+    uint32_t b = sub ^ ((sub ^ nrm) & (0u - (uint32_t)(e != 0u)));
+    b = min(b, 254u);
+    return b & (0u - (uint32_t)(sigma > 0.0f));
 }
 
 // Replace bytes of k-blocks at or past `kblocks` (K padding) with 1.0.
@@ -416,6 +419,23 @@ __device__ __forceinline__ void mma_one(f32x16 (&acc)[4][NB], const Frags<NB> &f
     }
 }
 
+// Where in a step's MFMA sequence the fragment reads and the ring loads go.
+#ifndef BSG_READ_SPAN_NUM
+#define BSG_READ_SPAN_NUM 3     // reads over the first 3/4 of the MFMAs
+#endif
+#ifndef BSG_LOAD_START_NUM
+#define BSG_LOAD_START_NUM 0    // loads from MFMA M*0/8 ...
+#endif
+#ifndef BSG_LOAD_SPAN_NUM
+#define BSG_LOAD_SPAN_NUM 8     // ... over M*8/8 MFMAs
+#endif
+template <int F, int NB>
+constexpr int read_span() { return mfmas_per_step<F, NB>() * BSG_READ_SPAN_NUM / 4; }
+template <int F, int NB>
+constexpr int load_start() { return mfmas_per_step<F, NB>() * BSG_LOAD_START_NUM / 8; }
+template <int F, int NB>
+constexpr int load_span() { return mfmas_per_step<F, NB>() * BSG_LOAD_SPAN_NUM / 8; }
+
 // One K step in ring slot U (K step ks = 4q + U): see the comment above.
 template <int F, int NB, int U>
 __device__ __forceinline__ void pipe_step(f32x16 (&acc)[4][NB], Frags<NB> &cur, Frags<NB> &nxt,
@@ -438,15 +458,23 @@ __device__ __forceinline__ void pipe_step(f32x16 (&acc)[4][NB], Frags<NB> &cur, 
     uint8_t *const lslot = ring.template at<U>();
     const ReadAddr ra = read_addr<F, NB>(ring.template at<(U + 1) % kRing>(), wm, wn, lane);
     __builtin_amdgcn_sched_barrier(0);
+    // Reads go out over the first MR MFMAs, so that the last of them has
+    // landed by the next step's wait; loads over MFMAs [LS, LS + ML).
+    constexpr int MR = read_span<F, NB>(), LS = load_start<F, NB>(), ML = load_span<F, NB>();
     static_for<M>([&](auto mm) {
         constexpr int m = decltype(mm)::value;
         mma_one<F, NB, m>(acc, cur, sa, sb);
-        static_for<(R * (m + 1)) / M - (R * m) / M>([&](auto rr) {
-            read_one<F, NB, (R * m) / M + decltype(rr)::value>(nxt, ra);
-        });
-        static_for<(V * (m + 1)) / M - (V * m) / M>([&](auto ll) {
-            load_one<F, NB, (V * m) / M + decltype(ll)::value>(d, lslot, la, w);
-        });
+        if constexpr (m < MR) {
+            static_for<(R * (m + 1)) / MR - (R * m) / MR>([&](auto rr) {
+                read_one<F, NB, (R * m) / MR + decltype(rr)::value>(nxt, ra);
+            });
+        }
+        if constexpr (m >= LS && m < LS + ML) {
+            constexpr int k = m - LS;
+            static_for<(V * (k + 1)) / ML - (V * k) / ML>([&](auto ll) {
+                load_one<F, NB, (V * k) / ML + decltype(ll)::value>(d, lslot, la, w);
+            });
+        }
         __builtin_amdgcn_sched_barrier(0);
     });
 }
@@ -558,15 +586,34 @@ __device__ __forceinline__ float dpp_mov(float x)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-// Max over the 32 lanes of each half-wave (lanes 0-31 and 32-63 separately):
-// quad and row DPP steps reduce 16 lanes, a swizzle folds the two rows.
-__device__ __forceinline__ float half_wave_max(float x)
+// Max over the 32 lanes of each half-wave (lanes 0-31 and 32-63 separately)
+// of each of N non-negative values: quad and row DPP steps reduce 16 lanes, a
+// swizzle folds the two rows.  The values are compared as unsigned bit
+// patterns, which orders non-negative floats correctly and lets each DPP move
+// fold into its max (no canonicalising moves).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t x)
 {
-    x = fmaxf(x, dpp_mov<0xB1>(x));    // quad_perm [1,0,3,2]
-    x = fmaxf(x, dpp_mov<0x4E>(x));    // quad_perm [2,3,0,1]
-    x = fmaxf(x, dpp_mov<0x141>(x));   // row_half_mirror
-    x = fmaxf(x, dpp_mov<0x140>(x));   // row_mirror
-    return fmaxf(x, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F)));  // lane ^ 16
+    return max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ void half_wave_max(float (&x)[N])
+{
+    uint32_t u[N];
+#pragma unroll
+    for (int v = 0; v < N; ++v) u[v] = __float_as_uint(x[v]);
+#pragma unroll
+    for (int v = 0; v < N; ++v) u[v] = dpp_umax<0xB1>(u[v]);     // quad_perm [1,0,3,2]
+#pragma unroll
+    for (int v = 0; v < N; ++v) u[v] = dpp_umax<0x4E>(u[v]);     // quad_perm [2,3,0,1]
+#pragma unroll
+    for (int v = 0; v < N; ++v) u[v] = dpp_umax<0x141>(u[v]);    // row_half_mirror
+#pragma unroll
+    for (int v = 0; v < N; ++v) u[v] = dpp_umax<0x140>(u[v]);    // row_mirror
+#pragma unroll
+    for (int v = 0; v < N; ++v) u[v] = max(u[v], (uint32_t)__builtin_amdgcn_ds_swizzle((int)u[v], 0x401F));  // lane ^ 16
+#pragma unroll
+    for (int v = 0; v < N; ++v) x[v] = __uint_as_float(u[v]);
 }
 
 // ---------------------------------------------------------------------------

@@ -293,10 +293,13 @@ __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x1
             float rinv;
             rword |= mx_scale_byte(rm, nc, rinv) << (8 * j);
             // column blocks: 32 rows of each column over the half-wave
-            float cinv[16];
+            float cinv[16], cm[16];
             uint32_t cb[16];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) cb[v] = mx_scale_byte(half_wave_max(fabsf(d[v])), nc, cinv[v]);
+            for (int v = 0; v < 16; ++v) cm[v] = fabsf(d[v]);
+            half_wave_max(cm);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) cb[v] = mx_scale_byte(cm[v], nc, cinv[v]);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 *reinterpret_cast<uint32_t *>(wd + 32 * j + 8 * q) =

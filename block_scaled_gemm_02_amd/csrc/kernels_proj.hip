@@ -133,10 +133,13 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
             float rinv;
             const uint32_t rb = mx_scale_byte(rm, 1.0f, rinv);
             // column direction: 32 tokens of one feature (a register over the half-wave)
-            float cinv[16];
+            float cinv[16], cm[16];
             uint32_t cb[16];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) cb[v] = mx_scale_byte(half_wave_max(fabsf(a[v])), 1.0f, cinv[v]);
+            for (int v = 0; v < 16; ++v) cm[v] = fabsf(a[v]);
+            half_wave_max(cm);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) cb[v] = mx_scale_byte(cm[v], 1.0f, cinv[v]);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 *reinterpret_cast<uint32_t *>(wr + 32 * j + 8 * q) =
