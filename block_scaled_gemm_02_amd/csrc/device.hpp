@@ -130,7 +130,10 @@ __device__ __forceinline__ i32x4 sanitize_scales(i32x4 w, int kt, int kblocks)
 // tiles are then 8 m-tiles x 4 n-tiles and share 8 A panels and 4 B panels
 // in its L2 (a row-major order gave each XCD 16 m-tiles x 2 n-tiles, with
 // every A panel fetched by all 8 XCDs).  The last partial round keeps b.
-constexpr int kXcds = 8, kCusPerXcd = 32, kGroupM = 8;
+#ifndef BSG_GROUP_M
+#define BSG_GROUP_M 8
+#endif
+constexpr int kXcds = 8, kCusPerXcd = 32, kGroupM = BSG_GROUP_M;
 
 struct TileCoord {
     int64_t l, mt, nt;
@@ -283,13 +286,17 @@ struct RingSlots {
     __shared__ __attribute__((aligned(16))) uint8_t name##_3[Ring<F>::kStage];                      \
     const ::bsg::RingSlots<F> name{name##_0, name##_1, name##_2, name##_3}
 
-// Per-step instruction counts of one wave.
+// Per-step instruction counts of one wave.  An E4M3 scale atom covers two
+// K steps (128 K elements): it is loaded and read with the even stage only,
+// and the odd stage reuses the even stage's scale words.
+template <int F>
+constexpr bool scales_in_stage(bool odd) { return Ring<F>::kScaled && !(F == FMT_E4M3 && odd); }
 template <int F, int NB>
-constexpr int loads_per_stage() { return 4 + NB + (Ring<F>::kScaled ? 1 : 0); }
+constexpr int loads_in_stage(bool odd) { return 4 + NB + (scales_in_stage<F>(odd) ? 1 : 0); }
 template <int F, int NB>
 constexpr int mfmas_per_step() { return (F == FMT_E4M3 ? 1 : 2) * 4 * NB; }
 template <int F, int NB>
-constexpr int reads_per_step() { return 8 + 2 * NB + (Ring<F>::kScaled ? 2 : 0); }
+constexpr int reads_in_stage(bool odd) { return 8 + 2 * NB + (scales_in_stage<F>(odd) ? 2 : 0); }
 
 // Where this wave's loads of step ks go: code offset (K position, or out of
 // range past the row end) and scale-atom offset.
@@ -323,11 +330,11 @@ __device__ __forceinline__ void load_one(const PipeDesc &d, uint8_t *st, const S
     }
 }
 
-template <int F, int NB>
+template <int F, int NB, bool ODD>
 __device__ __forceinline__ void issue_stage(const PipeDesc &d, uint8_t *st, int ks, int w)
 {
     const StageAddr a = stage_addr<F>(d, ks);
-    static_for<loads_per_stage<F, NB>()>([&](auto l) { load_one<F, NB, decltype(l)::value>(d, st, a, w); });
+    static_for<loads_in_stage<F, NB>(ODD)>([&](auto l) { load_one<F, NB, decltype(l)::value>(d, st, a, w); });
 }
 
 // LDS read number R of a step's fragments: A chunks (R < 8), B chunks, then
@@ -372,7 +379,7 @@ template <int F, int NB>
 __device__ __forceinline__ void read_frags(Frags<NB> &f, const uint8_t *st, int wm, int wn, int lane)
 {
     const ReadAddr r = read_addr<F, NB>(st, wm, wn, lane);
-    static_for<reads_per_step<F, NB>()>([&](auto q) { read_one<F, NB, decltype(q)::value>(f, r); });
+    static_for<reads_in_stage<F, NB>(false)>([&](auto q) { read_one<F, NB, decltype(q)::value>(f, r); });
 }
 
 // Byte of the scale word that an MFMA lane consumes is moved to byte 0
@@ -442,8 +449,11 @@ __device__ __forceinline__ void pipe_step(f32x16 (&acc)[4][NB], Frags<NB> &cur, 
                                           const PipeDesc &d, const RingSlots<F> &ring, int ks, int w,
                                           int wm, int wn, int lane)
 {
-    constexpr int V = loads_per_stage<F, NB>(), M = mfmas_per_step<F, NB>(), R = reads_per_step<F, NB>();
-    s_wait_vm<2 * V>();             // this wave's stage ks+1 has landed
+    // stage ks has the parity of U; stage ks+1 the other one
+    constexpr bool ODD = (U & 1) != 0;
+    constexpr int V = loads_in_stage<F, NB>(ODD), M = mfmas_per_step<F, NB>(), R = reads_in_stage<F, NB>(!ODD);
+    constexpr int VW = loads_in_stage<F, NB>(false) + loads_in_stage<F, NB>(true);
+    s_wait_vm<VW>();                // this wave's stage ks+1 has landed (ks+2, ks+3 in flight)
     s_wait_lgkm0();                 // our reads of stage ks are complete
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -457,6 +467,10 @@ __device__ __forceinline__ void pipe_step(f32x16 (&acc)[4][NB], Frags<NB> &cur, 
     const StageAddr la = stage_addr<F>(d, ks + kRing);
     uint8_t *const lslot = ring.template at<U>();
     const ReadAddr ra = read_addr<F, NB>(ring.template at<(U + 1) % kRing>(), wm, wn, lane);
+    if constexpr (Ring<F>::kScaled && !scales_in_stage<F>(!ODD)) {
+        nxt.sa = cur.sa;
+        nxt.sb = cur.sb;
+    }
     __builtin_amdgcn_sched_barrier(0);
     // Reads go out over the first MR MFMAs, so that the last of them has
     // landed by the next step's wait; loads over MFMAs [LS, LS + ML).
@@ -523,12 +537,12 @@ __device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[4][NB], const RingSl
 
     const int nks = (int)((A.row_bytes + kKS - 1) / kKS);
     Frags<NB> fx, fy;
-    issue_stage<F, NB>(d, ring.template at<0>(), 0, w);
-    issue_stage<F, NB>(d, ring.template at<1>(), 1, w);
-    issue_stage<F, NB>(d, ring.template at<2>(), 2, w);
-    issue_stage<F, NB>(d, ring.template at<3>(), 3, w);
-    constexpr int V = loads_per_stage<F, NB>();
-    s_wait_vm<3 * V>();
+    issue_stage<F, NB, false>(d, ring.template at<0>(), 0, w);
+    issue_stage<F, NB, true>(d, ring.template at<1>(), 1, w);
+    issue_stage<F, NB, false>(d, ring.template at<2>(), 2, w);
+    issue_stage<F, NB, true>(d, ring.template at<3>(), 3, w);
+    // stage 0 has landed; stages 1..3 may be in flight
+    s_wait_vm<2 * loads_in_stage<F, NB>(true) + loads_in_stage<F, NB>(false)>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     read_frags<F, NB>(fx, ring.template at<0>(), wm, wn, lane);
