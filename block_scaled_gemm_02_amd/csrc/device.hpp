@@ -729,6 +729,43 @@ __device__ __forceinline__ void store_quadrant(uint8_t *reg, char *dst, char *ds
     });
 }
 
+// Two outputs of the same type from one pass over the accumulators:
+// value(i, j, v, acc, c, d) sets both elements; C is staged at reg, D at
+// reg + 32 rows.  dst_d2, if non-null, receives a copy of D.
+template <int DT, int NB, class Fn>
+__device__ __forceinline__ void store_quadrant2(uint8_t *reg, char *dst_c, char *dst_d, char *dst_d2,
+                                                uint32_t row_bytes, int rows_valid, int cols_valid,
+                                                f32x16 (&acc)[4][NB], int lane, Fn &&value)
+{
+    constexpr int ES = DT == DT_F32 ? 4 : 2;
+    typedef StageGeom<ES, NB> G;
+    const int c = lane & 31, g = lane >> 5;
+    uint8_t *reg_d = reg + 32 * G::RBP;
+    uint8_t *wc = reg + c * G::RBP + 4 * g * ES, *wd = reg_d + c * G::RBP + 4 * g * ES;
+    static_for<4>([&](auto ii) {
+        constexpr int i = decltype(ii)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<NB>([&](auto jj) {
+            constexpr int j = decltype(jj)::value;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float xc[4], xd[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) value(i, j, 4 * q + u, acc[i][j][4 * q + u], xc[u], xd[u]);
+                *reinterpret_cast<typename Quad<ES>::T *>(wc + (32 * j + 8 * q) * ES) =
+                    pack_quad<DT>(xc[0], xc[1], xc[2], xc[3]);
+                *reinterpret_cast<typename Quad<ES>::T *>(wd + (32 * j + 8 * q) * ES) =
+                    pack_quad<DT>(xd[0], xd[1], xd[2], xd[3]);
+            }
+        });
+        const int rows = rows_valid - 32 * i;
+        const uint32_t roff = (uint32_t)(32 * i) * row_bytes;
+        stage_flush<ES, NB>(reg, dst_c + roff, row_bytes, rows, cols_valid * ES, lane);
+        stage_flush<ES, NB>(reg_d, dst_d + roff, row_bytes, rows, cols_valid * ES, lane);
+        if (dst_d2) stage_flush<ES, NB>(reg_d, dst_d2 + roff, row_bytes, rows, cols_valid * ES, lane);
+    });
+}
+
 // Value of x in lane l ^ 32.
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
@@ -763,19 +800,17 @@ __device__ __forceinline__ void block_amax_atomic(float local, float *dst, float
     }
 }
 
-// fp32 tanh for y >= 0: odd Taylor series y - y^3/3 + 2y^5/15 below 1/16
-// (the first omitted term, 17y^7/315, is below 4e-9 of the result there),
-// otherwise 1 - 2/(e^(2y) + 1) with e^(2y) = 2^(2y log2 e), which lies in
-// [0, 1].  Both forms are evaluated and one is selected, so the epilogue has
-// no divergent branch per element.
+// fp32 tanh for y >= 0: Taylor series y - y^3/3 below 1/64 (the first
+// omitted term, 2y^5/15, is below 1e-8 of the result there), otherwise
+// 1 - 2/(e^(2y) + 1) with e^(2y) = 2^(2y log2 e), which lies in [0, 1] and is
+// within about 1e-7 absolute of tanh.  Both forms are evaluated and one is
+// selected, so the epilogue has no divergent branch per element.
 __device__ __forceinline__ float tanh_pos(float y)
 {
-    const float y2 = y * y;
-    const float p = (2.0f / 15.0f) * y2 - 1.0f / 3.0f;
-    const float series = y + y * (p * y2);
+    const float series = fmaf(y * y, y * (-1.0f / 3.0f), y);
     const float e = __builtin_amdgcn_exp2f(fminf(y * 2.8853900817779268f, 64.0f)); // 2*log2(e)
-    const float closed = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
-    return y < 0.0625f ? series : closed;
+    const float closed = fmaf(-2.0f, __builtin_amdgcn_rcpf(e + 1.0f), 1.0f);
+    return y < 0.015625f ? series : closed;
 }
 
 }  // namespace bsg

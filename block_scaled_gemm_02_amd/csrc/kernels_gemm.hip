@@ -173,18 +173,24 @@ __device__ __forceinline__ int expert_of(const int32_t *offsets, int num, int64_
 // sReLU value of one pre-activation value g = alpha*acc: relu, optional tanh
 // clamp, times prob ("Grouped GEMM + sReLU (SM100)" Equations):
 // D = prob * (s * tanh(relu(g) / s))^2, or prob * relu(g)^2 without clamp.
+// prs2 = prob * s^2 (clamped form) or prob (plain form), per row.
 template <bool CLAMP>
-__device__ __forceinline__ float srelu_value(float gval, float pr, float s, float inv_s)
+__device__ __forceinline__ float srelu_value(float gval, float prs2, float inv_s)
 {
     const float r = fmaxf(gval, 0.0f);
-    const float x = CLAMP ? s * tanh_pos(r * inv_s) : r;
-    return pr * x * x;
+    const float x = CLAMP ? tanh_pos(r * inv_s) : r;
+    return prs2 * (x * x);
+}
+template <bool CLAMP>
+__device__ __forceinline__ float srelu_row_factor(float pr, float s)
+{
+    return CLAMP ? pr * (s * s) : pr;
 }
 
 // BF16 bias epilogue and sReLU epilogue with 16/32-bit outputs: C, then D
 // (and D_col, which equals D for unquantised outputs), each staged through
 // the wave's LDS region with its own compile-time store type.
-template <int EPI, bool CLAMP>
+template <int F, int EPI, bool CLAMP>
 __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, f32x16 (&acc)[4][4],
                                                  uint8_t *stage, int64_t m0, int64_t n0, int g, float alpha,
                                                  int wm, int wn, int lane, float *red)
@@ -213,6 +219,37 @@ __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, f32x16 
     // D = C; without bias C = G, D = prob*G.  sReLU: C = G, D = sReLU(G).
     const int64_t qr = m0 + 128 * wm, qc = n0 + 128 * wn;
     const int cols = clamp_extent(n - qc);
+    float prf[4];                                     // per-row sReLU factor
+#pragma unroll
+    for (int i = 0; i < 4; ++i) prf[i] = srelu_row_factor<CLAMP>(pr[i], p.tanh_s);
+    float lmax = 0.0f;
+    // C and D of one type, and both fit the staging slot: one pass
+    const int es = p.d_dtype == DT_F32 ? 4 : 2;
+    if (p.c && p.c_dtype == p.d_dtype && 2 * 32 * (128 * es + 16) <= Ring<F>::kStage) {
+        auto both = [&](int i, int j, int v, float a, float &cv, float &dv) {
+            const float gval = alpha * a;
+            if constexpr (EPI == EPI_BF16_BIAS) {
+                cv = has_bias ? gval + pr[i] * bv[j][v] : gval;
+                dv = has_bias ? cv : pr[i] * gval;
+            } else {
+                cv = gval;
+                dv = srelu_value<CLAMP>(gval, prf[i], p.tanh_inv_s);
+                lmax = fmaxf(lmax, fabsf(dv));
+            }
+        };
+        char *dd2 = EPI == EPI_BF16_BIAS ? nullptr : static_cast<char *>(p.d_col);
+        const size_t off = (size_t)(qr * n + qc) * es;
+        const uint32_t rb = (uint32_t)(n * es);
+        char *dc = static_cast<char *>(p.c) + off, *dd = static_cast<char *>(p.d) + off;
+        dd2 = dd2 ? dd2 + off : nullptr;
+        if (p.d_dtype == DT_F32) store_quadrant2<DT_F32, 4>(stage, dc, dd, dd2, rb, 128, cols, acc, lane, both);
+        else if (p.d_dtype == DT_BF16) store_quadrant2<DT_BF16, 4>(stage, dc, dd, dd2, rb, 128, cols, acc, lane, both);
+        else store_quadrant2<DT_F16, 4>(stage, dc, dd, dd2, rb, 128, cols, acc, lane, both);
+        if constexpr (EPI == EPI_SRELU) {
+            if (p.amax) block_amax_atomic(lmax, p.amax + g, red);
+        }
+        return;
+    }
     if (p.c) {
         store_quadrant_rt<4>(p.c_dtype, stage, p.c, nullptr, n, qr, qc, 128, cols, acc, lane,
                              [&](int i, int j, int v, float a) {
@@ -221,14 +258,13 @@ __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, f32x16 
             else return gval;
         });
     }
-    float lmax = 0.0f;
     store_quadrant_rt<4>(p.d_dtype, stage, p.d, EPI == EPI_BF16_BIAS ? nullptr : p.d_col, n, qr, qc, 128, cols,
                          acc, lane, [&](int i, int j, int v, float a) {
         const float gval = alpha * a;
         if constexpr (EPI == EPI_BF16_BIAS) {
             return has_bias ? gval + pr[i] * bv[j][v] : pr[i] * gval;
         } else {
-            const float d = srelu_value<CLAMP>(gval, pr[i], p.tanh_s, p.tanh_inv_s);
+            const float d = srelu_value<CLAMP>(gval, prf[i], p.tanh_inv_s);
             lmax = fmaxf(lmax, fabsf(d));
             return d;
         }
@@ -280,11 +316,12 @@ __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x1
         constexpr int i = decltype(ii)::value;
         __builtin_amdgcn_sched_barrier(0);
         uint32_t rword = 0u;                          // SFD_row bytes j = 0..3 of row 32i + c
+        const float prf = srelu_row_factor<CLAMP>(pr[i], p.tanh_s);
         static_for<4>([&](auto jj) {
             constexpr int j = decltype(jj)::value;
             float d[16];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) d[v] = srelu_value<CLAMP>(alpha * acc[i][j][v], pr[i], p.tanh_s, p.tanh_inv_s);
+            for (int v = 0; v < 16; ++v) d[v] = srelu_value<CLAMP>(alpha * acc[i][j][v], prf, p.tanh_inv_s);
             // row block: this lane's 16 columns and the partner half's 16
             float rm = 0.0f;
 #pragma unroll
@@ -355,7 +392,7 @@ __global__ void __launch_bounds__(256) k_grouped(GroupedParams p)
         epilogue_srelu_fp8<CLAMP>(p, acc, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), m0, n0, alpha,
                                   wm, wn, lane);
     } else {
-        epilogue_grouped<EPI, CLAMP>(p, acc, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), m0, n0, g,
+        epilogue_grouped<F, EPI, CLAMP>(p, acc, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), m0, n0, g,
                                      alpha, wm, wn, lane, red);
     }
 }
