@@ -276,8 +276,9 @@ def measure(step, steps, warmup):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps first: the GPU clock ramps up over the first tens of ms")
     ap.add_argument("--workload", default="moe_mxfp8_srelu", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--report", default=None, help="also append the JSON line to this file")

@@ -780,6 +780,25 @@ __device__ __forceinline__ uint32_t mx_scale_byte(float amax, float norm_const, 
     return byte;
 }
 
+// Column scales of one 32x32 block in the accumulator layout.  cm[v] is the
+// column maximum of register v (the same in all 32 lanes of a half-wave
+// after half_wave_max).  Lane c of each half-wave computes the E8M0 scale of
+// register c % 16 only, and every lane then gathers the 16 factors it needs
+// from lanes 32g + v.  Returns this lane's byte: the scale of register c % 16.
+__device__ __forceinline__ uint32_t col_scales(const float (&cm)[16], float nc, float (&cinv)[16], int lane)
+{
+    const int v0 = lane & 15;
+    float m = cm[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) m = v0 == v ? cm[v] : m;
+    float inv;
+    const uint32_t byte = mx_scale_byte(m, nc, inv);
+    const int base = lane & 32;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) cinv[v] = __shfl(inv, base + v);
+    return byte;
+}
+
 __device__ __forceinline__ float wave_max(float x)
 {
 #pragma unroll

@@ -331,12 +331,10 @@ __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x1
             rword |= mx_scale_byte(rm, nc, rinv) << (8 * j);
             // column blocks: 32 rows of each column over the half-wave
             float cinv[16], cm[16];
-            uint32_t cb[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v) cm[v] = fabsf(d[v]);
             half_wave_max(cm);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) cb[v] = mx_scale_byte(cm[v], nc, cinv[v]);
+            const uint32_t byte = col_scales(cm, nc, cinv, lane);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 *reinterpret_cast<uint32_t *>(wd + 32 * j + 8 * q) =
@@ -346,9 +344,6 @@ __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x1
                                d[4 * q + 2] * cinv[4 * q + 2], d[4 * q + 3] * cinv[4 * q + 3]);
             }
             // SFD_col byte i of column 32j + 8(c/4) + 4g + c%4 (lane c < 16: register c)
-            uint32_t byte = cb[0];
-#pragma unroll
-            for (int v = 1; v < 16; ++v) byte = c32 == v ? cb[v] : byte;
             const int64_t col = qc + 32 * j + 8 * (c32 >> 2) + 4 * gh + (c32 & 3);
             if (c32 < 16 && col < n) {
                 const int64_t off = (((col / 128) * col_kt + mt) * 32 + (col % 32)) * 16 + ((col % 128) / 32) * 4;

@@ -134,12 +134,10 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
             const uint32_t rb = mx_scale_byte(rm, 1.0f, rinv);
             // column direction: 32 tokens of one feature (a register over the half-wave)
             float cinv[16], cm[16];
-            uint32_t cb[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v) cm[v] = fabsf(a[v]);
             half_wave_max(cm);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) cb[v] = mx_scale_byte(cm[v], 1.0f, cinv[v]);
+            const uint32_t byte = col_scales(cm, 1.0f, cinv, lane);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 *reinterpret_cast<uint32_t *>(wr + 32 * j + 8 * q) =
@@ -151,9 +149,6 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
             if (blk_ok) {
                 if (gh == 0) p.s_row[(row * p.heads + h) * NBLK + blk] = (uint8_t)rb;
                 // lane c < 16 of each half writes the scale of its register c
-                uint32_t byte = cb[0];
-#pragma unroll
-                for (int v = 1; v < 16; ++v) byte = c32 == v ? cb[v] : byte;
                 if (c32 < 16) {
                     const int64_t col = h * HD + 32 * blk + 8 * (c32 >> 2) + 4 * gh + (c32 & 3);
                     p.s_col[(rbase / 32) * n_out + col] = (uint8_t)byte;
