@@ -175,38 +175,40 @@ struct OperandDesc {
     int64_t sf_mt_max;     // last valid atom row-group index
 };
 
-// A stage holds the A panel (256 rows x 64 B), the B panel (64*NB rows x
-// 64 B) and, for the block-scaled formats, the four 512-byte scale atoms the
-// tile needs for that step (A row groups 0 and 1, B row groups 0 and 1; each
-// padded to 1 KB).  Every lane of a direct-to-LDS load writes 16 bytes at
-// M0 + 16*lane, so one instruction fills 16 rows; lane l fetches logical
-// chunk (l%4) ^ ((row/4)%4) of row l/4, which stores chunk c of row r at
-// chunk c ^ ((r/4)%4).  The LDS serves a 128-bit read for 16 lanes per
-// cycle; those 16 lanes read one chunk of 16 consecutive rows, and the
-// swizzle spreads them over distinct banks.  Loads past a row's end or past
-// the panel read zeros (buffer range check), which covers ragged M, N and K.
+// The LDS holds two "pair slots"; a pair slot holds two consecutive K steps
+// (128 bytes of every row): the A panel (256 rows x 128 B), the B panel
+// (64*NB rows x 128 B) and, for the block-scaled formats, the scale atoms of
+// those 128 bytes (A row groups 0 and 1, B row groups 0 and 1; 1 KB each, two
+// sets for E2M1 whose atom covers one step).  Every lane of a direct-to-LDS
+// load writes 16 bytes at M0 + 16*lane, so one instruction fills 8 rows x
+// 128 B: each row is one whole 128-byte line of the operand, fetched with one
+// request (64-byte rows per instruction took two requests per line and
+// twice the miss-tracking entries of the L1).  Lane l fetches logical chunk
+// (l%8) ^ (l/8) of row l/8, which stores chunk c of row r at chunk c ^ (r%8);
+// the 16 lanes of a 128-bit LDS read then hit 8 distinct chunk positions.
+// Loads past a row's end or past the panel read zeros (buffer range check),
+// which covers ragged M, N and K.
 //
-// Step ks (ring slot U = ks % 4): wait until this wave's loads of stage ks+1
-// have landed, barrier (every wave's part of stage ks+1 is in LDS and no wave
-// still reads slot U), then interleave the step's MFMAs on stage ks (held in
-// registers), the LDS reads of stage ks+1 into the idle register set, and
-// the loads of stage ks+4 into slot U -- one MFMA, then its share of reads
-// and loads, so that the memory instructions issue while the matrix core is
-// busy.  Issuing a step's loads as one burst stalled the wave on the
-// address unit and left the matrix core idle for ~40% of the step.
+// Step ks uses pair slot (ks/2) % 2, half ks % 2.  Odd steps wait until this
+// wave's loads of the next pair have landed and barrier (every wave's part of
+// it is in LDS, and no wave still reads the other slot), then issue the loads
+// of the pair after next into that slot; even steps need neither.  Every step
+// interleaves its MFMAs on stage ks (held in registers) with the LDS reads of
+// stage ks+1 into the idle register set and, on odd steps, the loads -- one
+// MFMA, then its share of reads and loads, so that memory instructions issue
+// while the matrix core is busy.
 constexpr int kKS = 64;                    // bytes per row per step
-constexpr int kRing = 4;                   // stages in flight
-constexpr int kStA = kTileM * kKS;         // 16 KB
-constexpr int kStB = 256 * kKS;            // 16 KB (NB = 4)
-constexpr int kStS = 4 * 1024;             // scale atoms
-constexpr int kStageScaled = kStA + kStB + kStS;
-constexpr int kStagePlain = kStA + kStB;
+constexpr int kPK = 2 * kKS;               // bytes per row per pair slot
+constexpr int kPA = kTileM * kPK;          // 32 KB
+constexpr int kPB = 256 * kPK;             // 32 KB (NB = 4)
 
 template <int F>
 struct Ring {
     static constexpr bool kScaled = F != FMT_BF16;
-    static constexpr int kStage = kScaled ? kStageScaled : kStagePlain;
-    static constexpr int kBytes = kRing * kStage;
+    static constexpr int kScaleSets = F == FMT_E2M1 ? 2 : (F == FMT_E4M3 ? 1 : 0);
+    static constexpr int kSlot = kPA + kPB + kScaleSets * 4096;
+    static constexpr int kBytes = 2 * kSlot;
+    static constexpr int kWaveStage = kSlot / 2 & ~15;   // epilogue staging bytes per wave
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -219,8 +221,8 @@ __device__ __forceinline__ i32x4 make_rsrc_words(const void *base, uint32_t byte
 }
 
 // 16 bytes per lane from a buffer straight into LDS at dst + 16*lane.  Issued
-// through asm so that the compiler, which cannot tell the ring slots apart,
-// adds no waits of its own: completion is tracked explicitly with vmcnt and
+// through asm so that the compiler, which cannot tell the slots apart, adds
+// no waits of its own: completion is tracked explicitly with vmcnt and
 // published to the other waves with a barrier.  One wait state separates the
 // M0 write from the load that reads it.
 __device__ __forceinline__ void lds_load16(const i32x4 &rsrc, uint8_t *dst, uint32_t voff)
@@ -253,110 +255,120 @@ __device__ __forceinline__ void s_wait_lgkm0()
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
+template <int NB>
 struct PipeDesc {
+    static constexpr int LB = 2 * NB;  // B loads per wave per pair (16*NB rows / 8)
     i32x4 ra, rb, rs;         // operand panels; this wave's scale atoms (buffer resources)
     uint32_t row_bytes;
-    uint32_t va[4], vb[4];    // per-lane voffset of this wave's code loads (step 0)
+    uint32_t va[8], vb[LB];   // per-lane voffset of this wave's code loads (pair 0)
     uint32_t lc16;            // 16 * logical chunk of this lane's loads
     uint32_t vs;              // per-lane voffset of this wave's scale atom (kt = 0)
     int kblocks;              // valid 32-wide K blocks
     int sf_kt;                // K atoms per row group (ceil(K/128))
 };
 
-// The four ring slots are distinct LDS objects, selected by compile-time
-// index.
+// The two pair slots are distinct LDS objects, selected by compile-time index.
 template <int F>
 struct RingSlots {
-    uint8_t *s0, *s1, *s2, *s3;
-    template <int U>
+    uint8_t *s0, *s1;
+    template <int S>
     __device__ __forceinline__ uint8_t *at() const
     {
-        if constexpr (U == 0) return s0;
-        else if constexpr (U == 1) return s1;
-        else if constexpr (U == 2) return s2;
-        else return s3;
+        if constexpr (S == 0) return s0;
+        else return s1;
     }
 };
 
 // Declares the ring in the calling kernel's shared memory.
 #define BSG_DECLARE_RING(F, name)                                                                    \
-    __shared__ __attribute__((aligned(16))) uint8_t name##_0[Ring<F>::kStage];                      \
-    __shared__ __attribute__((aligned(16))) uint8_t name##_1[Ring<F>::kStage];                      \
-    __shared__ __attribute__((aligned(16))) uint8_t name##_2[Ring<F>::kStage];                      \
-    __shared__ __attribute__((aligned(16))) uint8_t name##_3[Ring<F>::kStage];                      \
-    const ::bsg::RingSlots<F> name{name##_0, name##_1, name##_2, name##_3}
+    __shared__ __attribute__((aligned(16))) uint8_t name##_0[Ring<F>::kSlot];                       \
+    __shared__ __attribute__((aligned(16))) uint8_t name##_1[Ring<F>::kSlot];                       \
+    const ::bsg::RingSlots<F> name{name##_0, name##_1}
 
-// Per-step instruction counts of one wave.  An E4M3 scale atom covers two
-// K steps (128 K elements): it is loaded and read with the even stage only,
-// and the odd stage reuses the even stage's scale words.
+// After the K loop each wave stages epilogue output in half a pair slot.
+template <int F>
+__device__ __forceinline__ uint8_t *wave_stage(const RingSlots<F> &ring, int w)
+{
+    return (w < 2 ? ring.s0 : ring.s1) + (w & 1) * Ring<F>::kWaveStage;
+}
+
+// Per-pair / per-step instruction counts of one wave.  An E4M3 scale atom
+// covers a whole pair (128 K elements): it is read with the even stage, and
+// the odd stage reuses the even stage's scale words.
 template <int F>
 constexpr bool scales_in_stage(bool odd) { return Ring<F>::kScaled && !(F == FMT_E4M3 && odd); }
 template <int F, int NB>
-constexpr int loads_in_stage(bool odd) { return 4 + NB + (scales_in_stage<F>(odd) ? 1 : 0); }
+constexpr int loads_per_pair() { return 8 + 2 * NB + Ring<F>::kScaleSets; }
 template <int F, int NB>
 constexpr int mfmas_per_step() { return (F == FMT_E4M3 ? 1 : 2) * 4 * NB; }
 template <int F, int NB>
 constexpr int reads_in_stage(bool odd) { return 8 + 2 * NB + (scales_in_stage<F>(odd) ? 2 : 0); }
 
-// Where this wave's loads of step ks go: code offset (K position, or out of
-// range past the row end) and scale-atom offset.
-struct StageAddr {
+// Where this wave's loads of pair p go: code offset (K position, or out of
+// range past the row end) and scale-atom offset of each atom set.
+struct PairAddr {
     uint32_t kb_oob;          // added to va/vb
-    uint32_t so;              // scale-atom voffset
+    uint32_t so[2];           // scale-atom voffsets
 };
-template <int F>
-__device__ __forceinline__ StageAddr stage_addr(const PipeDesc &d, int ks)
+template <int F, int NB>
+__device__ __forceinline__ PairAddr pair_addr(const PipeDesc<NB> &d, int pair)
 {
-    StageAddr a;
-    const uint32_t kb = (uint32_t)ks * kKS;
+    PairAddr a;
+    const uint32_t kb = (uint32_t)pair * kPK;
     a.kb_oob = kb + ((kb + d.lc16 < d.row_bytes) ? 0u : kOOB);
-    // atom kt of this step: 128 K elements = 2 steps (E4M3) or 1 (E2M1)
-    const int kt = F == FMT_E4M3 ? ks >> 1 : ks;
-    a.so = kt < d.sf_kt ? d.vs + (uint32_t)kt * 512u : kOOB;
+    // an atom covers 128 K elements: one pair (E4M3) or one step (E2M1)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int kt = F == FMT_E4M3 ? pair : 2 * pair + h;
+        a.so[h] = kt < d.sf_kt ? d.vs + (uint32_t)kt * 512u : kOOB;
+    }
     return a;
 }
 
-// Load number L of this wave's share of a stage: A rows (L < 4), B rows
-// (L < 4+NB), then the scale atom.
+// Load number L of this wave's share of a pair: A rows (L < 8), B rows
+// (L < 8 + 2NB), then the scale atom(s).
 template <int F, int NB, int L>
-__device__ __forceinline__ void load_one(const PipeDesc &d, uint8_t *st, const StageAddr &a, int w)
+__device__ __forceinline__ void load_one(const PipeDesc<NB> &d, uint8_t *st, const PairAddr &a, int w)
 {
-    if constexpr (L < 4) {
-        lds_load16(d.ra, st + 1024 * (4 * w + L), d.va[L] + a.kb_oob);
-    } else if constexpr (L < 4 + NB) {
-        lds_load16(d.rb, st + kStA + 1024 * (NB * w + (L - 4)), d.vb[L - 4] + a.kb_oob);
+    constexpr int LB = 2 * NB;
+    if constexpr (L < 8) {
+        lds_load16(d.ra, st + 1024 * (8 * w + L), d.va[L] + a.kb_oob);
+    } else if constexpr (L < 8 + LB) {
+        lds_load16(d.rb, st + kPA + 1024 * (LB * w + (L - 8)), d.vb[L - 8] + a.kb_oob);
     } else {
-        lds_load16(d.rs, st + kStA + kStB + 1024 * w, a.so);
+        constexpr int h = L - 8 - LB;
+        lds_load16(d.rs, st + kPA + kPB + 4096 * h + 1024 * w, a.so[h]);
     }
 }
 
-template <int F, int NB, bool ODD>
-__device__ __forceinline__ void issue_stage(const PipeDesc &d, uint8_t *st, int ks, int w)
+template <int F, int NB>
+__device__ __forceinline__ void issue_pair(const PipeDesc<NB> &d, uint8_t *st, int pair, int w)
 {
-    const StageAddr a = stage_addr<F>(d, ks);
-    static_for<loads_in_stage<F, NB>(ODD)>([&](auto l) { load_one<F, NB, decltype(l)::value>(d, st, a, w); });
+    const PairAddr a = pair_addr<F, NB>(d, pair);
+    static_for<loads_per_pair<F, NB>()>([&](auto l) { load_one<F, NB, decltype(l)::value>(d, st, a, w); });
 }
 
 // LDS read number R of a step's fragments: A chunks (R < 8), B chunks, then
-// the two scale words.  The lane reads chunks g and 2+g of its row, stored
-// at chunk ^ ((row/4)%4).
+// the two scale words.  In half H of a pair slot the lane reads logical
+// chunks 4H+g and 4H+2+g of its row, stored at chunk ^ (row % 8).
 struct ReadAddr {
     const uint8_t *a0, *b0;   // this lane's A / B row in block 0
     uint32_t p0, p1;          // byte offsets of its two chunks
     const uint8_t *sa, *sb;   // this lane's scale words
 };
-template <int F, int NB>
+template <int F, int NB, int H>
 __device__ __forceinline__ ReadAddr read_addr(const uint8_t *st, int wm, int wn, int lane)
 {
     ReadAddr r;
     const uint32_t row = lane & 31, g = lane >> 5;
-    const uint32_t swz = (row >> 2) & 3;
-    r.p0 = 16u * (g ^ swz);
-    r.p1 = 16u * ((2u + g) ^ swz);
-    r.a0 = st + (128u * wm + row) * kKS;
-    r.b0 = st + kStA + (32u * NB * wn + row) * kKS;
-    r.sa = st + kStA + kStB + 1024 * wm + 16 * row;
-    r.sb = st + kStA + kStB + 1024 * (2 + wn) + 16 * row;
+    const uint32_t swz = row & 7;
+    r.p0 = 16u * ((4u * H + g) ^ swz);
+    r.p1 = 16u * ((4u * H + 2u + g) ^ swz);
+    r.a0 = st + (128u * wm + row) * kPK;
+    r.b0 = st + kPA + (32u * NB * wn + row) * kPK;
+    const uint8_t *sc = st + kPA + kPB + (F == FMT_E2M1 ? 4096 * H : 0);
+    r.sa = sc + 1024 * wm + 16 * row;
+    r.sb = sc + 1024 * (2 + wn) + 16 * row;
     return r;
 }
 template <int F, int NB, int R>
@@ -364,10 +376,10 @@ __device__ __forceinline__ void read_one(Frags<NB> &f, const ReadAddr &r)
 {
     if constexpr (R < 8) {
         constexpr int i = R / 2, h = R % 2;
-        f.a[i][h] = *reinterpret_cast<const i32x4 *>(r.a0 + 32 * kKS * i + (h ? r.p1 : r.p0));
+        f.a[i][h] = *reinterpret_cast<const i32x4 *>(r.a0 + 32 * kPK * i + (h ? r.p1 : r.p0));
     } else if constexpr (R < 8 + 2 * NB) {
         constexpr int j = (R - 8) / 2, h = (R - 8) % 2;
-        f.b[j][h] = *reinterpret_cast<const i32x4 *>(r.b0 + 32 * kKS * j + (h ? r.p1 : r.p0));
+        f.b[j][h] = *reinterpret_cast<const i32x4 *>(r.b0 + 32 * kPK * j + (h ? r.p1 : r.p0));
     } else if constexpr (R == 8 + 2 * NB) {
         f.sa = *reinterpret_cast<const i32x4 *>(r.sa);
     } else {
@@ -376,9 +388,9 @@ __device__ __forceinline__ void read_one(Frags<NB> &f, const ReadAddr &r)
 }
 
 template <int F, int NB>
-__device__ __forceinline__ void read_frags(Frags<NB> &f, const uint8_t *st, int wm, int wn, int lane)
+__device__ __forceinline__ void read_frags0(Frags<NB> &f, const uint8_t *st, int wm, int wn, int lane)
 {
-    const ReadAddr r = read_addr<F, NB>(st, wm, wn, lane);
+    const ReadAddr r = read_addr<F, NB, 0>(st, wm, wn, lane);
     static_for<reads_in_stage<F, NB>(false)>([&](auto q) { read_one<F, NB, decltype(q)::value>(f, r); });
 }
 
@@ -426,36 +438,32 @@ __device__ __forceinline__ void mma_one(f32x16 (&acc)[4][NB], const Frags<NB> &f
     }
 }
 
-// Where in a step's MFMA sequence the fragment reads and the ring loads go.
+// Where in a step's MFMA sequence the fragment reads and the pair loads go.
 #ifndef BSG_READ_SPAN_NUM
 #define BSG_READ_SPAN_NUM 3     // reads over the first 3/4 of the MFMAs
 #endif
-#ifndef BSG_LOAD_START_NUM
-#define BSG_LOAD_START_NUM 0    // loads from MFMA M*0/8 ...
-#endif
-#ifndef BSG_LOAD_SPAN_NUM
-#define BSG_LOAD_SPAN_NUM 8     // ... over M*8/8 MFMAs
-#endif
 template <int F, int NB>
 constexpr int read_span() { return mfmas_per_step<F, NB>() * BSG_READ_SPAN_NUM / 4; }
-template <int F, int NB>
-constexpr int load_start() { return mfmas_per_step<F, NB>() * BSG_LOAD_START_NUM / 8; }
-template <int F, int NB>
-constexpr int load_span() { return mfmas_per_step<F, NB>() * BSG_LOAD_SPAN_NUM / 8; }
 
-// One K step in ring slot U (K step ks = 4q + U): see the comment above.
+// One K step, ks = 4q + U: see the comment above the pair-slot constants.
 template <int F, int NB, int U>
 __device__ __forceinline__ void pipe_step(f32x16 (&acc)[4][NB], Frags<NB> &cur, Frags<NB> &nxt,
-                                          const PipeDesc &d, const RingSlots<F> &ring, int ks, int w,
+                                          const PipeDesc<NB> &d, const RingSlots<F> &ring, int ks, int w,
                                           int wm, int wn, int lane)
 {
-    // stage ks has the parity of U; stage ks+1 the other one
-    constexpr bool ODD = (U & 1) != 0;
-    constexpr int V = loads_in_stage<F, NB>(ODD), M = mfmas_per_step<F, NB>(), R = reads_in_stage<F, NB>(!ODD);
-    constexpr int VW = loads_in_stage<F, NB>(false) + loads_in_stage<F, NB>(true);
-    s_wait_vm<VW>();                // this wave's stage ks+1 has landed (ks+2, ks+3 in flight)
-    s_wait_lgkm0();                 // our reads of stage ks are complete
-    __builtin_amdgcn_s_barrier();
+    constexpr bool ODD = (U & 1) != 0;           // stage ks parity; stage ks+1 has the other
+    constexpr int RS = ((U + 1) / 2) % 2;        // pair slot of stage ks+1 ...
+    constexpr int RH = (U + 1) % 2;              // ... and its half
+    constexpr int LSL = ((U + 3) / 2) % 2;       // slot the odd step refills
+    constexpr int M = mfmas_per_step<F, NB>(), R = reads_in_stage<F, NB>(!ODD);
+    constexpr int V = ODD ? loads_per_pair<F, NB>() : 0;
+    if constexpr (ODD) {
+        s_wait_vm<0>();             // this wave's part of the pair holding stage ks+1 has landed
+        s_wait_lgkm0();             // our reads of stage ks are complete
+        __builtin_amdgcn_s_barrier();
+    } else {
+        s_wait_lgkm0();             // our reads of stage ks are complete
+    }
     __builtin_amdgcn_sched_barrier(0);
     const int g = lane >> 5;
     i32x4 sa{}, sb{};
@@ -464,17 +472,18 @@ __device__ __forceinline__ void pipe_step(f32x16 (&acc)[4][NB], Frags<NB> &cur, 
         sa = prep_scales<F, U & 1>(cur.sa, kt, d.kblocks, g);
         sb = prep_scales<F, U & 1>(cur.sb, kt, d.kblocks, g);
     }
-    const StageAddr la = stage_addr<F>(d, ks + kRing);
-    uint8_t *const lslot = ring.template at<U>();
-    const ReadAddr ra = read_addr<F, NB>(ring.template at<(U + 1) % kRing>(), wm, wn, lane);
+    PairAddr la{};
+    if constexpr (ODD) la = pair_addr<F, NB>(d, (ks + 3) >> 1);
+    uint8_t *const lslot = ring.template at<LSL>();
+    const ReadAddr ra = read_addr<F, NB, RH>(ring.template at<RS>(), wm, wn, lane);
     if constexpr (Ring<F>::kScaled && !scales_in_stage<F>(!ODD)) {
         nxt.sa = cur.sa;
         nxt.sb = cur.sb;
     }
     __builtin_amdgcn_sched_barrier(0);
     // Reads go out over the first MR MFMAs, so that the last of them has
-    // landed by the next step's wait; loads over MFMAs [LS, LS + ML).
-    constexpr int MR = read_span<F, NB>(), LS = load_start<F, NB>(), ML = load_span<F, NB>();
+    // landed by the next step's wait; loads over all MFMAs.
+    constexpr int MR = read_span<F, NB>();
     static_for<M>([&](auto mm) {
         constexpr int m = decltype(mm)::value;
         mma_one<F, NB, m>(acc, cur, sa, sb);
@@ -483,10 +492,9 @@ __device__ __forceinline__ void pipe_step(f32x16 (&acc)[4][NB], Frags<NB> &cur, 
                 read_one<F, NB, (R * m) / MR + decltype(rr)::value>(nxt, ra);
             });
         }
-        if constexpr (m >= LS && m < LS + ML) {
-            constexpr int k = m - LS;
-            static_for<(V * (k + 1)) / ML - (V * k) / ML>([&](auto ll) {
-                load_one<F, NB, (V * k) / ML + decltype(ll)::value>(d, lslot, la, w);
+        if constexpr (V > 0) {
+            static_for<(V * (m + 1)) / M - (V * m) / M>([&](auto ll) {
+                load_one<F, NB, (V * m) / M + decltype(ll)::value>(d, lslot, la, w);
             });
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -509,17 +517,18 @@ __device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[4][NB], const RingSl
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    PipeDesc d;
+    PipeDesc<NB> d;
     d.ra = make_rsrc_words(A.base, A.bytes);
     d.rb = make_rsrc_words(B.base, B.bytes);
     d.row_bytes = A.row_bytes;
-    const uint32_t lrow = (uint32_t)lane >> 2;                       // row within a 16-row load
-    const uint32_t lchunk = ((uint32_t)lane & 3) ^ ((lrow >> 2) & 3);
+    const uint32_t lrow = (uint32_t)lane >> 3;                       // row within an 8-row load
+    const uint32_t lchunk = ((uint32_t)lane & 7) ^ lrow;
     d.lc16 = 16u * lchunk;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) d.va[q] = (16u * (4 * w + q) + lrow) * A.row_bytes + d.lc16;
+    for (int q = 0; q < 8; ++q) d.va[q] = (64u * w + 8u * q + lrow) * A.row_bytes + d.lc16;
 #pragma unroll
-    for (int q = 0; q < NB; ++q) d.vb[q] = (16u * (NB * w + q) + lrow) * B.row_bytes + d.lc16;
+    for (int q = 0; q < PipeDesc<NB>::LB; ++q)
+        d.vb[q] = (16u * NB * w + 8u * q + lrow) * B.row_bytes + d.lc16;
     d.kblocks = (int)(k / 32);
     d.sf_kt = 0;
     d.rs = d.ra;
@@ -537,16 +546,13 @@ __device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[4][NB], const RingSl
 
     const int nks = (int)((A.row_bytes + kKS - 1) / kKS);
     Frags<NB> fx, fy;
-    issue_stage<F, NB, false>(d, ring.template at<0>(), 0, w);
-    issue_stage<F, NB, true>(d, ring.template at<1>(), 1, w);
-    issue_stage<F, NB, false>(d, ring.template at<2>(), 2, w);
-    issue_stage<F, NB, true>(d, ring.template at<3>(), 3, w);
-    // stage 0 has landed; stages 1..3 may be in flight
-    s_wait_vm<2 * loads_in_stage<F, NB>(true) + loads_in_stage<F, NB>(false)>();
+    issue_pair<F, NB>(d, ring.template at<0>(), 0, w);
+    issue_pair<F, NB>(d, ring.template at<1>(), 1, w);
+    s_wait_vm<loads_per_pair<F, NB>()>();    // pair 0 has landed; pair 1 may be in flight
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    read_frags<F, NB>(fx, ring.template at<0>(), wm, wn, lane);
-    for (int ks = 0; ks < nks; ks += kRing) {
+    read_frags0<F, NB>(fx, ring.template at<0>(), wm, wn, lane);
+    for (int ks = 0; ks < nks; ks += 4) {
         pipe_step<F, NB, 0>(acc, fx, fy, d, ring, ks, w, wm, wn, lane);
         if (ks + 1 < nks) pipe_step<F, NB, 1>(acc, fy, fx, d, ring, ks + 1, w, wm, wn, lane);
         if (ks + 2 < nks) pipe_step<F, NB, 2>(acc, fx, fy, d, ring, ks + 2, w, wm, wn, lane);

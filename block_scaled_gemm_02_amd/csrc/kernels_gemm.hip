@@ -63,12 +63,6 @@ __device__ __forceinline__ void store_quadrant_rt(int dt, uint8_t *reg, void *ba
 // store (see the file comment).
 __device__ __forceinline__ void wait_loads() { s_wait_vm<0>(); }
 
-template <int F>
-__device__ __forceinline__ uint8_t *wave_stage(const RingSlots<F> &ring, int w)
-{
-    return w == 0 ? ring.s0 : (w == 1 ? ring.s1 : (w == 2 ? ring.s2 : ring.s3));
-}
-
 __device__ __forceinline__ int clamp_extent(int64_t extent) { return extent < 0 ? 0 : (extent > 128 ? 128 : (int)extent); }
 
 // ---------------------------------------------------------------------------
@@ -225,7 +219,7 @@ __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, f32x16 
     float lmax = 0.0f;
     // C and D of one type, and both fit the staging slot: one pass
     const int es = p.d_dtype == DT_F32 ? 4 : 2;
-    if (p.c && p.c_dtype == p.d_dtype && 2 * 32 * (128 * es + 16) <= Ring<F>::kStage) {
+    if (p.c && p.c_dtype == p.d_dtype && 2 * 32 * (128 * es + 16) <= Ring<F>::kWaveStage) {
         auto both = [&](int i, int j, int v, float a, float &cv, float &dv) {
             const float gval = alpha * a;
             if constexpr (EPI == EPI_BF16_BIAS) {

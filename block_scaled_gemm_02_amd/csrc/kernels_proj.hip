@@ -108,10 +108,10 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
 
     // ---- dual MXFP8 quantisation (norm_const 1) ----
     // One 32-token block at a time: both code arrays are staged in the wave's
-    // LDS region (its ring slot; the K loop is over) and stored as whole
+    // LDS region (half a pair slot; the K loop is over) and stored as whole
     // 96-byte row segments; scale bytes are written directly.
     typedef StageGeom<1, 3> G;
-    uint8_t *stage = w == 0 ? ring.s0 : (w == 1 ? ring.s1 : (w == 2 ? ring.s2 : ring.s3));
+    uint8_t *stage = wave_stage(ring, __builtin_amdgcn_readfirstlane(w));
     uint8_t *sr = stage, *sc = stage + 32 * G::RBP;
     uint8_t *wr = sr + c32 * G::RBP + 4 * gh, *wc = sc + c32 * G::RBP + 4 * gh;
     const int64_t col0 = h * HD + 96 * wn;              // the wave's first feature column
