@@ -192,11 +192,12 @@ struct OperandDesc {
 // Step ks uses pair slot (ks/2) % 2, half ks % 2.  Odd steps wait until this
 // wave's loads of the next pair have landed and barrier (every wave's part of
 // it is in LDS, and no wave still reads the other slot), then issue the loads
-// of the pair after next into that slot; even steps need neither.  Every step
-// interleaves its MFMAs on stage ks (held in registers) with the LDS reads of
-// stage ks+1 into the idle register set and, on odd steps, the loads -- one
-// MFMA, then its share of reads and loads, so that memory instructions issue
-// while the matrix core is busy.
+// of the pair after next into that slot; even steps need neither, and only
+// prefetch A lines into L2 (see prefetch_a).  Every step interleaves its
+// MFMAs on stage ks (held in registers) with the LDS reads of stage ks+1 into
+// the idle register set and, on odd steps, the loads -- one MFMA, then its
+// share of reads and loads, so that memory instructions issue while the
+// matrix core is busy.
 constexpr int kKS = 64;                    // bytes per row per step
 constexpr int kPK = 2 * kKS;               // bytes per row per pair slot
 constexpr int kPA = kTileM * kPK;          // 32 KB
@@ -234,6 +235,16 @@ __device__ __forceinline__ void lds_load16(const i32x4 &rsrc, uint8_t *dst, uint
                  : "memory", "m0");
 }
 
+// 4 bytes per lane from a buffer into LDS at dst + 4*lane.
+__device__ __forceinline__ void lds_load4(const i32x4 &rsrc, uint8_t *dst, uint32_t voff)
+{
+    const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void *)dst;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+
 // Operand fragments of one step for one wave: two 16-byte chunks per
 // 32-row block (E4M3: low/high halves of one MFMA operand; E2M1 and BF16:
 // the operands of the step's two MFMAs), plus the scale words.
@@ -263,6 +274,7 @@ struct PipeDesc {
     uint32_t va[8], vb[LB];   // per-lane voffset of this wave's code loads (pair 0)
     uint32_t lc16;            // 16 * logical chunk of this lane's loads
     uint32_t vs;              // per-lane voffset of this wave's scale atom (kt = 0)
+    uint32_t pa;              // per-lane voffset of the A line this lane prefetches (pair 0)
     int kblocks;              // valid 32-wide K blocks
     int sf_kt;                // K atoms per row group (ceil(K/128))
 };
@@ -271,6 +283,7 @@ struct PipeDesc {
 template <int F>
 struct RingSlots {
     uint8_t *s0, *s1;
+    uint8_t *sink;            // 256 B per wave where the L2 prefetches land
     template <int S>
     __device__ __forceinline__ uint8_t *at() const
     {
@@ -283,7 +296,8 @@ struct RingSlots {
 #define BSG_DECLARE_RING(F, name)                                                                    \
     __shared__ __attribute__((aligned(16))) uint8_t name##_0[Ring<F>::kSlot];                       \
     __shared__ __attribute__((aligned(16))) uint8_t name##_1[Ring<F>::kSlot];                       \
-    const ::bsg::RingSlots<F> name{name##_0, name##_1}
+    __shared__ __attribute__((aligned(16))) uint8_t name##_pf[1024];                                 \
+    const ::bsg::RingSlots<F> name{name##_0, name##_1, name##_pf}
 
 // After the K loop each wave stages epilogue output in half a pair slot.
 template <int F>
@@ -346,6 +360,19 @@ __device__ __forceinline__ void issue_pair(const PipeDesc<NB> &d, uint8_t *st, i
 {
     const PairAddr a = pair_addr<F, NB>(d, pair);
     static_for<loads_per_pair<F, NB>()>([&](auto l) { load_one<F, NB, decltype(l)::value>(d, st, a, w); });
+}
+
+// L2 prefetch of the A panel: each lane touches the 128-byte line of pair
+// `pair` in one of this wave's 64 A rows, so that the pair's loads, issued one
+// step later, find it in L2.  (An A panel is shared by fewer concurrent tiles
+// than a B panel, so more of its lines miss; prefetching B as well cost more
+// than it saved.)  The 4 bytes per lane land in the wave's sink; nothing
+// reads them.
+template <int F, int NB>
+__device__ __forceinline__ void prefetch_a(const PipeDesc<NB> &d, const RingSlots<F> &ring, int pair, int w)
+{
+    const uint32_t kb = (uint32_t)pair * kPK;
+    lds_load4(d.ra, ring.sink + 256 * w, kb < d.row_bytes ? d.pa + kb : kOOB);
 }
 
 // LDS read number R of a step's fragments: A chunks (R < 8), B chunks, then
@@ -458,7 +485,9 @@ __device__ __forceinline__ void pipe_step(f32x16 (&acc)[4][NB], Frags<NB> &cur, 
     constexpr int M = mfmas_per_step<F, NB>(), R = reads_in_stage<F, NB>(!ODD);
     constexpr int V = ODD ? loads_per_pair<F, NB>() : 0;
     if constexpr (ODD) {
-        s_wait_vm<0>();             // this wave's part of the pair holding stage ks+1 has landed
+        // this wave's part of the pair holding stage ks+1 has landed (the
+        // prefetch issued after it may still be in flight)
+        s_wait_vm<1>();
         s_wait_lgkm0();             // our reads of stage ks are complete
         __builtin_amdgcn_s_barrier();
     } else {
@@ -497,6 +526,9 @@ __device__ __forceinline__ void pipe_step(f32x16 (&acc)[4][NB], Frags<NB> &cur, 
                 load_one<F, NB, (V * m) / M + decltype(ll)::value>(d, lslot, la, w);
             });
         }
+        // even step: prefetch the A lines of the pair after the one the next
+        // (odd) step loads
+        if constexpr (!ODD && m == 0) prefetch_a<F, NB>(d, ring, (ks + 4) >> 1, w);
         __builtin_amdgcn_sched_barrier(0);
     });
 }
@@ -529,6 +561,7 @@ __device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[4][NB], const RingSl
 #pragma unroll
     for (int q = 0; q < PipeDesc<NB>::LB; ++q)
         d.vb[q] = (16u * NB * w + 8u * q + lrow) * B.row_bytes + d.lc16;
+    d.pa = (64u * w + (uint32_t)lane) * A.row_bytes;
     d.kblocks = (int)(k / 32);
     d.sf_kt = 0;
     d.rs = d.ra;

@@ -90,12 +90,12 @@ def _sf_bytes(n: int, centre: int, spread: int, g: torch.Generator, device) -> t
 
 
 def zipf_padded_offsets(tokens: int, experts: int, exponent: float, align: int,
-                        seed: int) -> np.ndarray:
+                        seed: int) -> tuple[np.ndarray, np.ndarray]:
     """Expert row ranges of a Zipf-popularity top-k routing.
 
     Row counts are one multinomial draw of `tokens` over experts with
     p_g proportional to (g+1)^-exponent; each count is padded up to a multiple
-    of `align`; the result is the int32 cumulative padded ends.
+    of `align`.  Returns the int32 cumulative padded ends and the int64 counts.
     """
     rng = np.random.default_rng(seed)
     p = (np.arange(1, experts + 1, dtype=np.float64)) ** (-exponent)
