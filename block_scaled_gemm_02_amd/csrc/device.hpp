@@ -721,8 +721,13 @@ __device__ __forceinline__ void stage_flush(const uint8_t *reg, char *dst, uint3
     if (rows <= 0) return;
     const int lr = lane / G::LPR, cb = (lane % G::LPR) * 16;
     const uint8_t *src = reg + lr * G::RBP + cb;
-    const uint32_t nrec = (uint32_t)(rows < 32 ? rows : 32) * row_bytes;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(dst, (short)0, (int)nrec, 0x00020000);
+    // the destination and extent are wave-uniform: say so, so that the
+    // resource is built once in SGPRs instead of in a loop over lane values
+    const uint64_t base = (uint64_t)(uintptr_t)dst;
+    char *const udst = (char *)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(base >> 32)) << 32) |
+                                           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base));
+    const uint32_t nrec = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(rows < 32 ? rows : 32) * row_bytes));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(udst, (short)0, (int)nrec, 0x00020000);
     const uint32_t voff = (cb < col_bytes && lr < G::RPI) ? (uint32_t)lr * row_bytes + (uint32_t)cb : kOOB;
 #pragma unroll
     for (int k = 0; k < G::NK; ++k) {

@@ -134,7 +134,7 @@ hipError_t launch_gemm_amax(const GemmAmaxArgs &a, hipStream_t s)
 // ---------------------------------------------------------------------------
 // Grouped GEMM over padded_offsets expert ranges
 // ---------------------------------------------------------------------------
-enum : int { EPI_BF16_BIAS = 0, EPI_SRELU = 1, EPI_SRELU_FP8 = 2 };
+enum : int { EPI_BF16_BIAS = 0, EPI_SRELU = 1, EPI_SRELU_FP8 = 2, EPI_BF16 = 3 };
 
 struct GroupedParams {
     const uint8_t *a, *b, *sfa, *sfb;
@@ -193,21 +193,23 @@ __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, f32x16 
     float pr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) pr[i] = p.prob[m0 + acc_row(wm, i, lane)];
-    // bias of this lane's 16 columns of each block
-    float bv[4][16];
-    const bool has_bias = EPI == EPI_BF16_BIAS && p.bias != nullptr;
-    if constexpr (EPI == EPI_BF16_BIAS) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t c = n0 + acc_col<4>(wn, j, q, lane);
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    bv[j][4 * q + u] = (has_bias && c < n) ? load_elem(p.bias, (int64_t)g * n + c + u, p.bias_dtype)
-                                                           : 0.0f;
-            }
+    // The bias of the wave's 128 columns goes to the last 512 bytes of its
+    // staging region as floats (two per lane), and is read back per element:
+    // held in registers it took 64 per lane.
+    // (EPI_BF16_BIAS: the BF16 operation with bias; EPI_BF16: without.)
+    constexpr bool kBf16 = EPI == EPI_BF16_BIAS || EPI == EPI_BF16, has_bias = EPI == EPI_BF16_BIAS;
+    float *const bias_lds = reinterpret_cast<float *>(stage + Ring<F>::kWaveStage - 512);
+    if constexpr (has_bias) {
+        const int64_t c = n0 + 128 * wn + 2 * lane;          // N % 8 == 0: c + 1 < n with c
+        float b0 = 0.0f, b1 = 0.0f;
+        if (c < n) {
+            b0 = load_elem(p.bias, (int64_t)g * n + c, p.bias_dtype);
+            b1 = load_elem(p.bias, (int64_t)g * n + c + 1, p.bias_dtype);
+        }
+        *reinterpret_cast<float2 *>(bias_lds + 2 * lane) = make_float2(b0, b1);
     }
+    const int gh = lane >> 5;
+    auto bias_of = [&](int j, int v) { return bias_lds[32 * j + 8 * (v >> 2) + 4 * gh + (v & 3)]; };
     wait_loads();
     // "Grouped GEMM (SM100 BF16)", Operation: with bias C = G + prob*bias,
     // D = C; without bias C = G, D = prob*G.  sReLU: C = G, D = sReLU(G).
@@ -219,19 +221,22 @@ __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, f32x16 
     float lmax = 0.0f;
     // C and D of one type, and both fit the staging slot: one pass
     const int es = p.d_dtype == DT_F32 ? 4 : 2;
-    if (p.c && p.c_dtype == p.d_dtype && 2 * 32 * (128 * es + 16) <= Ring<F>::kWaveStage) {
+    if (p.c && p.c_dtype == p.d_dtype && 2 * 32 * (128 * es + 16) + 512 <= Ring<F>::kWaveStage) {
         auto both = [&](int i, int j, int v, float a, float &cv, float &dv) {
             const float gval = alpha * a;
-            if constexpr (EPI == EPI_BF16_BIAS) {
-                cv = has_bias ? gval + pr[i] * bv[j][v] : gval;
-                dv = has_bias ? cv : pr[i] * gval;
+            if constexpr (has_bias) {
+                cv = gval + pr[i] * bias_of(j, v);
+                dv = cv;
+            } else if constexpr (kBf16) {
+                cv = gval;
+                dv = pr[i] * gval;
             } else {
                 cv = gval;
                 dv = srelu_value<CLAMP>(gval, prf[i], p.tanh_inv_s);
                 lmax = fmaxf(lmax, fabsf(dv));
             }
         };
-        char *dd2 = EPI == EPI_BF16_BIAS ? nullptr : static_cast<char *>(p.d_col);
+        char *dd2 = kBf16 ? nullptr : static_cast<char *>(p.d_col);
         const size_t off = (size_t)(qr * n + qc) * es;
         const uint32_t rb = (uint32_t)(n * es);
         char *dc = static_cast<char *>(p.c) + off, *dd = static_cast<char *>(p.d) + off;
@@ -248,15 +253,17 @@ __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, f32x16 
         store_quadrant_rt<4>(p.c_dtype, stage, p.c, nullptr, n, qr, qc, 128, cols, acc, lane,
                              [&](int i, int j, int v, float a) {
             const float gval = alpha * a;
-            if constexpr (EPI == EPI_BF16_BIAS) return has_bias ? gval + pr[i] * bv[j][v] : gval;
+            if constexpr (has_bias) return gval + pr[i] * bias_of(j, v);
             else return gval;
         });
     }
-    store_quadrant_rt<4>(p.d_dtype, stage, p.d, EPI == EPI_BF16_BIAS ? nullptr : p.d_col, n, qr, qc, 128, cols,
+    store_quadrant_rt<4>(p.d_dtype, stage, p.d, kBf16 ? nullptr : p.d_col, n, qr, qc, 128, cols,
                          acc, lane, [&](int i, int j, int v, float a) {
         const float gval = alpha * a;
-        if constexpr (EPI == EPI_BF16_BIAS) {
-            return has_bias ? gval + pr[i] * bv[j][v] : pr[i] * gval;
+        if constexpr (has_bias) {
+            return gval + pr[i] * bias_of(j, v);
+        } else if constexpr (kBf16) {
+            return pr[i] * gval;
         } else {
             const float d = srelu_value<CLAMP>(gval, prf[i], p.tanh_inv_s);
             lmax = fmaxf(lmax, fabsf(d));
@@ -407,7 +414,8 @@ hipError_t launch_grouped_gemm(const GroupedArgs &a, hipStream_t s)
     if (a.m == 0 || a.n == 0) return hipSuccess;
     GroupedParams p = grouped_params(a);
     dim3 grid((unsigned)(((a.n + kTileN - 1) / kTileN) * (a.m / kTileM)));
-    hipLaunchKernelGGL((k_grouped<FMT_BF16, EPI_BF16_BIAS, false>), grid, dim3(kThreads), 0, s, p);
+    if (p.bias) hipLaunchKernelGGL((k_grouped<FMT_BF16, EPI_BF16_BIAS, false>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((k_grouped<FMT_BF16, EPI_BF16, false>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
