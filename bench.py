@@ -8,7 +8,9 @@ already resident in HBM.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--report PATH]
 
-Prints one JSON line: throughput in TFLOP/s (algorithmic flops, padded rows
+Defaults: K = 50 timed steps after W = 100 untimed ones.  The GPU clock
+ramps up over the first tens of milliseconds of sustained load, so shorter
+warm-ups time a cold clock.  Prints one JSON line: throughput in TFLOP/s (algorithmic flops, padded rows
 included), a roofline object for the dominant kernel timed with HIP events
 on the launch stream, and the CPU oracle timed on a bounded sample of the
 same workload.
