@@ -611,34 +611,6 @@ __device__ __forceinline__ int acc_col(int wn, int j, int q, int lane)
 
 enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_E4M3 = 3 };
 
-// Four consecutive values of one row: 16 bytes (fp32) or 8 bytes (16-bit).
-template <int DT>
-__device__ __forceinline__ void store4(void *base, int64_t idx, float x0, float x1, float x2, float x3)
-{
-    if constexpr (DT == DT_F32) {
-        *reinterpret_cast<float4 *>(static_cast<float *>(base) + idx) = make_float4(x0, x1, x2, x3);
-    } else if constexpr (DT == DT_BF16) {
-        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(base) + idx) =
-            make_uint2(pack2_bf16(x0, x1), pack2_bf16(x2, x3));
-    } else {
-        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(base) + idx) =
-            make_uint2(pack2_f16(x0, x1), pack2_f16(x2, x3));
-    }
-}
-__device__ __forceinline__ void store4_rt(void *base, int64_t idx, float x0, float x1, float x2, float x3,
-                                          int dt)
-{
-    if (dt == DT_F32) store4<DT_F32>(base, idx, x0, x1, x2, x3);
-    else if (dt == DT_BF16) store4<DT_BF16>(base, idx, x0, x1, x2, x3);
-    else store4<DT_F16>(base, idx, x0, x1, x2, x3);
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
 // Max over the 32 lanes of each half-wave (lanes 0-31 and 32-63 separately)
 // of each of N non-negative values: quad and row DPP steps reduce 16 lanes, a
 // swizzle folds the two rows.  The values are compared as unsigned bit
