@@ -6,8 +6,9 @@ kernels behind the C ABI declared in include/bsg.h.  There is no fallback:
 if libbsg.so is missing or a call fails, a RuntimeError is raised.
 
 Entry points keep the C names:
-    gemm_amax, grouped_gemm, grouped_gemm_srelu, gemm_proj_rope_mxfp8
-and the host-only checks validate_<name>(...) mirror bsg_validate_<name>.
+    gemm_amax, grouped_gemm, grouped_gemm_srelu, gemm_proj_rope_mxfp8,
+    grouped_gemm_discrete, grouped_gemm_srelu_discrete
+and validate_only=True calls the host-only check bsg_validate_<name>.
 """
 from __future__ import annotations
 
@@ -48,6 +49,10 @@ def lib():
             "grouped_gemm": [p] * 8 + [i64] * 4 + [i32] * 3 + [p],
             "grouped_gemm_srelu": [p] * 14 + [i64] * 4 + [i32] * 4 + [f32, p],
             "gemm_proj_rope_mxfp8": [p] * 10 + [i64] * 5 + [i32, i32, p],
+            "grouped_gemm_discrete": [p] * 8 + [i64] * 4 + [i32] * 3 + [p],
+            "grouped_gemm_srelu_discrete": [p] * 14 + [i64] * 4 + [i32] * 4 + [f32, p],
+            "bsg_validate_grouped_gemm_discrete": [p] * 8 + [i64] * 4 + [i32] * 3,
+            "bsg_validate_grouped_gemm_srelu_discrete": [p] * 14 + [i64] * 4 + [i32] * 4 + [f32],
             "bsg_validate_gemm_amax": [p] * 6 + [i64] * 4 + [i32] * 3,
             "bsg_validate_grouped_gemm": [p] * 8 + [i64] * 4 + [i32] * 3,
             "bsg_validate_grouped_gemm_srelu": [p] * 14 + [i64] * 4 + [i32] * 4 + [f32],
@@ -69,8 +74,10 @@ def lib():
 def symbols():
     """Names of the C entry points this binding expects libbsg.so to export."""
     return ["gemm_amax", "grouped_gemm", "grouped_gemm_srelu", "gemm_proj_rope_mxfp8",
+            "grouped_gemm_discrete", "grouped_gemm_srelu_discrete",
             "bsg_validate_gemm_amax", "bsg_validate_grouped_gemm",
             "bsg_validate_grouped_gemm_srelu", "bsg_validate_gemm_proj_rope_mxfp8",
+            "bsg_validate_grouped_gemm_discrete", "bsg_validate_grouped_gemm_srelu_discrete",
             "bsg_status_string", "bsg_last_error", "bsg_version"]
 
 
@@ -153,6 +160,49 @@ def grouped_gemm_srelu(a, b, sfa, sfb, padded_offsets, alpha, prob, norm_const, 
     if validate_only:
         return lib().bsg_validate_grouped_gemm_srelu(*args)
     _check(lib().grouped_gemm_srelu(*args, _stream(stream)))
+
+
+def pointer_array(tensors):
+    """(L,) int64 device tensor of the tensors' data pointers, for the
+    discrete-weight calls (b_ptrs / sfb_ptrs).  The caller keeps the tensors
+    alive until the stream has finished with them."""
+    ptrs = [t.data_ptr() for t in tensors]
+    return torch.tensor(ptrs, dtype=torch.int64).to(tensors[0].device)
+
+
+def grouped_gemm_discrete(a, b_ptrs, padded_offsets, alpha, prob, bias, c, d, m, n, k, num_experts,
+                          bias_dtype=None, c_dtype=None, d_dtype=None, stream=None, validate_only=False):
+    """grouped_gemm with per-expert weight allocations: b_ptrs is an (L,)
+    int64 device tensor of (N,K) bf16 matrices (see include/bsg.h)."""
+    bd = dtype_code(bias_dtype if bias_dtype is not None else (bias if bias is not None else torch.bfloat16))
+    cd = dtype_code(c_dtype if c_dtype is not None else (c if c is not None else torch.bfloat16))
+    dd = dtype_code(d_dtype if d_dtype is not None else d)
+    args = [_ptr(a), _ptr(b_ptrs), _ptr(padded_offsets), _ptr(alpha), _ptr(prob), _ptr(bias),
+            _ptr(c), _ptr(d), m, n, k, num_experts, bd, cd, dd]
+    if validate_only:
+        return lib().bsg_validate_grouped_gemm_discrete(*args)
+    _check(lib().grouped_gemm_discrete(*args, _stream(stream)))
+
+
+def grouped_gemm_srelu_discrete(a, b_ptrs, sfa, sfb_ptrs, padded_offsets, alpha, prob, norm_const, c, d,
+                                d_col, sfd_row, sfd_col, amax, m, n, k, num_experts, ab_dtype="e4m3",
+                                c_dtype=None, d_dtype=None, sf_vec_size=32, tanh_clamp_scale=0.0,
+                                stream=None, validate_only=False):
+    """grouped_gemm_srelu with per-expert weight and scale allocations:
+    b_ptrs / sfb_ptrs are (L,) int64 device tensors (see include/bsg.h)."""
+    cd = dtype_code(c_dtype if c_dtype is not None else (c if c is not None else torch.bfloat16))
+    if d_dtype in ("e4m3", E4M3):
+        dd = E4M3
+    else:
+        dd = dtype_code(d_dtype if d_dtype is not None else d)
+    s = float(tanh_clamp_scale) if tanh_clamp_scale is not None else 0.0
+    args = [_ptr(a), _ptr(b_ptrs), _ptr(sfa), _ptr(sfb_ptrs), _ptr(padded_offsets), _ptr(alpha),
+            _ptr(prob), _ptr(norm_const), _ptr(c), _ptr(d), _ptr(d_col), _ptr(sfd_row),
+            _ptr(sfd_col), _ptr(amax), m, n, k, num_experts, _ab_code(ab_dtype), cd, dd,
+            sf_vec_size, s]
+    if validate_only:
+        return lib().bsg_validate_grouped_gemm_srelu_discrete(*args)
+    _check(lib().grouped_gemm_srelu_discrete(*args, _stream(stream)))
 
 
 def gemm_proj_rope_mxfp8(x, w, x_scale, w_scale, cos, sin, out_fp8_row, out_scales_row,

@@ -159,9 +159,11 @@ int gemm_amax(const void *a, const void *b, const uint8_t *sfa, const uint8_t *s
 // ---------------------------------------------------------------------------
 // Grouped: shared checks
 // ---------------------------------------------------------------------------
+// b is the weight tensor, or with `discrete` the device array of per-expert
+// weight pointers (8-byte aligned; its targets are the caller's contract).
 static int check_grouped_common(const void *a, const void *b, const int32_t *offsets,
                                 const float *alpha, const float *prob, void *d, int64_t m, int64_t n,
-                                int64_t k, int64_t num_experts)
+                                int64_t k, int64_t num_experts, bool discrete = false)
 {
     if (m < 0 || n < 0 || k < 0) return fail(BSG_ERR_SHAPE, "negative size");
     if (num_experts < 1 || num_experts > 1024)
@@ -170,20 +172,22 @@ static int check_grouped_common(const void *a, const void *b, const int32_t *off
     if (!offsets || !alpha) return fail(BSG_ERR_NULLPTR, "padded_offsets and alpha are required");
     if (!prob) return fail(BSG_ERR_NULLPTR, "prob is required");
     if (m * n == 0) return BSG_OK;
-    if (!a || !b || !d) return fail(BSG_ERR_NULLPTR, "a, b and d are required");
-    if (k > 0 && (!aligned16(a) || !aligned16(b))) return fail(BSG_ERR_ALIGN, "A and B must be 16-byte aligned");
+    if (!a || !b || !d) return fail(BSG_ERR_NULLPTR, discrete ? "a, b_ptrs and d are required" : "a, b and d are required");
+    if (discrete && (reinterpret_cast<uintptr_t>(b) & 7u)) return fail(BSG_ERR_ALIGN, "b_ptrs must be 8-byte aligned");
+    if (k > 0 && (!aligned16(a) || (!discrete && !aligned16(b))))
+        return fail(BSG_ERR_ALIGN, "A and B must be 16-byte aligned");
     return check_tiles(m / 256, n, 1);
 }
 
 // ---------------------------------------------------------------------------
 // grouped_gemm (BF16)
 // ---------------------------------------------------------------------------
-int bsg_validate_grouped_gemm(const void *a, const void *b, const int32_t *padded_offsets,
-                              const float *alpha, const float *prob, const void *bias, void *c,
-                              void *d, int64_t m, int64_t n, int64_t k, int64_t num_experts,
-                              int bias_dtype, int c_dtype, int d_dtype)
+static int validate_grouped(const void *a, const void *b, const int32_t *padded_offsets,
+                            const float *alpha, const float *prob, const void *bias, void *c,
+                            void *d, int64_t m, int64_t n, int64_t k, int64_t num_experts,
+                            int bias_dtype, int c_dtype, int d_dtype, bool discrete)
 {
-    int st = check_grouped_common(a, b, padded_offsets, alpha, prob, d, m, n, k, num_experts);
+    int st = check_grouped_common(a, b, padded_offsets, alpha, prob, d, m, n, k, num_experts, discrete);
     if (st) return st;
     if (k % 8) return fail(BSG_ERR_ALIGN, "K=%lld: rows of bf16 A/B must be 16-byte multiples", (long long)k);
     if (!is_float_out(c_dtype) || !is_float_out(d_dtype))
@@ -196,38 +200,76 @@ int bsg_validate_grouped_gemm(const void *a, const void *b, const int32_t *padde
     return BSG_OK;
 }
 
+static int run_grouped(const void *a, const void *b, const uint64_t *b_ptrs, const int32_t *padded_offsets,
+                       const float *alpha, const float *prob, const void *bias, void *c, void *d,
+                       int64_t m, int64_t n, int64_t k, int64_t num_experts, int bias_dtype, int c_dtype,
+                       int d_dtype, void *stream, const char *name)
+{
+    int st = validate_grouped(a, b_ptrs ? static_cast<const void *>(b_ptrs) : b, padded_offsets, alpha, prob,
+                              bias, c, d, m, n, k, num_experts, bias_dtype, c_dtype, d_dtype, b_ptrs != nullptr);
+    if (st) return st;
+    if ((st = check_device())) return st;
+    bsg::GroupedArgs args{};
+    args.a = static_cast<const uint8_t *>(a); args.b = static_cast<const uint8_t *>(b); args.b_ptrs = b_ptrs;
+    args.offsets = padded_offsets; args.alpha = alpha; args.prob = prob; args.bias = bias;
+    args.c = c; args.d = d; args.m = m; args.n = n; args.k = k; args.num_experts = num_experts;
+    args.fmt = 2; args.c_dtype = c_dtype; args.d_dtype = d_dtype; args.bias_dtype = bias_dtype;
+    return launch_status(bsg::launch_grouped_gemm(args, static_cast<hipStream_t>(stream)), name);
+}
+
+int bsg_validate_grouped_gemm(const void *a, const void *b, const int32_t *padded_offsets,
+                              const float *alpha, const float *prob, const void *bias, void *c,
+                              void *d, int64_t m, int64_t n, int64_t k, int64_t num_experts,
+                              int bias_dtype, int c_dtype, int d_dtype)
+{
+    return validate_grouped(a, b, padded_offsets, alpha, prob, bias, c, d, m, n, k, num_experts,
+                            bias_dtype, c_dtype, d_dtype, false);
+}
+
+int bsg_validate_grouped_gemm_discrete(const void *a, const uint64_t *b_ptrs,
+                                       const int32_t *padded_offsets, const float *alpha,
+                                       const float *prob, const void *bias, void *c, void *d,
+                                       int64_t m, int64_t n, int64_t k, int64_t num_experts,
+                                       int bias_dtype, int c_dtype, int d_dtype)
+{
+    return validate_grouped(a, b_ptrs, padded_offsets, alpha, prob, bias, c, d, m, n, k, num_experts,
+                            bias_dtype, c_dtype, d_dtype, true);
+}
+
 int grouped_gemm(const void *a, const void *b, const int32_t *padded_offsets, const float *alpha,
                  const float *prob, const void *bias, void *c, void *d, int64_t m, int64_t n,
                  int64_t k, int64_t num_experts, int bias_dtype, int c_dtype, int d_dtype,
                  void *stream)
 {
-    int st = bsg_validate_grouped_gemm(a, b, padded_offsets, alpha, prob, bias, c, d, m, n, k,
-                                       num_experts, bias_dtype, c_dtype, d_dtype);
-    if (st) return st;
-    if ((st = check_device())) return st;
-    bsg::GroupedArgs args{};
-    args.a = static_cast<const uint8_t *>(a); args.b = static_cast<const uint8_t *>(b);
-    args.offsets = padded_offsets; args.alpha = alpha; args.prob = prob; args.bias = bias;
-    args.c = c; args.d = d; args.m = m; args.n = n; args.k = k; args.num_experts = num_experts;
-    args.fmt = 2; args.c_dtype = c_dtype; args.d_dtype = d_dtype; args.bias_dtype = bias_dtype;
-    return launch_status(bsg::launch_grouped_gemm(args, static_cast<hipStream_t>(stream)), "grouped_gemm");
+    return run_grouped(a, b, nullptr, padded_offsets, alpha, prob, bias, c, d, m, n, k, num_experts,
+                       bias_dtype, c_dtype, d_dtype, stream, "grouped_gemm");
+}
+
+int grouped_gemm_discrete(const void *a, const uint64_t *b_ptrs, const int32_t *padded_offsets,
+                          const float *alpha, const float *prob, const void *bias, void *c, void *d,
+                          int64_t m, int64_t n, int64_t k, int64_t num_experts, int bias_dtype,
+                          int c_dtype, int d_dtype, void *stream)
+{
+    if (!b_ptrs) return fail(BSG_ERR_NULLPTR, "b_ptrs is required");
+    return run_grouped(a, nullptr, b_ptrs, padded_offsets, alpha, prob, bias, c, d, m, n, k, num_experts,
+                       bias_dtype, c_dtype, d_dtype, stream, "grouped_gemm_discrete");
 }
 
 // ---------------------------------------------------------------------------
 // grouped_gemm_srelu
 // ---------------------------------------------------------------------------
-int bsg_validate_grouped_gemm_srelu(const void *a, const void *b, const uint8_t *sfa,
-                                    const uint8_t *sfb, const int32_t *padded_offsets,
-                                    const float *alpha, const float *prob, const float *norm_const,
-                                    void *c, void *d, void *d_col, uint8_t *sfd_row,
-                                    uint8_t *sfd_col, float *amax, int64_t m, int64_t n, int64_t k,
-                                    int64_t num_experts, int ab_dtype, int c_dtype, int d_dtype,
-                                    int sf_vec_size, float tanh_clamp_scale)
+static int validate_srelu(const void *a, const void *b, const uint8_t *sfa, const void *sfb,
+                          const int32_t *padded_offsets, const float *alpha, const float *prob,
+                          const float *norm_const, void *c, void *d, void *d_col, uint8_t *sfd_row,
+                          uint8_t *sfd_col, float *amax, int64_t m, int64_t n, int64_t k,
+                          int64_t num_experts, int ab_dtype, int c_dtype, int d_dtype, int sf_vec_size,
+                          float tanh_clamp_scale, bool discrete)
 {
     (void)amax;
     int st = check_ab_sf(ab_dtype, sf_vec_size);
     if (st) return st;
-    if ((st = check_grouped_common(a, b, padded_offsets, alpha, prob, d, m, n, k, num_experts))) return st;
+    if ((st = check_grouped_common(a, b, padded_offsets, alpha, prob, d, m, n, k, num_experts, discrete)))
+        return st;
     if (k % 32) return fail(BSG_ERR_SHAPE, "K=%lld must be a multiple of sf_vec_size 32", (long long)k);
     if (n % 32) return fail(BSG_ERR_SHAPE, "N=%lld must be a multiple of 32", (long long)n);
     if (!(tanh_clamp_scale == tanh_clamp_scale)) return fail(BSG_ERR_SHAPE, "tanh_clamp_scale is NaN");
@@ -245,7 +287,8 @@ int bsg_validate_grouped_gemm_srelu(const void *a, const void *b, const uint8_t 
             return fail(BSG_ERR_NULLPTR, "FP8 D needs norm_const, d_col, sfd_row and sfd_col");
     }
     if (m * n == 0) return BSG_OK;
-    if (!sfa || !sfb) return fail(BSG_ERR_NULLPTR, "sfa and sfb are required");
+    if (!sfa || !sfb) return fail(BSG_ERR_NULLPTR, discrete ? "sfa and sfb_ptrs are required" : "sfa and sfb are required");
+    if (discrete && (reinterpret_cast<uintptr_t>(sfb) & 7u)) return fail(BSG_ERR_ALIGN, "sfb_ptrs must be 8-byte aligned");
     const int db = fp8_out ? 1 : elem_bytes(d_dtype);
     if (!aligned16(d) || (n * db) % 16 || (d_col && !aligned16(d_col)) ||
         (c && (!aligned16(c) || (n * elem_bytes(c_dtype)) % 16)))
@@ -256,21 +299,23 @@ int bsg_validate_grouped_gemm_srelu(const void *a, const void *b, const uint8_t 
     return BSG_OK;
 }
 
-int grouped_gemm_srelu(const void *a, const void *b, const uint8_t *sfa, const uint8_t *sfb,
-                       const int32_t *padded_offsets, const float *alpha, const float *prob,
-                       const float *norm_const, void *c, void *d, void *d_col, uint8_t *sfd_row,
-                       uint8_t *sfd_col, float *amax, int64_t m, int64_t n, int64_t k,
-                       int64_t num_experts, int ab_dtype, int c_dtype, int d_dtype, int sf_vec_size,
-                       float tanh_clamp_scale, void *stream)
+static int run_srelu(const void *a, const void *b, const uint64_t *b_ptrs, const uint8_t *sfa,
+                     const uint8_t *sfb, const uint64_t *sfb_ptrs, const int32_t *padded_offsets,
+                     const float *alpha, const float *prob, const float *norm_const, void *c, void *d,
+                     void *d_col, uint8_t *sfd_row, uint8_t *sfd_col, float *amax, int64_t m, int64_t n,
+                     int64_t k, int64_t num_experts, int ab_dtype, int c_dtype, int d_dtype,
+                     int sf_vec_size, float tanh_clamp_scale, void *stream, const char *name)
 {
-    int st = bsg_validate_grouped_gemm_srelu(a, b, sfa, sfb, padded_offsets, alpha, prob, norm_const,
-                                             c, d, d_col, sfd_row, sfd_col, amax, m, n, k,
-                                             num_experts, ab_dtype, c_dtype, d_dtype, sf_vec_size,
-                                             tanh_clamp_scale);
+    const bool discrete = b_ptrs != nullptr;
+    int st = validate_srelu(a, discrete ? static_cast<const void *>(b_ptrs) : b, sfa,
+                            discrete ? static_cast<const void *>(sfb_ptrs) : sfb, padded_offsets, alpha,
+                            prob, norm_const, c, d, d_col, sfd_row, sfd_col, amax, m, n, k, num_experts,
+                            ab_dtype, c_dtype, d_dtype, sf_vec_size, tanh_clamp_scale, discrete);
     if (st) return st;
     if ((st = check_device())) return st;
     bsg::GroupedArgs args{};
     args.a = static_cast<const uint8_t *>(a); args.b = static_cast<const uint8_t *>(b);
+    args.b_ptrs = b_ptrs; args.sfb_ptrs = sfb_ptrs;
     args.sfa = sfa; args.sfb = sfb; args.offsets = padded_offsets; args.alpha = alpha;
     args.prob = prob; args.norm_const = norm_const; args.c = c; args.d = d; args.d_col = d_col;
     args.sfd_row = sfd_row; args.sfd_col = sfd_col;
@@ -278,8 +323,61 @@ int grouped_gemm_srelu(const void *a, const void *b, const uint8_t *sfa, const u
     args.m = m; args.n = n; args.k = k; args.num_experts = num_experts;
     args.fmt = ab_dtype == BSG_E2M1X2 ? 1 : 0; args.c_dtype = c_dtype; args.d_dtype = d_dtype;
     args.tanh_s = tanh_clamp_scale > 0.0f ? tanh_clamp_scale : 0.0f;
-    return launch_status(bsg::launch_grouped_srelu(args, static_cast<hipStream_t>(stream)),
-                         "grouped_gemm_srelu");
+    return launch_status(bsg::launch_grouped_srelu(args, static_cast<hipStream_t>(stream)), name);
+}
+
+int bsg_validate_grouped_gemm_srelu(const void *a, const void *b, const uint8_t *sfa,
+                                    const uint8_t *sfb, const int32_t *padded_offsets,
+                                    const float *alpha, const float *prob, const float *norm_const,
+                                    void *c, void *d, void *d_col, uint8_t *sfd_row,
+                                    uint8_t *sfd_col, float *amax, int64_t m, int64_t n, int64_t k,
+                                    int64_t num_experts, int ab_dtype, int c_dtype, int d_dtype,
+                                    int sf_vec_size, float tanh_clamp_scale)
+{
+    return validate_srelu(a, b, sfa, sfb, padded_offsets, alpha, prob, norm_const, c, d, d_col, sfd_row,
+                          sfd_col, amax, m, n, k, num_experts, ab_dtype, c_dtype, d_dtype, sf_vec_size,
+                          tanh_clamp_scale, false);
+}
+
+int bsg_validate_grouped_gemm_srelu_discrete(const void *a, const uint64_t *b_ptrs,
+                                             const uint8_t *sfa, const uint64_t *sfb_ptrs,
+                                             const int32_t *padded_offsets, const float *alpha,
+                                             const float *prob, const float *norm_const, void *c,
+                                             void *d, void *d_col, uint8_t *sfd_row,
+                                             uint8_t *sfd_col, float *amax, int64_t m, int64_t n,
+                                             int64_t k, int64_t num_experts, int ab_dtype,
+                                             int c_dtype, int d_dtype, int sf_vec_size,
+                                             float tanh_clamp_scale)
+{
+    return validate_srelu(a, b_ptrs, sfa, sfb_ptrs, padded_offsets, alpha, prob, norm_const, c, d, d_col,
+                          sfd_row, sfd_col, amax, m, n, k, num_experts, ab_dtype, c_dtype, d_dtype,
+                          sf_vec_size, tanh_clamp_scale, true);
+}
+
+int grouped_gemm_srelu(const void *a, const void *b, const uint8_t *sfa, const uint8_t *sfb,
+                       const int32_t *padded_offsets, const float *alpha, const float *prob,
+                       const float *norm_const, void *c, void *d, void *d_col, uint8_t *sfd_row,
+                       uint8_t *sfd_col, float *amax, int64_t m, int64_t n, int64_t k,
+                       int64_t num_experts, int ab_dtype, int c_dtype, int d_dtype, int sf_vec_size,
+                       float tanh_clamp_scale, void *stream)
+{
+    return run_srelu(a, b, nullptr, sfa, sfb, nullptr, padded_offsets, alpha, prob, norm_const, c, d, d_col,
+                     sfd_row, sfd_col, amax, m, n, k, num_experts, ab_dtype, c_dtype, d_dtype, sf_vec_size,
+                     tanh_clamp_scale, stream, "grouped_gemm_srelu");
+}
+
+int grouped_gemm_srelu_discrete(const void *a, const uint64_t *b_ptrs, const uint8_t *sfa,
+                                const uint64_t *sfb_ptrs, const int32_t *padded_offsets,
+                                const float *alpha, const float *prob, const float *norm_const,
+                                void *c, void *d, void *d_col, uint8_t *sfd_row, uint8_t *sfd_col,
+                                float *amax, int64_t m, int64_t n, int64_t k, int64_t num_experts,
+                                int ab_dtype, int c_dtype, int d_dtype, int sf_vec_size,
+                                float tanh_clamp_scale, void *stream)
+{
+    if (!b_ptrs) return fail(BSG_ERR_NULLPTR, "b_ptrs is required");
+    return run_srelu(a, nullptr, b_ptrs, sfa, nullptr, sfb_ptrs, padded_offsets, alpha, prob, norm_const, c,
+                     d, d_col, sfd_row, sfd_col, amax, m, n, k, num_experts, ab_dtype, c_dtype, d_dtype,
+                     sf_vec_size, tanh_clamp_scale, stream, "grouped_gemm_srelu_discrete");
 }
 
 // ---------------------------------------------------------------------------

@@ -138,6 +138,7 @@ enum : int { EPI_BF16_BIAS = 0, EPI_SRELU = 1, EPI_SRELU_FP8 = 2, EPI_BF16 = 3 }
 
 struct GroupedParams {
     const uint8_t *a, *b, *sfa, *sfb;
+    const uint64_t *b_ptrs, *sfb_ptrs;   // discrete weights (else null)
     const int32_t *offsets;
     const float *alpha, *prob, *norm_const;
     const void *bias;
@@ -378,8 +379,13 @@ __global__ void __launch_bounds__(256) k_grouped(GroupedParams p)
 
     OperandDesc A{p.a + m0 * p.row_bytes, (uint32_t)(kTileM * p.row_bytes), p.row_bytes, p.sfa,
                   0, p.m_t, p.k_t, m0 / 128, p.m_t - 1};
-    OperandDesc B{p.b + ((int64_t)g * p.n + n0) * p.row_bytes, (uint32_t)(rows_b * p.row_bytes),
-                  p.row_bytes, p.sfb, g, p.n_t, p.k_t, n0 / 128, p.n_t - 1};
+    // Expert g's weights: slice g of the (N,K,L) tensor and of its scale
+    // atoms, or (discrete weights) the expert's own allocations, whose scale
+    // atoms have L = 1.
+    const uint8_t *bg = p.b_ptrs ? reinterpret_cast<const uint8_t *>(p.b_ptrs[g]) : p.b + (int64_t)g * p.n * p.row_bytes;
+    const uint8_t *sfbg = p.sfb_ptrs ? reinterpret_cast<const uint8_t *>(p.sfb_ptrs[g]) : p.sfb;
+    OperandDesc B{bg + n0 * p.row_bytes, (uint32_t)(rows_b * p.row_bytes), p.row_bytes, sfbg,
+                  p.sfb_ptrs ? 0 : g, p.n_t, p.k_t, n0 / 128, p.n_t - 1};
     f32x16 acc[4][4];
     mainloop_pipe<F>(acc, ring, A, B, p.k);
 
@@ -397,6 +403,7 @@ static GroupedParams grouped_params(const GroupedArgs &a)
 {
     GroupedParams p;
     p.a = a.a; p.b = a.b; p.sfa = a.sfa; p.sfb = a.sfb; p.offsets = a.offsets;
+    p.b_ptrs = a.b_ptrs; p.sfb_ptrs = a.sfb_ptrs;
     p.alpha = a.alpha; p.prob = a.prob; p.norm_const = a.norm_const; p.bias = a.bias;
     p.c = a.c; p.d = a.d; p.d_col = a.d_col; p.amax = a.amax;
     p.sfd_row = a.sfd_row; p.sfd_col = a.sfd_col;

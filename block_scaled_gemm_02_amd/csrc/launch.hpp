@@ -17,6 +17,7 @@ struct GemmAmaxArgs {
 
 struct GroupedArgs {
     const uint8_t *a, *b, *sfa, *sfb;   // sfa/sfb null for BF16
+    const uint64_t *b_ptrs, *sfb_ptrs;  // discrete weights: per-expert B / SFB addresses (else null)
     const int32_t *offsets;
     const float *alpha, *prob, *norm_const;
     const void *bias;

@@ -158,6 +158,38 @@ int grouped_gemm_srelu(const void *a, const void *b, const uint8_t *sfa, const u
                        float tanh_clamp_scale, void *stream);
 
 /*
+ * Discrete-weight forms -- "Grouped GEMM (SM100 BF16)", discrete mode of the
+ * weight arguments, and "Grouped GEMM + sReLU (SM100)", Discrete-weight
+ * wrapper and the b_ptrs / sfb_ptrs inputs.  The math is that of the dense
+ * call; only the weight addressing differs: expert g's B is its own
+ * allocation instead of slice g of one (N,K,L) tensor.
+ *
+ *  b_ptrs    (L,) contiguous device array of uint64: b_ptrs[g] is the
+ *            device address of expert g's (N,K) k-major B (bf16 for
+ *            grouped_gemm_discrete; E4M3 / packed E2M1 codes for
+ *            grouped_gemm_srelu_discrete)
+ *  sfb_ptrs  (L,) contiguous device array of uint64: sfb_ptrs[g] is expert
+ *            g's scale atoms over (N, K, 1)
+ *  Every other argument, size limit and status is that of grouped_gemm /
+ *  grouped_gemm_srelu.  The pointer arrays must be non-null and 8-byte
+ *  aligned (checked); each target must be 16-byte aligned and stay alive
+ *  and unmodified until the stream completes (the caller's contract, as
+ *  for padded_offsets: device values are not checked).  An expert with no
+ *  rows has its pointers never read.
+ */
+int grouped_gemm_discrete(const void *a, const uint64_t *b_ptrs, const int32_t *padded_offsets,
+                          const float *alpha, const float *prob, const void *bias,
+                          void *c, void *d, int64_t m, int64_t n, int64_t k, int64_t num_experts,
+                          int bias_dtype, int c_dtype, int d_dtype, void *stream);
+int grouped_gemm_srelu_discrete(const void *a, const uint64_t *b_ptrs, const uint8_t *sfa,
+                                const uint64_t *sfb_ptrs, const int32_t *padded_offsets,
+                                const float *alpha, const float *prob, const float *norm_const,
+                                void *c, void *d, void *d_col, uint8_t *sfd_row, uint8_t *sfd_col,
+                                float *amax, int64_t m, int64_t n, int64_t k, int64_t num_experts,
+                                int ab_dtype, int c_dtype, int d_dtype, int sf_vec_size,
+                                float tanh_clamp_scale, void *stream);
+
+/*
  * gemm_proj_rope_mxfp8 -- "GEMM + RoPE + MXFP8 Projection (SM100)",
  * Equations:
  *     Y[t,h,:] = (x W) reshaped to [tokens, num_heads, head_dim]
@@ -207,6 +239,20 @@ int bsg_validate_grouped_gemm_srelu(const void *a, const void *b, const uint8_t 
                                     int64_t m, int64_t n, int64_t k, int64_t num_experts,
                                     int ab_dtype, int c_dtype, int d_dtype, int sf_vec_size,
                                     float tanh_clamp_scale);
+int bsg_validate_grouped_gemm_discrete(const void *a, const uint64_t *b_ptrs,
+                                       const int32_t *padded_offsets, const float *alpha,
+                                       const float *prob, const void *bias, void *c, void *d,
+                                       int64_t m, int64_t n, int64_t k, int64_t num_experts,
+                                       int bias_dtype, int c_dtype, int d_dtype);
+int bsg_validate_grouped_gemm_srelu_discrete(const void *a, const uint64_t *b_ptrs,
+                                             const uint8_t *sfa, const uint64_t *sfb_ptrs,
+                                             const int32_t *padded_offsets, const float *alpha,
+                                             const float *prob, const float *norm_const, void *c,
+                                             void *d, void *d_col, uint8_t *sfd_row,
+                                             uint8_t *sfd_col, float *amax, int64_t m, int64_t n,
+                                             int64_t k, int64_t num_experts, int ab_dtype,
+                                             int c_dtype, int d_dtype, int sf_vec_size,
+                                             float tanh_clamp_scale);
 int bsg_validate_gemm_proj_rope_mxfp8(const void *x, const void *w, const uint8_t *x_scale,
                                       const uint8_t *w_scale, const void *cos, const void *sin,
                                       uint8_t *out_fp8_row, uint8_t *out_scales_row,

@@ -94,6 +94,38 @@ def test_grouped_bf16_validation():
     assert vg(d_dtype=bsg.E4M3) == DTYPE
 
 
+def test_discrete_weight_validation():
+    """Discrete weights ("Grouped GEMM (SM100 BF16)" discrete mode; "Grouped GEMM
+    + sReLU (SM100)" b_ptrs / sfb_ptrs): the pointer arrays are required and
+    8-byte aligned; everything else is checked as in the dense calls."""
+    def vgd(**kw):
+        base = dict(a=P, b_ptrs=P, padded_offsets=P, alpha=P, prob=P, bias=None, c=P, d=P, m=512,
+                    n=256, k=256, num_experts=8, bias_dtype=bsg.BF16, c_dtype=bsg.BF16, d_dtype=bsg.BF16)
+        base.update(kw)
+        return bsg.grouped_gemm_discrete(**base, validate_only=True)
+
+    def vsd(**kw):
+        base = dict(a=P, b_ptrs=P, sfa=P, sfb_ptrs=P, padded_offsets=P, alpha=P, prob=P,
+                    norm_const=None, c=P, d=P, d_col=None, sfd_row=None, sfd_col=None, amax=P,
+                    m=512, n=256, k=256, num_experts=4, ab_dtype="e4m3", c_dtype=bsg.BF16,
+                    d_dtype=bsg.BF16, sf_vec_size=32, tanh_clamp_scale=32.0)
+        base.update(kw)
+        return bsg.grouped_gemm_srelu_discrete(**base, validate_only=True)
+
+    assert vgd() == OK
+    assert vgd(b_ptrs=P + 8) == OK                       # an int64 array needs 8-byte alignment only
+    assert vgd(b_ptrs=P + 4) == ALIGN
+    assert vgd(b_ptrs=None) == NULLPTR
+    assert vgd(m=300) == SHAPE
+    assert vsd() == OK
+    assert vsd(sfb_ptrs=P + 8, b_ptrs=P + 8) == OK
+    assert vsd(sfb_ptrs=P + 4) == ALIGN
+    assert vsd(sfb_ptrs=None) == NULLPTR
+    assert vsd(b_ptrs=None) == NULLPTR
+    assert vsd(n=80) == SHAPE
+    assert vsd(d_dtype=bsg.E4M3) == NULLPTR
+
+
 def vp(**kw):
     base = dict(x=P, w=P, x_scale=None, w_scale=None, cos=P, sin=P, out_fp8_row=P,
                 out_scales_row=P, out_fp8_col=P, out_scales_col=P, tokens=256, q_lora=1536,
