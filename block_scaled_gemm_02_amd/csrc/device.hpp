@@ -581,7 +581,9 @@ __device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[4][NB], const RingSl
     Frags<NB> fx, fy;
     issue_pair<F, NB>(d, ring.template at<0>(), 0, w);
     issue_pair<F, NB>(d, ring.template at<1>(), 1, w);
-    s_wait_vm<loads_per_pair<F, NB>()>();    // pair 0 has landed; pair 1 may be in flight
+    // pair 0 has landed, and with it any direct-to-LDS load the caller issued
+    // before this call (loads complete in issue order); pair 1 may be in flight
+    s_wait_vm<loads_per_pair<F, NB>()>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     read_frags0<F, NB>(fx, ring.template at<0>(), wm, wn, lane);

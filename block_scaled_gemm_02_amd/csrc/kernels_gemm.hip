@@ -185,15 +185,15 @@ __device__ __forceinline__ float srelu_row_factor(float pr, float s)
 // BF16 bias epilogue and sReLU epilogue with 16/32-bit outputs: C, then D
 // (and D_col, which equals D for unquantised outputs), each staged through
 // the wave's LDS region with its own compile-time store type.
-template <int F, int EPI, bool CLAMP>
+template <int F, int EPI, bool CLAMP, int OT>
 __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, f32x16 (&acc)[4][4],
                                                  uint8_t *stage, int64_t m0, int64_t n0, int g, float alpha,
-                                                 int wm, int wn, int lane, float *red)
+                                                 int wm, int wn, int lane, float *red, const float *prob_lds)
 {
     const int64_t n = p.n;
     float pr[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = p.prob[m0 + acc_row(wm, i, lane)];
+    for (int i = 0; i < 4; ++i) pr[i] = prob_lds[acc_row(wm, i, lane)];
     // The bias of the wave's 128 columns goes to the last 512 bytes of its
     // staging region as floats (two per lane), and is read back per element:
     // held in registers it took 64 per lane.
@@ -211,7 +211,7 @@ __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, f32x16 
     }
     const int gh = lane >> 5;
     auto bias_of = [&](int j, int v) { return bias_lds[32 * j + 8 * (v >> 2) + 4 * gh + (v & 3)]; };
-    wait_loads();
+    if constexpr (has_bias) wait_loads();
     // "Grouped GEMM (SM100 BF16)", Operation: with bias C = G + prob*bias,
     // D = C; without bias C = G, D = prob*G.  sReLU: C = G, D = sReLU(G).
     const int64_t qr = m0 + 128 * wm, qc = n0 + 128 * wn;
@@ -221,8 +221,8 @@ __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, f32x16 
     for (int i = 0; i < 4; ++i) prf[i] = srelu_row_factor<CLAMP>(pr[i], p.tanh_s);
     float lmax = 0.0f;
     // C and D of one type, and both fit the staging slot: one pass
-    const int es = p.d_dtype == DT_F32 ? 4 : 2;
-    if (p.c && p.c_dtype == p.d_dtype && 2 * 32 * (128 * es + 16) + 512 <= Ring<F>::kWaveStage) {
+    const int es = OT >= 0 ? (OT == DT_F32 ? 4 : 2) : (p.d_dtype == DT_F32 ? 4 : 2);
+    if (OT >= 0 || (p.c && p.c_dtype == p.d_dtype && 2 * 32 * (128 * es + 16) + 512 <= Ring<F>::kWaveStage)) {
         auto both = [&](int i, int j, int v, float a, float &cv, float &dv) {
             const float gval = alpha * a;
             if constexpr (has_bias) {
@@ -242,7 +242,8 @@ __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, f32x16 
         const uint32_t rb = (uint32_t)(n * es);
         char *dc = static_cast<char *>(p.c) + off, *dd = static_cast<char *>(p.d) + off;
         dd2 = dd2 ? dd2 + off : nullptr;
-        if (p.d_dtype == DT_F32) store_quadrant2<DT_F32, 4>(stage, dc, dd, dd2, rb, 128, cols, acc, lane, both);
+        if constexpr (OT >= 0) store_quadrant2<OT, 4>(stage, dc, dd, dd2, rb, 128, cols, acc, lane, both);
+        else if (p.d_dtype == DT_F32) store_quadrant2<DT_F32, 4>(stage, dc, dd, dd2, rb, 128, cols, acc, lane, both);
         else if (p.d_dtype == DT_BF16) store_quadrant2<DT_BF16, 4>(stage, dc, dd, dd2, rb, 128, cols, acc, lane, both);
         else store_quadrant2<DT_F16, 4>(stage, dc, dd, dd2, rb, 128, cols, acc, lane, both);
         if constexpr (EPI == EPI_SRELU) {
@@ -250,6 +251,7 @@ __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, f32x16 
         }
         return;
     }
+    if constexpr (OT >= 0) return;
     if (p.c) {
         store_quadrant_rt<4>(p.c_dtype, stage, p.c, nullptr, n, qr, qc, 128, cols, acc, lane,
                              [&](int i, int j, int v, float a) {
@@ -291,7 +293,7 @@ __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, f32x16 
 template <bool CLAMP>
 __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x16 (&acc)[4][4],
                                                    uint8_t *stage, int64_t m0, int64_t n0, float alpha,
-                                                   int wm, int wn, int lane)
+                                                   int wm, int wn, int lane, const float *prob_lds)
 {
     typedef StageGeom<1, 4> G;
     const float nc = *p.norm_const;
@@ -304,8 +306,7 @@ __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x1
 
     float pr[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = p.prob[m0 + acc_row(wm, i, lane)];
-    wait_loads();
+    for (int i = 0; i < 4; ++i) pr[i] = prob_lds[acc_row(wm, i, lane)];
     if (p.c) {
         store_quadrant_rt<4>(p.c_dtype, stage, p.c, nullptr, n, qr, qc, 128, cols, acc, lane,
                              [&](int, int, int, float a) { return alpha * a; });
@@ -364,17 +365,18 @@ __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x1
     });
 }
 
-template <int F, int EPI, bool CLAMP>
+template <int F, int EPI, bool CLAMP, int OT = -1>
 __global__ void __launch_bounds__(256) k_grouped(GroupedParams p)
 {
     BSG_DECLARE_RING(F, ring);
     __shared__ float red[4];
+    __shared__ __attribute__((aligned(16))) float prob_lds[kTileM];
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
     const TileCoord tc = tile_of(blockIdx.x, p.m / kTileM, (p.n + kTileN - 1) / kTileN, (int64_t)gridDim.x);
     const int64_t m0 = tc.mt * kTileM, n0 = tc.nt * kTileN;
     const int64_t valid_m = p.offsets[p.num_experts - 1];
     if (m0 >= valid_m) return;                      // uniform per workgroup
-    const int g = expert_of(p.offsets, (int)p.num_experts, m0);
+    const int g = __builtin_amdgcn_readfirstlane(expert_of(p.offsets, (int)p.num_experts, m0));
     const int64_t rows_b = p.n - n0 < kTileN ? p.n - n0 : kTileN;
 
     OperandDesc A{p.a + m0 * p.row_bytes, (uint32_t)(kTileM * p.row_bytes), p.row_bytes, p.sfa,
@@ -386,16 +388,26 @@ __global__ void __launch_bounds__(256) k_grouped(GroupedParams p)
     const uint8_t *sfbg = p.sfb_ptrs ? reinterpret_cast<const uint8_t *>(p.sfb_ptrs[g]) : p.sfb;
     OperandDesc B{bg + n0 * p.row_bytes, (uint32_t)(rows_b * p.row_bytes), p.row_bytes, sfbg,
                   p.sfb_ptrs ? 0 : g, p.n_t, p.k_t, n0 / 128, p.n_t - 1};
+    const float alpha = p.alpha[g];
+    // The tile's 256 prob values go straight to LDS ahead of the operand
+    // loads (wave w: rows 64w..64w+63; M is a multiple of 256), so the K
+    // loop's first wait and barrier cover them and the epilogue starts with
+    // no global load.  (Issued after every scalar load above: the asm is a
+    // memory clobber, and values loaded after it would not stay in SGPRs.)
+    {
+        const int wu = __builtin_amdgcn_readfirstlane(w);
+        lds_load4(make_rsrc_words(p.prob + m0, kTileM * 4), reinterpret_cast<uint8_t *>(prob_lds) + 256 * wu,
+                  4u * (64u * (uint32_t)wu + (uint32_t)lane));
+    }
     f32x16 acc[4][4];
     mainloop_pipe<F>(acc, ring, A, B, p.k);
 
-    const float alpha = p.alpha[g];
     if constexpr (EPI == EPI_SRELU_FP8) {
         epilogue_srelu_fp8<CLAMP>(p, acc, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), m0, n0, alpha,
-                                  wm, wn, lane);
+                                  wm, wn, lane, prob_lds);
     } else {
-        epilogue_grouped<F, EPI, CLAMP>(p, acc, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), m0, n0, g,
-                                     alpha, wm, wn, lane, red);
+        epilogue_grouped<F, EPI, CLAMP, OT>(p, acc, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), m0, n0, g,
+                                            alpha, wm, wn, lane, red, prob_lds);
     }
 }
 
@@ -421,18 +433,32 @@ hipError_t launch_grouped_gemm(const GroupedArgs &a, hipStream_t s)
     if (a.m == 0 || a.n == 0) return hipSuccess;
     GroupedParams p = grouped_params(a);
     dim3 grid((unsigned)(((a.n + kTileN - 1) / kTileN) * (a.m / kTileM)));
-    if (p.bias) hipLaunchKernelGGL((k_grouped<FMT_BF16, EPI_BF16_BIAS, false>), grid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((k_grouped<FMT_BF16, EPI_BF16, false>), grid, dim3(kThreads), 0, s, p);
+    const bool fast = p.c && p.c_dtype == DT_BF16 && p.d_dtype == DT_BF16;
+    if (p.bias) {
+        if (fast) hipLaunchKernelGGL((k_grouped<FMT_BF16, EPI_BF16_BIAS, false, DT_BF16>), grid, dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_grouped<FMT_BF16, EPI_BF16_BIAS, false>), grid, dim3(kThreads), 0, s, p);
+    } else {
+        if (fast) hipLaunchKernelGGL((k_grouped<FMT_BF16, EPI_BF16, false, DT_BF16>), grid, dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_grouped<FMT_BF16, EPI_BF16, false>), grid, dim3(kThreads), 0, s, p);
+    }
     return hipGetLastError();
 }
 
 template <int F, int EPI>
 static void launch_srelu_variant(const GroupedParams &p, dim3 grid, hipStream_t s)
 {
-    if (p.tanh_s > 0.0f)
-        hipLaunchKernelGGL((k_grouped<F, EPI, true>), grid, dim3(kThreads), 0, s, p);
-    else
-        hipLaunchKernelGGL((k_grouped<F, EPI, false>), grid, dim3(kThreads), 0, s, p);
+    // C and D both bf16: a kernel whose epilogue has one compile-time store
+    // path (with every output type in one kernel the register allocator
+    // spilled accumulators, and the spill reloads waited on the stores)
+    if constexpr (EPI == EPI_SRELU) {
+        if (p.c && p.c_dtype == DT_BF16 && p.d_dtype == DT_BF16) {
+            if (p.tanh_s > 0.0f) hipLaunchKernelGGL((k_grouped<F, EPI, true, DT_BF16>), grid, dim3(kThreads), 0, s, p);
+            else hipLaunchKernelGGL((k_grouped<F, EPI, false, DT_BF16>), grid, dim3(kThreads), 0, s, p);
+            return;
+        }
+    }
+    if (p.tanh_s > 0.0f) hipLaunchKernelGGL((k_grouped<F, EPI, true>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((k_grouped<F, EPI, false>), grid, dim3(kThreads), 0, s, p);
 }
 
 hipError_t launch_grouped_srelu(const GroupedArgs &a, hipStream_t s)
