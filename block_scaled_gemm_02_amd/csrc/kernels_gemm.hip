@@ -78,7 +78,9 @@ struct GemmAmaxParams {
     int c_dtype;
 };
 
-template <int F>
+// CT: the C store type, a compile-time choice (one store path per kernel
+// keeps the epilogue free of register spills).
+template <int F, int CT>
 __global__ void __launch_bounds__(256) k_gemm_amax(GemmAmaxParams p)
 {
     BSG_DECLARE_RING(F, ring);
@@ -102,14 +104,22 @@ __global__ void __launch_bounds__(256) k_gemm_amax(GemmAmaxParams p)
     // rows of A / B and not stored
     float lmax = 0.0f;
     const int64_t qr = m0 + 128 * wm, qc = n0 + 128 * wn;
-    store_quadrant_rt<4>(p.c_dtype, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)),
-                         static_cast<char *>(p.c) + batch * p.m * p.n * (p.c_dtype == DT_F32 ? 4 : 2), nullptr,
-                         p.n, qr, qc, clamp_extent(p.m - qr), clamp_extent(p.n - qc), acc, lane,
-                         [&](int, int, int, float a) {
-                             lmax = fmaxf(lmax, fabsf(a));
-                             return a;
-                         });
+    constexpr int es = CT == DT_F32 ? 4 : 2;
+    char *const dst = static_cast<char *>(p.c) + ((batch * p.m + qr) * p.n + qc) * es;
+    store_quadrant<CT, 4>(wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), dst, nullptr, (uint32_t)(p.n * es),
+                          clamp_extent(p.m - qr), clamp_extent(p.n - qc), acc, lane, [&](int, int, int, float a) {
+                              lmax = fmaxf(lmax, fabsf(a));
+                              return a;
+                          });
     if (p.amax) block_amax_atomic(lmax, p.amax, red);
+}
+
+template <int F>
+static void launch_gemm_amax_fmt(const GemmAmaxParams &p, dim3 grid, hipStream_t s)
+{
+    if (p.c_dtype == DT_F32) hipLaunchKernelGGL((k_gemm_amax<F, DT_F32>), grid, dim3(kThreads), 0, s, p);
+    else if (p.c_dtype == DT_BF16) hipLaunchKernelGGL((k_gemm_amax<F, DT_BF16>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((k_gemm_amax<F, DT_F16>), grid, dim3(kThreads), 0, s, p);
 }
 
 hipError_t launch_gemm_amax(const GemmAmaxArgs &a, hipStream_t s)
@@ -124,10 +134,8 @@ hipError_t launch_gemm_amax(const GemmAmaxArgs &a, hipStream_t s)
     p.row_bytes = row_bytes_of(a.fmt, a.k);
     p.c_dtype = a.c_dtype;
     dim3 grid((unsigned)(((a.n + kTileN - 1) / kTileN) * ((a.m + kTileM - 1) / kTileM) * a.l));
-    if (a.fmt == FMT_E4M3)
-        hipLaunchKernelGGL(k_gemm_amax<FMT_E4M3>, grid, dim3(kThreads), 0, s, p);
-    else
-        hipLaunchKernelGGL(k_gemm_amax<FMT_E2M1>, grid, dim3(kThreads), 0, s, p);
+    if (a.fmt == FMT_E4M3) launch_gemm_amax_fmt<FMT_E4M3>(p, grid, s);
+    else launch_gemm_amax_fmt<FMT_E2M1>(p, grid, s);
     return hipGetLastError();
 }
 

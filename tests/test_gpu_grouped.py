@@ -48,7 +48,7 @@ SRELU_CASES = [
     dict(sizes=[256, 768], n=96, k=512, fmt="e4m3", s=0.5, c=torch.float16, d=torch.float16),
     dict(sizes=[0, 256, 256], n=288, k=256, fmt="e2m1", s=32.0, c=torch.bfloat16, d=torch.bfloat16),
     dict(sizes=[256], n=512, k=1024, fmt="e2m1", s=0.0, c=torch.float32, d=torch.bfloat16),
-    dict(sizes=[256, 512], n=200, k=320, fmt="e4m3", s=0.0, c=torch.bfloat16, d=torch.bfloat16),
+    dict(sizes=[256, 512], n=224, k=320, fmt="e4m3", s=0.0, c=torch.bfloat16, d=torch.bfloat16),
 ]
 
 
