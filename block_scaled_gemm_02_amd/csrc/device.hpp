@@ -844,17 +844,38 @@ __device__ __forceinline__ void block_amax_atomic(float local, float *dst, float
     }
 }
 
-// fp32 tanh for y >= 0: Taylor series y - y^3/3 below 1/64 (the first
-// omitted term, 2y^5/15, is below 1e-8 of the result there), otherwise
-// 1 - 2/(e^(2y) + 1) with e^(2y) = 2^(2y log2 e), which lies in [0, 1] and is
-// within about 1e-7 absolute of tanh.  Both forms are evaluated and one is
-// selected, so the epilogue has no divergent branch per element.
-__device__ __forceinline__ float tanh_pos(float y)
+// tanh(r/s)^2 for r >= 0, s > 0, in fp32.  Below r/s = 1/64 it is the
+// series y^2 (1 - 2y^2/3) with y = r/s (the first omitted term, 17y^6/45, is
+// below 1e-8 of the result there); otherwise (1 - 2/(e^(2y) + 1))^2 with
+// e^(2y) = 2^(r * 2 log2(e) / s), which overflows to +inf for large r and then
+// gives exactly 1.  Both forms are evaluated and one is selected, so the
+// epilogue has no divergent branch per element.  t = 1 - 2/(e^(2y)+1) is
+// within about 1e-7 absolute of tanh(y).  The per-call constants come from
+// the host (tanh_sq_const) and live in scalar registers.
+struct TanhSqConst {
+    float is2;      // 1/s^2
+    float c4;       // -(2/3)/s^4
+    float k_exp;    // 2 log2(e)/s
+    float thr;      // s/64: the series below it
+};
+inline TanhSqConst tanh_sq_const(float s)
 {
-    const float series = fmaf(y * y, y * (-1.0f / 3.0f), y);
-    const float e = __builtin_amdgcn_exp2f(fminf(y * 2.8853900817779268f, 64.0f)); // 2*log2(e)
-    const float closed = fmaf(-2.0f, __builtin_amdgcn_rcpf(e + 1.0f), 1.0f);
-    return y < 0.015625f ? series : closed;
+    TanhSqConst t{0.0f, 0.0f, 0.0f, 0.0f};
+    if (s > 0.0f) {
+        const double is = 1.0 / (double)s;
+        t.is2 = (float)(is * is);
+        t.c4 = (float)(-(2.0 / 3.0) * is * is * is * is);
+        t.k_exp = (float)(2.0 * 1.4426950408889634 * is);
+        t.thr = (float)((double)s / 64.0);
+    }
+    return t;
+}
+__device__ __forceinline__ float tanh_sq(float r, const TanhSqConst &tq)
+{
+    const float r2 = r * r;
+    const float series = r2 * fmaf(r2, tq.c4, tq.is2);
+    const float t = fmaf(-2.0f, __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(r * tq.k_exp) + 1.0f), 1.0f);
+    return r < tq.thr ? series : t * t;
 }
 
 }  // namespace bsg

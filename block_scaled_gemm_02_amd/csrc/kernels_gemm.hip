@@ -157,7 +157,8 @@ struct GroupedParams {
     int64_t m_t, n_t, k_t;
     uint32_t row_bytes;
     int c_dtype, d_dtype, bias_dtype;
-    float tanh_s, tanh_inv_s;
+    float tanh_s;
+    TanhSqConst tq;      // constants of tanh(r/s)^2 (see tanh_sq)
 };
 
 // Index of the expert whose range [offsets[g-1], offsets[g]) holds row r:
@@ -178,11 +179,10 @@ __device__ __forceinline__ int expert_of(const int32_t *offsets, int num, int64_
 // D = prob * (s * tanh(relu(g) / s))^2, or prob * relu(g)^2 without clamp.
 // prs2 = prob * s^2 (clamped form) or prob (plain form), per row.
 template <bool CLAMP>
-__device__ __forceinline__ float srelu_value(float gval, float prs2, float inv_s)
+__device__ __forceinline__ float srelu_value(float gval, float prs2, const TanhSqConst &tq)
 {
     const float r = fmaxf(gval, 0.0f);
-    const float x = CLAMP ? tanh_pos(r * inv_s) : r;
-    return prs2 * (x * x);
+    return prs2 * (CLAMP ? tanh_sq(r, tq) : r * r);
 }
 template <bool CLAMP>
 __device__ __forceinline__ float srelu_row_factor(float pr, float s)
@@ -241,7 +241,7 @@ __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, f32x16 
                 dv = pr[i] * gval;
             } else {
                 cv = gval;
-                dv = srelu_value<CLAMP>(gval, prf[i], p.tanh_inv_s);
+                dv = srelu_value<CLAMP>(gval, prf[i], p.tq);
                 lmax = fmaxf(lmax, fabsf(dv));
             }
         };
@@ -276,7 +276,7 @@ __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, f32x16 
         } else if constexpr (kBf16) {
             return pr[i] * gval;
         } else {
-            const float d = srelu_value<CLAMP>(gval, prf[i], p.tanh_inv_s);
+            const float d = srelu_value<CLAMP>(gval, prf[i], p.tq);
             lmax = fmaxf(lmax, fabsf(d));
             return d;
         }
@@ -332,7 +332,7 @@ __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x1
             constexpr int j = decltype(jj)::value;
             float d[16];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) d[v] = srelu_value<CLAMP>(alpha * acc[i][j][v], prf, p.tanh_inv_s);
+            for (int v = 0; v < 16; ++v) d[v] = srelu_value<CLAMP>(alpha * acc[i][j][v], prf, p.tq);
             // row block: this lane's 16 columns and the partner half's 16
             float rm = 0.0f;
 #pragma unroll
@@ -432,7 +432,7 @@ static GroupedParams grouped_params(const GroupedArgs &a)
     p.row_bytes = row_bytes_of(a.fmt, a.k);
     p.c_dtype = a.c_dtype; p.d_dtype = a.d_dtype; p.bias_dtype = a.bias_dtype;
     p.tanh_s = a.tanh_s;
-    p.tanh_inv_s = a.tanh_s > 0.0f ? 1.0f / a.tanh_s : 0.0f;
+    p.tq = tanh_sq_const(a.tanh_s);
     return p;
 }
 
