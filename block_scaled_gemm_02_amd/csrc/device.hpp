@@ -805,6 +805,15 @@ __device__ __forceinline__ uint32_t mx_scale_byte(float amax, float norm_const, 
     return byte;
 }
 
+// Per-lane select with a wave-uniform lane mask: x1 in lanes whose mask bit
+// is set, else x0 (one v_cndmask_b32).
+__device__ __forceinline__ float lane_select(uint64_t mask, float x0, float x1)
+{
+    float r;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(x0), "v"(x1), "s"(mask));
+    return r;
+}
+
 // Column scales of one 32x32 block in the accumulator layout.  cm[v] is the
 // column maximum of register v (the same in all 32 lanes of a half-wave
 // after half_wave_max).  Lane c of each half-wave computes the E8M0 scale of
@@ -812,10 +821,18 @@ __device__ __forceinline__ uint32_t mx_scale_byte(float amax, float norm_const, 
 // from lanes 32g + v.  Returns this lane's byte: the scale of register c % 16.
 __device__ __forceinline__ uint32_t col_scales(const float (&cm)[16], float nc, float (&cinv)[16], int lane)
 {
-    const int v0 = lane & 15;
-    float m = cm[0];
+    // m = cm[lane % 16]: a tree of selects on the bits of the lane index,
+    // whose lane masks are constants.  Written as v_cndmask with an explicit
+    // mask: the compiler otherwise turns selects among the 16 values back
+    // into an indexed load, which moves them through scratch memory.
+    float t8[8], t4[4], t2[2];
 #pragma unroll
-    for (int v = 1; v < 16; ++v) m = v0 == v ? cm[v] : m;
+    for (int k = 0; k < 8; ++k) t8[k] = lane_select(0xAAAAAAAAAAAAAAAAull, cm[2 * k], cm[2 * k + 1]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) t4[k] = lane_select(0xCCCCCCCCCCCCCCCCull, t8[2 * k], t8[2 * k + 1]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) t2[k] = lane_select(0xF0F0F0F0F0F0F0F0ull, t4[2 * k], t4[2 * k + 1]);
+    const float m = lane_select(0xFF00FF00FF00FF00ull, t2[0], t2[1]);
     float inv;
     const uint32_t byte = mx_scale_byte(m, nc, inv);
     const int base = lane & 32;
