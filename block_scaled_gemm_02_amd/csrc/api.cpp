@@ -390,16 +390,23 @@ int bsg_validate_gemm_proj_rope_mxfp8(const void *x, const void *w, const uint8_
                                       int64_t tokens, int64_t q_lora, int64_t num_heads,
                                       int64_t head_dim, int64_t qk_rope, int in_dtype, int w_out_in)
 {
-    if (in_dtype == BSG_E4M3) return fail(BSG_ERR_UNSUPPORTED, "MXFP8-input projection is not built");
-    if (in_dtype != BSG_BF16) return fail(BSG_ERR_DTYPE, "x/w dtype must be BF16");
-    if (x_scale || w_scale) return fail(BSG_ERR_SHAPE, "x_scale/w_scale must be NULL for BF16 inputs");
+    if (in_dtype != BSG_BF16 && in_dtype != BSG_E4M3) return fail(BSG_ERR_DTYPE, "x/w dtype must be BF16 or E4M3");
+    const bool mx = in_dtype == BSG_E4M3;
+    if (!mx && (x_scale || w_scale)) return fail(BSG_ERR_SHAPE, "x_scale/w_scale must be NULL for BF16 inputs");
     if (tokens < 0 || q_lora < 0 || num_heads < 0) return fail(BSG_ERR_SHAPE, "negative size");
     if (tokens % 128) return fail(BSG_ERR_SHAPE, "tokens=%lld must be a multiple of 128", (long long)tokens);
     if (q_lora % 32) return fail(BSG_ERR_SHAPE, "q_lora must be a multiple of 32");
     if (head_dim != 192 || qk_rope != 64)
         return fail(BSG_ERR_UNSUPPORTED, "only head_dim 192 with qk_rope 64 is built");
     if (w_out_in != 0 && w_out_in != 1) return fail(BSG_ERR_SHAPE, "w_out_in must be 0 or 1");
+    if (mx && !w_out_in)
+        return fail(BSG_ERR_UNSUPPORTED, "MXFP8 inputs need w as [out, in] (transpose codes and w_scale first)");
+    if (mx && q_lora % 128)
+        return fail(BSG_ERR_UNSUPPORTED, "MXFP8 inputs need q_lora to be a multiple of 128");
     if (tokens * num_heads == 0) return BSG_OK;
+    if (mx && (!x_scale || !w_scale)) return fail(BSG_ERR_NULLPTR, "x_scale and w_scale are required for E4M3 inputs");
+    if (mx && ((uintptr_t)x_scale % 4 || (uintptr_t)w_scale % 4))
+        return fail(BSG_ERR_ALIGN, "x_scale and w_scale must be 4-byte aligned");
     if (!x || !w || !cos || !sin || !out_fp8_row || !out_scales_row || !out_fp8_col || !out_scales_col)
         return fail(BSG_ERR_NULLPTR, "all tensors are required");
     if (!aligned16(x) || !aligned16(w) || !aligned16(out_fp8_row) || !aligned16(out_fp8_col) ||
@@ -419,10 +426,11 @@ int gemm_proj_rope_mxfp8(const void *x, const void *w, const uint8_t *x_scale, c
                                                q_lora, num_heads, head_dim, qk_rope, in_dtype, w_out_in);
     if (st) return st;
     if ((st = check_device())) return st;
-    bsg::ProjRopeArgs args{static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w),
+    bsg::ProjRopeArgs args{x, w, x_scale, w_scale,
                            static_cast<const uint16_t *>(cos), static_cast<const uint16_t *>(sin),
                            out_fp8_row, out_scales_row, out_fp8_col, out_scales_col,
-                           tokens, q_lora, num_heads, head_dim, qk_rope, w_out_in};
+                           tokens, q_lora, num_heads, head_dim, qk_rope, w_out_in,
+                           in_dtype == BSG_E4M3 ? 1 : 0};
     return launch_status(bsg::launch_proj_rope(args, static_cast<hipStream_t>(stream)),
                          "gemm_proj_rope_mxfp8");
 }

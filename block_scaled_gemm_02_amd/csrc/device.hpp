@@ -45,7 +45,11 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-enum Fmt : int { FMT_E4M3 = 0, FMT_E2M1 = 1, FMT_BF16 = 2 };
+// FMT_E4M3_RM: E4M3 codes whose E8M0 scales are row-major, one byte per 32
+// K elements of a row ("GEMM + RoPE + MXFP8 Projection (SM100)", x_scale and
+// w_scale), instead of the scale-atom layout of the other block-scaled ops.
+enum Fmt : int { FMT_E4M3 = 0, FMT_E2M1 = 1, FMT_BF16 = 2, FMT_E4M3_RM = 3 };
+constexpr bool is_e4m3(int f) { return f == FMT_E4M3 || f == FMT_E4M3_RM; }
 
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;
@@ -173,6 +177,9 @@ struct OperandDesc {
     int64_t sf_l, sf_mn_t, sf_k_t;  // batch index, ceil(MN/128), ceil(K/128)
     int64_t sf_mt0;        // atom row-group index of this tile's row 0
     int64_t sf_mt_max;     // last valid atom row-group index
+    // FMT_E4M3_RM only: sf is the scale row of this tile's row 0, sf_rm the
+    // bytes per scale row (K/32, a multiple of 4), sf_bytes the readable bytes
+    uint32_t sf_rm = 0, sf_bytes = 0;
 };
 
 // The LDS holds two "pair slots"; a pair slot holds two consecutive K steps
@@ -212,7 +219,7 @@ constexpr int kPB = 256 * kPK;             // 32 KB (NB = 4)
 template <int F>
 struct Ring {
     static constexpr bool kScaled = F != FMT_BF16;
-    static constexpr int kScaleSets = F == FMT_E2M1 ? 2 : (F == FMT_E4M3 ? 1 : 0);
+    static constexpr int kScaleSets = F == FMT_E2M1 ? 2 : (is_e4m3(F) ? 1 : 0);
     static constexpr int kSlot = kPA + kPB + kScaleSets * 4096;
     static constexpr int kBytes = 2 * kSlot;
     static constexpr int kWaveStage = kSlot / 2 & ~15;   // epilogue staging bytes per wave
@@ -281,6 +288,7 @@ struct PipeDesc {
     uint32_t lc16;            // 16 * logical chunk of this lane's loads
     uint32_t vs;              // per-lane voffset of this wave's scale atom (kt = 0)
     uint32_t pa;              // per-lane voffset of the A line this lane prefetches (pair 0)
+    uint32_t vsr[2];          // row-major scales: per-lane voffsets of this wave's two scale loads (pair 0)
     int kblocks;              // valid 32-wide K blocks
     int sf_kt;                // K atoms per row group (ceil(K/128))
 };
@@ -316,11 +324,11 @@ __device__ __forceinline__ uint8_t *wave_stage(const RingSlots<F> &ring, int w)
 // covers a whole pair (128 K elements): it is read with the even stage, and
 // the odd stage reuses the even stage's scale words.
 template <int F>
-constexpr bool scales_in_stage(bool odd) { return Ring<F>::kScaled && !(F == FMT_E4M3 && odd); }
+constexpr bool scales_in_stage(bool odd) { return Ring<F>::kScaled && !(is_e4m3(F) && odd); }
 template <int F, int NB>
-constexpr int loads_per_pair() { return 8 + 2 * NB + Ring<F>::kScaleSets; }
+constexpr int loads_per_pair() { return 8 + 2 * NB + (F == FMT_E4M3_RM ? 2 : Ring<F>::kScaleSets); }
 template <int F, int NB>
-constexpr int mfmas_per_step() { return (F == FMT_E4M3 ? 1 : 2) * 4 * NB; }
+constexpr int mfmas_per_step() { return (is_e4m3(F) ? 1 : 2) * 4 * NB; }
 template <int F, int NB>
 constexpr int reads_in_stage(bool odd) { return 8 + 2 * NB + (scales_in_stage<F>(odd) ? 2 : 0); }
 
@@ -337,11 +345,17 @@ __device__ __forceinline__ PairAddr pair_addr(const PipeDesc<NB> &d, int pair)
     const uint32_t kb = (uint32_t)pair * kPK;
     a.kb_oob[0] = kb + ((kb + d.lc16 < d.row_bytes) ? 0u : kOOB);
     a.kb_oob[1] = kb + ((kb + (d.lc16 ^ 16u) < d.row_bytes) ? 0u : kOOB);
-    // an atom covers 128 K elements: one pair (E4M3) or one step (E2M1)
+    if constexpr (F == FMT_E4M3_RM) {
+        // row-major scales: the pair's 4 bytes of a row follow its previous pair's
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int kt = F == FMT_E4M3 ? pair : 2 * pair + h;
-        a.so[h] = kt < d.sf_kt ? d.vs + (uint32_t)kt * 512u : kOOB;
+        for (int h = 0; h < 2; ++h) a.so[h] = pair < d.sf_kt ? d.vsr[h] + 4u * (uint32_t)pair : kOOB;
+    } else {
+        // an atom covers 128 K elements: one pair (E4M3) or one step (E2M1)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int kt = F == FMT_E4M3 ? pair : 2 * pair + h;
+            a.so[h] = kt < d.sf_kt ? d.vs + (uint32_t)kt * 512u : kOOB;
+        }
     }
     return a;
 }
@@ -356,6 +370,9 @@ __device__ __forceinline__ void load_one(const PipeDesc<NB> &d, uint8_t *st, con
         lds_load16(d.ra, st + 1024 * (8 * w + L), d.va[L] + a.kb_oob[L & 1]);
     } else if constexpr (L < 8 + LB) {
         lds_load16(d.rb, st + kPA + 1024 * (LB * w + (L - 8)), d.vb[L - 8] + a.kb_oob[(L - 8) & 1]);
+    } else if constexpr (F == FMT_E4M3_RM) {
+        constexpr int h = L - 8 - LB;      // rows 0-15 (h = 0) or 16-31 (h = 1) of each 32-row block
+        lds_load4(d.rs, st + kPA + kPB + 1024 * w + 256 * h, a.so[h]);
     } else {
         constexpr int h = L - 8 - LB;
         lds_load16(d.rs, st + kPA + kPB + 4096 * h + 1024 * w, a.so[h]);
@@ -434,7 +451,7 @@ template <int F, int PAR>
 __device__ __forceinline__ i32x4 prep_scales(i32x4 w, int kt, int kblocks, int g)
 {
     w = sanitize_scales(w, kt, kblocks);
-    const uint32_t sh = F == FMT_E4M3 ? 8u * (g + 2 * PAR) : 8u * g;
+    const uint32_t sh = is_e4m3(F) ? 8u * (g + 2 * PAR) : 8u * g;
     w.x = (int)((uint32_t)w.x >> sh);
     w.y = (int)((uint32_t)w.y >> sh);
     w.z = (int)((uint32_t)w.z >> sh);
@@ -453,7 +470,7 @@ __device__ __forceinline__ void mma_one(f32x16 (&acc)[4][NB], const Frags<NB> &f
                                         const i32x4 &sb)
 {
     constexpr int S = M / (4 * NB), i = (M % (4 * NB)) / NB, j = M % NB;
-    if constexpr (F == FMT_E4M3) {
+    if constexpr (is_e4m3(F)) {
         const i32x8 av{f.a[i][0].x, f.a[i][0].y, f.a[i][0].z, f.a[i][0].w,
                        f.a[i][1].x, f.a[i][1].y, f.a[i][1].z, f.a[i][1].w};
         const i32x8 bv{f.b[j][0].x, f.b[j][0].y, f.b[j][0].z, f.b[j][0].w,
@@ -504,7 +521,7 @@ __device__ __forceinline__ void pipe_step(f32x16 (&acc)[4][NB], Frags<NB> &cur, 
     const int g = lane >> 5;
     i32x4 sa{}, sb{};
     if constexpr (Ring<F>::kScaled) {
-        const int kt = F == FMT_E4M3 ? ks >> 1 : ks;
+        const int kt = is_e4m3(F) ? ks >> 1 : ks;
         sa = prep_scales<F, U & 1>(cur.sa, kt, d.kblocks, g);
         sb = prep_scales<F, U & 1>(cur.sb, kt, d.kblocks, g);
     }
@@ -545,7 +562,7 @@ template <int F, int NB = 4>
 __device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[4][NB], const RingSlots<F> &ring,
                                               const OperandDesc &A, const OperandDesc &B, int64_t k)
 {
-    static_assert(NB == 4 || F == FMT_BF16, "scaled formats need 128-column wave tiles");
+    static_assert(NB == 4 || F == FMT_BF16 || F == FMT_E4M3_RM, "atom scales need 128-column wave tiles");
     // the wave index is uniform: keep everything derived from it in SGPRs
     const int t = threadIdx.x, lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w >> 1, wn = w & 1;
@@ -573,7 +590,25 @@ __device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[4][NB], const RingSl
     d.sf_kt = 0;
     d.rs = d.ra;
     d.vs = kOOB;
-    if constexpr (Ring<F>::kScaled) {
+    d.vsr[0] = d.vsr[1] = kOOB;
+    if constexpr (F == FMT_E4M3_RM) {
+        // Row-major scales, staged in the layout the fragment reads expect:
+        // wave w fills 512 bytes at 1 KB * w, where the 16 bytes at 16*r32 are
+        // the pair's 4 scale bytes of the rows 32q + r32 (q = 0..3) of A row
+        // group w (w < 2), or of the NB 32-row blocks of B wave column w - 2.
+        // Each load moves 4 bytes per lane: lane l covers r32 = 16h + l/4 and
+        // q = l%4 (load h = 0, 1); rows that do not exist read zeros.
+        const OperandDesc &S = w < 2 ? A : B;
+        d.rs = make_rsrc_words(S.sf, S.sf_bytes);
+        const uint32_t q = (uint32_t)lane & 3;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t r32 = 16u * h + ((uint32_t)lane >> 2);
+            const uint32_t row = (w < 2 ? 128u * (w & 1) : 32u * NB * (w & 1)) + 32u * q + r32;
+            d.vsr[h] = (w < 2 || q < (uint32_t)NB) ? row * S.sf_rm : kOOB;
+        }
+        d.sf_kt = (int)((k + 127) / 128);
+    } else if constexpr (Ring<F>::kScaled) {
         // wave w loads the K atom of atom row group w&1 of A (w < 2) or B (w >= 2)
         const OperandDesc &S = w < 2 ? A : B;
         const int64_t mt = S.sf_mt0 + (w & 1);

@@ -2,7 +2,9 @@
 // gfx950 ("GEMM + RoPE + MXFP8 Projection (SM100)", Equations).
 //
 // One workgroup computes 256 tokens x one head (192 features) of
-// Y = x W^T with the BF16 32x32x16 MFMA (fp32 accumulation); the waves are
+// Y = x W^T with the BF16 32x32x16 MFMA, or, for MXFP8 inputs (E4M3 codes
+// with row-major E8M0 scales per 32 elements of a row), the scaled
+// 32x32x64 f8f6f4 MFMA (fp32 accumulation either way); the waves are
 // 2 (tokens) x 2 (features: 0..95 and 96..191).  The second feature wave
 // holds the rotary part (features 128..191) in two 32-column accumulator
 // blocks and applies the interleaved-in / halves-out rotation in registers
@@ -17,6 +19,7 @@ namespace bsg {
 
 struct ProjParams {
     const uint8_t *x, *w;
+    const uint8_t *x_scale, *w_scale;   // MXFP8 inputs only
     const uint16_t *cos, *sin;
     uint8_t *q_row, *s_row, *q_col, *s_col;
     int64_t tokens, q_lora, heads;
@@ -26,10 +29,11 @@ struct ProjParams {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+template <int F>
 __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
 {
     constexpr int HD = 192, HALF = 32, ROPE = 64, NBLK = HD / 32;
-    BSG_DECLARE_RING(FMT_BF16, ring);
+    BSG_DECLARE_RING(F, ring);
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
     const int c32 = lane & 31, gh = lane >> 5;
     const int64_t h = blockIdx.x;
@@ -41,8 +45,17 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
                   0, 0, 0, 0, 0};
     OperandDesc B{p.w + h * HD * p.row_bytes, (uint32_t)(HD * p.row_bytes), p.row_bytes, nullptr,
                   0, 0, 0, 0, 0};
+    if constexpr (F == FMT_E4M3_RM) {
+        const uint32_t srow = (uint32_t)(p.q_lora / 32);          // scale bytes per row
+        A.sf = p.x_scale + m0 * srow;
+        A.sf_rm = srow;
+        A.sf_bytes = (uint32_t)(rows_a * srow);
+        B.sf = p.w_scale + h * HD * srow;
+        B.sf_rm = srow;
+        B.sf_bytes = (uint32_t)(HD * srow);
+    }
     f32x16 acc[4][3];
-    mainloop_pipe<FMT_BF16, 3>(acc, ring, A, B, p.q_lora);
+    mainloop_pipe<F, 3>(acc, ring, A, B, p.q_lora);
     // Block (i, j) lane (c, g) register 4q+u: token 32i + c of the wave's rows,
     // head feature 96wn + 32j + 8q + 4g + u.
 
@@ -168,12 +181,15 @@ hipError_t launch_proj_rope(const ProjRopeArgs &a, hipStream_t s)
     ProjParams p;
     p.x = reinterpret_cast<const uint8_t *>(a.x);
     p.w = reinterpret_cast<const uint8_t *>(a.w);
+    p.x_scale = a.x_scale;
+    p.w_scale = a.w_scale;
     p.cos = a.cos; p.sin = a.sin;
     p.q_row = a.q_row; p.s_row = a.s_row; p.q_col = a.q_col; p.s_col = a.s_col;
     p.tokens = a.tokens; p.q_lora = a.q_lora; p.heads = a.heads;
-    p.row_bytes = (uint32_t)(2 * a.q_lora);
+    p.row_bytes = (uint32_t)(a.mxfp8 ? a.q_lora : 2 * a.q_lora);
     dim3 grid((unsigned)a.heads, (unsigned)((a.tokens + kTileM - 1) / kTileM));
-    hipLaunchKernelGGL(k_proj_rope, grid, dim3(kThreads), 0, s, p);
+    if (a.mxfp8) hipLaunchKernelGGL(k_proj_rope<FMT_E4M3_RM>, grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL(k_proj_rope<FMT_BF16>, grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -31,10 +31,13 @@ struct GroupedArgs {
 };
 
 struct ProjRopeArgs {
-    const uint16_t *x, *w, *cos, *sin;
+    const void *x, *w;                  // bf16, or E4M3 codes when mxfp8
+    const uint8_t *x_scale, *w_scale;   // row-major E8M0 (mxfp8 only)
+    const uint16_t *cos, *sin;
     uint8_t *q_row, *s_row, *q_col, *s_col;
     int64_t tokens, q_lora, heads, head_dim, qk_rope;
     int w_out_in;
+    int mxfp8;                          // 1: E4M3 inputs with x_scale / w_scale
 };
 
 hipError_t launch_gemm_amax(const GemmAmaxArgs &a, hipStream_t s);

@@ -68,6 +68,8 @@ def lib():
         L.orc_grouped_bf16.argtypes = [p] * 6 + [i64] * 6 + [p, p, p, p]
         L.orc_proj_rope.restype = i32
         L.orc_proj_rope.argtypes = [p] * 4 + [i64] * 5 + [i32, i64, i64, p, p]
+        L.orc_proj_rope_mx.restype = i32
+        L.orc_proj_rope_mx.argtypes = [p] * 6 + [i64] * 7 + [p, p]
         L.orc_mx_quant_rows.restype = None
         L.orc_mx_quant_rows.argtypes = [p, i64, i64, i64, ctypes.c_float, p, p]
         L.orc_mx_quant_cols.restype = None
@@ -253,6 +255,23 @@ def proj_rope(x_bits, w_bits, cos_bits, sin_bits, tokens, q_lora, heads, head_di
                          head_dim, qk_rope, int(w_out_in), t0, t1, _ptr(y), _ptr(s))
     if rc:
         raise ValueError(f"orc_proj_rope failed ({rc})")
+    return y, s
+
+
+def proj_rope_mx(x_codes, x_scale, w_codes, w_scale, cos_bits, sin_bits, tokens, q_lora, heads,
+                 head_dim, qk_rope, t0=0, t1=None):
+    """MXFP8-input projection ([PR] Shapes: E4M3 codes with row-wise E8M0 scales per
+    32 elements; w as [out, in]): rows [t0, t1) of Y after RoPE, fp64, plus Sabs."""
+    L = lib()
+    t1 = tokens if t1 is None else t1
+    x = _np(x_codes, np.uint8); xs = _np(x_scale, np.uint8)
+    w = _np(w_codes, np.uint8); ws = _np(w_scale, np.uint8)
+    cs = _np(cos_bits, np.uint16); sn = _np(sin_bits, np.uint16)
+    y = np.empty((t1 - t0, heads * head_dim)); s = np.empty_like(y)
+    rc = L.orc_proj_rope_mx(_ptr(x), _ptr(xs), _ptr(w), _ptr(ws), _ptr(cs), _ptr(sn), tokens, q_lora,
+                            heads, head_dim, qk_rope, t0, t1, _ptr(y), _ptr(s))
+    if rc:
+        raise ValueError(f"orc_proj_rope_mx failed ({rc})")
     return y, s
 
 

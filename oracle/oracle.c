@@ -426,31 +426,19 @@ int orc_grouped_bf16(const uint16_t *a, const uint16_t *b, const int32_t *offset
 /*   a_j = Y[.., nope + 2j],  b_j = Y[.., nope + 2j + 1],  j < qk_rope/2      */
 /*   out[nope + j]        = a_j cos[t, j]        - b_j sin[t, j]            */
 /*   out[nope + half + j] = b_j cos[t, half + j] + a_j sin[t, half + j]     */
-/* w_out_in = 1: w is [out, in]; 0: w is [in, out].                         */
-/* Rows [t0, t1); y_out and sabs_out (nullable) are (t1-t0, heads*head_dim). */
+/* proj_rope_rows takes x rows [t0, t1) as xr (rows x q_lora) and the weight */
+/* as wt [out][in], both already decoded to fp64, and frees them.           */
+/* y_out and sabs_out (nullable) are (t1-t0, heads*head_dim).               */
 /* ------------------------------------------------------------------------ */
-int orc_proj_rope(const uint16_t *x, const uint16_t *w, const uint16_t *cosv, const uint16_t *sinv,
-                  int64_t tokens, int64_t q_lora, int64_t heads, int64_t head_dim,
-                  int64_t qk_rope, int w_out_in, int64_t t0, int64_t t1,
-                  double *y_out, double *sabs_out)
+static int proj_rope_rows(double *xr, double *wt, const uint16_t *cosv, const uint16_t *sinv,
+                          int64_t q_lora, int64_t heads, int64_t head_dim, int64_t qk_rope,
+                          int64_t t0, int64_t t1, double *y_out, double *sabs_out)
 {
     int64_t nout = heads * head_dim, nope = head_dim - qk_rope, half = qk_rope / 2;
     int64_t rows = t1 - t0;
-    double *wt, *xr, *yr, *sr;
-    if (t0 < 0 || t1 > tokens || t0 > t1 || qk_rope % 2 || qk_rope > head_dim) return 1;
-    wt = (double *)malloc(sizeof(double) * (size_t)(nout * q_lora));
-    xr = (double *)malloc(sizeof(double) * (size_t)(q_lora * (rows > 0 ? rows : 1)));
-    yr = (double *)malloc(sizeof(double) * (size_t)(nout * (rows > 0 ? rows : 1)));
-    sr = (double *)malloc(sizeof(double) * (size_t)(nout * (rows > 0 ? rows : 1)));
-    if (!wt || !xr || !yr || !sr) { free(wt); free(xr); free(yr); free(sr); return 3; }
-    /* weight as [out][in] */
-    #pragma omp parallel for schedule(static)
-    for (int64_t o = 0; o < nout; ++o)
-        for (int64_t i = 0; i < q_lora; ++i)
-            wt[o * q_lora + i] = orc_dec_bf16(w_out_in ? w[o * q_lora + i] : w[i * nout + o]);
-    for (int64_t t = t0; t < t1; ++t)
-        for (int64_t i = 0; i < q_lora; ++i)
-            xr[(t - t0) * q_lora + i] = orc_dec_bf16(x[t * q_lora + i]);
+    double *yr = (double *)malloc(sizeof(double) * (size_t)(nout * (rows > 0 ? rows : 1)));
+    double *sr = (double *)malloc(sizeof(double) * (size_t)(nout * (rows > 0 ? rows : 1)));
+    if (!yr || !sr) { free(wt); free(xr); free(yr); free(sr); return 3; }
     #pragma omp parallel for collapse(2) schedule(static)
     for (int64_t t = t0; t < t1; ++t)
         for (int64_t o = 0; o < nout; ++o) {
@@ -490,6 +478,56 @@ int orc_proj_rope(const uint16_t *x, const uint16_t *w, const uint16_t *cosv, co
     free(yr);
     free(sr);
     return 0;
+}
+
+/* [PR] BF16 inputs.  w_out_in = 1: w is [out, in]; 0: w is [in, out].      */
+int orc_proj_rope(const uint16_t *x, const uint16_t *w, const uint16_t *cosv, const uint16_t *sinv,
+                  int64_t tokens, int64_t q_lora, int64_t heads, int64_t head_dim,
+                  int64_t qk_rope, int w_out_in, int64_t t0, int64_t t1,
+                  double *y_out, double *sabs_out)
+{
+    int64_t nout = heads * head_dim, rows = t1 - t0;
+    double *wt, *xr;
+    if (t0 < 0 || t1 > tokens || t0 > t1 || qk_rope % 2 || qk_rope > head_dim) return 1;
+    wt = (double *)malloc(sizeof(double) * (size_t)(nout * q_lora));
+    xr = (double *)malloc(sizeof(double) * (size_t)(q_lora * (rows > 0 ? rows : 1)));
+    if (!wt || !xr) { free(wt); free(xr); return 3; }
+    /* weight as [out][in] */
+    #pragma omp parallel for schedule(static)
+    for (int64_t o = 0; o < nout; ++o)
+        for (int64_t i = 0; i < q_lora; ++i)
+            wt[o * q_lora + i] = orc_dec_bf16(w_out_in ? w[o * q_lora + i] : w[i * nout + o]);
+    for (int64_t t = t0; t < t1; ++t)
+        for (int64_t i = 0; i < q_lora; ++i)
+            xr[(t - t0) * q_lora + i] = orc_dec_bf16(x[t * q_lora + i]);
+    return proj_rope_rows(xr, wt, cosv, sinv, q_lora, heads, head_dim, qk_rope, t0, t1, y_out, sabs_out);
+}
+
+/* [PR] MXFP8 inputs (Shapes: x_scale (tokens, Q_LORA/BLOCK), w_scale       */
+/* (heads*head_dim, Q_LORA/BLOCK) for the [out, in] weight; E8M0 row-wise    */
+/* block scales, BLOCK = 32):                                               */
+/*   x^[t, i] = dec_e4m3(x[t, i]) * dec_e8m0(x_scale[t, i / 32])            */
+/*   w^[o, i] = dec_e4m3(w[o, i]) * dec_e8m0(w_scale[o, i / 32])            */
+/* then the same projection and rotary embedding as the BF16 inputs.        */
+int orc_proj_rope_mx(const uint8_t *x, const uint8_t *x_scale, const uint8_t *w,
+                     const uint8_t *w_scale, const uint16_t *cosv, const uint16_t *sinv,
+                     int64_t tokens, int64_t q_lora, int64_t heads, int64_t head_dim,
+                     int64_t qk_rope, int64_t t0, int64_t t1, double *y_out, double *sabs_out)
+{
+    int64_t nout = heads * head_dim, rows = t1 - t0, nb = q_lora / 32;
+    double *wt, *xr;
+    if (t0 < 0 || t1 > tokens || t0 > t1 || qk_rope % 2 || qk_rope > head_dim || q_lora % 32) return 1;
+    wt = (double *)malloc(sizeof(double) * (size_t)(nout * q_lora));
+    xr = (double *)malloc(sizeof(double) * (size_t)(q_lora * (rows > 0 ? rows : 1)));
+    if (!wt || !xr) { free(wt); free(xr); return 3; }
+    #pragma omp parallel for schedule(static)
+    for (int64_t o = 0; o < nout; ++o)
+        for (int64_t i = 0; i < q_lora; ++i)
+            wt[o * q_lora + i] = orc_dec_e4m3(w[o * q_lora + i]) * orc_dec_e8m0(w_scale[o * nb + i / 32]);
+    for (int64_t t = t0; t < t1; ++t)
+        for (int64_t i = 0; i < q_lora; ++i)
+            xr[(t - t0) * q_lora + i] = orc_dec_e4m3(x[t * q_lora + i]) * orc_dec_e8m0(x_scale[t * nb + i / 32]);
+    return proj_rope_rows(xr, wt, cosv, sinv, q_lora, heads, head_dim, qk_rope, t0, t1, y_out, sabs_out);
 }
 
 /* ------------------------------------------------------------------------ */

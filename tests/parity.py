@@ -108,18 +108,40 @@ def e4m3_ordered(codes: np.ndarray) -> np.ndarray:
 
 def check_quant(gpu_codes: np.ndarray, gpu_scales: np.ndarray, o_codes: np.ndarray,
                 o_scales: np.ndarray, sigma_near_pow2: np.ndarray | None = None, what="",
-                max_flip_frac: float = 1e-3):
+                max_flip_frac: float = 1e-3, escape: np.ndarray | None = None,
+                max_escape_frac: float = 1e-2):
     """Scales identical (except blocks flagged near a power-of-two boundary),
-    codes equal or one step apart on at most `max_flip_frac` of elements."""
+    codes equal or one step apart on at most `max_flip_frac` of elements.
+    `escape` marks elements whose code may lie further off because the value's
+    error bound spans more than one code step (cancellation); at most
+    `max_escape_frac` of the elements may use it."""
     sc_bad = gpu_scales != o_scales
     if sigma_near_pow2 is not None:
         sc_bad &= ~sigma_near_pow2
     assert not sc_bad.any(), f"{what}: {int(sc_bad.sum())} scale bytes differ"
     d = np.abs(e4m3_ordered(gpu_codes) - e4m3_ordered(o_codes))
-    assert d.max(initial=0) <= 1, f"{what}: code differs by {d.max()} steps"
+    far = d > 1
+    esc = far & escape if escape is not None else np.zeros_like(far)
+    assert not (far & ~esc).any(), f"{what}: code differs by {d[far & ~esc].max()} steps outside the error bound"
+    n_esc = int(esc.sum())
+    assert n_esc <= max(1, max_escape_frac * d.size), f"{what}: {n_esc}/{d.size} codes use the error bound"
     flips = int((d == 1).sum())
     assert flips <= max(1, max_flip_frac * d.size), f"{what}: {flips}/{d.size} one-step flips"
-    return dict(flips=flips, n=int(d.size))
+    return dict(flips=flips, escapes=n_esc, n=int(d.size))
+
+
+def code_window(d_o: np.ndarray, bound: np.ndarray, scales: np.ndarray, axis: int, norm_const=1.0):
+    """Ordered E4M3 codes of d_o - bound and d_o + bound under the given E8M0
+    block scales (blocks of 32 along `axis`): the codes a value within the
+    error bound can take.  The encode is torch's float8_e4m3fn (RNE) after
+    saturation to +-448."""
+    inv = norm_const * 2.0 ** (127.0 - np.repeat(scales.astype(np.float64), 32, axis=axis))
+
+    def enc(v):
+        v = np.clip(v * inv, -448.0, 448.0).astype(np.float32)
+        return e4m3_ordered(torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+
+    return enc(d_o - bound), enc(d_o + bound)
 
 
 def sf_slice(sf: torch.Tensor, l: int, mn_t: int, k_t: int, mt0: int, mt1: int) -> torch.Tensor:
@@ -158,12 +180,20 @@ def check_mx_outputs(d_o: np.ndarray, bound: np.ndarray, gpu_row_codes, gpu_row_
     c_near = near_pow2_boundary(cmax, cb, norm_const)
     out = {}
     # row direction: compare codes where the block's scale agrees
+    # codes beyond one step are accepted where the value's error bound spans
+    # them (cancellation under the scaled MFMA's per-block truncation)
     same_r = np.repeat(gpu_row_scales == rs, 32, axis=1)
-    out["row"] = check_quant(np.where(same_r, gpu_row_codes, rc), gpu_row_scales, rc, rs,
-                             r_near, what=what + " row")
+    g_r = np.where(same_r, gpu_row_codes, rc)
+    lo, hi = code_window(d_o, bound, rs, 1, norm_const)
+    o_r = e4m3_ordered(g_r)
+    out["row"] = check_quant(g_r, gpu_row_scales, rc, rs, r_near, what=what + " row",
+                             escape=(o_r >= lo - 1) & (o_r <= hi + 1))
     same_c = np.repeat(gpu_col_scales == cs, 32, axis=0)
-    out["col"] = check_quant(np.where(same_c, gpu_col_codes, cc), gpu_col_scales, cc, cs,
-                             c_near, what=what + " col")
+    g_c = np.where(same_c, gpu_col_codes, cc)
+    lo, hi = code_window(d_o, bound, cs, 0, norm_const)
+    o_c = e4m3_ordered(g_c)
+    out["col"] = check_quant(g_c, gpu_col_scales, cc, cs, c_near, what=what + " col",
+                             escape=(o_c >= lo - 1) & (o_c <= hi + 1))
     out["row_scale_mismatch_near_pow2"] = int((gpu_row_scales != rs).sum())
     out["col_scale_mismatch_near_pow2"] = int((gpu_col_scales != cs).sum())
     return out

@@ -137,7 +137,13 @@ def vp(**kw):
 def test_proj_rope_validation():
     assert vp() == OK
     assert vp(tokens=200) == SHAPE                       # tokens % TILE_M (128)
-    assert vp(in_dtype=bsg.E4M3) == UNSUP                # MXFP8-input path not built
+    # MXFP8 inputs: row-major E8M0 scales required, 4-byte aligned, [out, in] weight, q_lora % 128
+    assert vp(in_dtype=bsg.E4M3) == NULLPTR
+    assert vp(in_dtype=bsg.E4M3, x_scale=P, w_scale=P) == OK
+    assert vp(in_dtype=bsg.E4M3, x_scale=P + 2, w_scale=P) == ALIGN
+    assert vp(in_dtype=bsg.E4M3, x_scale=P, w_scale=P, w_out_in=0) == UNSUP
+    assert vp(in_dtype=bsg.E4M3, x_scale=P, w_scale=P, q_lora=160) == UNSUP
+    assert vp(in_dtype=bsg.E2M1X2) == DTYPE
     assert vp(x_scale=P) == SHAPE                        # scales only on the MXFP8 path
     assert vp(head_dim=128) == UNSUP
     assert vp(q_lora=100) == SHAPE

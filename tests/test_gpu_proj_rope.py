@@ -1,5 +1,6 @@
 """GPU parity of gemm_proj_rope_mxfp8 ("GEMM + RoPE + MXFP8 Projection
-(SM100)") against the CPU oracle, through the C ABI."""
+(SM100)") against the CPU oracle, through the C ABI: BF16 inputs, and MXFP8
+inputs (E4M3 codes with row-major E8M0 scales x_scale / w_scale)."""
 import numpy as np
 import pytest
 import torch
@@ -24,19 +25,49 @@ def run_proj(p):
     qc = torch.full((T, H, D), 0xEE, dtype=torch.uint8, device="cuda")
     sr = torch.full((T, H, D // 32), 0xEE, dtype=torch.uint8, device="cuda")
     sc = torch.full((T // 32, H, D), 0xEE, dtype=torch.uint8, device="cuda")
-    bsg.gemm_proj_rope_mxfp8(t["x"], t["w"], None, None, t["cos"], t["sin"], qr, sr, qc, sc,
-                             T, s["q_lora"], H, D, s["qk_rope"], w_out_in=s["w_out_in"])
+    mx = s.get("in_dtype") == "e4m3"
+    bsg.gemm_proj_rope_mxfp8(t["x"], t["w"], t.get("x_scale"), t.get("w_scale"), t["cos"], t["sin"],
+                             qr, sr, qc, sc, T, s["q_lora"], H, D, s["qk_rope"],
+                             in_dtype=bsg.E4M3 if mx else bsg.BF16, w_out_in=s["w_out_in"])
     torch.cuda.synchronize()
     return qr, sr, qc, sc
+
+
+def mx_block_bound(p, t0, t1):
+    """Upper bound of Bmax (sum over 32-wide K blocks of the largest |product|)
+    for MXFP8 inputs: sum_b max|x^[t,b]| * max|w^[o,b]|, carried through the
+    rotary mixing with |cos| and |sin| like the oracle's Sabs."""
+    s = p.sizes
+    H, D, Q = s["heads"], s["head_dim"], s["q_lora"]
+
+    def dec(codes, scales):
+        v = codes.view(torch.float8_e4m3fn).double().numpy()
+        v = v.reshape(v.shape[0], Q // 32, 32)
+        return np.abs(v).max(-1) * 2.0 ** (scales.numpy().astype(np.float64) - 127)
+
+    bx = dec(p.t["x"][t0:t1], p.t["x_scale"][t0:t1])
+    bw = dec(p.t["w"], p.t["w_scale"])
+    b = (bx @ bw.T).reshape(t1 - t0, H, D)
+    cos = np.abs(p.t["cos"][t0:t1].double().numpy())[:, None, :]
+    sin = np.abs(p.t["sin"][t0:t1].double().numpy())[:, None, :]
+    ev, od = b[..., 128::2].copy(), b[..., 129::2].copy()
+    b[..., 128:160] = cos[..., :32] * ev + sin[..., :32] * od
+    b[..., 160:] = cos[..., 32:] * od + sin[..., 32:] * ev
+    return b.reshape(t1 - t0, H * D)
 
 
 def oracle_check(p, qr, sr, qc, sc, t0, t1, what):
     s = p.sizes
     T, H, D = s["tokens"], s["heads"], s["head_dim"]
-    y, sab = O.proj_rope(O.bits16(p.t["x"]), O.bits16(p.t["w"]), O.bits16(p.t["cos"]),
-                         O.bits16(p.t["sin"]), T, s["q_lora"], H, D, s["qk_rope"],
-                         s["w_out_in"], t0, t1)
-    bound = sum_bound(sab, s["q_lora"]) + 1e-6 * sab
+    if s.get("in_dtype") == "e4m3":
+        y, sab = O.proj_rope_mx(p.t["x"], p.t["x_scale"], p.t["w"], p.t["w_scale"], O.bits16(p.t["cos"]),
+                                O.bits16(p.t["sin"]), T, s["q_lora"], H, D, s["qk_rope"], t0, t1)
+        bound = sum_bound(sab, s["q_lora"], bmax=mx_block_bound(p, t0, t1)) + 1e-6 * sab
+    else:
+        y, sab = O.proj_rope(O.bits16(p.t["x"]), O.bits16(p.t["w"]), O.bits16(p.t["cos"]),
+                             O.bits16(p.t["sin"]), T, s["q_lora"], H, D, s["qk_rope"],
+                             s["w_out_in"], t0, t1)
+        bound = sum_bound(sab, s["q_lora"]) + 1e-6 * sab
     N = H * D
     res = check_mx_outputs(y, bound, qr[t0:t1].reshape(t1 - t0, N).cpu().numpy(),
                            sr[t0:t1].reshape(t1 - t0, N // 32).cpu().numpy(),
@@ -78,3 +109,43 @@ def test_proj_rope_full_size_sampled():
     for t0 in (0, 3968):
         say(f"  oracle tokens {t0}..{t0 + 127}")
         oracle_check(p, qr, sr, qc, sc, t0, t0 + 128, f"tokens {t0}")
+
+
+@pytest.mark.parametrize("case", [
+    dict(tokens=256, q_lora=256, heads=3),
+    dict(tokens=384, q_lora=128, heads=2),     # a 128-token tail tile
+    dict(tokens=128, q_lora=1536, heads=1),
+])
+def test_proj_rope_mxfp8_inputs_match_oracle(case):
+    say(f"proj_rope MXFP8-input parity {case}")
+    p = W.proj_rope_problem(case["tokens"], case["q_lora"], case["heads"], seed=7, in_dtype="e4m3")
+    qr, sr, qc, sc = run_proj(p)
+    oracle_check(p, qr, sr, qc, sc, 0, case["tokens"], "mx " + str(case))
+
+
+def test_proj_rope_mxfp8_unit_scales_equal_bf16_path():
+    """With every scale byte 127 the MXFP8-input call sees the same values as
+    the BF16-input call on the decoded codes (exact in bf16)."""
+    say("proj_rope MXFP8 unit scales vs BF16 path")
+    p = W.proj_rope_problem(256, 256, 2, seed=8, in_dtype="e4m3")
+    p.t["x_scale"].fill_(127)
+    p.t["w_scale"].fill_(127)
+    mx = run_proj(p)
+    pb = W.proj_rope_problem(256, 256, 2, seed=8)
+    pb.t["x"] = p.t["x"].view(torch.float8_e4m3fn).to(torch.bfloat16)
+    pb.t["w"] = p.t["w"].view(torch.float8_e4m3fn).to(torch.bfloat16)
+    pb.t["cos"], pb.t["sin"] = p.t["cos"], p.t["sin"]
+    bf = run_proj(pb)
+    oracle_check(p, *mx, 0, 256, "mx unit scales")
+    oracle_check(pb, *bf, 0, 256, "bf16 of the same values")
+
+
+def test_proj_rope_mxfp8_full_size_sampled():
+    """MXFP8 x (4096,1536), w (24576,1536), 128 heads x 192: sampled panels vs the oracle."""
+    say("proj_rope MXFP8 full size")
+    p = W.proj_rope_dsv3(device="cuda", in_dtype="e4m3")
+    qr, sr, qc, sc = run_proj(p)
+    p.t = {k: v.cpu() for k, v in p.t.items()}
+    for t0 in (0, 3968):
+        say(f"  oracle tokens {t0}..{t0 + 127}")
+        oracle_check(p, qr, sr, qc, sc, t0, t0 + 128, f"mx tokens {t0}")

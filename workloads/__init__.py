@@ -255,19 +255,33 @@ def rope_tables(tokens: int, rope_dim: int = 64, base: float = 10000.0, device="
 
 def proj_rope_problem(tokens: int, q_lora: int, heads: int = 128, head_dim: int = 192,
                       qk_rope: int = 64, *, seed: int = 0, device="cpu",
-                      w_out_in: bool = True) -> Problem:
+                      w_out_in: bool = True, in_dtype: str = "bf16") -> Problem:
     """x (tokens,Q_LORA) bf16 N(0,1); w bf16 N(0,0.02), [out,in] when w_out_in
-    else [in,out]; bf16 cos/sin (tokens,qk_rope) from positions, base 10000."""
+    else [in,out]; bf16 cos/sin (tokens,qk_rope) from positions, base 10000.
+
+    in_dtype "e4m3" (MXFP8 inputs, w [out,in] only): x and w are E4M3 codes of
+    block-stretched normal draws with row-major E8M0 scale bytes x_scale
+    (tokens, Q_LORA/32) and w_scale (out, Q_LORA/32), drawn around the bytes
+    that give N(0,1) and N(0,0.02) magnitudes (w six binades below x)."""
     g = _gen(seed + 3, device)
-    x = torch.randn(tokens, q_lora, generator=g, device=device).to(torch.bfloat16)
-    w = (torch.randn(heads * head_dim, q_lora, generator=g, device=device) * 0.02).to(torch.bfloat16)
-    if not w_out_in:
-        w = w.t().contiguous()
+    extra = {}
+    if in_dtype == E4M3:
+        assert w_out_in, "MXFP8 inputs take w as [out, in]"
+        x = _codes_from_normal(torch.randn(tokens, q_lora, generator=g, device=device), E4M3)
+        w = _codes_from_normal(torch.randn(heads * head_dim, q_lora, generator=g, device=device), E4M3)
+        extra["x_scale"] = _sf_bytes(tokens * (q_lora // 32), 120, 1, g, device).reshape(tokens, q_lora // 32)
+        extra["w_scale"] = _sf_bytes(heads * head_dim * (q_lora // 32), 114, 1, g, device).reshape(
+            heads * head_dim, q_lora // 32)
+    else:
+        x = torch.randn(tokens, q_lora, generator=g, device=device).to(torch.bfloat16)
+        w = (torch.randn(heads * head_dim, q_lora, generator=g, device=device) * 0.02).to(torch.bfloat16)
+        if not w_out_in:
+            w = w.t().contiguous()
     cos, sin = rope_tables(tokens, qk_rope, device=device)
     return Problem("gemm_proj_rope_mxfp8",
                    dict(tokens=tokens, q_lora=q_lora, heads=heads, head_dim=head_dim,
-                        qk_rope=qk_rope, w_out_in=int(w_out_in)),
-                   dict(x=x.contiguous(), w=w.contiguous(), cos=cos, sin=sin))
+                        qk_rope=qk_rope, w_out_in=int(w_out_in), in_dtype=in_dtype),
+                   dict(x=x.contiguous(), w=w.contiguous(), cos=cos, sin=sin, **extra))
 
 
 # ---------------------------------------------------------------------------
@@ -297,6 +311,6 @@ def moe_mxfp8_srelu(device="cuda", seed=0, tokens=28672, experts=32, n=4096, k=7
                                  tanh_clamp=32.0, d_dtype=d_dtype, **kw)
 
 
-def proj_rope_dsv3(device="cuda", seed=0, tokens=4096):
+def proj_rope_dsv3(device="cuda", seed=0, tokens=4096, in_dtype="bf16"):
     """DeepSeek-V3 Q up-projection: x (4096,1536), 128 heads x 192, rope on trailing 64."""
-    return proj_rope_problem(tokens, 1536, 128, 192, 64, seed=seed, device=device)
+    return proj_rope_problem(tokens, 1536, 128, 192, 64, seed=seed, device=device, in_dtype=in_dtype)
