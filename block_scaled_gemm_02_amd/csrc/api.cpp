@@ -399,8 +399,9 @@ int bsg_validate_gemm_proj_rope_mxfp8(const void *x, const void *w, const uint8_
     if (head_dim != 192 || qk_rope != 64)
         return fail(BSG_ERR_UNSUPPORTED, "only head_dim 192 with qk_rope 64 is built");
     if (w_out_in != 0 && w_out_in != 1) return fail(BSG_ERR_SHAPE, "w_out_in must be 0 or 1");
-    if (mx && !w_out_in)
-        return fail(BSG_ERR_UNSUPPORTED, "MXFP8 inputs need w as [out, in] (transpose codes and w_scale first)");
+    if (!w_out_in)
+        return fail(BSG_ERR_UNSUPPORTED, "w as [in, out] (w_out_in = 0) is not built: pass w as [out, in]%s",
+                    mx ? " (transpose the codes and w_scale)" : "");
     if (mx && q_lora % 128)
         return fail(BSG_ERR_UNSUPPORTED, "MXFP8 inputs need q_lora to be a multiple of 128");
     if (tokens * num_heads == 0) return BSG_OK;

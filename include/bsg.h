@@ -203,9 +203,9 @@ int grouped_gemm_srelu_discrete(const void *a, const uint64_t *b_ptrs, const uin
  *
  *  x    (tokens, q_lora) row-major: bf16 (in_dtype BF16) or E4M3 codes
  *       (in_dtype E4M3, the page's MXFP8-input path)
- *  w    w_out_in = 1: (num_heads*head_dim, q_lora) [out, in];
- *       w_out_in = 0: (q_lora, num_heads*head_dim) [in, out] (BF16 only);
- *       same dtype as x
+ *  w    w_out_in = 1: (num_heads*head_dim, q_lora) [out, in], same dtype
+ *       as x.  w_out_in = 0 ([in, out]) returns UNSUPPORTED: that layout is
+ *       not built.
  *  x_scale  (tokens, q_lora/32) E8M0, row-major: byte (t, b) scales
  *           x[t, 32b .. 32b+31]                      (E4M3 inputs only)
  *  w_scale  (num_heads*head_dim, q_lora/32) E8M0, row-major, [out, in]
@@ -217,10 +217,10 @@ int grouped_gemm_srelu_discrete(const void *a, const uint64_t *b_ptrs, const uin
  *  out_scales_row             (tokens, num_heads, head_dim/32) E8M0
  *  out_scales_col             (tokens/32, num_heads, head_dim) E8M0
  *  Sizes: tokens % 128 == 0, q_lora % 32 == 0 (BF16) or % 128 == 0
- *  (E4M3), head_dim == 192, qk_rope == 64.  E4M3 inputs need w_out_in = 1
- *  (the page's class API takes [out, in] codes and scales; an [in, out]
- *  weight is transposed by the caller) and 4-byte aligned x_scale/w_scale;
- *  otherwise UNSUPPORTED / ALIGN before anything is enqueued.
+ *  (E4M3), head_dim == 192, qk_rope == 64.  E4M3 inputs need 4-byte
+ *  aligned x_scale/w_scale (the page's MXFP8 class API also takes [out, in]
+ *  codes and scales only).  Violations return SHAPE / UNSUPPORTED / ALIGN
+ *  before anything is enqueued.
  */
 int gemm_proj_rope_mxfp8(const void *x, const void *w, const uint8_t *x_scale,
                          const uint8_t *w_scale, const void *cos, const void *sin,

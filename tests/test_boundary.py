@@ -147,4 +147,4 @@ def test_proj_rope_validation():
     assert vp(x_scale=P) == SHAPE                        # scales only on the MXFP8 path
     assert vp(head_dim=128) == UNSUP
     assert vp(q_lora=100) == SHAPE
-    assert vp(w_out_in=0) == OK
+    assert vp(w_out_in=0) == UNSUP                       # [in, out] weight not built
