@@ -112,7 +112,7 @@ def dtype_code(x) -> int:
 
 
 def _ab_code(fmt) -> int:
-    return {"e4m3": E4M3, "e2m1": E2M1X2, E4M3: E4M3, E2M1X2: E2M1X2, E5M2: E5M2}[fmt]
+    return {"e4m3": E4M3, "e5m2": E5M2, "e2m1": E2M1X2, E4M3: E4M3, E2M1X2: E2M1X2, E5M2: E5M2}[fmt]
 
 
 # ---------------------------------------------------------------------------

@@ -68,11 +68,8 @@ int launch_status(hipError_t e, const char *what)
 
 int check_ab_sf(int ab_dtype, int sf_vec_size)
 {
-    if (ab_dtype != BSG_E4M3 && ab_dtype != BSG_E2M1X2) {
-        if (ab_dtype == BSG_E5M2)
-            return fail(BSG_ERR_UNSUPPORTED, "ab_dtype E5M2 is not built (E4M3 and E2M1X2 are)");
+    if (ab_dtype != BSG_E4M3 && ab_dtype != BSG_E5M2 && ab_dtype != BSG_E2M1X2)
         return fail(BSG_ERR_DTYPE, "ab_dtype %d is not a block-scaled operand dtype", ab_dtype);
-    }
     if (sf_vec_size != 32) {
         if (sf_vec_size == 16)
             return fail(BSG_ERR_UNSUPPORTED, "sf_vec_size 16 is not built (32 is)");
@@ -82,6 +79,9 @@ int check_ab_sf(int ab_dtype, int sf_vec_size)
 }
 
 int row_bytes(int ab_dtype, int64_t k) { return (int)(ab_dtype == BSG_E2M1X2 ? k / 2 : k); }
+
+// Kernel operand format of a block-scaled ab_dtype (bsg::Fmt values).
+int fmt_of(int ab_dtype) { return ab_dtype == BSG_E2M1X2 ? 1 : (ab_dtype == BSG_E5M2 ? 4 : 0); }
 
 }  // namespace
 
@@ -152,7 +152,7 @@ int gemm_amax(const void *a, const void *b, const uint8_t *sfa, const uint8_t *s
     if (st) return st;
     if ((st = check_device())) return st;
     bsg::GemmAmaxArgs args{static_cast<const uint8_t *>(a), static_cast<const uint8_t *>(b), sfa, sfb,
-                           c, amax, m, n, k, l, ab_dtype == BSG_E2M1X2 ? 1 : 0, c_dtype};
+                           c, amax, m, n, k, l, fmt_of(ab_dtype), c_dtype};
     return launch_status(bsg::launch_gemm_amax(args, static_cast<hipStream_t>(stream)), "gemm_amax");
 }
 
@@ -281,7 +281,7 @@ static int validate_srelu(const void *a, const void *b, const uint8_t *sfa, cons
         return fail(BSG_ERR_DTYPE, "D dtype %d invalid", d_dtype);
     }
     if (fp8_out) {
-        if (ab_dtype != BSG_E4M3)
+        if (ab_dtype == BSG_E2M1X2)
             return fail(BSG_ERR_DTYPE, "FP8 D requires FP8 A/B (FP4 inputs take fp16/bf16/fp32 D)");
         if (!norm_const || !sfd_row || !sfd_col || !d_col)
             return fail(BSG_ERR_NULLPTR, "FP8 D needs norm_const, d_col, sfd_row and sfd_col");
@@ -321,7 +321,7 @@ static int run_srelu(const void *a, const void *b, const uint64_t *b_ptrs, const
     args.sfd_row = sfd_row; args.sfd_col = sfd_col;
     args.amax = d_dtype == BSG_E4M3 ? nullptr : amax;
     args.m = m; args.n = n; args.k = k; args.num_experts = num_experts;
-    args.fmt = ab_dtype == BSG_E2M1X2 ? 1 : 0; args.c_dtype = c_dtype; args.d_dtype = d_dtype;
+    args.fmt = fmt_of(ab_dtype); args.c_dtype = c_dtype; args.d_dtype = d_dtype;
     args.tanh_s = tanh_clamp_scale > 0.0f ? tanh_clamp_scale : 0.0f;
     return launch_status(bsg::launch_grouped_srelu(args, static_cast<hipStream_t>(stream)), name);
 }

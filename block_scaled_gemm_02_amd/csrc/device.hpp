@@ -48,8 +48,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // FMT_E4M3_RM: E4M3 codes whose E8M0 scales are row-major, one byte per 32
 // K elements of a row ("GEMM + RoPE + MXFP8 Projection (SM100)", x_scale and
 // w_scale), instead of the scale-atom layout of the other block-scaled ops.
-enum Fmt : int { FMT_E4M3 = 0, FMT_E2M1 = 1, FMT_BF16 = 2, FMT_E4M3_RM = 3 };
-constexpr bool is_e4m3(int f) { return f == FMT_E4M3 || f == FMT_E4M3_RM; }
+// FMT_E5M2: E5M2 codes (one byte each) with scale atoms, like FMT_E4M3.
+enum Fmt : int { FMT_E4M3 = 0, FMT_E2M1 = 1, FMT_BF16 = 2, FMT_E4M3_RM = 3, FMT_E5M2 = 4 };
+// one-byte codes: one 32x32x64 MFMA per block per 64-byte step
+constexpr bool is_fp8(int f) { return f == FMT_E4M3 || f == FMT_E4M3_RM || f == FMT_E5M2; }
 
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;
@@ -219,7 +221,7 @@ constexpr int kPB = 256 * kPK;             // 32 KB (NB = 4)
 template <int F>
 struct Ring {
     static constexpr bool kScaled = F != FMT_BF16;
-    static constexpr int kScaleSets = F == FMT_E2M1 ? 2 : (is_e4m3(F) ? 1 : 0);
+    static constexpr int kScaleSets = F == FMT_E2M1 ? 2 : (is_fp8(F) ? 1 : 0);
     static constexpr int kSlot = kPA + kPB + kScaleSets * 4096;
     static constexpr int kBytes = 2 * kSlot;
     static constexpr int kWaveStage = kSlot / 2 & ~15;   // epilogue staging bytes per wave
@@ -324,11 +326,11 @@ __device__ __forceinline__ uint8_t *wave_stage(const RingSlots<F> &ring, int w)
 // covers a whole pair (128 K elements): it is read with the even stage, and
 // the odd stage reuses the even stage's scale words.
 template <int F>
-constexpr bool scales_in_stage(bool odd) { return Ring<F>::kScaled && !(is_e4m3(F) && odd); }
+constexpr bool scales_in_stage(bool odd) { return Ring<F>::kScaled && !(is_fp8(F) && odd); }
 template <int F, int NB>
 constexpr int loads_per_pair() { return 8 + 2 * NB + (F == FMT_E4M3_RM ? 2 : Ring<F>::kScaleSets); }
 template <int F, int NB>
-constexpr int mfmas_per_step() { return (is_e4m3(F) ? 1 : 2) * 4 * NB; }
+constexpr int mfmas_per_step() { return (is_fp8(F) ? 1 : 2) * 4 * NB; }
 template <int F, int NB>
 constexpr int reads_in_stage(bool odd) { return 8 + 2 * NB + (scales_in_stage<F>(odd) ? 2 : 0); }
 
@@ -353,7 +355,7 @@ __device__ __forceinline__ PairAddr pair_addr(const PipeDesc<NB> &d, int pair)
         // an atom covers 128 K elements: one pair (E4M3) or one step (E2M1)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int kt = F == FMT_E4M3 ? pair : 2 * pair + h;
+            const int kt = F == FMT_E2M1 ? 2 * pair + h : pair;
             a.so[h] = kt < d.sf_kt ? d.vs + (uint32_t)kt * 512u : kOOB;
         }
     }
@@ -451,7 +453,7 @@ template <int F, int PAR>
 __device__ __forceinline__ i32x4 prep_scales(i32x4 w, int kt, int kblocks, int g)
 {
     w = sanitize_scales(w, kt, kblocks);
-    const uint32_t sh = is_e4m3(F) ? 8u * (g + 2 * PAR) : 8u * g;
+    const uint32_t sh = is_fp8(F) ? 8u * (g + 2 * PAR) : 8u * g;
     w.x = (int)((uint32_t)w.x >> sh);
     w.y = (int)((uint32_t)w.y >> sh);
     w.z = (int)((uint32_t)w.z >> sh);
@@ -470,12 +472,14 @@ __device__ __forceinline__ void mma_one(f32x16 (&acc)[4][NB], const Frags<NB> &f
                                         const i32x4 &sb)
 {
     constexpr int S = M / (4 * NB), i = (M % (4 * NB)) / NB, j = M % NB;
-    if constexpr (is_e4m3(F)) {
+    if constexpr (is_fp8(F)) {
         const i32x8 av{f.a[i][0].x, f.a[i][0].y, f.a[i][0].z, f.a[i][0].w,
                        f.a[i][1].x, f.a[i][1].y, f.a[i][1].z, f.a[i][1].w};
         const i32x8 bv{f.b[j][0].x, f.b[j][0].y, f.b[j][0].z, f.b[j][0].w,
                        f.b[j][1].x, f.b[j][1].y, f.b[j][1].z, f.b[j][1].w};
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], 0, 0, 0, sb[j], 0,
+        // operand format: 0 = E4M3, 1 = E5M2 (for both operands)
+        constexpr int fm = F == FMT_E5M2 ? 1 : 0;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], fm, fm, 0, sb[j], 0,
                                                                       sa[i]);
     } else if constexpr (F == FMT_E2M1) {
         const i32x8 av{f.a[i][S].x, f.a[i][S].y, f.a[i][S].z, f.a[i][S].w, 0, 0, 0, 0};
@@ -521,7 +525,7 @@ __device__ __forceinline__ void pipe_step(f32x16 (&acc)[4][NB], Frags<NB> &cur, 
     const int g = lane >> 5;
     i32x4 sa{}, sb{};
     if constexpr (Ring<F>::kScaled) {
-        const int kt = is_e4m3(F) ? ks >> 1 : ks;
+        const int kt = is_fp8(F) ? ks >> 1 : ks;
         sa = prep_scales<F, U & 1>(cur.sa, kt, d.kblocks, g);
         sb = prep_scales<F, U & 1>(cur.sb, kt, d.kblocks, g);
     }

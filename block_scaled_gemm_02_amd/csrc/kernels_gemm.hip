@@ -135,6 +135,7 @@ hipError_t launch_gemm_amax(const GemmAmaxArgs &a, hipStream_t s)
     p.c_dtype = a.c_dtype;
     dim3 grid((unsigned)(((a.n + kTileN - 1) / kTileN) * ((a.m + kTileM - 1) / kTileM) * a.l));
     if (a.fmt == FMT_E4M3) launch_gemm_amax_fmt<FMT_E4M3>(p, grid, s);
+    else if (a.fmt == FMT_E5M2) launch_gemm_amax_fmt<FMT_E5M2>(p, grid, s);
     else launch_gemm_amax_fmt<FMT_E2M1>(p, grid, s);
     return hipGetLastError();
 }
@@ -477,10 +478,13 @@ hipError_t launch_grouped_srelu(const GroupedArgs &a, hipStream_t s)
     GroupedParams p = grouped_params(a);
     dim3 grid((unsigned)(((a.n + kTileN - 1) / kTileN) * (a.m / kTileM)));
     if (a.d_dtype == DT_E4M3) {
-        if (a.fmt != FMT_E4M3) return hipErrorNotSupported;
-        launch_srelu_variant<FMT_E4M3, EPI_SRELU_FP8>(p, grid, s);
+        if (a.fmt == FMT_E4M3) launch_srelu_variant<FMT_E4M3, EPI_SRELU_FP8>(p, grid, s);
+        else if (a.fmt == FMT_E5M2) launch_srelu_variant<FMT_E5M2, EPI_SRELU_FP8>(p, grid, s);
+        else return hipErrorNotSupported;
     } else if (a.fmt == FMT_E4M3) {
         launch_srelu_variant<FMT_E4M3, EPI_SRELU>(p, grid, s);
+    } else if (a.fmt == FMT_E5M2) {
+        launch_srelu_variant<FMT_E5M2, EPI_SRELU>(p, grid, s);
     } else {
         launch_srelu_variant<FMT_E2M1, EPI_SRELU>(p, grid, s);
     }

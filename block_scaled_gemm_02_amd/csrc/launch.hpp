@@ -11,7 +11,7 @@ struct GemmAmaxArgs {
     void *c;
     float *amax;
     int64_t m, n, k, l;
-    int fmt;       // 0 = E4M3, 1 = E2M1
+    int fmt;       // bsg::Fmt: 0 = E4M3, 1 = E2M1, 4 = E5M2
     int c_dtype;   // bsg_dtype
 };
 
@@ -25,7 +25,7 @@ struct GroupedArgs {
     uint8_t *sfd_row, *sfd_col;
     float *amax;
     int64_t m, n, k, num_experts;
-    int fmt;        // 0 = E4M3, 1 = E2M1, 2 = BF16
+    int fmt;        // bsg::Fmt: 0 = E4M3, 1 = E2M1, 2 = BF16, 4 = E5M2
     int c_dtype, d_dtype, bias_dtype;
     float tanh_s;   // <= 0: no clamp
 };

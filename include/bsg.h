@@ -79,14 +79,15 @@ typedef enum bsg_dtype {
  *     Amax     = max_{m,n,l} |C[m,n,l]|
  * with dequant(X)[r,k,l] = X[r,k,l] * 2^(SF byte - 127) per 32-wide K block.
  *
- *  a     (M,K,L) codes, k-major; E4M3: M*K*L bytes; E2M1X2: M*(K/2)*L bytes
+ *  a     (M,K,L) codes, k-major; E4M3 / E5M2: M*K*L bytes; E2M1X2: M*(K/2)*L bytes
  *  b     (N,K,L) codes, k-major, same dtype as a
  *  sfa   scale atoms over (M, K, L);  sfb: scale atoms over (N, K, L)
  *  c     (M,N,L) output, n-major, c_dtype in {F32, BF16, F16}; RNE cast
  *        of the fp32 accumulator
  *  amax  one float32 (nullable): max |C| of the fp32 accumulators (before
  *        the output cast); the library zero-fills it on `stream` first
- *  ab_dtype in {E4M3, E2M1X2}; sf_vec_size must be 32.
+ *  ab_dtype in {E4M3, E5M2, E2M1X2} (the page's float8_e4m3fn, float8_e5m2
+ *  and float4_e2m1fn_x2 A/B); sf_vec_size must be 32.
  *  Sizes: M, N, L >= 0; K >= 0 with K % 32 == 0.  M or N need not be tile
  *  multiples.  Accumulation is fp32 (the pages' only accumulator dtype).
  */
@@ -145,7 +146,8 @@ int grouped_gemm(const void *a, const void *b, const int32_t *padded_offsets,
  *      sfd_col  scale atoms over (N, M, 1)  (MN = N, "K" = M)
  *      norm_const (1,) fp32 device scalar, required
  *  tanh_clamp_scale: s; a value <= 0 means no clamp (the pages' None).
- *  ab_dtype in {E4M3, E2M1X2}; sf_vec_size == 32.
+ *  ab_dtype in {E4M3, E5M2, E2M1X2}; sf_vec_size == 32.  E4M3 D needs FP8
+ *  (E4M3 or E5M2) A/B.
  *  Sizes: M % 256 == 0, 1 <= L <= 1024, K % 32 == 0, N % 32 == 0.
  *  Rows at or past padded_offsets[L-1] are not written.
  */

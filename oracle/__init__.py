@@ -25,8 +25,8 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-E4M3, E2M1 = 0, 1
-_FMT = {"e4m3": E4M3, "e2m1": E2M1, E4M3: E4M3, E2M1: E2M1}
+E4M3, E2M1, E5M2 = 0, 1, 2
+_FMT = {"e4m3": E4M3, "e2m1": E2M1, "e5m2": E5M2, E4M3: E4M3, E2M1: E2M1, E5M2: E5M2}
 
 
 def build(force: bool = False) -> str:
@@ -50,6 +50,7 @@ def lib():
                                ctypes.c_int, ctypes.c_void_p)
         L.orc_dec_e4m3.restype = d; L.orc_dec_e4m3.argtypes = [u32]
         L.orc_dec_e2m1.restype = d; L.orc_dec_e2m1.argtypes = [u32]
+        L.orc_dec_e5m2.restype = d; L.orc_dec_e5m2.argtypes = [u32]
         L.orc_dec_e8m0.restype = d; L.orc_dec_e8m0.argtypes = [u32]
         L.orc_dec_bf16.restype = d; L.orc_dec_bf16.argtypes = [u32]
         L.orc_enc_e4m3.restype = u32; L.orc_enc_e4m3.argtypes = [d]
@@ -111,6 +112,7 @@ def threads() -> int:
 # ---------------------------------------------------------------------------
 def dec_e4m3(code: int) -> float: return lib().orc_dec_e4m3(code)
 def dec_e2m1(nib: int) -> float: return lib().orc_dec_e2m1(nib)
+def dec_e5m2(code: int) -> float: return lib().orc_dec_e5m2(code)
 def dec_e8m0(b: int) -> float: return lib().orc_dec_e8m0(b)
 def dec_bf16(h: int) -> float: return lib().orc_dec_bf16(h)
 def enc_e4m3(x: float) -> int: return lib().orc_enc_e4m3(float(x))

@@ -18,7 +18,8 @@
  *   [GB]  "Grouped GEMM (SM100 BF16)": Operation; Tensors and layouts.
  *   [PR]  "GEMM + RoPE + MXFP8 Projection (SM100)": Equations; Shapes.
  * Number formats follow the OCP Microscaling (MX) v1.0 definitions of
- * E4M3 ("fn", no infinities), E2M1 and E8M0.
+ * E4M3 ("fn", no infinities), E5M2 (IEEE-like, with Inf and NaN), E2M1 and
+ * E8M0.
  *
  * Build: gcc -O2 -fopenmp -shared -fPIC oracle.c -o liboracle.so -lm
  */
@@ -44,6 +45,19 @@ double orc_dec_e4m3(uint32_t code)
     if (e == 15u && m == 7u) return NAN;
     if (e == 0u) v = ldexp((double)m / 8.0, -6);
     else v = ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+    return s ? -v : v;
+}
+
+/* E5M2: 1 sign, 5 exponent bits (bias 15), 2 mantissa bits, IEEE-like:
+ * exponent field 0 is subnormal (m/4 * 2^-14); field 31 is Inf (m = 0) or
+ * NaN.  Largest finite magnitude 57344. */
+double orc_dec_e5m2(uint32_t code)
+{
+    uint32_t s = (code >> 7) & 1u, e = (code >> 2) & 31u, m = code & 3u;
+    double v;
+    if (e == 31u) v = m ? NAN : INFINITY;
+    else if (e == 0u) v = ldexp((double)m / 4.0, -14);
+    else v = ldexp(1.0 + (double)m / 4.0, (int)e - 15);
     return s ? -v : v;
 }
 
@@ -187,10 +201,11 @@ void orc_sf_offset_grid(int64_t r0, int64_t r1, int64_t nkb, int64_t l, int64_t 
 /* Dequantisation ([GA] Equations: A_hat = dequantize(A, SFA, sf_vec_size)) */
 /* ------------------------------------------------------------------------ */
 /* fmt 0: one E4M3 code per byte.  fmt 1: E2M1, two per byte, element 2j in
- * the low nibble and 2j+1 in the high nibble. */
+ * the low nibble and 2j+1 in the high nibble.  fmt 2: one E5M2 code per byte. */
 static double code_value(const uint8_t *row, int fmt, int64_t kk)
 {
     if (fmt == 0) return orc_dec_e4m3(row[kk]);
+    if (fmt == 2) return orc_dec_e5m2(row[kk]);
     {
         uint8_t byte = row[kk >> 1];
         return orc_dec_e2m1((kk & 1) ? (byte >> 4) : (byte & 15u));
@@ -201,7 +216,7 @@ static double code_value(const uint8_t *row, int fmt, int64_t kk)
 static void dequant_row(const uint8_t *codes, const uint8_t *sf, int fmt,
                         int64_t r, int64_t l, int64_t mn, int64_t k, double *out)
 {
-    int64_t rowbytes = fmt == 0 ? k : k / 2;
+    int64_t rowbytes = fmt == 1 ? k / 2 : k;
     int64_t kblocks = (k + 31) / 32;
     const uint8_t *row = codes + (l * mn + r) * rowbytes;
     for (int64_t kk = 0; kk < k; ++kk) {

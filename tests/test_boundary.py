@@ -40,7 +40,7 @@ def va(**kw):
 
 def test_gemm_amax_validation():
     assert va() == OK
-    assert va(ab_dtype=bsg.E5M2) == UNSUP              # E5M2 not built
+    assert va(ab_dtype=bsg.E5M2) == OK                 # float8_e5m2 A/B
     assert va(sf_vec_size=16) == UNSUP                   # NVFP4-style sf 16 not built
     assert va(sf_vec_size=8) == SHAPE
     assert va(k=48) == SHAPE                             # K % 32

@@ -36,6 +36,8 @@ def run_gemm(p, c_dtype=torch.float32):
     dict(m=260, n=136, k=352, l=2, fmt="e2m1", c=torch.float32, plain=False),
     dict(m=512, n=512, k=1024, l=1, fmt="e2m1", c=torch.bfloat16, plain=False),
     dict(m=33, n=40, k=32, l=3, fmt="e4m3", c=torch.float16, plain=False),
+    dict(m=300, n=200, k=256, l=2, fmt="e5m2", c=torch.float32, plain=False),
+    dict(m=512, n=264, k=640, l=1, fmt="e5m2", c=torch.bfloat16, plain=False),
 ])
 def test_gemm_amax_matches_oracle(case):
     say(f"gemm_amax parity {case}")

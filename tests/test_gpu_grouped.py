@@ -49,6 +49,8 @@ SRELU_CASES = [
     dict(sizes=[0, 256, 256], n=288, k=256, fmt="e2m1", s=32.0, c=torch.bfloat16, d=torch.bfloat16),
     dict(sizes=[256], n=512, k=1024, fmt="e2m1", s=0.0, c=torch.float32, d=torch.bfloat16),
     dict(sizes=[256, 512], n=224, k=320, fmt="e4m3", s=0.0, c=torch.bfloat16, d=torch.bfloat16),
+    dict(sizes=[512, 0, 256], n=256, k=384, fmt="e5m2", s=32.0, c=torch.bfloat16, d=torch.bfloat16),
+    dict(sizes=[256, 256], n=160, k=256, fmt="e5m2", s=0.0, c=torch.float32, d=torch.float32),
 ]
 
 
@@ -185,6 +187,7 @@ FP8_CASES = [
     dict(sizes=[256, 0, 512, 256], n=320, k=192, s=32.0, nc=1.0),
     dict(sizes=[512, 256], n=256, k=512, s=0.0, nc=1.0),
     dict(sizes=[0, 256, 256], n=128, k=256, s=0.5, nc=4.0),
+    dict(sizes=[256, 512], n=192, k=256, s=32.0, nc=1.0, fmt="e5m2"),
 ]
 
 
@@ -193,14 +196,15 @@ def test_grouped_srelu_fp8_out_matches_oracle(case):
     say(f"grouped_srelu fp8 out {case}")
     off = np.cumsum(case["sizes"]).astype(np.int32)
     L = len(case["sizes"])
-    p = W.grouped_srelu_problem(0, L, case["n"], case["k"], "e4m3", seed=4, offsets=off,
+    fmt = case.get("fmt", "e4m3")
+    p = W.grouped_srelu_problem(0, L, case["n"], case["k"], fmt, seed=4, offsets=off,
                                 tanh_clamp=case["s"], extra_rows=256, d_dtype="e4m3")
     p.t["norm_const"] = torch.tensor([case["nc"]])
     s = p.sizes
     m, n, k = s["m"], s["n"], s["k"]
     c, d, d_col, sfd_row, sfd_col = run_srelu_fp8(p)
     r = O.grouped_srelu(p.t["a"], p.t["b"], p.t["sfa"], p.t["sfb"], off, p.t["alpha"], p.t["prob"],
-                        m, n, k, L, "e4m3", s["tanh_clamp"])
+                        m, n, k, L, fmt, s["tanh_clamp"])
     valid = s["valid_m"]
     prob = p.t["prob"].double().numpy()
     bc = sum_bound(r["sabs"], k, bmax=r["bmax"])

@@ -32,6 +32,19 @@ def test_e4m3_decode_matches_torch_all_codes():
     assert O.dec_e4m3(0x7E) == 448.0 and O.dec_e4m3(0x01) == 2.0 ** -9
 
 
+def test_e5m2_decode_matches_torch_all_codes():
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e5m2).double()
+    for c in range(256):
+        got = O.dec_e5m2(c)
+        want = float(ref[c])
+        if math.isnan(want):
+            assert math.isnan(got), c
+        else:
+            assert got == want and math.copysign(1, got) == math.copysign(1, want), c
+    assert O.dec_e5m2(0x7B) == 57344.0 and O.dec_e5m2(0x01) == 2.0 ** -16
+    assert O.dec_e5m2(0x7C) == math.inf and O.dec_e5m2(0xFC) == -math.inf
+
+
 def test_e8m0_decode_matches_torch_all_codes():
     ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e8m0fnu).double()
     for b in range(256):

@@ -67,6 +67,31 @@ def test_unit_scales_equal_plain_fp64_gemm(m, n, k, l):
     assert amax == np.abs(np.stack([a[i] @ b[i].T for i in range(l)])).max()
 
 
+def test_unit_scales_e5m2_equal_fp64_gemm():
+    # E5M2 operands (float8_e5m2 on the page): with unit scales the op is a
+    # plain GEMM of the codes decoded by torch; products have <= 6 significant
+    # bits, so the fp64 sums agree to rounding of a few units in 2^-53.
+    m, n, k, l = 96, 80, 256, 2
+    p = W.gemm_amax_problem(m, n, k, l, "e5m2", seed=4)
+    p.t["sfa"][:] = 127
+    p.t["sfb"][:] = 127
+    a = p.t["a"].view(torch.float8_e5m2).double().numpy()
+    b = p.t["b"].view(torch.float8_e5m2).double().numpy()
+    c, s, amax = O.gemm_amax_full(p.t["a"], p.t["b"], p.t["sfa"], p.t["sfb"], m, n, k, l, "e5m2")
+    for li in range(l):
+        np.testing.assert_allclose(c[li], a[li] @ b[li].T, rtol=1e-13, atol=0)
+        np.testing.assert_allclose(s[li], np.abs(a[li]) @ np.abs(b[li]).T, rtol=1e-13, atol=0)
+
+
+def test_e5m2_pow2_rescale_is_exact():
+    m, n, k, l = 64, 48, 128, 1
+    p = W.gemm_amax_problem(m, n, k, l, "e5m2", seed=5)
+    c0 = O.gemm_amax_full(p.t["a"], p.t["b"], p.t["sfa"], p.t["sfb"], m, n, k, l, "e5m2")[0]
+    p.t["sfb"] = (p.t["sfb"].int() + 3).to(torch.uint8)
+    c1 = O.gemm_amax_full(p.t["a"], p.t["b"], p.t["sfa"], p.t["sfb"], m, n, k, l, "e5m2")[0]
+    assert np.array_equal(c1, 8.0 * c0)
+
+
 def test_unit_scales_fp4_and_nibble_order():
     m, n, k = 64, 48, 64
     p = unit_scale_problem(m, n, k, 1, fmt="e2m1", seed=5)

@@ -41,9 +41,12 @@ import torch
 
 E4M3 = "e4m3"
 E2M1 = "e2m1"
+E5M2 = "e5m2"
 
 # Largest finite magnitude of each operand format (OCP MX formats).
-_FMT_MAX = {E4M3: 448.0, E2M1: 6.0}
+_FMT_MAX = {E4M3: 448.0, E2M1: 6.0, E5M2: 57344.0}
+# scale byte that puts a block-stretched N(0,1) draw back near unit size
+_SF_CENTRE = {E4M3: 120, E2M1: 126, E5M2: 113}
 # Decision points between adjacent E2M1 magnitudes {0,.5,1,1.5,2,3,4,6}.
 _E2M1_EDGES = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
 
@@ -66,8 +69,8 @@ def _gen(seed: int, device) -> torch.Generator:
 def _codes_from_normal(x: torch.Tensor, fmt: str) -> torch.Tensor:
     """Normal draws (..., K) -> uint8 code bytes, block-stretched to the format max.
 
-    E4M3 returns one byte per element; E2M1 returns two elements per byte,
-    element 2j in the low nibble and 2j+1 in the high nibble.
+    E4M3 and E5M2 return one byte per element; E2M1 returns two elements per
+    byte, element 2j in the low nibble and 2j+1 in the high nibble.
     """
     *lead, k = x.shape
     blk = x.reshape(*lead, k // 32, 32)
@@ -76,6 +79,9 @@ def _codes_from_normal(x: torch.Tensor, fmt: str) -> torch.Tensor:
     if fmt == E4M3:
         y = y.clamp(-448.0, 448.0)
         return y.to(torch.float8_e4m3fn).view(torch.uint8)
+    if fmt == E5M2:
+        y = y.clamp(-57344.0, 57344.0)
+        return y.to(torch.float8_e5m2).view(torch.uint8)
     edges = torch.tensor(_E2M1_EDGES, device=y.device, dtype=y.dtype)
     mag = torch.bucketize(y.abs(), edges).to(torch.uint8)          # 0..7
     code = mag | ((y < 0).to(torch.uint8) << 3)
@@ -141,7 +147,7 @@ def gemm_amax_problem(m: int, n: int, k: int, l: int, fmt: str = E4M3, *, seed: 
     """
     g = _gen(seed, device)
     if sf_centre is None:
-        sf_centre = 127 if plain_round else (120 if fmt == E4M3 else 126)
+        sf_centre = 127 if plain_round else _SF_CENTRE[fmt]
     xa = torch.randn(l, m, k, generator=g, device=device)
     xb = torch.randn(l, n, k, generator=g, device=device)
     if plain_round:
@@ -188,7 +194,7 @@ def grouped_srelu_problem(tokens: int, experts: int, n: int, k: int, fmt: str = 
     xb = torch.randn(experts, n, k, generator=g, device=device)
     b = _codes_from_normal(xb, fmt)
     del xb
-    centre_a = 120 if fmt == E4M3 else 126
+    centre_a = _SF_CENTRE[fmt]
     sfa = _sf_bytes(sf_atom_bytes(max(m, 1), k, 1), centre_a, 1, g, device)
     sfb = _sf_bytes(sf_atom_bytes(n, k, experts), centre_a - 6, 1, g, device)
     alpha = torch.rand(experts, generator=g, device=device) + 0.5
