@@ -38,11 +38,11 @@ def ceil_div(a, b):
 # ---------------------------------------------------------------------------
 # Workloads: each returns (step_fn, info) with inputs resident on the GPU.
 # ---------------------------------------------------------------------------
-def wl_moe_mxfp8_srelu(fp8_out=False, discrete=False):
+def wl_moe_mxfp8_srelu(fp8_out=False, discrete=False, fmt="e4m3"):
     import torch
     import block_scaled_gemm_02_amd as bsg
     import workloads as W
-    p = W.moe_mxfp8_srelu(device="cuda")
+    p = W.moe_mxfp8_srelu(device="cuda", fmt=fmt)
     s, t = p.sizes, p.t
     m, n, k, L = s["m"], s["n"], s["k"], s["l"]
     if discrete:
@@ -71,30 +71,32 @@ def wl_moe_mxfp8_srelu(fp8_out=False, discrete=False):
         if discrete:
             bsg.grouped_gemm_srelu_discrete(t["a"], b_ptrs, t["sfa"], sfb_ptrs, t["offsets"], t["alpha"],
                                             t["prob"], t["norm_const"], c, d, d_col, sfd_row, sfd_col,
-                                            amax, m, n, k, L, "e4m3", c_dtype=torch.bfloat16, d_dtype=dd,
+                                            amax, m, n, k, L, fmt, c_dtype=torch.bfloat16, d_dtype=dd,
                                             tanh_clamp_scale=32.0)
         else:
             bsg.grouped_gemm_srelu(t["a"], t["b"], t["sfa"], t["sfb"], t["offsets"], t["alpha"],
                                    t["prob"], t["norm_const"], c, d, d_col, sfd_row, sfd_col, amax,
-                                   m, n, k, L, "e4m3", c_dtype=torch.bfloat16, d_dtype=dd,
+                                   m, n, k, L, fmt, c_dtype=torch.bfloat16, d_dtype=dd,
                                    tanh_clamp_scale=32.0)
     step.keep = (b_list, sfb_list) if discrete else None
 
     valid_m = s["valid_m"]
     flops = 2.0 * valid_m * n * k
+    ab_bytes = valid_m * k + L * n * k if fmt == "e4m3" else (valid_m * k + L * n * k) // 2
     sf_bytes = t["sfa"].numel() + (sum(x.numel() for x in sfb_list) if discrete else t["sfb"].numel())
     out_bytes = valid_m * n * (2 + (2 if not fp8_out else 2) + 0)
-    alg_bytes = valid_m * k + L * n * k + sf_bytes + out_bytes
-    name = "moe_mxfp8_srelu" + ("_fp8d" if fp8_out else "") + ("_discrete" if discrete else "")
+    alg_bytes = ab_bytes + sf_bytes + out_bytes
+    name = ("moe_mxfp8_srelu" if fmt == "e4m3" else "moe_mxfp4_srelu") + ("_fp8d" if fp8_out else "") + \
+        ("_discrete" if discrete else "")
     info = dict(
-        name=name, fmt="e4m3", flops=flops, alg_bytes=alg_bytes, kernel="k_grouped",
-        config={"workload": "grouped MXFP8 (E4M3, E8M0 per 32 K) GEMM + prob-gated sReLU, "
-                            "tanh clamp s=32",
+        name=name, fmt=fmt, flops=flops, alg_bytes=alg_bytes, kernel="k_grouped",
+        config={"workload": ("grouped MXFP8 (E4M3" if fmt == "e4m3" else "grouped MXFP4 (E2M1")
+                + ", E8M0 per 32 K) GEMM + prob-gated sReLU, tanh clamp s=32",
                 "experts": L, "n": n, "k": k, "valid_m": valid_m, "routed_rows": 28672,
                 "routing": "multinomial Zipf(1.1), padded to 256",
                 "outputs": "C bf16, D " + ("E4M3 + SFD_row/SFD_col" if fp8_out else "bf16 + amax(L)"),
                 "weights": "per-expert allocations (b_ptrs, sfb_ptrs)" if discrete else "one (N,K,L) tensor"},
-        cpu=None if discrete else (lambda: cpu_sample_srelu(p)))
+        cpu=None if (discrete or fmt != "e4m3") else (lambda: cpu_sample_srelu(p)))
     return step, info
 
 
@@ -232,6 +234,7 @@ WORKLOADS = {
     "moe_mxfp8_srelu": lambda: wl_moe_mxfp8_srelu(False),
     "moe_mxfp8_srelu_fp8d": lambda: wl_moe_mxfp8_srelu(True),
     "moe_mxfp8_srelu_discrete": lambda: wl_moe_mxfp8_srelu(False, discrete=True),
+    "moe_mxfp4_srelu": lambda: wl_moe_mxfp8_srelu(False, fmt="e2m1"),
     "dense_8192_e4m3": lambda: wl_dense_8192("e4m3"),
     "dense_8192_e2m1": lambda: wl_dense_8192("e2m1"),
     "dense_256": wl_dense_256,
@@ -330,7 +333,7 @@ def main():
     peak = PEAK[info["fmt"]]
     out = {
         "metric": "TFLOP/s and % of MXFP8 MFMA peak, grouped MoE block-scaled GEMM + sReLU"
-        if info["name"].startswith("moe_mxfp8") else f"TFLOP/s, {info['name']}",
+        if info["name"] == "moe_mxfp8_srelu" else f"TFLOP/s, {info['name']}",
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,

@@ -311,9 +311,10 @@ def moe_bf16(device="cuda", seed=0, tokens=16384 * 8, experts=64, n=2048, k=7168
 
 
 def moe_mxfp8_srelu(device="cuda", seed=0, tokens=28672, experts=32, n=4096, k=7168,
-                    d_dtype="bf16", **kw):
-    """Grouped MXFP8 + sReLU: 32 experts, N=4096, K=7168, valid_m ~ 32768, s=32."""
-    return grouped_srelu_problem(tokens, experts, n, k, E4M3, seed=seed, device=device,
+                    d_dtype="bf16", fmt=E4M3, **kw):
+    """Grouped MXFP8 + sReLU: 32 experts, N=4096, K=7168, valid_m ~ 32768, s=32
+    (fmt E2M1: the same problem with MXFP4 operands)."""
+    return grouped_srelu_problem(tokens, experts, n, k, fmt, seed=seed, device=device,
                                  tanh_clamp=32.0, d_dtype=d_dtype, **kw)
 
 
