@@ -63,10 +63,9 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
     // Rotary position P of a token is held by block 1 + P/32, register group
     // (P%32)/8, half ((P%8)/4), element P%4.  Output position q8 = 8q + 4g + u
     // pairs inputs 2*q8 and 2*q8 + 1: block 1 + q/2, register group
-    // 2(q%2) + g, half u/2, elements 2(u%2) and 2(u%2) + 1.  Each lane fetches
-    // the other half's registers of both blocks, then picks pairs in-lane.
+    // 2(q%2) + g, half u/2, elements 2(u%2) and 2(u%2) + 1.  Each lane gets the
+    // other half-wave's registers it needs with v_permlane32_swap (below).
     if (wn == 1) {
-        const bool hi = gh == 1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t row = m0 + acc_row(wm, i, lane);
@@ -84,33 +83,32 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
                 cs1[4 * q] = bf16_lo(c1.x); cs1[4 * q + 1] = bf16_hi(c1.x); cs1[4 * q + 2] = bf16_lo(c1.y); cs1[4 * q + 3] = bf16_hi(c1.y);
                 sn1[4 * q] = bf16_lo(s1.x); sn1[4 * q + 1] = bf16_hi(s1.x); sn1[4 * q + 2] = bf16_lo(s1.y); sn1[4 * q + 3] = bf16_hi(s1.y);
             }
-            float own[2][16], oth[2][16];
+            // Rotary input pairs sit in registers 4q'+e (q' = 0, 2) of one half-wave
+            // and 4q'+4+e of the other (see above).  v_permlane32_swap of
+            // registers r and r + 4 (r = 0-3, 8-11) leaves in X[r] the value
+            // that outputs with u < 2 use and in Y[r] the one that u >= 2 use, in
+            // both half-waves: low lanes keep their register r in X and receive
+            // the high lanes' register r in Y; high lanes receive the low lanes'
+            // register r + 4 in X and keep their own in Y.
+            float X[2][16], Y[2][16];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                own[0][v] = acc[i][1][v];
-                own[1][v] = acc[i][2][v];
-                oth[0][v] = xor32(own[0][v]);
-                oth[1][v] = xor32(own[1][v]);
-            }
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < 12; ++r) {
+                    if ((r & 4) != 0) continue;
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i][1 + b][r]),
+                                                                     __float_as_uint(acc[i][1 + b][r + 4]),
+                                                                     false, false);
+                    X[b][r] = __uint_as_float(sw[0]);
+                    Y[b][r] = __uint_as_float(sw[1]);
+                }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const int b = q / 2, qb = 2 * (q % 2), ue = 2 * (u % 2);
-                    // register of the pair in the holding half: group qb + g (this lane's g)
-                    const float lo0 = own[b][4 * qb + ue], lo1 = own[b][4 * qb + ue + 1];
-                    const float hi0 = own[b][4 * (qb + 1) + ue], hi1 = own[b][4 * (qb + 1) + ue + 1];
-                    const float olo0 = oth[b][4 * qb + ue], olo1 = oth[b][4 * qb + ue + 1];
-                    const float ohi0 = oth[b][4 * (qb + 1) + ue], ohi1 = oth[b][4 * (qb + 1) + ue + 1];
-                    // holder half is u/2: this lane when u/2 == g, else the other half
-                    float ea, eb;
-                    if (u / 2 == 0) {
-                        ea = hi ? ohi0 : lo0;
-                        eb = hi ? ohi1 : lo1;
-                    } else {
-                        ea = hi ? hi0 : olo0;
-                        eb = hi ? hi1 : olo1;
-                    }
+                    const int b = q / 2, r = 4 * (2 * (q % 2)) + 2 * (u % 2);
+                    const float ea = u < 2 ? X[b][r] : Y[b][r];
+                    const float eb = u < 2 ? X[b][r + 1] : Y[b][r + 1];
                     const int v = 4 * q + u;
                     acc[i][1][v] = ea * cs0[v] - eb * sn0[v];
                     acc[i][2][v] = eb * cs1[v] + ea * sn1[v];
