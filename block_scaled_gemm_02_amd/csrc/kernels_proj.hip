@@ -66,18 +66,28 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
     // 2(q%2) + g, half u/2, elements 2(u%2) and 2(u%2) + 1.  Each lane gets the
     // other half-wave's registers it needs with v_permlane32_swap (below).
     if (wn == 1) {
+        // every cos/sin value of the wave's 128 tokens is loaded first, so the
+        // four 32-token blocks wait for one round trip instead of four
+        uint2 tab[4][4][4];                                // [block][q][cos lo, sin lo, cos hi, sin hi]
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t row = m0 + acc_row(wm, i, lane);
             const int64_t tr = row < p.tokens ? row : 0;
-            float cs0[16], sn0[16], cs1[16], sn1[16];      // cos/sin at q8 and 32 + q8
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int q8 = 8 * q + 4 * gh;
-                const uint2 c0 = *reinterpret_cast<const uint2 *>(p.cos + tr * ROPE + q8);
-                const uint2 s0 = *reinterpret_cast<const uint2 *>(p.sin + tr * ROPE + q8);
-                const uint2 c1 = *reinterpret_cast<const uint2 *>(p.cos + tr * ROPE + HALF + q8);
-                const uint2 s1 = *reinterpret_cast<const uint2 *>(p.sin + tr * ROPE + HALF + q8);
+                tab[i][q][0] = *reinterpret_cast<const uint2 *>(p.cos + tr * ROPE + q8);
+                tab[i][q][1] = *reinterpret_cast<const uint2 *>(p.sin + tr * ROPE + q8);
+                tab[i][q][2] = *reinterpret_cast<const uint2 *>(p.cos + tr * ROPE + HALF + q8);
+                tab[i][q][3] = *reinterpret_cast<const uint2 *>(p.sin + tr * ROPE + HALF + q8);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float cs0[16], sn0[16], cs1[16], sn1[16];      // cos/sin at q8 and 32 + q8
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint2 c0 = tab[i][q][0], s0 = tab[i][q][1], c1 = tab[i][q][2], s1 = tab[i][q][3];
                 cs0[4 * q] = bf16_lo(c0.x); cs0[4 * q + 1] = bf16_hi(c0.x); cs0[4 * q + 2] = bf16_lo(c0.y); cs0[4 * q + 3] = bf16_hi(c0.y);
                 sn0[4 * q] = bf16_lo(s0.x); sn0[4 * q + 1] = bf16_hi(s0.x); sn0[4 * q + 2] = bf16_lo(s0.y); sn0[4 * q + 3] = bf16_hi(s0.y);
                 cs1[4 * q] = bf16_lo(c1.x); cs1[4 * q + 1] = bf16_hi(c1.x); cs1[4 * q + 2] = bf16_lo(c1.y); cs1[4 * q + 3] = bf16_hi(c1.y);
