@@ -13,7 +13,8 @@ BUILD = os.path.join(HERE, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-# Packed-FP32 VALU forms are disabled for every device pass.
+# Packed-FP32 VALU forms (v_pk_*_f32) are disabled for every device pass: the
+# kernels use scalar fp32 arithmetic only.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function"]
 

@@ -95,7 +95,7 @@ const char *bsg_status_string(int status)
     case BSG_ERR_SHAPE: return "invalid or inconsistent shape";
     case BSG_ERR_DTYPE: return "invalid dtype";
     case BSG_ERR_ALIGN: return "16-byte alignment violated";
-    case BSG_ERR_UNSUPPORTED: return "combination not supported by this build";
+    case BSG_ERR_UNSUPPORTED: return "combination not supported by this library";
     case BSG_ERR_DEVICE: return "device error (not gfx950 or HIP failure)";
     case BSG_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
