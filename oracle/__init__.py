@@ -65,6 +65,8 @@ def lib():
         L.orc_gemm_amax.argtypes = [p, p, p, p, i64, i64, i64, i64, i32, i64, i64, i64, p, p, p]
         L.orc_grouped_srelu.restype = i32
         L.orc_grouped_srelu.argtypes = [p] * 7 + [i64] * 4 + [i32, d, i64, i64, p, p, p, p, p]
+        L.orc_grouped_dswiglu.restype = i32
+        L.orc_grouped_dswiglu.argtypes = [p] * 9 + [i64] * 4 + [i32, i64, i64] + [p] * 5
         L.orc_grouped_bf16.restype = i32
         L.orc_grouped_bf16.argtypes = [p] * 6 + [i64] * 6 + [p, p, p, p]
         L.orc_proj_rope.restype = i32
@@ -204,6 +206,25 @@ def grouped_srelu(a, b, sfa, sfb, offsets, alpha, prob, m, n, k, L_, fmt, s, r0=
     if rc:
         raise ValueError(f"orc_grouped_srelu failed ({rc})")
     return dict(c=c, d=d, sabs=sab, group=grp, bmax=bm)
+
+
+def grouped_dswiglu(a, b, sfa, sfb, offsets, alpha, beta, prob, c_bits, m, n, k, L_, fmt, r0=0, r1=None):
+    """[GD] Steps 1-2, rows [r0, r1): dict(ref (rows,N), d (rows,2N), dprob (rows,),
+    sabs, bmax) in fp64; C given as bf16 bits (rows of the full (M, 2N) tensor)."""
+    L = lib()
+    r1 = m if r1 is None else r1
+    a, b, sfa, sfb = (_np(x, np.uint8) for x in (a, b, sfa, sfb))
+    off = _np(offsets, np.int32); al = _np(alpha, np.float32); bt = _np(beta, np.float32)
+    pr = _np(prob, np.float32); cb = _np(c_bits, np.uint16)
+    rows = r1 - r0
+    ref = np.empty((rows, n)); d = np.empty((rows, 2 * n)); dp = np.empty(rows)
+    sab = np.empty((rows, n)); bm = np.empty((rows, n))
+    rc = L.orc_grouped_dswiglu(_ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), _ptr(off), _ptr(al), _ptr(bt),
+                               _ptr(pr), _ptr(cb), m, n, k, L_, _FMT[fmt], r0, r1, _ptr(ref), _ptr(d),
+                               _ptr(dp), _ptr(sab), _ptr(bm))
+    if rc:
+        raise ValueError(f"orc_grouped_dswiglu failed ({rc})")
+    return dict(ref=ref, d=d, dprob=dp, sabs=sab, bmax=bm)
 
 
 def expert_amax(d: np.ndarray, group: np.ndarray, L_: int) -> np.ndarray:

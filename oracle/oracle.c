@@ -14,7 +14,8 @@
  *   [GA]  "GEMM + Amax (SM100)": Equations; Shapes; Input/Output tensors.
  *   [GS]  "Grouped GEMM + sReLU (SM100)": Equations; Tanh soft clamp;
  *         Shapes (SFD_row / SFD_col atom shapes).
- *   [GD]  "Grouped GEMM + dSwiGLU (SM100)": Step 3, output quantisation.
+ *   [GD]  "Grouped GEMM + dSwiGLU (SM100)": Steps 1-2 (dSwiGLU backward
+ *         epilogue), Step 3 (output quantisation).
  *   [GB]  "Grouped GEMM (SM100 BF16)": Operation; Tensors and layouts.
  *   [PR]  "GEMM + RoPE + MXFP8 Projection (SM100)": Equations; Shapes.
  * Number formats follow the OCP Microscaling (MX) v1.0 definitions of
@@ -366,6 +367,74 @@ int orc_grouped_srelu(const uint8_t *a, const uint8_t *b, const uint8_t *sfa, co
                 bmax_out[(i - r0) * n + j] =
                     fabs((double)alpha[g]) * block_max_sum(ah + (i - r0) * k, bh + j * k, k);
         }
+    }
+    free(ah);
+    free(bh);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* [GD] Step 1 and Step 2 (grouped GEMM + dSwiGLU backward epilogue):       */
+/*   ref[m,n] = alpha_g^2 * sum_k dequant(A)[m,k] * dequant(B)[n,k,g]        */
+/*   C (rows, 2N) holds 32-column blocks in pairs: columns [64b, 64b+32)    */
+/*   are the input and [64b+32, 64b+64) the gate of ref columns             */
+/*   [32b, 32b+32); both are scaled by beta_g.                              */
+/*   swish = gate * sigmoid(gate)                                           */
+/*   ab    = ref * prob * swish                                             */
+/*   dsw   = ref * prob * input * sigmoid(gate) * (1 + gate*(1 - sigmoid))  */
+/*   D has the same pairing: ab in [64b, 64b+32), dsw in [64b+32, 64b+64).  */
+/*   dprob[m] = sum_n swish * input * ref                                   */
+/* C is bf16 (bits).  Rows [r0, r1); ref_out (rows, N), d_out (rows, 2N),    */
+/* dprob_out (rows); sabs_out / bmax_out (rows, N, nullable) carry          */
+/* |alpha_g|^2 * sum|products| and the block-max sum of the GEMM.           */
+/* ------------------------------------------------------------------------ */
+int orc_grouped_dswiglu(const uint8_t *a, const uint8_t *b, const uint8_t *sfa, const uint8_t *sfb,
+                        const int32_t *offsets, const float *alpha, const float *beta,
+                        const float *prob, const uint16_t *c, int64_t m, int64_t n, int64_t k,
+                        int64_t L, int fmt, int64_t r0, int64_t r1, double *ref_out, double *d_out,
+                        double *dprob_out, double *sabs_out, double *bmax_out)
+{
+    double *bh = NULL, *ah;
+    int64_t rows = r1 - r0, have = -1;
+    if (r0 < 0 || r1 > m || r0 > r1 || n % 32) return 1;
+    if (fmt == 1 && (k % 2)) return 2;
+    ah = (double *)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1) * (size_t)(rows > 0 ? rows : 1));
+    bh = (double *)malloc(sizeof(double) * (size_t)(n * k > 0 ? n * k : 1));
+    if (!ah || !bh) { free(ah); free(bh); return 3; }
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = r0; i < r1; ++i)
+        dequant_row(a, sfa, fmt, i, 0, m, k, ah + (i - r0) * k);
+    for (int64_t i = r0; i < r1; ++i) {
+        int64_t g = orc_expert_of_row(offsets, L, i);
+        double a2, bt, pr, dp = 0.0;
+        if (g < 0) {
+            for (int64_t j = 0; j < n; ++j) ref_out[(i - r0) * n + j] = NAN;
+            for (int64_t j = 0; j < 2 * n; ++j) d_out[(i - r0) * 2 * n + j] = NAN;
+            dprob_out[i - r0] = NAN;
+            continue;
+        }
+        if (g != have) { dequant_matrix(b, sfb, fmt, g, n, k, bh); have = g; }
+        a2 = (double)alpha[g] * (double)alpha[g];
+        bt = (double)beta[g];
+        pr = (double)prob[i];
+        #pragma omp parallel for schedule(static) reduction(+ : dp)
+        for (int64_t j = 0; j < n; ++j) {
+            double acc, t, ref, in, gt, sg, sw;
+            int64_t cin = 64 * (j / 32) + j % 32, cgt = cin + 32;
+            dot(ah + (i - r0) * k, bh + j * k, k, &acc, &t);
+            ref = a2 * acc;
+            in = bt * orc_dec_bf16(c[i * 2 * n + cin]);
+            gt = bt * orc_dec_bf16(c[i * 2 * n + cgt]);
+            sg = 1.0 / (1.0 + exp(-gt));
+            sw = gt * sg;
+            ref_out[(i - r0) * n + j] = ref;
+            d_out[(i - r0) * 2 * n + cin] = ref * pr * sw;
+            d_out[(i - r0) * 2 * n + cgt] = ref * pr * in * sg * (1.0 + gt * (1.0 - sg));
+            dp += sw * in * ref;
+            if (sabs_out) sabs_out[(i - r0) * n + j] = a2 * t;
+            if (bmax_out) bmax_out[(i - r0) * n + j] = a2 * block_max_sum(ah + (i - r0) * k, bh + j * k, k);
+        }
+        dprob_out[i - r0] = dp;
     }
     free(ah);
     free(bh);

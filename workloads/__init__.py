@@ -208,6 +208,27 @@ def grouped_srelu_problem(tokens: int, experts: int, n: int, k: int, fmt: str = 
                         norm_const=torch.ones(1, device=device)))
 
 
+def grouped_dswiglu_problem(tokens: int, experts: int, n: int, k: int, fmt: str = E4M3, *,
+                            seed: int = 0, device="cpu", offsets: np.ndarray | None = None,
+                            extra_rows: int = 0) -> Problem:
+    """Grouped GEMM + dSwiGLU backward operands: the grouped sReLU problem's
+    A, B, scales, routing, alpha and prob, plus beta U(0.5,1.5) per expert and
+    the forward tensor C (M, 2N) bf16 N(0,1) (input and gate in 32-column
+    blocks), zero on padding rows; MXFP8 output with norm_const 1."""
+    p = grouped_srelu_problem(tokens, experts, n, k, fmt, seed=seed, device=device, offsets=offsets,
+                              extra_rows=extra_rows, d_dtype="e4m3")
+    m = p.sizes["m"]
+    g = _gen(seed + 5, device)
+    beta = torch.rand(experts, generator=g, device=device) + 0.5
+    c = torch.randn(m, 2 * n, generator=g, device=device)
+    routed = p.t["prob"] > 0                      # prob is 0 exactly on padding rows
+    c = torch.where(routed[:, None], c, torch.zeros_like(c)).to(torch.bfloat16)
+    p.op = "grouped_gemm_dswiglu"
+    p.t["beta"] = beta
+    p.t["c"] = c.contiguous()
+    return p
+
+
 # ---------------------------------------------------------------------------
 # Unfused BF16 grouped GEMM
 # ---------------------------------------------------------------------------
