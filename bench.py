@@ -132,6 +132,38 @@ def cpu_sample_srelu(p, rows=1024):
                 sample=f"{rows} rows of expert 0 (x N={n}, K={k}), fp64 oracle incl. B dequantisation")
 
 
+def wl_moe_dswiglu():
+    import torch
+    import block_scaled_gemm_02_amd as bsg
+    import workloads as W
+    # config-4 routing (32 experts, Zipf(1.1), valid_m ~ 32768) with K = 7168 and
+    # N = 2048: ref is (valid_m, 2048), C and D are (valid_m, 4096)
+    p = W.grouped_dswiglu_problem(28672, 32, 2048, 7168, "e4m3", seed=0, device="cuda")
+    s, t = p.sizes, p.t
+    m, n, k, L = s["m"], s["n"], s["k"], s["l"]
+    d = torch.empty(m, 2 * n, dtype=torch.uint8, device="cuda")
+    d_col = torch.empty(m, 2 * n, dtype=torch.uint8, device="cuda")
+    sfd_row = torch.empty(W.sf_atom_bytes(m, 2 * n, 1), dtype=torch.uint8, device="cuda")
+    sfd_col = torch.empty(W.sf_atom_bytes(2 * n, m, 1), dtype=torch.uint8, device="cuda")
+    dprob = torch.zeros(m, device="cuda")
+
+    def step():
+        dprob.zero_()
+        bsg.grouped_gemm_dswiglu(t["a"], t["b"], t["sfa"], t["sfb"], t["c"], t["offsets"], t["alpha"], t["beta"],
+                                 t["prob"], t["norm_const"], d, d_col, sfd_row, sfd_col, dprob, m, n, k, L, "e4m3")
+
+    valid_m = s["valid_m"]
+    alg = valid_m * k + L * n * k + t["sfa"].numel() + t["sfb"].numel() + valid_m * 2 * n * 2 \
+        + 2 * valid_m * 2 * n + sfd_row.numel() + sfd_col.numel() + 4 * valid_m
+    info = dict(name="moe_mxfp8_dswiglu", fmt="e4m3", flops=2.0 * valid_m * n * k, alg_bytes=alg,
+                kernel="k_grouped",
+                config={"workload": "grouped MXFP8 GEMM + dSwiGLU backward, MXFP8 D (row + column) and dprob",
+                        "experts": L, "n": n, "k": k, "valid_m": valid_m, "routed_rows": 28672,
+                        "routing": "multinomial Zipf(1.1), padded to 256", "c": "bf16 (valid_m, 2N)"},
+                cpu=None)
+    return step, info
+
+
 def wl_dense_8192(fmt):
     import torch
     import block_scaled_gemm_02_amd as bsg
@@ -235,6 +267,7 @@ WORKLOADS = {
     "moe_mxfp8_srelu_fp8d": lambda: wl_moe_mxfp8_srelu(True),
     "moe_mxfp8_srelu_discrete": lambda: wl_moe_mxfp8_srelu(False, discrete=True),
     "moe_mxfp4_srelu": lambda: wl_moe_mxfp8_srelu(False, fmt="e2m1"),
+    "moe_mxfp8_dswiglu": wl_moe_dswiglu,
     "dense_8192_e4m3": lambda: wl_dense_8192("e4m3"),
     "dense_8192_e2m1": lambda: wl_dense_8192("e2m1"),
     "dense_256": wl_dense_256,

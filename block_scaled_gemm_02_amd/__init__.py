@@ -6,8 +6,8 @@ kernels behind the C ABI declared in include/bsg.h.  There is no fallback:
 if libbsg.so is missing or a call fails, a RuntimeError is raised.
 
 Entry points keep the C names:
-    gemm_amax, grouped_gemm, grouped_gemm_srelu, gemm_proj_rope_mxfp8,
-    grouped_gemm_discrete, grouped_gemm_srelu_discrete
+    gemm_amax, grouped_gemm, grouped_gemm_srelu, grouped_gemm_dswiglu,
+    gemm_proj_rope_mxfp8, grouped_gemm_discrete, grouped_gemm_srelu_discrete
 and validate_only=True calls the host-only check bsg_validate_<name>.
 """
 from __future__ import annotations
@@ -49,6 +49,8 @@ def lib():
             "grouped_gemm": [p] * 8 + [i64] * 4 + [i32] * 3 + [p],
             "grouped_gemm_srelu": [p] * 14 + [i64] * 4 + [i32] * 4 + [f32, p],
             "gemm_proj_rope_mxfp8": [p] * 10 + [i64] * 5 + [i32, i32, p],
+            "grouped_gemm_dswiglu": [p] * 15 + [i64] * 4 + [i32] * 4 + [p],
+            "bsg_validate_grouped_gemm_dswiglu": [p] * 15 + [i64] * 4 + [i32] * 4,
             "grouped_gemm_discrete": [p] * 8 + [i64] * 4 + [i32] * 3 + [p],
             "grouped_gemm_srelu_discrete": [p] * 14 + [i64] * 4 + [i32] * 4 + [f32, p],
             "bsg_validate_grouped_gemm_discrete": [p] * 8 + [i64] * 4 + [i32] * 3,
@@ -74,9 +76,10 @@ def lib():
 def symbols():
     """Names of the C entry points this binding expects libbsg.so to export."""
     return ["gemm_amax", "grouped_gemm", "grouped_gemm_srelu", "gemm_proj_rope_mxfp8",
-            "grouped_gemm_discrete", "grouped_gemm_srelu_discrete",
+            "grouped_gemm_discrete", "grouped_gemm_srelu_discrete", "grouped_gemm_dswiglu",
             "bsg_validate_gemm_amax", "bsg_validate_grouped_gemm",
             "bsg_validate_grouped_gemm_srelu", "bsg_validate_gemm_proj_rope_mxfp8",
+            "bsg_validate_grouped_gemm_dswiglu",
             "bsg_validate_grouped_gemm_discrete", "bsg_validate_grouped_gemm_srelu_discrete",
             "bsg_status_string", "bsg_last_error", "bsg_version"]
 
@@ -203,6 +206,21 @@ def grouped_gemm_srelu_discrete(a, b_ptrs, sfa, sfb_ptrs, padded_offsets, alpha,
     if validate_only:
         return lib().bsg_validate_grouped_gemm_srelu_discrete(*args)
     _check(lib().grouped_gemm_srelu_discrete(*args, _stream(stream)))
+
+
+def grouped_gemm_dswiglu(a, b, sfa, sfb, c, padded_offsets, alpha, beta, prob, norm_const, d_row, d_col,
+                         sfd_row, sfd_col, dprob, m, n, k, num_experts, ab_dtype="e4m3", c_dtype=None,
+                         d_dtype="e4m3", sf_vec_size=32, stream=None, validate_only=False):
+    """Grouped GEMM + dSwiGLU backward with MXFP8 output (see include/bsg.h).
+    dprob is accumulated: zero-fill it first."""
+    cd = BF16 if c_dtype is None else (_TORCH_DT[c_dtype] if c_dtype in _TORCH_DT else c_dtype)
+    dd = E4M3 if d_dtype in ("e4m3", E4M3) else (_TORCH_DT[d_dtype] if d_dtype in _TORCH_DT else d_dtype)
+    args = [_ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), _ptr(c), _ptr(padded_offsets), _ptr(alpha), _ptr(beta),
+            _ptr(prob), _ptr(norm_const), _ptr(d_row), _ptr(d_col), _ptr(sfd_row), _ptr(sfd_col), _ptr(dprob),
+            m, n, k, num_experts, _ab_code(ab_dtype), cd, dd, sf_vec_size]
+    if validate_only:
+        return lib().bsg_validate_grouped_gemm_dswiglu(*args)
+    _check(lib().grouped_gemm_dswiglu(*args, _stream(stream)))
 
 
 def gemm_proj_rope_mxfp8(x, w, x_scale, w_scale, cos, sin, out_fp8_row, out_scales_row,

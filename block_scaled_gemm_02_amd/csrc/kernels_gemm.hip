@@ -143,7 +143,7 @@ hipError_t launch_gemm_amax(const GemmAmaxArgs &a, hipStream_t s)
 // ---------------------------------------------------------------------------
 // Grouped GEMM over padded_offsets expert ranges
 // ---------------------------------------------------------------------------
-enum : int { EPI_BF16_BIAS = 0, EPI_SRELU = 1, EPI_SRELU_FP8 = 2, EPI_BF16 = 3 };
+enum : int { EPI_BF16_BIAS = 0, EPI_SRELU = 1, EPI_SRELU_FP8 = 2, EPI_BF16 = 3, EPI_DSWIGLU_FP8 = 4 };
 
 struct GroupedParams {
     const uint8_t *a, *b, *sfa, *sfb;
@@ -160,6 +160,10 @@ struct GroupedParams {
     int c_dtype, d_dtype, bias_dtype;
     float tanh_s;
     TanhSqConst tq;      // constants of tanh(r/s)^2 (see tanh_sq)
+    // dSwiGLU backward only: beta (L,), the forward tensor C (M, 2N) bf16, dprob (M,)
+    const float *beta;
+    const uint16_t *cfwd;
+    float *dprob;
 };
 
 // Index of the expert whose range [offsets[g-1], offsets[g]) holds row r:
@@ -374,6 +378,126 @@ __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x1
     });
 }
 
+// dSwiGLU backward epilogue with MXFP8 output ("Grouped GEMM + dSwiGLU
+// (SM100)", Steps 2 and 3).  ref = alpha_g^2 * acc; the forward tensor C
+// holds, for ref columns [32b, 32b+32), the input in C columns [64b, 64b+32)
+// and the gate in [64b+32, 64b+64), both scaled by beta_g;
+//   swish = gate*sigmoid(gate),  ab = ref*prob*swish,
+//   dswiglu = ref*prob*input*sigmoid(gate)*(1 + gate*(1 - sigmoid(gate))),
+// written to D with the same pairing, and dprob[m] += sum swish*input*ref.
+// The wave's 128 ref columns become 256 D columns (8 blocks of 32: ab of ref
+// block j is D block 2j, dswiglu 2j+1), quantised along D (SFD_row atoms over
+// (M, 2N)) and along M (SFD_col atoms over (2N, M)) as in the sReLU MXFP8
+// epilogue.  A lane's four C values of register group q are consecutive,
+// one 8-byte load each for input and gate.
+__device__ __forceinline__ float bf16_at(uint2 w, int u)
+{
+    const uint32_t x = (u < 2) ? w.x : w.y;
+    return __uint_as_float((u & 1) ? (x & 0xFFFF0000u) : (x << 16));
+}
+__device__ __forceinline__ void epilogue_dswiglu_fp8(const GroupedParams &p, f32x16 (&acc)[4][4], uint8_t *stage,
+                                                     int64_t m0, int64_t n0, float alpha2, float beta, int wm,
+                                                     int wn, int lane, const float *prob_lds)
+{
+    typedef StageGeom<1, 8> G;                       // 256 code bytes per staged row
+    const float nc = *p.norm_const;
+    const int64_t n = p.n, n2 = 2 * n;
+    const int64_t row_kt = (n2 / 32 + 3) / 4;       // SFD_row: K' over 2N
+    const int64_t col_kt = (p.m / 32 + 3) / 4;      // SFD_col: K' over M
+    const int c32 = lane & 31, gh = lane >> 5;
+    const int64_t qr = m0 + 128 * wm, qc = n0 + 128 * wn, dq = 2 * qc;
+    const int cols = clamp_extent(n - qc);          // valid ref columns (a multiple of 32)
+    const int dcols = 2 * cols;
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = prob_lds[acc_row(wm, i, lane)];
+    uint8_t *sd = stage, *sdc = stage + 32 * G::RBP;
+    uint8_t *wd = sd + c32 * G::RBP + 4 * gh, *wdc = sdc + c32 * G::RBP + 4 * gh;
+    const int64_t mt = qr / 128;
+    static_for<4>([&](auto ii) {
+        constexpr int i = decltype(ii)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        const int64_t row = qr + 32 * i + c32;
+        // input and gate of this lane's 64 ref columns (zero past N)
+        uint2 cin[4][4], cgt[4][4];
+        const uint16_t *crow = p.cfwd + row * n2 + 64 * (qc / 32) + 4 * gh;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const bool ok = 32 * j < cols;
+                cin[j][q] = ok ? *reinterpret_cast<const uint2 *>(crow + 64 * j + 8 * q) : make_uint2(0u, 0u);
+                cgt[j][q] = ok ? *reinterpret_cast<const uint2 *>(crow + 64 * j + 32 + 8 * q) : make_uint2(0u, 0u);
+            }
+        uint32_t rword[2] = {0u, 0u};                // SFD_row bytes of D blocks 0-3 and 4-7
+        float dpr = 0.0f;
+        auto quant_block = [&](const float (&dv)[16], int blk) {
+            // row direction: 32 D columns of one row (this lane and lane ^ 32)
+            float rm = 0.0f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) rm = fmaxf(rm, fabsf(dv[v]));
+            rm = fmaxf(rm, xor32(rm));
+            float rinv;
+            rword[blk >> 2] |= mx_scale_byte(rm, nc, rinv) << (8 * (blk & 3));
+            // column direction: 32 rows of one D column over the half-wave
+            float cinv[16], cm[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) cm[v] = fabsf(dv[v]);
+            half_wave_max(cm);
+            const uint32_t byte = col_scales(cm, nc, cinv, lane);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                *reinterpret_cast<uint32_t *>(wd + 32 * blk + 8 * q) =
+                    pack4_e4m3(dv[4 * q] * rinv, dv[4 * q + 1] * rinv, dv[4 * q + 2] * rinv, dv[4 * q + 3] * rinv);
+                *reinterpret_cast<uint32_t *>(wdc + 32 * blk + 8 * q) =
+                    pack4_e4m3(dv[4 * q] * cinv[4 * q], dv[4 * q + 1] * cinv[4 * q + 1],
+                               dv[4 * q + 2] * cinv[4 * q + 2], dv[4 * q + 3] * cinv[4 * q + 3]);
+            }
+            // SFD_col byte i of D column dq + 32 blk + 8(c/4) + 4g + c%4 (lane c < 16: register c)
+            const int64_t col = dq + 32 * blk + 8 * (c32 >> 2) + 4 * gh + (c32 & 3);
+            if (c32 < 16 && 32 * blk < dcols) {
+                const int64_t off = (((col / 128) * col_kt + mt) * 32 + (col % 32)) * 16 + ((col % 128) / 32) * 4;
+                p.sfd_col[off + i] = (uint8_t)byte;
+            }
+        };
+        static_for<4>([&](auto jj) {
+            constexpr int j = decltype(jj)::value;
+            float ab[16], ds[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float ref = alpha2 * acc[i][j][v];
+                const float in = beta * bf16_at(cin[j][v >> 2], v & 3);
+                const float gt = beta * bf16_at(cgt[j][v >> 2], v & 3);
+                const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gt));
+                const float sw = gt * sg;
+                const float rp = ref * pr[i];
+                ab[v] = rp * sw;
+                ds[v] = rp * in * sg * fmaf(gt, 1.0f - sg, 1.0f);
+                dpr = fmaf(sw * in, ref, dpr);
+            }
+            quant_block(ab, 2 * j);
+            quant_block(ds, 2 * j + 1);
+        });
+        // dprob: this lane's 64 columns plus the other half-wave's 64 of the same row
+        dpr += xor32(dpr);
+        if (gh == 0 && cols > 0) atomicAdd(p.dprob + row, dpr);
+        const uint32_t rb = (uint32_t)n2;
+        stage_flush<1, 8>(sd, static_cast<char *>(p.d) + (qr + 32 * i) * n2 + dq, rb, 32, dcols, lane);
+        stage_flush<1, 8>(sdc, static_cast<char *>(p.d_col) + (qr + 32 * i) * n2 + dq, rb, 32, dcols, lane);
+        // SFD_row words of this row: K' groups dq/128 and dq/128 + 1 (when they exist)
+        if (gh == 0) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int64_t kg = dq / 128 + h;
+                if (128 * h < dcols && kg < row_kt) {
+                    const int64_t off = (((row / 128) * row_kt + kg) * 32 + (row % 32)) * 16 + ((row % 128) / 32) * 4;
+                    *reinterpret_cast<uint32_t *>(p.sfd_row + off) = rword[h];
+                }
+            }
+        }
+    });
+}
+
 template <int F, int EPI, bool CLAMP, int OT = -1>
 __global__ void __launch_bounds__(256) k_grouped(GroupedParams p)
 {
@@ -414,6 +538,9 @@ __global__ void __launch_bounds__(256) k_grouped(GroupedParams p)
     if constexpr (EPI == EPI_SRELU_FP8) {
         epilogue_srelu_fp8<CLAMP>(p, acc, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), m0, n0, alpha,
                                   wm, wn, lane, prob_lds);
+    } else if constexpr (EPI == EPI_DSWIGLU_FP8) {
+        epilogue_dswiglu_fp8(p, acc, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), m0, n0, alpha * alpha,
+                             p.beta[g], wm, wn, lane, prob_lds);
     } else {
         epilogue_grouped<F, EPI, CLAMP, OT>(p, acc, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), m0, n0, g,
                                             alpha, wm, wn, lane, red, prob_lds);
@@ -434,6 +561,9 @@ static GroupedParams grouped_params(const GroupedArgs &a)
     p.c_dtype = a.c_dtype; p.d_dtype = a.d_dtype; p.bias_dtype = a.bias_dtype;
     p.tanh_s = a.tanh_s;
     p.tq = tanh_sq_const(a.tanh_s);
+    p.beta = a.beta;
+    p.cfwd = a.cfwd;
+    p.dprob = a.dprob;
     return p;
 }
 
@@ -488,6 +618,21 @@ hipError_t launch_grouped_srelu(const GroupedArgs &a, hipStream_t s)
     } else {
         launch_srelu_variant<FMT_E2M1, EPI_SRELU>(p, grid, s);
     }
+    return hipGetLastError();
+}
+
+}  // namespace bsg
+
+namespace bsg {
+
+hipError_t launch_grouped_dswiglu(const GroupedArgs &a, hipStream_t s)
+{
+    if (a.m == 0 || a.n == 0) return hipSuccess;
+    GroupedParams p = grouped_params(a);
+    dim3 grid((unsigned)(((a.n + kTileN - 1) / kTileN) * (a.m / kTileM)));
+    if (a.fmt == FMT_E4M3) hipLaunchKernelGGL((k_grouped<FMT_E4M3, EPI_DSWIGLU_FP8, false>), grid, dim3(kThreads), 0, s, p);
+    else if (a.fmt == FMT_E5M2) hipLaunchKernelGGL((k_grouped<FMT_E5M2, EPI_DSWIGLU_FP8, false>), grid, dim3(kThreads), 0, s, p);
+    else return hipErrorNotSupported;
     return hipGetLastError();
 }
 

@@ -28,6 +28,10 @@ struct GroupedArgs {
     int fmt;        // bsg::Fmt: 0 = E4M3, 1 = E2M1, 2 = BF16, 4 = E5M2
     int c_dtype, d_dtype, bias_dtype;
     float tanh_s;   // <= 0: no clamp
+    // grouped_gemm_dswiglu only (else null): beta (L,), forward C (M, 2N) bf16, dprob (M,)
+    const float *beta = nullptr;
+    const uint16_t *cfwd = nullptr;
+    float *dprob = nullptr;
 };
 
 struct ProjRopeArgs {
@@ -44,5 +48,6 @@ hipError_t launch_gemm_amax(const GemmAmaxArgs &a, hipStream_t s);
 hipError_t launch_grouped_gemm(const GroupedArgs &a, hipStream_t s);
 hipError_t launch_grouped_srelu(const GroupedArgs &a, hipStream_t s);
 hipError_t launch_proj_rope(const ProjRopeArgs &a, hipStream_t s);
+hipError_t launch_grouped_dswiglu(const GroupedArgs &a, hipStream_t s);
 
 }  // namespace bsg

@@ -7,6 +7,7 @@
  *   gemm_amax             "GEMM + Amax (SM100)"
  *   grouped_gemm          "Grouped GEMM (SM100 BF16)"
  *   grouped_gemm_srelu    "Grouped GEMM + sReLU (SM100)"
+ *   grouped_gemm_dswiglu  "Grouped GEMM + dSwiGLU (SM100)"
  *   gemm_proj_rope_mxfp8  "GEMM + RoPE + MXFP8 Projection (SM100)"
  *
  * Conventions shared by every entry point
@@ -192,6 +193,41 @@ int grouped_gemm_srelu_discrete(const void *a, const uint64_t *b_ptrs, const uin
                                 float tanh_clamp_scale, void *stream);
 
 /*
+ * grouped_gemm_dswiglu -- "Grouped GEMM + dSwiGLU (SM100)", Equations.
+ * For rows m of expert g (ranges as in grouped_gemm):
+ *     ref[m,n] = alpha[g]^2 * sum_k dequant(A)[m,k] * dequant(B)[n,k,g]
+ *     input, gate: C[m, 64b + o] and C[m, 64b + 32 + o] times beta[g],
+ *                  for ref column n = 32b + o (32-column pairs)
+ *     swish   = gate * sigmoid(gate)
+ *     D[m, 64b + o]      = ref * prob[m] * swish                      (ab)
+ *     D[m, 64b + 32 + o] = ref * prob[m] * input * sigmoid(gate)
+ *                           * (1 + gate * (1 - sigmoid(gate)))         (dswiglu)
+ *     dprob[m] += sum_n swish * input * ref
+ * evaluated in fp32 from the accumulator, then MXFP8-quantised like the
+ * FP8 D of grouped_gemm_srelu (Step 3, rcp_max = 1/448):
+ *  a, sfa, b, sfb, padded_offsets, alpha, prob   as for grouped_gemm_srelu
+ *  c        (M, 2N) bf16, n-major: the forward input/gate tensor
+ *  beta     (L,) fp32
+ *  d_row    (M, 2N) E4M3 codes in 32-wide blocks along 2N; sfd_row: scale
+ *           atoms over (M, 2N, 1)
+ *  d_col    (M, 2N) E4M3 codes in 32-tall blocks along M; sfd_col: scale
+ *           atoms over (2N, M, 1)
+ *  norm_const (1,) fp32 device scalar
+ *  dprob    (M,) fp32, accumulated with atomic adds: the caller zero-fills
+ *           it (as the page requires); 4-byte aligned
+ *  ab_dtype in {E4M3, E5M2} with c_dtype BF16 and d_dtype E4M3; FP4 inputs
+ *  (bf16/fp32 D with per-expert amax), other C dtypes and E5M2 D return
+ *  UNSUPPORTED.  Sizes: M % 256 == 0, 1 <= L <= 1024, K % 32 == 0,
+ *  N % 32 == 0.  Rows at or past padded_offsets[L-1] are not written.
+ */
+int grouped_gemm_dswiglu(const void *a, const void *b, const uint8_t *sfa, const uint8_t *sfb,
+                         const void *c, const int32_t *padded_offsets, const float *alpha,
+                         const float *beta, const float *prob, const float *norm_const,
+                         void *d_row, void *d_col, uint8_t *sfd_row, uint8_t *sfd_col,
+                         float *dprob, int64_t m, int64_t n, int64_t k, int64_t num_experts,
+                         int ab_dtype, int c_dtype, int d_dtype, int sf_vec_size, void *stream);
+
+/*
  * gemm_proj_rope_mxfp8 -- "GEMM + RoPE + MXFP8 Projection (SM100)",
  * Equations:
  *     Y[t,h,:] = (x W) reshaped to [tokens, num_heads, head_dim]
@@ -264,6 +300,14 @@ int bsg_validate_grouped_gemm_srelu_discrete(const void *a, const uint64_t *b_pt
                                              int64_t k, int64_t num_experts, int ab_dtype,
                                              int c_dtype, int d_dtype, int sf_vec_size,
                                              float tanh_clamp_scale);
+int bsg_validate_grouped_gemm_dswiglu(const void *a, const void *b, const uint8_t *sfa,
+                                      const uint8_t *sfb, const void *c,
+                                      const int32_t *padded_offsets, const float *alpha,
+                                      const float *beta, const float *prob,
+                                      const float *norm_const, void *d_row, void *d_col,
+                                      uint8_t *sfd_row, uint8_t *sfd_col, float *dprob,
+                                      int64_t m, int64_t n, int64_t k, int64_t num_experts,
+                                      int ab_dtype, int c_dtype, int d_dtype, int sf_vec_size);
 int bsg_validate_gemm_proj_rope_mxfp8(const void *x, const void *w, const uint8_t *x_scale,
                                       const uint8_t *w_scale, const void *cos, const void *sin,
                                       uint8_t *out_fp8_row, uint8_t *out_scales_row,

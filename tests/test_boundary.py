@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import block_scaled_gemm_02_amd as bsg
 
@@ -148,3 +149,28 @@ def test_proj_rope_validation():
     assert vp(head_dim=128) == UNSUP
     assert vp(q_lora=100) == SHAPE
     assert vp(w_out_in=0) == UNSUP                       # [in, out] weight not built
+
+
+def vdsw(**kw):
+    base = dict(a=P, b=P, sfa=P, sfb=P, c=P, padded_offsets=P, alpha=P, beta=P, prob=P, norm_const=P,
+                d_row=P, d_col=P, sfd_row=P, sfd_col=P, dprob=P, m=512, n=256, k=256, num_experts=4,
+                ab_dtype="e4m3")
+    base.update(kw)
+    return bsg.grouped_gemm_dswiglu(**base, validate_only=True)
+
+
+def test_dswiglu_validation():
+    assert vdsw() == OK
+    assert vdsw(ab_dtype="e5m2") == OK
+    assert vdsw(ab_dtype="e2m1") == UNSUP                # FP4 inputs (bf16 D + amax) not built
+    assert vdsw(m=300) == SHAPE                          # M % 256
+    assert vdsw(n=80) == SHAPE                           # N % 32
+    assert vdsw(k=48) == SHAPE                           # K % 32
+    assert vdsw(beta=None) == NULLPTR
+    assert vdsw(dprob=None) == NULLPTR
+    assert vdsw(c=None) == NULLPTR
+    assert vdsw(c_dtype=torch.float32) == UNSUP
+    assert vdsw(d_dtype=bsg.E5M2) == UNSUP
+    assert vdsw(d_dtype=torch.bfloat16) == DTYPE
+    assert vdsw(dprob=P + 2) == ALIGN
+    assert vdsw(num_experts=0) == SHAPE

@@ -1,0 +1,99 @@
+"""GPU parity of grouped_gemm_dswiglu ("Grouped GEMM + dSwiGLU (SM100)")
+against the CPU oracle, through the C ABI: MXFP8 D (row and column
+quantisation with their scale atoms) and dprob."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_gemm_02_amd as bsg
+import oracle as O
+import workloads as W
+from parity import U, ceil_div, check_mx_outputs, sum_bound
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def run_dswiglu(p):
+    s = p.sizes
+    t = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in p.t.items()}
+    m, n, k, L = s["m"], s["n"], s["k"], s["l"]
+    d = torch.full((m, 2 * n), 0xEE, dtype=torch.uint8, device="cuda")
+    d_col = torch.full((m, 2 * n), 0xEE, dtype=torch.uint8, device="cuda")
+    sfd_row = torch.full((W.sf_atom_bytes(m, 2 * n, 1),), 0xEE, dtype=torch.uint8, device="cuda")
+    sfd_col = torch.full((W.sf_atom_bytes(2 * n, m, 1),), 0xEE, dtype=torch.uint8, device="cuda")
+    dprob = torch.zeros(m, device="cuda")
+    bsg.grouped_gemm_dswiglu(t["a"], t["b"], t["sfa"], t["sfb"], t["c"], t["offsets"], t["alpha"], t["beta"],
+                             t["prob"], t["norm_const"], d, d_col, sfd_row, sfd_col, dprob, m, n, k, L,
+                             s["fmt"])
+    torch.cuda.synchronize()
+    return d, d_col, sfd_row, sfd_col, dprob
+
+
+def gather_scales(sfd_row, sfd_col, r0, r1, m, n2):
+    row_idx = O.sf_offset_grid(r0, r1, n2 // 32, 0, m, n2 // 32)
+    col_idx = O.sf_offset_grid(0, n2, ceil_div(r1, 32), 0, n2, m // 32)[:, r0 // 32:]
+    return sfd_row.cpu().numpy()[row_idx], sfd_col.cpu().numpy()[col_idx].T
+
+
+def bounds(p, r, valid):
+    """Error bounds of D and dprob from the bound of ref (fp32 accumulation and
+    the scaled MFMA's per-block truncation) and the epilogue's fp32 arithmetic."""
+    s = p.sizes
+    n, k = s["n"], s["k"]
+    off = p.t["offsets"].numpy()
+    grp = np.searchsorted(off, np.arange(valid), side="right")
+    beta = p.t["beta"].double().numpy()[grp][:, None]
+    c = p.t["c"][:valid].double().numpy()
+    cols = np.arange(n) // 32 * 64 + np.arange(n) % 32
+    x_in, x_gt = beta * c[:, cols], beta * c[:, cols + 32]
+    sg = 1.0 / (1.0 + np.exp(-x_gt))
+    sw = x_gt * sg
+    prob = p.t["prob"][:valid].double().numpy()[:, None]
+    ref = r["ref"][:valid]
+    bref = sum_bound(r["sabs"][:valid], k, bmax=r["bmax"][:valid])
+    d = r["d"][:valid]
+    b_ab = np.abs(prob * sw) * bref + 1e-5 * np.abs(d[:, cols]) + 1e-6 * np.abs(ref * prob) * (1 + np.abs(x_gt))
+    g_ds = np.abs(prob * x_in * sg * (1 + x_gt * (1 - sg)))
+    b_ds = g_ds * bref + 1e-5 * np.abs(d[:, cols + 32]) + 1e-6 * np.abs(ref * prob * x_in) * (1 + np.abs(x_gt))
+    bd = np.empty_like(d)
+    bd[:, cols], bd[:, cols + 32] = b_ab, b_ds
+    terms = np.abs(sw * x_in)
+    b_dp = (terms * bref).sum(1) + (1e-5 + 2 * 2 * n * U) * (terms * np.abs(ref)).sum(1)
+    return bd, b_dp
+
+
+CASES = [
+    dict(sizes=[256, 0, 512], n=160, k=256, fmt="e4m3"),       # ragged last n-tile (32 columns)
+    dict(sizes=[512, 256], n=256, k=384, fmt="e5m2"),
+    dict(sizes=[1024, 512, 0, 768, 256], n=512, k=1024, fmt="e4m3"),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_grouped_dswiglu_matches_oracle(case):
+    say(f"grouped_dswiglu parity {case}")
+    off = np.cumsum(case["sizes"]).astype(np.int32)
+    L = len(case["sizes"])
+    p = W.grouped_dswiglu_problem(0, L, case["n"], case["k"], case["fmt"], seed=6, offsets=off, extra_rows=256)
+    s = p.sizes
+    m, n, k = s["m"], s["n"], s["k"]
+    d, d_col, sfd_row, sfd_col, dprob = run_dswiglu(p)
+    valid = s["valid_m"]
+    r = O.grouped_dswiglu(p.t["a"], p.t["b"], p.t["sfa"], p.t["sfb"], off, p.t["alpha"], p.t["beta"],
+                          p.t["prob"], O.bits16(p.t["c"]), m, n, k, L, case["fmt"], 0, valid)
+    bd, b_dp = bounds(p, r, valid)
+    rs, cs = gather_scales(sfd_row, sfd_col, 0, valid, m, 2 * n)
+    res = check_mx_outputs(r["d"], bd, d[:valid].cpu().numpy(), rs, d_col[:valid].cpu().numpy(), cs, 1.0,
+                           what="D")
+    say(f"  {res}")
+    g = dprob[:valid].cpu().double().numpy()
+    err = np.abs(g - r["dprob"])
+    assert np.all(err <= b_dp), f"dprob: worst {float((err / np.maximum(b_dp, 1e-300)).max())} of its bound"
+    say(f"  dprob: max err / bound {float((err / np.maximum(b_dp, 1e-300)).max()):.3g}")
+    # rows at or past valid_m are not written; dprob there stays as the caller left it
+    assert torch.all(d[valid:] == 0xEE) and torch.all(d_col[valid:] == 0xEE)
+    assert torch.all(dprob[valid:] == 0)
