@@ -387,8 +387,9 @@ int bsg_validate_grouped_gemm_dswiglu(const void *a, const void *b, const uint8_
                                       const void *c, const int32_t *padded_offsets, const float *alpha,
                                       const float *beta, const float *prob, const float *norm_const,
                                       void *d_row, void *d_col, uint8_t *sfd_row, uint8_t *sfd_col,
-                                      float *dprob, int64_t m, int64_t n, int64_t k, int64_t num_experts,
-                                      int ab_dtype, int c_dtype, int d_dtype, int sf_vec_size)
+                                      float *dprob, float *amax, int64_t m, int64_t n, int64_t k,
+                                      int64_t num_experts, int ab_dtype, int c_dtype, int d_dtype,
+                                      int sf_vec_size)
 {
     int st = check_ab_sf(ab_dtype, sf_vec_size);
     if (st) return st;
@@ -396,28 +397,31 @@ int bsg_validate_grouped_gemm_dswiglu(const void *a, const void *b, const uint8_
         return st;
     if (k % 32) return fail(BSG_ERR_SHAPE, "K=%lld must be a multiple of sf_vec_size 32", (long long)k);
     if (n % 32) return fail(BSG_ERR_SHAPE, "N=%lld must be a multiple of 32", (long long)n);
-    if (ab_dtype == BSG_E2M1X2)
-        return fail(BSG_ERR_UNSUPPORTED, "FP4 inputs (bf16/fp32 D with amax) are not built; FP8 A/B are");
+    const bool fp4 = ab_dtype == BSG_E2M1X2;
     if (c_dtype != BSG_BF16) {
         if (is_float_out(c_dtype) || c_dtype == BSG_E4M3 || c_dtype == BSG_E5M2)
             return fail(BSG_ERR_UNSUPPORTED, "C dtype %d is not built (BF16 is)", c_dtype);
         return fail(BSG_ERR_DTYPE, "C dtype %d invalid", c_dtype);
     }
-    if (d_dtype != BSG_E4M3) {
+    if (fp4) {
+        // FP4 inputs: bf16 / fp32 D (d_col an optional copy), per-expert amax (L, 2) nullable
+        if (d_dtype != BSG_BF16 && d_dtype != BSG_F32) return fail(BSG_ERR_DTYPE, "FP4 inputs take a bf16 or fp32 D");
+    } else if (d_dtype != BSG_E4M3) {
         if (d_dtype == BSG_E5M2) return fail(BSG_ERR_UNSUPPORTED, "D dtype E5M2 is not built (E4M3 is)");
         return fail(BSG_ERR_DTYPE, "FP8 inputs take an FP8 D");
     }
     if (!beta) return fail(BSG_ERR_NULLPTR, "beta is required");
-    if (!norm_const || !d_col || !sfd_row || !sfd_col || !dprob)
-        return fail(BSG_ERR_NULLPTR, "norm_const, d_col, sfd_row, sfd_col and dprob are required");
+    if (!dprob) return fail(BSG_ERR_NULLPTR, "dprob is required");
+    if (!fp4 && (!norm_const || !d_col || !sfd_row || !sfd_col))
+        return fail(BSG_ERR_NULLPTR, "FP8 D needs norm_const, d_col, sfd_row and sfd_col");
     if (m * n == 0) return BSG_OK;
     if (!c) return fail(BSG_ERR_NULLPTR, "c is required");
     if (!sfa || !sfb) return fail(BSG_ERR_NULLPTR, "sfa and sfb are required");
-    if (!aligned16(c) || !aligned16(d_row) || !aligned16(d_col))
+    if (!aligned16(c) || !aligned16(d_row) || (d_col && !aligned16(d_col)))
         return fail(BSG_ERR_ALIGN, "C, D_row and D_col must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(sfd_row) | reinterpret_cast<uintptr_t>(sfd_col) |
-         reinterpret_cast<uintptr_t>(dprob)) & 3u)
-        return fail(BSG_ERR_ALIGN, "sfd_row, sfd_col and dprob must be 4-byte aligned");
+         reinterpret_cast<uintptr_t>(dprob) | reinterpret_cast<uintptr_t>(amax)) & 3u)
+        return fail(BSG_ERR_ALIGN, "sfd_row, sfd_col, dprob and amax must be 4-byte aligned");
     if ((int64_t)row_bytes(ab_dtype, k) * 256 >= (1ll << 31) || m * 2 * n >= (1ll << 31))
         return fail(BSG_ERR_UNSUPPORTED, "K or M*2N too large");
     return BSG_OK;
@@ -426,12 +430,12 @@ int bsg_validate_grouped_gemm_dswiglu(const void *a, const void *b, const uint8_
 int grouped_gemm_dswiglu(const void *a, const void *b, const uint8_t *sfa, const uint8_t *sfb, const void *c,
                          const int32_t *padded_offsets, const float *alpha, const float *beta,
                          const float *prob, const float *norm_const, void *d_row, void *d_col,
-                         uint8_t *sfd_row, uint8_t *sfd_col, float *dprob, int64_t m, int64_t n, int64_t k,
-                         int64_t num_experts, int ab_dtype, int c_dtype, int d_dtype, int sf_vec_size,
-                         void *stream)
+                         uint8_t *sfd_row, uint8_t *sfd_col, float *dprob, float *amax, int64_t m, int64_t n,
+                         int64_t k, int64_t num_experts, int ab_dtype, int c_dtype, int d_dtype,
+                         int sf_vec_size, void *stream)
 {
     int st = bsg_validate_grouped_gemm_dswiglu(a, b, sfa, sfb, c, padded_offsets, alpha, beta, prob, norm_const,
-                                               d_row, d_col, sfd_row, sfd_col, dprob, m, n, k, num_experts,
+                                               d_row, d_col, sfd_row, sfd_col, dprob, amax, m, n, k, num_experts,
                                                ab_dtype, c_dtype, d_dtype, sf_vec_size);
     if (st) return st;
     if ((st = check_device())) return st;
@@ -443,6 +447,7 @@ int grouped_gemm_dswiglu(const void *a, const void *b, const uint8_t *sfa, const
     args.m = m; args.n = n; args.k = k; args.num_experts = num_experts;
     args.fmt = fmt_of(ab_dtype); args.c_dtype = c_dtype; args.d_dtype = d_dtype;
     args.beta = beta; args.cfwd = static_cast<const uint16_t *>(c); args.dprob = dprob;
+    args.amax = ab_dtype == BSG_E2M1X2 ? amax : nullptr;
     return launch_status(bsg::launch_grouped_dswiglu(args, static_cast<hipStream_t>(stream)),
                          "grouped_gemm_dswiglu");
 }

@@ -143,7 +143,8 @@ hipError_t launch_gemm_amax(const GemmAmaxArgs &a, hipStream_t s)
 // ---------------------------------------------------------------------------
 // Grouped GEMM over padded_offsets expert ranges
 // ---------------------------------------------------------------------------
-enum : int { EPI_BF16_BIAS = 0, EPI_SRELU = 1, EPI_SRELU_FP8 = 2, EPI_BF16 = 3, EPI_DSWIGLU_FP8 = 4 };
+enum : int { EPI_BF16_BIAS = 0, EPI_SRELU = 1, EPI_SRELU_FP8 = 2, EPI_BF16 = 3, EPI_DSWIGLU_FP8 = 4,
+             EPI_DSWIGLU = 5 };
 
 struct GroupedParams {
     const uint8_t *a, *b, *sfa, *sfb;
@@ -498,11 +499,98 @@ __device__ __forceinline__ void epilogue_dswiglu_fp8(const GroupedParams &p, f32
     });
 }
 
+// dSwiGLU backward with an unquantised D (FP4 inputs: "Grouped GEMM + dSwiGLU
+// (SM100)", Input/Output tensors: bf16 or fp32 D, per-expert amax (L, 2)).
+// Same arithmetic as epilogue_dswiglu_fp8; D (and the optional D_col copy)
+// is stored through the wave's staging rows, and amax[2g] / amax[2g+1] take
+// max |ab| / max |dswiglu| (fp32 values) with one atomic each per workgroup.
+template <int OT>
+__device__ __forceinline__ void epilogue_dswiglu(const GroupedParams &p, f32x16 (&acc)[4][4], uint8_t *stage,
+                                                 int64_t m0, int64_t n0, int g, float alpha2, float beta,
+                                                 int wm, int wn, int lane, float *red, const float *prob_lds)
+{
+    constexpr int ES = OT == DT_F32 ? 4 : 2;
+    typedef StageGeom<ES, 8> G;                     // the wave's 256 D columns per staged row
+    const int64_t n = p.n, n2 = 2 * n;
+    const int c32 = lane & 31, gh = lane >> 5;
+    const int64_t qr = m0 + 128 * wm, qc = n0 + 128 * wn, dq = 2 * qc;
+    const int cols = clamp_extent(n - qc);
+    const int dcols = 2 * cols;
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = prob_lds[acc_row(wm, i, lane)];
+    uint8_t *wd = stage + c32 * G::RBP + 4 * gh * ES;
+    float mab = 0.0f, mds = 0.0f;
+    static_for<4>([&](auto ii) {
+        constexpr int i = decltype(ii)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        const int64_t row = qr + 32 * i + c32;
+        const uint16_t *crow = p.cfwd + row * n2 + 64 * (qc / 32) + 4 * gh;
+        float dpr = 0.0f;
+        static_for<4>([&](auto jj) {
+            constexpr int j = decltype(jj)::value;
+            const bool ok = 32 * j < cols;
+            uint2 ci[4], cg[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                ci[q] = ok ? *reinterpret_cast<const uint2 *>(crow + 64 * j + 8 * q) : make_uint2(0u, 0u);
+                cg[q] = ok ? *reinterpret_cast<const uint2 *>(crow + 64 * j + 32 + 8 * q) : make_uint2(0u, 0u);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float ab[4], ds[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int v = 4 * q + u;
+                    const float ref = alpha2 * acc[i][j][v];
+                    const float in = beta * bf16_at(ci[q], u);
+                    const float gt = beta * bf16_at(cg[q], u);
+                    const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gt));
+                    const float sw = gt * sg;
+                    const float rp = ref * pr[i];
+                    ab[u] = rp * sw;
+                    ds[u] = rp * in * sg * fmaf(gt, 1.0f - sg, 1.0f);
+                    dpr = fmaf(sw * in, ref, dpr);
+                    mab = fmaxf(mab, fabsf(ab[u]));
+                    mds = fmaxf(mds, fabsf(ds[u]));
+                }
+                *reinterpret_cast<typename Quad<ES>::T *>(wd + (64 * j + 8 * q) * ES) =
+                    pack_quad<OT>(ab[0], ab[1], ab[2], ab[3]);
+                *reinterpret_cast<typename Quad<ES>::T *>(wd + (64 * j + 32 + 8 * q) * ES) =
+                    pack_quad<OT>(ds[0], ds[1], ds[2], ds[3]);
+            }
+        });
+        dpr += xor32(dpr);
+        if (gh == 0 && cols > 0) atomicAdd(p.dprob + row, dpr);
+        const uint32_t rb = (uint32_t)(n2 * ES);
+        stage_flush<ES, 8>(stage, static_cast<char *>(p.d) + ((qr + 32 * i) * n2 + dq) * ES, rb, 32, dcols * ES, lane);
+        if (p.d_col)
+            stage_flush<ES, 8>(stage, static_cast<char *>(p.d_col) + ((qr + 32 * i) * n2 + dq) * ES, rb, 32,
+                               dcols * ES, lane);
+    });
+    if (p.amax) {
+        // both maxima with one barrier: red[w] and red[4 + w]
+        const float wab = wave_max(mab), wds = wave_max(mds);
+        const int t = threadIdx.x;
+        if ((t & 63) == 0) {
+            red[t >> 6] = wab;
+            red[4 + (t >> 6)] = wds;
+        }
+        __syncthreads();
+        if (t == 0) {
+            const float a0 = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+            const float a1 = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
+            if (a0 > 0.0f) atomicMax(reinterpret_cast<unsigned int *>(p.amax + 2 * g), __float_as_uint(a0));
+            if (a1 > 0.0f) atomicMax(reinterpret_cast<unsigned int *>(p.amax + 2 * g + 1), __float_as_uint(a1));
+        }
+    }
+}
+
 template <int F, int EPI, bool CLAMP, int OT = -1>
 __global__ void __launch_bounds__(256) k_grouped(GroupedParams p)
 {
     BSG_DECLARE_RING(F, ring);
-    __shared__ float red[4];
+    __shared__ float red[8];
     __shared__ __attribute__((aligned(16))) float prob_lds[kTileM];
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
     const TileCoord tc = tile_of(blockIdx.x, p.m / kTileM, (p.n + kTileN - 1) / kTileN, (int64_t)gridDim.x);
@@ -541,6 +629,9 @@ __global__ void __launch_bounds__(256) k_grouped(GroupedParams p)
     } else if constexpr (EPI == EPI_DSWIGLU_FP8) {
         epilogue_dswiglu_fp8(p, acc, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), m0, n0, alpha * alpha,
                              p.beta[g], wm, wn, lane, prob_lds);
+    } else if constexpr (EPI == EPI_DSWIGLU) {
+        epilogue_dswiglu<OT>(p, acc, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), m0, n0, g, alpha * alpha,
+                             p.beta[g], wm, wn, lane, red, prob_lds);
     } else {
         epilogue_grouped<F, EPI, CLAMP, OT>(p, acc, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), m0, n0, g,
                                             alpha, wm, wn, lane, red, prob_lds);
@@ -627,12 +718,24 @@ namespace bsg {
 
 hipError_t launch_grouped_dswiglu(const GroupedArgs &a, hipStream_t s)
 {
+    if (a.fmt == FMT_E2M1) {
+        // FP4 inputs: per-expert amax (L, 2), zero-filled first (also for an empty problem)
+        hipError_t e = zero_floats(a.amax, 2 * a.num_experts, s);
+        if (e != hipSuccess) return e;
+    }
     if (a.m == 0 || a.n == 0) return hipSuccess;
     GroupedParams p = grouped_params(a);
     dim3 grid((unsigned)(((a.n + kTileN - 1) / kTileN) * (a.m / kTileM)));
-    if (a.fmt == FMT_E4M3) hipLaunchKernelGGL((k_grouped<FMT_E4M3, EPI_DSWIGLU_FP8, false>), grid, dim3(kThreads), 0, s, p);
-    else if (a.fmt == FMT_E5M2) hipLaunchKernelGGL((k_grouped<FMT_E5M2, EPI_DSWIGLU_FP8, false>), grid, dim3(kThreads), 0, s, p);
-    else return hipErrorNotSupported;
+    if (a.fmt == FMT_E2M1) {
+        if (a.d_dtype == DT_F32) hipLaunchKernelGGL((k_grouped<FMT_E2M1, EPI_DSWIGLU, false, DT_F32>), grid, dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_grouped<FMT_E2M1, EPI_DSWIGLU, false, DT_BF16>), grid, dim3(kThreads), 0, s, p);
+    } else if (a.fmt == FMT_E4M3) {
+        hipLaunchKernelGGL((k_grouped<FMT_E4M3, EPI_DSWIGLU_FP8, false>), grid, dim3(kThreads), 0, s, p);
+    } else if (a.fmt == FMT_E5M2) {
+        hipLaunchKernelGGL((k_grouped<FMT_E5M2, EPI_DSWIGLU_FP8, false>), grid, dim3(kThreads), 0, s, p);
+    } else {
+        return hipErrorNotSupported;
+    }
     return hipGetLastError();
 }
 

@@ -203,8 +203,9 @@ int grouped_gemm_srelu_discrete(const void *a, const uint64_t *b_ptrs, const uin
  *     D[m, 64b + 32 + o] = ref * prob[m] * input * sigmoid(gate)
  *                           * (1 + gate * (1 - sigmoid(gate)))         (dswiglu)
  *     dprob[m] += sum_n swish * input * ref
- * evaluated in fp32 from the accumulator, then MXFP8-quantised like the
- * FP8 D of grouped_gemm_srelu (Step 3, rcp_max = 1/448):
+ * evaluated in fp32 from the accumulator.  With FP8 (E4M3 / E5M2) A/B, D is
+ * MXFP8-quantised like the FP8 D of grouped_gemm_srelu (Step 3, rcp_max =
+ * 1/448):
  *  a, sfa, b, sfb, padded_offsets, alpha, prob   as for grouped_gemm_srelu
  *  c        (M, 2N) bf16, n-major: the forward input/gate tensor
  *  beta     (L,) fp32
@@ -215,17 +216,22 @@ int grouped_gemm_srelu_discrete(const void *a, const uint64_t *b_ptrs, const uin
  *  norm_const (1,) fp32 device scalar
  *  dprob    (M,) fp32, accumulated with atomic adds: the caller zero-fills
  *           it (as the page requires); 4-byte aligned
- *  ab_dtype in {E4M3, E5M2} with c_dtype BF16 and d_dtype E4M3; FP4 inputs
- *  (bf16/fp32 D with per-expert amax), other C dtypes and E5M2 D return
- *  UNSUPPORTED.  Sizes: M % 256 == 0, 1 <= L <= 1024, K % 32 == 0,
- *  N % 32 == 0.  Rows at or past padded_offsets[L-1] are not written.
+ * With FP4 (E2M1X2) A/B, D is unquantised (the page's FP4-input form):
+ *  d_row    (M, 2N) d_dtype BF16 or F32 (RNE cast); d_col: nullable copy
+ *  amax     (L, 2) fp32, nullable: amax[g][0] = max |ab|, amax[g][1] =
+ *           max |dswiglu| over expert g's rows (fp32 values before the
+ *           cast); zero-filled by the library; norm_const and sfd_* unused
+ *  c_dtype BF16.  E5M2 D and other C dtypes return UNSUPPORTED.
+ *  Sizes: M % 256 == 0, 1 <= L <= 1024, K % 32 == 0, N % 32 == 0.  Rows at
+ *  or past padded_offsets[L-1] are not written.
  */
 int grouped_gemm_dswiglu(const void *a, const void *b, const uint8_t *sfa, const uint8_t *sfb,
                          const void *c, const int32_t *padded_offsets, const float *alpha,
                          const float *beta, const float *prob, const float *norm_const,
                          void *d_row, void *d_col, uint8_t *sfd_row, uint8_t *sfd_col,
-                         float *dprob, int64_t m, int64_t n, int64_t k, int64_t num_experts,
-                         int ab_dtype, int c_dtype, int d_dtype, int sf_vec_size, void *stream);
+                         float *dprob, float *amax, int64_t m, int64_t n, int64_t k,
+                         int64_t num_experts, int ab_dtype, int c_dtype, int d_dtype,
+                         int sf_vec_size, void *stream);
 
 /*
  * gemm_proj_rope_mxfp8 -- "GEMM + RoPE + MXFP8 Projection (SM100)",
@@ -306,8 +312,9 @@ int bsg_validate_grouped_gemm_dswiglu(const void *a, const void *b, const uint8_
                                       const float *beta, const float *prob,
                                       const float *norm_const, void *d_row, void *d_col,
                                       uint8_t *sfd_row, uint8_t *sfd_col, float *dprob,
-                                      int64_t m, int64_t n, int64_t k, int64_t num_experts,
-                                      int ab_dtype, int c_dtype, int d_dtype, int sf_vec_size);
+                                      float *amax, int64_t m, int64_t n, int64_t k,
+                                      int64_t num_experts, int ab_dtype, int c_dtype,
+                                      int d_dtype, int sf_vec_size);
 int bsg_validate_gemm_proj_rope_mxfp8(const void *x, const void *w, const uint8_t *x_scale,
                                       const uint8_t *w_scale, const void *cos, const void *sin,
                                       uint8_t *out_fp8_row, uint8_t *out_scales_row,

@@ -162,7 +162,11 @@ def vdsw(**kw):
 def test_dswiglu_validation():
     assert vdsw() == OK
     assert vdsw(ab_dtype="e5m2") == OK
-    assert vdsw(ab_dtype="e2m1") == UNSUP                # FP4 inputs (bf16 D + amax) not built
+    assert vdsw(ab_dtype="e2m1") == DTYPE                # FP4 inputs take a bf16 / fp32 D
+    assert vdsw(ab_dtype="e2m1", d_dtype=torch.bfloat16, norm_const=None, sfd_row=None, sfd_col=None,
+                d_col=None, amax=P) == OK
+    assert vdsw(ab_dtype="e2m1", d_dtype=torch.float32) == OK
+    assert vdsw(ab_dtype="e2m1", d_dtype=torch.bfloat16, amax=P + 2) == ALIGN
     assert vdsw(m=300) == SHAPE                          # M % 256
     assert vdsw(n=80) == SHAPE                           # N % 32
     assert vdsw(k=48) == SHAPE                           # K % 32

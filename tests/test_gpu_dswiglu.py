@@ -8,7 +8,7 @@ import torch
 import block_scaled_gemm_02_amd as bsg
 import oracle as O
 import workloads as W
-from parity import U, ceil_div, check_mx_outputs, sum_bound
+from parity import U, ceil_div, check_float, check_mx_outputs, sum_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -97,3 +97,51 @@ def test_grouped_dswiglu_matches_oracle(case):
     # rows at or past valid_m are not written; dprob there stays as the caller left it
     assert torch.all(d[valid:] == 0xEE) and torch.all(d_col[valid:] == 0xEE)
     assert torch.all(dprob[valid:] == 0)
+
+
+FP4_CASES = [
+    dict(sizes=[256, 0, 512], n=160, k=256, d=torch.bfloat16),
+    dict(sizes=[512, 256, 256], n=256, k=512, d=torch.float32),
+]
+
+
+@pytest.mark.parametrize("case", FP4_CASES)
+def test_grouped_dswiglu_fp4_inputs_bf16_or_f32_d_and_amax(case):
+    """FP4 inputs: unquantised D (RNE cast), its optional copy D_col, and the
+    per-expert amax (L, 2) of ab and dswiglu, against the oracle."""
+    say(f"grouped_dswiglu FP4 inputs {case}")
+    off = np.cumsum(case["sizes"]).astype(np.int32)
+    L = len(case["sizes"])
+    p = W.grouped_dswiglu_problem(0, L, case["n"], case["k"], "e2m1", seed=8, offsets=off, extra_rows=256)
+    s = p.sizes
+    m, n, k = s["m"], s["n"], s["k"]
+    t = {kk: (v.cuda() if isinstance(v, torch.Tensor) else v) for kk, v in p.t.items()}
+    sent = float("nan")
+    d = torch.full((m, 2 * n), sent, dtype=case["d"], device="cuda")
+    d_col = torch.full((m, 2 * n), sent, dtype=case["d"], device="cuda")
+    dprob = torch.zeros(m, device="cuda")
+    amax = torch.full((L, 2), -1.0, device="cuda")
+    bsg.grouped_gemm_dswiglu(t["a"], t["b"], t["sfa"], t["sfb"], t["c"], t["offsets"], t["alpha"], t["beta"],
+                             t["prob"], None, d, d_col, None, None, dprob, m, n, k, L, "e2m1",
+                             d_dtype=case["d"], amax=amax)
+    torch.cuda.synchronize()
+    valid = s["valid_m"]
+    r = O.grouped_dswiglu(p.t["a"], p.t["b"], p.t["sfa"], p.t["sfb"], off, p.t["alpha"], p.t["beta"],
+                          p.t["prob"], O.bits16(p.t["c"]), m, n, k, L, "e2m1", 0, valid)
+    bd, b_dp = bounds(p, r, valid)
+    res = check_float(d[:valid].cpu(), r["d"], bd, what="D")
+    say(f"  D: {res}")
+    assert torch.equal(d_col[:valid], d[:valid])
+    g = dprob[:valid].cpu().double().numpy()
+    assert np.all(np.abs(g - r["dprob"]) <= b_dp)
+    # amax (L, 2): max |ab| and max |dswiglu| over each expert's rows, 0 for an empty expert
+    grp = np.searchsorted(off, np.arange(valid), side="right")
+    cols = np.arange(n) // 32 * 64 + np.arange(n) % 32
+    ga = amax.cpu().double().numpy()
+    for gi in range(L):
+        sel = grp == gi
+        for h, cc in ((0, cols), (1, cols + 32)):
+            o = float(np.abs(r["d"][sel][:, cc]).max()) if sel.any() else 0.0
+            bnd = float(bd[sel][:, cc].max()) if sel.any() else 0.0
+            assert abs(ga[gi, h] - o) <= bnd + 1e-6 * o, (gi, h, ga[gi, h], o, bnd)
+    assert torch.all(torch.isnan(d[valid:].float())) and torch.all(dprob[valid:] == 0)
