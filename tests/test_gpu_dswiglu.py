@@ -39,23 +39,24 @@ def gather_scales(sfd_row, sfd_col, r0, r1, m, n2):
     return sfd_row.cpu().numpy()[row_idx], sfd_col.cpu().numpy()[col_idx].T
 
 
-def bounds(p, r, valid):
-    """Error bounds of D and dprob from the bound of ref (fp32 accumulation and
-    the scaled MFMA's per-block truncation) and the epilogue's fp32 arithmetic."""
+def bounds(p, r, r0, r1):
+    """Error bounds of D and dprob for rows [r0, r1) (the rows of oracle result
+    r) from the bound of ref (fp32 accumulation and the scaled MFMA's per-block
+    truncation) and the epilogue's fp32 arithmetic."""
     s = p.sizes
     n, k = s["n"], s["k"]
-    off = p.t["offsets"].numpy()
-    grp = np.searchsorted(off, np.arange(valid), side="right")
-    beta = p.t["beta"].double().numpy()[grp][:, None]
-    c = p.t["c"][:valid].double().numpy()
+    off = p.t["offsets"].cpu().numpy()
+    grp = np.searchsorted(off, np.arange(r0, r1), side="right")
+    beta = p.t["beta"].cpu().double().numpy()[grp][:, None]
+    c = p.t["c"][r0:r1].cpu().double().numpy()
     cols = np.arange(n) // 32 * 64 + np.arange(n) % 32
     x_in, x_gt = beta * c[:, cols], beta * c[:, cols + 32]
     sg = 1.0 / (1.0 + np.exp(-x_gt))
     sw = x_gt * sg
-    prob = p.t["prob"][:valid].double().numpy()[:, None]
-    ref = r["ref"][:valid]
-    bref = sum_bound(r["sabs"][:valid], k, bmax=r["bmax"][:valid])
-    d = r["d"][:valid]
+    prob = p.t["prob"][r0:r1].cpu().double().numpy()[:, None]
+    ref = r["ref"]
+    bref = sum_bound(r["sabs"], k, bmax=r["bmax"])
+    d = r["d"]
     b_ab = np.abs(prob * sw) * bref + 1e-5 * np.abs(d[:, cols]) + 1e-6 * np.abs(ref * prob) * (1 + np.abs(x_gt))
     g_ds = np.abs(prob * x_in * sg * (1 + x_gt * (1 - sg)))
     b_ds = g_ds * bref + 1e-5 * np.abs(d[:, cols + 32]) + 1e-6 * np.abs(ref * prob * x_in) * (1 + np.abs(x_gt))
@@ -85,7 +86,7 @@ def test_grouped_dswiglu_matches_oracle(case):
     valid = s["valid_m"]
     r = O.grouped_dswiglu(p.t["a"], p.t["b"], p.t["sfa"], p.t["sfb"], off, p.t["alpha"], p.t["beta"],
                           p.t["prob"], O.bits16(p.t["c"]), m, n, k, L, case["fmt"], 0, valid)
-    bd, b_dp = bounds(p, r, valid)
+    bd, b_dp = bounds(p, r, 0, valid)
     rs, cs = gather_scales(sfd_row, sfd_col, 0, valid, m, 2 * n)
     res = check_mx_outputs(r["d"], bd, d[:valid].cpu().numpy(), rs, d_col[:valid].cpu().numpy(), cs, 1.0,
                            what="D")
@@ -128,7 +129,7 @@ def test_grouped_dswiglu_fp4_inputs_bf16_or_f32_d_and_amax(case):
     valid = s["valid_m"]
     r = O.grouped_dswiglu(p.t["a"], p.t["b"], p.t["sfa"], p.t["sfb"], off, p.t["alpha"], p.t["beta"],
                           p.t["prob"], O.bits16(p.t["c"]), m, n, k, L, "e2m1", 0, valid)
-    bd, b_dp = bounds(p, r, valid)
+    bd, b_dp = bounds(p, r, 0, valid)
     res = check_float(d[:valid].cpu(), r["d"], bd, what="D")
     say(f"  D: {res}")
     assert torch.equal(d_col[:valid], d[:valid])
@@ -145,3 +146,37 @@ def test_grouped_dswiglu_fp4_inputs_bf16_or_f32_d_and_amax(case):
             bnd = float(bd[sel][:, cc].max()) if sel.any() else 0.0
             assert abs(ga[gi, h] - o) <= bnd + 1e-6 * o, (gi, h, ga[gi, h], o, bnd)
     assert torch.all(torch.isnan(d[valid:].float())) and torch.all(dprob[valid:] == 0)
+
+
+def test_grouped_dswiglu_full_size_sampled():
+    """The bench configuration (config-4 routing, N = 2048, K = 7168, MXFP8 D):
+    the first 128 rows (routed rows) of three experts against the oracle
+    computed for those rows alone (D codes and scale atoms in both
+    directions, dprob)."""
+    say("grouped_dswiglu full size")
+    p = W.grouped_dswiglu_problem(28672, 32, 2048, 7168, "e4m3", seed=0, device="cuda")
+    s = p.sizes
+    m, n, k, L = s["m"], s["n"], s["k"], s["l"]
+    d, d_col, sfd_row, sfd_col, dprob = run_dswiglu(p)
+    t = p.t
+    off = t["offsets"].cpu().numpy()
+    m_t, n_t, k_t = ceil_div(m, 128), ceil_div(n, 128), ceil_div(k, 128)
+    begins = np.concatenate([[0], off[:-1]])
+    nonempty = [g for g in range(L) if off[g] > begins[g]]
+    for g in (nonempty[0], nonempty[len(nonempty) // 2], nonempty[-1]):
+        r0 = int(begins[g])
+        assert float(t["prob"][r0].item()) > 0.0           # a routed row
+        say(f"  oracle expert {g} rows {r0}..{r0 + 127}")
+        sfa = t["sfa"][(r0 // 128) * k_t * 512:(r0 // 128 + 1) * k_t * 512]
+        sfb = t["sfb"][g * n_t * k_t * 512:(g + 1) * n_t * k_t * 512]
+        r = O.grouped_dswiglu(t["a"][r0:r0 + 128].cpu(), t["b"][g:g + 1].cpu(), sfa.cpu(), sfb.cpu(),
+                              np.array([128], np.int32), t["alpha"][g:g + 1].cpu(), t["beta"][g:g + 1].cpu(),
+                              t["prob"][r0:r0 + 128].cpu(), O.bits16(t["c"][r0:r0 + 128].cpu()), 128, n, k, 1,
+                              "e4m3")
+        bd, b_dp = bounds(p, r, r0, r0 + 128)
+        rs, cs = gather_scales(sfd_row, sfd_col, r0, r0 + 128, m, 2 * n)
+        res = check_mx_outputs(r["d"], bd, d[r0:r0 + 128].cpu().numpy(), rs, d_col[r0:r0 + 128].cpu().numpy(),
+                               cs, 1.0, what=f"D e{g}")
+        say(f"  {res}")
+        gdp = dprob[r0:r0 + 128].cpu().double().numpy()
+        assert np.all(np.abs(gdp - r["dprob"]) <= b_dp)

@@ -128,8 +128,8 @@ def test_grouped_srelu_full_size_sampled():
     begins = np.concatenate([[0], off[:-1]])
     nonempty = [g for g in range(L) if off[g] > begins[g]]
     for g in (nonempty[0], nonempty[len(nonempty) // 2], nonempty[-1]):
-        r0 = int(off[g]) - 128                     # last 128-row group of expert g
-        assert O.expert_of_row(off, L, r0) == g
+        r0 = int(begins[g])                        # first 128 rows of expert g: routed rows
+        assert O.expert_of_row(off, L, r0) == g and float(t["prob"][r0].item()) > 0.0
         say(f"  oracle expert {g} rows {r0}..{r0 + 127}")
         sub = O.grouped_srelu(t["a"][r0:r0 + 128].cpu(), t["b"][g:g + 1].cpu(),
                               sf_slice(t["sfa"], 0, m_t, k_t, r0 // 128, r0 // 128 + 1).cpu(),
@@ -230,7 +230,8 @@ def test_grouped_srelu_fp8_out_full_size_sampled():
     begins = np.concatenate([[0], off[:-1]])
     nonempty = [g for g in range(L) if off[g] > begins[g]]
     for g in (nonempty[0], nonempty[-1]):
-        r0 = int(off[g]) - 128
+        r0 = int(begins[g])                        # routed rows
+        assert float(t["prob"][r0].item()) > 0.0
         say(f"  oracle expert {g} rows {r0}..{r0 + 127}")
         sub = O.grouped_srelu(t["a"][r0:r0 + 128].cpu(), t["b"][g:g + 1].cpu(),
                               sf_slice(t["sfa"], 0, m_t, k_t, r0 // 128, r0 // 128 + 1).cpu(),
@@ -305,8 +306,8 @@ def test_grouped_bf16_full_size_sampled():
     begins = np.concatenate([[0], off[:-1]])
     nonempty = [g for g in range(L) if off[g] > begins[g]]
     for g in (nonempty[0], nonempty[len(nonempty) // 2], nonempty[-1]):
-        r0 = int(off[g]) - 64
-        assert O.expert_of_row(off, L, r0) == g
+        r0 = int(begins[g])                        # first 64 rows of expert g: routed rows
+        assert O.expert_of_row(off, L, r0) == g and float(t["prob"][r0].item()) > 0.0
         say(f"  oracle expert {g} rows {r0}..{r0 + 63}")
         sub = O.grouped_bf16(O.bits16(t["a"][r0:r0 + 64]), O.bits16(t["b"][g:g + 1]),
                              np.array([64], np.int32), t["alpha"][g:g + 1].cpu(),
