@@ -54,6 +54,7 @@ def lib():
         L.orc_dec_e8m0.restype = d; L.orc_dec_e8m0.argtypes = [u32]
         L.orc_dec_bf16.restype = d; L.orc_dec_bf16.argtypes = [u32]
         L.orc_enc_e4m3.restype = u32; L.orc_enc_e4m3.argtypes = [d]
+        L.orc_enc_e5m2.restype = u32; L.orc_enc_e5m2.argtypes = [d]
         L.orc_rne_bf16.restype = u32; L.orc_rne_bf16.argtypes = [d]
         L.orc_e8m0_ceil.restype = u32; L.orc_e8m0_ceil.argtypes = [d]
         L.orc_rne_bf16_array.restype = None; L.orc_rne_bf16_array.argtypes = [p, p, i64]
@@ -74,9 +75,9 @@ def lib():
         L.orc_proj_rope_mx.restype = i32
         L.orc_proj_rope_mx.argtypes = [p] * 6 + [i64] * 7 + [p, p]
         L.orc_mx_quant_rows.restype = None
-        L.orc_mx_quant_rows.argtypes = [p, i64, i64, i64, ctypes.c_float, p, p]
+        L.orc_mx_quant_rows.argtypes = [p, i64, i64, i64, ctypes.c_float, i32, p, p]
         L.orc_mx_quant_cols.restype = None
-        L.orc_mx_quant_cols.argtypes = [p, i64, i64, i64, ctypes.c_float, p, p]
+        L.orc_mx_quant_cols.argtypes = [p, i64, i64, i64, ctypes.c_float, i32, p, p]
         L.orc_num_threads.restype = i32
         _lib = L
     return _lib
@@ -118,6 +119,7 @@ def dec_e5m2(code: int) -> float: return lib().orc_dec_e5m2(code)
 def dec_e8m0(b: int) -> float: return lib().orc_dec_e8m0(b)
 def dec_bf16(h: int) -> float: return lib().orc_dec_bf16(h)
 def enc_e4m3(x: float) -> int: return lib().orc_enc_e4m3(float(x))
+def enc_e5m2(x: float) -> int: return lib().orc_enc_e5m2(float(x))
 def rne_bf16(x: float) -> int: return lib().orc_rne_bf16(float(x))
 def e8m0_ceil(sigma: float) -> int: return lib().orc_e8m0_ceil(float(sigma))
 
@@ -301,21 +303,22 @@ def proj_rope_mx(x_codes, x_scale, w_codes, w_scale, cos_bits, sin_bits, tokens,
 # ---------------------------------------------------------------------------
 # [GD] Step 3: MX output quantiser (row and column direction, blocks of 32)
 # ---------------------------------------------------------------------------
-def mx_quant_rows(d: np.ndarray, norm_const: float = 1.0):
-    """Blocks of 32 along each row -> (codes uint8 (R,C), scales uint8 (R, ceil(C/32)))."""
+def mx_quant_rows(d: np.ndarray, norm_const: float = 1.0, fmt: str = "e4m3"):
+    """Blocks of 32 along each row -> (codes uint8 (R,C), scales uint8 (R, ceil(C/32)));
+    fmt "e4m3" (rcp_max 1/448) or "e5m2" (1/57344)."""
     d = np.ascontiguousarray(d, dtype=np.float64)
     r, c = d.shape
     codes = np.empty((r, c), dtype=np.uint8)
     scales = np.empty((r, -(-c // 32)), dtype=np.uint8)
-    lib().orc_mx_quant_rows(_ptr(d), r, c, c, float(norm_const), _ptr(codes), _ptr(scales))
+    lib().orc_mx_quant_rows(_ptr(d), r, c, c, float(norm_const), _FMT[fmt], _ptr(codes), _ptr(scales))
     return codes, scales
 
 
-def mx_quant_cols(d: np.ndarray, norm_const: float = 1.0):
+def mx_quant_cols(d: np.ndarray, norm_const: float = 1.0, fmt: str = "e4m3"):
     """Blocks of 32 down each column -> (codes (R,C), scales (ceil(R/32), C))."""
     d = np.ascontiguousarray(d, dtype=np.float64)
     r, c = d.shape
     codes = np.empty((r, c), dtype=np.uint8)
     scales = np.empty((-(-r // 32), c), dtype=np.uint8)
-    lib().orc_mx_quant_cols(_ptr(d), r, c, c, float(norm_const), _ptr(codes), _ptr(scales))
+    lib().orc_mx_quant_cols(_ptr(d), r, c, c, float(norm_const), _FMT[fmt], _ptr(codes), _ptr(scales))
     return codes, scales

@@ -129,6 +129,33 @@ uint32_t orc_enc_e4m3(double x)
     }
 }
 
+/* fp64 -> E5M2 code, round to nearest even; magnitudes at or above the
+ * largest finite value (57344) saturate to it; never returns Inf or NaN. */
+uint32_t orc_enc_e5m2(double x)
+{
+    uint32_t s = signbit(x) ? 0x80u : 0u;
+    double a = fabs(x), q;
+    int e2;
+    if (isnan(x)) return 0x7Fu;
+    if (a >= 57344.0) return s | 0x7Bu;
+    if (a == 0.0) return s;
+    frexp(a, &e2);
+    {
+        int ulp_exp = e2 - 1 - 2;          /* 2 stored mantissa bits */
+        if (ulp_exp < -16) ulp_exp = -16;  /* subnormal spacing 2^-16 */
+        q = rne_to_step(a, ldexp(1.0, ulp_exp));
+    }
+    if (q >= 57344.0) return s | 0x7Bu;
+    if (q == 0.0) return s;
+    if (q < ldexp(1.0, -14)) return s | (uint32_t)(q / ldexp(1.0, -16));   /* subnormal */
+    frexp(q, &e2);
+    {
+        int E = e2 - 1;
+        uint32_t m = (uint32_t)((q / ldexp(1.0, E) - 1.0) * 4.0);
+        return s | ((uint32_t)(E + 15) << 2) | m;
+    }
+}
+
 /* fp64 -> bf16 bits with a single round-to-nearest-even step. */
 uint32_t orc_rne_bf16(double x)
 {
@@ -618,7 +645,8 @@ int orc_proj_rope_mx(const uint8_t *x, const uint8_t *x_scale, const uint8_t *w,
 /* MX output quantiser ([GD] Step 3):                                       */
 /*   SFD = norm_const * max_{k in block} |D| * rcp_max                      */
 /*   D_q = D * norm_const / SFD                                             */
-/* with rcp_max = 1/448 for E4M3 and blocks of 32 consecutive elements.     */
+/* with rcp_max = 1/448 for E4M3 (1/57344 for E5M2) and blocks of 32       */
+/* consecutive elements.                                                    */
 /* SFD is stored as E8M0: the smallest power of two >= the computed value   */
 /* (so |D_q| <= 448 needs no clipping); codes are E4M3 by round to nearest  */
 /* even, saturating.  The decisions are taken in binary32, in this order:   */
@@ -629,12 +657,12 @@ int orc_proj_rope_mx(const uint8_t *x, const uint8_t *x_scale, const uint8_t *w,
 /*   inv   = min(norm_const * 2^(127 - byte), FLT_MAX)  (power-of-two step) */
 /*   code  = e4m3_rne_sat(fp32(v * inv))                                    */
 /* ------------------------------------------------------------------------ */
-static void quant_block(const double *d, int64_t cnt, int64_t stride, float norm_const,
+static void quant_block(const double *d, int64_t cnt, int64_t stride, float norm_const, int fmt,
                         uint8_t *codes, int64_t cstride, uint8_t *scale)
 {
     float amax = 0.0f, sigma, inv;
     uint32_t byte;
-    const float rcp_max = 1.0f / 448.0f;
+    const float rcp_max = fmt == 2 ? 1.0f / 57344.0f : 1.0f / 448.0f;
     for (int64_t i = 0; i < cnt; ++i) {
         float v = fabsf((float)d[i * stride]);
         if (v > amax) amax = v;
@@ -646,22 +674,23 @@ static void quant_block(const double *d, int64_t cnt, int64_t stride, float norm
     for (int64_t i = 0; i < cnt; ++i) {
         float v = (float)d[i * stride];
         float y = v * inv;
-        codes[i * cstride] = (uint8_t)orc_enc_e4m3((double)y);
+        codes[i * cstride] = (uint8_t)(fmt == 2 ? orc_enc_e5m2((double)y) : orc_enc_e4m3((double)y));
     }
     *scale = (uint8_t)byte;
 }
 
 /* Row direction: blocks of 32 along each row.  d is (rows, cols) with
  * leading dimension ld; codes (rows, cols); scales (rows, ceil(cols/32)). */
+/* fmt 0: E4M3 codes; fmt 2: E5M2 codes. */
 void orc_mx_quant_rows(const double *d, int64_t rows, int64_t cols, int64_t ld,
-                       float norm_const, uint8_t *codes, uint8_t *scales)
+                       float norm_const, int fmt, uint8_t *codes, uint8_t *scales)
 {
     int64_t nb = (cols + 31) / 32;
     #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t b = 0; b < nb; ++b) {
             int64_t c0 = b * 32, cnt = cols - c0 < 32 ? cols - c0 : 32;
-            quant_block(d + r * ld + c0, cnt, 1, norm_const, codes + r * cols + c0, 1,
+            quant_block(d + r * ld + c0, cnt, 1, norm_const, fmt, codes + r * cols + c0, 1,
                         scales + r * nb + b);
         }
 }
@@ -669,14 +698,14 @@ void orc_mx_quant_rows(const double *d, int64_t rows, int64_t cols, int64_t ld,
 /* Column direction: blocks of 32 consecutive rows in each column.
  * codes (rows, cols); scales (ceil(rows/32), cols). */
 void orc_mx_quant_cols(const double *d, int64_t rows, int64_t cols, int64_t ld,
-                       float norm_const, uint8_t *codes, uint8_t *scales)
+                       float norm_const, int fmt, uint8_t *codes, uint8_t *scales)
 {
     int64_t nb = (rows + 31) / 32;
     #pragma omp parallel for schedule(static)
     for (int64_t c = 0; c < cols; ++c)
         for (int64_t b = 0; b < nb; ++b) {
             int64_t r0 = b * 32, cnt = rows - r0 < 32 ? rows - r0 : 32;
-            quant_block(d + r0 * ld + c, cnt, ld, norm_const, codes + r0 * cols + c, cols,
+            quant_block(d + r0 * ld + c, cnt, ld, norm_const, fmt, codes + r0 * cols + c, cols,
                         scales + b * cols + c);
         }
 }

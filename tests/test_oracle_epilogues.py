@@ -181,3 +181,29 @@ def test_quantiser_columns_equal_rows_of_transpose():
     cc, cs = O.mx_quant_cols(d)
     rc, rs = O.mx_quant_rows(np.ascontiguousarray(d.T))
     assert np.array_equal(cc, rc.T) and np.array_equal(cs, rs.T)
+
+
+def test_quantiser_e5m2_power_of_two_closed_forms():
+    # E5M2 codes: block max exactly 57344 * 2^j -> scale byte 127 + j, that
+    # element encodes to the top finite code 0x7B, the rest to RNE(D / 2^j).
+    rng = np.random.default_rng(15)
+    for j in (-30, -2, 0, 3, 20):
+        blk = rng.uniform(-1, 1, 32) * 57344 * 2.0 ** j
+        blk[11] = 57344 * 2.0 ** j
+        codes, scales = O.mx_quant_rows(blk[None, :], fmt="e5m2")
+        assert scales[0, 0] == 127 + j
+        assert codes[0, 11] == 0x7B
+        for i in range(32):
+            v = float(np.float32(blk[i])) / 2.0 ** j
+            assert codes[0, i] == O.enc_e5m2(v)
+    # the same block quantised as E4M3 uses a scale 7 binades larger (448 = 1.75 * 2^8
+    # against 57344 = 1.75 * 2^15)
+    blk = rng.standard_normal(32) * 10.0
+    _, s4 = O.mx_quant_rows(blk[None, :])
+    _, s5 = O.mx_quant_rows(blk[None, :], fmt="e5m2")
+    assert int(s4[0, 0]) - int(s5[0, 0]) == 7
+    # columns agree with rows of the transpose in E5M2 too
+    d = rng.standard_normal((64, 40))
+    cr, sr = O.mx_quant_cols(d, fmt="e5m2")
+    ct, st = O.mx_quant_rows(np.ascontiguousarray(d.T), fmt="e5m2")
+    assert np.array_equal(cr, ct.T) and np.array_equal(sr, st.T)

@@ -177,3 +177,40 @@ def test_sf_offset_bijective_and_row_words_contiguous():
                 w = offs[4 * kt:4 * kt + 4]
                 assert w == list(range(w[0], w[0] + 4)) and w[0] % 4 == 0
     assert seen == set(range(l * 2 * 2 * 512))
+
+
+def test_e5m2_encode_roundtrip_every_finite_code():
+    for c in range(256):
+        v = O.dec_e5m2(c)
+        if math.isnan(v) or math.isinf(v):
+            continue
+        assert O.enc_e5m2(v) == c, hex(c)
+
+
+def test_e5m2_encode_rne_matches_torch_in_range():
+    # In range (|x| <= 57344) torch's float32 -> float8_e5m2 conversion rounds
+    # to nearest even, so the oracle must agree with it exactly.
+    g = torch.Generator().manual_seed(2)
+    x = torch.cat([torch.randn(20000, generator=g) * s for s in (1e-5, 1e-2, 1, 300, 9000)])
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e5m2).float()
+    finite = codes[torch.isfinite(codes)].unique()
+    mids = ((finite[1:] + finite[:-1]) / 2).double()
+    x = torch.cat([x.double(), mids, -mids]).clamp(-57344.0, 57344.0)
+    ref = x.float().to(torch.float8_e5m2).view(torch.uint8)
+    for v, r in zip(x.tolist(), ref.tolist()):
+        got = O.enc_e5m2(v)
+        if r in (0x00, 0x80) and got in (0x00, 0x80):
+            continue
+        assert got == r, (v, hex(got), hex(r))
+
+
+def test_e5m2_encode_ties_saturation_and_subnormals():
+    # 1.0 = 0x3C, next 1.25 = 0x3D; midpoint 1.125 ties to the even mantissa (0x3C),
+    # midpoint 1.375 rounds up to 1.5 (0x3E).
+    assert O.enc_e5m2(1.125) == 0x3C and O.enc_e5m2(1.375) == 0x3E
+    # the largest finite value 57344 = 0x7B; anything larger saturates to it, never Inf
+    assert O.enc_e5m2(57344.0) == 0x7B and O.enc_e5m2(61440.0) == 0x7B
+    assert O.enc_e5m2(1e30) == 0x7B and O.enc_e5m2(-1e30) == 0xFB
+    # smallest subnormal 2^-16; half of it ties to zero (even), 3/2 of it to 2^-15
+    assert O.enc_e5m2(2.0 ** -16) == 0x01 and O.enc_e5m2(2.0 ** -17) == 0x00
+    assert O.enc_e5m2(3 * 2.0 ** -17) == 0x02
