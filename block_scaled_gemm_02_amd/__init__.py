@@ -118,6 +118,16 @@ def _ab_code(fmt) -> int:
     return {"e4m3": E4M3, "e5m2": E5M2, "e2m1": E2M1X2, E4M3: E4M3, E2M1X2: E2M1X2, E5M2: E5M2}[fmt]
 
 
+def _d_code(d_dtype, d) -> int:
+    """D dtype code: "e4m3" / "e5m2" (MX-quantised D), else a torch float dtype
+    (taken from the tensor d when d_dtype is None)."""
+    if d_dtype in ("e4m3", E4M3):
+        return E4M3
+    if d_dtype in ("e5m2", E5M2):
+        return E5M2
+    return dtype_code(d_dtype if d_dtype is not None else d)
+
+
 # ---------------------------------------------------------------------------
 def gemm_amax(a, b, sfa, sfb, c, amax, m, n, k, l, ab_dtype="e4m3", c_dtype=None,
               sf_vec_size=32, stream=None, validate_only=False):
@@ -149,12 +159,9 @@ def grouped_gemm_srelu(a, b, sfa, sfb, padded_offsets, alpha, prob, norm_const, 
                        stream=None, validate_only=False):
     """Grouped block-scaled GEMM + prob-gated squared ReLU (see include/bsg.h).
 
-    d_dtype: a torch float dtype, or "e4m3" for MXFP8 output with SFD_row/col."""
+    d_dtype: a torch float dtype, or "e4m3" / "e5m2" for MXFP8 output with SFD_row/col."""
     cd = dtype_code(c_dtype if c_dtype is not None else (c if c is not None else torch.bfloat16))
-    if d_dtype in ("e4m3", E4M3):
-        dd = E4M3
-    else:
-        dd = dtype_code(d_dtype if d_dtype is not None else d)
+    dd = _d_code(d_dtype, d)
     s = float(tanh_clamp_scale) if tanh_clamp_scale is not None else 0.0
     args = [_ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), _ptr(padded_offsets), _ptr(alpha),
             _ptr(prob), _ptr(norm_const), _ptr(c), _ptr(d), _ptr(d_col), _ptr(sfd_row),
@@ -194,10 +201,7 @@ def grouped_gemm_srelu_discrete(a, b_ptrs, sfa, sfb_ptrs, padded_offsets, alpha,
     """grouped_gemm_srelu with per-expert weight and scale allocations:
     b_ptrs / sfb_ptrs are (L,) int64 device tensors (see include/bsg.h)."""
     cd = dtype_code(c_dtype if c_dtype is not None else (c if c is not None else torch.bfloat16))
-    if d_dtype in ("e4m3", E4M3):
-        dd = E4M3
-    else:
-        dd = dtype_code(d_dtype if d_dtype is not None else d)
+    dd = _d_code(d_dtype, d)
     s = float(tanh_clamp_scale) if tanh_clamp_scale is not None else 0.0
     args = [_ptr(a), _ptr(b_ptrs), _ptr(sfa), _ptr(sfb_ptrs), _ptr(padded_offsets), _ptr(alpha),
             _ptr(prob), _ptr(norm_const), _ptr(c), _ptr(d), _ptr(d_col), _ptr(sfd_row),
@@ -215,7 +219,7 @@ def grouped_gemm_dswiglu(a, b, sfa, sfb, c, padded_offsets, alpha, beta, prob, n
     inputs, bf16/fp32 D with amax (L, 2) for FP4 inputs.  dprob is accumulated:
     zero-fill it first."""
     cd = BF16 if c_dtype is None else (_TORCH_DT[c_dtype] if c_dtype in _TORCH_DT else c_dtype)
-    dd = E4M3 if d_dtype in ("e4m3", E4M3) else (_TORCH_DT[d_dtype] if d_dtype in _TORCH_DT else d_dtype)
+    dd = _d_code(d_dtype, d_row)
     args = [_ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), _ptr(c), _ptr(padded_offsets), _ptr(alpha), _ptr(beta),
             _ptr(prob), _ptr(norm_const), _ptr(d_row), _ptr(d_col), _ptr(sfd_row), _ptr(sfd_col), _ptr(dprob),
             _ptr(amax), m, n, k, num_experts, _ab_code(ab_dtype), cd, dd, sf_vec_size]

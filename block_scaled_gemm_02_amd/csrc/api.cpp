@@ -274,9 +274,9 @@ static int validate_srelu(const void *a, const void *b, const uint8_t *sfa, cons
     if (n % 32) return fail(BSG_ERR_SHAPE, "N=%lld must be a multiple of 32", (long long)n);
     if (!(tanh_clamp_scale == tanh_clamp_scale)) return fail(BSG_ERR_SHAPE, "tanh_clamp_scale is NaN");
     if (c && !is_float_out(c_dtype)) return fail(BSG_ERR_DTYPE, "C dtype must be F32, F16 or BF16");
-    const bool fp8_out = d_dtype == BSG_E4M3;
+    const bool fp8_out = d_dtype == BSG_E4M3 || d_dtype == BSG_E5M2;
     if (!fp8_out && !is_float_out(d_dtype)) {
-        if (d_dtype == BSG_E5M2 || d_dtype == BSG_E2M1X2)
+        if (d_dtype == BSG_E2M1X2)
             return fail(BSG_ERR_UNSUPPORTED, "D dtype %d is not built", d_dtype);
         return fail(BSG_ERR_DTYPE, "D dtype %d invalid", d_dtype);
     }
@@ -319,7 +319,7 @@ static int run_srelu(const void *a, const void *b, const uint64_t *b_ptrs, const
     args.sfa = sfa; args.sfb = sfb; args.offsets = padded_offsets; args.alpha = alpha;
     args.prob = prob; args.norm_const = norm_const; args.c = c; args.d = d; args.d_col = d_col;
     args.sfd_row = sfd_row; args.sfd_col = sfd_col;
-    args.amax = d_dtype == BSG_E4M3 ? nullptr : amax;
+    args.amax = (d_dtype == BSG_E4M3 || d_dtype == BSG_E5M2) ? nullptr : amax;
     args.m = m; args.n = n; args.k = k; args.num_experts = num_experts;
     args.fmt = fmt_of(ab_dtype); args.c_dtype = c_dtype; args.d_dtype = d_dtype;
     args.tanh_s = tanh_clamp_scale > 0.0f ? tanh_clamp_scale : 0.0f;
@@ -406,9 +406,8 @@ int bsg_validate_grouped_gemm_dswiglu(const void *a, const void *b, const uint8_
     if (fp4) {
         // FP4 inputs: bf16 / fp32 D (d_col an optional copy), per-expert amax (L, 2) nullable
         if (d_dtype != BSG_BF16 && d_dtype != BSG_F32) return fail(BSG_ERR_DTYPE, "FP4 inputs take a bf16 or fp32 D");
-    } else if (d_dtype != BSG_E4M3) {
-        if (d_dtype == BSG_E5M2) return fail(BSG_ERR_UNSUPPORTED, "D dtype E5M2 is not built (E4M3 is)");
-        return fail(BSG_ERR_DTYPE, "FP8 inputs take an FP8 D");
+    } else if (d_dtype != BSG_E4M3 && d_dtype != BSG_E5M2) {
+        return fail(BSG_ERR_DTYPE, "FP8 inputs take an FP8 (E4M3 or E5M2) D");
     }
     if (!beta) return fail(BSG_ERR_NULLPTR, "beta is required");
     if (!dprob) return fail(BSG_ERR_NULLPTR, "dprob is required");

@@ -88,10 +88,25 @@ __device__ __forceinline__ uint32_t pack2_e4m3(float a, float b)
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
-// Four E4M3 codes, x0 in the lowest byte.
+// Two floats -> two E5M2 codes (round to nearest even), clamped to the
+// largest finite value +-57344 first so that nothing becomes Inf.
+__device__ __forceinline__ uint32_t pack2_e5m2(float a, float b)
+{
+    a = fminf(fmaxf(a, -57344.0f), 57344.0f);
+    b = fminf(fmaxf(b, -57344.0f), 57344.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// Four E4M3 (E5 = false) or E5M2 (E5 = true) codes, x0 in the lowest byte.
+template <bool E5 = false>
+__device__ __forceinline__ uint32_t pack4_fp8(float x0, float x1, float x2, float x3)
+{
+    if constexpr (E5) return pack2_e5m2(x0, x1) | (pack2_e5m2(x2, x3) << 16);
+    else return pack2_e4m3(x0, x1) | (pack2_e4m3(x2, x3) << 16);
+}
 __device__ __forceinline__ uint32_t pack4_e4m3(float x0, float x1, float x2, float x3)
 {
-    return pack2_e4m3(x0, x1) | (pack2_e4m3(x2, x3) << 16);
+    return pack4_fp8<false>(x0, x1, x2, x3);
 }
 
 // E8M0 byte of the smallest power of two >= sigma (sigma >= 0), clamped to
@@ -657,7 +672,7 @@ __device__ __forceinline__ int acc_col(int wn, int j, int q, int lane)
     return 32 * NB * wn + 32 * j + 8 * q + 4 * (lane >> 5);
 }
 
-enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_E4M3 = 3 };
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_E4M3 = 3, DT_E5M2 = 4 };
 
 // Max over the 32 lanes of each half-wave (lanes 0-31 and 32-63 separately)
 // of each of N non-negative values: quad and row DPP steps reduce 16 lanes, a
@@ -834,11 +849,13 @@ __device__ __forceinline__ void store_quadrant2(uint8_t *reg, char *dst_c, char 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
 // The MX output quantiser's scale step for a block with max |D| = amax:
-// SF = smallest power of two >= norm_const * amax / 448 (E8M0 byte), and
-// the factor norm_const / SF that maps the block into E4M3 range.
+// SF = smallest power of two >= norm_const * amax / fmax (E8M0 byte), with
+// fmax = 448 for E4M3 codes and 57344 for E5M2 (E5 = true), and the factor
+// norm_const / SF that maps the block into the code format's range.
+template <bool E5 = false>
 __device__ __forceinline__ uint32_t mx_scale_byte(float amax, float norm_const, float &inv)
 {
-    const float sigma = (norm_const * amax) * (1.0f / 448.0f);
+    const float sigma = (norm_const * amax) * (E5 ? 1.0f / 57344.0f : 1.0f / 448.0f);
     const uint32_t byte = e8m0_ceil(sigma);
     inv = fminf(ldexpf(norm_const, 127 - (int)byte), 3.402823466e38f);
     return byte;
@@ -858,6 +875,7 @@ __device__ __forceinline__ float lane_select(uint64_t mask, float x0, float x1)
 // after half_wave_max).  Lane c of each half-wave computes the E8M0 scale of
 // register c % 16 only, and every lane then gathers the 16 factors it needs
 // from lanes 32g + v.  Returns this lane's byte: the scale of register c % 16.
+template <bool E5 = false>
 __device__ __forceinline__ uint32_t col_scales(const float (&cm)[16], float nc, float (&cinv)[16], int lane)
 {
     // m = cm[lane % 16]: a tree of selects on the bits of the lane index,
@@ -873,7 +891,7 @@ __device__ __forceinline__ uint32_t col_scales(const float (&cm)[16], float nc, 
     for (int k = 0; k < 2; ++k) t2[k] = lane_select(0xF0F0F0F0F0F0F0F0ull, t4[2 * k], t4[2 * k + 1]);
     const float m = lane_select(0xFF00FF00FF00FF00ull, t2[0], t2[1]);
     float inv;
-    const uint32_t byte = mx_scale_byte(m, nc, inv);
+    const uint32_t byte = mx_scale_byte<E5>(m, nc, inv);
     const int base = lane & 32;
 #pragma unroll
     for (int v = 0; v < 16; ++v) cinv[v] = __shfl(inv, base + v);

@@ -295,7 +295,8 @@ __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, f32x16 
 // MXFP8 output: D quantised in 32-wide blocks along N (codes to d, scales to
 // the SFD_row atoms over (M, N)) and in 32-tall blocks along M (codes to
 // d_col, scales to the SFD_col atoms over (N, M)), with the quantiser of
-// "Grouped GEMM + dSwiGLU (SM100)", Step 3 (rcp_max = 1/448).
+// "Grouped GEMM + dSwiGLU (SM100)", Step 3 (rcp_max = 1/448; E5 selects
+// E5M2 codes with rcp_max = 1/57344).
 //
 // A row's 32 values of block j sit in this lane (16) and lane ^ 32 (16); a
 // column's 32 values of block i sit in one register of the 32 lanes of a
@@ -304,7 +305,7 @@ __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, f32x16 
 // staged in the wave's LDS region and stored as whole rows, and the scale
 // bytes are written: SFD_row as one word per row (the wave's four 32-column
 // blocks are one K' group), SFD_col byte by byte.
-template <bool CLAMP>
+template <bool CLAMP, bool E5>
 __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x16 (&acc)[4][4],
                                                    uint8_t *stage, int64_t m0, int64_t n0, float alpha,
                                                    int wm, int wn, int lane, const float *prob_lds)
@@ -345,19 +346,19 @@ __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x1
             for (int v = 0; v < 16; ++v) rm = fmaxf(rm, fabsf(d[v]));
             rm = fmaxf(rm, xor32(rm));
             float rinv;
-            rword |= mx_scale_byte(rm, nc, rinv) << (8 * j);
+            rword |= mx_scale_byte<E5>(rm, nc, rinv) << (8 * j);
             // column blocks: 32 rows of each column over the half-wave
             float cinv[16], cm[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v) cm[v] = fabsf(d[v]);
             half_wave_max(cm);
-            const uint32_t byte = col_scales(cm, nc, cinv, lane);
+            const uint32_t byte = col_scales<E5>(cm, nc, cinv, lane);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 *reinterpret_cast<uint32_t *>(wd + 32 * j + 8 * q) =
-                    pack4_e4m3(d[4 * q] * rinv, d[4 * q + 1] * rinv, d[4 * q + 2] * rinv, d[4 * q + 3] * rinv);
+                    pack4_fp8<E5>(d[4 * q] * rinv, d[4 * q + 1] * rinv, d[4 * q + 2] * rinv, d[4 * q + 3] * rinv);
                 *reinterpret_cast<uint32_t *>(wdc + 32 * j + 8 * q) =
-                    pack4_e4m3(d[4 * q] * cinv[4 * q], d[4 * q + 1] * cinv[4 * q + 1],
+                    pack4_fp8<E5>(d[4 * q] * cinv[4 * q], d[4 * q + 1] * cinv[4 * q + 1],
                                d[4 * q + 2] * cinv[4 * q + 2], d[4 * q + 3] * cinv[4 * q + 3]);
             }
             // SFD_col byte i of column 32j + 8(c/4) + 4g + c%4 (lane c < 16: register c)
@@ -389,13 +390,14 @@ __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x1
 // The wave's 128 ref columns become 256 D columns (8 blocks of 32: ab of ref
 // block j is D block 2j, dswiglu 2j+1), quantised along D (SFD_row atoms over
 // (M, 2N)) and along M (SFD_col atoms over (2N, M)) as in the sReLU MXFP8
-// epilogue.  A lane's four C values of register group q are consecutive,
-// one 8-byte load each for input and gate.
+// epilogue (E5: E5M2 codes).  A lane's four C values of register group q
+// are consecutive, one 8-byte load each for input and gate.
 __device__ __forceinline__ float bf16_at(uint2 w, int u)
 {
     const uint32_t x = (u < 2) ? w.x : w.y;
     return __uint_as_float((u & 1) ? (x & 0xFFFF0000u) : (x << 16));
 }
+template <bool E5>
 __device__ __forceinline__ void epilogue_dswiglu_fp8(const GroupedParams &p, f32x16 (&acc)[4][4], uint8_t *stage,
                                                      int64_t m0, int64_t n0, float alpha2, float beta, int wm,
                                                      int wn, int lane, const float *prob_lds)
@@ -439,19 +441,19 @@ __device__ __forceinline__ void epilogue_dswiglu_fp8(const GroupedParams &p, f32
             for (int v = 0; v < 16; ++v) rm = fmaxf(rm, fabsf(dv[v]));
             rm = fmaxf(rm, xor32(rm));
             float rinv;
-            rword[blk >> 2] |= mx_scale_byte(rm, nc, rinv) << (8 * (blk & 3));
+            rword[blk >> 2] |= mx_scale_byte<E5>(rm, nc, rinv) << (8 * (blk & 3));
             // column direction: 32 rows of one D column over the half-wave
             float cinv[16], cm[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v) cm[v] = fabsf(dv[v]);
             half_wave_max(cm);
-            const uint32_t byte = col_scales(cm, nc, cinv, lane);
+            const uint32_t byte = col_scales<E5>(cm, nc, cinv, lane);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 *reinterpret_cast<uint32_t *>(wd + 32 * blk + 8 * q) =
-                    pack4_e4m3(dv[4 * q] * rinv, dv[4 * q + 1] * rinv, dv[4 * q + 2] * rinv, dv[4 * q + 3] * rinv);
+                    pack4_fp8<E5>(dv[4 * q] * rinv, dv[4 * q + 1] * rinv, dv[4 * q + 2] * rinv, dv[4 * q + 3] * rinv);
                 *reinterpret_cast<uint32_t *>(wdc + 32 * blk + 8 * q) =
-                    pack4_e4m3(dv[4 * q] * cinv[4 * q], dv[4 * q + 1] * cinv[4 * q + 1],
+                    pack4_fp8<E5>(dv[4 * q] * cinv[4 * q], dv[4 * q + 1] * cinv[4 * q + 1],
                                dv[4 * q + 2] * cinv[4 * q + 2], dv[4 * q + 3] * cinv[4 * q + 3]);
             }
             // SFD_col byte i of D column dq + 32 blk + 8(c/4) + 4g + c%4 (lane c < 16: register c)
@@ -624,10 +626,10 @@ __global__ void __launch_bounds__(256) k_grouped(GroupedParams p)
     mainloop_pipe<F>(acc, ring, A, B, p.k);
 
     if constexpr (EPI == EPI_SRELU_FP8) {
-        epilogue_srelu_fp8<CLAMP>(p, acc, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), m0, n0, alpha,
+        epilogue_srelu_fp8<CLAMP, OT == DT_E5M2>(p, acc, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), m0, n0, alpha,
                                   wm, wn, lane, prob_lds);
     } else if constexpr (EPI == EPI_DSWIGLU_FP8) {
-        epilogue_dswiglu_fp8(p, acc, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), m0, n0, alpha * alpha,
+        epilogue_dswiglu_fp8<OT == DT_E5M2>(p, acc, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), m0, n0, alpha * alpha,
                              p.beta[g], wm, wn, lane, prob_lds);
     } else if constexpr (EPI == EPI_DSWIGLU) {
         epilogue_dswiglu<OT>(p, acc, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), m0, n0, g, alpha * alpha,
@@ -674,7 +676,7 @@ hipError_t launch_grouped_gemm(const GroupedArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int F, int EPI>
+template <int F, int EPI, int OT = -1>
 static void launch_srelu_variant(const GroupedParams &p, dim3 grid, hipStream_t s)
 {
     // C and D both bf16: a kernel whose epilogue has one compile-time store
@@ -687,8 +689,8 @@ static void launch_srelu_variant(const GroupedParams &p, dim3 grid, hipStream_t 
             return;
         }
     }
-    if (p.tanh_s > 0.0f) hipLaunchKernelGGL((k_grouped<F, EPI, true>), grid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((k_grouped<F, EPI, false>), grid, dim3(kThreads), 0, s, p);
+    if (p.tanh_s > 0.0f) hipLaunchKernelGGL((k_grouped<F, EPI, true, OT>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((k_grouped<F, EPI, false, OT>), grid, dim3(kThreads), 0, s, p);
 }
 
 hipError_t launch_grouped_srelu(const GroupedArgs &a, hipStream_t s)
@@ -701,6 +703,10 @@ hipError_t launch_grouped_srelu(const GroupedArgs &a, hipStream_t s)
     if (a.d_dtype == DT_E4M3) {
         if (a.fmt == FMT_E4M3) launch_srelu_variant<FMT_E4M3, EPI_SRELU_FP8>(p, grid, s);
         else if (a.fmt == FMT_E5M2) launch_srelu_variant<FMT_E5M2, EPI_SRELU_FP8>(p, grid, s);
+        else return hipErrorNotSupported;
+    } else if (a.d_dtype == DT_E5M2) {
+        if (a.fmt == FMT_E4M3) launch_srelu_variant<FMT_E4M3, EPI_SRELU_FP8, DT_E5M2>(p, grid, s);
+        else if (a.fmt == FMT_E5M2) launch_srelu_variant<FMT_E5M2, EPI_SRELU_FP8, DT_E5M2>(p, grid, s);
         else return hipErrorNotSupported;
     } else if (a.fmt == FMT_E4M3) {
         launch_srelu_variant<FMT_E4M3, EPI_SRELU>(p, grid, s);
@@ -730,9 +736,11 @@ hipError_t launch_grouped_dswiglu(const GroupedArgs &a, hipStream_t s)
         if (a.d_dtype == DT_F32) hipLaunchKernelGGL((k_grouped<FMT_E2M1, EPI_DSWIGLU, false, DT_F32>), grid, dim3(kThreads), 0, s, p);
         else hipLaunchKernelGGL((k_grouped<FMT_E2M1, EPI_DSWIGLU, false, DT_BF16>), grid, dim3(kThreads), 0, s, p);
     } else if (a.fmt == FMT_E4M3) {
-        hipLaunchKernelGGL((k_grouped<FMT_E4M3, EPI_DSWIGLU_FP8, false>), grid, dim3(kThreads), 0, s, p);
+        if (a.d_dtype == DT_E5M2) hipLaunchKernelGGL((k_grouped<FMT_E4M3, EPI_DSWIGLU_FP8, false, DT_E5M2>), grid, dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_grouped<FMT_E4M3, EPI_DSWIGLU_FP8, false>), grid, dim3(kThreads), 0, s, p);
     } else if (a.fmt == FMT_E5M2) {
-        hipLaunchKernelGGL((k_grouped<FMT_E5M2, EPI_DSWIGLU_FP8, false>), grid, dim3(kThreads), 0, s, p);
+        if (a.d_dtype == DT_E5M2) hipLaunchKernelGGL((k_grouped<FMT_E5M2, EPI_DSWIGLU_FP8, false, DT_E5M2>), grid, dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_grouped<FMT_E5M2, EPI_DSWIGLU_FP8, false>), grid, dim3(kThreads), 0, s, p);
     } else {
         return hipErrorNotSupported;
     }

@@ -139,15 +139,15 @@ int grouped_gemm(const void *a, const void *b, const int32_t *padded_offsets,
  *      amax   (L,) fp32, nullable: amax[g] = max |D| over expert g's rows
  *             (fp32 values before the cast); zero-filled by the library;
  *             an expert with no rows reports 0
- *  d_dtype == E4M3 (MXFP8 output, "Grouped GEMM + dSwiGLU (SM100)" Step 3
- *  quantiser with rcp_max = 1/448):
- *      d        (M,N) E4M3 codes quantised in 32-wide blocks along N
+ *  d_dtype == E4M3 or E5M2 (MXFP8 output, "Grouped GEMM + dSwiGLU (SM100)"
+ *  Step 3 quantiser with rcp_max = 1/448 for E4M3 codes, 1/57344 for E5M2):
+ *      d        (M,N) FP8 codes quantised in 32-wide blocks along N
  *      sfd_row  scale atoms over (M, N, 1)  (MN = M, "K" = N)
- *      d_col    (M,N) E4M3 codes quantised in 32-tall blocks along M
+ *      d_col    (M,N) FP8 codes quantised in 32-tall blocks along M
  *      sfd_col  scale atoms over (N, M, 1)  (MN = N, "K" = M)
  *      norm_const (1,) fp32 device scalar, required
  *  tanh_clamp_scale: s; a value <= 0 means no clamp (the pages' None).
- *  ab_dtype in {E4M3, E5M2, E2M1X2}; sf_vec_size == 32.  E4M3 D needs FP8
+ *  ab_dtype in {E4M3, E5M2, E2M1X2}; sf_vec_size == 32.  FP8 D needs FP8
  *  (E4M3 or E5M2) A/B.
  *  Sizes: M % 256 == 0, 1 <= L <= 1024, K % 32 == 0, N % 32 == 0.
  *  Rows at or past padded_offsets[L-1] are not written.
@@ -204,14 +204,14 @@ int grouped_gemm_srelu_discrete(const void *a, const uint64_t *b_ptrs, const uin
  *                           * (1 + gate * (1 - sigmoid(gate)))         (dswiglu)
  *     dprob[m] += sum_n swish * input * ref
  * evaluated in fp32 from the accumulator.  With FP8 (E4M3 / E5M2) A/B, D is
- * MXFP8-quantised like the FP8 D of grouped_gemm_srelu (Step 3, rcp_max =
- * 1/448):
+ * MXFP8-quantised like the FP8 D of grouped_gemm_srelu (Step 3; d_dtype E4M3
+ * with rcp_max = 1/448, or E5M2 with rcp_max = 1/57344):
  *  a, sfa, b, sfb, padded_offsets, alpha, prob   as for grouped_gemm_srelu
  *  c        (M, 2N) bf16, n-major: the forward input/gate tensor
  *  beta     (L,) fp32
- *  d_row    (M, 2N) E4M3 codes in 32-wide blocks along 2N; sfd_row: scale
+ *  d_row    (M, 2N) FP8 codes in 32-wide blocks along 2N; sfd_row: scale
  *           atoms over (M, 2N, 1)
- *  d_col    (M, 2N) E4M3 codes in 32-tall blocks along M; sfd_col: scale
+ *  d_col    (M, 2N) FP8 codes in 32-tall blocks along M; sfd_col: scale
  *           atoms over (2N, M, 1)
  *  norm_const (1,) fp32 device scalar
  *  dprob    (M,) fp32, accumulated with atomic adds: the caller zero-fills
@@ -221,7 +221,7 @@ int grouped_gemm_srelu_discrete(const void *a, const uint64_t *b_ptrs, const uin
  *  amax     (L, 2) fp32, nullable: amax[g][0] = max |ab|, amax[g][1] =
  *           max |dswiglu| over expert g's rows (fp32 values before the
  *           cast); zero-filled by the library; norm_const and sfd_* unused
- *  c_dtype BF16.  E5M2 D and other C dtypes return UNSUPPORTED.
+ *  c_dtype BF16; other C dtypes return UNSUPPORTED.
  *  Sizes: M % 256 == 0, 1 <= L <= 1024, K % 32 == 0, N % 32 == 0.  Rows at
  *  or past padded_offsets[L-1] are not written.
  */

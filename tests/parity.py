@@ -3,7 +3,7 @@
 Tolerances come from the stated targets: fp32 outputs within relative
 1e-3, bf16/fp16 outputs within one step of the correctly rounded oracle
 value, amax within relative 1e-5, quantised outputs with identical E8M0
-scales and E4M3 codes within one code step on at most 0.1% of elements.
+scales and FP8 (E4M3 or E5M2) codes within one code step on at most 0.1% of elements.
 
 Cancellation escape: where a sum nearly cancels, a relative test on the
 result is meaningless.  An element that misses the relative rule passes if
@@ -130,16 +130,22 @@ def check_quant(gpu_codes: np.ndarray, gpu_scales: np.ndarray, o_codes: np.ndarr
     return dict(flips=flips, escapes=n_esc, n=int(d.size))
 
 
-def code_window(d_o: np.ndarray, bound: np.ndarray, scales: np.ndarray, axis: int, norm_const=1.0):
-    """Ordered E4M3 codes of d_o - bound and d_o + bound under the given E8M0
+FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
+_TORCH_FP8 = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+
+
+def code_window(d_o: np.ndarray, bound: np.ndarray, scales: np.ndarray, axis: int, norm_const=1.0,
+                fmt: str = "e4m3"):
+    """Ordered FP8 codes of d_o - bound and d_o + bound under the given E8M0
     block scales (blocks of 32 along `axis`): the codes a value within the
-    error bound can take.  The encode is torch's float8_e4m3fn (RNE) after
-    saturation to +-448."""
+    error bound can take.  The encode is torch's float8_e4m3fn / float8_e5m2
+    (RNE) after saturation to the format's largest finite value."""
     inv = norm_const * 2.0 ** (127.0 - np.repeat(scales.astype(np.float64), 32, axis=axis))
+    fmax = FP8_MAX[fmt]
 
     def enc(v):
-        v = np.clip(v * inv, -448.0, 448.0).astype(np.float32)
-        return e4m3_ordered(torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+        v = np.clip(v * inv, -fmax, fmax).astype(np.float32)
+        return e4m3_ordered(torch.from_numpy(v).to(_TORCH_FP8[fmt]).view(torch.uint8).numpy())
 
     return enc(d_o - bound), enc(d_o + bound)
 
@@ -154,43 +160,48 @@ def ceil_div(a, b):
     return -(-a // b)
 
 
-def near_pow2_boundary(amax: np.ndarray, bound: np.ndarray, norm_const: float = 1.0) -> np.ndarray:
+def near_pow2_boundary(amax: np.ndarray, bound: np.ndarray, norm_const: float = 1.0,
+                       fmax: float = 448.0) -> np.ndarray:
     """True where the E8M0 scale of a block whose true max is `amax` could
     legitimately differ: [amax - bound, amax + bound] straddles a threshold
-    448 * 2^k / norm_const of the quantiser's round-up."""
-    lo = np.maximum(amax - bound, 0.0) * norm_const / 448.0
-    hi = (amax + bound) * norm_const / 448.0
+    fmax * 2^k / norm_const of the quantiser's round-up (fmax = 448 for E4M3
+    codes, 57344 for E5M2)."""
+    lo = np.maximum(amax - bound, 0.0) * norm_const / fmax
+    hi = (amax + bound) * norm_const / fmax
     with np.errstate(divide="ignore"):
         return (np.ceil(np.log2(np.maximum(lo, 1e-300))) != np.ceil(np.log2(np.maximum(hi, 1e-300)))) | (lo == 0)
 
 
 def check_mx_outputs(d_o: np.ndarray, bound: np.ndarray, gpu_row_codes, gpu_row_scales,
-                     gpu_col_codes, gpu_col_scales, norm_const=1.0, what=""):
+                     gpu_col_codes, gpu_col_scales, norm_const=1.0, what="", fmt="e4m3"):
     """Dual-direction MX quantisation of oracle D (rows x cols, rows % 32 == 0)
-    vs the GPU's codes / scales given in logical (row, block) order."""
-    rc, rs = O.mx_quant_rows(d_o, norm_const)
-    cc, cs = O.mx_quant_cols(d_o, norm_const)
+    vs the GPU's codes / scales given in logical (row, block) order; fmt is
+    the code format ("e4m3" or "e5m2").  Sign-magnitude codes of both formats
+    are ordered like their values, so one code step is one integer step."""
+    rc, rs = O.mx_quant_rows(d_o, norm_const, fmt)
+    cc, cs = O.mx_quant_cols(d_o, norm_const, fmt)
+    fmax = FP8_MAX[fmt]
     R, C = d_o.shape
     d32 = d_o.astype(np.float32).astype(np.float64)
     rmax = np.abs(d32).reshape(R, C // 32, 32).max(-1)
     rb = bound.reshape(R, C // 32, 32).max(-1)
     cmax = np.abs(d32).reshape(R // 32, 32, C).max(1)
     cb = bound.reshape(R // 32, 32, C).max(1)
-    r_near = near_pow2_boundary(rmax, rb, norm_const)
-    c_near = near_pow2_boundary(cmax, cb, norm_const)
+    r_near = near_pow2_boundary(rmax, rb, norm_const, fmax)
+    c_near = near_pow2_boundary(cmax, cb, norm_const, fmax)
     out = {}
     # row direction: compare codes where the block's scale agrees
     # codes beyond one step are accepted where the value's error bound spans
     # them (cancellation under the scaled MFMA's per-block truncation)
     same_r = np.repeat(gpu_row_scales == rs, 32, axis=1)
     g_r = np.where(same_r, gpu_row_codes, rc)
-    lo, hi = code_window(d_o, bound, rs, 1, norm_const)
+    lo, hi = code_window(d_o, bound, rs, 1, norm_const, fmt)
     o_r = e4m3_ordered(g_r)
     out["row"] = check_quant(g_r, gpu_row_scales, rc, rs, r_near, what=what + " row",
                              escape=(o_r >= lo - 1) & (o_r <= hi + 1))
     same_c = np.repeat(gpu_col_scales == cs, 32, axis=0)
     g_c = np.where(same_c, gpu_col_codes, cc)
-    lo, hi = code_window(d_o, bound, cs, 0, norm_const)
+    lo, hi = code_window(d_o, bound, cs, 0, norm_const, fmt)
     o_c = e4m3_ordered(g_c)
     out["col"] = check_quant(g_c, gpu_col_scales, cc, cs, c_near, what=what + " col",
                              escape=(o_c >= lo - 1) & (o_c <= hi + 1))

@@ -73,6 +73,9 @@ def test_grouped_srelu_validation():
     assert vs(d_dtype=bsg.E4M3) == NULLPTR               # FP8 D needs norm_const / SFD / D_col
     assert vs(d_dtype=bsg.E4M3, norm_const=P, d_col=P, sfd_row=P, sfd_col=P) == OK
     assert vs(d_dtype=bsg.E4M3, norm_const=P, d_col=P, sfd_row=P, sfd_col=P, ab_dtype="e2m1") == DTYPE
+    assert vs(d_dtype=bsg.E5M2) == NULLPTR
+    assert vs(d_dtype="e5m2", norm_const=P, d_col=P, sfd_row=P, sfd_col=P) == OK
+    assert vs(d_dtype=bsg.E5M2, norm_const=P, d_col=P, sfd_row=P, sfd_col=P, ab_dtype="e2m1") == DTYPE
     assert vs(n=80) == SHAPE                             # N % 32
     assert vs(tanh_clamp_scale=float("nan")) == SHAPE
     assert vs(tanh_clamp_scale=0.0) == OK                # None
@@ -174,7 +177,9 @@ def test_dswiglu_validation():
     assert vdsw(dprob=None) == NULLPTR
     assert vdsw(c=None) == NULLPTR
     assert vdsw(c_dtype=torch.float32) == UNSUP
-    assert vdsw(d_dtype=bsg.E5M2) == UNSUP
+    assert vdsw(d_dtype=bsg.E5M2) == OK                   # E5M2 D codes
+    assert vdsw(d_dtype="e5m2", sfd_col=None) == NULLPTR
+    assert vdsw(ab_dtype="e2m1", d_dtype="e5m2") == DTYPE  # FP4 inputs take bf16 / fp32 D
     assert vdsw(d_dtype=torch.bfloat16) == DTYPE
     assert vdsw(dprob=P + 2) == ALIGN
     assert vdsw(num_experts=0) == SHAPE

@@ -17,7 +17,7 @@ def say(msg):
     print(msg, flush=True)
 
 
-def run_dswiglu(p):
+def run_dswiglu(p, d_fmt="e4m3"):
     s = p.sizes
     t = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in p.t.items()}
     m, n, k, L = s["m"], s["n"], s["k"], s["l"]
@@ -28,7 +28,7 @@ def run_dswiglu(p):
     dprob = torch.zeros(m, device="cuda")
     bsg.grouped_gemm_dswiglu(t["a"], t["b"], t["sfa"], t["sfb"], t["c"], t["offsets"], t["alpha"], t["beta"],
                              t["prob"], t["norm_const"], d, d_col, sfd_row, sfd_col, dprob, m, n, k, L,
-                             s["fmt"])
+                             s["fmt"], d_dtype=d_fmt)
     torch.cuda.synchronize()
     return d, d_col, sfd_row, sfd_col, dprob
 
@@ -71,6 +71,9 @@ CASES = [
     dict(sizes=[256, 0, 512], n=160, k=256, fmt="e4m3"),       # ragged last n-tile (32 columns)
     dict(sizes=[512, 256], n=256, k=384, fmt="e5m2"),
     dict(sizes=[1024, 512, 0, 768, 256], n=512, k=1024, fmt="e4m3"),
+    # E5M2 D codes (rcp_max 1/57344)
+    dict(sizes=[256, 0, 512], n=160, k=256, fmt="e4m3", d="e5m2"),
+    dict(sizes=[512, 256], n=256, k=384, fmt="e5m2", d="e5m2"),
 ]
 
 
@@ -82,14 +85,15 @@ def test_grouped_dswiglu_matches_oracle(case):
     p = W.grouped_dswiglu_problem(0, L, case["n"], case["k"], case["fmt"], seed=6, offsets=off, extra_rows=256)
     s = p.sizes
     m, n, k = s["m"], s["n"], s["k"]
-    d, d_col, sfd_row, sfd_col, dprob = run_dswiglu(p)
+    d_fmt = case.get("d", "e4m3")
+    d, d_col, sfd_row, sfd_col, dprob = run_dswiglu(p, d_fmt)
     valid = s["valid_m"]
     r = O.grouped_dswiglu(p.t["a"], p.t["b"], p.t["sfa"], p.t["sfb"], off, p.t["alpha"], p.t["beta"],
                           p.t["prob"], O.bits16(p.t["c"]), m, n, k, L, case["fmt"], 0, valid)
     bd, b_dp = bounds(p, r, 0, valid)
     rs, cs = gather_scales(sfd_row, sfd_col, 0, valid, m, 2 * n)
     res = check_mx_outputs(r["d"], bd, d[:valid].cpu().numpy(), rs, d_col[:valid].cpu().numpy(), cs, 1.0,
-                           what="D")
+                           what="D", fmt=d_fmt)
     say(f"  {res}")
     g = dprob[:valid].cpu().double().numpy()
     err = np.abs(g - r["dprob"])

@@ -157,7 +157,7 @@ def test_grouped_srelu_full_size_sampled():
 # ---------------------------------------------------------------------------
 # MXFP8 output (d_dtype = E4M3): dual-direction quantisation
 # ---------------------------------------------------------------------------
-def run_srelu_fp8(p, with_c=True):
+def run_srelu_fp8(p, with_c=True, d_fmt="e4m3"):
     s = p.sizes
     t = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in p.t.items()}
     m, n = s["m"], s["n"]
@@ -168,7 +168,7 @@ def run_srelu_fp8(p, with_c=True):
     sfd_col = torch.full((W.sf_atom_bytes(n, m, 1),), 0xEE, dtype=torch.uint8, device="cuda")
     bsg.grouped_gemm_srelu(t["a"], t["b"], t["sfa"], t["sfb"], t["offsets"], t["alpha"], t["prob"],
                            t["norm_const"], c, d, d_col, sfd_row, sfd_col, None, m, n, s["k"], s["l"],
-                           s["fmt"], c_dtype=torch.bfloat16, d_dtype="e4m3",
+                           s["fmt"], c_dtype=torch.bfloat16, d_dtype=d_fmt,
                            tanh_clamp_scale=s["tanh_clamp"])
     torch.cuda.synchronize()
     return c, d, d_col, sfd_row, sfd_col
@@ -188,6 +188,10 @@ FP8_CASES = [
     dict(sizes=[512, 256], n=256, k=512, s=0.0, nc=1.0),
     dict(sizes=[0, 256, 256], n=128, k=256, s=0.5, nc=4.0),
     dict(sizes=[256, 512], n=192, k=256, s=32.0, nc=1.0, fmt="e5m2"),
+    # E5M2 D codes (rcp_max 1/57344)
+    dict(sizes=[256, 0, 512, 256], n=320, k=192, s=32.0, nc=1.0, d="e5m2"),
+    dict(sizes=[0, 256, 256], n=128, k=256, s=0.0, nc=4.0, d="e5m2"),
+    dict(sizes=[512, 256], n=224, k=320, s=0.5, nc=1.0, fmt="e5m2", d="e5m2"),
 ]
 
 
@@ -202,7 +206,8 @@ def test_grouped_srelu_fp8_out_matches_oracle(case):
     p.t["norm_const"] = torch.tensor([case["nc"]])
     s = p.sizes
     m, n, k = s["m"], s["n"], s["k"]
-    c, d, d_col, sfd_row, sfd_col = run_srelu_fp8(p)
+    d_fmt = case.get("d", "e4m3")
+    c, d, d_col, sfd_row, sfd_col = run_srelu_fp8(p, d_fmt=d_fmt)
     r = O.grouped_srelu(p.t["a"], p.t["b"], p.t["sfa"], p.t["sfb"], off, p.t["alpha"], p.t["prob"],
                         m, n, k, L, fmt, s["tanh_clamp"])
     valid = s["valid_m"]
@@ -212,7 +217,7 @@ def test_grouped_srelu_fp8_out_matches_oracle(case):
     bd = d_bound(r["c"], bc, prob, s["tanh_clamp"])[:valid]
     rs, cs = gather_scales(sfd_row, sfd_col, 0, valid, m, n)
     res = check_mx_outputs(r["d"][:valid], bd, d[:valid].cpu().numpy(), rs, d_col[:valid].cpu().numpy(),
-                           cs, case["nc"], what="D")
+                           cs, case["nc"], what="D", fmt=d_fmt)
     say(f"  {res}")
     assert torch.all(d[valid:] == 0xEE) and torch.all(d_col[valid:] == 0xEE)
 
