@@ -38,7 +38,7 @@ def ceil_div(a, b):
 # ---------------------------------------------------------------------------
 # Workloads: each returns (step_fn, info) with inputs resident on the GPU.
 # ---------------------------------------------------------------------------
-def wl_moe_mxfp8_srelu(fp8_out=False, discrete=False, fmt="e4m3"):
+def wl_moe_mxfp8_srelu(fp8_out=False, discrete=False, fmt="e4m3", d_fp8="e4m3"):
     import torch
     import block_scaled_gemm_02_amd as bsg
     import workloads as W
@@ -60,7 +60,7 @@ def wl_moe_mxfp8_srelu(fp8_out=False, discrete=False, fmt="e4m3"):
         sfd_row = torch.empty(W.sf_atom_bytes(m, n, 1), dtype=torch.uint8, device="cuda")
         sfd_col = torch.empty(W.sf_atom_bytes(n, m, 1), dtype=torch.uint8, device="cuda")
         amax = None
-        dd = "e4m3"
+        dd = d_fp8
     else:
         d = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
         d_col = sfd_row = sfd_col = None
@@ -86,15 +86,15 @@ def wl_moe_mxfp8_srelu(fp8_out=False, discrete=False, fmt="e4m3"):
     sf_bytes = t["sfa"].numel() + (sum(x.numel() for x in sfb_list) if discrete else t["sfb"].numel())
     out_bytes = valid_m * n * (2 + (2 if not fp8_out else 2) + 0)
     alg_bytes = ab_bytes + sf_bytes + out_bytes
-    name = ("moe_mxfp8_srelu" if fmt == "e4m3" else "moe_mxfp4_srelu") + ("_fp8d" if fp8_out else "") + \
-        ("_discrete" if discrete else "")
+    name = ("moe_mxfp8_srelu" if fmt == "e4m3" else "moe_mxfp4_srelu") + \
+        (("_fp8d" if d_fp8 == "e4m3" else "_e5m2d") if fp8_out else "") + ("_discrete" if discrete else "")
     info = dict(
         name=name, fmt=fmt, flops=flops, alg_bytes=alg_bytes, kernel="k_grouped",
         config={"workload": ("grouped MXFP8 (E4M3" if fmt == "e4m3" else "grouped MXFP4 (E2M1")
                 + ", E8M0 per 32 K) GEMM + prob-gated sReLU, tanh clamp s=32",
                 "experts": L, "n": n, "k": k, "valid_m": valid_m, "routed_rows": 28672,
                 "routing": "multinomial Zipf(1.1), padded to 256",
-                "outputs": "C bf16, D " + ("E4M3 + SFD_row/SFD_col" if fp8_out else "bf16 + amax(L)"),
+                "outputs": "C bf16, D " + (d_fp8.upper() + " + SFD_row/SFD_col" if fp8_out else "bf16 + amax(L)"),
                 "weights": "per-expert allocations (b_ptrs, sfb_ptrs)" if discrete else "one (N,K,L) tensor"},
         cpu=None if (discrete or fmt != "e4m3") else (lambda: cpu_sample_srelu(p)))
     return step, info
@@ -266,6 +266,7 @@ WORKLOADS = {
     "proj_rope_mxfp8": lambda: wl_proj_rope(True),
     "moe_mxfp8_srelu": lambda: wl_moe_mxfp8_srelu(False),
     "moe_mxfp8_srelu_fp8d": lambda: wl_moe_mxfp8_srelu(True),
+    "moe_mxfp8_srelu_e5m2d": lambda: wl_moe_mxfp8_srelu(True, d_fp8="e5m2"),
     "moe_mxfp8_srelu_discrete": lambda: wl_moe_mxfp8_srelu(False, discrete=True),
     "moe_mxfp4_srelu": lambda: wl_moe_mxfp8_srelu(False, fmt="e2m1"),
     "moe_mxfp8_dswiglu": wl_moe_dswiglu,
