@@ -119,20 +119,25 @@ def _ab_code(fmt) -> int:
 
 
 def _d_code(d_dtype, d) -> int:
-    """D dtype code: "e4m3" / "e5m2" (MX-quantised D), else a torch float dtype
-    (taken from the tensor d when d_dtype is None)."""
-    if d_dtype in ("e4m3", E4M3):
+    """Output dtype code: "e4m3" / "e5m2" (or torch's float8_e4m3fn /
+    float8_e5m2) for FP8 outputs, else a torch float dtype (taken from the
+    tensor d when d_dtype is None)."""
+    x = d_dtype if d_dtype is not None else d
+    if isinstance(x, torch.Tensor):
+        x = x.dtype
+    if x in ("e4m3", E4M3, torch.float8_e4m3fn):
         return E4M3
-    if d_dtype in ("e5m2", E5M2):
+    if x in ("e5m2", E5M2, torch.float8_e5m2):
         return E5M2
-    return dtype_code(d_dtype if d_dtype is not None else d)
+    return dtype_code(x)
 
 
 # ---------------------------------------------------------------------------
 def gemm_amax(a, b, sfa, sfb, c, amax, m, n, k, l, ab_dtype="e4m3", c_dtype=None,
               sf_vec_size=32, stream=None, validate_only=False):
-    """C = sum_k A_hat B_hat per batch and Amax = max |C| (see include/bsg.h)."""
-    cd = dtype_code(c_dtype if c_dtype is not None else c)
+    """C = sum_k A_hat B_hat per batch and Amax = max |C| (see include/bsg.h).
+    c_dtype: a torch float dtype, or "e4m3" / "e5m2" (FP8 C, FP4 operands only)."""
+    cd = _d_code(c_dtype, c)
     args = [_ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), _ptr(c), _ptr(amax), m, n, k, l,
             _ab_code(ab_dtype), cd, sf_vec_size]
     if validate_only:

@@ -129,9 +129,11 @@ int bsg_validate_gemm_amax(const void *a, const void *b, const uint8_t *sfa, con
     if (st) return st;
     if (m < 0 || n < 0 || k < 0 || l < 0) return fail(BSG_ERR_SHAPE, "negative size");
     if (k % 32) return fail(BSG_ERR_SHAPE, "K=%lld must be a multiple of sf_vec_size 32", (long long)k);
-    if (!is_float_out(c_dtype)) {
-        if (c_dtype == BSG_E4M3 || c_dtype == BSG_E5M2 || c_dtype == BSG_E2M1X2)
-            return fail(BSG_ERR_UNSUPPORTED, "low-precision C dtype %d is not built", c_dtype);
+    const bool fp8_c = c_dtype == BSG_E4M3 || c_dtype == BSG_E5M2;
+    if (fp8_c && ab_dtype != BSG_E2M1X2)
+        return fail(BSG_ERR_UNSUPPORTED, "FP8 C with FP8 A/B is disabled (FP8 C takes FP4 A/B)");
+    if (!is_float_out(c_dtype) && !fp8_c) {
+        if (c_dtype == BSG_E2M1X2) return fail(BSG_ERR_UNSUPPORTED, "FP4 C is not built");
         return fail(BSG_ERR_DTYPE, "c_dtype %d is not an output dtype", c_dtype);
     }
     if (m * n * l == 0) return BSG_OK;   // nothing to read or write but amax

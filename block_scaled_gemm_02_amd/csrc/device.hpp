@@ -732,13 +732,19 @@ template <> struct Quad<1> { typedef uint32_t T; };
 template <> struct Quad<2> { typedef uint2 T; };
 template <> struct Quad<4> { typedef float4 T; };
 
-// Packs four output values for output type DT.
+// Stored bytes per element of output type DT.
+template <int DT> constexpr int es_of() { return DT == DT_F32 ? 4 : ((DT == DT_E4M3 || DT == DT_E5M2) ? 1 : 2); }
+
+// Packs four output values for output type DT.  The FP8 types are plain
+// saturating casts (round to nearest even, clamped to the largest finite
+// value of the format).
 template <int DT>
-__device__ __forceinline__ typename Quad<DT == DT_F32 ? 4 : 2>::T pack_quad(float x0, float x1, float x2,
-                                                                             float x3)
+__device__ __forceinline__ typename Quad<es_of<DT>()>::T pack_quad(float x0, float x1, float x2, float x3)
 {
     if constexpr (DT == DT_F32) return make_float4(x0, x1, x2, x3);
     else if constexpr (DT == DT_BF16) return make_uint2(pack2_bf16(x0, x1), pack2_bf16(x2, x3));
+    else if constexpr (DT == DT_E4M3) return pack4_fp8<false>(x0, x1, x2, x3);
+    else if constexpr (DT == DT_E5M2) return pack4_fp8<true>(x0, x1, x2, x3);
     else return make_uint2(pack2_f16(x0, x1), pack2_f16(x2, x3));
 }
 
@@ -780,7 +786,7 @@ __device__ __forceinline__ void store_quadrant(uint8_t *reg, char *dst, char *ds
                                                int rows_valid, int cols_valid, f32x16 (&acc)[4][NB],
                                                int lane, Fn &&value)
 {
-    constexpr int ES = DT == DT_F32 ? 4 : 2;
+    constexpr int ES = es_of<DT>();
     typedef StageGeom<ES, NB> G;
     const int c = lane & 31, g = lane >> 5;
     uint8_t *wrow = reg + c * G::RBP + 4 * g * ES;

@@ -104,7 +104,7 @@ __global__ void __launch_bounds__(256) k_gemm_amax(GemmAmaxParams p)
     // rows of A / B and not stored
     float lmax = 0.0f;
     const int64_t qr = m0 + 128 * wm, qc = n0 + 128 * wn;
-    constexpr int es = CT == DT_F32 ? 4 : 2;
+    constexpr int es = es_of<CT>();
     char *const dst = static_cast<char *>(p.c) + ((batch * p.m + qr) * p.n + qc) * es;
     store_quadrant<CT, 4>(wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), dst, nullptr, (uint32_t)(p.n * es),
                           clamp_extent(p.m - qr), clamp_extent(p.n - qc), acc, lane, [&](int, int, int, float a) {
@@ -119,7 +119,12 @@ static void launch_gemm_amax_fmt(const GemmAmaxParams &p, dim3 grid, hipStream_t
 {
     if (p.c_dtype == DT_F32) hipLaunchKernelGGL((k_gemm_amax<F, DT_F32>), grid, dim3(kThreads), 0, s, p);
     else if (p.c_dtype == DT_BF16) hipLaunchKernelGGL((k_gemm_amax<F, DT_BF16>), grid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((k_gemm_amax<F, DT_F16>), grid, dim3(kThreads), 0, s, p);
+    else if (p.c_dtype == DT_F16) hipLaunchKernelGGL((k_gemm_amax<F, DT_F16>), grid, dim3(kThreads), 0, s, p);
+    else if constexpr (F == FMT_E2M1) {
+        // FP8 C: only with FP4 operands ("GEMM + Amax (SM100)", Dtypes)
+        if (p.c_dtype == DT_E4M3) hipLaunchKernelGGL((k_gemm_amax<F, DT_E4M3>), grid, dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_gemm_amax<F, DT_E5M2>), grid, dim3(kThreads), 0, s, p);
+    }
 }
 
 hipError_t launch_gemm_amax(const GemmAmaxArgs &a, hipStream_t s)

@@ -84,7 +84,11 @@ typedef enum bsg_dtype {
  *  b     (N,K,L) codes, k-major, same dtype as a
  *  sfa   scale atoms over (M, K, L);  sfb: scale atoms over (N, K, L)
  *  c     (M,N,L) output, n-major, c_dtype in {F32, BF16, F16}; RNE cast
- *        of the fp32 accumulator
+ *        of the fp32 accumulator.  With E2M1X2 A/B, c_dtype may also be
+ *        E4M3 or E5M2 (the page's Dtypes allow FP8 C only with FP4 A/B): a
+ *        plain RNE cast with no scale factor, saturated to +-448 / +-57344
+ *        (never NaN or Inf); rows of N bytes, N % 16 == 0.  FP8 C with FP8
+ *        A/B, and FP4 C, return UNSUPPORTED.
  *  amax  one float32 (nullable): max |C| of the fp32 accumulators (before
  *        the output cast); the library zero-fills it on `stream` first
  *  ab_dtype in {E4M3, E5M2, E2M1X2} (the page's float8_e4m3fn, float8_e5m2

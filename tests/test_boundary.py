@@ -45,7 +45,12 @@ def test_gemm_amax_validation():
     assert va(sf_vec_size=16) == UNSUP                   # NVFP4-style sf 16 not built
     assert va(sf_vec_size=8) == SHAPE
     assert va(k=48) == SHAPE                             # K % 32
-    assert va(c_dtype=bsg.E4M3) == UNSUP                 # FP8 C disabled on the page too
+    assert va(c_dtype=bsg.E4M3) == UNSUP                 # FP8 A/B with FP8 C disabled on the page too
+    assert va(c_dtype="e5m2", ab_dtype="e5m2") == UNSUP
+    assert va(c_dtype="e4m3", ab_dtype="e2m1") == OK     # FP8 C with FP4 A/B
+    assert va(c_dtype=torch.float8_e5m2, ab_dtype="e2m1") == OK
+    assert va(c_dtype="e4m3", ab_dtype="e2m1", n=40) == ALIGN   # 40-byte FP8 rows
+    assert va(c_dtype=bsg.E2M1X2, ab_dtype="e2m1") == UNSUP    # FP4 C not built
     assert va(a=0) == NULLPTR
     assert va(a=P + 8) == ALIGN                          # 16-byte alignment
     assert va(n=250) == ALIGN                            # fp32 C row of 1000 bytes

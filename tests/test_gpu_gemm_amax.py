@@ -9,7 +9,7 @@ import torch
 import block_scaled_gemm_02_amd as bsg
 import oracle as O
 import workloads as W
-from parity import check_amax, check_float, ceil_div, sf_slice, sum_bound
+from parity import FP8_MAX, check_amax, check_float, ceil_div, e4m3_ordered, sf_slice, sum_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -143,3 +143,51 @@ def test_gemm_amax_full_size_sampled(fmt):
     # amax is the max of the fp32 values whose bf16 roundings are in C
     cmax = c.float().abs().max().item()
     assert abs(amax.item() - cmax) <= cmax * 2.0 ** -8
+
+
+FP8_C_CASES = [
+    dict(m=260, n=144, k=352, l=2, c="e4m3"),     # ragged M
+    dict(m=512, n=272, k=4096, l=1, c="e4m3"),    # |C| reaches past 448: saturation
+    dict(m=300, n=208, k=256, l=2, c="e5m2"),
+]
+
+
+@pytest.mark.parametrize("case", FP8_C_CASES)
+def test_gemm_amax_fp8_c_with_fp4_inputs(case):
+    """FP8 C ("GEMM + Amax (SM100)" allows it with FP4 A/B): a saturating
+    round-to-nearest-even cast of each output.  Every code must lie between
+    the codes of oracle C -/+ its error bound (the cast is monotone), and
+    within one step of the oracle's own encode of the fp64 value; amax is of
+    the values before the cast."""
+    say(f"gemm_amax FP8 C {case}")
+    m, n, k, l, fmt = case["m"], case["n"], case["k"], case["l"], case["c"]
+    p = W.gemm_amax_problem(m, n, k, l, "e2m1", seed=5)
+    t = {kk: v.cuda() for kk, v in p.t.items()}
+    c = torch.full((l, m, n), 0xEE, dtype=torch.uint8, device="cuda")
+    amax = torch.full((1,), -7.0, device="cuda")
+    bsg.gemm_amax(t["a"], t["b"], t["sfa"], t["sfb"], c, amax, m, n, k, l, "e2m1", c_dtype=fmt)
+    torch.cuda.synchronize()
+    oc, os_, oamax, obm = O.gemm_amax_full(p.t["a"], p.t["b"], p.t["sfa"], p.t["sfb"], m, n, k, l, "e2m1",
+                                           want_bmax=True)
+    bound = sum_bound(os_, k, bmax=obm)
+    fmax = FP8_MAX[fmt]
+    tdt = torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2
+
+    def enc(v):
+        v = np.clip(v, -fmax, fmax).astype(np.float32)
+        return e4m3_ordered(torch.from_numpy(v).to(tdt).view(torch.uint8).numpy())
+
+    lo, hi = enc(oc - bound), enc(oc + bound)
+    g = e4m3_ordered(c.cpu().numpy())
+    bad = (g < lo) | (g > hi)
+    assert not bad.any(), f"{int(bad.sum())} codes outside the error-bound window"
+    oenc = O.enc_e4m3 if fmt == "e4m3" else O.enc_e5m2
+    eo = e4m3_ordered(np.array([oenc(v) for v in oc.ravel()], dtype=np.uint32).reshape(oc.shape))
+    step = np.abs(g - eo)
+    assert step.max() <= 1
+    assert int((step == 1).sum()) <= max(1, 1e-3 * step.size)
+    top = 0x7E if fmt == "e4m3" else 0x7B
+    sat = int((np.abs(oc) > fmax).sum())
+    assert np.all((np.abs(g) == top)[np.abs(oc) - bound > fmax])
+    say(f"  one-step flips {int((step == 1).sum())}/{step.size}, saturated {sat}")
+    check_amax(float(amax.item()), oamax, float(bound.ravel()[np.argmax(np.abs(oc))]))
