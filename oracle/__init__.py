@@ -55,6 +55,7 @@ def lib():
         L.orc_dec_bf16.restype = d; L.orc_dec_bf16.argtypes = [u32]
         L.orc_enc_e4m3.restype = u32; L.orc_enc_e4m3.argtypes = [d]
         L.orc_enc_e5m2.restype = u32; L.orc_enc_e5m2.argtypes = [d]
+        L.orc_enc_e2m1.restype = u32; L.orc_enc_e2m1.argtypes = [d]
         L.orc_rne_bf16.restype = u32; L.orc_rne_bf16.argtypes = [d]
         L.orc_e8m0_ceil.restype = u32; L.orc_e8m0_ceil.argtypes = [d]
         L.orc_rne_bf16_array.restype = None; L.orc_rne_bf16_array.argtypes = [p, p, i64]
@@ -120,6 +121,7 @@ def dec_e8m0(b: int) -> float: return lib().orc_dec_e8m0(b)
 def dec_bf16(h: int) -> float: return lib().orc_dec_bf16(h)
 def enc_e4m3(x: float) -> int: return lib().orc_enc_e4m3(float(x))
 def enc_e5m2(x: float) -> int: return lib().orc_enc_e5m2(float(x))
+def enc_e2m1(x: float) -> int: return lib().orc_enc_e2m1(float(x))
 def rne_bf16(x: float) -> int: return lib().orc_rne_bf16(float(x))
 def e8m0_ceil(sigma: float) -> int: return lib().orc_e8m0_ceil(float(sigma))
 

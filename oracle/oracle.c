@@ -73,6 +73,22 @@ double orc_dec_e2m1(uint32_t nib)
     return s ? -v : v;
 }
 
+/* fp64 -> E2M1 nibble: the nearest of the eight magnitudes (0, 0.5, 1, 1.5,
+ * 2, 3, 4, 6), a tie going to the code whose mantissa bit is 0 (round to
+ * nearest even); magnitudes past 6 saturate to 6.  Sign in bit 3. */
+uint32_t orc_enc_e2m1(double x)
+{
+    uint32_t s = signbit(x) ? 8u : 0u, best = 0u, c;
+    double a = fabs(x), bd = INFINITY;
+    if (isnan(x)) return 7u;
+    if (a >= 6.0) return s | 7u;
+    for (c = 0u; c < 8u; ++c) {
+        double dist = fabs(orc_dec_e2m1(c) - a);
+        if (dist < bd || (dist == bd && (c & 1u) == 0u)) { bd = dist; best = c; }
+    }
+    return s | best;
+}
+
 /* E8M0: unsigned biased exponent 2^(b-127); 0xFF is NaN. */
 double orc_dec_e8m0(uint32_t b)
 {

@@ -214,3 +214,30 @@ def test_e5m2_encode_ties_saturation_and_subnormals():
     # smallest subnormal 2^-16; half of it ties to zero (even), 3/2 of it to 2^-15
     assert O.enc_e5m2(2.0 ** -16) == 0x01 and O.enc_e5m2(2.0 ** -17) == 0x00
     assert O.enc_e5m2(3 * 2.0 ** -17) == 0x02
+
+
+def test_e2m1_encode_roundtrip_ties_and_saturation():
+    # every code round-trips (the negative zero code 0x8 decodes to -0.0)
+    for c in range(16):
+        assert O.enc_e2m1(O.dec_e2m1(c)) == c, hex(c)
+    # midpoints tie to the even mantissa: 0.25->0, 0.75->1.0, 1.25->1.0,
+    # 1.75->2, 2.5->2, 3.5->4, 5->4; just past a midpoint rounds up
+    for v, c in [(0.25, 0x0), (0.75, 0x2), (1.25, 0x2), (1.75, 0x4), (2.5, 0x4), (3.5, 0x6), (5.0, 0x6),
+                 (0.2500001, 0x1), (1.2500001, 0x3), (2.5000001, 0x5), (5.0000001, 0x7)]:
+        assert O.enc_e2m1(v) == c, (v, c)
+        assert O.enc_e2m1(-v) == c | 0x8, (-v, c)
+    # saturation at 6, never past it
+    assert O.enc_e2m1(6.0) == 0x7 and O.enc_e2m1(7.9) == 0x7 and O.enc_e2m1(1e30) == 0x7
+    assert O.enc_e2m1(-1e30) == 0xF
+
+
+def test_e2m1_encode_is_nearest_by_brute_force():
+    # against the decode table: the encoded magnitude is never farther from x
+    # than any other code's
+    mags = [O.dec_e2m1(c) for c in range(8)]
+    rng = np.random.default_rng(11)
+    for x in np.concatenate([rng.uniform(-7, 7, 4000), rng.uniform(-0.6, 0.6, 1000)]):
+        got = O.dec_e2m1(O.enc_e2m1(float(x)))
+        best = min(abs(m - min(abs(x), 6.0)) for m in mags)
+        assert abs(abs(got) - min(abs(x), 6.0)) == best, x
+        assert got == 0.0 or math.copysign(1, got) == math.copysign(1, x)
