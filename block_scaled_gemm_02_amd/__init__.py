@@ -129,6 +129,8 @@ def _d_code(d_dtype, d) -> int:
         return E4M3
     if x in ("e5m2", E5M2, torch.float8_e5m2):
         return E5M2
+    if x in ("e2m1", E2M1X2):
+        return E2M1X2
     return dtype_code(x)
 
 
@@ -136,7 +138,8 @@ def _d_code(d_dtype, d) -> int:
 def gemm_amax(a, b, sfa, sfb, c, amax, m, n, k, l, ab_dtype="e4m3", c_dtype=None,
               sf_vec_size=32, stream=None, validate_only=False):
     """C = sum_k A_hat B_hat per batch and Amax = max |C| (see include/bsg.h).
-    c_dtype: a torch float dtype, or "e4m3" / "e5m2" (FP8 C, FP4 operands only)."""
+    c_dtype: a torch float dtype, "e4m3" / "e5m2" (FP8 C) or "e2m1" (packed
+    FP4 C, (M, N/2, L) bytes); the last three with FP4 operands only."""
     cd = _d_code(c_dtype, c)
     args = [_ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), _ptr(c), _ptr(amax), m, n, k, l,
             _ab_code(ab_dtype), cd, sf_vec_size]

@@ -129,18 +129,17 @@ int bsg_validate_gemm_amax(const void *a, const void *b, const uint8_t *sfa, con
     if (st) return st;
     if (m < 0 || n < 0 || k < 0 || l < 0) return fail(BSG_ERR_SHAPE, "negative size");
     if (k % 32) return fail(BSG_ERR_SHAPE, "K=%lld must be a multiple of sf_vec_size 32", (long long)k);
-    const bool fp8_c = c_dtype == BSG_E4M3 || c_dtype == BSG_E5M2;
+    const bool fp8_c = c_dtype == BSG_E4M3 || c_dtype == BSG_E5M2, fp4_c = c_dtype == BSG_E2M1X2;
     if (fp8_c && ab_dtype != BSG_E2M1X2)
         return fail(BSG_ERR_UNSUPPORTED, "FP8 C with FP8 A/B is disabled (FP8 C takes FP4 A/B)");
-    if (!is_float_out(c_dtype) && !fp8_c) {
-        if (c_dtype == BSG_E2M1X2) return fail(BSG_ERR_UNSUPPORTED, "FP4 C is not built");
+    if (fp4_c && ab_dtype != BSG_E2M1X2) return fail(BSG_ERR_DTYPE, "FP4 C requires FP4 A/B");
+    if (!is_float_out(c_dtype) && !fp8_c && !fp4_c)
         return fail(BSG_ERR_DTYPE, "c_dtype %d is not an output dtype", c_dtype);
-    }
     if (m * n * l == 0) return BSG_OK;   // nothing to read or write but amax
     if (!a || !b || !sfa || !sfb || !c) return fail(BSG_ERR_NULLPTR, "a, b, sfa, sfb and c are required");
     if (k > 0 && (!aligned16(a) || !aligned16(b))) return fail(BSG_ERR_ALIGN, "A and B must be 16-byte aligned");
-    if (!aligned16(c) || (n * elem_bytes(c_dtype)) % 16)
-        return fail(BSG_ERR_ALIGN, "C must be 16-byte aligned with N*sizeof(C) a multiple of 16");
+    if (!aligned16(c) || (fp4_c ? n % 32 : (n * elem_bytes(c_dtype)) % 16))
+        return fail(BSG_ERR_ALIGN, "C must be 16-byte aligned with rows of a multiple of 16 bytes");
     if ((int64_t)row_bytes(ab_dtype, k) * 256 >= (1ll << 31))
         return fail(BSG_ERR_UNSUPPORTED, "K too large for 32-bit tile offsets");
     return check_tiles((m + 255) / 256, n, l);

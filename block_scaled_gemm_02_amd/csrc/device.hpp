@@ -672,7 +672,7 @@ __device__ __forceinline__ int acc_col(int wn, int j, int q, int lane)
     return 32 * NB * wn + 32 * j + 8 * q + 4 * (lane >> 5);
 }
 
-enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_E4M3 = 3, DT_E5M2 = 4 };
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_E4M3 = 3, DT_E5M2 = 4, DT_E2M1 = 5 };
 
 // Max over the 32 lanes of each half-wave (lanes 0-31 and 32-63 separately)
 // of each of N non-negative values: quad and row DPP steps reduce 16 lanes, a
@@ -811,6 +811,49 @@ __device__ __forceinline__ void store_quadrant(uint8_t *reg, char *dst, char *ds
         stage_flush<ES, NB>(reg, dst + (uint32_t)(32 * i) * row_bytes, row_bytes, rows, cols_valid * ES, lane);
         if (dst2)
             stage_flush<ES, NB>(reg, dst2 + (uint32_t)(32 * i) * row_bytes, row_bytes, rows, cols_valid * ES, lane);
+    });
+}
+
+// E2M1 code of x: round to nearest even, saturating at 6.  The magnitude
+// code is the number of rounding thresholds |x| passes, the thresholds being
+// the midpoints between the eight magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.  At
+// a midpoint the code with an even mantissa bit wins, so the thresholds
+// below an even code are inclusive and the others strict.  Sign in bit 3.
+__device__ __forceinline__ uint32_t e2m1_code(float x)
+{
+    const float a = fabsf(x);
+    const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+    return c | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+// store_quadrant for packed E2M1 output: two codes per byte, the even
+// column in the low nibble.  A lane's four consecutive columns are two
+// bytes; a staged row of 32*NB columns is 16*NB bytes (StageGeom<1, NB/2>).
+template <int NB, class Fn>
+__device__ __forceinline__ void store_quadrant_fp4(uint8_t *reg, char *dst, uint32_t row_bytes, int rows_valid,
+                                                   int cols_valid, f32x16 (&acc)[4][NB], int lane, Fn &&value)
+{
+    static_assert(NB % 2 == 0, "whole 16-byte chunks per staged row");
+    typedef StageGeom<1, NB / 2> G;
+    const int c = lane & 31, g = lane >> 5;
+    uint8_t *wrow = reg + c * G::RBP + 2 * g;
+    static_for<4>([&](auto ii) {
+        constexpr int i = decltype(ii)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<NB>([&](auto jj) {
+            constexpr int j = decltype(jj)::value;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t e0 = e2m1_code(value(i, j, 4 * q, acc[i][j][4 * q]));
+                const uint32_t e1 = e2m1_code(value(i, j, 4 * q + 1, acc[i][j][4 * q + 1]));
+                const uint32_t e2 = e2m1_code(value(i, j, 4 * q + 2, acc[i][j][4 * q + 2]));
+                const uint32_t e3 = e2m1_code(value(i, j, 4 * q + 3, acc[i][j][4 * q + 3]));
+                *reinterpret_cast<uint16_t *>(wrow + 16 * j + 4 * q) = (uint16_t)(e0 | (e1 << 4) | (e2 << 8) | (e3 << 12));
+            }
+        });
+        stage_flush<1, NB / 2>(reg, dst + (uint32_t)(32 * i) * row_bytes, row_bytes, rows_valid - 32 * i,
+                               cols_valid / 2, lane);
     });
 }
 

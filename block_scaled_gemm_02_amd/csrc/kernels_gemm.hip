@@ -104,13 +104,21 @@ __global__ void __launch_bounds__(256) k_gemm_amax(GemmAmaxParams p)
     // rows of A / B and not stored
     float lmax = 0.0f;
     const int64_t qr = m0 + 128 * wm, qc = n0 + 128 * wn;
-    constexpr int es = es_of<CT>();
-    char *const dst = static_cast<char *>(p.c) + ((batch * p.m + qr) * p.n + qc) * es;
-    store_quadrant<CT, 4>(wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), dst, nullptr, (uint32_t)(p.n * es),
-                          clamp_extent(p.m - qr), clamp_extent(p.n - qc), acc, lane, [&](int, int, int, float a) {
-                              lmax = fmaxf(lmax, fabsf(a));
-                              return a;
-                          });
+    auto val = [&](int, int, int, float a) {
+        lmax = fmaxf(lmax, fabsf(a));
+        return a;
+    };
+    if constexpr (CT == DT_E2M1) {
+        // packed E2M1 C: N / 2 bytes per row (N % 32 == 0, checked on the host)
+        char *const dst = static_cast<char *>(p.c) + ((batch * p.m + qr) * p.n + qc) / 2;
+        store_quadrant_fp4<4>(wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), dst, (uint32_t)(p.n / 2),
+                              clamp_extent(p.m - qr), clamp_extent(p.n - qc), acc, lane, val);
+    } else {
+        constexpr int es = es_of<CT>();
+        char *const dst = static_cast<char *>(p.c) + ((batch * p.m + qr) * p.n + qc) * es;
+        store_quadrant<CT, 4>(wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), dst, nullptr,
+                              (uint32_t)(p.n * es), clamp_extent(p.m - qr), clamp_extent(p.n - qc), acc, lane, val);
+    }
     if (p.amax) block_amax_atomic(lmax, p.amax, red);
 }
 
@@ -121,9 +129,10 @@ static void launch_gemm_amax_fmt(const GemmAmaxParams &p, dim3 grid, hipStream_t
     else if (p.c_dtype == DT_BF16) hipLaunchKernelGGL((k_gemm_amax<F, DT_BF16>), grid, dim3(kThreads), 0, s, p);
     else if (p.c_dtype == DT_F16) hipLaunchKernelGGL((k_gemm_amax<F, DT_F16>), grid, dim3(kThreads), 0, s, p);
     else if constexpr (F == FMT_E2M1) {
-        // FP8 C: only with FP4 operands ("GEMM + Amax (SM100)", Dtypes)
+        // FP8 and FP4 C: only with FP4 operands ("GEMM + Amax (SM100)", Dtypes)
         if (p.c_dtype == DT_E4M3) hipLaunchKernelGGL((k_gemm_amax<F, DT_E4M3>), grid, dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((k_gemm_amax<F, DT_E5M2>), grid, dim3(kThreads), 0, s, p);
+        else if (p.c_dtype == DT_E5M2) hipLaunchKernelGGL((k_gemm_amax<F, DT_E5M2>), grid, dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_gemm_amax<F, DT_E2M1>), grid, dim3(kThreads), 0, s, p);
     }
 }
 

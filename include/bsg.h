@@ -87,8 +87,11 @@ typedef enum bsg_dtype {
  *        of the fp32 accumulator.  With E2M1X2 A/B, c_dtype may also be
  *        E4M3 or E5M2 (the page's Dtypes allow FP8 C only with FP4 A/B): a
  *        plain RNE cast with no scale factor, saturated to +-448 / +-57344
- *        (never NaN or Inf); rows of N bytes, N % 16 == 0.  FP8 C with FP8
- *        A/B, and FP4 C, return UNSUPPORTED.
+ *        (never NaN or Inf); rows of N bytes, N % 16 == 0.  Also with
+ *        E2M1X2 A/B: c_dtype E2M1X2, packed FP4 C of (M, N/2, L) bytes, two
+ *        codes per byte with the even column in the low nibble, an RNE cast
+ *        saturated to +-6; N % 32 == 0.  FP8 C with FP8 A/B returns
+ *        UNSUPPORTED; FP4 C with FP8 A/B returns DTYPE.
  *  amax  one float32 (nullable): max |C| of the fp32 accumulators (before
  *        the output cast); the library zero-fills it on `stream` first
  *  ab_dtype in {E4M3, E5M2, E2M1X2} (the page's float8_e4m3fn, float8_e5m2

@@ -50,7 +50,9 @@ def test_gemm_amax_validation():
     assert va(c_dtype="e4m3", ab_dtype="e2m1") == OK     # FP8 C with FP4 A/B
     assert va(c_dtype=torch.float8_e5m2, ab_dtype="e2m1") == OK
     assert va(c_dtype="e4m3", ab_dtype="e2m1", n=40) == ALIGN   # 40-byte FP8 rows
-    assert va(c_dtype=bsg.E2M1X2, ab_dtype="e2m1") == UNSUP    # FP4 C not built
+    assert va(c_dtype=bsg.E2M1X2, ab_dtype="e2m1") == OK       # packed FP4 C
+    assert va(c_dtype="e2m1", ab_dtype="e2m1", n=48) == ALIGN   # 24-byte FP4 rows
+    assert va(c_dtype="e2m1", ab_dtype="e4m3") == DTYPE         # FP4 C requires FP4 A/B
     assert va(a=0) == NULLPTR
     assert va(a=P + 8) == ALIGN                          # 16-byte alignment
     assert va(n=250) == ALIGN                            # fp32 C row of 1000 bytes

@@ -191,3 +191,44 @@ def test_gemm_amax_fp8_c_with_fp4_inputs(case):
     assert np.all((np.abs(g) == top)[np.abs(oc) - bound > fmax])
     say(f"  one-step flips {int((step == 1).sum())}/{step.size}, saturated {sat}")
     check_amax(float(amax.item()), oamax, float(bound.ravel()[np.argmax(np.abs(oc))]))
+
+
+def _e2m1_ordered(nibs: np.ndarray) -> np.ndarray:
+    n = nibs.astype(np.int64)
+    return np.where(n & 8, -(n & 7), n & 7)
+
+
+@pytest.mark.parametrize("case", [dict(m=260, n=160, k=352, l=2), dict(m=512, n=544, k=1024, l=1)])
+def test_gemm_amax_fp4_c_with_fp4_inputs(case):
+    """Packed E2M1 C (two codes per byte, even column in the low nibble): a
+    saturating round-to-nearest-even cast.  The SFA bytes are lowered by 6
+    (C / 64) so that C spans the E2M1 range and past it.  Every code must lie
+    between the oracle encoder's codes of C -/+ its error bound, and equal
+    the oracle's encode of the fp64 value up to one step on at most 0.1%."""
+    say(f"gemm_amax FP4 C {case}")
+    m, n, k, l = case["m"], case["n"], case["k"], case["l"]
+    p = W.gemm_amax_problem(m, n, k, l, "e2m1", seed=9)
+    p.t["sfa"] = (p.t["sfa"].to(torch.int32) - 6).clamp(min=0).to(torch.uint8)
+    t = {kk: v.cuda() for kk, v in p.t.items()}
+    c = torch.full((l, m, n // 2), 0xEE, dtype=torch.uint8, device="cuda")
+    amax = torch.full((1,), -7.0, device="cuda")
+    bsg.gemm_amax(t["a"], t["b"], t["sfa"], t["sfb"], c, amax, m, n, k, l, "e2m1", c_dtype="e2m1")
+    torch.cuda.synchronize()
+    oc, os_, oamax, obm = O.gemm_amax_full(p.t["a"], p.t["b"], p.t["sfa"], p.t["sfb"], m, n, k, l, "e2m1",
+                                           want_bmax=True)
+    bound = sum_bound(os_, k, bmax=obm)
+    enc = np.vectorize(lambda v: O.enc_e2m1(float(v)), otypes=[np.uint32])
+    lo, hi = _e2m1_ordered(enc(oc - bound)), _e2m1_ordered(enc(oc + bound))
+    raw = c.cpu().numpy()
+    nib = np.empty((l, m, n), dtype=np.uint8)
+    nib[..., 0::2], nib[..., 1::2] = raw & 15, raw >> 4
+    g = _e2m1_ordered(nib)
+    bad = (g < lo) | (g > hi)
+    assert not bad.any(), f"{int(bad.sum())} codes outside the error-bound window"
+    step = np.abs(g - _e2m1_ordered(enc(oc)))
+    assert step.max() <= 1 and int((step == 1).sum()) <= max(1, 1e-3 * step.size)
+    sat = int((np.abs(oc) > 6).sum())
+    assert 0 < sat < oc.size                       # both in-range and saturated values occur
+    say(f"  one-step flips {int((step == 1).sum())}/{step.size}, saturated {sat}, "
+        f"codes used {len(np.unique(g))}")
+    check_amax(float(amax.item()), oamax, float(bound.ravel()[np.argmax(np.abs(oc))]))
