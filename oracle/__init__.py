@@ -307,7 +307,8 @@ def proj_rope_mx(x_codes, x_scale, w_codes, w_scale, cos_bits, sin_bits, tokens,
 # ---------------------------------------------------------------------------
 def mx_quant_rows(d: np.ndarray, norm_const: float = 1.0, fmt: str = "e4m3"):
     """Blocks of 32 along each row -> (codes uint8 (R,C), scales uint8 (R, ceil(C/32)));
-    fmt "e4m3" (rcp_max 1/448) or "e5m2" (1/57344)."""
+    fmt "e4m3" (rcp_max 1/448), "e5m2" (1/57344) or "e2m1" (1/6; one code
+    per byte, unpacked)."""
     d = np.ascontiguousarray(d, dtype=np.float64)
     r, c = d.shape
     codes = np.empty((r, c), dtype=np.uint8)

@@ -661,8 +661,8 @@ int orc_proj_rope_mx(const uint8_t *x, const uint8_t *x_scale, const uint8_t *w,
 /* MX output quantiser ([GD] Step 3):                                       */
 /*   SFD = norm_const * max_{k in block} |D| * rcp_max                      */
 /*   D_q = D * norm_const / SFD                                             */
-/* with rcp_max = 1/448 for E4M3 (1/57344 for E5M2) and blocks of 32       */
-/* consecutive elements.                                                    */
+/* with rcp_max = 1/448 for E4M3 (1/57344 for E5M2, 1/6 for E2M1) and     */
+/* blocks of 32 consecutive elements.                                       */
 /* SFD is stored as E8M0: the smallest power of two >= the computed value   */
 /* (so |D_q| <= 448 needs no clipping); codes are E4M3 by round to nearest  */
 /* even, saturating.  The decisions are taken in binary32, in this order:   */
@@ -678,7 +678,7 @@ static void quant_block(const double *d, int64_t cnt, int64_t stride, float norm
 {
     float amax = 0.0f, sigma, inv;
     uint32_t byte;
-    const float rcp_max = fmt == 2 ? 1.0f / 57344.0f : 1.0f / 448.0f;
+    const float rcp_max = fmt == 2 ? 1.0f / 57344.0f : (fmt == 1 ? 1.0f / 6.0f : 1.0f / 448.0f);
     for (int64_t i = 0; i < cnt; ++i) {
         float v = fabsf((float)d[i * stride]);
         if (v > amax) amax = v;
@@ -690,14 +690,15 @@ static void quant_block(const double *d, int64_t cnt, int64_t stride, float norm
     for (int64_t i = 0; i < cnt; ++i) {
         float v = (float)d[i * stride];
         float y = v * inv;
-        codes[i * cstride] = (uint8_t)(fmt == 2 ? orc_enc_e5m2((double)y) : orc_enc_e4m3((double)y));
+        codes[i * cstride] = (uint8_t)(fmt == 2 ? orc_enc_e5m2((double)y)
+                                                : (fmt == 1 ? orc_enc_e2m1((double)y) : orc_enc_e4m3((double)y)));
     }
     *scale = (uint8_t)byte;
 }
 
 /* Row direction: blocks of 32 along each row.  d is (rows, cols) with
  * leading dimension ld; codes (rows, cols); scales (rows, ceil(cols/32)). */
-/* fmt 0: E4M3 codes; fmt 2: E5M2 codes. */
+/* fmt 0: E4M3 codes; fmt 1: E2M1 codes (one nibble per byte); fmt 2: E5M2. */
 void orc_mx_quant_rows(const double *d, int64_t rows, int64_t cols, int64_t ld,
                        float norm_const, int fmt, uint8_t *codes, uint8_t *scales)
 {

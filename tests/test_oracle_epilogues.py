@@ -207,3 +207,36 @@ def test_quantiser_e5m2_power_of_two_closed_forms():
     cr, sr = O.mx_quant_cols(d, fmt="e5m2")
     ct, st = O.mx_quant_rows(np.ascontiguousarray(d.T), fmt="e5m2")
     assert np.array_equal(cr, ct.T) and np.array_equal(sr, st.T)
+
+
+def test_quantiser_e2m1_power_of_two_closed_forms():
+    # E2M1 codes (rcp_max 1/6): block max exactly 6 * 2^j -> scale byte 127 + j,
+    # that element encodes to the top code 7, the rest to RNE(D / 2^j).
+    rng = np.random.default_rng(16)
+    for j in (-40, -1, 0, 2, 25):
+        blk = rng.uniform(-1, 1, 32) * 6 * 2.0 ** j
+        blk[5] = -6 * 2.0 ** j
+        codes, scales = O.mx_quant_rows(blk[None, :], fmt="e2m1")
+        assert scales[0, 0] == 127 + j
+        assert codes[0, 5] == 0xF
+        for i in range(32):
+            v = float(np.float32(blk[i])) / 2.0 ** j
+            assert codes[0, i] == O.enc_e2m1(v)
+    # just above 6 * 2^j the scale rounds up and no code saturates
+    blk = np.full(32, 6.0); blk[0] = 6.5
+    c, sc = O.mx_quant_rows(blk[None, :], fmt="e2m1")
+    assert sc[0, 0] == 128 and c[0, 0] == O.enc_e2m1(3.25) and c[0, 1] == O.enc_e2m1(3.0)
+    # dequantised codes stay within half a code step of the value: steps are
+    # 0.5 below 2, 1 in [2, 4) and 2 in [4, 6] (in units of the block scale)
+    d = rng.standard_normal((32, 64)) * np.exp(rng.uniform(-5, 5, (32, 1)))
+    c, sc = O.mx_quant_rows(d, fmt="e2m1")
+    sf = 2.0 ** (np.repeat(sc.astype(float), 32, 1) - 127)
+    y = np.abs(d) / sf
+    assert np.all(y <= 6.0)                        # the round-up scale leaves nothing to saturate
+    half = np.where(y < 2, 0.25, np.where(y < 4, 0.5, 1.0))
+    deq = np.vectorize(O.dec_e2m1)(c.astype(np.uint32)) * sf
+    assert np.all(np.abs(deq - d) <= half * sf)
+    # columns agree with rows of the transpose
+    cr, sr = O.mx_quant_cols(d, fmt="e2m1")
+    ct, st = O.mx_quant_rows(np.ascontiguousarray(d.T), fmt="e2m1")
+    assert np.array_equal(cr, ct.T) and np.array_equal(sr, st.T)
