@@ -55,8 +55,9 @@ def wl_moe_mxfp8_srelu(fp8_out=False, discrete=False, fmt="e4m3", d_fp8="e4m3"):
         del t["b"], t["sfb"]
     c = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
     if fp8_out:
-        d = torch.empty(m, n, dtype=torch.uint8, device="cuda")
-        d_col = torch.empty(m, n, dtype=torch.uint8, device="cuda")
+        nb = n // 2 if d_fp8 == "e2m1" else n       # E2M1 codes: two per byte
+        d = torch.empty(m, nb, dtype=torch.uint8, device="cuda")
+        d_col = torch.empty(m, nb, dtype=torch.uint8, device="cuda")
         sfd_row = torch.empty(W.sf_atom_bytes(m, n, 1), dtype=torch.uint8, device="cuda")
         sfd_col = torch.empty(W.sf_atom_bytes(n, m, 1), dtype=torch.uint8, device="cuda")
         amax = None
@@ -84,10 +85,12 @@ def wl_moe_mxfp8_srelu(fp8_out=False, discrete=False, fmt="e4m3", d_fp8="e4m3"):
     flops = 2.0 * valid_m * n * k
     ab_bytes = valid_m * k + L * n * k if fmt == "e4m3" else (valid_m * k + L * n * k) // 2
     sf_bytes = t["sfa"].numel() + (sum(x.numel() for x in sfb_list) if discrete else t["sfb"].numel())
-    out_bytes = valid_m * n * (2 + (2 if not fp8_out else 2) + 0)
+    # C bf16, then D (bf16), or D and D_col codes (1 byte each, E2M1 half a byte each)
+    out_bytes = valid_m * n * (2 + (2 if not fp8_out else (1 if d_fp8 == "e2m1" else 2)))
     alg_bytes = ab_bytes + sf_bytes + out_bytes
     name = ("moe_mxfp8_srelu" if fmt == "e4m3" else "moe_mxfp4_srelu") + \
-        (("_fp8d" if d_fp8 == "e4m3" else "_e5m2d") if fp8_out else "") + ("_discrete" if discrete else "")
+        ({"e4m3": "_fp8d", "e5m2": "_e5m2d", "e2m1": "_mxfp4d"}[d_fp8] if fp8_out else "") + \
+        ("_discrete" if discrete else "")
     info = dict(
         name=name, fmt=fmt, flops=flops, alg_bytes=alg_bytes, kernel="k_grouped",
         config={"workload": ("grouped MXFP8 (E4M3" if fmt == "e4m3" else "grouped MXFP4 (E2M1")
@@ -267,6 +270,7 @@ WORKLOADS = {
     "moe_mxfp8_srelu": lambda: wl_moe_mxfp8_srelu(False),
     "moe_mxfp8_srelu_fp8d": lambda: wl_moe_mxfp8_srelu(True),
     "moe_mxfp8_srelu_e5m2d": lambda: wl_moe_mxfp8_srelu(True, d_fp8="e5m2"),
+    "moe_mxfp8_srelu_mxfp4d": lambda: wl_moe_mxfp8_srelu(True, d_fp8="e2m1"),
     "moe_mxfp8_srelu_discrete": lambda: wl_moe_mxfp8_srelu(False, discrete=True),
     "moe_mxfp4_srelu": lambda: wl_moe_mxfp8_srelu(False, fmt="e2m1"),
     "moe_mxfp8_dswiglu": wl_moe_dswiglu,

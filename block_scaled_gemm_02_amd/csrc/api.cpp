@@ -275,17 +275,14 @@ static int validate_srelu(const void *a, const void *b, const uint8_t *sfa, cons
     if (n % 32) return fail(BSG_ERR_SHAPE, "N=%lld must be a multiple of 32", (long long)n);
     if (!(tanh_clamp_scale == tanh_clamp_scale)) return fail(BSG_ERR_SHAPE, "tanh_clamp_scale is NaN");
     if (c && !is_float_out(c_dtype)) return fail(BSG_ERR_DTYPE, "C dtype must be F32, F16 or BF16");
-    const bool fp8_out = d_dtype == BSG_E4M3 || d_dtype == BSG_E5M2;
-    if (!fp8_out && !is_float_out(d_dtype)) {
-        if (d_dtype == BSG_E2M1X2)
-            return fail(BSG_ERR_UNSUPPORTED, "D dtype %d is not built", d_dtype);
-        return fail(BSG_ERR_DTYPE, "D dtype %d invalid", d_dtype);
-    }
+    // quantised D: E4M3 / E5M2 codes, or E2M1 codes two per byte
+    const bool fp8_out = d_dtype == BSG_E4M3 || d_dtype == BSG_E5M2 || d_dtype == BSG_E2M1X2;
+    if (!fp8_out && !is_float_out(d_dtype)) return fail(BSG_ERR_DTYPE, "D dtype %d invalid", d_dtype);
     if (fp8_out) {
         if (ab_dtype == BSG_E2M1X2)
-            return fail(BSG_ERR_DTYPE, "FP8 D requires FP8 A/B (FP4 inputs take fp16/bf16/fp32 D)");
+            return fail(BSG_ERR_DTYPE, "quantised D requires FP8 A/B (FP4 inputs take fp16/bf16/fp32 D)");
         if (!norm_const || !sfd_row || !sfd_col || !d_col)
-            return fail(BSG_ERR_NULLPTR, "FP8 D needs norm_const, d_col, sfd_row and sfd_col");
+            return fail(BSG_ERR_NULLPTR, "quantised D needs norm_const, d_col, sfd_row and sfd_col");
     }
     if (m * n == 0) return BSG_OK;
     if (!sfa || !sfb) return fail(BSG_ERR_NULLPTR, discrete ? "sfa and sfb_ptrs are required" : "sfa and sfb are required");
@@ -320,7 +317,7 @@ static int run_srelu(const void *a, const void *b, const uint64_t *b_ptrs, const
     args.sfa = sfa; args.sfb = sfb; args.offsets = padded_offsets; args.alpha = alpha;
     args.prob = prob; args.norm_const = norm_const; args.c = c; args.d = d; args.d_col = d_col;
     args.sfd_row = sfd_row; args.sfd_col = sfd_col;
-    args.amax = (d_dtype == BSG_E4M3 || d_dtype == BSG_E5M2) ? nullptr : amax;
+    args.amax = (d_dtype == BSG_E4M3 || d_dtype == BSG_E5M2 || d_dtype == BSG_E2M1X2) ? nullptr : amax;
     args.m = m; args.n = n; args.k = k; args.num_experts = num_experts;
     args.fmt = fmt_of(ab_dtype); args.c_dtype = c_dtype; args.d_dtype = d_dtype;
     args.tanh_s = tanh_clamp_scale > 0.0f ? tanh_clamp_scale : 0.0f;

@@ -827,6 +827,12 @@ __device__ __forceinline__ uint32_t e2m1_code(float x)
     return c | ((__float_as_uint(x) >> 28) & 8u);
 }
 
+// Four E2M1 codes, x0 in the lowest nibble.
+__device__ __forceinline__ uint32_t pack4_e2m1(float x0, float x1, float x2, float x3)
+{
+    return e2m1_code(x0) | (e2m1_code(x1) << 4) | (e2m1_code(x2) << 8) | (e2m1_code(x3) << 12);
+}
+
 // store_quadrant for packed E2M1 output: two codes per byte, the even
 // column in the low nibble.  A lane's four consecutive columns are two
 // bytes; a staged row of 32*NB columns is 16*NB bytes (StageGeom<1, NB/2>).
@@ -899,12 +905,14 @@ __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
 // The MX output quantiser's scale step for a block with max |D| = amax:
 // SF = smallest power of two >= norm_const * amax / fmax (E8M0 byte), with
-// fmax = 448 for E4M3 codes and 57344 for E5M2 (E5 = true), and the factor
-// norm_const / SF that maps the block into the code format's range.
-template <bool E5 = false>
+// fmax = 448 for E4M3 codes, 57344 for E5M2 and 6 for E2M1 (DF: DT_E4M3,
+// DT_E5M2 or DT_E2M1), and the factor norm_const / SF that maps the block
+// into the code format's range.
+template <int DF = DT_E4M3>
 __device__ __forceinline__ uint32_t mx_scale_byte(float amax, float norm_const, float &inv)
 {
-    const float sigma = (norm_const * amax) * (E5 ? 1.0f / 57344.0f : 1.0f / 448.0f);
+    const float rcp_max = DF == DT_E5M2 ? 1.0f / 57344.0f : (DF == DT_E2M1 ? 1.0f / 6.0f : 1.0f / 448.0f);
+    const float sigma = (norm_const * amax) * rcp_max;
     const uint32_t byte = e8m0_ceil(sigma);
     inv = fminf(ldexpf(norm_const, 127 - (int)byte), 3.402823466e38f);
     return byte;
@@ -924,7 +932,7 @@ __device__ __forceinline__ float lane_select(uint64_t mask, float x0, float x1)
 // after half_wave_max).  Lane c of each half-wave computes the E8M0 scale of
 // register c % 16 only, and every lane then gathers the 16 factors it needs
 // from lanes 32g + v.  Returns this lane's byte: the scale of register c % 16.
-template <bool E5 = false>
+template <int DF = DT_E4M3>
 __device__ __forceinline__ uint32_t col_scales(const float (&cm)[16], float nc, float (&cinv)[16], int lane)
 {
     // m = cm[lane % 16]: a tree of selects on the bits of the lane index,
@@ -940,7 +948,7 @@ __device__ __forceinline__ uint32_t col_scales(const float (&cm)[16], float nc, 
     for (int k = 0; k < 2; ++k) t2[k] = lane_select(0xF0F0F0F0F0F0F0F0ull, t4[2 * k], t4[2 * k + 1]);
     const float m = lane_select(0xFF00FF00FF00FF00ull, t2[0], t2[1]);
     float inv;
-    const uint32_t byte = mx_scale_byte<E5>(m, nc, inv);
+    const uint32_t byte = mx_scale_byte<DF>(m, nc, inv);
     const int base = lane & 32;
 #pragma unroll
     for (int v = 0; v < 16; ++v) cinv[v] = __shfl(inv, base + v);

@@ -309,8 +309,10 @@ __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, f32x16 
 // MXFP8 output: D quantised in 32-wide blocks along N (codes to d, scales to
 // the SFD_row atoms over (M, N)) and in 32-tall blocks along M (codes to
 // d_col, scales to the SFD_col atoms over (N, M)), with the quantiser of
-// "Grouped GEMM + dSwiGLU (SM100)", Step 3 (rcp_max = 1/448; E5 selects
-// E5M2 codes with rcp_max = 1/57344).
+// "Grouped GEMM + dSwiGLU (SM100)", Step 3.  DF is the code format:
+// DT_E4M3 (rcp_max = 1/448), DT_E5M2 (1/57344) or DT_E2M1 (1/6, two codes
+// per byte with the even column in the low nibble, so D and D_col rows are
+// N/2 bytes).
 //
 // A row's 32 values of block j sit in this lane (16) and lane ^ 32 (16); a
 // column's 32 values of block i sit in one register of the 32 lanes of a
@@ -319,12 +321,14 @@ __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, f32x16 
 // staged in the wave's LDS region and stored as whole rows, and the scale
 // bytes are written: SFD_row as one word per row (the wave's four 32-column
 // blocks are one K' group), SFD_col byte by byte.
-template <bool CLAMP, bool E5>
+template <bool CLAMP, int DF>
 __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x16 (&acc)[4][4],
                                                    uint8_t *stage, int64_t m0, int64_t n0, float alpha,
                                                    int wm, int wn, int lane, const float *prob_lds)
 {
-    typedef StageGeom<1, 4> G;
+    constexpr bool FP4 = DF == DT_E2M1;
+    constexpr int PB = FP4 ? 2 : 1;                   // codes per byte
+    typedef StageGeom<1, 4 / PB> G;
     const float nc = *p.norm_const;
     const int64_t n = p.n;
     const int64_t row_kt = (n / 32 + 3) / 4;          // SFD_row: K' over N
@@ -342,7 +346,7 @@ __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x1
     }
 
     uint8_t *sd = stage, *sdc = stage + 32 * G::RBP;
-    uint8_t *wd = sd + c32 * G::RBP + 4 * gh, *wdc = sdc + c32 * G::RBP + 4 * gh;
+    uint8_t *wd = sd + c32 * G::RBP + (4 / PB) * gh, *wdc = sdc + c32 * G::RBP + (4 / PB) * gh;
     const int64_t mt = qr / 128;
     static_for<4>([&](auto ii) {
         constexpr int i = decltype(ii)::value;
@@ -360,20 +364,28 @@ __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x1
             for (int v = 0; v < 16; ++v) rm = fmaxf(rm, fabsf(d[v]));
             rm = fmaxf(rm, xor32(rm));
             float rinv;
-            rword |= mx_scale_byte<E5>(rm, nc, rinv) << (8 * j);
+            rword |= mx_scale_byte<DF>(rm, nc, rinv) << (8 * j);
             // column blocks: 32 rows of each column over the half-wave
             float cinv[16], cm[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v) cm[v] = fabsf(d[v]);
             half_wave_max(cm);
-            const uint32_t byte = col_scales<E5>(cm, nc, cinv, lane);
+            const uint32_t byte = col_scales<DF>(cm, nc, cinv, lane);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                *reinterpret_cast<uint32_t *>(wd + 32 * j + 8 * q) =
-                    pack4_fp8<E5>(d[4 * q] * rinv, d[4 * q + 1] * rinv, d[4 * q + 2] * rinv, d[4 * q + 3] * rinv);
-                *reinterpret_cast<uint32_t *>(wdc + 32 * j + 8 * q) =
-                    pack4_fp8<E5>(d[4 * q] * cinv[4 * q], d[4 * q + 1] * cinv[4 * q + 1],
-                               d[4 * q + 2] * cinv[4 * q + 2], d[4 * q + 3] * cinv[4 * q + 3]);
+                if constexpr (FP4) {
+                    *reinterpret_cast<uint16_t *>(wd + 16 * j + 4 * q) = (uint16_t)pack4_e2m1(
+                        d[4 * q] * rinv, d[4 * q + 1] * rinv, d[4 * q + 2] * rinv, d[4 * q + 3] * rinv);
+                    *reinterpret_cast<uint16_t *>(wdc + 16 * j + 4 * q) = (uint16_t)pack4_e2m1(
+                        d[4 * q] * cinv[4 * q], d[4 * q + 1] * cinv[4 * q + 1], d[4 * q + 2] * cinv[4 * q + 2],
+                        d[4 * q + 3] * cinv[4 * q + 3]);
+                } else {
+                    *reinterpret_cast<uint32_t *>(wd + 32 * j + 8 * q) = pack4_fp8<DF == DT_E5M2>(
+                        d[4 * q] * rinv, d[4 * q + 1] * rinv, d[4 * q + 2] * rinv, d[4 * q + 3] * rinv);
+                    *reinterpret_cast<uint32_t *>(wdc + 32 * j + 8 * q) = pack4_fp8<DF == DT_E5M2>(
+                        d[4 * q] * cinv[4 * q], d[4 * q + 1] * cinv[4 * q + 1], d[4 * q + 2] * cinv[4 * q + 2],
+                        d[4 * q + 3] * cinv[4 * q + 3]);
+                }
             }
             // SFD_col byte i of column 32j + 8(c/4) + 4g + c%4 (lane c < 16: register c)
             const int64_t col = qc + 32 * j + 8 * (c32 >> 2) + 4 * gh + (c32 & 3);
@@ -382,9 +394,10 @@ __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x1
                 p.sfd_col[off + i] = (uint8_t)byte;
             }
         });
-        const uint32_t rb = (uint32_t)n;
-        stage_flush<1, 4>(sd, static_cast<char *>(p.d) + (qr + 32 * i) * n + qc, rb, 32, cols, lane);
-        stage_flush<1, 4>(sdc, static_cast<char *>(p.d_col) + (qr + 32 * i) * n + qc, rb, 32, cols, lane);
+        const uint32_t rb = (uint32_t)(n / PB);
+        stage_flush<1, 4 / PB>(sd, static_cast<char *>(p.d) + ((qr + 32 * i) * n + qc) / PB, rb, 32, cols / PB, lane);
+        stage_flush<1, 4 / PB>(sdc, static_cast<char *>(p.d_col) + ((qr + 32 * i) * n + qc) / PB, rb, 32, cols / PB,
+                               lane);
         // SFD_row word of row r; columns past N carry the scale of an all-zero block
         if (gh == 0 && cols > 0) {
             const int64_t r = m0 + acc_row(wm, i, lane);
@@ -455,13 +468,13 @@ __device__ __forceinline__ void epilogue_dswiglu_fp8(const GroupedParams &p, f32
             for (int v = 0; v < 16; ++v) rm = fmaxf(rm, fabsf(dv[v]));
             rm = fmaxf(rm, xor32(rm));
             float rinv;
-            rword[blk >> 2] |= mx_scale_byte<E5>(rm, nc, rinv) << (8 * (blk & 3));
+            rword[blk >> 2] |= mx_scale_byte<E5 ? DT_E5M2 : DT_E4M3>(rm, nc, rinv) << (8 * (blk & 3));
             // column direction: 32 rows of one D column over the half-wave
             float cinv[16], cm[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v) cm[v] = fabsf(dv[v]);
             half_wave_max(cm);
-            const uint32_t byte = col_scales<E5>(cm, nc, cinv, lane);
+            const uint32_t byte = col_scales<E5 ? DT_E5M2 : DT_E4M3>(cm, nc, cinv, lane);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 *reinterpret_cast<uint32_t *>(wd + 32 * blk + 8 * q) =
@@ -640,7 +653,7 @@ __global__ void __launch_bounds__(256) k_grouped(GroupedParams p)
     mainloop_pipe<F>(acc, ring, A, B, p.k);
 
     if constexpr (EPI == EPI_SRELU_FP8) {
-        epilogue_srelu_fp8<CLAMP, OT == DT_E5M2>(p, acc, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), m0, n0, alpha,
+        epilogue_srelu_fp8<CLAMP, OT == -1 ? DT_E4M3 : OT>(p, acc, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), m0, n0, alpha,
                                   wm, wn, lane, prob_lds);
     } else if constexpr (EPI == EPI_DSWIGLU_FP8) {
         epilogue_dswiglu_fp8<OT == DT_E5M2>(p, acc, wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), m0, n0, alpha * alpha,
@@ -721,6 +734,10 @@ hipError_t launch_grouped_srelu(const GroupedArgs &a, hipStream_t s)
     } else if (a.d_dtype == DT_E5M2) {
         if (a.fmt == FMT_E4M3) launch_srelu_variant<FMT_E4M3, EPI_SRELU_FP8, DT_E5M2>(p, grid, s);
         else if (a.fmt == FMT_E5M2) launch_srelu_variant<FMT_E5M2, EPI_SRELU_FP8, DT_E5M2>(p, grid, s);
+        else return hipErrorNotSupported;
+    } else if (a.d_dtype == DT_E2M1) {
+        if (a.fmt == FMT_E4M3) launch_srelu_variant<FMT_E4M3, EPI_SRELU_FP8, DT_E2M1>(p, grid, s);
+        else if (a.fmt == FMT_E5M2) launch_srelu_variant<FMT_E5M2, EPI_SRELU_FP8, DT_E2M1>(p, grid, s);
         else return hipErrorNotSupported;
     } else if (a.fmt == FMT_E4M3) {
         launch_srelu_variant<FMT_E4M3, EPI_SRELU>(p, grid, s);

@@ -146,16 +146,18 @@ int grouped_gemm(const void *a, const void *b, const int32_t *padded_offsets,
  *      amax   (L,) fp32, nullable: amax[g] = max |D| over expert g's rows
  *             (fp32 values before the cast); zero-filled by the library;
  *             an expert with no rows reports 0
- *  d_dtype == E4M3 or E5M2 (MXFP8 output, "Grouped GEMM + dSwiGLU (SM100)"
- *  Step 3 quantiser with rcp_max = 1/448 for E4M3 codes, 1/57344 for E5M2):
- *      d        (M,N) FP8 codes quantised in 32-wide blocks along N
+ *  d_dtype == E4M3, E5M2 or E2M1X2 (MX output, "Grouped GEMM + dSwiGLU
+ *  (SM100)" Step 3 quantiser with rcp_max = 1/448 for E4M3 codes, 1/57344
+ *  for E5M2 and 1/6 for E2M1; E2M1 codes are packed two per byte with the
+ *  even column in the low nibble, so d and d_col are (M, N/2) bytes):
+ *      d        (M,N) codes quantised in 32-wide blocks along N
  *      sfd_row  scale atoms over (M, N, 1)  (MN = M, "K" = N)
- *      d_col    (M,N) FP8 codes quantised in 32-tall blocks along M
+ *      d_col    (M,N) codes quantised in 32-tall blocks along M
  *      sfd_col  scale atoms over (N, M, 1)  (MN = N, "K" = M)
  *      norm_const (1,) fp32 device scalar, required
  *  tanh_clamp_scale: s; a value <= 0 means no clamp (the pages' None).
- *  ab_dtype in {E4M3, E5M2, E2M1X2}; sf_vec_size == 32.  FP8 D needs FP8
- *  (E4M3 or E5M2) A/B.
+ *  ab_dtype in {E4M3, E5M2, E2M1X2}; sf_vec_size == 32.  A quantised D
+ *  needs FP8 (E4M3 or E5M2) A/B.
  *  Sizes: M % 256 == 0, 1 <= L <= 1024, K % 32 == 0, N % 32 == 0.
  *  Rows at or past padded_offsets[L-1] are not written.
  */

@@ -106,10 +106,28 @@ def e4m3_ordered(codes: np.ndarray) -> np.ndarray:
     return np.where(c & 0x80, -mag, mag)
 
 
+def e2m1_ordered(codes: np.ndarray) -> np.ndarray:
+    """E2M1 nibbles (sign in bit 3) -> integers ordered like their values."""
+    c = codes.astype(np.int64)
+    return np.where(c & 8, -(c & 7), c & 7)
+
+
+def ordered(codes: np.ndarray, fmt: str) -> np.ndarray:
+    return e2m1_ordered(codes) if fmt == "e2m1" else e4m3_ordered(codes)
+
+
+def unpack_e2m1(raw: np.ndarray) -> np.ndarray:
+    """Bytes holding two E2M1 codes (even column in the low nibble) -> one
+    nibble per element along the last axis."""
+    out = np.empty(raw.shape[:-1] + (2 * raw.shape[-1],), dtype=np.uint8)
+    out[..., 0::2], out[..., 1::2] = raw & 15, raw >> 4
+    return out
+
+
 def check_quant(gpu_codes: np.ndarray, gpu_scales: np.ndarray, o_codes: np.ndarray,
                 o_scales: np.ndarray, sigma_near_pow2: np.ndarray | None = None, what="",
                 max_flip_frac: float = 1e-3, escape: np.ndarray | None = None,
-                max_escape_frac: float = 1e-2):
+                max_escape_frac: float = 1e-2, fmt: str = "e4m3"):
     """Scales identical (except blocks flagged near a power-of-two boundary),
     codes equal or one step apart on at most `max_flip_frac` of elements.
     `escape` marks elements whose code may lie further off because the value's
@@ -119,7 +137,7 @@ def check_quant(gpu_codes: np.ndarray, gpu_scales: np.ndarray, o_codes: np.ndarr
     if sigma_near_pow2 is not None:
         sc_bad &= ~sigma_near_pow2
     assert not sc_bad.any(), f"{what}: {int(sc_bad.sum())} scale bytes differ"
-    d = np.abs(e4m3_ordered(gpu_codes) - e4m3_ordered(o_codes))
+    d = np.abs(ordered(gpu_codes, fmt) - ordered(o_codes, fmt))
     far = d > 1
     esc = far & escape if escape is not None else np.zeros_like(far)
     assert not (far & ~esc).any(), f"{what}: code differs by {d[far & ~esc].max()} steps outside the error bound"
@@ -130,7 +148,7 @@ def check_quant(gpu_codes: np.ndarray, gpu_scales: np.ndarray, o_codes: np.ndarr
     return dict(flips=flips, escapes=n_esc, n=int(d.size))
 
 
-FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
+FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0, "e2m1": 6.0}
 _TORCH_FP8 = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
 
 
@@ -145,6 +163,8 @@ def code_window(d_o: np.ndarray, bound: np.ndarray, scales: np.ndarray, axis: in
 
     def enc(v):
         v = np.clip(v * inv, -fmax, fmax).astype(np.float32)
+        if fmt == "e2m1":   # no torch encode for E2M1: the oracle's (pinned) encoder
+            return e2m1_ordered(np.vectorize(lambda x: O.enc_e2m1(float(x)), otypes=[np.uint32])(v))
         return e4m3_ordered(torch.from_numpy(v).to(_TORCH_FP8[fmt]).view(torch.uint8).numpy())
 
     return enc(d_o - bound), enc(d_o + bound)
@@ -176,8 +196,9 @@ def check_mx_outputs(d_o: np.ndarray, bound: np.ndarray, gpu_row_codes, gpu_row_
                      gpu_col_codes, gpu_col_scales, norm_const=1.0, what="", fmt="e4m3"):
     """Dual-direction MX quantisation of oracle D (rows x cols, rows % 32 == 0)
     vs the GPU's codes / scales given in logical (row, block) order; fmt is
-    the code format ("e4m3" or "e5m2").  Sign-magnitude codes of both formats
-    are ordered like their values, so one code step is one integer step."""
+    the code format ("e4m3", "e5m2" or "e2m1", the last as one nibble per
+    element).  Sign-magnitude codes of each format are ordered like their
+    values, so one code step is one integer step."""
     rc, rs = O.mx_quant_rows(d_o, norm_const, fmt)
     cc, cs = O.mx_quant_cols(d_o, norm_const, fmt)
     fmax = FP8_MAX[fmt]
@@ -196,15 +217,15 @@ def check_mx_outputs(d_o: np.ndarray, bound: np.ndarray, gpu_row_codes, gpu_row_
     same_r = np.repeat(gpu_row_scales == rs, 32, axis=1)
     g_r = np.where(same_r, gpu_row_codes, rc)
     lo, hi = code_window(d_o, bound, rs, 1, norm_const, fmt)
-    o_r = e4m3_ordered(g_r)
+    o_r = ordered(g_r, fmt)
     out["row"] = check_quant(g_r, gpu_row_scales, rc, rs, r_near, what=what + " row",
-                             escape=(o_r >= lo - 1) & (o_r <= hi + 1))
+                             escape=(o_r >= lo - 1) & (o_r <= hi + 1), fmt=fmt)
     same_c = np.repeat(gpu_col_scales == cs, 32, axis=0)
     g_c = np.where(same_c, gpu_col_codes, cc)
     lo, hi = code_window(d_o, bound, cs, 0, norm_const, fmt)
-    o_c = e4m3_ordered(g_c)
+    o_c = ordered(g_c, fmt)
     out["col"] = check_quant(g_c, gpu_col_scales, cc, cs, c_near, what=what + " col",
-                             escape=(o_c >= lo - 1) & (o_c <= hi + 1))
+                             escape=(o_c >= lo - 1) & (o_c <= hi + 1), fmt=fmt)
     out["row_scale_mismatch_near_pow2"] = int((gpu_row_scales != rs).sum())
     out["col_scale_mismatch_near_pow2"] = int((gpu_col_scales != cs).sum())
     return out

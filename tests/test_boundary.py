@@ -83,6 +83,9 @@ def test_grouped_srelu_validation():
     assert vs(d_dtype=bsg.E5M2) == NULLPTR
     assert vs(d_dtype="e5m2", norm_const=P, d_col=P, sfd_row=P, sfd_col=P) == OK
     assert vs(d_dtype=bsg.E5M2, norm_const=P, d_col=P, sfd_row=P, sfd_col=P, ab_dtype="e2m1") == DTYPE
+    assert vs(d_dtype="e2m1", norm_const=P, d_col=P, sfd_row=P, sfd_col=P) == OK    # MXFP4 D
+    assert vs(d_dtype="e2m1", norm_const=P, d_col=P, sfd_row=P, sfd_col=P, ab_dtype="e2m1") == DTYPE
+    assert vs(d_dtype="e2m1") == NULLPTR
     assert vs(n=80) == SHAPE                             # N % 32
     assert vs(tanh_clamp_scale=float("nan")) == SHAPE
     assert vs(tanh_clamp_scale=0.0) == OK                # None

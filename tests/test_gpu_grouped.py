@@ -8,7 +8,7 @@ import torch
 import block_scaled_gemm_02_amd as bsg
 import oracle as O
 import workloads as W
-from parity import check_amax, check_float, check_mx_outputs, ceil_div, sf_slice, sum_bound
+from parity import check_amax, check_float, check_mx_outputs, ceil_div, sf_slice, sum_bound, unpack_e2m1
 
 pytestmark = pytest.mark.gpu
 SENT = -1536.0    # exactly representable in bf16, fp16 and fp32
@@ -162,8 +162,9 @@ def run_srelu_fp8(p, with_c=True, d_fmt="e4m3"):
     t = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in p.t.items()}
     m, n = s["m"], s["n"]
     c = torch.full((m, n), SENT, dtype=torch.bfloat16, device="cuda") if with_c else None
-    d = torch.full((m, n), 0xEE, dtype=torch.uint8, device="cuda")
-    d_col = torch.full((m, n), 0xEE, dtype=torch.uint8, device="cuda")
+    nb = n // 2 if d_fmt == "e2m1" else n             # E2M1: two codes per byte
+    d = torch.full((m, nb), 0xEE, dtype=torch.uint8, device="cuda")
+    d_col = torch.full((m, nb), 0xEE, dtype=torch.uint8, device="cuda")
     sfd_row = torch.full((W.sf_atom_bytes(m, n, 1),), 0xEE, dtype=torch.uint8, device="cuda")
     sfd_col = torch.full((W.sf_atom_bytes(n, m, 1),), 0xEE, dtype=torch.uint8, device="cuda")
     bsg.grouped_gemm_srelu(t["a"], t["b"], t["sfa"], t["sfb"], t["offsets"], t["alpha"], t["prob"],
@@ -192,6 +193,9 @@ FP8_CASES = [
     dict(sizes=[256, 0, 512, 256], n=320, k=192, s=32.0, nc=1.0, d="e5m2"),
     dict(sizes=[0, 256, 256], n=128, k=256, s=0.0, nc=4.0, d="e5m2"),
     dict(sizes=[512, 256], n=224, k=320, s=0.5, nc=1.0, fmt="e5m2", d="e5m2"),
+    # MXFP4 D: E2M1 codes two per byte (rcp_max 1/6)
+    dict(sizes=[256, 0, 512, 256], n=320, k=192, s=32.0, nc=1.0, d="e2m1"),
+    dict(sizes=[0, 256, 256], n=160, k=256, s=0.0, nc=4.0, fmt="e5m2", d="e2m1"),
 ]
 
 
@@ -216,8 +220,10 @@ def test_grouped_srelu_fp8_out_matches_oracle(case):
     check_float(c[:valid].cpu(), r["c"][:valid], bc[:valid], what="C")
     bd = d_bound(r["c"], bc, prob, s["tanh_clamp"])[:valid]
     rs, cs = gather_scales(sfd_row, sfd_col, 0, valid, m, n)
-    res = check_mx_outputs(r["d"][:valid], bd, d[:valid].cpu().numpy(), rs, d_col[:valid].cpu().numpy(),
-                           cs, case["nc"], what="D", fmt=d_fmt)
+    gd, gdc = d[:valid].cpu().numpy(), d_col[:valid].cpu().numpy()
+    if d_fmt == "e2m1":
+        gd, gdc = unpack_e2m1(gd), unpack_e2m1(gdc)
+    res = check_mx_outputs(r["d"][:valid], bd, gd, rs, gdc, cs, case["nc"], what="D", fmt=d_fmt)
     say(f"  {res}")
     assert torch.all(d[valid:] == 0xEE) and torch.all(d_col[valid:] == 0xEE)
 
