@@ -152,16 +152,17 @@ def test_grouped_dswiglu_fp4_inputs_bf16_or_f32_d_and_amax(case):
     assert torch.all(torch.isnan(d[valid:].float())) and torch.all(dprob[valid:] == 0)
 
 
-def test_grouped_dswiglu_full_size_sampled():
-    """The bench configuration (config-4 routing, N = 2048, K = 7168, MXFP8 D):
-    the first 128 rows (routed rows) of three experts against the oracle
-    computed for those rows alone (D codes and scale atoms in both
-    directions, dprob)."""
-    say("grouped_dswiglu full size")
+@pytest.mark.parametrize("d_fmt", ["e4m3", "e5m2"])
+def test_grouped_dswiglu_full_size_sampled(d_fmt):
+    """The bench configuration (config-4 routing, N = 2048, K = 7168, MXFP8 D
+    with E4M3 or E5M2 codes): the first 128 rows (routed rows) of three
+    experts against the oracle computed for those rows alone (D codes and
+    scale atoms in both directions, dprob)."""
+    say(f"grouped_dswiglu full size, D {d_fmt}")
     p = W.grouped_dswiglu_problem(28672, 32, 2048, 7168, "e4m3", seed=0, device="cuda")
     s = p.sizes
     m, n, k, L = s["m"], s["n"], s["k"], s["l"]
-    d, d_col, sfd_row, sfd_col, dprob = run_dswiglu(p)
+    d, d_col, sfd_row, sfd_col, dprob = run_dswiglu(p, d_fmt)
     t = p.t
     off = t["offsets"].cpu().numpy()
     m_t, n_t, k_t = ceil_div(m, 128), ceil_div(n, 128), ceil_div(k, 128)
@@ -180,7 +181,7 @@ def test_grouped_dswiglu_full_size_sampled():
         bd, b_dp = bounds(p, r, r0, r0 + 128)
         rs, cs = gather_scales(sfd_row, sfd_col, r0, r0 + 128, m, 2 * n)
         res = check_mx_outputs(r["d"], bd, d[r0:r0 + 128].cpu().numpy(), rs, d_col[r0:r0 + 128].cpu().numpy(),
-                               cs, 1.0, what=f"D e{g}")
+                               cs, 1.0, what=f"D e{g}", fmt=d_fmt)
         say(f"  {res}")
         gdp = dprob[r0:r0 + 128].cpu().double().numpy()
         assert np.all(np.abs(gdp - r["dprob"]) <= b_dp)

@@ -228,13 +228,15 @@ def test_grouped_srelu_fp8_out_matches_oracle(case):
     assert torch.all(d[valid:] == 0xEE) and torch.all(d_col[valid:] == 0xEE)
 
 
-def test_grouped_srelu_fp8_out_full_size_sampled():
-    """Full grouped MXFP8 + sReLU workload with FP8 D: sampled 128-row panels."""
-    say("grouped_srelu fp8 out full size")
+@pytest.mark.parametrize("d_fmt", ["e4m3", "e5m2", "e2m1"])
+def test_grouped_srelu_fp8_out_full_size_sampled(d_fmt):
+    """Full grouped MXFP8 + sReLU workload with quantised D (E4M3, E5M2 or
+    E2M1 codes), as bench.py times it: sampled 128-row panels."""
+    say(f"grouped_srelu quantised D ({d_fmt}) full size")
     p = W.moe_mxfp8_srelu(device="cuda", d_dtype="e4m3")
     s = p.sizes
     m, n, k, L = s["m"], s["n"], s["k"], s["l"]
-    c, d, d_col, sfd_row, sfd_col = run_srelu_fp8(p, with_c=False)
+    c, d, d_col, sfd_row, sfd_col = run_srelu_fp8(p, with_c=False, d_fmt=d_fmt)
     t = p.t
     off = t["offsets"].cpu().numpy()
     m_t, n_t, k_t = ceil_div(m, 128), ceil_div(n, 128), ceil_div(k, 128)
@@ -253,8 +255,10 @@ def test_grouped_srelu_fp8_out_full_size_sampled():
         bc = sum_bound(sub["sabs"], k, bmax=sub["bmax"])
         bd = d_bound(sub["c"], bc, prob, 32.0)
         rs, cs = gather_scales(sfd_row, sfd_col, r0, r0 + 128, m, n)
-        res = check_mx_outputs(sub["d"], bd, d[r0:r0 + 128].cpu().numpy(), rs,
-                               d_col[r0:r0 + 128].cpu().numpy(), cs, 1.0, what=f"e{g}")
+        gd, gdc = d[r0:r0 + 128].cpu().numpy(), d_col[r0:r0 + 128].cpu().numpy()
+        if d_fmt == "e2m1":
+            gd, gdc = unpack_e2m1(gd), unpack_e2m1(gdc)
+        res = check_mx_outputs(sub["d"], bd, gd, rs, gdc, cs, 1.0, what=f"e{g}", fmt=d_fmt)
         say(f"  {res}")
 
 
