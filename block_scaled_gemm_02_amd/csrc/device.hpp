@@ -814,23 +814,18 @@ __device__ __forceinline__ void store_quadrant(uint8_t *reg, char *dst, char *ds
     });
 }
 
-// E2M1 code of x: round to nearest even, saturating at 6.  The magnitude
-// code is the number of rounding thresholds |x| passes, the thresholds being
-// the midpoints between the eight magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.  At
-// a midpoint the code with an even mantissa bit wins, so the thresholds
-// below an even code are inclusive and the others strict.  Sign in bit 3.
-__device__ __forceinline__ uint32_t e2m1_code(float x)
-{
-    const float a = fabsf(x);
-    const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
-    return c | ((__float_as_uint(x) >> 28) & 8u);
-}
-
-// Four E2M1 codes, x0 in the lowest nibble.
+// Four E2M1 codes, x0 in the lowest nibble: round to nearest even,
+// saturating at +-6, sign in bit 3 of each nibble.  gfx950's packed FP4
+// conversion with a unit scale does exactly this (the low byte takes the
+// first value in its low nibble; the rest of the word is left at the
+// given old value, zero here); its results equal a nearest-even,
+// saturating E2M1 encode at every midpoint between codes, at the fp32
+// neighbours of each midpoint, past 6 up to 1e30, and at signed zeros.
 __device__ __forceinline__ uint32_t pack4_e2m1(float x0, float x1, float x2, float x3)
 {
-    return e2m1_code(x0) | (e2m1_code(x1) << 4) | (e2m1_code(x2) << 8) | (e2m1_code(x3) << 12);
+    const uint32_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x0, x1, 1.0f, 0);
+    const uint32_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x2, x3, 1.0f, 0);
+    return (lo & 0xFFu) | ((hi & 0xFFu) << 8);
 }
 
 // store_quadrant for packed E2M1 output: two codes per byte, the even
@@ -851,11 +846,11 @@ __device__ __forceinline__ void store_quadrant_fp4(uint8_t *reg, char *dst, uint
             constexpr int j = decltype(jj)::value;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint32_t e0 = e2m1_code(value(i, j, 4 * q, acc[i][j][4 * q]));
-                const uint32_t e1 = e2m1_code(value(i, j, 4 * q + 1, acc[i][j][4 * q + 1]));
-                const uint32_t e2 = e2m1_code(value(i, j, 4 * q + 2, acc[i][j][4 * q + 2]));
-                const uint32_t e3 = e2m1_code(value(i, j, 4 * q + 3, acc[i][j][4 * q + 3]));
-                *reinterpret_cast<uint16_t *>(wrow + 16 * j + 4 * q) = (uint16_t)(e0 | (e1 << 4) | (e2 << 8) | (e3 << 12));
+                const float x0 = value(i, j, 4 * q, acc[i][j][4 * q]);
+                const float x1 = value(i, j, 4 * q + 1, acc[i][j][4 * q + 1]);
+                const float x2 = value(i, j, 4 * q + 2, acc[i][j][4 * q + 2]);
+                const float x3 = value(i, j, 4 * q + 3, acc[i][j][4 * q + 3]);
+                *reinterpret_cast<uint16_t *>(wrow + 16 * j + 4 * q) = (uint16_t)pack4_e2m1(x0, x1, x2, x3);
             }
         });
         stage_flush<1, NB / 2>(reg, dst + (uint32_t)(32 * i) * row_bytes, row_bytes, rows_valid - 32 * i,

@@ -232,3 +232,47 @@ def test_gemm_amax_fp4_c_with_fp4_inputs(case):
     say(f"  one-step flips {int((step == 1).sum())}/{step.size}, saturated {sat}, "
         f"codes used {len(np.unique(g))}")
     check_amax(float(amax.item()), oamax, float(bound.ravel()[np.argmax(np.abs(oc))]))
+
+
+def test_gemm_amax_fp4_c_rounding_ties_exact():
+    """Packed E2M1 C on every rounding tie and every saturation case, bit for
+    bit.  B's two K=0,1 codes run over all 16 x 16 pairs (one per column) with
+    the B scale 2^-1; A's rows pick b0 / 2, (b0 + b1) / 2, b0 + b1 (A scale 2)
+    and (b1 - b0) / 2.  Every C is exact in fp32 and includes all seven
+    midpoints between E2M1 magnitudes in both signs and values past 6, so the
+    codes must equal the oracle encoder's (ties to even, saturating)."""
+    say("gemm_amax FP4 C rounding ties")
+    m, n, k, l = 32, 256, 64, 1
+    a = np.zeros((m, k), np.uint8)
+    a[0, 0] = 0x2                                  # 1.0
+    a[1, 0] = a[1, 1] = 0x2
+    a[2, 0] = a[2, 1] = 0x2
+    a[3, 0], a[3, 1] = 0xA, 0x2                    # -1.0, 1.0
+    b = np.zeros((n, k), np.uint8)
+    b[:, 0], b[:, 1] = np.arange(n) // 16, np.arange(n) % 16
+
+    def pack(x):
+        return np.ascontiguousarray(x[:, 0::2] | (x[:, 1::2] << 4)).astype(np.uint8)
+
+    sfa = np.full(W.sf_atom_bytes(m, k, l), 127, np.uint8)
+    sfb = np.full(W.sf_atom_bytes(n, k, l), 126, np.uint8)
+    sfa[O.sf_offset_grid(2, 3, k // 32, 0, m, k // 32)] = 128
+    t = dict(a=torch.from_numpy(pack(a)), b=torch.from_numpy(pack(b)), sfa=torch.from_numpy(sfa),
+             sfb=torch.from_numpy(sfb))
+    oc, _, oamax = O.gemm_amax_full(t["a"], t["b"], t["sfa"], t["sfb"], m, n, k, l, "e2m1")
+    vals = oc[0, :4].ravel()
+    for mid in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0):
+        assert np.any(vals == mid) and np.any(vals == -mid), mid
+    assert np.any(vals > 6) and np.any(vals < -6)
+    g = {kk: v.cuda() for kk, v in t.items()}
+    c = torch.full((l, m, n // 2), 0xEE, dtype=torch.uint8, device="cuda")
+    amax = torch.full((1,), -7.0, device="cuda")
+    bsg.gemm_amax(g["a"], g["b"], g["sfa"], g["sfb"], c, amax, m, n, k, l, "e2m1", c_dtype="e2m1")
+    torch.cuda.synchronize()
+    raw = c.cpu().numpy()
+    nib = np.empty((l, m, n), np.uint8)
+    nib[..., 0::2], nib[..., 1::2] = raw & 15, raw >> 4
+    want = np.array([O.enc_e2m1(float(v)) for v in oc.ravel()], np.uint8).reshape(oc.shape)
+    same = _e2m1_ordered(nib) == _e2m1_ordered(want)          # +0 and -0 compare equal
+    assert same.all(), f"{int((~same).sum())} codes differ, first at {np.argwhere(~same)[0]}"
+    assert amax.item() == oamax
