@@ -274,6 +274,8 @@ static int validate_srelu(const void *a, const void *b, const uint8_t *sfa, cons
     if (k % 32) return fail(BSG_ERR_SHAPE, "K=%lld must be a multiple of sf_vec_size 32", (long long)k);
     if (n % 32) return fail(BSG_ERR_SHAPE, "N=%lld must be a multiple of 32", (long long)n);
     if (!(tanh_clamp_scale == tanh_clamp_scale)) return fail(BSG_ERR_SHAPE, "tanh_clamp_scale is NaN");
+    if (c && (c_dtype == BSG_E4M3 || c_dtype == BSG_E5M2 || c_dtype == BSG_E2M1X2))
+        return fail(BSG_ERR_UNSUPPORTED, "FP8 / FP4 C is not built (F32, F16 and BF16 are)");
     if (c && !is_float_out(c_dtype)) return fail(BSG_ERR_DTYPE, "C dtype must be F32, F16 or BF16");
     // quantised D: E4M3 / E5M2 codes, or E2M1 codes two per byte
     const bool fp8_out = d_dtype == BSG_E4M3 || d_dtype == BSG_E5M2 || d_dtype == BSG_E2M1X2;

@@ -86,6 +86,8 @@ def test_grouped_srelu_validation():
     assert vs(d_dtype="e2m1", norm_const=P, d_col=P, sfd_row=P, sfd_col=P) == OK    # MXFP4 D
     assert vs(d_dtype="e2m1", norm_const=P, d_col=P, sfd_row=P, sfd_col=P, ab_dtype="e2m1") == DTYPE
     assert vs(d_dtype="e2m1") == NULLPTR
+    assert vs(c_dtype=bsg.E4M3) == UNSUP                     # FP8 C of the sReLU op not built
+    assert vs(c_dtype=99) == DTYPE
     assert vs(n=80) == SHAPE                             # N % 32
     assert vs(tanh_clamp_scale=float("nan")) == SHAPE
     assert vs(tanh_clamp_scale=0.0) == OK                # None
