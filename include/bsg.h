@@ -140,7 +140,7 @@ int grouped_gemm(const void *a, const void *b, const int32_t *padded_offsets,
  *  b, sfb          (N,K,L) codes [L][N][K]; scale atoms over (N, K, L)
  *  padded_offsets, alpha, prob   as for grouped_gemm
  *  c               (M,N) pre-activation alpha*acc, nullable; c_dtype in
- *                  {BF16, F16, F32}
+ *                  {BF16, F16, F32} (FP8 / FP4 C return UNSUPPORTED)
  *  d_dtype in {BF16, F16, F32}:
  *      d      (M,N) D, RNE cast;  d_col: nullable copy of d
  *      amax   (L,) fp32, nullable: amax[g] = max |D| over expert g's rows
