@@ -140,7 +140,7 @@ def wl_moe_dswiglu():
     import torch
     import block_scaled_gemm_02_amd as bsg
     import workloads as W
-    # config-4 routing (32 experts, Zipf(1.1), valid_m ~ 32768) with K = 7168 and
+    # the grouped sReLU workload's routing (32 experts, Zipf(1.1), valid_m ~ 32768) with K = 7168 and
     # N = 2048: ref is (valid_m, 2048), C and D are (valid_m, 4096)
     p = W.grouped_dswiglu_problem(28672, 32, 2048, 7168, "e4m3", seed=0, device="cuda")
     s, t = p.sizes, p.t

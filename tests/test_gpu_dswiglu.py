@@ -154,10 +154,10 @@ def test_grouped_dswiglu_fp4_inputs_bf16_or_f32_d_and_amax(case):
 
 @pytest.mark.parametrize("d_fmt", ["e4m3", "e5m2"])
 def test_grouped_dswiglu_full_size_sampled(d_fmt):
-    """The bench configuration (config-4 routing, N = 2048, K = 7168, MXFP8 D
-    with E4M3 or E5M2 codes): the first 128 rows (routed rows) of three
-    experts against the oracle computed for those rows alone (D codes and
-    scale atoms in both directions, dprob)."""
+    """The bench configuration (28672 tokens over 32 experts, Zipf(1.1)
+    routing, N = 2048, K = 7168, MXFP8 D with E4M3 or E5M2 codes): the first
+    128 rows (routed rows) of three experts against the oracle computed for
+    those rows alone (D codes and scale atoms in both directions, dprob)."""
     say(f"grouped_dswiglu full size, D {d_fmt}")
     p = W.grouped_dswiglu_problem(28672, 32, 2048, 7168, "e4m3", seed=0, device="cuda")
     s = p.sizes
