@@ -100,6 +100,19 @@ def test_proj_rope_special_tables(cs):
     oracle_check(p, qr, sr, qc, sc, 0, 256, f"tables {cs}")
 
 
+@pytest.mark.parametrize("in_dtype", ["bf16", "e4m3"])
+def test_proj_rope_independent_angle_tables(in_dtype):
+    """cos/sin from independent angles per (token, column): the two halves of
+    a row differ and every row differs, so a kernel that read column j for
+    output 32 + j, one fixed column, or a row relative to the tile would
+    disagree with the oracle (whose column and row use is pinned on the CPU)."""
+    say(f"proj_rope independent-angle tables ({in_dtype})")
+    p = W.proj_rope_problem(384, 256 if in_dtype == "bf16" else 128, 2, seed=9, in_dtype=in_dtype)
+    p.t["cos"], p.t["sin"], _ = W.rope_tables_random(384, 64, seed=10)
+    qr, sr, qc, sc = run_proj(p)
+    oracle_check(p, qr, sr, qc, sc, 0, 384, f"random tables {in_dtype}")
+
+
 def test_proj_rope_full_size_sampled():
     """x (4096,1536), 128 heads x 192: sampled 128-token panels vs the oracle."""
     say("proj_rope full size")

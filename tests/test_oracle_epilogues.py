@@ -134,6 +134,54 @@ def test_rope_weight_layouts_agree_and_norm_preserved_at_angle0():
     assert torch.all(cos[0] == 1) and torch.all(sin[0] == 0)
 
 
+def test_rope_tables_by_column_and_absolute_row():
+    """Every rotary output against the complex product (a_j + i b_j) e^(i theta)
+    of the plain projection's pair (2j, 2j+1), with theta from the test's own
+    angle array: the real part (output j) takes table column j, the imaginary
+    part (output 32 + j) column 32 + j, and rows [t0, t1) read table row t, not
+    t - t0.  The angles are independent per column and per row, so reading
+    column j where 32 + j is meant, one fixed column, or a row relative to t0
+    changes the result."""
+    tokens, q_lora, heads, t0 = 12, 64, 2, 5
+    p = W.proj_rope_problem(tokens, q_lora, heads, 192, 64, seed=11)
+    cos, sin, ang = W.rope_tables_random(tokens, 64, seed=12)
+    assert not np.array_equal(ang[:, :32], ang[:, 32:])
+    y, _ = O.proj_rope(O.bits16(p.t["x"]), O.bits16(p.t["w"]), O.bits16(cos), O.bits16(sin),
+                       tokens, q_lora, heads, 192, 64, 1, t0, tokens)
+    plain = p.t["x"].double().numpy() @ p.t["w"].double().numpy().T
+    plain = plain.reshape(tokens, heads, 192)[t0:]
+    y = y.reshape(tokens - t0, heads, 192)
+    # the table entries the kernel sees are the bf16 values of cos/sin theta
+    e = (cos.double().numpy() + 1j * sin.double().numpy())[t0:, None, :]   # (rows, 1, 64)
+    z = plain[..., 128::2] + 1j * plain[..., 129::2]                        # (rows, heads, 32)
+    np.testing.assert_allclose(y[..., 128:160], (z * e[..., :32]).real, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(y[..., 160:], (z * e[..., 32:]).imag, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(y[..., :128], plain[..., :128], rtol=1e-13, atol=1e-13)
+    # the angles themselves: within bf16 rounding of cos/sin, the same products
+    ez = np.exp(1j * ang)[t0:, None, :]
+    np.testing.assert_allclose(y[..., 128:160], (z * ez[..., :32]).real, atol=2 ** -7 * np.abs(z).max())
+    np.testing.assert_allclose(y[..., 160:], (z * ez[..., 32:]).imag, atol=2 ** -7 * np.abs(z).max())
+
+
+def test_rope_standard_tables_rotate_pairs_by_the_position_angle():
+    """With equal halves (the generated tables) each output pair (j, 32 + j) is
+    the rotation of (a_j, b_j) by theta = t * 10000^(-j/32): its norm is kept
+    to bf16 accuracy of cos/sin, and it matches (a + i b) e^(i theta)."""
+    tokens, q_lora, heads = 64, 64, 2
+    p = W.proj_rope_problem(tokens, q_lora, heads, 192, 64, seed=13)
+    y, _ = O.proj_rope(O.bits16(p.t["x"]), O.bits16(p.t["w"]), O.bits16(p.t["cos"]),
+                       O.bits16(p.t["sin"]), tokens, q_lora, heads, 192, 64, 1)
+    plain = (p.t["x"].double().numpy() @ p.t["w"].double().numpy().T).reshape(tokens, heads, 192)
+    y = y.reshape(tokens, heads, 192)
+    theta = np.arange(tokens)[:, None] * 10000.0 ** (-np.arange(32) / 32.0)
+    z = plain[..., 128::2] + 1j * plain[..., 129::2]
+    rot = z * np.exp(1j * theta)[:, None, :]
+    out = y[..., 128:160] + 1j * y[..., 160:]
+    tol = 2 ** -7 * np.abs(z)
+    assert np.all(np.abs(out - rot) <= tol + 1e-12)
+    assert np.all(np.abs(np.abs(out) - np.abs(z)) <= tol + 1e-12)
+
+
 def test_quantiser_power_of_two_closed_forms():
     # block max exactly 448 * 2^j -> scale byte 127 + j and codes = RNE(D / 2^j)
     rng = np.random.default_rng(5)

@@ -280,6 +280,18 @@ def rope_tables(tokens: int, rope_dim: int = 64, base: float = 10000.0, device="
     return cos.to(device).contiguous(), sin.to(device).contiguous()
 
 
+def rope_tables_random(tokens: int, rope_dim: int = 64, seed: int = 0, device="cpu"):
+    """bf16 cos/sin (tokens, rope_dim) of independent angles U(-pi, pi) per
+    (token, column), returned with the fp64 angles: unlike rope_tables, the
+    two halves of a row differ and every row differs, so a table read from
+    the wrong column or the wrong row gives different values."""
+    rng = np.random.default_rng(seed)
+    ang = rng.uniform(-np.pi, np.pi, size=(tokens, rope_dim))
+    cos = torch.from_numpy(np.cos(ang)).to(torch.bfloat16)
+    sin = torch.from_numpy(np.sin(ang)).to(torch.bfloat16)
+    return cos.to(device).contiguous(), sin.to(device).contiguous(), ang
+
+
 def proj_rope_problem(tokens: int, q_lora: int, heads: int = 128, head_dim: int = 192,
                       qk_rope: int = 64, *, seed: int = 0, device="cpu",
                       w_out_in: bool = True, in_dtype: str = "bf16") -> Problem:
