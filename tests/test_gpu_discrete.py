@@ -11,7 +11,7 @@ import torch
 import block_scaled_gemm_02_amd as bsg
 import oracle as O
 import workloads as W
-from parity import check_float, ceil_div, sf_slice, sum_bound
+from parity import check_float, check_mx_outputs, ceil_div, d_bound, gather_scales, sf_slice, sum_bound
 
 pytestmark = pytest.mark.gpu
 SENT = -1536.0
@@ -90,12 +90,20 @@ def test_srelu_discrete_matches_oracle_and_dense(case):
     ref = srelu_call(t, s, None, None, case["c"], None if fp8 else case["d"], fp8)
     for x, y in zip(got, ref):
         assert torch.equal(x, y)
-    # and C against the oracle
+    # and C and D against the oracle
     r = O.grouped_srelu(p.t["a"], p.t["b"], p.t["sfa"], p.t["sfb"], off, p.t["alpha"], p.t["prob"],
                         m, n, k, L, s["fmt"], s["tanh_clamp"])
     valid = s["valid_m"]
     bc = sum_bound(r["sabs"], k, bmax=r["bmax"])
     say(f"  C {check_float(got[0][:valid].cpu(), r['c'][:valid], bc[:valid], what='C')}")
+    bd = d_bound(r["c"], bc, p.t["prob"].double().numpy(), s["tanh_clamp"])[:valid]
+    if fp8:
+        rs, cs = gather_scales(got[3], got[4], 0, valid, m, n)
+        res = check_mx_outputs(r["d"][:valid], bd, got[1][:valid].cpu().numpy(), rs,
+                               got[2][:valid].cpu().numpy(), cs, 1.0, what="D")
+        say(f"  D {res}")
+    else:
+        say(f"  D {check_float(got[1][:valid].cpu(), r['d'][:valid], bd, what='D')}")
     del keep
 
 
@@ -136,13 +144,15 @@ def test_bf16_discrete_matches_oracle_and_dense(case):
     valid = s["valid_m"]
     bnd = sum_bound(r["sabs"], k) + 1e-7 * np.abs(r["c"])
     say(f"  C {check_float(outs[0][0][:valid].cpu(), r['c'][:valid], bnd[:valid], what='C')}")
+    dbnd = bnd * (1 if bias is not None else p.t["prob"].double().numpy()[:, None])
+    say(f"  D {check_float(outs[0][1][:valid].cpu(), r['d'][:valid], dbnd[:valid], what='D')}")
     del keep
 
 
 def test_srelu_discrete_full_size_equals_dense():
     """The grouped MXFP8 + sReLU workload (32 experts, N=4096, K=7168) with
-    per-expert weight allocations: identical outputs to the dense call, whose
-    parity with the oracle the sampled full-size test checks."""
+    per-expert weight allocations: identical outputs to the dense call, and
+    the first 256-row tile of the most popular expert against the oracle."""
     say("grouped_srelu discrete full size")
     p = W.moe_mxfp8_srelu(device="cuda")
     s = p.sizes
@@ -153,4 +163,14 @@ def test_srelu_discrete_full_size_equals_dense():
     ref = srelu_call(t, s, None, None, torch.bfloat16, torch.bfloat16, False)
     for x, y in zip(got, ref):
         assert torch.equal(x, y)
+    m = s["m"]
+    m_t, n_t, k_t = ceil_div(m, 128), ceil_div(n, 128), ceil_div(k, 128)
+    say("  oracle expert 0 rows 0..255")
+    sub = O.grouped_srelu(t["a"][:256].cpu(), t["b"][0:1].cpu(), sf_slice(t["sfa"], 0, m_t, k_t, 0, 2).cpu(),
+                          sf_slice(t["sfb"], 0, n_t, k_t, 0, n_t).cpu(), np.array([256], np.int32),
+                          t["alpha"][0:1].cpu(), t["prob"][:256].cpu(), 256, n, k, 1, "e4m3", 32.0)
+    bc = sum_bound(sub["sabs"], k, bmax=sub["bmax"])
+    bd = d_bound(sub["c"], bc, t["prob"][:256].double().cpu().numpy(), 32.0)
+    say(f"  C {check_float(got[0][:256].cpu(), sub['c'], bc, what='C')}")
+    say(f"  D {check_float(got[1][:256].cpu(), sub['d'], bd, what='D')}")
     del keep

@@ -156,8 +156,9 @@ def test_grouped_dswiglu_fp4_inputs_bf16_or_f32_d_and_amax(case):
 def test_grouped_dswiglu_full_size_sampled(d_fmt):
     """The bench configuration (28672 tokens over 32 experts, Zipf(1.1)
     routing, N = 2048, K = 7168, MXFP8 D with E4M3 or E5M2 codes): the first
-    128 rows (routed rows) of three experts against the oracle computed for
-    those rows alone (D codes and scale atoms in both directions, dprob)."""
+    whole 256-row tile (both wave rows) of three experts against the oracle
+    computed for those rows alone (D codes and scale atoms in both
+    directions, dprob)."""
     say(f"grouped_dswiglu full size, D {d_fmt}")
     p = W.grouped_dswiglu_problem(28672, 32, 2048, 7168, "e4m3", seed=0, device="cuda")
     s = p.sizes
@@ -171,17 +172,17 @@ def test_grouped_dswiglu_full_size_sampled(d_fmt):
     for g in (nonempty[0], nonempty[len(nonempty) // 2], nonempty[-1]):
         r0 = int(begins[g])
         assert float(t["prob"][r0].item()) > 0.0           # a routed row
-        say(f"  oracle expert {g} rows {r0}..{r0 + 127}")
-        sfa = t["sfa"][(r0 // 128) * k_t * 512:(r0 // 128 + 1) * k_t * 512]
+        say(f"  oracle expert {g} rows {r0}..{r0 + 255}")
+        sfa = t["sfa"][(r0 // 128) * k_t * 512:(r0 // 128 + 2) * k_t * 512]
         sfb = t["sfb"][g * n_t * k_t * 512:(g + 1) * n_t * k_t * 512]
-        r = O.grouped_dswiglu(t["a"][r0:r0 + 128].cpu(), t["b"][g:g + 1].cpu(), sfa.cpu(), sfb.cpu(),
-                              np.array([128], np.int32), t["alpha"][g:g + 1].cpu(), t["beta"][g:g + 1].cpu(),
-                              t["prob"][r0:r0 + 128].cpu(), O.bits16(t["c"][r0:r0 + 128].cpu()), 128, n, k, 1,
+        r = O.grouped_dswiglu(t["a"][r0:r0 + 256].cpu(), t["b"][g:g + 1].cpu(), sfa.cpu(), sfb.cpu(),
+                              np.array([256], np.int32), t["alpha"][g:g + 1].cpu(), t["beta"][g:g + 1].cpu(),
+                              t["prob"][r0:r0 + 256].cpu(), O.bits16(t["c"][r0:r0 + 256].cpu()), 256, n, k, 1,
                               "e4m3")
-        bd, b_dp = bounds(p, r, r0, r0 + 128)
-        rs, cs = gather_scales(sfd_row, sfd_col, r0, r0 + 128, m, 2 * n)
-        res = check_mx_outputs(r["d"], bd, d[r0:r0 + 128].cpu().numpy(), rs, d_col[r0:r0 + 128].cpu().numpy(),
+        bd, b_dp = bounds(p, r, r0, r0 + 256)
+        rs, cs = gather_scales(sfd_row, sfd_col, r0, r0 + 256, m, 2 * n)
+        res = check_mx_outputs(r["d"], bd, d[r0:r0 + 256].cpu().numpy(), rs, d_col[r0:r0 + 256].cpu().numpy(),
                                cs, 1.0, what=f"D e{g}", fmt=d_fmt)
         say(f"  {res}")
-        gdp = dprob[r0:r0 + 128].cpu().double().numpy()
+        gdp = dprob[r0:r0 + 256].cpu().double().numpy()
         assert np.all(np.abs(gdp - r["dprob"]) <= b_dp)

@@ -8,7 +8,8 @@ import torch
 import block_scaled_gemm_02_amd as bsg
 import oracle as O
 import workloads as W
-from parity import check_amax, check_float, check_mx_outputs, ceil_div, sf_slice, sum_bound, unpack_e2m1
+from parity import (check_amax, check_float, check_mx_outputs, ceil_div, d_bound, gather_scales, sf_slice,
+                    sum_bound, unpack_e2m1)
 
 pytestmark = pytest.mark.gpu
 SENT = -1536.0    # exactly representable in bf16, fp16 and fp32
@@ -16,15 +17,6 @@ SENT = -1536.0    # exactly representable in bf16, fp16 and fp32
 
 def say(msg):
     print(msg, flush=True)
-
-
-def d_bound(o_c, bc, prob, s):
-    """Escape bound for D = prob * f(C) given C's bound bc: |f'| <= 2|C| + bc,
-    plus the clamp's tanh error (absolute 1e-6 on t, i.e. 2 s^2 1e-6 on f)."""
-    b = prob[:, None] * (2 * np.abs(o_c) + bc) * bc
-    if s > 0:
-        b = b + prob[:, None] * 2 * s * s * 1e-6
-    return b
 
 
 def run_srelu(p, c_dtype=torch.bfloat16, d_dtype=torch.bfloat16, with_c=True, with_dcol=True):
@@ -109,10 +101,31 @@ def test_grouped_srelu_routing_bit_exact():
     assert np.array_equal(c.cpu().numpy(), np.broadcast_to(want[:, None], (m, n)))
 
 
-def test_grouped_srelu_full_size_sampled():
-    """32 experts, N=4096, K=7168, valid_m ~ 32768, s = 32: sampled row panels."""
-    say("grouped_srelu full size")
-    p = W.moe_mxfp8_srelu(device="cuda")
+def oracle_tile(t, g, r0, rows, m, n, k, fmt, s=32.0):
+    """The oracle on rows [r0, r0 + rows) of the full-size problem, all of
+    them routed to expert g (rows is a multiple of 128)."""
+    m_t, n_t, k_t = ceil_div(m, 128), ceil_div(n, 128), ceil_div(k, 128)
+    return O.grouped_srelu(t["a"][r0:r0 + rows].cpu(), t["b"][g:g + 1].cpu(),
+                           sf_slice(t["sfa"], 0, m_t, k_t, r0 // 128, (r0 + rows) // 128).cpu(),
+                           sf_slice(t["sfb"], g, n_t, k_t, 0, n_t).cpu(),
+                           np.array([rows], np.int32), t["alpha"][g:g + 1].cpu(),
+                           t["prob"][r0:r0 + rows].cpu(), rows, n, k, 1, fmt, s)
+
+
+def sampled_experts(off, L):
+    """The first, middle and last non-empty experts with their begins."""
+    begins = np.concatenate([[0], off[:-1]])
+    nonempty = [g for g in range(L) if off[g] > begins[g]]
+    return begins, [nonempty[0], nonempty[len(nonempty) // 2], nonempty[-1]]
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_grouped_srelu_full_size_sampled(fmt):
+    """32 experts, N=4096, K=7168, valid_m ~ 32768, s = 32, with MXFP8 (E4M3)
+    or MXFP4 (E2M1) operands as bench.py times them: the first whole 256-row
+    tile (both wave rows) of three experts against the oracle."""
+    say(f"grouped_srelu full size ({fmt})")
+    p = W.moe_mxfp8_srelu(device="cuda", fmt=fmt)
     s = p.sizes
     m, n, k, L = s["m"], s["n"], s["k"], s["l"]
     c = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
@@ -120,29 +133,23 @@ def test_grouped_srelu_full_size_sampled():
     amax = torch.empty(L, device="cuda")
     t = p.t
     bsg.grouped_gemm_srelu(t["a"], t["b"], t["sfa"], t["sfb"], t["offsets"], t["alpha"], t["prob"],
-                           None, c, d, None, None, None, amax, m, n, k, L, "e4m3",
+                           None, c, d, None, None, None, amax, m, n, k, L, fmt,
                            c_dtype=torch.bfloat16, d_dtype=torch.bfloat16, tanh_clamp_scale=32.0)
     torch.cuda.synchronize()
     off = t["offsets"].cpu().numpy()
-    m_t, n_t, k_t = ceil_div(m, 128), ceil_div(n, 128), ceil_div(k, 128)
-    begins = np.concatenate([[0], off[:-1]])
-    nonempty = [g for g in range(L) if off[g] > begins[g]]
-    for g in (nonempty[0], nonempty[len(nonempty) // 2], nonempty[-1]):
-        r0 = int(begins[g])                        # first 128 rows of expert g: routed rows
-        assert O.expert_of_row(off, L, r0) == g and float(t["prob"][r0].item()) > 0.0
-        say(f"  oracle expert {g} rows {r0}..{r0 + 127}")
-        sub = O.grouped_srelu(t["a"][r0:r0 + 128].cpu(), t["b"][g:g + 1].cpu(),
-                              sf_slice(t["sfa"], 0, m_t, k_t, r0 // 128, r0 // 128 + 1).cpu(),
-                              sf_slice(t["sfb"], g, n_t, k_t, 0, n_t).cpu(),
-                              np.array([128], np.int32), t["alpha"][g:g + 1].cpu(),
-                              t["prob"][r0:r0 + 128].cpu(), 128, n, k, 1, "e4m3", 32.0)
-        prob = t["prob"][r0:r0 + 128].double().cpu().numpy()
+    begins, experts = sampled_experts(off, L)
+    for g in experts:
+        r0 = int(begins[g])                        # the expert's first tile: rows r0 .. r0 + 255
+        assert O.expert_of_row(off, L, r0) == g and O.expert_of_row(off, L, r0 + 255) == g
+        assert float(t["prob"][r0].item()) > 0.0
+        say(f"  oracle expert {g} rows {r0}..{r0 + 255} ({int(off[g]) - r0} rows in the expert)")
+        sub = oracle_tile(t, g, r0, 256, m, n, k, fmt)
+        prob = t["prob"][r0:r0 + 256].double().cpu().numpy()
         bc = sum_bound(sub["sabs"], k, bmax=sub["bmax"])
-        rc = check_float(c[r0:r0 + 128].cpu(), sub["c"], bc, what=f"C e{g}")
-        rd = check_float(d[r0:r0 + 128].cpu(), sub["d"], d_bound(sub["c"], bc, prob, 32.0),
-                         what=f"D e{g}")
-        say(f"  C {rc} D {rd}")
         bd = d_bound(sub["c"], bc, prob, 32.0)
+        rc = check_float(c[r0:r0 + 256].cpu(), sub["c"], bc, what=f"C e{g}")
+        rd = check_float(d[r0:r0 + 256].cpu(), sub["d"], bd, what=f"D e{g}")
+        say(f"  C {rc} D {rd}")
         assert amax[g].item() >= (np.abs(sub["d"]) - bd).max() * (1 - 1e-5)
     # amax[g] is the max of D over expert g: compare with the GPU's own D
     for g in range(L):
@@ -173,15 +180,6 @@ def run_srelu_fp8(p, with_c=True, d_fmt="e4m3"):
                            tanh_clamp_scale=s["tanh_clamp"])
     torch.cuda.synchronize()
     return c, d, d_col, sfd_row, sfd_col
-
-
-def gather_scales(sfd_row, sfd_col, r0, r1, m, n):
-    """Logical (row, N/32) and (rows/32, N) scale arrays for rows [r0, r1)."""
-    row_idx = O.sf_offset_grid(r0, r1, n // 32, 0, m, n // 32)
-    col_idx = O.sf_offset_grid(0, n, ceil_div(r1, 32), 0, n, m // 32)[:, r0 // 32:]
-    rs = sfd_row.cpu().numpy()[row_idx]
-    cs = sfd_col.cpu().numpy()[col_idx].T
-    return rs, cs
 
 
 FP8_CASES = [
@@ -231,7 +229,8 @@ def test_grouped_srelu_fp8_out_matches_oracle(case):
 @pytest.mark.parametrize("d_fmt", ["e4m3", "e5m2", "e2m1"])
 def test_grouped_srelu_fp8_out_full_size_sampled(d_fmt):
     """Full grouped MXFP8 + sReLU workload with quantised D (E4M3, E5M2 or
-    E2M1 codes), as bench.py times it: sampled 128-row panels."""
+    E2M1 codes), as bench.py times it: the first whole 256-row tile of three
+    experts."""
     say(f"grouped_srelu quantised D ({d_fmt}) full size")
     p = W.moe_mxfp8_srelu(device="cuda", d_dtype="e4m3")
     s = p.sizes
@@ -239,23 +238,17 @@ def test_grouped_srelu_fp8_out_full_size_sampled(d_fmt):
     c, d, d_col, sfd_row, sfd_col = run_srelu_fp8(p, with_c=False, d_fmt=d_fmt)
     t = p.t
     off = t["offsets"].cpu().numpy()
-    m_t, n_t, k_t = ceil_div(m, 128), ceil_div(n, 128), ceil_div(k, 128)
-    begins = np.concatenate([[0], off[:-1]])
-    nonempty = [g for g in range(L) if off[g] > begins[g]]
-    for g in (nonempty[0], nonempty[-1]):
-        r0 = int(begins[g])                        # routed rows
+    begins, experts = sampled_experts(off, L)
+    for g in experts:
+        r0 = int(begins[g])
         assert float(t["prob"][r0].item()) > 0.0
-        say(f"  oracle expert {g} rows {r0}..{r0 + 127}")
-        sub = O.grouped_srelu(t["a"][r0:r0 + 128].cpu(), t["b"][g:g + 1].cpu(),
-                              sf_slice(t["sfa"], 0, m_t, k_t, r0 // 128, r0 // 128 + 1).cpu(),
-                              sf_slice(t["sfb"], g, n_t, k_t, 0, n_t).cpu(),
-                              np.array([128], np.int32), t["alpha"][g:g + 1].cpu(),
-                              t["prob"][r0:r0 + 128].cpu(), 128, n, k, 1, "e4m3", 32.0)
-        prob = t["prob"][r0:r0 + 128].double().cpu().numpy()
+        say(f"  oracle expert {g} rows {r0}..{r0 + 255}")
+        sub = oracle_tile(t, g, r0, 256, m, n, k, "e4m3")
+        prob = t["prob"][r0:r0 + 256].double().cpu().numpy()
         bc = sum_bound(sub["sabs"], k, bmax=sub["bmax"])
         bd = d_bound(sub["c"], bc, prob, 32.0)
-        rs, cs = gather_scales(sfd_row, sfd_col, r0, r0 + 128, m, n)
-        gd, gdc = d[r0:r0 + 128].cpu().numpy(), d_col[r0:r0 + 128].cpu().numpy()
+        rs, cs = gather_scales(sfd_row, sfd_col, r0, r0 + 256, m, n)
+        gd, gdc = d[r0:r0 + 256].cpu().numpy(), d_col[r0:r0 + 256].cpu().numpy()
         if d_fmt == "e2m1":
             gd, gdc = unpack_e2m1(gd), unpack_e2m1(gdc)
         res = check_mx_outputs(sub["d"], bd, gd, rs, gdc, cs, 1.0, what=f"e{g}", fmt=d_fmt)
@@ -318,16 +311,15 @@ def test_grouped_bf16_full_size_sampled():
                      bias_dtype=torch.bfloat16, c_dtype=torch.bfloat16, d_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     off = t["offsets"].cpu().numpy()
-    begins = np.concatenate([[0], off[:-1]])
-    nonempty = [g for g in range(L) if off[g] > begins[g]]
-    for g in (nonempty[0], nonempty[len(nonempty) // 2], nonempty[-1]):
-        r0 = int(begins[g])                        # first 64 rows of expert g: routed rows
+    begins, experts = sampled_experts(off, L)
+    for g in experts:
+        r0 = int(begins[g])                        # the expert's first whole 256-row tile
         assert O.expert_of_row(off, L, r0) == g and float(t["prob"][r0].item()) > 0.0
-        say(f"  oracle expert {g} rows {r0}..{r0 + 63}")
-        sub = O.grouped_bf16(O.bits16(t["a"][r0:r0 + 64]), O.bits16(t["b"][g:g + 1]),
-                             np.array([64], np.int32), t["alpha"][g:g + 1].cpu(),
-                             t["prob"][r0:r0 + 64].cpu(), t["bias"][g:g + 1].double().cpu().numpy(),
-                             64, n, k, 1)
+        say(f"  oracle expert {g} rows {r0}..{r0 + 255}")
+        sub = O.grouped_bf16(O.bits16(t["a"][r0:r0 + 256]), O.bits16(t["b"][g:g + 1]),
+                             np.array([256], np.int32), t["alpha"][g:g + 1].cpu(),
+                             t["prob"][r0:r0 + 256].cpu(), t["bias"][g:g + 1].double().cpu().numpy(),
+                             256, n, k, 1)
         bnd = sum_bound(sub["sabs"], k) + 1e-7 * np.abs(sub["c"])
-        say(f"  C {check_float(c[r0:r0 + 64].cpu(), sub['c'], bnd, what=f'C e{g}')}")
-        say(f"  D {check_float(d[r0:r0 + 64].cpu(), sub['d'], bnd, what=f'D e{g}')}")
+        say(f"  C {check_float(c[r0:r0 + 256].cpu(), sub['c'], bnd, what=f'C e{g}')}")
+        say(f"  D {check_float(d[r0:r0 + 256].cpu(), sub['d'], bnd, what=f'D e{g}')}")
