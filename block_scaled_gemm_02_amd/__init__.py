@@ -92,6 +92,63 @@ def _ptr(t):
     return t.data_ptr()
 
 
+# ---------------------------------------------------------------------------
+# Tensor checks.  The C ABI receives bare pointers and cannot see how large a
+# buffer is, so the binding checks every torch tensor it is handed against
+# what the kernels will read or write for the given sizes: device, dense
+# row-major layout, element type and byte count.  Plain integers are device
+# addresses; their extent is the caller's contract.
+# ---------------------------------------------------------------------------
+_OUT_TORCH = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}
+_BYTES = {F32: 4.0, F16: 2.0, BF16: 2.0, E4M3: 1.0, E5M2: 1.0, E2M1X2: 0.5}
+
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+def sf_atom_bytes(mn: int, k: int, l: int = 1) -> int:
+    """Bytes of a (32, 4, ceil(MN/128), 4, ceil(K/128), L) E8M0 scale-atom buffer."""
+    return 512 * _cdiv(mn, 128) * _cdiv(_cdiv(k, 32), 4) * l
+
+
+def _need(t, name, nbytes, kind=None):
+    """Reject a tensor that the kernel cannot use as `name`: kind is a
+    bsg_dtype code (a float dtype must match exactly; FP8 / FP4 codes need
+    one-byte elements), a torch dtype, or None (any element type)."""
+    if t is None or isinstance(t, int):
+        return
+    if not t.is_cuda or t.device.index != torch.cuda.current_device():
+        raise BsgError(6, f"{name} must be on the current CUDA device (got {t.device})")
+    if not t.is_contiguous():
+        raise BsgError(4, f"{name} must be contiguous")
+    if isinstance(kind, torch.dtype):
+        if t.dtype != kind:
+            raise BsgError(3, f"{name} must be {kind} (got {t.dtype})")
+    elif kind in _OUT_TORCH:
+        if t.dtype != _OUT_TORCH[kind]:
+            raise BsgError(3, f"{name} must be {_OUT_TORCH[kind]} for dtype code {kind} (got {t.dtype})")
+    elif kind is not None and t.element_size() != 1:
+        raise BsgError(3, f"{name} holds one-byte codes (got {t.dtype})")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise BsgError(2, f"{name} holds {have} bytes; these sizes need {int(nbytes)}")
+
+
+def _out_bytes(code, count):
+    return int(_BYTES.get(code, 1.0) * count)
+
+
+def _ab_row_bytes(ab, k):
+    return k // 2 if ab == E2M1X2 else k
+
+
+def _grouped_common_need(padded_offsets, alpha, prob, m, num_experts):
+    _need(padded_offsets, "padded_offsets", 4 * num_experts, torch.int32)
+    _need(alpha, "alpha", 4 * num_experts, torch.float32)
+    _need(prob, "prob", 4 * m, torch.float32)
+
+
 def _stream(stream):
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -141,8 +198,15 @@ def gemm_amax(a, b, sfa, sfb, c, amax, m, n, k, l, ab_dtype="e4m3", c_dtype=None
     c_dtype: a torch float dtype, "e4m3" / "e5m2" (FP8 C) or "e2m1" (packed
     FP4 C, (M, N/2, L) bytes); the last three with FP4 operands only."""
     cd = _d_code(c_dtype, c)
+    ab = _ab_code(ab_dtype)
+    if m * n * l > 0:
+        rb = _ab_row_bytes(ab, k)
+        _need(a, "a", l * m * rb, ab); _need(b, "b", l * n * rb, ab)
+        _need(sfa, "sfa", sf_atom_bytes(m, k, l), E8M0); _need(sfb, "sfb", sf_atom_bytes(n, k, l), E8M0)
+        _need(c, "c", _out_bytes(cd, l * m * n), cd)
+    _need(amax, "amax", 4, torch.float32)
     args = [_ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), _ptr(c), _ptr(amax), m, n, k, l,
-            _ab_code(ab_dtype), cd, sf_vec_size]
+            ab, cd, sf_vec_size]
     if validate_only:
         return lib().bsg_validate_gemm_amax(*args)
     _check(lib().gemm_amax(*args, _stream(stream)))
@@ -154,6 +218,11 @@ def grouped_gemm(a, b, padded_offsets, alpha, prob, bias, c, d, m, n, k, num_exp
     bd = dtype_code(bias_dtype if bias_dtype is not None else (bias if bias is not None else torch.bfloat16))
     cd = dtype_code(c_dtype if c_dtype is not None else (c if c is not None else torch.bfloat16))
     dd = dtype_code(d_dtype if d_dtype is not None else d)
+    _grouped_common_need(padded_offsets, alpha, prob, m, num_experts)
+    if m * n > 0:
+        _need(a, "a", 2 * m * k, torch.bfloat16); _need(b, "b", 2 * num_experts * n * k, torch.bfloat16)
+        _need(bias, "bias", _out_bytes(bd, n * num_experts), bd)
+        _need(c, "c", _out_bytes(cd, m * n), cd); _need(d, "d", _out_bytes(dd, m * n), dd)
     args = [_ptr(a), _ptr(b), _ptr(padded_offsets), _ptr(alpha), _ptr(prob), _ptr(bias),
             _ptr(c), _ptr(d), m, n, k, num_experts, bd, cd, dd]
     if validate_only:
@@ -171,9 +240,22 @@ def grouped_gemm_srelu(a, b, sfa, sfb, padded_offsets, alpha, prob, norm_const, 
     cd = dtype_code(c_dtype if c_dtype is not None else (c if c is not None else torch.bfloat16))
     dd = _d_code(d_dtype, d)
     s = float(tanh_clamp_scale) if tanh_clamp_scale is not None else 0.0
+    ab = _ab_code(ab_dtype)
+    _grouped_common_need(padded_offsets, alpha, prob, m, num_experts)
+    _need(amax, "amax", 4 * num_experts, torch.float32)
+    if m * n > 0:
+        rb = _ab_row_bytes(ab, k)
+        _need(a, "a", m * rb, ab); _need(sfa, "sfa", sf_atom_bytes(m, k, 1), E8M0)
+        _need(b, "b", num_experts * n * rb, ab)
+        _need(sfb, "sfb", sf_atom_bytes(n, k, num_experts), E8M0)
+        _need(c, "c", _out_bytes(cd, m * n), cd)
+        _need(d, "d", _out_bytes(dd, m * n), dd); _need(d_col, "d_col", _out_bytes(dd, m * n), dd)
+        _need(norm_const, "norm_const", 4, torch.float32)
+        _need(sfd_row, "sfd_row", sf_atom_bytes(m, n, 1), E8M0)
+        _need(sfd_col, "sfd_col", sf_atom_bytes(n, m, 1), E8M0)
     args = [_ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), _ptr(padded_offsets), _ptr(alpha),
             _ptr(prob), _ptr(norm_const), _ptr(c), _ptr(d), _ptr(d_col), _ptr(sfd_row),
-            _ptr(sfd_col), _ptr(amax), m, n, k, num_experts, _ab_code(ab_dtype), cd, dd,
+            _ptr(sfd_col), _ptr(amax), m, n, k, num_experts, ab, cd, dd,
             sf_vec_size, s]
     if validate_only:
         return lib().bsg_validate_grouped_gemm_srelu(*args)
@@ -195,6 +277,11 @@ def grouped_gemm_discrete(a, b_ptrs, padded_offsets, alpha, prob, bias, c, d, m,
     bd = dtype_code(bias_dtype if bias_dtype is not None else (bias if bias is not None else torch.bfloat16))
     cd = dtype_code(c_dtype if c_dtype is not None else (c if c is not None else torch.bfloat16))
     dd = dtype_code(d_dtype if d_dtype is not None else d)
+    _grouped_common_need(padded_offsets, alpha, prob, m, num_experts)
+    if m * n > 0:
+        _need(a, "a", 2 * m * k, torch.bfloat16); _need(b_ptrs, "b_ptrs", 8 * num_experts, torch.int64)
+        _need(bias, "bias", _out_bytes(bd, n * num_experts), bd)
+        _need(c, "c", _out_bytes(cd, m * n), cd); _need(d, "d", _out_bytes(dd, m * n), dd)
     args = [_ptr(a), _ptr(b_ptrs), _ptr(padded_offsets), _ptr(alpha), _ptr(prob), _ptr(bias),
             _ptr(c), _ptr(d), m, n, k, num_experts, bd, cd, dd]
     if validate_only:
@@ -211,9 +298,22 @@ def grouped_gemm_srelu_discrete(a, b_ptrs, sfa, sfb_ptrs, padded_offsets, alpha,
     cd = dtype_code(c_dtype if c_dtype is not None else (c if c is not None else torch.bfloat16))
     dd = _d_code(d_dtype, d)
     s = float(tanh_clamp_scale) if tanh_clamp_scale is not None else 0.0
+    ab = _ab_code(ab_dtype)
+    _grouped_common_need(padded_offsets, alpha, prob, m, num_experts)
+    _need(amax, "amax", 4 * num_experts, torch.float32)
+    if m * n > 0:
+        rb = _ab_row_bytes(ab, k)
+        _need(a, "a", m * rb, ab); _need(sfa, "sfa", sf_atom_bytes(m, k, 1), E8M0)
+        _need(b_ptrs, "b_ptrs", 8 * num_experts, torch.int64)
+        _need(sfb_ptrs, "sfb_ptrs", 8 * num_experts, torch.int64)
+        _need(c, "c", _out_bytes(cd, m * n), cd)
+        _need(d, "d", _out_bytes(dd, m * n), dd); _need(d_col, "d_col", _out_bytes(dd, m * n), dd)
+        _need(norm_const, "norm_const", 4, torch.float32)
+        _need(sfd_row, "sfd_row", sf_atom_bytes(m, n, 1), E8M0)
+        _need(sfd_col, "sfd_col", sf_atom_bytes(n, m, 1), E8M0)
     args = [_ptr(a), _ptr(b_ptrs), _ptr(sfa), _ptr(sfb_ptrs), _ptr(padded_offsets), _ptr(alpha),
             _ptr(prob), _ptr(norm_const), _ptr(c), _ptr(d), _ptr(d_col), _ptr(sfd_row),
-            _ptr(sfd_col), _ptr(amax), m, n, k, num_experts, _ab_code(ab_dtype), cd, dd,
+            _ptr(sfd_col), _ptr(amax), m, n, k, num_experts, ab, cd, dd,
             sf_vec_size, s]
     if validate_only:
         return lib().bsg_validate_grouped_gemm_srelu_discrete(*args)
@@ -228,9 +328,23 @@ def grouped_gemm_dswiglu(a, b, sfa, sfb, c, padded_offsets, alpha, beta, prob, n
     zero-fill it first."""
     cd = BF16 if c_dtype is None else (_TORCH_DT[c_dtype] if c_dtype in _TORCH_DT else c_dtype)
     dd = _d_code(d_dtype, d_row)
+    ab = _ab_code(ab_dtype)
+    _grouped_common_need(padded_offsets, alpha, prob, m, num_experts)
+    _need(beta, "beta", 4 * num_experts, torch.float32)
+    _need(amax, "amax", 8 * num_experts, torch.float32)
+    if m * n > 0:
+        rb = _ab_row_bytes(ab, k)
+        _need(a, "a", m * rb, ab); _need(b, "b", num_experts * n * rb, ab)
+        _need(sfa, "sfa", sf_atom_bytes(m, k, 1), E8M0); _need(sfb, "sfb", sf_atom_bytes(n, k, num_experts), E8M0)
+        _need(c, "c", 2 * m * 2 * n, torch.bfloat16)
+        _need(d_row, "d_row", _out_bytes(dd, m * 2 * n), dd); _need(d_col, "d_col", _out_bytes(dd, m * 2 * n), dd)
+        _need(norm_const, "norm_const", 4, torch.float32)
+        _need(sfd_row, "sfd_row", sf_atom_bytes(m, 2 * n, 1), E8M0)
+        _need(sfd_col, "sfd_col", sf_atom_bytes(2 * n, m, 1), E8M0)
+        _need(dprob, "dprob", 4 * m, torch.float32)
     args = [_ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), _ptr(c), _ptr(padded_offsets), _ptr(alpha), _ptr(beta),
             _ptr(prob), _ptr(norm_const), _ptr(d_row), _ptr(d_col), _ptr(sfd_row), _ptr(sfd_col), _ptr(dprob),
-            _ptr(amax), m, n, k, num_experts, _ab_code(ab_dtype), cd, dd, sf_vec_size]
+            _ptr(amax), m, n, k, num_experts, ab, cd, dd, sf_vec_size]
     if validate_only:
         return lib().bsg_validate_grouped_gemm_dswiglu(*args)
     _check(lib().grouped_gemm_dswiglu(*args, _stream(stream)))
@@ -241,6 +355,17 @@ def gemm_proj_rope_mxfp8(x, w, x_scale, w_scale, cos, sin, out_fp8_row, out_scal
                          head_dim=192, qk_rope=64, in_dtype=BF16, w_out_in=1, stream=None,
                          validate_only=False):
     """Projection GEMM + per-head RoPE + dual MXFP8 quantisation (see include/bsg.h)."""
+    if tokens * num_heads > 0:
+        nout = num_heads * head_dim
+        es = 1 if in_dtype == E4M3 else 2
+        kind = E4M3 if in_dtype == E4M3 else torch.bfloat16
+        _need(x, "x", es * tokens * q_lora, kind); _need(w, "w", es * nout * q_lora, kind)
+        _need(x_scale, "x_scale", tokens * (q_lora // 32), E8M0)
+        _need(w_scale, "w_scale", nout * (q_lora // 32), E8M0)
+        _need(cos, "cos", 2 * tokens * qk_rope, torch.bfloat16); _need(sin, "sin", 2 * tokens * qk_rope, torch.bfloat16)
+        _need(out_fp8_row, "out_fp8_row", tokens * nout, E4M3); _need(out_fp8_col, "out_fp8_col", tokens * nout, E4M3)
+        _need(out_scales_row, "out_scales_row", tokens * nout // 32, E8M0)
+        _need(out_scales_col, "out_scales_col", (tokens // 32) * nout, E8M0)
     args = [_ptr(x), _ptr(w), _ptr(x_scale), _ptr(w_scale), _ptr(cos), _ptr(sin),
             _ptr(out_fp8_row), _ptr(out_scales_row), _ptr(out_fp8_col), _ptr(out_scales_col),
             tokens, q_lora, num_heads, head_dim, qk_rope, in_dtype, int(w_out_in)]

@@ -195,3 +195,12 @@ def test_dswiglu_validation():
     assert vdsw(d_dtype=torch.bfloat16) == DTYPE
     assert vdsw(dprob=P + 2) == ALIGN
     assert vdsw(num_experts=0) == SHAPE
+
+
+def test_binding_rejects_host_tensors():
+    """Tensors are checked before the C call: a host tensor is refused with
+    the DEVICE status (the kernels only take device memory)."""
+    a = torch.zeros(256, 256, dtype=torch.uint8)
+    with pytest.raises(bsg.BsgError) as e:
+        va(a=a)
+    assert e.value.status == 6
