@@ -236,8 +236,11 @@ def grouped_gemm_srelu(a, b, sfa, sfb, padded_offsets, alpha, prob, norm_const, 
                        stream=None, validate_only=False):
     """Grouped block-scaled GEMM + prob-gated squared ReLU (see include/bsg.h).
 
-    d_dtype: a torch float dtype, or "e4m3" / "e5m2" for MXFP8 output with SFD_row/col."""
-    cd = dtype_code(c_dtype if c_dtype is not None else (c if c is not None else torch.bfloat16))
+    d_dtype: a torch float dtype, or "e4m3" / "e5m2" / "e2m1" for MX-quantised
+    output with SFD_row/col.  c_dtype: a torch float dtype, or "e4m3" /
+    "e5m2" / "e2m1" for an unscaled saturating cast of C (E2M1 packed two
+    per byte)."""
+    cd = _d_code(c_dtype if c_dtype is not None else (c if c is not None else torch.bfloat16), None)
     dd = _d_code(d_dtype, d)
     s = float(tanh_clamp_scale) if tanh_clamp_scale is not None else 0.0
     ab = _ab_code(ab_dtype)
@@ -295,7 +298,7 @@ def grouped_gemm_srelu_discrete(a, b_ptrs, sfa, sfb_ptrs, padded_offsets, alpha,
                                 stream=None, validate_only=False):
     """grouped_gemm_srelu with per-expert weight and scale allocations:
     b_ptrs / sfb_ptrs are (L,) int64 device tensors (see include/bsg.h)."""
-    cd = dtype_code(c_dtype if c_dtype is not None else (c if c is not None else torch.bfloat16))
+    cd = _d_code(c_dtype if c_dtype is not None else (c if c is not None else torch.bfloat16), None)
     dd = _d_code(d_dtype, d)
     s = float(tanh_clamp_scale) if tanh_clamp_scale is not None else 0.0
     ab = _ab_code(ab_dtype)

@@ -274,9 +274,11 @@ static int validate_srelu(const void *a, const void *b, const uint8_t *sfa, cons
     if (k % 32) return fail(BSG_ERR_SHAPE, "K=%lld must be a multiple of sf_vec_size 32", (long long)k);
     if (n % 32) return fail(BSG_ERR_SHAPE, "N=%lld must be a multiple of 32", (long long)n);
     if (!(tanh_clamp_scale == tanh_clamp_scale)) return fail(BSG_ERR_SHAPE, "tanh_clamp_scale is NaN");
-    if (c && (c_dtype == BSG_E4M3 || c_dtype == BSG_E5M2 || c_dtype == BSG_E2M1X2))
-        return fail(BSG_ERR_UNSUPPORTED, "FP8 / FP4 C is not built (F32, F16 and BF16 are)");
-    if (c && !is_float_out(c_dtype)) return fail(BSG_ERR_DTYPE, "C dtype must be F32, F16 or BF16");
+    // C: fp32 / fp16 / bf16, or an unscaled saturating FP8 / packed FP4 cast
+    // ("Grouped GEMM + sReLU (SM100)", Input/Output tensors lists all six)
+    const bool fp8_c = c_dtype == BSG_E4M3 || c_dtype == BSG_E5M2 || c_dtype == BSG_E2M1X2;
+    if (c && !is_float_out(c_dtype) && !fp8_c)
+        return fail(BSG_ERR_DTYPE, "C dtype must be F32, F16, BF16, E4M3, E5M2 or E2M1X2");
     // quantised D: E4M3 / E5M2 codes, or E2M1 codes two per byte
     const bool fp8_out = d_dtype == BSG_E4M3 || d_dtype == BSG_E5M2 || d_dtype == BSG_E2M1X2;
     if (!fp8_out && !is_float_out(d_dtype)) return fail(BSG_ERR_DTYPE, "D dtype %d invalid", d_dtype);
@@ -290,8 +292,9 @@ static int validate_srelu(const void *a, const void *b, const uint8_t *sfa, cons
     if (!sfa || !sfb) return fail(BSG_ERR_NULLPTR, discrete ? "sfa and sfb_ptrs are required" : "sfa and sfb are required");
     if (discrete && (reinterpret_cast<uintptr_t>(sfb) & 7u)) return fail(BSG_ERR_ALIGN, "sfb_ptrs must be 8-byte aligned");
     const int db = fp8_out ? 1 : elem_bytes(d_dtype);
+    const int64_t c_row = c_dtype == BSG_E2M1X2 ? n / 2 : n * elem_bytes(c_dtype);
     if (!aligned16(d) || (n * db) % 16 || (d_col && !aligned16(d_col)) ||
-        (c && (!aligned16(c) || (n * elem_bytes(c_dtype)) % 16)))
+        (c && (!aligned16(c) || c_row % 16)))
         return fail(BSG_ERR_ALIGN, "C/D/D_col must be 16-byte aligned with 16-byte rows");
     if (fp8_out && ((reinterpret_cast<uintptr_t>(sfd_row) | reinterpret_cast<uintptr_t>(sfd_col)) & 3u))
         return fail(BSG_ERR_ALIGN, "sfd_row and sfd_col must be 4-byte aligned");

@@ -43,20 +43,30 @@ static inline uint32_t row_bytes_of(int fmt, int64_t k)
 }
 
 // One output of a wave's 128 x (32*NB) quadrant through the wave's LDS
-// staging region: dispatches on the run-time output type.  (row0, col0) is
-// the quadrant's first element; rows_valid / cols_valid bound it.
+// staging region: dispatches on the run-time output type (fp32 / fp16 /
+// bf16, or the unscaled saturating E4M3 / E5M2 / packed E2M1 casts of an FP8
+// or FP4 C).  (row0, col0) is the quadrant's first element; rows_valid /
+// cols_valid bound it.  base2, if non-null, receives a copy (16-bit and
+// 32-bit types only).
 template <int NB, class Fn>
 __device__ __forceinline__ void store_quadrant_rt(int dt, uint8_t *reg, void *base, void *base2, int64_t n,
                                                   int64_t row0, int64_t col0, int rows_valid, int cols_valid,
                                                   f32x16 (&acc)[4][NB], int lane, Fn &&value)
 {
-    const int es = dt == DT_F32 ? 4 : 2;
+    if (dt == DT_E2M1) {
+        char *dst = static_cast<char *>(base) + (row0 * n + col0) / 2;
+        store_quadrant_fp4<NB>(reg, dst, (uint32_t)(n / 2), rows_valid, cols_valid, acc, lane, value);
+        return;
+    }
+    const int es = dt == DT_F32 ? 4 : ((dt == DT_E4M3 || dt == DT_E5M2) ? 1 : 2);
     char *dst = static_cast<char *>(base) + (row0 * n + col0) * es;
     char *dst2 = base2 ? static_cast<char *>(base2) + (row0 * n + col0) * es : nullptr;
     const uint32_t rb = (uint32_t)(n * es);
     if (dt == DT_F32) store_quadrant<DT_F32, NB>(reg, dst, dst2, rb, rows_valid, cols_valid, acc, lane, value);
     else if (dt == DT_BF16) store_quadrant<DT_BF16, NB>(reg, dst, dst2, rb, rows_valid, cols_valid, acc, lane, value);
-    else store_quadrant<DT_F16, NB>(reg, dst, dst2, rb, rows_valid, cols_valid, acc, lane, value);
+    else if (dt == DT_F16) store_quadrant<DT_F16, NB>(reg, dst, dst2, rb, rows_valid, cols_valid, acc, lane, value);
+    else if (dt == DT_E4M3) store_quadrant<DT_E4M3, NB>(reg, dst, nullptr, rb, rows_valid, cols_valid, acc, lane, value);
+    else store_quadrant<DT_E5M2, NB>(reg, dst, nullptr, rb, rows_valid, cols_valid, acc, lane, value);
 }
 
 // Waits for every outstanding vector-memory load before the epilogue's first

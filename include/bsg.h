@@ -140,7 +140,10 @@ int grouped_gemm(const void *a, const void *b, const int32_t *padded_offsets,
  *  b, sfb          (N,K,L) codes [L][N][K]; scale atoms over (N, K, L)
  *  padded_offsets, alpha, prob   as for grouped_gemm
  *  c               (M,N) pre-activation alpha*acc, nullable; c_dtype in
- *                  {BF16, F16, F32} (FP8 / FP4 C return UNSUPPORTED)
+ *                  {BF16, F16, F32} (RNE cast), or E4M3 / E5M2 (a round to
+ *                  nearest even saturated to +-448 / +-57344, no scale
+ *                  factor) or E2M1X2 ((M, N/2) bytes, two codes per byte,
+ *                  the even column in the low nibble, saturated to +-6)
  *  d_dtype in {BF16, F16, F32}:
  *      d      (M,N) D, RNE cast;  d_col: nullable copy of d
  *      amax   (L,) fp32, nullable: amax[g] = max |D| over expert g's rows

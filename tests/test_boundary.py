@@ -86,7 +86,9 @@ def test_grouped_srelu_validation():
     assert vs(d_dtype="e2m1", norm_const=P, d_col=P, sfd_row=P, sfd_col=P) == OK    # MXFP4 D
     assert vs(d_dtype="e2m1", norm_const=P, d_col=P, sfd_row=P, sfd_col=P, ab_dtype="e2m1") == DTYPE
     assert vs(d_dtype="e2m1") == NULLPTR
-    assert vs(c_dtype=bsg.E4M3) == UNSUP                     # FP8 C of the sReLU op not built
+    assert vs(c_dtype=bsg.E4M3) == OK                        # FP8 C (unscaled saturating cast)
+    assert vs(c_dtype="e2m1") == OK                          # packed FP4 C
+    assert vs(c_dtype="e5m2", n=48) == SHAPE                 # N % 32
     assert vs(c_dtype=99) == DTYPE
     assert vs(n=80) == SHAPE                             # N % 32
     assert vs(tanh_clamp_scale=float("nan")) == SHAPE

@@ -8,8 +8,8 @@ import torch
 import block_scaled_gemm_02_amd as bsg
 import oracle as O
 import workloads as W
-from parity import (check_amax, check_float, check_mx_outputs, ceil_div, d_bound, gather_scales, sf_slice,
-                    sum_bound, unpack_e2m1)
+from parity import (FP8_MAX, check_amax, check_float, check_mx_outputs, ceil_div, d_bound, e2m1_ordered,
+                    e4m3_ordered, gather_scales, sf_slice, sum_bound, unpack_e2m1)
 
 pytestmark = pytest.mark.gpu
 SENT = -1536.0    # exactly representable in bf16, fp16 and fp32
@@ -323,3 +323,87 @@ def test_grouped_bf16_full_size_sampled():
         bnd = sum_bound(sub["sabs"], k) + 1e-7 * np.abs(sub["c"])
         say(f"  C {check_float(c[r0:r0 + 256].cpu(), sub['c'], bnd, what=f'C e{g}')}")
         say(f"  D {check_float(d[r0:r0 + 256].cpu(), sub['d'], bnd, what=f'D e{g}')}")
+
+
+# ---------------------------------------------------------------------------
+# FP8 / FP4 C ("Grouped GEMM + sReLU (SM100)", Input/Output tensors: C may be
+# float8_e4m3fn, float8_e5m2 or float4_e2m1fn_x2): an unscaled round to
+# nearest even of alpha * acc, saturated to the format's largest value
+# ---------------------------------------------------------------------------
+def _c_codes_check(raw, o_c, bc, fmt):
+    """Every GPU code lies between the codes of oracle C -/+ its bound (the
+    cast is monotone) and equals the oracle's own encode of the fp64 value,
+    except one-step flips on at most 0.1%."""
+    if fmt == "e2m1":
+        enc = np.vectorize(lambda v: O.enc_e2m1(float(v)), otypes=[np.uint32])
+        g = e2m1_ordered(unpack_e2m1(raw))
+        lo, hi, own = e2m1_ordered(enc(o_c - bc)), e2m1_ordered(enc(o_c + bc)), e2m1_ordered(enc(o_c))
+    else:
+        fmax = FP8_MAX[fmt]
+        tdt = torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2
+
+        def enc(v):
+            v = np.clip(v, -fmax, fmax).astype(np.float32)
+            return e4m3_ordered(torch.from_numpy(v).to(tdt).view(torch.uint8).numpy())
+        oenc = O.enc_e4m3 if fmt == "e4m3" else O.enc_e5m2
+        g = e4m3_ordered(raw)
+        lo, hi = enc(o_c - bc), enc(o_c + bc)
+        own = e4m3_ordered(np.array([oenc(v) for v in o_c.ravel()], dtype=np.uint32).reshape(o_c.shape))
+    bad = (g < lo) | (g > hi)
+    assert not bad.any(), f"{int(bad.sum())} C codes outside the error-bound window"
+    step = np.abs(g - own)
+    assert step.max(initial=0) <= 1 and int((step == 1).sum()) <= max(1, 1e-3 * step.size)
+    return int((step == 1).sum())
+
+
+@pytest.mark.parametrize("case", [
+    dict(sizes=[256, 0, 512, 256], n=320, k=192, fmt="e4m3", c="e4m3", d=torch.bfloat16, s=32.0),
+    dict(sizes=[512, 256], n=256, k=512, fmt="e5m2", c="e5m2", d=torch.float32, s=0.0),
+    dict(sizes=[0, 256, 256], n=288, k=256, fmt="e2m1", c="e2m1", d=torch.bfloat16, s=32.0),
+    dict(sizes=[256, 512], n=224, k=320, fmt="e4m3", c="e2m1", d="e4m3", s=0.5),
+    dict(sizes=[256, 256], n=160, k=256, fmt="e4m3", c="e5m2", d="e2m1", s=32.0),
+])
+def test_grouped_srelu_fp8_fp4_c(case):
+    say(f"grouped_srelu FP8/FP4 C {case}")
+    off = np.cumsum(case["sizes"]).astype(np.int32)
+    L = len(case["sizes"])
+    qd = isinstance(case["d"], str)
+    p = W.grouped_srelu_problem(0, L, case["n"], case["k"], case["fmt"], seed=6, offsets=off,
+                                tanh_clamp=case["s"], extra_rows=256, d_dtype="e4m3" if qd else "bf16")
+    s = p.sizes
+    m, n, k = s["m"], s["n"], s["k"]
+    t = {kk: (v.cuda() if isinstance(v, torch.Tensor) else v) for kk, v in p.t.items()}
+    cb = n // 2 if case["c"] == "e2m1" else n
+    c = torch.full((m, cb), 0xEE, dtype=torch.uint8, device="cuda")
+    if qd:
+        db = n // 2 if case["d"] == "e2m1" else n
+        d = torch.full((m, db), 0xEE, dtype=torch.uint8, device="cuda")
+        d_col = torch.full((m, db), 0xEE, dtype=torch.uint8, device="cuda")
+        sfd_row = torch.full((W.sf_atom_bytes(m, n, 1),), 0xEE, dtype=torch.uint8, device="cuda")
+        sfd_col = torch.full((W.sf_atom_bytes(n, m, 1),), 0xEE, dtype=torch.uint8, device="cuda")
+        amax, nc = None, torch.ones(1, device="cuda")
+    else:
+        d = torch.full((m, n), SENT, dtype=case["d"], device="cuda")
+        d_col = sfd_row = sfd_col = None
+        amax, nc = torch.full((L,), -1.0, device="cuda"), None
+    bsg.grouped_gemm_srelu(t["a"], t["b"], t["sfa"], t["sfb"], t["offsets"], t["alpha"], t["prob"], nc,
+                           c, d, d_col, sfd_row, sfd_col, amax, m, n, k, L, case["fmt"], c_dtype=case["c"],
+                           d_dtype=case["d"], tanh_clamp_scale=case["s"])
+    torch.cuda.synchronize()
+    r = O.grouped_srelu(p.t["a"], p.t["b"], p.t["sfa"], p.t["sfb"], off, p.t["alpha"], p.t["prob"],
+                        m, n, k, L, case["fmt"], case["s"])
+    valid = s["valid_m"]
+    bc = sum_bound(r["sabs"], k, bmax=r["bmax"])
+    flips = _c_codes_check(c[:valid].cpu().numpy(), r["c"][:valid], bc[:valid], case["c"])
+    assert torch.all(c[valid:] == 0xEE)
+    # D is unchanged by C's type
+    bd = d_bound(r["c"], bc, p.t["prob"].double().numpy(), case["s"])[:valid]
+    if qd:
+        rs, cs = gather_scales(sfd_row, sfd_col, 0, valid, m, n)
+        gd, gdc = d[:valid].cpu().numpy(), d_col[:valid].cpu().numpy()
+        if case["d"] == "e2m1":
+            gd, gdc = unpack_e2m1(gd), unpack_e2m1(gdc)
+        res = check_mx_outputs(r["d"][:valid], bd, gd, rs, gdc, cs, 1.0, what="D", fmt=case["d"])
+    else:
+        res = check_float(d[:valid].cpu(), r["d"][:valid], bd, what="D")
+    say(f"  C one-step flips {flips}; D {res}")
