@@ -231,11 +231,11 @@ def wl_moe_bf16():
     return step, info
 
 
-def wl_proj_rope(mxfp8=False):
+def wl_proj_rope(mxfp8=False, w_out_in=True):
     import torch
     import block_scaled_gemm_02_amd as bsg
     import workloads as W
-    p = W.proj_rope_dsv3(device="cuda", in_dtype="e4m3" if mxfp8 else "bf16")
+    p = W.proj_rope_dsv3(device="cuda", in_dtype="e4m3" if mxfp8 else "bf16", w_out_in=w_out_in)
     s, t = p.sizes, p.t
     T, H, D = s["tokens"], s["heads"], s["head_dim"]
     qr = torch.empty(T, H, D, dtype=torch.uint8, device="cuda")
@@ -246,19 +246,21 @@ def wl_proj_rope(mxfp8=False):
     def step():
         bsg.gemm_proj_rope_mxfp8(t["x"], t["w"], t.get("x_scale"), t.get("w_scale"), t["cos"], t["sin"],
                                  qr, sr, qc, sc, T, s["q_lora"], H, D, s["qk_rope"],
-                                 in_dtype=bsg.E4M3 if mxfp8 else bsg.BF16, w_out_in=1)
+                                 in_dtype=bsg.E4M3 if mxfp8 else bsg.BF16, w_out_in=int(w_out_in))
 
     n = H * D
     q = s["q_lora"]
     # inputs: x and w (2 bytes per element, or 1 byte + 1/32 byte of scale), cos/sin;
     # outputs: row and column codes (1 byte each) and both scale arrays
     in_bytes = (T * q + n * q) * (1 + 1 / 32) if mxfp8 else 2 * (T * q + n * q)
-    info = dict(name="proj_rope_mxfp8" if mxfp8 else "proj_rope", fmt="e4m3" if mxfp8 else "bf16",
+    info = dict(name=("proj_rope_mxfp8" if mxfp8 else "proj_rope") + ("" if w_out_in else "_w_in_out"),
+                fmt="e4m3" if mxfp8 else "bf16",
                 flops=2.0 * T * n * q,
                 alg_bytes=in_bytes + 2 * 2 * T * 64 + 2 * T * n + T * n // 16,
                 kernel="k_proj_rope",
                 config={"workload": "projection GEMM + per-head RoPE + dual MXFP8, DeepSeek-V3 Q up-proj"
-                        + (", MXFP8 inputs (E4M3, row-major E8M0 per 32)" if mxfp8 else ", bf16 inputs"),
+                        + (", MXFP8 inputs (E4M3, row-major E8M0 per 32)" if mxfp8 else ", bf16 inputs")
+                        + ("" if w_out_in else ", w as [in, out]"),
                         "tokens": T, "q_lora": q, "heads": H, "head_dim": D, "qk_rope": 64},
                 cpu=None)
     return step, info
@@ -267,6 +269,7 @@ def wl_proj_rope(mxfp8=False):
 WORKLOADS = {
     "proj_rope": wl_proj_rope,
     "proj_rope_mxfp8": lambda: wl_proj_rope(True),
+    "proj_rope_w_in_out": lambda: wl_proj_rope(False, w_out_in=False),
     "moe_mxfp8_srelu": lambda: wl_moe_mxfp8_srelu(False),
     "moe_mxfp8_srelu_fp8d": lambda: wl_moe_mxfp8_srelu(True),
     "moe_mxfp8_srelu_e5m2d": lambda: wl_moe_mxfp8_srelu(True, d_fp8="e5m2"),

@@ -49,9 +49,24 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // K elements of a row ("GEMM + RoPE + MXFP8 Projection (SM100)", x_scale and
 // w_scale), instead of the scale-atom layout of the other block-scaled ops.
 // FMT_E5M2: E5M2 codes (one byte each) with scale atoms, like FMT_E4M3.
-enum Fmt : int { FMT_E4M3 = 0, FMT_E2M1 = 1, FMT_BF16 = 2, FMT_E4M3_RM = 3, FMT_E5M2 = 4 };
+// FMT_BF16_BT: BF16 whose B operand is stored [K][N] ("GEMM + RoPE + MXFP8
+// Projection (SM100)", w as (Q_LORA, NUM_HEADS*HEAD_DIM) when w_out_in is
+// false): each pair's B tile is staged K-major and its fragments are formed
+// with the transposing LDS reads (see the B loads and read_one).
+enum Fmt : int { FMT_E4M3 = 0, FMT_E2M1 = 1, FMT_BF16 = 2, FMT_E4M3_RM = 3, FMT_E5M2 = 4, FMT_BF16_BT = 5 };
 // one-byte codes: one 32x32x64 MFMA per block per 64-byte step
 constexpr bool is_fp8(int f) { return f == FMT_E4M3 || f == FMT_E4M3_RM || f == FMT_E5M2; }
+constexpr bool is_bf16(int f) { return f == FMT_BF16 || f == FMT_BF16_BT; }
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+
+// K-major B tile of FMT_BF16_BT in a pair slot: the pair's 64 K rows, each
+// holding the tile's (up to 192) BF16 columns in 384 bytes, at a stride of
+// 448 bytes (28 KB).  The padding puts the four K rows that one 16-lane
+// group of a transposing read touches on four different 64-byte bank groups
+// (448 = 256 + 192), so the reads are conflict-free.
+constexpr int kBtRow = 448, kBtData = 384, kBtLoads = 64 * kBtRow / 1024 / 4;   // 7 loads per wave
 
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;
@@ -235,7 +250,7 @@ constexpr int kPB = 256 * kPK;             // 32 KB (NB = 4)
 
 template <int F>
 struct Ring {
-    static constexpr bool kScaled = F != FMT_BF16;
+    static constexpr bool kScaled = !is_bf16(F);
     static constexpr int kScaleSets = F == FMT_E2M1 ? 2 : (is_fp8(F) ? 1 : 0);
     static constexpr int kSlot = kPA + kPB + kScaleSets * 4096;
     static constexpr int kBytes = 2 * kSlot;
@@ -301,7 +316,8 @@ struct PipeDesc {
     static constexpr int LB = 2 * NB;  // B loads per wave per pair (16*NB rows / 8)
     i32x4 ra, rb, rs;         // operand panels; this wave's scale atoms (buffer resources)
     uint32_t row_bytes;
-    uint32_t va[8], vb[LB];   // per-lane voffset of this wave's code loads (pair 0)
+    uint32_t va[8], vb[LB > kBtLoads ? LB : kBtLoads];   // per-lane voffset of this wave's code loads (pair 0)
+    uint32_t bt_pair;         // FMT_BF16_BT: bytes of B per pair along K (64 K rows)
     uint32_t lc16;            // 16 * logical chunk of this lane's loads
     uint32_t vs;              // per-lane voffset of this wave's scale atom (kt = 0)
     uint32_t pa;              // per-lane voffset of the A line this lane prefetches (pair 0)
@@ -343,17 +359,24 @@ __device__ __forceinline__ uint8_t *wave_stage(const RingSlots<F> &ring, int w)
 template <int F>
 constexpr bool scales_in_stage(bool odd) { return Ring<F>::kScaled && !(is_fp8(F) && odd); }
 template <int F, int NB>
-constexpr int loads_per_pair() { return 8 + 2 * NB + (F == FMT_E4M3_RM ? 2 : Ring<F>::kScaleSets); }
+constexpr int b_loads() { return F == FMT_BF16_BT ? kBtLoads : 2 * NB; }
+template <int F, int NB>
+constexpr int loads_per_pair() { return 8 + b_loads<F, NB>() + (F == FMT_E4M3_RM ? 2 : Ring<F>::kScaleSets); }
 template <int F, int NB>
 constexpr int mfmas_per_step() { return (is_fp8(F) ? 1 : 2) * 4 * NB; }
+// B reads of a stage: one 16-byte read per chunk, or (FMT_BF16_BT) two
+// 8-byte transposing reads per chunk
 template <int F, int NB>
-constexpr int reads_in_stage(bool odd) { return 8 + 2 * NB + (scales_in_stage<F>(odd) ? 2 : 0); }
+constexpr int b_reads() { return F == FMT_BF16_BT ? 4 * NB : 2 * NB; }
+template <int F, int NB>
+constexpr int reads_in_stage(bool odd) { return 8 + b_reads<F, NB>() + (scales_in_stage<F>(odd) ? 2 : 0); }
 
 // Where this wave's loads of pair p go: code offset (K position, or out of
 // range past the row end) and scale-atom offset of each atom set.
 struct PairAddr {
     uint32_t kb_oob[2];       // added to va/vb of loads with even / odd index
     uint32_t so[2];           // scale-atom voffsets
+    uint32_t kbt;             // FMT_BF16_BT: added to vb (K rows past K read zeros: range check)
 };
 template <int F, int NB>
 __device__ __forceinline__ PairAddr pair_addr(const PipeDesc<NB> &d, int pair)
@@ -362,6 +385,7 @@ __device__ __forceinline__ PairAddr pair_addr(const PipeDesc<NB> &d, int pair)
     const uint32_t kb = (uint32_t)pair * kPK;
     a.kb_oob[0] = kb + ((kb + d.lc16 < d.row_bytes) ? 0u : kOOB);
     a.kb_oob[1] = kb + ((kb + (d.lc16 ^ 16u) < d.row_bytes) ? 0u : kOOB);
+    a.kbt = (uint32_t)pair * d.bt_pair;
     if constexpr (F == FMT_E4M3_RM) {
         // row-major scales: the pair's 4 bytes of a row follow its previous pair's
 #pragma unroll
@@ -382,9 +406,13 @@ __device__ __forceinline__ PairAddr pair_addr(const PipeDesc<NB> &d, int pair)
 template <int F, int NB, int L>
 __device__ __forceinline__ void load_one(const PipeDesc<NB> &d, uint8_t *st, const PairAddr &a, int w)
 {
-    constexpr int LB = 2 * NB;
+    constexpr int LB = b_loads<F, NB>();
     if constexpr (L < 8) {
         lds_load16(d.ra, st + 1024 * (8 * w + L), d.va[L] + a.kb_oob[L & 1]);
+    } else if constexpr (F == FMT_BF16_BT && L < 8 + LB) {
+        // K-major B: 1 KB of the pair's 28 KB K-row block per load (padding
+        // lanes read zeros)
+        lds_load16(d.rb, st + kPA + 1024 * (LB * w + (L - 8)), d.vb[L - 8] + a.kbt);
     } else if constexpr (L < 8 + LB) {
         lds_load16(d.rb, st + kPA + 1024 * (LB * w + (L - 8)), d.vb[L - 8] + a.kb_oob[(L - 8) & 1]);
     } else if constexpr (F == FMT_E4M3_RM) {
@@ -433,7 +461,18 @@ __device__ __forceinline__ ReadAddr read_addr(const uint8_t *st, int wm, int wn,
     r.p0 = 16u * ((4u * H + g) ^ swz);
     r.p1 = 16u * ((4u * H + 2u + g) ^ swz);
     r.a0 = st + (128u * wm + row) * kPK;
-    r.b0 = st + kPA + (32u * NB * wn + row) * kPK;
+    if constexpr (F == FMT_BF16_BT) {
+        // transposing reads (16-lane group G = lane / 16, lane s = lane % 16
+        // in it): lane s reads 4 columns of K row 8(G/2) + s/4 (+ 4 for the
+        // second read of a chunk, + 16 for chunk 1, + 32 in the pair's second
+        // step), columns 16(G%2) + 4(s%4) of the block; lane j of the group
+        // then holds 4 consecutive K values of column 16(G%2) + j
+        const uint32_t G = (uint32_t)lane >> 4, s = (uint32_t)lane & 15;
+        r.b0 = st + kPA + (32u * H + 8u * (G >> 1) + (s >> 2)) * kBtRow +
+               2u * (32u * NB * wn + 16u * (G & 1) + 4u * (s & 3));
+    } else {
+        r.b0 = st + kPA + (32u * NB * wn + row) * kPK;
+    }
     const uint8_t *sc = st + kPA + kPB + (F == FMT_E2M1 ? 4096 * H : 0);
     r.sa = sc + 1024 * wm + 16 * row;
     r.sb = sc + 1024 * (2 + wn) + 16 * row;
@@ -445,10 +484,24 @@ __device__ __forceinline__ void read_one(Frags<NB> &f, const ReadAddr &r)
     if constexpr (R < 8) {
         constexpr int i = R / 2, h = R % 2;
         f.a[i][h] = *reinterpret_cast<const i32x4 *>(r.a0 + 32 * kPK * i + (h ? r.p1 : r.p0));
+    } else if constexpr (F == FMT_BF16_BT && R < 8 + 4 * NB) {
+        // chunk h of block j: K [8g + 16h, +8) of the lane's column as two
+        // reads of 4 K values each (e = 0, 1)
+        constexpr int q = R - 8, j = q / 4, h = (q / 2) % 2, e = q % 2;
+        const uint8_t *p = r.b0 + (16 * h + 4 * e) * kBtRow + 64 * j;
+        const auto v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(lds_void *)p);
+        const i32x2_t u = __builtin_bit_cast(i32x2_t, v);
+        if constexpr (e == 0) {
+            f.b[j][h].x = u.x;
+            f.b[j][h].y = u.y;
+        } else {
+            f.b[j][h].z = u.x;
+            f.b[j][h].w = u.y;
+        }
     } else if constexpr (R < 8 + 2 * NB) {
         constexpr int j = (R - 8) / 2, h = (R - 8) % 2;
         f.b[j][h] = *reinterpret_cast<const i32x4 *>(r.b0 + 32 * kPK * j + (h ? r.p1 : r.p0));
-    } else if constexpr (R == 8 + 2 * NB) {
+    } else if constexpr (R == 8 + b_reads<F, NB>()) {
         f.sa = *reinterpret_cast<const i32x4 *>(r.sa);
     } else {
         f.sb = *reinterpret_cast<const i32x4 *>(r.sb);
@@ -581,7 +634,8 @@ template <int F, int NB = 4>
 __device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[4][NB], const RingSlots<F> &ring,
                                               const OperandDesc &A, const OperandDesc &B, int64_t k)
 {
-    static_assert(NB == 4 || F == FMT_BF16 || F == FMT_E4M3_RM, "atom scales need 128-column wave tiles");
+    static_assert(NB == 4 || is_bf16(F) || F == FMT_E4M3_RM, "atom scales need 128-column wave tiles");
+    static_assert(F != FMT_BF16_BT || 64 * NB <= kBtData / 2, "a K-major B row holds the tile's columns");
     // the wave index is uniform: keep everything derived from it in SGPRs
     const int t = threadIdx.x, lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w >> 1, wn = w & 1;
@@ -604,6 +658,20 @@ __device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[4][NB], const RingSl
 #pragma unroll
     for (int q = 0; q < PipeDesc<NB>::LB; ++q)
         d.vb[q] = (16u * NB * w + 8u * q + lrow) * B.row_bytes + (d.lc16 ^ (16u * (q & 1)));
+    d.bt_pair = 0;
+    if constexpr (F == FMT_BF16_BT) {
+        // B is [K][N] with B.row_bytes between K rows: load q of wave w fills
+        // bytes 1024 (7w + q) .. of the pair's K-row block, 16 per lane, so a
+        // lane's byte o sits in K row o / 448 at column byte o % 448 (zeros
+        // for the padding past 384)
+#pragma unroll
+        for (int q = 0; q < kBtLoads; ++q) {
+            const uint32_t o = 1024u * (kBtLoads * w + q) + 16u * (uint32_t)lane;
+            const uint32_t kr = o / kBtRow, cb = o % kBtRow;
+            d.vb[q] = cb < (uint32_t)kBtData ? kr * B.row_bytes + cb : kOOB;
+        }
+        d.bt_pair = 64u * B.row_bytes;
+    }
     d.pa = (64u * w + (uint32_t)lane) * A.row_bytes;
     d.kblocks = (int)(k / 32);
     d.sf_kt = 0;

@@ -2,7 +2,8 @@
 // gfx950 ("GEMM + RoPE + MXFP8 Projection (SM100)", Equations).
 //
 // One workgroup computes 256 tokens x one head (192 features) of
-// Y = x W^T with the BF16 32x32x16 MFMA, or, for MXFP8 inputs (E4M3 codes
+// Y = x W^T (w as [out, in], or as [in, out] staged K-major and read with
+// the transposing LDS reads) with the BF16 32x32x16 MFMA, or, for MXFP8 inputs (E4M3 codes
 // with row-major E8M0 scales per 32 elements of a row), the scaled
 // 32x32x64 f8f6f4 MFMA (fp32 accumulation either way); the waves are
 // 2 (tokens) x 2 (features: 0..95 and 96..191).  The second feature wave
@@ -43,8 +44,16 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
 
     OperandDesc A{p.x + m0 * p.row_bytes, (uint32_t)(rows_a * p.row_bytes), p.row_bytes, nullptr,
                   0, 0, 0, 0, 0};
+    // B: head h's 192 rows of w [out, in], or (FMT_BF16_BT) its 192 columns
+    // of w [in, out], read K row by K row (K rows past q_lora read zeros)
     OperandDesc B{p.w + h * HD * p.row_bytes, (uint32_t)(HD * p.row_bytes), p.row_bytes, nullptr,
                   0, 0, 0, 0, 0};
+    if constexpr (F == FMT_BF16_BT) {
+        const uint32_t kstride = (uint32_t)(2 * n_out);
+        B.base = p.w + 2 * HD * h;
+        B.bytes = (uint32_t)(p.q_lora - 1) * kstride + 2u * HD;
+        B.row_bytes = kstride;
+    }
     if constexpr (F == FMT_E4M3_RM) {
         const uint32_t srow = (uint32_t)(p.q_lora / 32);          // scale bytes per row
         A.sf = p.x_scale + m0 * srow;
@@ -185,7 +194,7 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
 hipError_t launch_proj_rope(const ProjRopeArgs &a, hipStream_t s)
 {
     if (a.tokens == 0 || a.heads == 0) return hipSuccess;
-    if (!a.w_out_in) return hipErrorNotSupported;
+    if (!a.w_out_in && a.mxfp8) return hipErrorNotSupported;
     ProjParams p;
     p.x = reinterpret_cast<const uint8_t *>(a.x);
     p.w = reinterpret_cast<const uint8_t *>(a.w);
@@ -197,7 +206,8 @@ hipError_t launch_proj_rope(const ProjRopeArgs &a, hipStream_t s)
     p.row_bytes = (uint32_t)(a.mxfp8 ? a.q_lora : 2 * a.q_lora);
     dim3 grid((unsigned)a.heads, (unsigned)((a.tokens + kTileM - 1) / kTileM));
     if (a.mxfp8) hipLaunchKernelGGL(k_proj_rope<FMT_E4M3_RM>, grid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL(k_proj_rope<FMT_BF16>, grid, dim3(kThreads), 0, s, p);
+    else if (a.w_out_in) hipLaunchKernelGGL(k_proj_rope<FMT_BF16>, grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL(k_proj_rope<FMT_BF16_BT>, grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -260,8 +260,10 @@ int grouped_gemm_dswiglu(const void *a, const void *b, const uint8_t *sfa, const
  *  x    (tokens, q_lora) row-major: bf16 (in_dtype BF16) or E4M3 codes
  *       (in_dtype E4M3, the page's MXFP8-input path)
  *  w    w_out_in = 1: (num_heads*head_dim, q_lora) [out, in], same dtype
- *       as x.  w_out_in = 0 ([in, out]) returns UNSUPPORTED: that layout is
- *       not built.
+ *       as x.  w_out_in = 0: (q_lora, num_heads*head_dim) [in, out], the
+ *       page's default layout, BF16 inputs only (the page's MXFP8 inputs
+ *       take w and w_scale as [out, in]; E4M3 with w_out_in = 0 returns
+ *       UNSUPPORTED).  Both layouts give identical results.
  *  x_scale  (tokens, q_lora/32) E8M0, row-major: byte (t, b) scales
  *           x[t, 32b .. 32b+31]                      (E4M3 inputs only)
  *  w_scale  (num_heads*head_dim, q_lora/32) E8M0, row-major, [out, in]

@@ -159,13 +159,14 @@ def test_proj_rope_validation():
     assert vp(in_dtype=bsg.E4M3) == NULLPTR
     assert vp(in_dtype=bsg.E4M3, x_scale=P, w_scale=P) == OK
     assert vp(in_dtype=bsg.E4M3, x_scale=P + 2, w_scale=P) == ALIGN
-    assert vp(in_dtype=bsg.E4M3, x_scale=P, w_scale=P, w_out_in=0) == UNSUP
+    assert vp(in_dtype=bsg.E4M3, x_scale=P, w_scale=P, w_out_in=0) == UNSUP   # MXFP8 w comes [out, in]
     assert vp(in_dtype=bsg.E4M3, x_scale=P, w_scale=P, q_lora=160) == UNSUP
     assert vp(in_dtype=bsg.E2M1X2) == DTYPE
     assert vp(x_scale=P) == SHAPE                        # scales only on the MXFP8 path
     assert vp(head_dim=128) == UNSUP
     assert vp(q_lora=100) == SHAPE
-    assert vp(w_out_in=0) == UNSUP                       # [in, out] weight not built
+    assert vp(w_out_in=0) == OK                          # BF16 w as [in, out]
+    assert vp(w_out_in=2) == SHAPE
 
 
 def vdsw(**kw):

@@ -113,6 +113,51 @@ def test_proj_rope_independent_angle_tables(in_dtype):
     oracle_check(p, qr, sr, qc, sc, 0, 384, f"random tables {in_dtype}")
 
 
+@pytest.mark.parametrize("case", [
+    dict(tokens=256, q_lora=256, heads=3),
+    dict(tokens=384, q_lora=96, heads=2),      # a 128-token tail tile, K = 96 (a partial pair)
+    dict(tokens=128, q_lora=1536, heads=1),
+])
+def test_proj_rope_w_in_out_matches_oracle(case):
+    """w as [in, out] (w_out_in = 0, "GEMM + RoPE + MXFP8 Projection (SM100)",
+    Shapes: w is (Q_LORA, NUM_HEADS * HEAD_DIM)): the B tile is staged K-major
+    and read with the transposing LDS reads."""
+    say(f"proj_rope w [in, out] parity {case}")
+    p = W.proj_rope_problem(case["tokens"], case["q_lora"], case["heads"], seed=11, w_out_in=False)
+    assert p.t["w"].shape == (case["q_lora"], case["heads"] * 192)
+    qr, sr, qc, sc = run_proj(p)
+    oracle_check(p, qr, sr, qc, sc, 0, case["tokens"], "w_in_out " + str(case))
+
+
+def test_proj_rope_w_layouts_agree_bit_for_bit():
+    """The same weights as [out, in] and as [in, out] give identical outputs:
+    both layouts feed the MFMA the same values in the same order."""
+    say("proj_rope w layouts")
+    p1 = W.proj_rope_problem(256, 512, 4, seed=12, w_out_in=True)
+    p0 = W.proj_rope_problem(256, 512, 4, seed=12, w_out_in=True)
+    p0.t["w"] = p1.t["w"].t().contiguous()
+    p0.sizes["w_out_in"] = False
+    p0.t["cos"], p0.t["sin"], _ = W.rope_tables_random(256, 64, seed=13)
+    p1.t["cos"], p1.t["sin"] = p0.t["cos"], p0.t["sin"]
+    a = run_proj(p1)
+    b = run_proj(p0)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    oracle_check(p0, *b, 0, 256, "w [in, out] random tables")
+
+
+def test_proj_rope_w_in_out_full_size_sampled():
+    """x (4096,1536), w (1536, 24576) as [in, out], 128 heads x 192: the first
+    and last 128-token panels against the oracle."""
+    say("proj_rope w [in, out] full size")
+    p = W.proj_rope_problem(4096, 1536, 128, seed=0, device="cuda", w_out_in=False)
+    qr, sr, qc, sc = run_proj(p)
+    p.t = {k: v.cpu() for k, v in p.t.items()}
+    for t0 in (0, 3968):
+        say(f"  oracle tokens {t0}..{t0 + 127}")
+        oracle_check(p, qr, sr, qc, sc, t0, t0 + 128, f"w_in_out tokens {t0}")
+
+
 def test_proj_rope_full_size_sampled():
     """x (4096,1536), 128 heads x 192: sampled 128-token panels vs the oracle."""
     say("proj_rope full size")

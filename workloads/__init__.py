@@ -351,6 +351,8 @@ def moe_mxfp8_srelu(device="cuda", seed=0, tokens=28672, experts=32, n=4096, k=7
                                  tanh_clamp=32.0, d_dtype=d_dtype, **kw)
 
 
-def proj_rope_dsv3(device="cuda", seed=0, tokens=4096, in_dtype="bf16"):
-    """DeepSeek-V3 Q up-projection: x (4096,1536), 128 heads x 192, rope on trailing 64."""
-    return proj_rope_problem(tokens, 1536, 128, 192, 64, seed=seed, device=device, in_dtype=in_dtype)
+def proj_rope_dsv3(device="cuda", seed=0, tokens=4096, in_dtype="bf16", w_out_in=True):
+    """DeepSeek-V3 Q up-projection: x (4096,1536), 128 heads x 192, rope on trailing 64;
+    w as [out, in] (w_out_in) or [in, out]."""
+    return proj_rope_problem(tokens, 1536, 128, 192, 64, seed=seed, device=device, in_dtype=in_dtype,
+                             w_out_in=w_out_in)
