@@ -45,7 +45,7 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         p, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
         sigs = {
-            "gemm_amax": [p] * 6 + [i64] * 4 + [i32] * 3 + [p],
+            "gemm_amax": [p] * 6 + [i64] * 4 + [i32] * 6 + [p],
             "grouped_gemm": [p] * 8 + [i64] * 4 + [i32] * 3 + [p],
             "grouped_gemm_srelu": [p] * 14 + [i64] * 4 + [i32] * 4 + [f32, p],
             "gemm_proj_rope_mxfp8": [p] * 10 + [i64] * 5 + [i32, i32, p],
@@ -55,7 +55,7 @@ def lib():
             "grouped_gemm_srelu_discrete": [p] * 14 + [i64] * 4 + [i32] * 4 + [f32, p],
             "bsg_validate_grouped_gemm_discrete": [p] * 8 + [i64] * 4 + [i32] * 3,
             "bsg_validate_grouped_gemm_srelu_discrete": [p] * 14 + [i64] * 4 + [i32] * 4 + [f32],
-            "bsg_validate_gemm_amax": [p] * 6 + [i64] * 4 + [i32] * 3,
+            "bsg_validate_gemm_amax": [p] * 6 + [i64] * 4 + [i32] * 6,
             "bsg_validate_grouped_gemm": [p] * 8 + [i64] * 4 + [i32] * 3,
             "bsg_validate_grouped_gemm_srelu": [p] * 14 + [i64] * 4 + [i32] * 4 + [f32],
             "bsg_validate_gemm_proj_rope_mxfp8": [p] * 10 + [i64] * 5 + [i32, i32],
@@ -192,11 +192,20 @@ def _d_code(d_dtype, d) -> int:
 
 
 # ---------------------------------------------------------------------------
+def _major(x, allowed, name):
+    """A major argument as the character code the C ABI takes."""
+    if not isinstance(x, str) or len(x) != 1:
+        raise ValueError(f"{name} must be one of {allowed!r}, got {x!r}")
+    return ord(x)
+
+
 def gemm_amax(a, b, sfa, sfb, c, amax, m, n, k, l, ab_dtype="e4m3", c_dtype=None,
-              sf_vec_size=32, stream=None, validate_only=False):
+              sf_vec_size=32, a_major="k", b_major="k", c_major="n", stream=None, validate_only=False):
     """C = sum_k A_hat B_hat per batch and Amax = max |C| (see include/bsg.h).
     c_dtype: a torch float dtype, "e4m3" / "e5m2" (FP8 C) or "e2m1" (packed
-    FP4 C, (M, N/2, L) bytes); the last three with FP4 operands only."""
+    FP4 C, (M, N/2, L) bytes); the last three with FP4 operands only.
+    a_major "k" (memory [L][M][K]) or "m" ([L][K][M]); b_major "k" or "n"
+    ([L][K][N]); c_major "n" ([L][M][N]) or "m" ([L][N][M])."""
     cd = _d_code(c_dtype, c)
     ab = _ab_code(ab_dtype)
     if m * n * l > 0:
@@ -206,7 +215,8 @@ def gemm_amax(a, b, sfa, sfb, c, amax, m, n, k, l, ab_dtype="e4m3", c_dtype=None
         _need(c, "c", _out_bytes(cd, l * m * n), cd)
     _need(amax, "amax", 4, torch.float32)
     args = [_ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), _ptr(c), _ptr(amax), m, n, k, l,
-            ab, cd, sf_vec_size]
+            ab, cd, sf_vec_size, _major(a_major, "km", "a_major"), _major(b_major, "kn", "b_major"),
+            _major(c_major, "nm", "c_major")]
     if validate_only:
         return lib().bsg_validate_gemm_amax(*args)
     _check(lib().gemm_amax(*args, _stream(stream)))

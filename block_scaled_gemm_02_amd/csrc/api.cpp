@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <utility>
 
 #include "../../include/bsg.h"
 #include "launch.hpp"
@@ -122,38 +123,64 @@ static int check_tiles(int64_t m_tiles, int64_t n, int64_t l)
 
 int bsg_validate_gemm_amax(const void *a, const void *b, const uint8_t *sfa, const uint8_t *sfb,
                            void *c, float *amax, int64_t m, int64_t n, int64_t k, int64_t l,
-                           int ab_dtype, int c_dtype, int sf_vec_size)
+                           int ab_dtype, int c_dtype, int sf_vec_size, int a_major, int b_major, int c_major)
 {
     (void)amax;
     int st = check_ab_sf(ab_dtype, sf_vec_size);
     if (st) return st;
     if (m < 0 || n < 0 || k < 0 || l < 0) return fail(BSG_ERR_SHAPE, "negative size");
     if (k % 32) return fail(BSG_ERR_SHAPE, "K=%lld must be a multiple of sf_vec_size 32", (long long)k);
+    if ((a_major != 'k' && a_major != 'm') || (b_major != 'k' && b_major != 'n') ||
+        (c_major != 'n' && c_major != 'm'))
+        return fail(BSG_ERR_SHAPE, "majors must be a_major 'k'/'m', b_major 'k'/'n', c_major 'n'/'m'");
     const bool fp8_c = c_dtype == BSG_E4M3 || c_dtype == BSG_E5M2, fp4_c = c_dtype == BSG_E2M1X2;
     if (fp8_c && ab_dtype != BSG_E2M1X2)
         return fail(BSG_ERR_UNSUPPORTED, "FP8 C with FP8 A/B is disabled (FP8 C takes FP4 A/B)");
     if (fp4_c && ab_dtype != BSG_E2M1X2) return fail(BSG_ERR_DTYPE, "FP4 C requires FP4 A/B");
     if (!is_float_out(c_dtype) && !fp8_c && !fp4_c)
         return fail(BSG_ERR_DTYPE, "c_dtype %d is not an output dtype", c_dtype);
+    // "GEMM + Amax (SM100)", Layouts and strides: packed FP4 A/B are k-major, packed FP4 C n-major
+    if (ab_dtype == BSG_E2M1X2 && (a_major != 'k' || b_major != 'k'))
+        return fail(BSG_ERR_SHAPE, "packed FP4 A and B must be k-major");
+    if (fp4_c && c_major != 'n') return fail(BSG_ERR_SHAPE, "packed FP4 C must be n-major");
     if (m * n * l == 0) return BSG_OK;   // nothing to read or write but amax
     if (!a || !b || !sfa || !sfb || !c) return fail(BSG_ERR_NULLPTR, "a, b, sfa, sfb and c are required");
     if (k > 0 && (!aligned16(a) || !aligned16(b))) return fail(BSG_ERR_ALIGN, "A and B must be 16-byte aligned");
-    if (!aligned16(c) || (fp4_c ? n % 32 : (n * elem_bytes(c_dtype)) % 16))
+    // C rows run along its contiguous dimension: N (n-major) or M (m-major)
+    const int64_t c_row = c_major == 'n' ? n : m;
+    if (!aligned16(c) || (fp4_c ? c_row % 32 : (c_row * elem_bytes(c_dtype)) % 16))
         return fail(BSG_ERR_ALIGN, "C must be 16-byte aligned with rows of a multiple of 16 bytes");
     if ((int64_t)row_bytes(ab_dtype, k) * 256 >= (1ll << 31))
         return fail(BSG_ERR_UNSUPPORTED, "K too large for 32-bit tile offsets");
-    return check_tiles((m + 255) / 256, n, l);
+    // MN-major operands: K rows of M (N) one-byte codes, 16-byte aligned, and
+    // a batch's K + 256 rows within 32-bit offsets
+    if (a_major == 'm' && m % 16) return fail(BSG_ERR_ALIGN, "m-major A needs M %% 16 == 0 (M=%lld)", (long long)m);
+    if (b_major == 'n' && n % 16) return fail(BSG_ERR_ALIGN, "n-major B needs N %% 16 == 0 (N=%lld)", (long long)n);
+    if ((a_major == 'm' && (k + 256) * m >= (1ll << 31)) || (b_major == 'n' && (k + 256) * n >= (1ll << 31)))
+        return fail(BSG_ERR_UNSUPPORTED, "MN-major operand too large for 32-bit offsets");
+    return c_major == 'n' ? check_tiles((m + 255) / 256, n, l) : check_tiles((n + 255) / 256, m, l);
 }
 
 int gemm_amax(const void *a, const void *b, const uint8_t *sfa, const uint8_t *sfb, void *c,
               float *amax, int64_t m, int64_t n, int64_t k, int64_t l, int ab_dtype, int c_dtype,
-              int sf_vec_size, void *stream)
+              int sf_vec_size, int a_major, int b_major, int c_major, void *stream)
 {
-    int st = bsg_validate_gemm_amax(a, b, sfa, sfb, c, amax, m, n, k, l, ab_dtype, c_dtype, sf_vec_size);
+    int st = bsg_validate_gemm_amax(a, b, sfa, sfb, c, amax, m, n, k, l, ab_dtype, c_dtype, sf_vec_size,
+                                    a_major, b_major, c_major);
     if (st) return st;
     if ((st = check_device())) return st;
     bsg::GemmAmaxArgs args{static_cast<const uint8_t *>(a), static_cast<const uint8_t *>(b), sfa, sfb,
                            c, amax, m, n, k, l, fmt_of(ab_dtype), c_dtype};
+    args.a_mn = a_major == 'm';
+    args.b_mn = b_major == 'n';
+    if (c_major == 'm') {
+        // C stored m-major is C^T stored n-major: compute C^T = B A^T, with
+        // B (and its scales) as the first operand
+        std::swap(args.a, args.b);
+        std::swap(args.sfa, args.sfb);
+        std::swap(args.m, args.n);
+        std::swap(args.a_mn, args.b_mn);
+    }
     return launch_status(bsg::launch_gemm_amax(args, static_cast<hipStream_t>(stream)), "gemm_amax");
 }
 

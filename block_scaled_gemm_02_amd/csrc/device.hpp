@@ -54,12 +54,37 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // false): each pair's B tile is staged K-major and its fragments are formed
 // with the transposing LDS reads (see the B loads and read_one).
 enum Fmt : int { FMT_E4M3 = 0, FMT_E2M1 = 1, FMT_BF16 = 2, FMT_E4M3_RM = 3, FMT_E5M2 = 4, FMT_BF16_BT = 5 };
+// Layout flags added to FMT_E4M3 / FMT_E5M2: operand A is stored m-major
+// (FMT_TA, memory [L][K][M]) or B n-major (FMT_TB, [L][K][N]) instead of
+// k-major ("GEMM + Amax (SM100)", Input/Output tensors: the (1, M, M*K)
+// strides).  Such an operand's pair tile is staged K-major in LDS and its
+// fragments are formed with the 8-bit transposing LDS reads (see the
+// constants kTRow... and read_one).
+enum : int { FMT_TA = 8, FMT_TB = 16 };
+constexpr int fmt_base(int f) { return f & 7; }
+constexpr bool a_t(int f) { return (f & FMT_TA) != 0; }
+constexpr bool b_t(int f) { return (f & FMT_TB) != 0; }
 // one-byte codes: one 32x32x64 MFMA per block per 64-byte step
-constexpr bool is_fp8(int f) { return f == FMT_E4M3 || f == FMT_E4M3_RM || f == FMT_E5M2; }
+constexpr bool is_fp8(int f)
+{
+    return fmt_base(f) == FMT_E4M3 || fmt_base(f) == FMT_E4M3_RM || fmt_base(f) == FMT_E5M2;
+}
 constexpr bool is_bf16(int f) { return f == FMT_BF16 || f == FMT_BF16_BT; }
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2;
+
+// K-major FP8 operand tile (FMT_TA / FMT_TB) in a pair slot: the pair's 128
+// K rows, each holding the tile's 256 MN columns (one byte each) at a
+// stride of 288 bytes (36 KB).  A transposing read has the 16 lanes of a
+// group read 8 bytes each from 8 consecutive K rows (two lanes per row);
+// the two groups of a half-wave cover 32 columns of those 8 rows, and with
+// 288 = 256 + 32 the 8 row segments start 32 bytes apart in the 256-byte
+// bank space, so the read is conflict-free.  9 direct-to-LDS loads per wave
+// fill the 36 KB; lanes that fall in the 32 padding bytes of a row, or on
+// columns past M (N), read zeros.
+constexpr int kTRow = 288, kTData = 256, kTBytes = 128 * kTRow, kTLoads = kTBytes / 1024 / 4;
 
 // K-major B tile of FMT_BF16_BT in a pair slot: the pair's 64 K rows, each
 // holding the tile's (up to 192) BF16 columns in 384 bytes, at a stride of
@@ -212,6 +237,10 @@ struct OperandDesc {
     // FMT_E4M3_RM only: sf is the scale row of this tile's row 0, sf_rm the
     // bytes per scale row (K/32, a multiple of 4), sf_bytes the readable bytes
     uint32_t sf_rm = 0, sf_bytes = 0;
+    // MN-major operand (FMT_TA / FMT_TB): base is the tile's first column in
+    // K row 0, row_bytes the stride between K rows (M or N), bytes ends at
+    // the last K row's last column, and mn_valid columns of the tile exist
+    uint32_t mn_valid = 0;
 };
 
 // The LDS holds two "pair slots"; a pair slot holds two consecutive K steps
@@ -248,11 +277,17 @@ constexpr int kPK = 2 * kKS;               // bytes per row per pair slot
 constexpr int kPA = kTileM * kPK;          // 32 KB
 constexpr int kPB = 256 * kPK;             // 32 KB (NB = 4)
 
+// Bytes of a pair slot's A and B regions (the scale atoms follow them).
+template <int F>
+constexpr int a_region() { return a_t(F) ? kTBytes : kPA; }
+template <int F>
+constexpr int b_region() { return b_t(F) ? kTBytes : kPB; }
+
 template <int F>
 struct Ring {
     static constexpr bool kScaled = !is_bf16(F);
-    static constexpr int kScaleSets = F == FMT_E2M1 ? 2 : (is_fp8(F) ? 1 : 0);
-    static constexpr int kSlot = kPA + kPB + kScaleSets * 4096;
+    static constexpr int kScaleSets = fmt_base(F) == FMT_E2M1 ? 2 : (is_fp8(F) ? 1 : 0);
+    static constexpr int kSlot = a_region<F>() + b_region<F>() + kScaleSets * 4096;
     static constexpr int kBytes = 2 * kSlot;
     static constexpr int kWaveStage = kSlot / 2 & ~15;   // epilogue staging bytes per wave
 };
@@ -315,9 +350,11 @@ template <int NB>
 struct PipeDesc {
     static constexpr int LB = 2 * NB;  // B loads per wave per pair (16*NB rows / 8)
     i32x4 ra, rb, rs;         // operand panels; this wave's scale atoms (buffer resources)
-    uint32_t row_bytes;
-    uint32_t va[8], vb[LB > kBtLoads ? LB : kBtLoads];   // per-lane voffset of this wave's code loads (pair 0)
-    uint32_t bt_pair;         // FMT_BF16_BT: bytes of B per pair along K (64 K rows)
+    uint32_t row_bytes;       // bytes of a k-major row along K (the K extent)
+    static constexpr int LV = LB > kTLoads ? LB : kTLoads;   // >= kBtLoads
+    uint32_t va[kTLoads], vb[LV];   // per-lane voffset of this wave's code loads (pair 0)
+    uint32_t at_pair;         // FMT_TA: bytes of A per pair along K (128 K rows)
+    uint32_t bt_pair;         // FMT_BF16_BT / FMT_TB: bytes of B per pair along K (64 / 128 K rows)
     uint32_t lc16;            // 16 * logical chunk of this lane's loads
     uint32_t vs;              // per-lane voffset of this wave's scale atom (kt = 0)
     uint32_t pa;              // per-lane voffset of the A line this lane prefetches (pair 0)
@@ -358,25 +395,35 @@ __device__ __forceinline__ uint8_t *wave_stage(const RingSlots<F> &ring, int w)
 // the odd stage reuses the even stage's scale words.
 template <int F>
 constexpr bool scales_in_stage(bool odd) { return Ring<F>::kScaled && !(is_fp8(F) && odd); }
+template <int F>
+constexpr int a_loads() { return a_t(F) ? kTLoads : 8; }
 template <int F, int NB>
-constexpr int b_loads() { return F == FMT_BF16_BT ? kBtLoads : 2 * NB; }
+constexpr int b_loads() { return b_t(F) ? kTLoads : (F == FMT_BF16_BT ? kBtLoads : 2 * NB); }
 template <int F, int NB>
-constexpr int loads_per_pair() { return 8 + b_loads<F, NB>() + (F == FMT_E4M3_RM ? 2 : Ring<F>::kScaleSets); }
+constexpr int loads_per_pair()
+{
+    return a_loads<F>() + b_loads<F, NB>() + (F == FMT_E4M3_RM ? 2 : Ring<F>::kScaleSets);
+}
 template <int F, int NB>
 constexpr int mfmas_per_step() { return (is_fp8(F) ? 1 : 2) * 4 * NB; }
-// B reads of a stage: one 16-byte read per chunk, or (FMT_BF16_BT) two
+// Reads of a stage: one 16-byte read per chunk, or (K-major staging) two
 // 8-byte transposing reads per chunk
+template <int F>
+constexpr int a_reads() { return a_t(F) ? 16 : 8; }
 template <int F, int NB>
-constexpr int b_reads() { return F == FMT_BF16_BT ? 4 * NB : 2 * NB; }
+constexpr int b_reads() { return (b_t(F) || F == FMT_BF16_BT) ? 4 * NB : 2 * NB; }
 template <int F, int NB>
-constexpr int reads_in_stage(bool odd) { return 8 + b_reads<F, NB>() + (scales_in_stage<F>(odd) ? 2 : 0); }
+constexpr int reads_in_stage(bool odd)
+{
+    return a_reads<F>() + b_reads<F, NB>() + (scales_in_stage<F>(odd) ? 2 : 0);
+}
 
 // Where this wave's loads of pair p go: code offset (K position, or out of
 // range past the row end) and scale-atom offset of each atom set.
 struct PairAddr {
     uint32_t kb_oob[2];       // added to va/vb of loads with even / odd index
     uint32_t so[2];           // scale-atom voffsets
-    uint32_t kbt;             // FMT_BF16_BT: added to vb (K rows past K read zeros: range check)
+    uint32_t kat, kbt;        // K-major staging: added to va / vb (K rows past K read zeros: range check)
 };
 template <int F, int NB>
 __device__ __forceinline__ PairAddr pair_addr(const PipeDesc<NB> &d, int pair)
@@ -385,6 +432,7 @@ __device__ __forceinline__ PairAddr pair_addr(const PipeDesc<NB> &d, int pair)
     const uint32_t kb = (uint32_t)pair * kPK;
     a.kb_oob[0] = kb + ((kb + d.lc16 < d.row_bytes) ? 0u : kOOB);
     a.kb_oob[1] = kb + ((kb + (d.lc16 ^ 16u) < d.row_bytes) ? 0u : kOOB);
+    a.kat = (uint32_t)pair * d.at_pair;
     a.kbt = (uint32_t)pair * d.bt_pair;
     if constexpr (F == FMT_E4M3_RM) {
         // row-major scales: the pair's 4 bytes of a row follow its previous pair's
@@ -394,33 +442,34 @@ __device__ __forceinline__ PairAddr pair_addr(const PipeDesc<NB> &d, int pair)
         // an atom covers 128 K elements: one pair (E4M3) or one step (E2M1)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int kt = F == FMT_E2M1 ? 2 * pair + h : pair;
+            const int kt = fmt_base(F) == FMT_E2M1 ? 2 * pair + h : pair;
             a.so[h] = kt < d.sf_kt ? d.vs + (uint32_t)kt * 512u : kOOB;
         }
     }
     return a;
 }
 
-// Load number L of this wave's share of a pair: A rows (L < 8), B rows
-// (L < 8 + 2NB), then the scale atom(s).
+// Load number L of this wave's share of a pair: A (8 loads of 8 rows, or 9
+// KB of the K-major tile), B, then the scale atom(s).  Each load fills the
+// 1 KB of the region that follows the wave's previous one.
 template <int F, int NB, int L>
 __device__ __forceinline__ void load_one(const PipeDesc<NB> &d, uint8_t *st, const PairAddr &a, int w)
 {
-    constexpr int LB = b_loads<F, NB>();
-    if constexpr (L < 8) {
-        lds_load16(d.ra, st + 1024 * (8 * w + L), d.va[L] + a.kb_oob[L & 1]);
-    } else if constexpr (F == FMT_BF16_BT && L < 8 + LB) {
-        // K-major B: 1 KB of the pair's 28 KB K-row block per load (padding
-        // lanes read zeros)
-        lds_load16(d.rb, st + kPA + 1024 * (LB * w + (L - 8)), d.vb[L - 8] + a.kbt);
-    } else if constexpr (L < 8 + LB) {
-        lds_load16(d.rb, st + kPA + 1024 * (LB * w + (L - 8)), d.vb[L - 8] + a.kb_oob[(L - 8) & 1]);
+    constexpr int LA = a_loads<F>(), LB = b_loads<F, NB>();
+    constexpr int SC = a_region<F>() + b_region<F>();
+    if constexpr (L < LA) {
+        lds_load16(d.ra, st + 1024 * (LA * w + L), d.va[L] + (a_t(F) ? a.kat : a.kb_oob[L & 1]));
+    } else if constexpr (L < LA + LB) {
+        // K-major B (FMT_BF16_BT, FMT_TB): K rows past K and padding lanes read zeros
+        constexpr int q = L - LA;
+        constexpr bool kmaj = b_t(F) || F == FMT_BF16_BT;
+        lds_load16(d.rb, st + a_region<F>() + 1024 * (LB * w + q), d.vb[q] + (kmaj ? a.kbt : a.kb_oob[q & 1]));
     } else if constexpr (F == FMT_E4M3_RM) {
-        constexpr int h = L - 8 - LB;      // rows 0-15 (h = 0) or 16-31 (h = 1) of each 32-row block
-        lds_load4(d.rs, st + kPA + kPB + 1024 * w + 256 * h, a.so[h]);
+        constexpr int h = L - LA - LB;     // rows 0-15 (h = 0) or 16-31 (h = 1) of each 32-row block
+        lds_load4(d.rs, st + SC + 1024 * w + 256 * h, a.so[h]);
     } else {
-        constexpr int h = L - 8 - LB;
-        lds_load16(d.rs, st + kPA + kPB + 4096 * h + 1024 * w, a.so[h]);
+        constexpr int h = L - LA - LB;
+        lds_load16(d.rs, st + SC + 4096 * h + 1024 * w, a.so[h]);
     }
 }
 
@@ -440,8 +489,13 @@ __device__ __forceinline__ void issue_pair(const PipeDesc<NB> &d, uint8_t *st, i
 template <int F, int NB>
 __device__ __forceinline__ void prefetch_a(const PipeDesc<NB> &d, const RingSlots<F> &ring, int pair, int w)
 {
-    const uint32_t kb = (uint32_t)pair * kPK;
-    lds_load4(d.ra, ring.sink + 256 * w, kb < d.row_bytes ? d.pa + kb : kOOB);
+    if constexpr (a_t(F)) {
+        // m-major A: the pair's 256 lines are 2 per K row (past K: range check)
+        lds_load4(d.ra, ring.sink + 256 * w, d.pa + (uint32_t)pair * d.at_pair);
+    } else {
+        const uint32_t kb = (uint32_t)pair * kPK;
+        lds_load4(d.ra, ring.sink + 256 * w, kb < d.row_bytes ? d.pa + kb : kOOB);
+    }
 }
 
 // LDS read number R of a step's fragments: A chunks (R < 8), B chunks, then
@@ -460,34 +514,67 @@ __device__ __forceinline__ ReadAddr read_addr(const uint8_t *st, int wm, int wn,
     const uint32_t swz = (row & 7) ^ ((row >> 3) & 1);
     r.p0 = 16u * ((4u * H + g) ^ swz);
     r.p1 = 16u * ((4u * H + 2u + g) ^ swz);
-    r.a0 = st + (128u * wm + row) * kPK;
-    if constexpr (F == FMT_BF16_BT) {
+    // K-major FP8 tile (16-lane group G = lane / 16, lane s = lane % 16 in
+    // it; the group holds MFMA rows 16(G%2) .. + 15 with K half g = G/2):
+    // lane s reads 8 columns, 8(s%2) onwards, of K row 16(G/2) + s/2 of the
+    // step (+ 32 for chunk 1, + 8 for a chunk's second read); lane j of the
+    // group then holds 8 consecutive K values of column 16(G%2) + j
+    const uint32_t G = (uint32_t)lane >> 4, s = (uint32_t)lane & 15;
+    const uint32_t trow = (64u * H + 16u * (G >> 1) + (s >> 1)) * kTRow + 16u * (G & 1) + 8u * (s & 1);
+    if constexpr (a_t(F)) r.a0 = st + trow + 128u * wm;
+    else r.a0 = st + (128u * wm + row) * kPK;
+    if constexpr (b_t(F)) {
+        r.b0 = st + a_region<F>() + trow + 32u * NB * wn;
+    } else if constexpr (F == FMT_BF16_BT) {
         // transposing reads (16-lane group G = lane / 16, lane s = lane % 16
         // in it): lane s reads 4 columns of K row 8(G/2) + s/4 (+ 4 for the
         // second read of a chunk, + 16 for chunk 1, + 32 in the pair's second
         // step), columns 16(G%2) + 4(s%4) of the block; lane j of the group
         // then holds 4 consecutive K values of column 16(G%2) + j
-        const uint32_t G = (uint32_t)lane >> 4, s = (uint32_t)lane & 15;
-        r.b0 = st + kPA + (32u * H + 8u * (G >> 1) + (s >> 2)) * kBtRow +
+        r.b0 = st + a_region<F>() + (32u * H + 8u * (G >> 1) + (s >> 2)) * kBtRow +
                2u * (32u * NB * wn + 16u * (G & 1) + 4u * (s & 3));
     } else {
-        r.b0 = st + kPA + (32u * NB * wn + row) * kPK;
+        r.b0 = st + a_region<F>() + (32u * NB * wn + row) * kPK;
     }
-    const uint8_t *sc = st + kPA + kPB + (F == FMT_E2M1 ? 4096 * H : 0);
+    const uint8_t *sc = st + a_region<F>() + b_region<F>() + (fmt_base(F) == FMT_E2M1 ? 4096 * H : 0);
     r.sa = sc + 1024 * wm + 16 * row;
     r.sb = sc + 1024 * (2 + wn) + 16 * row;
     return r;
 }
+// One 8-byte transposing read of a K-major FP8 tile into half e of chunk
+// register c: K values [8e, 8e + 8) of the chunk's 16.
+template <int E>
+__device__ __forceinline__ void read_tr8(i32x4 &c, const uint8_t *p)
+{
+    const i32x2_t u = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(lds_void *)p);
+    if constexpr (E == 0) {
+        c.x = u.x;
+        c.y = u.y;
+    } else {
+        c.z = u.x;
+        c.w = u.y;
+    }
+}
+
 template <int F, int NB, int R>
 __device__ __forceinline__ void read_one(Frags<NB> &f, const ReadAddr &r)
 {
-    if constexpr (R < 8) {
+    constexpr int RA = a_reads<F>();
+    if constexpr (a_t(F) && R < RA) {
+        // chunk h of block i: K [16g + 32h, +16) of the lane's column as two
+        // reads of 8 K values each (e = 0, 1)
+        constexpr int i = R / 4, h = (R / 2) % 2, e = R % 2;
+        read_tr8<e>(f.a[i][h], r.a0 + (32 * h + 8 * e) * kTRow + 32 * i);
+    } else if constexpr (R < RA) {
         constexpr int i = R / 2, h = R % 2;
         f.a[i][h] = *reinterpret_cast<const i32x4 *>(r.a0 + 32 * kPK * i + (h ? r.p1 : r.p0));
-    } else if constexpr (F == FMT_BF16_BT && R < 8 + 4 * NB) {
+    } else if constexpr (b_t(F) && R < RA + 4 * NB) {
+        constexpr int q = R - RA, j = q / 4, h = (q / 2) % 2, e = q % 2;
+        read_tr8<e>(f.b[j][h], r.b0 + (32 * h + 8 * e) * kTRow + 32 * j);
+    } else if constexpr (F == FMT_BF16_BT && R < RA + 4 * NB) {
         // chunk h of block j: K [8g + 16h, +8) of the lane's column as two
         // reads of 4 K values each (e = 0, 1)
-        constexpr int q = R - 8, j = q / 4, h = (q / 2) % 2, e = q % 2;
+        constexpr int q = R - RA, j = q / 4, h = (q / 2) % 2, e = q % 2;
         const uint8_t *p = r.b0 + (16 * h + 4 * e) * kBtRow + 64 * j;
         const auto v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(lds_void *)p);
         const i32x2_t u = __builtin_bit_cast(i32x2_t, v);
@@ -498,10 +585,10 @@ __device__ __forceinline__ void read_one(Frags<NB> &f, const ReadAddr &r)
             f.b[j][h].z = u.x;
             f.b[j][h].w = u.y;
         }
-    } else if constexpr (R < 8 + 2 * NB) {
-        constexpr int j = (R - 8) / 2, h = (R - 8) % 2;
+    } else if constexpr (R < RA + 2 * NB) {
+        constexpr int j = (R - RA) / 2, h = (R - RA) % 2;
         f.b[j][h] = *reinterpret_cast<const i32x4 *>(r.b0 + 32 * kPK * j + (h ? r.p1 : r.p0));
-    } else if constexpr (R == 8 + b_reads<F, NB>()) {
+    } else if constexpr (R == RA + b_reads<F, NB>()) {
         f.sa = *reinterpret_cast<const i32x4 *>(r.sa);
     } else {
         f.sb = *reinterpret_cast<const i32x4 *>(r.sb);
@@ -546,10 +633,10 @@ __device__ __forceinline__ void mma_one(f32x16 (&acc)[4][NB], const Frags<NB> &f
         const i32x8 bv{f.b[j][0].x, f.b[j][0].y, f.b[j][0].z, f.b[j][0].w,
                        f.b[j][1].x, f.b[j][1].y, f.b[j][1].z, f.b[j][1].w};
         // operand format: 0 = E4M3, 1 = E5M2 (for both operands)
-        constexpr int fm = F == FMT_E5M2 ? 1 : 0;
+        constexpr int fm = fmt_base(F) == FMT_E5M2 ? 1 : 0;
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], fm, fm, 0, sb[j], 0,
                                                                       sa[i]);
-    } else if constexpr (F == FMT_E2M1) {
+    } else if constexpr (fmt_base(F) == FMT_E2M1) {
         const i32x8 av{f.a[i][S].x, f.a[i][S].y, f.a[i][S].z, f.a[i][S].w, 0, 0, 0, 0};
         const i32x8 bv{f.b[j][S].x, f.b[j][S].y, f.b[j][S].z, f.b[j][S].w, 0, 0, 0, 0};
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], 4, 4, 2 * S, sb[j],
@@ -636,6 +723,8 @@ __device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[4][NB], const RingSl
 {
     static_assert(NB == 4 || is_bf16(F) || F == FMT_E4M3_RM, "atom scales need 128-column wave tiles");
     static_assert(F != FMT_BF16_BT || 64 * NB <= kBtData / 2, "a K-major B row holds the tile's columns");
+    static_assert(!(a_t(F) || b_t(F)) || (is_fp8(F) && F != FMT_E4M3_RM && NB == 4),
+                  "MN-major operands: FP8 with scale atoms, 256 x 256 tiles");
     // the wave index is uniform: keep everything derived from it in SGPRs
     const int t = threadIdx.x, lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w >> 1, wn = w & 1;
@@ -649,16 +738,33 @@ __device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[4][NB], const RingSl
     PipeDesc<NB> d;
     d.ra = make_rsrc_words(A.base, A.bytes);
     d.rb = make_rsrc_words(B.base, B.bytes);
-    d.row_bytes = A.row_bytes;
+    // K extent of a row in bytes
+    d.row_bytes = (uint32_t)(is_fp8(F) ? k : (fmt_base(F) == FMT_E2M1 ? k / 2 : 2 * k));
     const uint32_t lrow = (uint32_t)lane >> 3;                       // row within an 8-row load
     const uint32_t lchunk = ((uint32_t)lane & 7) ^ lrow;
     d.lc16 = 16u * lchunk;
+    // MN-major operand: load q of wave w fills bytes 1024 (9w + q) .. of the
+    // pair's K-major tile, 16 per lane, so a lane's byte o sits in K row
+    // o / 288 at column o % 288 (zeros for the padding past 256 and for
+    // columns past the operand's M or N)
+    auto kmajor_off = [&](int q, const OperandDesc &X) {
+        const uint32_t o = 1024u * (kTLoads * w + q) + 16u * (uint32_t)lane;
+        const uint32_t kr = o / kTRow, cb = o % kTRow;
+        return (cb < (uint32_t)kTData && cb < X.mn_valid) ? kr * X.row_bytes + cb : kOOB;
+    };
 #pragma unroll
-    for (int q = 0; q < 8; ++q) d.va[q] = (64u * w + 8u * q + lrow) * A.row_bytes + (d.lc16 ^ (16u * (q & 1)));
+    for (int q = 0; q < a_loads<F>(); ++q) {
+        if constexpr (a_t(F)) d.va[q] = kmajor_off(q, A);
+        else d.va[q] = (64u * w + 8u * q + lrow) * A.row_bytes + (d.lc16 ^ (16u * (q & 1)));
+    }
 #pragma unroll
-    for (int q = 0; q < PipeDesc<NB>::LB; ++q)
-        d.vb[q] = (16u * NB * w + 8u * q + lrow) * B.row_bytes + (d.lc16 ^ (16u * (q & 1)));
-    d.bt_pair = 0;
+    for (int q = 0; q < b_loads<F, NB>(); ++q) {
+        if constexpr (b_t(F)) d.vb[q] = kmajor_off(q, B);
+        else if constexpr (F != FMT_BF16_BT)
+            d.vb[q] = (16u * NB * w + 8u * q + lrow) * B.row_bytes + (d.lc16 ^ (16u * (q & 1)));
+    }
+    d.at_pair = a_t(F) ? 128u * A.row_bytes : 0u;
+    d.bt_pair = b_t(F) ? 128u * B.row_bytes : 0u;
     if constexpr (F == FMT_BF16_BT) {
         // B is [K][N] with B.row_bytes between K rows: load q of wave w fills
         // bytes 1024 (7w + q) .. of the pair's K-row block, 16 per lane, so a
@@ -672,7 +778,13 @@ __device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[4][NB], const RingSl
         }
         d.bt_pair = 64u * B.row_bytes;
     }
-    d.pa = (64u * w + (uint32_t)lane) * A.row_bytes;
+    if constexpr (a_t(F)) {
+        // lane (w, l) touches line (64w + l) % 2 of K row (64w + l) / 2
+        const uint32_t tl = 64u * w + (uint32_t)lane, cb = 128u * (tl & 1);
+        d.pa = cb < A.mn_valid ? (tl >> 1) * A.row_bytes + cb : kOOB;
+    } else {
+        d.pa = (64u * w + (uint32_t)lane) * A.row_bytes;
+    }
     d.kblocks = (int)(k / 32);
     d.sf_kt = 0;
     d.rs = d.ra;
@@ -706,7 +818,7 @@ __device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[4][NB], const RingSl
         d.sf_kt = (int)S.sf_k_t;
     }
 
-    const int nks = (int)((A.row_bytes + kKS - 1) / kKS);
+    const int nks = (int)((d.row_bytes + kKS - 1) / kKS);
     Frags<NB> fx, fy;
     issue_pair<F, NB>(d, ring.template at<0>(), 0, w);
     issue_pair<F, NB>(d, ring.template at<1>(), 1, w);

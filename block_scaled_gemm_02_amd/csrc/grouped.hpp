@@ -1,172 +1,19 @@
-// Dense and grouped block-scaled GEMM kernels for gfx950.
-//
-//   k_gemm_amax      "GEMM + Amax (SM100)": C = sum_k A_hat B_hat per batch,
-//                    Amax = max |C| (one atomicMax per workgroup).
-//   k_grouped        "Grouped GEMM (SM100 BF16)" and "Grouped GEMM + sReLU
-//                    (SM100)": tiles of 256 rows never straddle an expert
-//                    because every padded_offsets entry is a multiple of 256.
+// Grouped GEMM kernels for gfx950: "Grouped GEMM (SM100 BF16)", "Grouped
+// GEMM + sReLU (SM100)" and "Grouped GEMM + dSwiGLU (SM100)".  Tiles of 256
+// rows never straddle an expert because every padded_offsets entry is a
+// multiple of 256.  The kernel template is instantiated by
+// kernels_grouped.hip, kernels_srelu*.hip and kernels_dswiglu.hip.
 //
 // Epilogues work on the accumulator layout of mma_one: lane (c, g) of block
 // (i, j) owns row 32i + c and the column runs 32j + 8q + 4g + [0, 4).  Every
 // value a store depends on (prob, bias) is loaded before the first store:
 // loads and stores share one counter, so a load issued after stores would
 // wait for all of them.
-#include "device.hpp"
-#include "launch.hpp"
+#pragma once
+#include "kernels_common.hpp"
 
 namespace bsg {
 
-__device__ __forceinline__ float load_elem(const void *base, int64_t idx, int dtype)
-{
-    if (dtype == DT_F32) return static_cast<const float *>(base)[idx];
-    uint16_t h = static_cast<const uint16_t *>(base)[idx];
-    if (dtype == DT_BF16) return __uint_as_float((uint32_t)h << 16);
-    return (float)__builtin_bit_cast(_Float16, h);
-}
-
-__global__ void k_fill_zero(float *p, int64_t n)
-{
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0.0f;
-}
-
-static hipError_t zero_floats(float *p, int64_t n, hipStream_t s)
-{
-    if (!p || n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
-    return hipGetLastError();
-}
-
-static inline uint32_t row_bytes_of(int fmt, int64_t k)
-{
-    return (uint32_t)(fmt == FMT_E2M1 ? k / 2 : (fmt == FMT_BF16 ? 2 * k : k));
-}
-
-// One output of a wave's 128 x (32*NB) quadrant through the wave's LDS
-// staging region: dispatches on the run-time output type (fp32 / fp16 /
-// bf16, or the unscaled saturating E4M3 / E5M2 / packed E2M1 casts of an FP8
-// or FP4 C).  (row0, col0) is the quadrant's first element; rows_valid /
-// cols_valid bound it.  base2, if non-null, receives a copy (16-bit and
-// 32-bit types only).
-template <int NB, class Fn>
-__device__ __forceinline__ void store_quadrant_rt(int dt, uint8_t *reg, void *base, void *base2, int64_t n,
-                                                  int64_t row0, int64_t col0, int rows_valid, int cols_valid,
-                                                  f32x16 (&acc)[4][NB], int lane, Fn &&value)
-{
-    if (dt == DT_E2M1) {
-        char *dst = static_cast<char *>(base) + (row0 * n + col0) / 2;
-        store_quadrant_fp4<NB>(reg, dst, (uint32_t)(n / 2), rows_valid, cols_valid, acc, lane, value);
-        return;
-    }
-    const int es = dt == DT_F32 ? 4 : ((dt == DT_E4M3 || dt == DT_E5M2) ? 1 : 2);
-    char *dst = static_cast<char *>(base) + (row0 * n + col0) * es;
-    char *dst2 = base2 ? static_cast<char *>(base2) + (row0 * n + col0) * es : nullptr;
-    const uint32_t rb = (uint32_t)(n * es);
-    if (dt == DT_F32) store_quadrant<DT_F32, NB>(reg, dst, dst2, rb, rows_valid, cols_valid, acc, lane, value);
-    else if (dt == DT_BF16) store_quadrant<DT_BF16, NB>(reg, dst, dst2, rb, rows_valid, cols_valid, acc, lane, value);
-    else if (dt == DT_F16) store_quadrant<DT_F16, NB>(reg, dst, dst2, rb, rows_valid, cols_valid, acc, lane, value);
-    else if (dt == DT_E4M3) store_quadrant<DT_E4M3, NB>(reg, dst, nullptr, rb, rows_valid, cols_valid, acc, lane, value);
-    else store_quadrant<DT_E5M2, NB>(reg, dst, nullptr, rb, rows_valid, cols_valid, acc, lane, value);
-}
-
-// Waits for every outstanding vector-memory load before the epilogue's first
-// store (see the file comment).
-__device__ __forceinline__ void wait_loads() { s_wait_vm<0>(); }
-
-__device__ __forceinline__ int clamp_extent(int64_t extent) { return extent < 0 ? 0 : (extent > 128 ? 128 : (int)extent); }
-
-// ---------------------------------------------------------------------------
-// Dense batched GEMM + global amax
-// ---------------------------------------------------------------------------
-struct GemmAmaxParams {
-    const uint8_t *a, *b, *sfa, *sfb;
-    void *c;
-    float *amax;
-    int64_t m, n, k;
-    int64_t m_t, n_t, k_t;   // ceil(M/128), ceil(N/128), ceil(K/128)
-    uint32_t row_bytes;
-    int c_dtype;
-};
-
-// CT: the C store type, a compile-time choice (one store path per kernel
-// keeps the epilogue free of register spills).
-template <int F, int CT>
-__global__ void __launch_bounds__(256) k_gemm_amax(GemmAmaxParams p)
-{
-    BSG_DECLARE_RING(F, ring);
-    __shared__ float red[4];
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
-    const int64_t m_tiles = (p.m + kTileM - 1) / kTileM, n_tiles = (p.n + kTileN - 1) / kTileN;
-    const TileCoord tc = tile_of(blockIdx.x, m_tiles, n_tiles, (int64_t)gridDim.x);
-    const int64_t batch = tc.l;
-    const int64_t m0 = tc.mt * kTileM, n0 = tc.nt * kTileN;
-    const int64_t rows_a = p.m - m0 < kTileM ? p.m - m0 : kTileM;
-    const int64_t rows_b = p.n - n0 < kTileN ? p.n - n0 : kTileN;
-
-    OperandDesc A{p.a + (batch * p.m + m0) * p.row_bytes, (uint32_t)(rows_a * p.row_bytes),
-                  p.row_bytes, p.sfa, batch, p.m_t, p.k_t, m0 / 128, p.m_t - 1};
-    OperandDesc B{p.b + (batch * p.n + n0) * p.row_bytes, (uint32_t)(rows_b * p.row_bytes),
-                  p.row_bytes, p.sfb, batch, p.n_t, p.k_t, n0 / 128, p.n_t - 1};
-    f32x16 acc[4][4];
-    mainloop_pipe<F>(acc, ring, A, B, p.k);
-
-    // rows past M / columns past N (ragged last tiles) are computed from zero
-    // rows of A / B and not stored
-    float lmax = 0.0f;
-    const int64_t qr = m0 + 128 * wm, qc = n0 + 128 * wn;
-    auto val = [&](int, int, int, float a) {
-        lmax = fmaxf(lmax, fabsf(a));
-        return a;
-    };
-    if constexpr (CT == DT_E2M1) {
-        // packed E2M1 C: N / 2 bytes per row (N % 32 == 0, checked on the host)
-        char *const dst = static_cast<char *>(p.c) + ((batch * p.m + qr) * p.n + qc) / 2;
-        store_quadrant_fp4<4>(wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), dst, (uint32_t)(p.n / 2),
-                              clamp_extent(p.m - qr), clamp_extent(p.n - qc), acc, lane, val);
-    } else {
-        constexpr int es = es_of<CT>();
-        char *const dst = static_cast<char *>(p.c) + ((batch * p.m + qr) * p.n + qc) * es;
-        store_quadrant<CT, 4>(wave_stage(ring, __builtin_amdgcn_readfirstlane(w)), dst, nullptr,
-                              (uint32_t)(p.n * es), clamp_extent(p.m - qr), clamp_extent(p.n - qc), acc, lane, val);
-    }
-    if (p.amax) block_amax_atomic(lmax, p.amax, red);
-}
-
-template <int F>
-static void launch_gemm_amax_fmt(const GemmAmaxParams &p, dim3 grid, hipStream_t s)
-{
-    if (p.c_dtype == DT_F32) hipLaunchKernelGGL((k_gemm_amax<F, DT_F32>), grid, dim3(kThreads), 0, s, p);
-    else if (p.c_dtype == DT_BF16) hipLaunchKernelGGL((k_gemm_amax<F, DT_BF16>), grid, dim3(kThreads), 0, s, p);
-    else if (p.c_dtype == DT_F16) hipLaunchKernelGGL((k_gemm_amax<F, DT_F16>), grid, dim3(kThreads), 0, s, p);
-    else if constexpr (F == FMT_E2M1) {
-        // FP8 and FP4 C: only with FP4 operands ("GEMM + Amax (SM100)", Dtypes)
-        if (p.c_dtype == DT_E4M3) hipLaunchKernelGGL((k_gemm_amax<F, DT_E4M3>), grid, dim3(kThreads), 0, s, p);
-        else if (p.c_dtype == DT_E5M2) hipLaunchKernelGGL((k_gemm_amax<F, DT_E5M2>), grid, dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((k_gemm_amax<F, DT_E2M1>), grid, dim3(kThreads), 0, s, p);
-    }
-}
-
-hipError_t launch_gemm_amax(const GemmAmaxArgs &a, hipStream_t s)
-{
-    hipError_t e = zero_floats(a.amax, 1, s);
-    if (e != hipSuccess) return e;
-    if (a.m == 0 || a.n == 0 || a.l == 0) return hipSuccess;
-    GemmAmaxParams p;
-    p.a = a.a; p.b = a.b; p.sfa = a.sfa; p.sfb = a.sfb; p.c = a.c; p.amax = a.amax;
-    p.m = a.m; p.n = a.n; p.k = a.k;
-    p.m_t = (a.m + 127) / 128; p.n_t = (a.n + 127) / 128; p.k_t = (a.k + 127) / 128;
-    p.row_bytes = row_bytes_of(a.fmt, a.k);
-    p.c_dtype = a.c_dtype;
-    dim3 grid((unsigned)(((a.n + kTileN - 1) / kTileN) * ((a.m + kTileM - 1) / kTileM) * a.l));
-    if (a.fmt == FMT_E4M3) launch_gemm_amax_fmt<FMT_E4M3>(p, grid, s);
-    else if (a.fmt == FMT_E5M2) launch_gemm_amax_fmt<FMT_E5M2>(p, grid, s);
-    else launch_gemm_amax_fmt<FMT_E2M1>(p, grid, s);
-    return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// Grouped GEMM over padded_offsets expert ranges
-// ---------------------------------------------------------------------------
 enum : int { EPI_BF16_BIAS = 0, EPI_SRELU = 1, EPI_SRELU_FP8 = 2, EPI_BF16 = 3, EPI_DSWIGLU_FP8 = 4,
              EPI_DSWIGLU = 5 };
 
@@ -677,7 +524,7 @@ __global__ void __launch_bounds__(256) k_grouped(GroupedParams p)
     }
 }
 
-static GroupedParams grouped_params(const GroupedArgs &a)
+inline GroupedParams grouped_params(const GroupedArgs &a)
 {
     GroupedParams p;
     p.a = a.a; p.b = a.b; p.sfa = a.sfa; p.sfb = a.sfb; p.offsets = a.offsets;
@@ -697,22 +544,6 @@ static GroupedParams grouped_params(const GroupedArgs &a)
     return p;
 }
 
-hipError_t launch_grouped_gemm(const GroupedArgs &a, hipStream_t s)
-{
-    if (a.m == 0 || a.n == 0) return hipSuccess;
-    GroupedParams p = grouped_params(a);
-    dim3 grid((unsigned)(((a.n + kTileN - 1) / kTileN) * (a.m / kTileM)));
-    const bool fast = p.c && p.c_dtype == DT_BF16 && p.d_dtype == DT_BF16;
-    if (p.bias) {
-        if (fast) hipLaunchKernelGGL((k_grouped<FMT_BF16, EPI_BF16_BIAS, false, DT_BF16>), grid, dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((k_grouped<FMT_BF16, EPI_BF16_BIAS, false>), grid, dim3(kThreads), 0, s, p);
-    } else {
-        if (fast) hipLaunchKernelGGL((k_grouped<FMT_BF16, EPI_BF16, false, DT_BF16>), grid, dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((k_grouped<FMT_BF16, EPI_BF16, false>), grid, dim3(kThreads), 0, s, p);
-    }
-    return hipGetLastError();
-}
-
 template <int F, int EPI, int OT = -1>
 static void launch_srelu_variant(const GroupedParams &p, dim3 grid, hipStream_t s)
 {
@@ -730,62 +561,7 @@ static void launch_srelu_variant(const GroupedParams &p, dim3 grid, hipStream_t 
     else hipLaunchKernelGGL((k_grouped<F, EPI, false, OT>), grid, dim3(kThreads), 0, s, p);
 }
 
-hipError_t launch_grouped_srelu(const GroupedArgs &a, hipStream_t s)
-{
-    hipError_t e = zero_floats(a.amax, a.num_experts, s);
-    if (e != hipSuccess) return e;
-    if (a.m == 0 || a.n == 0) return hipSuccess;
-    GroupedParams p = grouped_params(a);
-    dim3 grid((unsigned)(((a.n + kTileN - 1) / kTileN) * (a.m / kTileM)));
-    if (a.d_dtype == DT_E4M3) {
-        if (a.fmt == FMT_E4M3) launch_srelu_variant<FMT_E4M3, EPI_SRELU_FP8>(p, grid, s);
-        else if (a.fmt == FMT_E5M2) launch_srelu_variant<FMT_E5M2, EPI_SRELU_FP8>(p, grid, s);
-        else return hipErrorNotSupported;
-    } else if (a.d_dtype == DT_E5M2) {
-        if (a.fmt == FMT_E4M3) launch_srelu_variant<FMT_E4M3, EPI_SRELU_FP8, DT_E5M2>(p, grid, s);
-        else if (a.fmt == FMT_E5M2) launch_srelu_variant<FMT_E5M2, EPI_SRELU_FP8, DT_E5M2>(p, grid, s);
-        else return hipErrorNotSupported;
-    } else if (a.d_dtype == DT_E2M1) {
-        if (a.fmt == FMT_E4M3) launch_srelu_variant<FMT_E4M3, EPI_SRELU_FP8, DT_E2M1>(p, grid, s);
-        else if (a.fmt == FMT_E5M2) launch_srelu_variant<FMT_E5M2, EPI_SRELU_FP8, DT_E2M1>(p, grid, s);
-        else return hipErrorNotSupported;
-    } else if (a.fmt == FMT_E4M3) {
-        launch_srelu_variant<FMT_E4M3, EPI_SRELU>(p, grid, s);
-    } else if (a.fmt == FMT_E5M2) {
-        launch_srelu_variant<FMT_E5M2, EPI_SRELU>(p, grid, s);
-    } else {
-        launch_srelu_variant<FMT_E2M1, EPI_SRELU>(p, grid, s);
-    }
-    return hipGetLastError();
-}
-
-}  // namespace bsg
-
-namespace bsg {
-
-hipError_t launch_grouped_dswiglu(const GroupedArgs &a, hipStream_t s)
-{
-    if (a.fmt == FMT_E2M1) {
-        // FP4 inputs: per-expert amax (L, 2), zero-filled first (also for an empty problem)
-        hipError_t e = zero_floats(a.amax, 2 * a.num_experts, s);
-        if (e != hipSuccess) return e;
-    }
-    if (a.m == 0 || a.n == 0) return hipSuccess;
-    GroupedParams p = grouped_params(a);
-    dim3 grid((unsigned)(((a.n + kTileN - 1) / kTileN) * (a.m / kTileM)));
-    if (a.fmt == FMT_E2M1) {
-        if (a.d_dtype == DT_F32) hipLaunchKernelGGL((k_grouped<FMT_E2M1, EPI_DSWIGLU, false, DT_F32>), grid, dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((k_grouped<FMT_E2M1, EPI_DSWIGLU, false, DT_BF16>), grid, dim3(kThreads), 0, s, p);
-    } else if (a.fmt == FMT_E4M3) {
-        if (a.d_dtype == DT_E5M2) hipLaunchKernelGGL((k_grouped<FMT_E4M3, EPI_DSWIGLU_FP8, false, DT_E5M2>), grid, dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((k_grouped<FMT_E4M3, EPI_DSWIGLU_FP8, false>), grid, dim3(kThreads), 0, s, p);
-    } else if (a.fmt == FMT_E5M2) {
-        if (a.d_dtype == DT_E5M2) hipLaunchKernelGGL((k_grouped<FMT_E5M2, EPI_DSWIGLU_FP8, false, DT_E5M2>), grid, dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((k_grouped<FMT_E5M2, EPI_DSWIGLU_FP8, false>), grid, dim3(kThreads), 0, s, p);
-    } else {
-        return hipErrorNotSupported;
-    }
-    return hipGetLastError();
-}
+// MX-quantised D of grouped_gemm_srelu (kernels_srelu_mx.hip).
+void launch_grouped_srelu_mx(const GroupedParams &p, int fmt, int d_dtype, dim3 grid, hipStream_t s);
 
 }  // namespace bsg

@@ -13,6 +13,8 @@ struct GemmAmaxArgs {
     int64_t m, n, k, l;
     int fmt;       // bsg::Fmt: 0 = E4M3, 1 = E2M1, 4 = E5M2
     int c_dtype;   // bsg_dtype
+    int a_mn = 0;  // A stored m-major ([L][K][M]; FP8 only)
+    int b_mn = 0;  // B stored n-major ([L][K][N]; FP8 only)
 };
 
 struct GroupedArgs {

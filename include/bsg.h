@@ -26,7 +26,9 @@
  *    caller's responsibility and are not checked ("Grouped GEMM + dSwiGLU
  *    (SM100)", JAX execution: offsets are the caller's responsibility).
  *  - Operand layouts: A (M,K,L) and B (N,K,L) are k-major, i.e. memory
- *    order [L][rows][K]; C/D are n-major, memory order [L][M][N].  Packed
+ *    order [L][rows][K], and C/D are n-major, memory order [L][M][N],
+ *    except where an entry point takes a major argument (gemm_amax and the
+ *    B operand of grouped_gemm_dswiglu).  Packed
  *    FP4 (E2M1X2) stores two codes per byte, element 2j in the low nibble,
  *    so a row holds K/2 bytes ("GEMM + Amax (SM100)", Layouts and strides).
  *  - Scale factors: one E8M0 byte per 32 consecutive K elements of a row
@@ -80,28 +82,41 @@ typedef enum bsg_dtype {
  *     Amax     = max_{m,n,l} |C[m,n,l]|
  * with dequant(X)[r,k,l] = X[r,k,l] * 2^(SF byte - 127) per 32-wide K block.
  *
- *  a     (M,K,L) codes, k-major; E4M3 / E5M2: M*K*L bytes; E2M1X2: M*(K/2)*L bytes
- *  b     (N,K,L) codes, k-major, same dtype as a
- *  sfa   scale atoms over (M, K, L);  sfb: scale atoms over (N, K, L)
- *  c     (M,N,L) output, n-major, c_dtype in {F32, BF16, F16}; RNE cast
+ *  a     (M,K,L) codes; E4M3 / E5M2: M*K*L bytes; E2M1X2: M*(K/2)*L bytes.
+ *        a_major 'k': k-major, memory [L][M][K] (stride (K, 1, M*K));
+ *        a_major 'm': m-major, memory [L][K][M] (stride (1, M, M*K)),
+ *        E4M3 / E5M2 only, M % 16 == 0 and (K + 256) * M < 2^31
+ *  b     (N,K,L) codes, same dtype as a; b_major 'k': memory [L][N][K];
+ *        b_major 'n': n-major, memory [L][K][N], under the same rules
+ *        ("GEMM + Amax (SM100)", Input/Output tensors and Layouts and
+ *        strides: packed FP4 A/B must be k-major)
+ *  sfa   scale atoms over (M, K, L);  sfb: scale atoms over (N, K, L); the
+ *        same layout whatever the operand majors
+ *  c     (M,N,L) output; c_major 'n': n-major, memory [L][M][N]; c_major
+ *        'm': m-major, memory [L][N][M] (the page's c_major; packed FP4 C
+ *        must be n-major).  c_dtype in {F32, BF16, F16}; RNE cast
  *        of the fp32 accumulator.  With E2M1X2 A/B, c_dtype may also be
  *        E4M3 or E5M2 (the page's Dtypes allow FP8 C only with FP4 A/B): a
  *        plain RNE cast with no scale factor, saturated to +-448 / +-57344
- *        (never NaN or Inf); rows of N bytes, N % 16 == 0.  Also with
- *        E2M1X2 A/B: c_dtype E2M1X2, packed FP4 C of (M, N/2, L) bytes, two
- *        codes per byte with the even column in the low nibble, an RNE cast
- *        saturated to +-6; N % 32 == 0.  FP8 C with FP8 A/B returns
- *        UNSUPPORTED; FP4 C with FP8 A/B returns DTYPE.
+ *        (never NaN or Inf).  Also with E2M1X2 A/B: c_dtype E2M1X2,
+ *        packed FP4 C of (M, N/2, L) bytes, two codes per byte with the
+ *        even column in the low nibble, an RNE cast saturated to +-6;
+ *        N % 32 == 0.  FP8 C with FP8 A/B returns UNSUPPORTED; FP4 C with
+ *        FP8 A/B returns DTYPE.  A row of C (along its contiguous
+ *        dimension) must be a multiple of 16 bytes.
  *  amax  one float32 (nullable): max |C| of the fp32 accumulators (before
  *        the output cast); the library zero-fills it on `stream` first
  *  ab_dtype in {E4M3, E5M2, E2M1X2} (the page's float8_e4m3fn, float8_e5m2
- *  and float4_e2m1fn_x2 A/B); sf_vec_size must be 32.
+ *  and float4_e2m1fn_x2 A/B); sf_vec_size must be 32.  a_major, b_major
+ *  and c_major are the characters above; any other value, an MN-major
+ *  packed FP4 operand or an m-major packed FP4 C returns SHAPE.
  *  Sizes: M, N, L >= 0; K >= 0 with K % 32 == 0.  M or N need not be tile
  *  multiples.  Accumulation is fp32 (the pages' only accumulator dtype).
  */
 int gemm_amax(const void *a, const void *b, const uint8_t *sfa, const uint8_t *sfb,
               void *c, float *amax, int64_t m, int64_t n, int64_t k, int64_t l,
-              int ab_dtype, int c_dtype, int sf_vec_size, void *stream);
+              int ab_dtype, int c_dtype, int sf_vec_size, int a_major, int b_major,
+              int c_major, void *stream);
 
 /*
  * grouped_gemm -- "Grouped GEMM (SM100 BF16)", Operation.  For expert g
@@ -293,7 +308,8 @@ int gemm_proj_rope_mxfp8(const void *x, const void *w, const uint8_t *x_scale,
  * the launch call would return before enqueueing anything. */
 int bsg_validate_gemm_amax(const void *a, const void *b, const uint8_t *sfa,
                            const uint8_t *sfb, void *c, float *amax, int64_t m, int64_t n,
-                           int64_t k, int64_t l, int ab_dtype, int c_dtype, int sf_vec_size);
+                           int64_t k, int64_t l, int ab_dtype, int c_dtype, int sf_vec_size,
+                           int a_major, int b_major, int c_major);
 int bsg_validate_grouped_gemm(const void *a, const void *b, const int32_t *padded_offsets,
                               const float *alpha, const float *prob, const void *bias,
                               void *c, void *d, int64_t m, int64_t n, int64_t k,

@@ -58,6 +58,27 @@ def test_gemm_amax_validation():
     assert va(n=250) == ALIGN                            # fp32 C row of 1000 bytes
     assert va(m=-1) == SHAPE
     assert va(m=0, a=0, b=0, c=0) == OK                  # empty problem: only amax is written
+
+
+def test_gemm_amax_major_validation():
+    """"GEMM + Amax (SM100)": A m-major / B n-major strides, c_major, and
+    Layouts and strides (packed FP4 A/B k-major, packed FP4 C n-major)."""
+    assert va(a_major="m") == OK and va(b_major="n") == OK and va(c_major="m") == OK
+    assert va(a_major="m", b_major="n", c_major="m", ab_dtype="e5m2") == OK
+    assert va(a_major="n") == SHAPE and va(b_major="m") == SHAPE and va(c_major="k") == SHAPE
+    assert va(a_major="m", ab_dtype="e2m1") == SHAPE      # packed FP4 A must be k-major
+    assert va(b_major="n", ab_dtype="e2m1") == SHAPE
+    assert va(c_major="m", ab_dtype="e2m1") == OK         # FP4 A/B, fp32 C m-major
+    assert va(c_major="m", ab_dtype="e2m1", c_dtype="e2m1") == SHAPE   # packed FP4 C n-major only
+    assert va(c_major="m", ab_dtype="e2m1", c_dtype="e4m3") == OK
+    assert va(a_major="m", m=264) == ALIGN                # M rows of 264 bytes: not 16-byte multiples
+    assert va(b_major="n", n=264, c_dtype=bsg.BF16) == ALIGN
+    assert va(a_major="m", m=272, n=256) == OK
+    assert va(c_major="m", m=250) == ALIGN                # m-major fp32 C rows of 1000 bytes
+    assert va(c_major="m", n=250) == OK                   # N is then the outer dimension
+    assert va(a_major="m", m=1 << 16, k=1 << 15) == UNSUP  # (K + 256) * M past 32-bit offsets
+    with pytest.raises(ValueError):
+        va(a_major="mm")
     msg = bsg.lib().bsg_last_error().decode()
     assert isinstance(msg, str)
 
