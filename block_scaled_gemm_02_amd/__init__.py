@@ -49,8 +49,8 @@ def lib():
             "grouped_gemm": [p] * 8 + [i64] * 4 + [i32] * 3 + [p],
             "grouped_gemm_srelu": [p] * 14 + [i64] * 4 + [i32] * 4 + [f32, p],
             "gemm_proj_rope_mxfp8": [p] * 10 + [i64] * 5 + [i32, i32, p],
-            "grouped_gemm_dswiglu": [p] * 16 + [i64] * 4 + [i32] * 4 + [p],
-            "bsg_validate_grouped_gemm_dswiglu": [p] * 16 + [i64] * 4 + [i32] * 4,
+            "grouped_gemm_dswiglu": [p] * 16 + [i64] * 4 + [i32] * 5 + [p],
+            "bsg_validate_grouped_gemm_dswiglu": [p] * 16 + [i64] * 4 + [i32] * 5,
             "grouped_gemm_discrete": [p] * 8 + [i64] * 4 + [i32] * 3 + [p],
             "grouped_gemm_srelu_discrete": [p] * 14 + [i64] * 4 + [i32] * 4 + [f32, p],
             "bsg_validate_grouped_gemm_discrete": [p] * 8 + [i64] * 4 + [i32] * 3,
@@ -335,10 +335,12 @@ def grouped_gemm_srelu_discrete(a, b_ptrs, sfa, sfb_ptrs, padded_offsets, alpha,
 
 def grouped_gemm_dswiglu(a, b, sfa, sfb, c, padded_offsets, alpha, beta, prob, norm_const, d_row, d_col,
                          sfd_row, sfd_col, dprob, m, n, k, num_experts, ab_dtype="e4m3", c_dtype=None,
-                         d_dtype="e4m3", sf_vec_size=32, amax=None, stream=None, validate_only=False):
+                         d_dtype="e4m3", sf_vec_size=32, amax=None, b_major="k", stream=None,
+                         validate_only=False):
     """Grouped GEMM + dSwiGLU backward (see include/bsg.h): MXFP8 D for FP8
     inputs, bf16/fp32 D with amax (L, 2) for FP4 inputs.  dprob is accumulated:
-    zero-fill it first."""
+    zero-fill it first.  b_major "k" (B memory [L][N][K]) or "n" ([L][K][N],
+    FP8 only)."""
     cd = BF16 if c_dtype is None else (_TORCH_DT[c_dtype] if c_dtype in _TORCH_DT else c_dtype)
     dd = _d_code(d_dtype, d_row)
     ab = _ab_code(ab_dtype)
@@ -357,7 +359,7 @@ def grouped_gemm_dswiglu(a, b, sfa, sfb, c, padded_offsets, alpha, beta, prob, n
         _need(dprob, "dprob", 4 * m, torch.float32)
     args = [_ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), _ptr(c), _ptr(padded_offsets), _ptr(alpha), _ptr(beta),
             _ptr(prob), _ptr(norm_const), _ptr(d_row), _ptr(d_col), _ptr(sfd_row), _ptr(sfd_col), _ptr(dprob),
-            _ptr(amax), m, n, k, num_experts, ab, cd, dd, sf_vec_size]
+            _ptr(amax), m, n, k, num_experts, ab, cd, dd, sf_vec_size, _major(b_major, "kn", "b_major")]
     if validate_only:
         return lib().bsg_validate_grouped_gemm_dswiglu(*args)
     _check(lib().grouped_gemm_dswiglu(*args, _stream(stream)))

@@ -419,10 +419,14 @@ int bsg_validate_grouped_gemm_dswiglu(const void *a, const void *b, const uint8_
                                       void *d_row, void *d_col, uint8_t *sfd_row, uint8_t *sfd_col,
                                       float *dprob, float *amax, int64_t m, int64_t n, int64_t k,
                                       int64_t num_experts, int ab_dtype, int c_dtype, int d_dtype,
-                                      int sf_vec_size)
+                                      int sf_vec_size, int b_major)
 {
     int st = check_ab_sf(ab_dtype, sf_vec_size);
     if (st) return st;
+    // "Grouped GEMM + dSwiGLU (SM100)", Layouts and strides: B k-major or
+    // n-major, k-major for FP4 inputs
+    if (b_major != 'k' && b_major != 'n') return fail(BSG_ERR_SHAPE, "b_major must be 'k' or 'n'");
+    if (b_major == 'n' && ab_dtype == BSG_E2M1X2) return fail(BSG_ERR_SHAPE, "packed FP4 B must be k-major");
     if ((st = check_grouped_common(a, b, padded_offsets, alpha, prob, d_row, m, n, k, num_experts)))
         return st;
     if (k % 32) return fail(BSG_ERR_SHAPE, "K=%lld must be a multiple of sf_vec_size 32", (long long)k);
@@ -453,6 +457,8 @@ int bsg_validate_grouped_gemm_dswiglu(const void *a, const void *b, const uint8_
         return fail(BSG_ERR_ALIGN, "sfd_row, sfd_col, dprob and amax must be 4-byte aligned");
     if ((int64_t)row_bytes(ab_dtype, k) * 256 >= (1ll << 31) || m * 2 * n >= (1ll << 31))
         return fail(BSG_ERR_UNSUPPORTED, "K or M*2N too large");
+    if (b_major == 'n' && (k + 256) * n >= (1ll << 31))
+        return fail(BSG_ERR_UNSUPPORTED, "n-major B too large for 32-bit offsets");
     return BSG_OK;
 }
 
@@ -461,11 +467,11 @@ int grouped_gemm_dswiglu(const void *a, const void *b, const uint8_t *sfa, const
                          const float *prob, const float *norm_const, void *d_row, void *d_col,
                          uint8_t *sfd_row, uint8_t *sfd_col, float *dprob, float *amax, int64_t m, int64_t n,
                          int64_t k, int64_t num_experts, int ab_dtype, int c_dtype, int d_dtype,
-                         int sf_vec_size, void *stream)
+                         int sf_vec_size, int b_major, void *stream)
 {
     int st = bsg_validate_grouped_gemm_dswiglu(a, b, sfa, sfb, c, padded_offsets, alpha, beta, prob, norm_const,
                                                d_row, d_col, sfd_row, sfd_col, dprob, amax, m, n, k, num_experts,
-                                               ab_dtype, c_dtype, d_dtype, sf_vec_size);
+                                               ab_dtype, c_dtype, d_dtype, sf_vec_size, b_major);
     if (st) return st;
     if ((st = check_device())) return st;
     bsg::GroupedArgs args{};
@@ -477,6 +483,7 @@ int grouped_gemm_dswiglu(const void *a, const void *b, const uint8_t *sfa, const
     args.fmt = fmt_of(ab_dtype); args.c_dtype = c_dtype; args.d_dtype = d_dtype;
     args.beta = beta; args.cfwd = static_cast<const uint16_t *>(c); args.dprob = dprob;
     args.amax = ab_dtype == BSG_E2M1X2 ? amax : nullptr;
+    args.b_mn = b_major == 'n';
     return launch_status(bsg::launch_grouped_dswiglu(args, static_cast<hipStream_t>(stream)),
                          "grouped_gemm_dswiglu");
 }

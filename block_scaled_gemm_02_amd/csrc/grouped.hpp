@@ -495,6 +495,8 @@ __global__ void __launch_bounds__(256) k_grouped(GroupedParams p)
     const uint8_t *sfbg = p.sfb_ptrs ? reinterpret_cast<const uint8_t *>(p.sfb_ptrs[g]) : p.sfb;
     OperandDesc B{bg + n0 * p.row_bytes, (uint32_t)(rows_b * p.row_bytes), p.row_bytes, sfbg,
                   p.sfb_ptrs ? 0 : g, p.n_t, p.k_t, n0 / 128, p.n_t - 1};
+    // n-major B ([L][K][N], FP8 only): expert g's K rows of N codes
+    if constexpr (b_t(F)) mn_major_operand(B, p.b, g, p.n, n0, rows_b, p.k);
     const float alpha = p.alpha[g];
     // The tile's 256 prob values go straight to LDS ahead of the operand
     // loads (wave w: rows 64w..64w+63; M is a multiple of 256), so the K
@@ -560,6 +562,9 @@ static void launch_srelu_variant(const GroupedParams &p, dim3 grid, hipStream_t 
     if (p.tanh_s > 0.0f) hipLaunchKernelGGL((k_grouped<F, EPI, true, OT>), grid, dim3(kThreads), 0, s, p);
     else hipLaunchKernelGGL((k_grouped<F, EPI, false, OT>), grid, dim3(kThreads), 0, s, p);
 }
+
+// grouped_gemm_dswiglu with FP8 operands and n-major B (kernels_dswiglu_mn.hip).
+void launch_dswiglu_bn(const GroupedParams &p, int fmt, int d_dtype, dim3 grid, hipStream_t s);
 
 // MX-quantised D of grouped_gemm_srelu (kernels_srelu_mx.hip).
 void launch_grouped_srelu_mx(const GroupedParams &p, int fmt, int d_dtype, dim3 grid, hipStream_t s);

@@ -55,4 +55,17 @@ __device__ __forceinline__ void wait_loads() { s_wait_vm<0>(); }
 
 __device__ __forceinline__ int clamp_extent(int64_t extent) { return extent < 0 ? 0 : (extent > 128 ? 128 : (int)extent); }
 
+// Operand X stored MN-major (FP8, memory [L][K][MN]): the tile's columns
+// [mn0, mn0 + cols) of every K row.  The readable range ends at the last K
+// row's last column, so K rows past K read zeros; columns past MN in the
+// other K rows are masked per lane (OperandDesc::mn_valid).
+__device__ __forceinline__ void mn_major_operand(OperandDesc &X, const uint8_t *x, int64_t batch, int64_t mn,
+                                                 int64_t mn0, int64_t cols, int64_t k)
+{
+    X.base = x + batch * mn * k + mn0;
+    X.bytes = k > 0 ? (uint32_t)((k - 1) * mn + (mn - mn0)) : 0u;
+    X.row_bytes = (uint32_t)mn;
+    X.mn_valid = (uint32_t)cols;
+}
+
 }  // namespace bsg

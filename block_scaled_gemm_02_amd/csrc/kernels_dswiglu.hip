@@ -16,6 +16,9 @@ hipError_t launch_grouped_dswiglu(const GroupedArgs &a, hipStream_t s)
     if (a.fmt == FMT_E2M1) {
         if (a.d_dtype == DT_F32) hipLaunchKernelGGL((k_grouped<FMT_E2M1, EPI_DSWIGLU, false, DT_F32>), grid, dim3(kThreads), 0, s, p);
         else hipLaunchKernelGGL((k_grouped<FMT_E2M1, EPI_DSWIGLU, false, DT_BF16>), grid, dim3(kThreads), 0, s, p);
+    } else if (a.b_mn) {
+        if (a.fmt != FMT_E4M3 && a.fmt != FMT_E5M2) return hipErrorNotSupported;
+        launch_dswiglu_bn(p, a.fmt, a.d_dtype, grid, s);
     } else if (a.fmt == FMT_E4M3) {
         if (a.d_dtype == DT_E5M2) hipLaunchKernelGGL((k_grouped<FMT_E4M3, EPI_DSWIGLU_FP8, false, DT_E5M2>), grid, dim3(kThreads), 0, s, p);
         else hipLaunchKernelGGL((k_grouped<FMT_E4M3, EPI_DSWIGLU_FP8, false>), grid, dim3(kThreads), 0, s, p);

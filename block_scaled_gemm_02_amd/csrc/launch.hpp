@@ -34,6 +34,7 @@ struct GroupedArgs {
     const float *beta = nullptr;
     const uint16_t *cfwd = nullptr;
     float *dprob = nullptr;
+    int b_mn = 0;   // B stored n-major ([L][K][N]; FP8 grouped_gemm_dswiglu only)
 };
 
 struct ProjRopeArgs {

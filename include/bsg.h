@@ -249,6 +249,11 @@ int grouped_gemm_srelu_discrete(const void *a, const uint64_t *b_ptrs, const uin
  *           max |dswiglu| over expert g's rows (fp32 values before the
  *           cast); zero-filled by the library; norm_const and sfd_* unused
  *  c_dtype BF16; other C dtypes return UNSUPPORTED.
+ *  b_major  'k': B k-major, memory [L][N][K]; 'n': B n-major, memory
+ *           [L][K][N] (stride (1, N, N*K)), FP8 A/B only and
+ *           (K + 256) * N < 2^31 ("Grouped GEMM + dSwiGLU (SM100)", Layouts
+ *           and strides: FP4 B must be k-major; other values return SHAPE).
+ *           Both give identical results.
  *  Sizes: M % 256 == 0, 1 <= L <= 1024, K % 32 == 0, N % 32 == 0.  Rows at
  *  or past padded_offsets[L-1] are not written.
  */
@@ -258,7 +263,7 @@ int grouped_gemm_dswiglu(const void *a, const void *b, const uint8_t *sfa, const
                          void *d_row, void *d_col, uint8_t *sfd_row, uint8_t *sfd_col,
                          float *dprob, float *amax, int64_t m, int64_t n, int64_t k,
                          int64_t num_experts, int ab_dtype, int c_dtype, int d_dtype,
-                         int sf_vec_size, void *stream);
+                         int sf_vec_size, int b_major, void *stream);
 
 /*
  * gemm_proj_rope_mxfp8 -- "GEMM + RoPE + MXFP8 Projection (SM100)",
@@ -344,7 +349,7 @@ int bsg_validate_grouped_gemm_dswiglu(const void *a, const void *b, const uint8_
                                       uint8_t *sfd_row, uint8_t *sfd_col, float *dprob,
                                       float *amax, int64_t m, int64_t n, int64_t k,
                                       int64_t num_experts, int ab_dtype, int c_dtype,
-                                      int d_dtype, int sf_vec_size);
+                                      int d_dtype, int sf_vec_size, int b_major);
 int bsg_validate_gemm_proj_rope_mxfp8(const void *x, const void *w, const uint8_t *x_scale,
                                       const uint8_t *w_scale, const void *cos, const void *sin,
                                       uint8_t *out_fp8_row, uint8_t *out_scales_row,

@@ -213,6 +213,11 @@ def test_dswiglu_validation():
     assert vdsw(dprob=None) == NULLPTR
     assert vdsw(c=None) == NULLPTR
     assert vdsw(c_dtype=torch.float32) == UNSUP
+    # "Grouped GEMM + dSwiGLU (SM100)", Layouts and strides: B k- or n-major, FP4 k-major
+    assert vdsw(b_major="n") == OK and vdsw(b_major="n", ab_dtype="e5m2") == OK
+    assert vdsw(b_major="m") == SHAPE
+    assert vdsw(b_major="n", ab_dtype="e2m1", d_dtype=torch.bfloat16) == SHAPE
+    assert vdsw(b_major="n", n=1 << 16, k=1 << 15) == UNSUP
     assert vdsw(d_dtype=bsg.E5M2) == OK                   # E5M2 D codes
     assert vdsw(d_dtype="e5m2", sfd_col=None) == NULLPTR
     assert vdsw(ab_dtype="e2m1", d_dtype="e5m2") == DTYPE  # FP4 inputs take bf16 / fp32 D

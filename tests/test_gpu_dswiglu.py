@@ -17,10 +17,13 @@ def say(msg):
     print(msg, flush=True)
 
 
-def run_dswiglu(p, d_fmt="e4m3"):
+def run_dswiglu(p, d_fmt="e4m3", b_major="k"):
     s = p.sizes
     t = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in p.t.items()}
     m, n, k, L = s["m"], s["n"], s["k"], s["l"]
+    if b_major == "n":
+        # the same codes stored [L][K][N] (stride (1, N, N*K))
+        t["b"] = t["b"].reshape(L, n, k).transpose(1, 2).contiguous()
     d = torch.full((m, 2 * n), 0xEE, dtype=torch.uint8, device="cuda")
     d_col = torch.full((m, 2 * n), 0xEE, dtype=torch.uint8, device="cuda")
     sfd_row = torch.full((W.sf_atom_bytes(m, 2 * n, 1),), 0xEE, dtype=torch.uint8, device="cuda")
@@ -28,7 +31,7 @@ def run_dswiglu(p, d_fmt="e4m3"):
     dprob = torch.zeros(m, device="cuda")
     bsg.grouped_gemm_dswiglu(t["a"], t["b"], t["sfa"], t["sfb"], t["c"], t["offsets"], t["alpha"], t["beta"],
                              t["prob"], t["norm_const"], d, d_col, sfd_row, sfd_col, dprob, m, n, k, L,
-                             s["fmt"], d_dtype=d_fmt)
+                             s["fmt"], d_dtype=d_fmt, b_major=b_major)
     torch.cuda.synchronize()
     return d, d_col, sfd_row, sfd_col, dprob
 
@@ -102,6 +105,32 @@ def test_grouped_dswiglu_matches_oracle(case):
     # rows at or past valid_m are not written; dprob there stays as the caller left it
     assert torch.all(d[valid:] == 0xEE) and torch.all(d_col[valid:] == 0xEE)
     assert torch.all(dprob[valid:] == 0)
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[2], CASES[4]])
+def test_grouped_dswiglu_n_major_b(case):
+    """B stored n-major ("Grouped GEMM + dSwiGLU (SM100)", Input/Output
+    tensors: B stride (1, N, N*K) for FP8 inputs): D codes and both scale
+    arrays equal the k-major call's bit for bit; dprob (atomic adds, whose
+    order varies) is checked against the oracle."""
+    say(f"grouped_dswiglu n-major B {case}")
+    off = np.cumsum(case["sizes"]).astype(np.int32)
+    L = len(case["sizes"])
+    p = W.grouped_dswiglu_problem(0, L, case["n"], case["k"], case["fmt"], seed=7, offsets=off, extra_rows=256)
+    s = p.sizes
+    m, n, k = s["m"], s["n"], s["k"]
+    d_fmt = case.get("d", "e4m3")
+    ref = run_dswiglu(p, d_fmt)
+    got = run_dswiglu(p, d_fmt, b_major="n")
+    for name, x, y in zip(("d", "d_col", "sfd_row", "sfd_col"), got[:4], ref[:4]):
+        assert torch.equal(x, y), name
+    valid = s["valid_m"]
+    r = O.grouped_dswiglu(p.t["a"], p.t["b"], p.t["sfa"], p.t["sfb"], off, p.t["alpha"], p.t["beta"],
+                          p.t["prob"], O.bits16(p.t["c"]), m, n, k, L, case["fmt"], 0, valid)
+    _, b_dp = bounds(p, r, 0, valid)
+    err = np.abs(got[4][:valid].cpu().double().numpy() - r["dprob"])
+    assert np.all(err <= b_dp), f"dprob: worst {float((err / np.maximum(b_dp, 1e-300)).max())} of its bound"
+    assert torch.all(got[4][valid:] == 0)
 
 
 FP4_CASES = [
@@ -186,3 +215,16 @@ def test_grouped_dswiglu_full_size_sampled(d_fmt):
         say(f"  {res}")
         gdp = dprob[r0:r0 + 256].cpu().double().numpy()
         assert np.all(np.abs(gdp - r["dprob"]) <= b_dp)
+
+
+def test_grouped_dswiglu_n_major_b_full_size():
+    """The bench configuration with B stored n-major: D codes and both scale
+    arrays equal the k-major call's bit for bit over the whole output."""
+    say("grouped_dswiglu full size, n-major B")
+    p = W.grouped_dswiglu_problem(28672, 32, 2048, 7168, "e4m3", seed=1, device="cuda")
+    ref = run_dswiglu(p)
+    got = run_dswiglu(p, b_major="n")
+    for name, x, y in zip(("d", "d_col", "sfd_row", "sfd_col"), got[:4], ref[:4]):
+        assert torch.equal(x, y), name
+    # dprob: the same per-row terms, added in a varying order
+    assert torch.allclose(got[4], ref[4], rtol=1e-5, atol=1e-6 * float(ref[4].abs().max()))
