@@ -149,6 +149,45 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float x0, float x1, float x2, flo
     return pack4_fp8<false>(x0, x1, x2, x3);
 }
 
+// Four MX-scaled values -> four E4M3 (E5 = false) or E5M2 codes, round to
+// nearest even, without the clamp of pack4_fp8.  A value x * (norm_const /
+// SF) with SF from mx_scale_byte exceeds the format's largest finite value
+// by at most a few ulp (the E8M0 decision is taken in fp32), and the hardware
+// conversion rounds everything below the midpoint past it (464 for E4M3,
+// 61440 for E5M2) to the largest finite code, as the plain clamp would.
+template <bool E5 = false>
+__device__ __forceinline__ uint32_t pack4_fp8_mx(float x0, float x1, float x2, float x3)
+{
+    uint32_t lo, hi;
+    if constexpr (E5) {
+        lo = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(x0, x1, 0, false) & 0xFFFFu;
+        hi = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(x2, x3, 0, false) & 0xFFFFu;
+    } else {
+        lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false) & 0xFFFFu;
+        hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, 0, false) & 0xFFFFu;
+    }
+    return lo | (hi << 16);
+}
+
+// Four values sharing one E8M0 scale -> four E4M3 codes of x / sf, with the
+// scaled conversion (v_cvt_scalef32_pk_fp8_f32 divides by its scale operand
+// exactly, a power of two here, and rounds to nearest even); sf is the
+// scale as a float, 2^(byte - 127) (subnormal for byte 0, which the
+// instruction also takes exactly).  Equal to pack4_fp8_mx(x * inv, ...) for
+// inv = 1 / sf, in one instruction per two values.
+typedef short s16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack4_e4m3_sf(float x0, float x1, float x2, float x3, float sf)
+{
+    const s16x2_t z = {0, 0};
+    const s16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, x0, x1, sf, false);
+    const s16x2_t w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, x2, x3, sf, true);
+    return __builtin_bit_cast(uint32_t, w);
+}
+__device__ __forceinline__ float sf_of_byte(uint32_t byte)
+{
+    return __uint_as_float(byte ? byte << 23 : 0x00400000u);
+}
+
 // E8M0 byte of the smallest power of two >= sigma (sigma >= 0), clamped to
 // [0, 254]; sigma == 0 (or NaN) gives 0.  Branch-free: it runs once per
 // quantisation block inside unrolled epilogues.
@@ -358,6 +397,7 @@ struct PipeDesc {
     uint32_t lc16;            // 16 * logical chunk of this lane's loads
     uint32_t vs;              // per-lane voffset of this wave's scale atom (kt = 0)
     uint32_t pa;              // per-lane voffset of the A line this lane prefetches (pair 0)
+    uint32_t pb;              // same for B (BSG_PF_B)
     uint32_t vsr[2];          // row-major scales: per-lane voffsets of this wave's two scale loads (pair 0)
     int kblocks;              // valid 32-wide K blocks
     int sf_kt;                // K atoms per row group (ceil(K/128))
@@ -496,7 +536,22 @@ __device__ __forceinline__ void prefetch_a(const PipeDesc<NB> &d, const RingSlot
         const uint32_t kb = (uint32_t)pair * kPK;
         lds_load4(d.ra, ring.sink + 256 * w, kb < d.row_bytes ? d.pa + kb : kOOB);
     }
+#if BSG_PF_B
+    if constexpr (!b_t(F) && F != FMT_BF16_BT) {
+        const uint32_t kb = (uint32_t)pair * kPK;
+        lds_load4(d.rb, ring.sink + 256 * w, kb < d.row_bytes ? d.pb + kb : kOOB);
+    }
+#endif
 }
+#ifndef BSG_PF_DIST
+#define BSG_PF_DIST 2
+#endif
+#ifndef BSG_PF_B
+#define BSG_PF_B 0
+#endif
+// Outstanding prefetch loads an odd step's wait leaves in flight.
+template <int F>
+constexpr int pf_loads() { return 1 + ((BSG_PF_B && !b_t(F) && F != FMT_BF16_BT) ? 1 : 0); }
 
 // LDS read number R of a step's fragments: A chunks (R < 8), B chunks, then
 // the two scale words.  In half H of a pair slot the lane reads logical
@@ -670,7 +725,7 @@ __device__ __forceinline__ void pipe_step(f32x16 (&acc)[4][NB], Frags<NB> &cur, 
     if constexpr (ODD) {
         // this wave's part of the pair holding stage ks+1 has landed (the
         // prefetch issued after it may still be in flight)
-        s_wait_vm<1>();
+        s_wait_vm<pf_loads<F>()>();
         s_wait_lgkm0();             // our reads of stage ks are complete
         __builtin_amdgcn_s_barrier();
     } else {
@@ -711,7 +766,7 @@ __device__ __forceinline__ void pipe_step(f32x16 (&acc)[4][NB], Frags<NB> &cur, 
         }
         // even step: prefetch the A lines of the pair after the one the next
         // (odd) step loads
-        if constexpr (!ODD && m == 0) prefetch_a<F, NB>(d, ring, (ks + 4) >> 1, w);
+        if constexpr (!ODD && m == 0) prefetch_a<F, NB>(d, ring, (ks + 2 * BSG_PF_DIST) >> 1, w);
         __builtin_amdgcn_sched_barrier(0);
     });
 }
@@ -785,6 +840,7 @@ __device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[4][NB], const RingSl
     } else {
         d.pa = (64u * w + (uint32_t)lane) * A.row_bytes;
     }
+    d.pb = (64u * w + (uint32_t)lane) * B.row_bytes;
     d.kblocks = (int)(k / 32);
     d.sf_kt = 0;
     d.rs = d.ra;
@@ -853,36 +909,6 @@ __device__ __forceinline__ int acc_col(int wn, int j, int q, int lane)
 }
 
 enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_E4M3 = 3, DT_E5M2 = 4, DT_E2M1 = 5 };
-
-// Max over the 32 lanes of each half-wave (lanes 0-31 and 32-63 separately)
-// of each of N non-negative values: quad and row DPP steps reduce 16 lanes, a
-// swizzle folds the two rows.  The values are compared as unsigned bit
-// patterns, which orders non-negative floats correctly and lets each DPP move
-// fold into its max (no canonicalising moves).
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_umax(uint32_t x)
-{
-    return max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false));
-}
-template <int N>
-__device__ __forceinline__ void half_wave_max(float (&x)[N])
-{
-    uint32_t u[N];
-#pragma unroll
-    for (int v = 0; v < N; ++v) u[v] = __float_as_uint(x[v]);
-#pragma unroll
-    for (int v = 0; v < N; ++v) u[v] = dpp_umax<0xB1>(u[v]);     // quad_perm [1,0,3,2]
-#pragma unroll
-    for (int v = 0; v < N; ++v) u[v] = dpp_umax<0x4E>(u[v]);     // quad_perm [2,3,0,1]
-#pragma unroll
-    for (int v = 0; v < N; ++v) u[v] = dpp_umax<0x141>(u[v]);    // row_half_mirror
-#pragma unroll
-    for (int v = 0; v < N; ++v) u[v] = dpp_umax<0x140>(u[v]);    // row_mirror
-#pragma unroll
-    for (int v = 0; v < N; ++v) u[v] = max(u[v], (uint32_t)__builtin_amdgcn_ds_swizzle((int)u[v], 0x401F));  // lane ^ 16
-#pragma unroll
-    for (int v = 0; v < N; ++v) x[v] = __uint_as_float(u[v]);
-}
 
 // ---------------------------------------------------------------------------
 // Output staging through LDS
@@ -1102,31 +1128,68 @@ __device__ __forceinline__ float lane_select(uint64_t mask, float x0, float x1)
     return r;
 }
 
-// Column scales of one 32x32 block in the accumulator layout.  cm[v] is the
-// column maximum of register v (the same in all 32 lanes of a half-wave
-// after half_wave_max).  Lane c of each half-wave computes the E8M0 scale of
-// register c % 16 only, and every lane then gathers the 16 factors it needs
-// from lanes 32g + v.  Returns this lane's byte: the scale of register c % 16.
-template <int DF = DT_E4M3>
-__device__ __forceinline__ uint32_t col_scales(const float (&cm)[16], float nc, float (&cinv)[16], int lane)
+// Column scales of one 32x32 block in the accumulator layout, by a
+// transposing butterfly.  d[v] is register v of this lane; a column's 32
+// values sit in one register over the 32 lanes of a half-wave.
+// Each step pairs registers (2m, 2m+1); a lane keeps the one chosen by the
+// lane bit in which it differs from its partner lane and takes the max with
+// the partner's copy of it, so the register count halves per step.  The
+// partners are l ^ 16 (v_permlane16_swap, which exchanges the pair between
+// the two rows of a half-wave in one instruction: no selects), l ^ 15
+// (row_mirror), l ^ 7 (row_half_mirror) and l ^ 2 (quad_perm), deciding on
+// lane bits 4, 3, 2 and 1; a last max with l ^ 1 covers all 32 lanes.  Lane
+// l then holds the column max of register col_reg_of_lane(l) = 8 b1 + 4 b2 +
+// 2 b3 + b4 (so do l and l ^ 1), computes its E8M0 byte, and the 16 factors
+// of each half-wave are broadcast back through xch (32 floats of LDS per
+// wave, 16-byte aligned).  Returns this lane's byte.
+__device__ __forceinline__ int col_reg_of_lane(int lane)
 {
-    // m = cm[lane % 16]: a tree of selects on the bits of the lane index,
-    // whose lane masks are constants.  Written as v_cndmask with an explicit
-    // mask: the compiler otherwise turns selects among the 16 values back
-    // into an indexed load, which moves them through scratch memory.
-    float t8[8], t4[4], t2[2];
+    return 8 * ((lane >> 1) & 1) + 4 * ((lane >> 2) & 1) + 2 * ((lane >> 3) & 1) + ((lane >> 4) & 1);
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+// One butterfly step: lanes whose mask bit is set keep x1 and send x0 to
+// their partner (DPP control CTRL), the others keep x0 and send x1.
+template <int CTRL>
+__device__ __forceinline__ uint32_t bfly_step(uint64_t mask, uint32_t x0, uint32_t x1)
+{
+    const uint32_t keep = __float_as_uint(lane_select(mask, __uint_as_float(x0), __uint_as_float(x1)));
+    const uint32_t send = __float_as_uint(lane_select(mask, __uint_as_float(x1), __uint_as_float(x0)));
+    return max(keep, dpp_mov<CTRL>(send));
+}
+template <int DF = DT_E4M3>
+__device__ __forceinline__ uint32_t col_scales_xch(const float (&d)[16], float nc, float (&cinv)[16], int lane,
+                                                   float *xch)
+{
+    uint32_t u[8], y[4], z[2];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) t8[k] = lane_select(0xAAAAAAAAAAAAAAAAull, cm[2 * k], cm[2 * k + 1]);
+    for (int m = 0; m < 8; ++m) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(d[2 * m]) & 0x7FFFFFFFu,
+                                                         __float_as_uint(d[2 * m + 1]) & 0x7FFFFFFFu, false, false);
+        u[m] = max((uint32_t)sw[0], (uint32_t)sw[1]);
+    }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) t4[k] = lane_select(0xCCCCCCCCCCCCCCCCull, t8[2 * k], t8[2 * k + 1]);
+    for (int m = 0; m < 4; ++m) y[m] = bfly_step<0x140>(0xFF00FF00FF00FF00ull, u[2 * m], u[2 * m + 1]);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) t2[k] = lane_select(0xF0F0F0F0F0F0F0F0ull, t4[2 * k], t4[2 * k + 1]);
-    const float m = lane_select(0xFF00FF00FF00FF00ull, t2[0], t2[1]);
+    for (int m = 0; m < 2; ++m) z[m] = bfly_step<0x141>(0xF0F0F0F0F0F0F0F0ull, y[2 * m], y[2 * m + 1]);
+    uint32_t t = bfly_step<0x4E>(0xCCCCCCCCCCCCCCCCull, z[0], z[1]);
+    t = max(t, dpp_mov<0xB1>(t));
     float inv;
-    const uint32_t byte = mx_scale_byte<DF>(m, nc, inv);
-    const int base = lane & 32;
+    const uint32_t byte = mx_scale_byte<DF>(__uint_as_float(t), nc, inv);
+    const int half = lane >> 5;
+    xch[16 * half + col_reg_of_lane(lane)] = inv;      // lanes l and l ^ 1 write the same value
+    const float4 *src = reinterpret_cast<const float4 *>(xch + 16 * half);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) cinv[v] = __shfl(inv, base + v);
+    for (int q = 0; q < 4; ++q) {
+        const float4 f = src[q];
+        cinv[4 * q] = f.x;
+        cinv[4 * q + 1] = f.y;
+        cinv[4 * q + 2] = f.z;
+        cinv[4 * q + 3] = f.w;
+    }
     return byte;
 }
 

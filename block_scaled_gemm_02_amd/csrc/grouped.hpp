@@ -204,6 +204,7 @@ __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x1
 
     uint8_t *sd = stage, *sdc = stage + 32 * G::RBP;
     uint8_t *wd = sd + c32 * G::RBP + (4 / PB) * gh, *wdc = sdc + c32 * G::RBP + (4 / PB) * gh;
+    float *const xch = reinterpret_cast<float *>(stage + 2 * 32 * G::RBP);   // column-scale exchange
     const int64_t mt = qr / 128;
     static_for<4>([&](auto ii) {
         constexpr int i = decltype(ii)::value;
@@ -223,11 +224,8 @@ __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x1
             float rinv;
             rword |= mx_scale_byte<DF>(rm, nc, rinv) << (8 * j);
             // column blocks: 32 rows of each column over the half-wave
-            float cinv[16], cm[16];
-#pragma unroll
-            for (int v = 0; v < 16; ++v) cm[v] = fabsf(d[v]);
-            half_wave_max(cm);
-            const uint32_t byte = col_scales<DF>(cm, nc, cinv, lane);
+            float cinv[16];
+            const uint32_t byte = col_scales_xch<DF>(d, nc, cinv, lane, xch);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 if constexpr (FP4) {
@@ -237,16 +235,18 @@ __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x1
                         d[4 * q] * cinv[4 * q], d[4 * q + 1] * cinv[4 * q + 1], d[4 * q + 2] * cinv[4 * q + 2],
                         d[4 * q + 3] * cinv[4 * q + 3]);
                 } else {
-                    *reinterpret_cast<uint32_t *>(wd + 32 * j + 8 * q) = pack4_fp8<DF == DT_E5M2>(
+                    *reinterpret_cast<uint32_t *>(wd + 32 * j + 8 * q) = pack4_fp8_mx<DF == DT_E5M2>(
                         d[4 * q] * rinv, d[4 * q + 1] * rinv, d[4 * q + 2] * rinv, d[4 * q + 3] * rinv);
-                    *reinterpret_cast<uint32_t *>(wdc + 32 * j + 8 * q) = pack4_fp8<DF == DT_E5M2>(
+                    *reinterpret_cast<uint32_t *>(wdc + 32 * j + 8 * q) = pack4_fp8_mx<DF == DT_E5M2>(
                         d[4 * q] * cinv[4 * q], d[4 * q + 1] * cinv[4 * q + 1], d[4 * q + 2] * cinv[4 * q + 2],
                         d[4 * q + 3] * cinv[4 * q + 3]);
                 }
             }
-            // SFD_col byte i of column 32j + 8(c/4) + 4g + c%4 (lane c < 16: register c)
-            const int64_t col = qc + 32 * j + 8 * (c32 >> 2) + 4 * gh + (c32 & 3);
-            if (c32 < 16 && col < n) {
+            // SFD_col byte i of the column of register r = col_reg_of_lane(lane):
+            // 32j + 8(r/4) + 4g + r%4 (even lanes; lane ^ 1 holds the same byte)
+            const int r = col_reg_of_lane(lane);
+            const int64_t col = qc + 32 * j + 8 * (r >> 2) + 4 * gh + (r & 3);
+            if ((lane & 1) == 0 && col < n) {
                 const int64_t off = (((col / 128) * col_kt + mt) * 32 + (col % 32)) * 16 + ((col % 128) / 32) * 4;
                 p.sfd_col[off + i] = (uint8_t)byte;
             }
@@ -300,6 +300,7 @@ __device__ __forceinline__ void epilogue_dswiglu_fp8(const GroupedParams &p, f32
     for (int i = 0; i < 4; ++i) pr[i] = prob_lds[acc_row(wm, i, lane)];
     uint8_t *sd = stage, *sdc = stage + 32 * G::RBP;
     uint8_t *wd = sd + c32 * G::RBP + 4 * gh, *wdc = sdc + c32 * G::RBP + 4 * gh;
+    float *const xch = reinterpret_cast<float *>(stage + 2 * 32 * G::RBP);   // column-scale exchange
     const int64_t mt = qr / 128;
     static_for<4>([&](auto ii) {
         constexpr int i = decltype(ii)::value;
@@ -327,22 +328,21 @@ __device__ __forceinline__ void epilogue_dswiglu_fp8(const GroupedParams &p, f32
             float rinv;
             rword[blk >> 2] |= mx_scale_byte<E5 ? DT_E5M2 : DT_E4M3>(rm, nc, rinv) << (8 * (blk & 3));
             // column direction: 32 rows of one D column over the half-wave
-            float cinv[16], cm[16];
-#pragma unroll
-            for (int v = 0; v < 16; ++v) cm[v] = fabsf(dv[v]);
-            half_wave_max(cm);
-            const uint32_t byte = col_scales<E5 ? DT_E5M2 : DT_E4M3>(cm, nc, cinv, lane);
+            float cinv[16];
+            const uint32_t byte = col_scales_xch<E5 ? DT_E5M2 : DT_E4M3>(dv, nc, cinv, lane, xch);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 *reinterpret_cast<uint32_t *>(wd + 32 * blk + 8 * q) =
-                    pack4_fp8<E5>(dv[4 * q] * rinv, dv[4 * q + 1] * rinv, dv[4 * q + 2] * rinv, dv[4 * q + 3] * rinv);
+                    pack4_fp8_mx<E5>(dv[4 * q] * rinv, dv[4 * q + 1] * rinv, dv[4 * q + 2] * rinv, dv[4 * q + 3] * rinv);
                 *reinterpret_cast<uint32_t *>(wdc + 32 * blk + 8 * q) =
-                    pack4_fp8<E5>(dv[4 * q] * cinv[4 * q], dv[4 * q + 1] * cinv[4 * q + 1],
+                    pack4_fp8_mx<E5>(dv[4 * q] * cinv[4 * q], dv[4 * q + 1] * cinv[4 * q + 1],
                                dv[4 * q + 2] * cinv[4 * q + 2], dv[4 * q + 3] * cinv[4 * q + 3]);
             }
-            // SFD_col byte i of D column dq + 32 blk + 8(c/4) + 4g + c%4 (lane c < 16: register c)
-            const int64_t col = dq + 32 * blk + 8 * (c32 >> 2) + 4 * gh + (c32 & 3);
-            if (c32 < 16 && 32 * blk < dcols) {
+            // SFD_col byte i of the D column of register r = col_reg_of_lane(lane):
+            // dq + 32 blk + 8(r/4) + 4g + r%4 (even lanes)
+            const int r = col_reg_of_lane(lane);
+            const int64_t col = dq + 32 * blk + 8 * (r >> 2) + 4 * gh + (r & 3);
+            if ((lane & 1) == 0 && 32 * blk < dcols) {
                 const int64_t off = (((col / 128) * col_kt + mt) * 32 + (col % 32)) * 16 + ((col % 128) / 32) * 4;
                 p.sfd_col[off + i] = (uint8_t)byte;
             }

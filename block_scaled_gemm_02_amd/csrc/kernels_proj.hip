@@ -143,6 +143,7 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
     typedef StageGeom<1, 3> G;
     uint8_t *stage = wave_stage(ring, __builtin_amdgcn_readfirstlane(w));
     uint8_t *sr = stage, *sc = stage + 32 * G::RBP;
+    float *const xch = reinterpret_cast<float *>(stage + 2 * 32 * G::RBP);   // column-scale exchange
     uint8_t *wr = sr + c32 * G::RBP + 4 * gh, *wc = sc + c32 * G::RBP + 4 * gh;
     const int64_t col0 = h * HD + 96 * wn;              // the wave's first feature column
     static_for<4>([&](auto ii) {
@@ -162,25 +163,26 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
             rm = fmaxf(rm, xor32(rm));
             float rinv;
             const uint32_t rb = mx_scale_byte(rm, 1.0f, rinv);
+            const float rsf = sf_of_byte(rb);              // norm_const 1: codes are a / SF
             // column direction: 32 tokens of one feature (a register over the half-wave)
-            float cinv[16], cm[16];
+            float cinv[16], av[16];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) cm[v] = fabsf(a[v]);
-            half_wave_max(cm);
-            const uint32_t byte = col_scales(cm, 1.0f, cinv, lane);
+            for (int v = 0; v < 16; ++v) av[v] = a[v];
+            const uint32_t byte = col_scales_xch(av, 1.0f, cinv, lane, xch);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 *reinterpret_cast<uint32_t *>(wr + 32 * j + 8 * q) =
-                    pack4_e4m3(a[4 * q] * rinv, a[4 * q + 1] * rinv, a[4 * q + 2] * rinv, a[4 * q + 3] * rinv);
+                    pack4_e4m3_sf(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3], rsf);
                 *reinterpret_cast<uint32_t *>(wc + 32 * j + 8 * q) =
-                    pack4_e4m3(a[4 * q] * cinv[4 * q], a[4 * q + 1] * cinv[4 * q + 1],
-                               a[4 * q + 2] * cinv[4 * q + 2], a[4 * q + 3] * cinv[4 * q + 3]);
+                    pack4_fp8_mx(a[4 * q] * cinv[4 * q], a[4 * q + 1] * cinv[4 * q + 1],
+                                 a[4 * q + 2] * cinv[4 * q + 2], a[4 * q + 3] * cinv[4 * q + 3]);
             }
             if (blk_ok) {
                 if (gh == 0) p.s_row[(row * p.heads + h) * NBLK + blk] = (uint8_t)rb;
-                // lane c < 16 of each half writes the scale of its register c
-                if (c32 < 16) {
-                    const int64_t col = h * HD + 32 * blk + 8 * (c32 >> 2) + 4 * gh + (c32 & 3);
+                // even lanes write the scale of register r = col_reg_of_lane(lane)
+                const int r = col_reg_of_lane(lane);
+                if ((lane & 1) == 0) {
+                    const int64_t col = h * HD + 32 * blk + 8 * (r >> 2) + 4 * gh + (r & 3);
                     p.s_col[(rbase / 32) * n_out + col] = (uint8_t)byte;
                 }
             }
