@@ -74,10 +74,12 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
     // pairs inputs 2*q8 and 2*q8 + 1: block 1 + q/2, register group
     // 2(q%2) + g, half u/2, elements 2(u%2) and 2(u%2) + 1.  Each lane gets the
     // other half-wave's registers it needs with v_permlane32_swap (below).
+    // The cos/sin values of the wave's 128 tokens are loaded first (wave
+    // column 1 only), so the four 32-token blocks wait for one round trip
+    // instead of four; RoPE then runs block by block inside the quantisation
+    // loop below, on copies of the accumulators, so its results stay in VGPRs.
+    uint2 tab[4][4][4];                                    // [block][q][cos lo, sin lo, cos hi, sin hi]
     if (wn == 1) {
-        // every cos/sin value of the wave's 128 tokens is loaded first, so the
-        // four 32-token blocks wait for one round trip instead of four
-        uint2 tab[4][4][4];                                // [block][q][cos lo, sin lo, cos hi, sin hi]
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t row = m0 + acc_row(wm, i, lane);
@@ -91,50 +93,51 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
                 tab[i][q][3] = *reinterpret_cast<const uint2 *>(p.sin + tr * ROPE + HALF + q8);
             }
         }
+    }
+    // RoPE of token block i: out[0] / out[1] are blocks 1 and 2 of the head
+    // after the rotation.
+    auto rope_block = [&](auto ii, float (&out)[2][16]) {
+        constexpr int i = decltype(ii)::value;
+        float cs0[16], sn0[16], cs1[16], sn1[16];          // cos/sin at q8 and 32 + q8
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float cs0[16], sn0[16], cs1[16], sn1[16];      // cos/sin at q8 and 32 + q8
+        for (int q = 0; q < 4; ++q) {
+            const uint2 c0 = tab[i][q][0], s0 = tab[i][q][1], c1 = tab[i][q][2], s1 = tab[i][q][3];
+            cs0[4 * q] = bf16_lo(c0.x); cs0[4 * q + 1] = bf16_hi(c0.x); cs0[4 * q + 2] = bf16_lo(c0.y); cs0[4 * q + 3] = bf16_hi(c0.y);
+            sn0[4 * q] = bf16_lo(s0.x); sn0[4 * q + 1] = bf16_hi(s0.x); sn0[4 * q + 2] = bf16_lo(s0.y); sn0[4 * q + 3] = bf16_hi(s0.y);
+            cs1[4 * q] = bf16_lo(c1.x); cs1[4 * q + 1] = bf16_hi(c1.x); cs1[4 * q + 2] = bf16_lo(c1.y); cs1[4 * q + 3] = bf16_hi(c1.y);
+            sn1[4 * q] = bf16_lo(s1.x); sn1[4 * q + 1] = bf16_hi(s1.x); sn1[4 * q + 2] = bf16_lo(s1.y); sn1[4 * q + 3] = bf16_hi(s1.y);
+        }
+        // Rotary input pairs sit in registers 4q'+e (q' = 0, 2) of one half-wave
+        // and 4q'+4+e of the other (see above).  v_permlane32_swap of
+        // registers r and r + 4 (r = 0-3, 8-11) leaves in X[r] the value
+        // that outputs with u < 2 use and in Y[r] the one that u >= 2 use, in
+        // both half-waves: low lanes keep their register r in X and receive
+        // the high lanes' register r in Y; high lanes receive the low lanes'
+        // register r + 4 in X and keep their own in Y.
+        float X[2][16], Y[2][16];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint2 c0 = tab[i][q][0], s0 = tab[i][q][1], c1 = tab[i][q][2], s1 = tab[i][q][3];
-                cs0[4 * q] = bf16_lo(c0.x); cs0[4 * q + 1] = bf16_hi(c0.x); cs0[4 * q + 2] = bf16_lo(c0.y); cs0[4 * q + 3] = bf16_hi(c0.y);
-                sn0[4 * q] = bf16_lo(s0.x); sn0[4 * q + 1] = bf16_hi(s0.x); sn0[4 * q + 2] = bf16_lo(s0.y); sn0[4 * q + 3] = bf16_hi(s0.y);
-                cs1[4 * q] = bf16_lo(c1.x); cs1[4 * q + 1] = bf16_hi(c1.x); cs1[4 * q + 2] = bf16_lo(c1.y); cs1[4 * q + 3] = bf16_hi(c1.y);
-                sn1[4 * q] = bf16_lo(s1.x); sn1[4 * q + 1] = bf16_hi(s1.x); sn1[4 * q + 2] = bf16_lo(s1.y); sn1[4 * q + 3] = bf16_hi(s1.y);
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 12; ++r) {
+                if ((r & 4) != 0) continue;
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i][1 + b][r]),
+                                                                 __float_as_uint(acc[i][1 + b][r + 4]), false, false);
+                X[b][r] = __uint_as_float(sw[0]);
+                Y[b][r] = __uint_as_float(sw[1]);
             }
-            // Rotary input pairs sit in registers 4q'+e (q' = 0, 2) of one half-wave
-            // and 4q'+4+e of the other (see above).  v_permlane32_swap of
-            // registers r and r + 4 (r = 0-3, 8-11) leaves in X[r] the value
-            // that outputs with u < 2 use and in Y[r] the one that u >= 2 use, in
-            // both half-waves: low lanes keep their register r in X and receive
-            // the high lanes' register r in Y; high lanes receive the low lanes'
-            // register r + 4 in X and keep their own in Y.
-            float X[2][16], Y[2][16];
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+        for (int q = 0; q < 4; ++q) {
 #pragma unroll
-                for (int r = 0; r < 12; ++r) {
-                    if ((r & 4) != 0) continue;
-                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i][1 + b][r]),
-                                                                     __float_as_uint(acc[i][1 + b][r + 4]),
-                                                                     false, false);
-                    X[b][r] = __uint_as_float(sw[0]);
-                    Y[b][r] = __uint_as_float(sw[1]);
-                }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int b = q / 2, r = 4 * (2 * (q % 2)) + 2 * (u % 2);
-                    const float ea = u < 2 ? X[b][r] : Y[b][r];
-                    const float eb = u < 2 ? X[b][r + 1] : Y[b][r + 1];
-                    const int v = 4 * q + u;
-                    acc[i][1][v] = ea * cs0[v] - eb * sn0[v];
-                    acc[i][2][v] = eb * cs1[v] + ea * sn1[v];
-                }
+            for (int u = 0; u < 4; ++u) {
+                const int b = q / 2, r = 4 * (2 * (q % 2)) + 2 * (u % 2);
+                const float ea = u < 2 ? X[b][r] : Y[b][r];
+                const float eb = u < 2 ? X[b][r + 1] : Y[b][r + 1];
+                const int v = 4 * q + u;
+                out[0][v] = ea * cs0[v] - eb * sn0[v];
+                out[1][v] = eb * cs1[v] + ea * sn1[v];
             }
         }
-    }
+    };
 
     // ---- dual MXFP8 quantisation (norm_const 1) ----
     // One 32-token block at a time: both code arrays are staged in the wave's
@@ -152,10 +155,22 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
         const int64_t rbase = m0 + 128 * wm + 32 * i;   // first token of this 32-token block
         const bool blk_ok = rbase < p.tokens;            // tokens % 128 == 0: blocks are whole
         const int64_t row = m0 + acc_row(wm, i, lane);
+        float rot[2][16];                                // blocks 1 and 2 after RoPE (wave column 1)
+        if (wn == 1) {
+            rope_block(ii, rot);
+        } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                rot[0][v] = acc[i][1][v];
+                rot[1][v] = acc[i][2][v];
+            }
+        }
         static_for<3>([&](auto jj) {
             constexpr int j = decltype(jj)::value;
             const int blk = 3 * wn + j;                  // 32-feature block within the head
-            const f32x16 &a = acc[i][j];
+            float a[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) a[v] = j == 0 ? acc[i][0][v] : rot[j - 1][v];
             // row direction: 32 features of one token (this lane and lane ^ 32)
             float rm = 0.0f;
 #pragma unroll
@@ -165,10 +180,8 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
             const uint32_t rb = mx_scale_byte(rm, 1.0f, rinv);
             const float rsf = sf_of_byte(rb);              // norm_const 1: codes are a / SF
             // column direction: 32 tokens of one feature (a register over the half-wave)
-            float cinv[16], av[16];
-#pragma unroll
-            for (int v = 0; v < 16; ++v) av[v] = a[v];
-            const uint32_t byte = col_scales_xch(av, 1.0f, cinv, lane, xch);
+            float cinv[16];
+            const uint32_t byte = col_scales_xch(a, 1.0f, cinv, lane, xch);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 *reinterpret_cast<uint32_t *>(wr + 32 * j + 8 * q) =
