@@ -270,6 +270,7 @@ WORKLOADS = {
     "proj_rope": wl_proj_rope,
     "proj_rope_mxfp8": lambda: wl_proj_rope(True),
     "proj_rope_w_in_out": lambda: wl_proj_rope(False, w_out_in=False),
+    "proj_rope_mxfp8_w_in_out": lambda: wl_proj_rope(True, w_out_in=False),
     "moe_mxfp8_srelu": lambda: wl_moe_mxfp8_srelu(False),
     "moe_mxfp8_srelu_fp8d": lambda: wl_moe_mxfp8_srelu(True),
     "moe_mxfp8_srelu_e5m2d": lambda: wl_moe_mxfp8_srelu(True, d_fp8="e5m2"),

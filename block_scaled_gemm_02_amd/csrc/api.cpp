@@ -507,11 +507,12 @@ int bsg_validate_gemm_proj_rope_mxfp8(const void *x, const void *w, const uint8_
     if (head_dim != 192 || qk_rope != 64)
         return fail(BSG_ERR_UNSUPPORTED, "only head_dim 192 with qk_rope 64 is built");
     if (w_out_in != 0 && w_out_in != 1) return fail(BSG_ERR_SHAPE, "w_out_in must be 0 or 1");
-    // w as [in, out] (w_out_in = 0, the page's default layout) is built for
-    // BF16 inputs; the page's MXFP8 inputs come as [out, in] codes and scales
-    if (!w_out_in && mx)
-        return fail(BSG_ERR_UNSUPPORTED, "MXFP8 inputs take w as [out, in] (w_out_in = 1)");
-    if (!w_out_in && q_lora * 2 * num_heads * head_dim >= (1ll << 31))
+    // w as [in, out] (w_out_in = 0, the page's default layout): with MXFP8
+    // inputs one head's w_scale columns are staged in LDS, which holds up to
+    // 64 scale bytes per feature
+    if (!w_out_in && mx && q_lora > 2048)
+        return fail(BSG_ERR_UNSUPPORTED, "MXFP8 inputs with w as [in, out] need q_lora <= 2048");
+    if (!w_out_in && (q_lora + 256) * (mx ? 1 : 2) * num_heads * head_dim >= (1ll << 31))
         return fail(BSG_ERR_UNSUPPORTED, "w as [in, out] too large for 32-bit offsets");
     if (mx && q_lora % 128)
         return fail(BSG_ERR_UNSUPPORTED, "MXFP8 inputs need q_lora to be a multiple of 128");

@@ -280,7 +280,17 @@ struct OperandDesc {
     // K row 0, row_bytes the stride between K rows (M or N), bytes ends at
     // the last K row's last column, and mn_valid columns of the tile exist
     uint32_t mn_valid = 0;
+    // FMT_E4M3_RM with FMT_TB (B only): B's scales for the whole K range,
+    // staged in LDS by the caller as rows of sf_lds_stride bytes, byte kb of
+    // row n at sf_lds + n * sf_lds_stride + kb (the layout of row-major
+    // scales); the ring's per-pair B scale loads then read nothing
+    const uint8_t *sf_lds = nullptr;
+    uint32_t sf_lds_stride = 0;
 };
+// Row-major E8M0 scales whose B operand has its scales staged in LDS (see
+// OperandDesc::sf_lds): the projection's MXFP8 path with w stored [in, out].
+template <int F>
+constexpr bool b_static_sf() { return F == (FMT_E4M3_RM | FMT_TB); }
 
 // The LDS holds two "pair slots"; a pair slot holds two consecutive K steps
 // (128 bytes of every row): the A panel (256 rows x 128 B), the B panel
@@ -401,6 +411,8 @@ struct PipeDesc {
     uint32_t vsr[2];          // row-major scales: per-lane voffsets of this wave's two scale loads (pair 0)
     int kblocks;              // valid 32-wide K blocks
     int sf_kt;                // K atoms per row group (ceil(K/128))
+    const uint8_t *bsf;       // b_static_sf: this lane's row of B scales in LDS (block 0)
+    uint32_t bsf_rm;          // b_static_sf: bytes between those rows
 };
 
 // The two pair slots are distinct LDS objects, selected by compile-time index.
@@ -442,7 +454,7 @@ constexpr int b_loads() { return b_t(F) ? kTLoads : (F == FMT_BF16_BT ? kBtLoads
 template <int F, int NB>
 constexpr int loads_per_pair()
 {
-    return a_loads<F>() + b_loads<F, NB>() + (F == FMT_E4M3_RM ? 2 : Ring<F>::kScaleSets);
+    return a_loads<F>() + b_loads<F, NB>() + (fmt_base(F) == FMT_E4M3_RM ? 2 : Ring<F>::kScaleSets);
 }
 template <int F, int NB>
 constexpr int mfmas_per_step() { return (is_fp8(F) ? 1 : 2) * 4 * NB; }
@@ -452,10 +464,14 @@ template <int F>
 constexpr int a_reads() { return a_t(F) ? 16 : 8; }
 template <int F, int NB>
 constexpr int b_reads() { return (b_t(F) || F == FMT_BF16_BT) ? 4 * NB : 2 * NB; }
+// scale reads of a stage that has them: one word set per operand, or (B
+// scales staged in LDS) one A read and one word per B block
+template <int F, int NB>
+constexpr int scale_reads() { return b_static_sf<F>() ? 1 + NB : 2; }
 template <int F, int NB>
 constexpr int reads_in_stage(bool odd)
 {
-    return a_reads<F>() + b_reads<F, NB>() + (scales_in_stage<F>(odd) ? 2 : 0);
+    return a_reads<F>() + b_reads<F, NB>() + (scales_in_stage<F>(odd) ? scale_reads<F, NB>() : 0);
 }
 
 // Where this wave's loads of pair p go: code offset (K position, or out of
@@ -474,7 +490,7 @@ __device__ __forceinline__ PairAddr pair_addr(const PipeDesc<NB> &d, int pair)
     a.kb_oob[1] = kb + ((kb + (d.lc16 ^ 16u) < d.row_bytes) ? 0u : kOOB);
     a.kat = (uint32_t)pair * d.at_pair;
     a.kbt = (uint32_t)pair * d.bt_pair;
-    if constexpr (F == FMT_E4M3_RM) {
+    if constexpr (fmt_base(F) == FMT_E4M3_RM) {
         // row-major scales: the pair's 4 bytes of a row follow its previous pair's
 #pragma unroll
         for (int h = 0; h < 2; ++h) a.so[h] = pair < d.sf_kt ? d.vsr[h] + 4u * (uint32_t)pair : kOOB;
@@ -504,7 +520,7 @@ __device__ __forceinline__ void load_one(const PipeDesc<NB> &d, uint8_t *st, con
         constexpr int q = L - LA;
         constexpr bool kmaj = b_t(F) || F == FMT_BF16_BT;
         lds_load16(d.rb, st + a_region<F>() + 1024 * (LB * w + q), d.vb[q] + (kmaj ? a.kbt : a.kb_oob[q & 1]));
-    } else if constexpr (F == FMT_E4M3_RM) {
+    } else if constexpr (fmt_base(F) == FMT_E4M3_RM) {
         constexpr int h = L - LA - LB;     // rows 0-15 (h = 0) or 16-31 (h = 1) of each 32-row block
         lds_load4(d.rs, st + SC + 1024 * w + 256 * h, a.so[h]);
     } else {
@@ -560,9 +576,12 @@ struct ReadAddr {
     const uint8_t *a0, *b0;   // this lane's A / B row in block 0
     uint32_t p0, p1;          // byte offsets of its two chunks
     const uint8_t *sa, *sb;   // this lane's scale words
+    uint32_t sb_blk;          // b_static_sf: bytes between the B scale words of blocks j and j + 1
 };
+// pair: K pair of the stage read (used by b_static_sf only)
 template <int F, int NB, int H>
-__device__ __forceinline__ ReadAddr read_addr(const uint8_t *st, int wm, int wn, int lane)
+__device__ __forceinline__ ReadAddr read_addr(const uint8_t *st, int wm, int wn, int lane, const PipeDesc<NB> &d,
+                                              int pair)
 {
     ReadAddr r;
     const uint32_t row = lane & 31, g = lane >> 5;
@@ -594,6 +613,14 @@ __device__ __forceinline__ ReadAddr read_addr(const uint8_t *st, int wm, int wn,
     const uint8_t *sc = st + a_region<F>() + b_region<F>() + (fmt_base(F) == FMT_E2M1 ? 4096 * H : 0);
     r.sa = sc + 1024 * wm + 16 * row;
     r.sb = sc + 1024 * (2 + wn) + 16 * row;
+    r.sb_blk = 0;
+    if constexpr (b_static_sf<F>()) {
+        r.sb = d.bsf + 4u * (uint32_t)pair;
+        r.sb_blk = 32u * d.bsf_rm;
+    } else {
+        (void)d;
+        (void)pair;
+    }
     return r;
 }
 // One 8-byte transposing read of a K-major FP8 tile into half e of chunk
@@ -645,15 +672,19 @@ __device__ __forceinline__ void read_one(Frags<NB> &f, const ReadAddr &r)
         f.b[j][h] = *reinterpret_cast<const i32x4 *>(r.b0 + 32 * kPK * j + (h ? r.p1 : r.p0));
     } else if constexpr (R == RA + b_reads<F, NB>()) {
         f.sa = *reinterpret_cast<const i32x4 *>(r.sa);
+    } else if constexpr (b_static_sf<F>()) {
+        constexpr int j = R - RA - b_reads<F, NB>() - 1;
+        f.sb[j] = *reinterpret_cast<const int *>(r.sb + j * r.sb_blk);
     } else {
         f.sb = *reinterpret_cast<const i32x4 *>(r.sb);
     }
 }
 
 template <int F, int NB>
-__device__ __forceinline__ void read_frags0(Frags<NB> &f, const uint8_t *st, int wm, int wn, int lane)
+__device__ __forceinline__ void read_frags0(Frags<NB> &f, const uint8_t *st, int wm, int wn, int lane,
+                                            const PipeDesc<NB> &d)
 {
-    const ReadAddr r = read_addr<F, NB, 0>(st, wm, wn, lane);
+    const ReadAddr r = read_addr<F, NB, 0>(st, wm, wn, lane, d, 0);
     static_for<reads_in_stage<F, NB>(false)>([&](auto q) { read_one<F, NB, decltype(q)::value>(f, r); });
 }
 
@@ -742,7 +773,7 @@ __device__ __forceinline__ void pipe_step(f32x16 (&acc)[4][NB], Frags<NB> &cur, 
     PairAddr la{};
     if constexpr (ODD) la = pair_addr<F, NB>(d, (ks + 3) >> 1);
     uint8_t *const lslot = ring.template at<LSL>();
-    const ReadAddr ra = read_addr<F, NB, RH>(ring.template at<RS>(), wm, wn, lane);
+    const ReadAddr ra = read_addr<F, NB, RH>(ring.template at<RS>(), wm, wn, lane, d, (ks + 1) >> 1);
     if constexpr (Ring<F>::kScaled && !scales_in_stage<F>(!ODD)) {
         nxt.sa = cur.sa;
         nxt.sb = cur.sb;
@@ -776,10 +807,11 @@ template <int F, int NB = 4>
 __device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[4][NB], const RingSlots<F> &ring,
                                               const OperandDesc &A, const OperandDesc &B, int64_t k)
 {
-    static_assert(NB == 4 || is_bf16(F) || F == FMT_E4M3_RM, "atom scales need 128-column wave tiles");
+    static_assert(NB == 4 || is_bf16(F) || fmt_base(F) == FMT_E4M3_RM, "atom scales need 128-column wave tiles");
     static_assert(F != FMT_BF16_BT || 64 * NB <= kBtData / 2, "a K-major B row holds the tile's columns");
-    static_assert(!(a_t(F) || b_t(F)) || (is_fp8(F) && F != FMT_E4M3_RM && NB == 4),
-                  "MN-major operands: FP8 with scale atoms, 256 x 256 tiles");
+    static_assert(!(a_t(F) || b_t(F)) || (is_fp8(F) && (NB == 4 || b_static_sf<F>())),
+                  "MN-major operands: FP8, 256 x 256 tiles (or the projection's [in, out] weights)");
+    static_assert(!a_t(F) || fmt_base(F) != FMT_E4M3_RM, "row-major scales with an m-major A are not built");
     // the wave index is uniform: keep everything derived from it in SGPRs
     const int t = threadIdx.x, lane = t & 63;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w >> 1, wn = w & 1;
@@ -846,7 +878,9 @@ __device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[4][NB], const RingSl
     d.rs = d.ra;
     d.vs = kOOB;
     d.vsr[0] = d.vsr[1] = kOOB;
-    if constexpr (F == FMT_E4M3_RM) {
+    d.bsf = nullptr;
+    d.bsf_rm = 0;
+    if constexpr (fmt_base(F) == FMT_E4M3_RM) {
         // Row-major scales, staged in the layout the fragment reads expect:
         // wave w fills 512 bytes at 1 KB * w, where the 16 bytes at 16*r32 are
         // the pair's 4 scale bytes of the rows 32q + r32 (q = 0..3) of A row
@@ -863,6 +897,12 @@ __device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[4][NB], const RingSl
             d.vsr[h] = (w < 2 || q < (uint32_t)NB) ? row * S.sf_rm : kOOB;
         }
         d.sf_kt = (int)((k + 127) / 128);
+        if constexpr (b_static_sf<F>()) {
+            // B's words come from the LDS copy; the ring's B scale loads read nothing
+            if (w >= 2) d.vsr[0] = d.vsr[1] = kOOB;
+            d.bsf = B.sf_lds + (32u * NB * wn + ((uint32_t)lane & 31u)) * B.sf_lds_stride;
+            d.bsf_rm = B.sf_lds_stride;
+        }
     } else if constexpr (Ring<F>::kScaled) {
         // wave w loads the K atom of atom row group w&1 of A (w < 2) or B (w >= 2)
         const OperandDesc &S = w < 2 ? A : B;
@@ -883,7 +923,7 @@ __device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[4][NB], const RingSl
     s_wait_vm<loads_per_pair<F, NB>()>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    read_frags0<F, NB>(fx, ring.template at<0>(), wm, wn, lane);
+    read_frags0<F, NB>(fx, ring.template at<0>(), wm, wn, lane, d);
     for (int ks = 0; ks < nks; ks += 4) {
         pipe_step<F, NB, 0>(acc, fx, fy, d, ring, ks, w, wm, wn, lane);
         if (ks + 1 < nks) pipe_step<F, NB, 1>(acc, fy, fx, d, ring, ks + 1, w, wm, wn, lane);

@@ -56,6 +56,9 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
 {
     constexpr int HD = 192, HALF = 32, ROPE = 64, NBLK = HD / 32;
     BSG_DECLARE_RING(F, ring);
+    // MXFP8 inputs with w as [in, out]: the head's w_scale columns, as rows
+    // of scale bytes per feature (up to 64 bytes, q_lora <= 2048)
+    __shared__ __attribute__((aligned(16))) uint8_t wsc[b_static_sf<F>() ? 192 * 68 : 16];
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
     const int c32 = lane & 31, gh = lane >> 5;
     int64_t h, m0;
@@ -75,14 +78,41 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
         B.bytes = (uint32_t)(p.q_lora - 1) * kstride + 2u * HD;
         B.row_bytes = kstride;
     }
-    if constexpr (F == FMT_E4M3_RM) {
+    if constexpr (b_static_sf<F>()) {
+        // w [in, out] E4M3 codes: the head's 192 columns of each of the q_lora
+        // K rows (n-major B); K rows past q_lora read zeros
+        const uint32_t kstride = (uint32_t)n_out;
+        B.base = p.w + HD * h;
+        B.bytes = (uint32_t)(p.q_lora - 1) * kstride + (uint32_t)(n_out - HD * h);
+        B.row_bytes = kstride;
+        B.mn_valid = HD;
+        // w_scale (q_lora/32, n_out): transpose the head's 192 columns into
+        // LDS rows of kb bytes per feature, at an odd number of words per row
+        // (the 32 rows one fragment read touches then hit distinct banks)
+        const uint32_t kb_n = (uint32_t)(p.q_lora / 32);
+        const uint32_t stride = (kb_n / 4) % 2 == 0 ? kb_n + 4 : kb_n;
+        for (uint32_t wd = (uint32_t)t; wd < kb_n * (HD / 4); wd += kThreads) {
+            const uint32_t kb = wd / (HD / 4), c4 = 4 * (wd % (HD / 4));
+            const uint32_t v = *reinterpret_cast<const uint32_t *>(p.w_scale + (int64_t)kb * n_out + HD * h + c4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wsc[(c4 + e) * stride + kb] = (uint8_t)(v >> (8 * e));
+        }
+        __syncthreads();
+        B.sf = nullptr;
+        B.sf_bytes = 0;
+        B.sf_lds = wsc;
+        B.sf_lds_stride = stride;
+    }
+    if constexpr (fmt_base(F) == FMT_E4M3_RM) {
         const uint32_t srow = (uint32_t)(p.q_lora / 32);          // scale bytes per row
         A.sf = p.x_scale + m0 * srow;
         A.sf_rm = srow;
         A.sf_bytes = (uint32_t)(rows_a * srow);
-        B.sf = p.w_scale + h * HD * srow;
-        B.sf_rm = srow;
-        B.sf_bytes = (uint32_t)(HD * srow);
+        if constexpr (!b_static_sf<F>()) {
+            B.sf = p.w_scale + h * HD * srow;
+            B.sf_rm = srow;
+            B.sf_bytes = (uint32_t)(HD * srow);
+        }
     }
     f32x16 acc[4][3];
     mainloop_pipe<F, 3>(acc, ring, A, B, p.q_lora);
@@ -230,7 +260,6 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
 hipError_t launch_proj_rope(const ProjRopeArgs &a, hipStream_t s)
 {
     if (a.tokens == 0 || a.heads == 0) return hipSuccess;
-    if (!a.w_out_in && a.mxfp8) return hipErrorNotSupported;
     ProjParams p;
     p.x = reinterpret_cast<const uint8_t *>(a.x);
     p.w = reinterpret_cast<const uint8_t *>(a.w);
@@ -241,7 +270,8 @@ hipError_t launch_proj_rope(const ProjRopeArgs &a, hipStream_t s)
     p.tokens = a.tokens; p.q_lora = a.q_lora; p.heads = a.heads;
     p.row_bytes = (uint32_t)(a.mxfp8 ? a.q_lora : 2 * a.q_lora);
     dim3 grid((unsigned)a.heads, (unsigned)((a.tokens + kTileM - 1) / kTileM));
-    if (a.mxfp8) hipLaunchKernelGGL(k_proj_rope<FMT_E4M3_RM>, grid, dim3(kThreads), 0, s, p);
+    if (a.mxfp8 && a.w_out_in) hipLaunchKernelGGL(k_proj_rope<FMT_E4M3_RM>, grid, dim3(kThreads), 0, s, p);
+    else if (a.mxfp8) hipLaunchKernelGGL((k_proj_rope<FMT_E4M3_RM | FMT_TB>), grid, dim3(kThreads), 0, s, p);
     else if (a.w_out_in) hipLaunchKernelGGL(k_proj_rope<FMT_BF16>, grid, dim3(kThreads), 0, s, p);
     else hipLaunchKernelGGL(k_proj_rope<FMT_BF16_BT>, grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();

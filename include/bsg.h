@@ -281,13 +281,14 @@ int grouped_gemm_dswiglu(const void *a, const void *b, const uint8_t *sfa, const
  *       (in_dtype E4M3, the page's MXFP8-input path)
  *  w    w_out_in = 1: (num_heads*head_dim, q_lora) [out, in], same dtype
  *       as x.  w_out_in = 0: (q_lora, num_heads*head_dim) [in, out], the
- *       page's default layout, BF16 inputs only (the page's MXFP8 inputs
- *       take w and w_scale as [out, in]; E4M3 with w_out_in = 0 returns
- *       UNSUPPORTED).  Both layouts give identical results.
+ *       page's default layout; with E4M3 inputs it needs q_lora <= 2048
+ *       (else UNSUPPORTED).  Both layouts give identical results.
  *  x_scale  (tokens, q_lora/32) E8M0, row-major: byte (t, b) scales
  *           x[t, 32b .. 32b+31]                      (E4M3 inputs only)
- *  w_scale  (num_heads*head_dim, q_lora/32) E8M0, row-major, [out, in]
- *                                                    (E4M3 inputs only)
+ *  w_scale  E8M0, following w's layout ("GEMM + RoPE + MXFP8 Projection
+ *           (SM100)", Shapes): (num_heads*head_dim, q_lora/32) when
+ *           w_out_in = 1, (q_lora/32, num_heads*head_dim) when w_out_in = 0;
+ *           byte (o, b) scales w[o, 32b .. 32b+31]   (E4M3 inputs only)
  *           The MXFP8 path contracts x[t,i]*2^(x_scale-127) with
  *           w[o,i]*2^(w_scale-127) in fp32; both must be NULL for BF16.
  *  cos, sin  (tokens, qk_rope) bf16
@@ -296,8 +297,7 @@ int grouped_gemm_dswiglu(const void *a, const void *b, const uint8_t *sfa, const
  *  out_scales_col             (tokens/32, num_heads, head_dim) E8M0
  *  Sizes: tokens % 128 == 0, q_lora % 32 == 0 (BF16) or % 128 == 0
  *  (E4M3), head_dim == 192, qk_rope == 64.  E4M3 inputs need 4-byte
- *  aligned x_scale/w_scale (the page's MXFP8 class API also takes [out, in]
- *  codes and scales only).  Violations return SHAPE / UNSUPPORTED / ALIGN
+ *  aligned x_scale/w_scale.  Violations return SHAPE / UNSUPPORTED / ALIGN
  *  before anything is enqueued.
  */
 int gemm_proj_rope_mxfp8(const void *x, const void *w, const uint8_t *x_scale,

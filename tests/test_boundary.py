@@ -176,11 +176,13 @@ def vp(**kw):
 def test_proj_rope_validation():
     assert vp() == OK
     assert vp(tokens=200) == SHAPE                       # tokens % TILE_M (128)
-    # MXFP8 inputs: row-major E8M0 scales required, 4-byte aligned, [out, in] weight, q_lora % 128
+    # MXFP8 inputs: row-major E8M0 scales required, 4-byte aligned, q_lora % 128; w [in, out] up to q_lora 2048
     assert vp(in_dtype=bsg.E4M3) == NULLPTR
     assert vp(in_dtype=bsg.E4M3, x_scale=P, w_scale=P) == OK
     assert vp(in_dtype=bsg.E4M3, x_scale=P + 2, w_scale=P) == ALIGN
-    assert vp(in_dtype=bsg.E4M3, x_scale=P, w_scale=P, w_out_in=0) == UNSUP   # MXFP8 w comes [out, in]
+    assert vp(in_dtype=bsg.E4M3, x_scale=P, w_scale=P, w_out_in=0) == OK      # MXFP8 w and w_scale [in, out]
+    assert vp(in_dtype=bsg.E4M3, x_scale=P, w_scale=P, w_out_in=0, q_lora=2176) == UNSUP   # > 64 scale bytes
+    assert vp(in_dtype=bsg.E4M3, x_scale=P, w_scale=P, w_out_in=0, q_lora=2048) == OK
     assert vp(in_dtype=bsg.E4M3, x_scale=P, w_scale=P, q_lora=160) == UNSUP
     assert vp(in_dtype=bsg.E2M1X2) == DTYPE
     assert vp(x_scale=P) == SHAPE                        # scales only on the MXFP8 path

@@ -33,6 +33,14 @@ def run_proj(p):
     return qr, sr, qc, sc
 
 
+def w_out_in_view(p):
+    """MXFP8 w and w_scale as [out, in] (the oracle's layout): transposed
+    back when the problem stores them [in, out]."""
+    if p.sizes["w_out_in"]:
+        return p.t["w"], p.t["w_scale"]
+    return p.t["w"].t().contiguous(), p.t["w_scale"].t().contiguous()
+
+
 def mx_block_bound(p, t0, t1):
     """Upper bound of Bmax (sum over 32-wide K blocks of the largest |product|)
     for MXFP8 inputs: sum_b max|x^[t,b]| * max|w^[o,b]|, carried through the
@@ -45,8 +53,9 @@ def mx_block_bound(p, t0, t1):
         v = v.reshape(v.shape[0], Q // 32, 32)
         return np.abs(v).max(-1) * 2.0 ** (scales.numpy().astype(np.float64) - 127)
 
+    w, ws = w_out_in_view(p)
     bx = dec(p.t["x"][t0:t1], p.t["x_scale"][t0:t1])
-    bw = dec(p.t["w"], p.t["w_scale"])
+    bw = dec(w, ws)
     b = (bx @ bw.T).reshape(t1 - t0, H, D)
     cos = np.abs(p.t["cos"][t0:t1].double().numpy())[:, None, :]
     sin = np.abs(p.t["sin"][t0:t1].double().numpy())[:, None, :]
@@ -60,7 +69,8 @@ def oracle_check(p, qr, sr, qc, sc, t0, t1, what):
     s = p.sizes
     T, H, D = s["tokens"], s["heads"], s["head_dim"]
     if s.get("in_dtype") == "e4m3":
-        y, sab = O.proj_rope_mx(p.t["x"], p.t["x_scale"], p.t["w"], p.t["w_scale"], O.bits16(p.t["cos"]),
+        w, ws = w_out_in_view(p)
+        y, sab = O.proj_rope_mx(p.t["x"], p.t["x_scale"], w, ws, O.bits16(p.t["cos"]),
                                 O.bits16(p.t["sin"]), T, s["q_lora"], H, D, s["qk_rope"], t0, t1)
         bound = sum_bound(sab, s["q_lora"], bmax=mx_block_bound(p, t0, t1)) + 1e-6 * sab
     else:
@@ -207,3 +217,49 @@ def test_proj_rope_mxfp8_full_size_sampled():
     for t0 in (0, 3968):
         say(f"  oracle tokens {t0}..{t0 + 127}")
         oracle_check(p, qr, sr, qc, sc, t0, t0 + 128, f"mx tokens {t0}")
+
+
+@pytest.mark.parametrize("case", [
+    dict(tokens=256, q_lora=256, heads=3),
+    dict(tokens=384, q_lora=128, heads=2),     # a 128-token tail tile
+    dict(tokens=128, q_lora=2048, heads=2),    # the largest q_lora of this path (64 scale bytes per feature)
+])
+def test_proj_rope_mxfp8_w_in_out_matches_oracle(case):
+    """MXFP8 inputs with w and w_scale as [in, out] (w_out_in = 0, "GEMM +
+    RoPE + MXFP8 Projection (SM100)", Shapes: w (Q_LORA, NUM_HEADS*HEAD_DIM),
+    w_scale (Q_LORA/32, NUM_HEADS*HEAD_DIM)): codes staged K-major, the head's
+    scale columns transposed into LDS."""
+    say(f"proj_rope MXFP8 w [in, out] parity {case}")
+    p = W.proj_rope_problem(case["tokens"], case["q_lora"], case["heads"], seed=14, in_dtype="e4m3",
+                            w_out_in=False)
+    assert p.t["w"].shape == (case["q_lora"], case["heads"] * 192)
+    assert p.t["w_scale"].shape == (case["q_lora"] // 32, case["heads"] * 192)
+    qr, sr, qc, sc = run_proj(p)
+    oracle_check(p, qr, sr, qc, sc, 0, case["tokens"], "mx w_in_out " + str(case))
+
+
+def test_proj_rope_mxfp8_w_layouts_agree_bit_for_bit():
+    """The same MXFP8 codes and scales as [out, in] and as [in, out] give
+    identical outputs."""
+    say("proj_rope MXFP8 w layouts")
+    p1 = W.proj_rope_problem(256, 1536, 4, seed=15, in_dtype="e4m3", w_out_in=True)
+    p0 = W.proj_rope_problem(256, 1536, 4, seed=15, in_dtype="e4m3", w_out_in=True)
+    p0.t["w"] = p1.t["w"].t().contiguous()
+    p0.t["w_scale"] = p1.t["w_scale"].t().contiguous()
+    p0.sizes["w_out_in"] = 0
+    a = run_proj(p1)
+    b = run_proj(p0)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_proj_rope_mxfp8_w_in_out_full_size_sampled():
+    """MXFP8 x (4096,1536), w (1536, 24576) and w_scale (48, 24576) as [in,
+    out], 128 heads x 192: the first and last 128-token panels vs the oracle."""
+    say("proj_rope MXFP8 w [in, out] full size")
+    p = W.proj_rope_dsv3(device="cuda", in_dtype="e4m3", w_out_in=False)
+    qr, sr, qc, sc = run_proj(p)
+    p.t = {k: v.cpu() for k, v in p.t.items()}
+    for t0 in (0, 3968):
+        say(f"  oracle tokens {t0}..{t0 + 127}")
+        oracle_check(p, qr, sr, qc, sc, t0, t0 + 128, f"mx w_in_out tokens {t0}")

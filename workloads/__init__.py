@@ -298,19 +298,22 @@ def proj_rope_problem(tokens: int, q_lora: int, heads: int = 128, head_dim: int 
     """x (tokens,Q_LORA) bf16 N(0,1); w bf16 N(0,0.02), [out,in] when w_out_in
     else [in,out]; bf16 cos/sin (tokens,qk_rope) from positions, base 10000.
 
-    in_dtype "e4m3" (MXFP8 inputs, w [out,in] only): x and w are E4M3 codes of
-    block-stretched normal draws with row-major E8M0 scale bytes x_scale
-    (tokens, Q_LORA/32) and w_scale (out, Q_LORA/32), drawn around the bytes
-    that give N(0,1) and N(0,0.02) magnitudes (w six binades below x)."""
+    in_dtype "e4m3" (MXFP8 inputs): x and w are E4M3 codes of block-stretched
+    normal draws with row-major E8M0 scale bytes x_scale (tokens, Q_LORA/32)
+    and w_scale (out, Q_LORA/32), drawn around the bytes that give N(0,1) and
+    N(0,0.02) magnitudes (w six binades below x); with w [in,out] both w and
+    w_scale are stored transposed, (Q_LORA, out) and (Q_LORA/32, out)."""
     g = _gen(seed + 3, device)
     extra = {}
     if in_dtype == E4M3:
-        assert w_out_in, "MXFP8 inputs take w as [out, in]"
         x = _codes_from_normal(torch.randn(tokens, q_lora, generator=g, device=device), E4M3)
         w = _codes_from_normal(torch.randn(heads * head_dim, q_lora, generator=g, device=device), E4M3)
         extra["x_scale"] = _sf_bytes(tokens * (q_lora // 32), 120, 1, g, device).reshape(tokens, q_lora // 32)
         extra["w_scale"] = _sf_bytes(heads * head_dim * (q_lora // 32), 114, 1, g, device).reshape(
             heads * head_dim, q_lora // 32)
+        if not w_out_in:
+            w = w.t().contiguous()
+            extra["w_scale"] = extra["w_scale"].t().contiguous()
     else:
         x = torch.randn(tokens, q_lora, generator=g, device=device).to(torch.bfloat16)
         w = (torch.randn(heads * head_dim, q_lora, generator=g, device=device) * 0.02).to(torch.bfloat16)
