@@ -136,7 +136,39 @@ def cpu_sample_srelu(p, rows=5120):
                 sample=f"{rows} rows of expert 0 (x N={n}, K={k}), fp64 oracle incl. B dequantisation")
 
 
-def wl_moe_dswiglu():
+def cpu_model():
+    """The host CPU's model name and logical CPU count."""
+    name = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{name} ({os.cpu_count()} logical CPUs)"
+
+
+def cpu_dense_256_one_thread():
+    """The oracle on the small dense workload (256^3, E4M3, fp32 C) with one
+    thread: the single-threaded CPU reference point."""
+    import oracle as O
+    import workloads as W
+    p = W.dense_256()
+    t = p.t
+    n_thr = O.threads()
+    O.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        O.gemm_amax_full(t["a"], t["b"], t["sfa"], t["sfb"], 256, 256, 256, 1, "e4m3")
+        dt = time.perf_counter() - t0
+    finally:
+        O.set_threads(n_thr)
+    return dict(seconds=round(dt, 4), value=round(2.0 * 256 ** 3 / dt / 1e9, 3), unit="GFLOP/s", cores=1)
+
+
+def wl_moe_dswiglu(b_major="k"):
     import torch
     import block_scaled_gemm_02_amd as bsg
     import workloads as W
@@ -150,42 +182,55 @@ def wl_moe_dswiglu():
     sfd_row = torch.empty(W.sf_atom_bytes(m, 2 * n, 1), dtype=torch.uint8, device="cuda")
     sfd_col = torch.empty(W.sf_atom_bytes(2 * n, m, 1), dtype=torch.uint8, device="cuda")
     dprob = torch.zeros(m, device="cuda")
+    if b_major == "n":
+        t["b"] = t["b"].reshape(L, n, k).transpose(1, 2).contiguous()
 
     def step():
         dprob.zero_()
         bsg.grouped_gemm_dswiglu(t["a"], t["b"], t["sfa"], t["sfb"], t["c"], t["offsets"], t["alpha"], t["beta"],
-                                 t["prob"], t["norm_const"], d, d_col, sfd_row, sfd_col, dprob, m, n, k, L, "e4m3")
+                                 t["prob"], t["norm_const"], d, d_col, sfd_row, sfd_col, dprob, m, n, k, L, "e4m3",
+                                 b_major=b_major)
 
     valid_m = s["valid_m"]
     alg = valid_m * k + L * n * k + t["sfa"].numel() + t["sfb"].numel() + valid_m * 2 * n * 2 \
         + 2 * valid_m * 2 * n + sfd_row.numel() + sfd_col.numel() + 4 * valid_m
-    info = dict(name="moe_mxfp8_dswiglu", fmt="e4m3", flops=2.0 * valid_m * n * k, alg_bytes=alg,
-                kernel="k_grouped",
+    info = dict(name="moe_mxfp8_dswiglu" + ("" if b_major == "k" else "_bn"), fmt="e4m3",
+                flops=2.0 * valid_m * n * k, alg_bytes=alg, kernel="k_grouped",
                 config={"workload": "grouped MXFP8 GEMM + dSwiGLU backward, MXFP8 D (row + column) and dprob",
                         "experts": L, "n": n, "k": k, "valid_m": valid_m, "routed_rows": 28672,
-                        "routing": "multinomial Zipf(1.1), padded to 256", "c": "bf16 (valid_m, 2N)"},
+                        "routing": "multinomial Zipf(1.1), padded to 256", "c": "bf16 (valid_m, 2N)",
+                        "b_major": b_major},
                 cpu=None)
     return step, info
 
 
-def wl_dense_8192(fmt):
+def wl_dense_8192(fmt, majors="kkn"):
+    """majors: A ('k' or 'm'), B ('k' or 'n') and C ('n' or 'm') storage."""
     import torch
     import block_scaled_gemm_02_amd as bsg
     import workloads as W
     p = W.dense_8192(fmt, device="cuda")
     s, t = p.sizes, p.t
-    c = torch.empty(s["l"], s["m"], s["n"], dtype=torch.bfloat16, device="cuda")
+    am, bm, cm = majors
+    L, m, n, k = s["l"], s["m"], s["n"], s["k"]
+    if am == "m":
+        t["a"] = t["a"].reshape(L, m, k).transpose(1, 2).contiguous()
+    if bm == "n":
+        t["b"] = t["b"].reshape(L, n, k).transpose(1, 2).contiguous()
+    c = torch.empty(L, m, n, dtype=torch.bfloat16, device="cuda")
     amax = torch.empty(1, device="cuda")
 
     def step():
-        bsg.gemm_amax(t["a"], t["b"], t["sfa"], t["sfb"], c, amax, s["m"], s["n"], s["k"], s["l"], fmt)
+        bsg.gemm_amax(t["a"], t["b"], t["sfa"], t["sfb"], c, amax, m, n, k, L, fmt,
+                      a_major=am, b_major=bm, c_major=cm)
 
-    flops = 2.0 * s["l"] * s["m"] * s["n"] * s["k"]
+    flops = 2.0 * L * m * n * k
     ab = t["a"].numel() + t["b"].numel() + t["sfa"].numel() + t["sfb"].numel()
-    info = dict(name=f"dense_8192_{fmt}", fmt=fmt, flops=flops, alg_bytes=ab + c.numel() * 2,
-                kernel="k_gemm_amax",
+    info = dict(name=f"dense_8192_{fmt}" + ("" if majors == "kkn" else "_" + majors), fmt=fmt, flops=flops,
+                alg_bytes=ab + c.numel() * 2, kernel="k_gemm_amax",
                 config={"workload": f"batched dense MX{'FP8' if fmt == 'e4m3' else 'FP4'} GEMM + amax",
-                        "m": 8192, "n": 8192, "k": 8192, "l": 4, "c": "bf16"},
+                        "m": 8192, "n": 8192, "k": 8192, "l": 4, "c": "bf16",
+                        "majors": {"a": am, "b": bm, "c": cm}},
                 cpu=None)
     return step, info
 
@@ -278,7 +323,10 @@ WORKLOADS = {
     "moe_mxfp8_srelu_discrete": lambda: wl_moe_mxfp8_srelu(False, discrete=True),
     "moe_mxfp4_srelu": lambda: wl_moe_mxfp8_srelu(False, fmt="e2m1"),
     "moe_mxfp8_dswiglu": wl_moe_dswiglu,
+    "moe_mxfp8_dswiglu_bn": lambda: wl_moe_dswiglu("n"),
     "dense_8192_e4m3": lambda: wl_dense_8192("e4m3"),
+    "dense_8192_e4m3_mnn": lambda: wl_dense_8192("e4m3", "mnn"),
+    "dense_8192_e4m3_kkm": lambda: wl_dense_8192("e4m3", "kkm"),
     "dense_8192_e2m1": lambda: wl_dense_8192("e2m1"),
     "dense_256": wl_dense_256,
     "moe_bf16": wl_moe_bf16,
@@ -399,6 +447,8 @@ def main():
     }
     if info.get("cpu") and not args.no_cpu:
         out["cpu_baseline"] = info["cpu"]()
+        out["cpu_baseline"]["cpu_model"] = cpu_model()
+        out["cpu_baseline"]["dense_256_one_thread"] = cpu_dense_256_one_thread()
     line = json.dumps(out)
     print(line, flush=True)
     if args.report:

@@ -80,6 +80,8 @@ def lib():
         L.orc_mx_quant_cols.restype = None
         L.orc_mx_quant_cols.argtypes = [p, i64, i64, i64, ctypes.c_float, i32, p, p]
         L.orc_num_threads.restype = i32
+        L.orc_set_threads.restype = None
+        L.orc_set_threads.argtypes = [i32]
         _lib = L
     return _lib
 
@@ -109,6 +111,11 @@ def bits16(t):
 
 def threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads for the oracle calls that follow (timing only)."""
+    lib().orc_set_threads(int(n))
 
 
 # ---------------------------------------------------------------------------

@@ -735,3 +735,14 @@ int orc_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads for the following calls (n <= 0: leave as is); the baseline
+ * timings use it to time one thread. */
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
