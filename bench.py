@@ -204,6 +204,37 @@ def wl_moe_dswiglu(b_major="k"):
     return step, info
 
 
+def wl_moe_dswiglu_fp4():
+    import torch
+    import block_scaled_gemm_02_amd as bsg
+    import workloads as W
+    # the MXFP8 dSwiGLU workload's routing and shapes with MXFP4 (E2M1) A and B: bf16 D and the
+    # per-expert amax (L, 2) of its two halves; no D_col copy
+    p = W.grouped_dswiglu_problem(28672, 32, 2048, 7168, "e2m1", seed=0, device="cuda")
+    s, t = p.sizes, p.t
+    m, n, k, L = s["m"], s["n"], s["k"], s["l"]
+    d = torch.empty(m, 2 * n, dtype=torch.bfloat16, device="cuda")
+    dprob = torch.zeros(m, device="cuda")
+    amax = torch.empty(L, 2, device="cuda")
+
+    def step():
+        dprob.zero_()
+        bsg.grouped_gemm_dswiglu(t["a"], t["b"], t["sfa"], t["sfb"], t["c"], t["offsets"], t["alpha"], t["beta"],
+                                 t["prob"], None, d, None, None, None, dprob, m, n, k, L, "e2m1",
+                                 d_dtype=torch.bfloat16, amax=amax)
+
+    valid_m = s["valid_m"]
+    alg = valid_m * k // 2 + L * n * k // 2 + t["sfa"].numel() + t["sfb"].numel() + valid_m * 2 * n * 2 \
+        + valid_m * 2 * n * 2 + 8 * L + 4 * valid_m
+    info = dict(name="moe_mxfp4_dswiglu", fmt="e2m1",
+                flops=2.0 * valid_m * n * k, alg_bytes=alg, kernel="k_grouped",
+                config={"workload": "grouped MXFP4 GEMM + dSwiGLU backward, bf16 D, per-expert amax and dprob",
+                        "experts": L, "n": n, "k": k, "valid_m": valid_m, "routed_rows": 28672,
+                        "routing": "multinomial Zipf(1.1), padded to 256", "c": "bf16 (valid_m, 2N)"},
+                cpu=None)
+    return step, info
+
+
 def wl_dense_8192(fmt, majors="kkn"):
     """majors: A ('k' or 'm'), B ('k' or 'n') and C ('n' or 'm') storage."""
     import torch
@@ -324,6 +355,7 @@ WORKLOADS = {
     "moe_mxfp4_srelu": lambda: wl_moe_mxfp8_srelu(False, fmt="e2m1"),
     "moe_mxfp8_dswiglu": wl_moe_dswiglu,
     "moe_mxfp8_dswiglu_bn": lambda: wl_moe_dswiglu("n"),
+    "moe_mxfp4_dswiglu": wl_moe_dswiglu_fp4,
     "dense_8192_e4m3": lambda: wl_dense_8192("e4m3"),
     "dense_8192_e4m3_mnn": lambda: wl_dense_8192("e4m3", "mnn"),
     "dense_8192_e4m3_kkm": lambda: wl_dense_8192("e4m3", "kkm"),

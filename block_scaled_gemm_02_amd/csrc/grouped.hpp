@@ -120,6 +120,10 @@ __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, f32x16 
                 cv = gval;
                 dv = srelu_value<CLAMP>(gval, prf[i], p.tq);
                 lmax = fmaxf(lmax, fabsf(dv));
+                // (runtime-typed kernels: keep the running max here; left
+                // free, the compiler moved the max chain into the amax branch
+                // below, kept every D value live until then and spilled)
+                if constexpr (OT < 0) asm volatile("" : "+v"(lmax));
             }
         };
         char *dd2 = kBf16 ? nullptr : static_cast<char *>(p.d_col);
@@ -155,6 +159,7 @@ __device__ __forceinline__ void epilogue_grouped(const GroupedParams &p, f32x16 
         } else {
             const float d = srelu_value<CLAMP>(gval, prf[i], p.tq);
             lmax = fmaxf(lmax, fabsf(d));
+            asm volatile("" : "+v"(lmax));
             return d;
         }
     });
@@ -448,6 +453,11 @@ __device__ __forceinline__ void epilogue_dswiglu(const GroupedParams &p, f32x16 
         });
         dpr += xor32(dpr);
         if (gh == 0 && cols > 0) atomicAdd(p.dprob + row, dpr);
+        // Materialise both maxima per row block: otherwise the compiler sinks
+        // their max chains into the amax branch at the end, keeping all 512
+        // ab/dswiglu values of the lane live across the epilogue (~1 KB of
+        // scratch per lane).
+        asm volatile("" : "+v"(mab), "+v"(mds));
         const uint32_t rb = (uint32_t)(n2 * ES);
         stage_flush<ES, 8>(stage, static_cast<char *>(p.d) + ((qr + 32 * i) * n2 + dq) * ES, rb, 32, dcols * ES, lane);
         if (p.d_col)

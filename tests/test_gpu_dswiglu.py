@@ -228,3 +228,53 @@ def test_grouped_dswiglu_n_major_b_full_size():
         assert torch.equal(x, y), name
     # dprob: the same per-row terms, added in a varying order
     assert torch.allclose(got[4], ref[4], rtol=1e-5, atol=1e-6 * float(ref[4].abs().max()))
+
+
+def test_grouped_dswiglu_fp4_full_size_sampled():
+    """The MXFP4 bench configuration (28672 tokens over 32 experts, N = 2048,
+    K = 7168, bf16 D with its D_col copy and the per-expert amax (L, 2)): the
+    first whole 256-row tile of three experts against the oracle computed for
+    those rows alone; over the whole output, D_col equals D and each amax
+    rounded to bf16 equals the largest |D| of its expert and half (RNE is
+    monotonic, so the bf16 maximum is the rounded fp32 maximum)."""
+    say("grouped_dswiglu FP4 inputs, full size")
+    p = W.grouped_dswiglu_problem(28672, 32, 2048, 7168, "e2m1", seed=0, device="cuda")
+    s, t = p.sizes, p.t
+    m, n, k, L = s["m"], s["n"], s["k"], s["l"]
+    d = torch.full((m, 2 * n), float("nan"), dtype=torch.bfloat16, device="cuda")
+    d_col = torch.full((m, 2 * n), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dprob = torch.zeros(m, device="cuda")
+    amax = torch.full((L, 2), -1.0, device="cuda")
+    bsg.grouped_gemm_dswiglu(t["a"], t["b"], t["sfa"], t["sfb"], t["c"], t["offsets"], t["alpha"], t["beta"],
+                             t["prob"], None, d, d_col, None, None, dprob, m, n, k, L, "e2m1",
+                             d_dtype=torch.bfloat16, amax=amax)
+    torch.cuda.synchronize()
+    valid = s["valid_m"]
+    assert torch.equal(d_col[:valid], d[:valid])
+    off = t["offsets"].cpu().numpy()
+    begins = np.concatenate([[0], off[:-1]])
+    cols = torch.arange(n, device="cuda") // 32 * 64 + torch.arange(n, device="cuda") % 32
+    for g in range(L):
+        for h, cc in ((0, cols), (1, cols + 32)):
+            if off[g] > begins[g]:
+                want = d[int(begins[g]):int(off[g])][:, cc].float().abs().max()
+                got = amax[g, h].to(torch.bfloat16).float()
+                assert got.item() == want.item(), (g, h, amax[g, h].item(), want.item())
+            else:
+                assert amax[g, h].item() == 0.0, (g, h)
+    m_t, n_t, k_t = ceil_div(m, 128), ceil_div(n, 128), ceil_div(k, 128)
+    nonempty = [g for g in range(L) if off[g] > begins[g]]
+    for g in (nonempty[0], nonempty[len(nonempty) // 2], nonempty[-1]):
+        r0 = int(begins[g])
+        assert float(t["prob"][r0].item()) > 0.0           # a routed row
+        say(f"  oracle expert {g} rows {r0}..{r0 + 255}")
+        sfa = t["sfa"][(r0 // 128) * k_t * 512:(r0 // 128 + 2) * k_t * 512]
+        sfb = t["sfb"][g * n_t * k_t * 512:(g + 1) * n_t * k_t * 512]
+        r = O.grouped_dswiglu(t["a"][r0:r0 + 256].cpu(), t["b"][g:g + 1].cpu(), sfa.cpu(), sfb.cpu(),
+                              np.array([256], np.int32), t["alpha"][g:g + 1].cpu(), t["beta"][g:g + 1].cpu(),
+                              t["prob"][r0:r0 + 256].cpu(), O.bits16(t["c"][r0:r0 + 256].cpu()), 256, n, k, 1,
+                              "e2m1")
+        bd, b_dp = bounds(p, r, r0, r0 + 256)
+        say(f"  D: {check_float(d[r0:r0 + 256].cpu(), r['d'], bd, what=f'D e{g}')}")
+        gdp = dprob[r0:r0 + 256].cpu().double().numpy()
+        assert np.all(np.abs(gdp - r["dprob"]) <= b_dp)
