@@ -118,31 +118,44 @@ __device__ __forceinline__ uint32_t pack2_f16(float a, float b)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
 }
 
-// Two floats -> two E4M3 codes (round to nearest even).  The hardware
-// conversion returns NaN beyond the format's range instead of saturating,
-// so inputs are clamped to +-448 first.
-__device__ __forceinline__ uint32_t pack2_e4m3(float a, float b)
+// Four codes from two packed conversions: the second writes the high half
+// of the first one's result (word_sel), so no masking or shifting is needed.
+template <bool E5>
+__device__ __forceinline__ uint32_t cvt4_fp8(float x0, float x1, float x2, float x3)
 {
-    a = fminf(fmaxf(a, -448.0f), 448.0f);
-    b = fminf(fmaxf(b, -448.0f), 448.0f);
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+    if constexpr (E5) {
+        const int lo = __builtin_amdgcn_cvt_pk_bf8_f32(x0, x1, 0, false);
+        return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(x2, x3, lo, true);
+    } else {
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+        return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, lo, true);
+    }
 }
 
-// Two floats -> two E5M2 codes (round to nearest even), clamped to the
-// largest finite value +-57344 first so that nothing becomes Inf.
-__device__ __forceinline__ uint32_t pack2_e5m2(float a, float b)
-{
-    a = fminf(fmaxf(a, -57344.0f), 57344.0f);
-    b = fminf(fmaxf(b, -57344.0f), 57344.0f);
-    return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false) & 0xFFFFu;
-}
-
-// Four E4M3 (E5 = false) or E5M2 (E5 = true) codes, x0 in the lowest byte.
+// Four E4M3 (E5 = false) or E5M2 (E5 = true) codes, x0 in the lowest byte,
+// round to nearest even.  The conversion gives NaN from the midpoint past the
+// largest finite value up instead of saturating, so the inputs are clamped to
+// +-448 (E4M3) or +-57344 (E5M2) first.  (The two halves are converted
+// separately and merged: the chained form of cvt4_fp8 made the register
+// allocator spill in the FP8-D sReLU kernels, whose runtime-typed C store
+// uses this cast.)
 template <bool E5 = false>
 __device__ __forceinline__ uint32_t pack4_fp8(float x0, float x1, float x2, float x3)
 {
-    if constexpr (E5) return pack2_e5m2(x0, x1) | (pack2_e5m2(x2, x3) << 16);
-    else return pack2_e4m3(x0, x1) | (pack2_e4m3(x2, x3) << 16);
+    constexpr float M = E5 ? 57344.0f : 448.0f;
+    x0 = fminf(fmaxf(x0, -M), M);
+    x1 = fminf(fmaxf(x1, -M), M);
+    x2 = fminf(fmaxf(x2, -M), M);
+    x3 = fminf(fmaxf(x3, -M), M);
+    uint32_t lo, hi;
+    if constexpr (E5) {
+        lo = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(x0, x1, 0, false) & 0xFFFFu;
+        hi = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(x2, x3, 0, false) & 0xFFFFu;
+    } else {
+        lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false) & 0xFFFFu;
+        hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, 0, false) & 0xFFFFu;
+    }
+    return lo | (hi << 16);
 }
 __device__ __forceinline__ uint32_t pack4_e4m3(float x0, float x1, float x2, float x3)
 {
@@ -158,15 +171,7 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float x0, float x1, float x2, flo
 template <bool E5 = false>
 __device__ __forceinline__ uint32_t pack4_fp8_mx(float x0, float x1, float x2, float x3)
 {
-    uint32_t lo, hi;
-    if constexpr (E5) {
-        lo = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(x0, x1, 0, false) & 0xFFFFu;
-        hi = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(x2, x3, 0, false) & 0xFFFFu;
-    } else {
-        lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false) & 0xFFFFu;
-        hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, 0, false) & 0xFFFFu;
-    }
-    return lo | (hi << 16);
+    return cvt4_fp8<E5>(x0, x1, x2, x3);
 }
 
 // Four values sharing one E8M0 scale -> four E4M3 codes of x / sf, with the
@@ -1141,8 +1146,22 @@ __device__ __forceinline__ void store_quadrant2(uint8_t *reg, char *dst_c, char 
     });
 }
 
-// Value of x in lane l ^ 32.
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+// max(x, x of lane l ^ 32) and x + (x of lane l ^ 32), identical in both
+// lanes of the pair.  v_permlane32_swap of x with itself leaves x of the low
+// half-wave in the first result and x of the high half-wave in the second,
+// in every lane, with no LDS round trip (a shuffle goes through
+// ds_bpermute); the sum is the same expression in both lanes, since
+// addition is commutative.
+__device__ __forceinline__ float max_xor32(float x)
+{
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float add_xor32(float x)
+{
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
 
 // The MX output quantiser's scale step for a block with max |D| = amax:
 // SF = smallest power of two >= norm_const * amax / fmax (E8M0 byte), with

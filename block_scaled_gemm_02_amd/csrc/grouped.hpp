@@ -211,6 +211,12 @@ __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x1
     uint8_t *wd = sd + c32 * G::RBP + (4 / PB) * gh, *wdc = sdc + c32 * G::RBP + (4 / PB) * gh;
     float *const xch = reinterpret_cast<float *>(stage + 2 * 32 * G::RBP);   // column-scale exchange
     const int64_t mt = qr / 128;
+    // SFD_col: even lanes write the byte of register r = col_reg_of_lane(lane),
+    // column qc + 32j + cl with cl = 8(r/4) + 4g + r%4 < 32; qc is a multiple
+    // of 128, so its atom offset is ((qc/128 * col_kt + mt) * 32 + cl) * 16
+    // + 4j, plus the row block i
+    const int rl = col_reg_of_lane(lane), cl = 8 * (rl >> 2) + 4 * gh + (rl & 3);
+    uint8_t *const sfc = p.sfd_col + (((qc / 128) * col_kt + mt) * 32 + cl) * 16;
     static_for<4>([&](auto ii) {
         constexpr int i = decltype(ii)::value;
         __builtin_amdgcn_sched_barrier(0);
@@ -225,7 +231,7 @@ __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x1
             float rm = 0.0f;
 #pragma unroll
             for (int v = 0; v < 16; ++v) rm = fmaxf(rm, fabsf(d[v]));
-            rm = fmaxf(rm, xor32(rm));
+            rm = max_xor32(rm);
             float rinv;
             rword |= mx_scale_byte<DF>(rm, nc, rinv) << (8 * j);
             // column blocks: 32 rows of each column over the half-wave
@@ -247,14 +253,8 @@ __device__ __forceinline__ void epilogue_srelu_fp8(const GroupedParams &p, f32x1
                         d[4 * q + 3] * cinv[4 * q + 3]);
                 }
             }
-            // SFD_col byte i of the column of register r = col_reg_of_lane(lane):
-            // 32j + 8(r/4) + 4g + r%4 (even lanes; lane ^ 1 holds the same byte)
-            const int r = col_reg_of_lane(lane);
-            const int64_t col = qc + 32 * j + 8 * (r >> 2) + 4 * gh + (r & 3);
-            if ((lane & 1) == 0 && col < n) {
-                const int64_t off = (((col / 128) * col_kt + mt) * 32 + (col % 32)) * 16 + ((col % 128) / 32) * 4;
-                p.sfd_col[off + i] = (uint8_t)byte;
-            }
+            // (lane ^ 1 holds the same byte)
+            if ((lane & 1) == 0 && 32 * j + cl < cols) sfc[4 * j + i] = (uint8_t)byte;
         });
         const uint32_t rb = (uint32_t)(n / PB);
         stage_flush<1, 4 / PB>(sd, static_cast<char *>(p.d) + ((qr + 32 * i) * n + qc) / PB, rb, 32, cols / PB, lane);
@@ -307,6 +307,13 @@ __device__ __forceinline__ void epilogue_dswiglu_fp8(const GroupedParams &p, f32
     uint8_t *wd = sd + c32 * G::RBP + 4 * gh, *wdc = sdc + c32 * G::RBP + 4 * gh;
     float *const xch = reinterpret_cast<float *>(stage + 2 * 32 * G::RBP);   // column-scale exchange
     const int64_t mt = qr / 128;
+    // SFD_col: even lanes write the byte of register r = col_reg_of_lane(lane),
+    // D column dq + 32 blk + cl with cl = 8(r/4) + 4g + r%4 < 32; dq is a
+    // multiple of 256, so its atom offset is ((dq/128 + blk/4) * col_kt + mt)
+    // * 512 + 16 cl + 4 (blk%4), plus the row block i
+    const int rl = col_reg_of_lane(lane), cl = 8 * (rl >> 2) + 4 * gh + (rl & 3);
+    uint8_t *const sfc = p.sfd_col + (((dq / 128) * col_kt + mt) * 32 + cl) * 16;
+    const int64_t sfc_k4 = col_kt * 512;            // the next 128 D columns' atoms
     static_for<4>([&](auto ii) {
         constexpr int i = decltype(ii)::value;
         __builtin_amdgcn_sched_barrier(0);
@@ -329,7 +336,7 @@ __device__ __forceinline__ void epilogue_dswiglu_fp8(const GroupedParams &p, f32
             float rm = 0.0f;
 #pragma unroll
             for (int v = 0; v < 16; ++v) rm = fmaxf(rm, fabsf(dv[v]));
-            rm = fmaxf(rm, xor32(rm));
+            rm = max_xor32(rm);
             float rinv;
             rword[blk >> 2] |= mx_scale_byte<E5 ? DT_E5M2 : DT_E4M3>(rm, nc, rinv) << (8 * (blk & 3));
             // column direction: 32 rows of one D column over the half-wave
@@ -343,14 +350,7 @@ __device__ __forceinline__ void epilogue_dswiglu_fp8(const GroupedParams &p, f32
                     pack4_fp8_mx<E5>(dv[4 * q] * cinv[4 * q], dv[4 * q + 1] * cinv[4 * q + 1],
                                dv[4 * q + 2] * cinv[4 * q + 2], dv[4 * q + 3] * cinv[4 * q + 3]);
             }
-            // SFD_col byte i of the D column of register r = col_reg_of_lane(lane):
-            // dq + 32 blk + 8(r/4) + 4g + r%4 (even lanes)
-            const int r = col_reg_of_lane(lane);
-            const int64_t col = dq + 32 * blk + 8 * (r >> 2) + 4 * gh + (r & 3);
-            if ((lane & 1) == 0 && 32 * blk < dcols) {
-                const int64_t off = (((col / 128) * col_kt + mt) * 32 + (col % 32)) * 16 + ((col % 128) / 32) * 4;
-                p.sfd_col[off + i] = (uint8_t)byte;
-            }
+            if ((lane & 1) == 0 && 32 * blk < dcols) sfc[(blk >> 2) * sfc_k4 + 4 * (blk & 3) + i] = (uint8_t)byte;
         };
         static_for<4>([&](auto jj) {
             constexpr int j = decltype(jj)::value;
@@ -371,7 +371,7 @@ __device__ __forceinline__ void epilogue_dswiglu_fp8(const GroupedParams &p, f32
             quant_block(ds, 2 * j + 1);
         });
         // dprob: this lane's 64 columns plus the other half-wave's 64 of the same row
-        dpr += xor32(dpr);
+        dpr = add_xor32(dpr);
         if (gh == 0 && cols > 0) atomicAdd(p.dprob + row, dpr);
         const uint32_t rb = (uint32_t)n2;
         stage_flush<1, 8>(sd, static_cast<char *>(p.d) + (qr + 32 * i) * n2 + dq, rb, 32, dcols, lane);
@@ -451,7 +451,7 @@ __device__ __forceinline__ void epilogue_dswiglu(const GroupedParams &p, f32x16 
                     pack_quad<OT>(ds[0], ds[1], ds[2], ds[3]);
             }
         });
-        dpr += xor32(dpr);
+        dpr = add_xor32(dpr);
         if (gh == 0 && cols > 0) atomicAdd(p.dprob + row, dpr);
         // Materialise both maxima per row block: otherwise the compiler sinks
         // their max chains into the amax branch at the end, keeping all 512

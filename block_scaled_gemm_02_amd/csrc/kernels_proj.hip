@@ -200,12 +200,19 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
     float *const xch = reinterpret_cast<float *>(stage + 2 * 32 * G::RBP);   // column-scale exchange
     uint8_t *wr = sr + c32 * G::RBP + 4 * gh, *wc = sc + c32 * G::RBP + 4 * gh;
     const int64_t col0 = h * HD + 96 * wn;              // the wave's first feature column
+    // scale bytes: out_scales_row (tokens, heads, 6) and out_scales_col
+    // (tokens/32, n_out); even lanes write the column scale of register
+    // r = col_reg_of_lane(lane), column col0 + 32j + 8(r/4) + 4g + r%4
+    const int rl = col_reg_of_lane(lane);
+    uint8_t *const scol_lane = p.s_col + col0 + 8 * (rl >> 2) + 4 * gh + (rl & 3);
     static_for<4>([&](auto ii) {
         constexpr int i = decltype(ii)::value;
         __builtin_amdgcn_sched_barrier(0);
         const int64_t rbase = m0 + 128 * wm + 32 * i;   // first token of this 32-token block
         const bool blk_ok = rbase < p.tokens;            // tokens % 128 == 0: blocks are whole
         const int64_t row = m0 + acc_row(wm, i, lane);
+        uint8_t *const srow_i = p.s_row + (row * p.heads + h) * NBLK + 3 * wn;
+        uint8_t *const scol_i = scol_lane + (rbase / 32) * n_out;
         float rot[2][16];                                // blocks 1 and 2 after RoPE (wave column 1)
         if (wn == 1) {
             rope_block(ii, rot);
@@ -218,7 +225,6 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
         }
         static_for<3>([&](auto jj) {
             constexpr int j = decltype(jj)::value;
-            const int blk = 3 * wn + j;                  // 32-feature block within the head
             float a[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v) a[v] = j == 0 ? acc[i][0][v] : rot[j - 1][v];
@@ -226,7 +232,7 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
             float rm = 0.0f;
 #pragma unroll
             for (int v = 0; v < 16; ++v) rm = fmaxf(rm, fabsf(a[v]));
-            rm = fmaxf(rm, xor32(rm));
+            rm = max_xor32(rm);
             float rinv;
             const uint32_t rb = mx_scale_byte(rm, 1.0f, rinv);
             const float rsf = sf_of_byte(rb);              // norm_const 1: codes are a / SF
@@ -242,13 +248,8 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
                                  a[4 * q + 2] * cinv[4 * q + 2], a[4 * q + 3] * cinv[4 * q + 3]);
             }
             if (blk_ok) {
-                if (gh == 0) p.s_row[(row * p.heads + h) * NBLK + blk] = (uint8_t)rb;
-                // even lanes write the scale of register r = col_reg_of_lane(lane)
-                const int r = col_reg_of_lane(lane);
-                if ((lane & 1) == 0) {
-                    const int64_t col = h * HD + 32 * blk + 8 * (r >> 2) + 4 * gh + (r & 3);
-                    p.s_col[(rbase / 32) * n_out + col] = (uint8_t)byte;
-                }
+                if (gh == 0) srow_i[j] = (uint8_t)rb;
+                if ((lane & 1) == 0) scol_i[32 * j] = (uint8_t)byte;
             }
         });
         const int rows = blk_ok ? 32 : 0;
