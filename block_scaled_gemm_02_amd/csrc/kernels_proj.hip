@@ -114,6 +114,29 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
             B.sf_bytes = (uint32_t)(HD * srow);
         }
     }
+    // Cos/sin rows for the rotation (wave column 1 only, which holds the
+    // rotary features): those of the first two 32-token blocks are loaded
+    // before the K loop, so they have landed by the epilogue (loads complete
+    // in issue order, so the K loop's counted waits stay correct); block
+    // i + 2's once block i's rotation has used its registers.  Two blocks'
+    // values (64 registers) are live at a time.
+    uint2 tab[2][4][4];                                    // [block % 2][q][cos lo, sin lo, cos hi, sin hi]
+    auto load_tab = [&](int i, uint2 (&t)[4][4]) {
+        const int64_t row = m0 + acc_row(wm, i, lane);
+        const int64_t tr = row < p.tokens ? row : 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int q8 = 8 * q + 4 * gh;
+            t[q][0] = *reinterpret_cast<const uint2 *>(p.cos + tr * ROPE + q8);
+            t[q][1] = *reinterpret_cast<const uint2 *>(p.sin + tr * ROPE + q8);
+            t[q][2] = *reinterpret_cast<const uint2 *>(p.cos + tr * ROPE + HALF + q8);
+            t[q][3] = *reinterpret_cast<const uint2 *>(p.sin + tr * ROPE + HALF + q8);
+        }
+    };
+    if (wn == 1) {
+        load_tab(0, tab[0]);
+        load_tab(1, tab[1]);
+    }
     f32x16 acc[4][3];
     mainloop_pipe<F, 3>(acc, ring, A, B, p.q_lora);
     // Block (i, j) lane (c, g) register 4q+u: token 32i + c of the wave's rows,
@@ -125,26 +148,6 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
     // pairs inputs 2*q8 and 2*q8 + 1: block 1 + q/2, register group
     // 2(q%2) + g, half u/2, elements 2(u%2) and 2(u%2) + 1.  Each lane gets the
     // other half-wave's registers it needs with v_permlane32_swap (below).
-    // The cos/sin values of the wave's 128 tokens are loaded first (wave
-    // column 1 only), so the four 32-token blocks wait for one round trip
-    // instead of four; RoPE then runs block by block inside the quantisation
-    // loop below, on copies of the accumulators, so its results stay in VGPRs.
-    uint2 tab[4][4][4];                                    // [block][q][cos lo, sin lo, cos hi, sin hi]
-    if (wn == 1) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t row = m0 + acc_row(wm, i, lane);
-            const int64_t tr = row < p.tokens ? row : 0;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int q8 = 8 * q + 4 * gh;
-                tab[i][q][0] = *reinterpret_cast<const uint2 *>(p.cos + tr * ROPE + q8);
-                tab[i][q][1] = *reinterpret_cast<const uint2 *>(p.sin + tr * ROPE + q8);
-                tab[i][q][2] = *reinterpret_cast<const uint2 *>(p.cos + tr * ROPE + HALF + q8);
-                tab[i][q][3] = *reinterpret_cast<const uint2 *>(p.sin + tr * ROPE + HALF + q8);
-            }
-        }
-    }
     // RoPE of token block i: out[0] / out[1] are blocks 1 and 2 of the head
     // after the rotation.
     auto rope_block = [&](auto ii, float (&out)[2][16]) {
@@ -152,7 +155,7 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
         float cs0[16], sn0[16], cs1[16], sn1[16];          // cos/sin at q8 and 32 + q8
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const uint2 c0 = tab[i][q][0], s0 = tab[i][q][1], c1 = tab[i][q][2], s1 = tab[i][q][3];
+            const uint2 c0 = tab[i % 2][q][0], s0 = tab[i % 2][q][1], c1 = tab[i % 2][q][2], s1 = tab[i % 2][q][3];
             cs0[4 * q] = bf16_lo(c0.x); cs0[4 * q + 1] = bf16_hi(c0.x); cs0[4 * q + 2] = bf16_lo(c0.y); cs0[4 * q + 3] = bf16_hi(c0.y);
             sn0[4 * q] = bf16_lo(s0.x); sn0[4 * q + 1] = bf16_hi(s0.x); sn0[4 * q + 2] = bf16_lo(s0.y); sn0[4 * q + 3] = bf16_hi(s0.y);
             cs1[4 * q] = bf16_lo(c1.x); cs1[4 * q + 1] = bf16_hi(c1.x); cs1[4 * q + 2] = bf16_lo(c1.y); cs1[4 * q + 3] = bf16_hi(c1.y);
@@ -216,6 +219,7 @@ __global__ void __launch_bounds__(256) k_proj_rope(ProjParams p)
         float rot[2][16];                                // blocks 1 and 2 after RoPE (wave column 1)
         if (wn == 1) {
             rope_block(ii, rot);
+            if constexpr (i + 2 < 4) load_tab(i + 2, tab[i % 2]);
         } else {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
