@@ -120,14 +120,17 @@ __device__ __forceinline__ uint32_t pack2_f16(float a, float b)
 
 // Four codes from two packed conversions: the second writes the high half
 // of the first one's result (word_sel), so no masking or shifting is needed.
+// The first one's own high half (taken from its "old" operand) is
+// overwritten, so x0's bits serve as that operand rather than a zero that
+// would cost a register move.
 template <bool E5>
 __device__ __forceinline__ uint32_t cvt4_fp8(float x0, float x1, float x2, float x3)
 {
     if constexpr (E5) {
-        const int lo = __builtin_amdgcn_cvt_pk_bf8_f32(x0, x1, 0, false);
+        const int lo = __builtin_amdgcn_cvt_pk_bf8_f32(x0, x1, __float_as_int(x0), false);
         return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(x2, x3, lo, true);
     } else {
-        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, __float_as_int(x0), false);
         return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, lo, true);
     }
 }
@@ -183,7 +186,8 @@ __device__ __forceinline__ uint32_t pack4_fp8_mx(float x0, float x1, float x2, f
 typedef short s16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack4_e4m3_sf(float x0, float x1, float x2, float x3, float sf)
 {
-    const s16x2_t z = {0, 0};
+    // (the first conversion's high half is overwritten by the second, as in cvt4_fp8)
+    const s16x2_t z = __builtin_bit_cast(s16x2_t, x0);
     const s16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, x0, x1, sf, false);
     const s16x2_t w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, x2, x3, sf, true);
     return __builtin_bit_cast(uint32_t, w);
@@ -1067,16 +1071,17 @@ __device__ __forceinline__ void store_quadrant(uint8_t *reg, char *dst, char *ds
 
 // Four E2M1 codes, x0 in the lowest nibble: round to nearest even,
 // saturating at +-6, sign in bit 3 of each nibble.  gfx950's packed FP4
-// conversion with a unit scale does exactly this (the low byte takes the
-// first value in its low nibble; the rest of the word is left at the
-// given old value, zero here); its results equal a nearest-even,
+// conversion with a unit scale does exactly this (the byte its selector
+// names takes the first value in its low nibble; the rest of the word is
+// left at the given old value); its results equal a nearest-even,
 // saturating E2M1 encode at every midpoint between codes, at the fp32
 // neighbours of each midpoint, past 6 up to 1e30, and at signed zeros.
+// The second conversion writes byte 1 of the first one's result; the two
+// high bytes (x0's bits, standing in for an old value) are masked off.
 __device__ __forceinline__ uint32_t pack4_e2m1(float x0, float x1, float x2, float x3)
 {
-    const uint32_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x0, x1, 1.0f, 0);
-    const uint32_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x2, x3, 1.0f, 0);
-    return (lo & 0xFFu) | ((hi & 0xFFu) << 8);
+    const uint32_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(__float_as_uint(x0), x0, x1, 1.0f, 0);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x2, x3, 1.0f, 1) & 0xFFFFu;
 }
 
 // store_quadrant for packed E2M1 output: two codes per byte, the even
