@@ -1025,10 +1025,14 @@ __device__ __forceinline__ void stage_flush(const uint8_t *reg, char *dst, uint3
     const uint32_t nrec = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(rows < 32 ? rows : 32) * row_bytes));
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(udst, (short)0, (int)nrec, 0x00020000);
     const uint32_t voff = (cb < col_bytes && lr < G::RPI) ? (uint32_t)lr * row_bytes + (uint32_t)cb : kOOB;
+    // Outputs are written once and not read back by the kernel: non-temporal
+    // stores (nt, cache-policy bit 2) leave the L2 to the operand panels
+    // (grouped MXFP8 + sReLU 2.7% faster, dense MXFP8 0.8%).
+    constexpr int kStoreNT = 2;
 #pragma unroll
     for (int k = 0; k < G::NK; ++k) {
         const i32x4 v = *reinterpret_cast<const i32x4 *>(src + k * G::RPI * G::RBP);
-        __builtin_amdgcn_raw_buffer_store_b128(v, rs, voff + (uint32_t)(k * G::RPI) * row_bytes, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, voff + (uint32_t)(k * G::RPI) * row_bytes, 0, kStoreNT);
     }
 }
 
