@@ -235,12 +235,15 @@ __device__ __forceinline__ i32x4 sanitize_scales(i32x4 w, int kt, int kblocks)
 // goes to XCD b % 8, and (one 147 KB-LDS workgroup per CU) each XCD runs 32
 // tiles at a time.  Launch index b is mapped to a tile sequence number s so
 // that every XCD works through runs of 32 consecutive s, and s walks the
-// tiles in groups of 8 m-tiles, column by column: an XCD's 32 concurrent
-// tiles are then 8 m-tiles x 4 n-tiles and share 8 A panels and 4 B panels
+// tiles in groups of 4 m-tiles, column by column: an XCD's 32 concurrent
+// tiles are then 4 m-tiles x 8 n-tiles and share 4 A panels and 8 B panels
 // in its L2 (a row-major order gave each XCD 16 m-tiles x 2 n-tiles, with
-// every A panel fetched by all 8 XCDs).  The last partial round keeps b.
+// every A panel fetched by all 8 XCDs).  Groups of 4 beat groups of 8 by
+// 0.5-1% on the grouped kernels once the outputs stopped filling the L2
+// (non-temporal stores); 2 and 16 were slower.  The last partial round
+// keeps b.
 #ifndef BSG_GROUP_M
-#define BSG_GROUP_M 8
+#define BSG_GROUP_M 4
 #endif
 constexpr int kXcds = 8, kCusPerXcd = 32, kGroupM = BSG_GROUP_M;
 
