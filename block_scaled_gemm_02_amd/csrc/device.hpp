@@ -1030,8 +1030,11 @@ __device__ __forceinline__ void stage_flush(const uint8_t *reg, char *dst, uint3
     const uint32_t voff = (cb < col_bytes && lr < G::RPI) ? (uint32_t)lr * row_bytes + (uint32_t)cb : kOOB;
     // Outputs are written once and not read back by the kernel: non-temporal
     // stores (nt, cache-policy bit 2) leave the L2 to the operand panels
-    // (grouped MXFP8 + sReLU 2.7% faster, dense MXFP8 0.8%).
-    constexpr int kStoreNT = 2;
+    // (grouped MXFP8 + sReLU 2.7% faster, dense MXFP8 0.8%).  Only for row
+    // segments of whole 128-byte lines: where two waves each write part of a
+    // line (96-byte projection rows, 64-byte packed FP4 rows) streaming
+    // stores reached HBM as partial lines, 25% more write traffic.
+    constexpr int kStoreNT = G::RB % 128 == 0 ? 2 : 0;
 #pragma unroll
     for (int k = 0; k < G::NK; ++k) {
         const i32x4 v = *reinterpret_cast<const i32x4 *>(src + k * G::RPI * G::RBP);
