@@ -11,8 +11,11 @@
 // blocks and applies the interleaved-in / halves-out rotation in registers
 // (pair (2j, 2j+1) -> outputs j and 32+j), then every wave quantises its
 // blocks to E4M3 with E8M0 scales: 32-wide blocks along the head dimension
-// (row) and 32-tall blocks along tokens (column).  All cos/sin loads happen
-// before the first store.
+// (row) and 32-tall blocks along tokens (column).  Each token block's cos/sin
+// rows are loaded at least one token block ahead of its rotation (the first
+// two before the K loop), so the wait before a rotation falls on loads, and
+// on the stores ahead of them in the shared in-order counter, that were
+// issued a block or more earlier.
 #include "device.hpp"
 #include "launch.hpp"
 
