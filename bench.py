@@ -27,7 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
-PEAK = {"e4m3": 5000.0, "e2m1": 10100.0, "bf16": 2500.0}
+PEAK = {"e4m3": 5000.0, "e5m2": 5000.0, "e2m1": 10100.0, "bf16": 2500.0}
 HBM_GBS = 8000.0
 
 
@@ -259,7 +259,8 @@ def wl_dense_8192(fmt, majors="kkn"):
     ab = t["a"].numel() + t["b"].numel() + t["sfa"].numel() + t["sfb"].numel()
     info = dict(name=f"dense_8192_{fmt}" + ("" if majors == "kkn" else "_" + majors), fmt=fmt, flops=flops,
                 alg_bytes=ab + c.numel() * 2, kernel="k_gemm_amax",
-                config={"workload": f"batched dense MX{'FP8' if fmt == 'e4m3' else 'FP4'} GEMM + amax",
+                config={"workload": "batched dense " + {"e4m3": "MXFP8 (E4M3)", "e5m2": "MXFP8 (E5M2)",
+                                                         "e2m1": "MXFP4"}[fmt] + " GEMM + amax",
                         "m": 8192, "n": 8192, "k": 8192, "l": 4, "c": "bf16",
                         "majors": {"a": am, "b": bm, "c": cm}},
                 cpu=None)
@@ -360,6 +361,7 @@ WORKLOADS = {
     "dense_8192_e4m3_mnn": lambda: wl_dense_8192("e4m3", "mnn"),
     "dense_8192_e4m3_kkm": lambda: wl_dense_8192("e4m3", "kkm"),
     "dense_8192_e2m1": lambda: wl_dense_8192("e2m1"),
+    "dense_8192_e5m2": lambda: wl_dense_8192("e5m2"),
     "dense_256": wl_dense_256,
     "moe_bf16": wl_moe_bf16,
 }
@@ -466,8 +468,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"e4m3": "mxfp8-e4m3 (fp32 accumulate)", "e2m1": "mxfp4-e2m1 (fp32 accumulate)",
-                  "bf16": "bf16 (fp32 accumulate)"}[info["fmt"]],
+        "dtype": {"e4m3": "mxfp8-e4m3 (fp32 accumulate)", "e5m2": "mxfp8-e5m2 (fp32 accumulate)",
+                  "e2m1": "mxfp4-e2m1 (fp32 accumulate)", "bf16": "bf16 (fp32 accumulate)"}[info["fmt"]],
         "data": "synthetic",
         "config": info["config"],
         "pct_of_peak": round(100.0 * tflops / peak, 2),
