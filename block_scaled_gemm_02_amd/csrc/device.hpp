@@ -447,11 +447,17 @@ struct RingSlots {
     __shared__ __attribute__((aligned(16))) uint8_t name##_pf[1024];                                 \
     const ::bsg::RingSlots<F> name{name##_0, name##_1, name##_pf}
 
-// After the K loop each wave stages epilogue output in half a pair slot.
+// After the K loop each wave stages epilogue output in half a pair slot
+// (a quarter in the eight-wave layout).
 template <int F>
 __device__ __forceinline__ uint8_t *wave_stage(const RingSlots<F> &ring, int w)
 {
     return (w < 2 ? ring.s0 : ring.s1) + (w & 1) * Ring<F>::kWaveStage;
+}
+template <int F>
+__device__ __forceinline__ uint8_t *wave_stage8(const RingSlots<F> &ring, int w)
+{
+    return (w < 4 ? ring.s0 : ring.s1) + (w & 3) * (Ring<F>::kWaveStage / 2 & ~15);
 }
 
 // Per-pair / per-step instruction counts of one wave.  An E4M3 scale atom
@@ -468,22 +474,23 @@ constexpr int loads_per_pair()
 {
     return a_loads<F>() + b_loads<F, NB>() + (fmt_base(F) == FMT_E4M3_RM ? 2 : Ring<F>::kScaleSets);
 }
-template <int F, int NB>
-constexpr int mfmas_per_step() { return (is_fp8(F) ? 1 : 2) * 4 * NB; }
+// MI: 32-row blocks per wave (4, or 2 in the eight-wave layout below).
+template <int F, int NB, int MI = 4>
+constexpr int mfmas_per_step() { return (is_fp8(F) ? 1 : 2) * MI * NB; }
 // Reads of a stage: one 16-byte read per chunk, or (K-major staging) two
 // 8-byte transposing reads per chunk
-template <int F>
-constexpr int a_reads() { return a_t(F) ? 16 : 8; }
+template <int F, int MI = 4>
+constexpr int a_reads() { return a_t(F) ? 16 : 2 * MI; }
 template <int F, int NB>
 constexpr int b_reads() { return (b_t(F) || F == FMT_BF16_BT) ? 4 * NB : 2 * NB; }
 // scale reads of a stage that has them: one word set per operand, or (B
 // scales staged in LDS) one A read and one word per B block
 template <int F, int NB>
 constexpr int scale_reads() { return b_static_sf<F>() ? 1 + NB : 2; }
-template <int F, int NB>
+template <int F, int NB, int MI = 4>
 constexpr int reads_in_stage(bool odd)
 {
-    return a_reads<F>() + b_reads<F, NB>() + (scales_in_stage<F>(odd) ? scale_reads<F, NB>() : 0);
+    return a_reads<F, MI>() + b_reads<F, NB>() + (scales_in_stage<F>(odd) ? scale_reads<F, NB>() : 0);
 }
 
 // Where this wave's loads of pair p go: code offset (K position, or out of
@@ -590,10 +597,11 @@ struct ReadAddr {
     const uint8_t *sa, *sb;   // this lane's scale words
     uint32_t sb_blk;          // b_static_sf: bytes between the B scale words of blocks j and j + 1
 };
-// pair: K pair of the stage read (used by b_static_sf only)
-template <int F, int NB, int H>
+// pair: K pair of the stage read (used by b_static_sf only); hh: the wave's
+// half of its 128-row group in the eight-wave layout (MI = 2)
+template <int F, int NB, int H, int MI = 4>
 __device__ __forceinline__ ReadAddr read_addr(const uint8_t *st, int wm, int wn, int lane, const PipeDesc<NB> &d,
-                                              int pair)
+                                              int pair, int hh = 0)
 {
     ReadAddr r;
     const uint32_t row = lane & 31, g = lane >> 5;
@@ -608,6 +616,7 @@ __device__ __forceinline__ ReadAddr read_addr(const uint8_t *st, int wm, int wn,
     const uint32_t G = (uint32_t)lane >> 4, s = (uint32_t)lane & 15;
     const uint32_t trow = (64u * H + 16u * (G >> 1) + (s >> 1)) * kTRow + 16u * (G & 1) + 8u * (s & 1);
     if constexpr (a_t(F)) r.a0 = st + trow + 128u * wm;
+    else if constexpr (MI == 2) r.a0 = st + (128u * wm + 64u * hh + row) * kPK;
     else r.a0 = st + (128u * wm + row) * kPK;
     if constexpr (b_t(F)) {
         r.b0 = st + a_region<F>() + trow + 32u * NB * wn;
@@ -623,7 +632,7 @@ __device__ __forceinline__ ReadAddr read_addr(const uint8_t *st, int wm, int wn,
         r.b0 = st + a_region<F>() + (32u * NB * wn + row) * kPK;
     }
     const uint8_t *sc = st + a_region<F>() + b_region<F>() + (fmt_base(F) == FMT_E2M1 ? 4096 * H : 0);
-    r.sa = sc + 1024 * wm + 16 * row;
+    r.sa = sc + 1024 * wm + 16 * row + (MI == 2 ? 8 * hh : 0);   // word q: the lane's row of block q
     r.sb = sc + 1024 * (2 + wn) + 16 * row;
     r.sb_blk = 0;
     if constexpr (b_static_sf<F>()) {
@@ -650,10 +659,10 @@ __device__ __forceinline__ void read_tr8(i32x4 &c, const uint8_t *p)
     }
 }
 
-template <int F, int NB, int R>
+template <int F, int NB, int R, int MI = 4>
 __device__ __forceinline__ void read_one(Frags<NB> &f, const ReadAddr &r)
 {
-    constexpr int RA = a_reads<F>();
+    constexpr int RA = a_reads<F, MI>();
     if constexpr (a_t(F) && R < RA) {
         // chunk h of block i: K [16g + 32h, +16) of the lane's column as two
         // reads of 8 K values each (e = 0, 1)
@@ -682,6 +691,9 @@ __device__ __forceinline__ void read_one(Frags<NB> &f, const ReadAddr &r)
     } else if constexpr (R < RA + 2 * NB) {
         constexpr int j = (R - RA) / 2, h = (R - RA) % 2;
         f.b[j][h] = *reinterpret_cast<const i32x4 *>(r.b0 + 32 * kPK * j + (h ? r.p1 : r.p0));
+    } else if constexpr (R == RA + b_reads<F, NB>() && MI == 2) {
+        const i32x2_t v = *reinterpret_cast<const i32x2_t *>(r.sa);     // the wave's two row blocks
+        f.sa = i32x4{v.x, v.y, 0, 0};
     } else if constexpr (R == RA + b_reads<F, NB>()) {
         f.sa = *reinterpret_cast<const i32x4 *>(r.sa);
     } else if constexpr (b_static_sf<F>()) {
@@ -692,12 +704,12 @@ __device__ __forceinline__ void read_one(Frags<NB> &f, const ReadAddr &r)
     }
 }
 
-template <int F, int NB>
+template <int F, int NB, int MI = 4>
 __device__ __forceinline__ void read_frags0(Frags<NB> &f, const uint8_t *st, int wm, int wn, int lane,
-                                            const PipeDesc<NB> &d)
+                                            const PipeDesc<NB> &d, int hh = 0)
 {
-    const ReadAddr r = read_addr<F, NB, 0>(st, wm, wn, lane, d, 0);
-    static_for<reads_in_stage<F, NB>(false)>([&](auto q) { read_one<F, NB, decltype(q)::value>(f, r); });
+    const ReadAddr r = read_addr<F, NB, 0, MI>(st, wm, wn, lane, d, 0, hh);
+    static_for<reads_in_stage<F, NB, MI>(false)>([&](auto q) { read_one<F, NB, decltype(q)::value, MI>(f, r); });
 }
 
 // Byte of the scale word that an MFMA lane consumes is moved to byte 0
@@ -714,17 +726,17 @@ __device__ __forceinline__ i32x4 prep_scales(i32x4 w, int kt, int kblocks, int g
     return w;
 }
 
-// MFMA number M of a step: block (i, j) = ((M % 4NB) / NB, M % NB), sub-step
-// S = M / 4NB (E2M1, BF16).  The B fragment is the instruction's first
+// MFMA number M of a step: block (i, j) = ((M % MI*NB) / NB, M % NB), sub-step
+// S = M / (MI*NB) (E2M1, BF16).  The B fragment is the instruction's first
 // operand and the A fragment its second, so the instruction computes the
 // transposed block (B A^T): lane (c, g) register v of block (i, j) then holds
 // C[32i + c][32j + 8(v/4) + 4g + v%4] -- one output row per lane with runs of
 // four consecutive columns, the layout the epilogue stores.
-template <int F, int NB, int M>
-__device__ __forceinline__ void mma_one(f32x16 (&acc)[4][NB], const Frags<NB> &f, const i32x4 &sa,
+template <int F, int NB, int M, int MI = 4>
+__device__ __forceinline__ void mma_one(f32x16 (&acc)[MI][NB], const Frags<NB> &f, const i32x4 &sa,
                                         const i32x4 &sb)
 {
-    constexpr int S = M / (4 * NB), i = (M % (4 * NB)) / NB, j = M % NB;
+    constexpr int S = M / (MI * NB), i = (M % (MI * NB)) / NB, j = M % NB;
     if constexpr (is_fp8(F)) {
         const i32x8 av{f.a[i][0].x, f.a[i][0].y, f.a[i][0].z, f.a[i][0].w,
                        f.a[i][1].x, f.a[i][1].y, f.a[i][1].z, f.a[i][1].w};
@@ -750,21 +762,23 @@ __device__ __forceinline__ void mma_one(f32x16 (&acc)[4][NB], const Frags<NB> &f
 #ifndef BSG_READ_SPAN_NUM
 #define BSG_READ_SPAN_NUM 3     // reads over the first 3/4 of the MFMAs
 #endif
-template <int F, int NB>
-constexpr int read_span() { return mfmas_per_step<F, NB>() * BSG_READ_SPAN_NUM / 4; }
+template <int F, int NB, int MI = 4>
+constexpr int read_span() { return mfmas_per_step<F, NB, MI>() * BSG_READ_SPAN_NUM / 4; }
 
 // One K step, ks = 4q + U: see the comment above the pair-slot constants.
-template <int F, int NB, int U>
-__device__ __forceinline__ void pipe_step(f32x16 (&acc)[4][NB], Frags<NB> &cur, Frags<NB> &nxt,
+// LOADER: the wave issues its share of the loads (always, except waves 4-7
+// of the eight-wave layout).
+template <int F, int NB, int U, int MI = 4, bool LOADER = true>
+__device__ __forceinline__ void pipe_step(f32x16 (&acc)[MI][NB], Frags<NB> &cur, Frags<NB> &nxt,
                                           const PipeDesc<NB> &d, const RingSlots<F> &ring, int ks, int w,
-                                          int wm, int wn, int lane)
+                                          int wm, int wn, int lane, int hh = 0)
 {
     constexpr bool ODD = (U & 1) != 0;           // stage ks parity; stage ks+1 has the other
     constexpr int RS = ((U + 1) / 2) % 2;        // pair slot of stage ks+1 ...
     constexpr int RH = (U + 1) % 2;              // ... and its half
     constexpr int LSL = ((U + 3) / 2) % 2;       // slot the odd step refills
-    constexpr int M = mfmas_per_step<F, NB>(), R = reads_in_stage<F, NB>(!ODD);
-    constexpr int V = ODD ? loads_per_pair<F, NB>() : 0;
+    constexpr int M = mfmas_per_step<F, NB, MI>(), R = reads_in_stage<F, NB, MI>(!ODD);
+    constexpr int V = ODD && LOADER ? loads_per_pair<F, NB>() : 0;
     if constexpr (ODD) {
         // this wave's part of the pair holding stage ks+1 has landed (the
         // prefetch issued after it may still be in flight)
@@ -785,7 +799,7 @@ __device__ __forceinline__ void pipe_step(f32x16 (&acc)[4][NB], Frags<NB> &cur, 
     PairAddr la{};
     if constexpr (ODD) la = pair_addr<F, NB>(d, (ks + 3) >> 1);
     uint8_t *const lslot = ring.template at<LSL>();
-    const ReadAddr ra = read_addr<F, NB, RH>(ring.template at<RS>(), wm, wn, lane, d, (ks + 1) >> 1);
+    const ReadAddr ra = read_addr<F, NB, RH, MI>(ring.template at<RS>(), wm, wn, lane, d, (ks + 1) >> 1, hh);
     if constexpr (Ring<F>::kScaled && !scales_in_stage<F>(!ODD)) {
         nxt.sa = cur.sa;
         nxt.sb = cur.sb;
@@ -793,13 +807,13 @@ __device__ __forceinline__ void pipe_step(f32x16 (&acc)[4][NB], Frags<NB> &cur, 
     __builtin_amdgcn_sched_barrier(0);
     // Reads go out over the first MR MFMAs, so that the last of them has
     // landed by the next step's wait; loads over all MFMAs.
-    constexpr int MR = read_span<F, NB>();
+    constexpr int MR = read_span<F, NB, MI>();
     static_for<M>([&](auto mm) {
         constexpr int m = decltype(mm)::value;
-        mma_one<F, NB, m>(acc, cur, sa, sb);
+        mma_one<F, NB, m, MI>(acc, cur, sa, sb);
         if constexpr (m < MR) {
             static_for<(R * (m + 1)) / MR - (R * m) / MR>([&](auto rr) {
-                read_one<F, NB, (R * m) / MR + decltype(rr)::value>(nxt, ra);
+                read_one<F, NB, (R * m) / MR + decltype(rr)::value, MI>(nxt, ra);
             });
         }
         if constexpr (V > 0) {
@@ -809,16 +823,27 @@ __device__ __forceinline__ void pipe_step(f32x16 (&acc)[4][NB], Frags<NB> &cur, 
         }
         // even step: prefetch the A lines of the pair after the one the next
         // (odd) step loads
-        if constexpr (!ODD && m == 0) prefetch_a<F, NB>(d, ring, (ks + 2 * BSG_PF_DIST) >> 1, w);
+        if constexpr (!ODD && m == 0 && LOADER) prefetch_a<F, NB>(d, ring, (ks + 2 * BSG_PF_DIST) >> 1, w);
         __builtin_amdgcn_sched_barrier(0);
     });
 }
 
 // K loop over a 256 x (64*NB) tile, 4 waves as 2 x 2 (wave: 128 x 32*NB).
-template <int F, int NB = 4>
-__device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[4][NB], const RingSlots<F> &ring,
+//
+// MI = 2 is the eight-wave layout (two waves per SIMD, 64 x 32*NB each) for
+// kernels whose epilogue is long against their K loop: waves w and w + 4
+// split the 128-row group of wave w's quadrant between them, and wave w + 4
+// takes the other wave column, so that the two waves on one SIMD (w and
+// w + 4) hold one quadrant half of each column.  Waves 0-3 issue every load
+// exactly as in the four-wave layout (same LDS layout and counts); waves 4-7
+// only read fragments and pass the same barriers.  Wave (wm, wn, hh) holds
+// rows 128 wm + 64 hh .. + 63 and columns 32 NB wn .. of the tile.
+template <int F, int NB = 4, int MI = 4>
+__device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[MI][NB], const RingSlots<F> &ring,
                                               const OperandDesc &A, const OperandDesc &B, int64_t k)
 {
+    static_assert(MI == 4 || (MI == 2 && !a_t(F) && (is_bf16(F) || fmt_base(F) == FMT_E4M3_RM)),
+                  "the eight-wave layout: k-major A, BF16 or row-major-scaled E4M3");
     static_assert(NB == 4 || is_bf16(F) || fmt_base(F) == FMT_E4M3_RM, "atom scales need 128-column wave tiles");
     static_assert(F != FMT_BF16_BT || 64 * NB <= kBtData / 2, "a K-major B row holds the tile's columns");
     static_assert(!(a_t(F) || b_t(F)) || (is_fp8(F) && (NB == 4 || b_static_sf<F>())),
@@ -826,9 +851,12 @@ __device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[4][NB], const RingSl
     static_assert(!a_t(F) || fmt_base(F) != FMT_E4M3_RM, "row-major scales with an m-major A are not built");
     // the wave index is uniform: keep everything derived from it in SGPRs
     const int t = threadIdx.x, lane = t & 63;
-    const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w >> 1, wn = w & 1;
+    const int wall = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int w = MI == 2 ? (wall & 3) : wall;          // load role (waves 0-3)
+    const int hh = MI == 2 ? (wall >> 2) : 0;
+    const int wm = w >> 1, wn = MI == 2 ? ((w & 1) ^ hh) : (w & 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j)
 #pragma unroll
@@ -928,19 +956,30 @@ __device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[4][NB], const RingSl
 
     const int nks = (int)((d.row_bytes + kKS - 1) / kKS);
     Frags<NB> fx, fy;
-    issue_pair<F, NB>(d, ring.template at<0>(), 0, w);
-    issue_pair<F, NB>(d, ring.template at<1>(), 1, w);
+    if (MI == 4 || hh == 0) {
+        issue_pair<F, NB>(d, ring.template at<0>(), 0, w);
+        issue_pair<F, NB>(d, ring.template at<1>(), 1, w);
+    }
     // pair 0 has landed, and with it any direct-to-LDS load the caller issued
     // before this call (loads complete in issue order); pair 1 may be in flight
     s_wait_vm<loads_per_pair<F, NB>()>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    read_frags0<F, NB>(fx, ring.template at<0>(), wm, wn, lane, d);
-    for (int ks = 0; ks < nks; ks += 4) {
-        pipe_step<F, NB, 0>(acc, fx, fy, d, ring, ks, w, wm, wn, lane);
-        if (ks + 1 < nks) pipe_step<F, NB, 1>(acc, fy, fx, d, ring, ks + 1, w, wm, wn, lane);
-        if (ks + 2 < nks) pipe_step<F, NB, 2>(acc, fx, fy, d, ring, ks + 2, w, wm, wn, lane);
-        if (ks + 3 < nks) pipe_step<F, NB, 3>(acc, fy, fx, d, ring, ks + 3, w, wm, wn, lane);
+    read_frags0<F, NB, MI>(fx, ring.template at<0>(), wm, wn, lane, d, hh);
+    auto kloop = [&](auto loader) {
+        constexpr bool L = decltype(loader)::value;
+        for (int ks = 0; ks < nks; ks += 4) {
+            pipe_step<F, NB, 0, MI, L>(acc, fx, fy, d, ring, ks, w, wm, wn, lane, hh);
+            if (ks + 1 < nks) pipe_step<F, NB, 1, MI, L>(acc, fy, fx, d, ring, ks + 1, w, wm, wn, lane, hh);
+            if (ks + 2 < nks) pipe_step<F, NB, 2, MI, L>(acc, fx, fy, d, ring, ks + 2, w, wm, wn, lane, hh);
+            if (ks + 3 < nks) pipe_step<F, NB, 3, MI, L>(acc, fy, fx, d, ring, ks + 3, w, wm, wn, lane, hh);
+        }
+    };
+    if constexpr (MI == 4) {
+        kloop(std::true_type{});
+    } else {
+        if (hh == 0) kloop(std::true_type{});
+        else kloop(std::false_type{});
     }
     s_wait_vm<0>();
     s_wait_lgkm0();
@@ -954,6 +993,11 @@ __device__ __forceinline__ void mainloop_pipe(f32x16 (&acc)[4][NB], const RingSl
 // Tile-relative row and first column of register group q (registers
 // 4q..4q+3) of accumulator block (i, j) in this lane (see mma_one).
 __device__ __forceinline__ int acc_row(int wm, int i, int lane) { return 128 * wm + 32 * i + (lane & 31); }
+// The same in the eight-wave layout (mainloop_pipe with MI = 2).
+__device__ __forceinline__ int acc_row8(int wm, int hh, int i, int lane)
+{
+    return 128 * wm + 64 * hh + 32 * i + (lane & 31);
+}
 template <int NB>
 __device__ __forceinline__ int acc_col(int wn, int j, int q, int lane)
 {
