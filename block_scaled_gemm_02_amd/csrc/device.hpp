@@ -192,6 +192,20 @@ __device__ __forceinline__ uint32_t pack4_e4m3_sf(float x0, float x1, float x2, 
     const s16x2_t w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, x2, x3, sf, true);
     return __builtin_bit_cast(uint32_t, w);
 }
+// The same for E5M2 codes (v_cvt_scalef32_pk_bf8_f32).
+__device__ __forceinline__ uint32_t pack4_e5m2_sf(float x0, float x1, float x2, float x3, float sf)
+{
+    const s16x2_t z = __builtin_bit_cast(s16x2_t, x0);
+    const s16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(z, x0, x1, sf, false);
+    const s16x2_t w = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(lo, x2, x3, sf, true);
+    return __builtin_bit_cast(uint32_t, w);
+}
+template <bool E5>
+__device__ __forceinline__ uint32_t pack4_fp8_sf(float x0, float x1, float x2, float x3, float sf)
+{
+    if constexpr (E5) return pack4_e5m2_sf(x0, x1, x2, x3, sf);
+    else return pack4_e4m3_sf(x0, x1, x2, x3, sf);
+}
 __device__ __forceinline__ float sf_of_byte(uint32_t byte)
 {
     return __uint_as_float(byte ? byte << 23 : 0x00400000u);

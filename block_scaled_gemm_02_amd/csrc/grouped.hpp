@@ -286,6 +286,24 @@ __device__ __forceinline__ float bf16_at(uint2 w, int u)
     const uint32_t x = (u < 2) ? w.x : w.y;
     return __uint_as_float((u & 1) ? (x & 0xFFFF0000u) : (x << 16));
 }
+// One ref element of the dSwiGLU backward, on the raw (unscaled) gate g and
+// input x of the forward tensor: with gt = beta*g and sg = sigmoid(gt),
+// t = g*sg = swish/beta and f = alpha^2 * prob * beta * scale (scale:
+// norm_const for the MX outputs, whose quantiser then divides by the E8M0
+// scale alone; 1 otherwise),
+//   ab = f*a*t,  dswiglu = f*a*x*sg*(1 + gt - beta*t)  (= ... * (1 + gt*(1 - sg))),
+// and t*x, which dprob accumulates times a; the row's dprob is that sum
+// times beta^2 alpha^2.  kx = -log2(e)*beta.
+struct DswigluTerms {
+    float ab, ds, tx;
+};
+__device__ __forceinline__ DswigluTerms dswiglu_terms(float a, float g, float x, float f, float beta, float kx)
+{
+    const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(kx * g));
+    const float t = g * sg;
+    const float fa = f * a;
+    return DswigluTerms{fa * t, fa * x * sg * fmaf(-beta, t, fmaf(beta, g, 1.0f)), t * x};
+}
 template <bool E5>
 __device__ __forceinline__ void epilogue_dswiglu_fp8(const GroupedParams &p, f32x16 (&acc)[4][4], uint8_t *stage,
                                                      int64_t m0, int64_t n0, float alpha2, float beta, int wm,
@@ -314,6 +332,7 @@ __device__ __forceinline__ void epilogue_dswiglu_fp8(const GroupedParams &p, f32
     const int rl = col_reg_of_lane(lane), cl = 8 * (rl >> 2) + 4 * gh + (rl & 3);
     uint8_t *const sfc = p.sfd_col + (((dq / 128) * col_kt + mt) * 32 + cl) * 16;
     const int64_t sfc_k4 = col_kt * 512;            // the next 128 D columns' atoms
+    const float kx = -1.4426950408889634f * beta, cdp = beta * beta * alpha2;
     static_for<4>([&](auto ii) {
         constexpr int i = decltype(ii)::value;
         __builtin_amdgcn_sched_barrier(0);
@@ -331,6 +350,10 @@ __device__ __forceinline__ void epilogue_dswiglu_fp8(const GroupedParams &p, f32
             }
         uint32_t rword[2] = {0u, 0u};                // SFD_row bytes of D blocks 0-3 and 4-7
         float dpr = 0.0f;
+        // dv holds norm_const * D (see dswiglu_terms), so the scale step takes
+        // norm_const 1, and a code is the value over the E8M0 scale: the row
+        // codes by the scaled conversion, the column codes times 1/SF (both
+        // exact power-of-two scalings of norm_const * D)
         auto quant_block = [&](const float (&dv)[16], int blk) {
             // row direction: 32 D columns of one row (this lane and lane ^ 32)
             float rm = 0.0f;
@@ -338,40 +361,39 @@ __device__ __forceinline__ void epilogue_dswiglu_fp8(const GroupedParams &p, f32
             for (int v = 0; v < 16; ++v) rm = fmaxf(rm, fabsf(dv[v]));
             rm = max_xor32(rm);
             float rinv;
-            rword[blk >> 2] |= mx_scale_byte<E5 ? DT_E5M2 : DT_E4M3>(rm, nc, rinv) << (8 * (blk & 3));
+            const uint32_t rb = mx_scale_byte<E5 ? DT_E5M2 : DT_E4M3>(rm, 1.0f, rinv);
+            const float rsf = sf_of_byte(rb);
+            rword[blk >> 2] |= rb << (8 * (blk & 3));
             // column direction: 32 rows of one D column over the half-wave
             float cinv[16];
-            const uint32_t byte = col_scales_xch<E5 ? DT_E5M2 : DT_E4M3>(dv, nc, cinv, lane, xch);
+            const uint32_t byte = col_scales_xch<E5 ? DT_E5M2 : DT_E4M3>(dv, 1.0f, cinv, lane, xch);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 *reinterpret_cast<uint32_t *>(wd + 32 * blk + 8 * q) =
-                    pack4_fp8_mx<E5>(dv[4 * q] * rinv, dv[4 * q + 1] * rinv, dv[4 * q + 2] * rinv, dv[4 * q + 3] * rinv);
+                    pack4_fp8_sf<E5>(dv[4 * q], dv[4 * q + 1], dv[4 * q + 2], dv[4 * q + 3], rsf);
                 *reinterpret_cast<uint32_t *>(wdc + 32 * blk + 8 * q) =
                     pack4_fp8_mx<E5>(dv[4 * q] * cinv[4 * q], dv[4 * q + 1] * cinv[4 * q + 1],
                                dv[4 * q + 2] * cinv[4 * q + 2], dv[4 * q + 3] * cinv[4 * q + 3]);
             }
             if ((lane & 1) == 0 && 32 * blk < dcols) sfc[(blk >> 2) * sfc_k4 + 4 * (blk & 3) + i] = (uint8_t)byte;
         };
+        const float fi = alpha2 * pr[i] * beta * nc;
         static_for<4>([&](auto jj) {
             constexpr int j = decltype(jj)::value;
             float ab[16], ds[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const float ref = alpha2 * acc[i][j][v];
-                const float in = beta * bf16_at(cin[j][v >> 2], v & 3);
-                const float gt = beta * bf16_at(cgt[j][v >> 2], v & 3);
-                const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gt));
-                const float sw = gt * sg;
-                const float rp = ref * pr[i];
-                ab[v] = rp * sw;
-                ds[v] = rp * in * sg * fmaf(gt, 1.0f - sg, 1.0f);
-                dpr = fmaf(sw * in, ref, dpr);
+                const DswigluTerms r = dswiglu_terms(acc[i][j][v], bf16_at(cgt[j][v >> 2], v & 3),
+                                                     bf16_at(cin[j][v >> 2], v & 3), fi, beta, kx);
+                ab[v] = r.ab;
+                ds[v] = r.ds;
+                dpr = fmaf(r.tx, acc[i][j][v], dpr);
             }
             quant_block(ab, 2 * j);
             quant_block(ds, 2 * j + 1);
         });
         // dprob: this lane's 64 columns plus the other half-wave's 64 of the same row
-        dpr = add_xor32(dpr);
+        dpr = add_xor32(dpr) * cdp;
         if (gh == 0 && cols > 0) atomicAdd(p.dprob + row, dpr);
         const uint32_t rb = (uint32_t)n2;
         stage_flush<1, 8>(sd, static_cast<char *>(p.d) + (qr + 32 * i) * n2 + dq, rb, 32, dcols, lane);
@@ -412,12 +434,14 @@ __device__ __forceinline__ void epilogue_dswiglu(const GroupedParams &p, f32x16 
     for (int i = 0; i < 4; ++i) pr[i] = prob_lds[acc_row(wm, i, lane)];
     uint8_t *wd = stage + c32 * G::RBP + 4 * gh * ES;
     float mab = 0.0f, mds = 0.0f;
+    const float kx = -1.4426950408889634f * beta, cdp = beta * beta * alpha2;
     static_for<4>([&](auto ii) {
         constexpr int i = decltype(ii)::value;
         __builtin_amdgcn_sched_barrier(0);
         const int64_t row = qr + 32 * i + c32;
         const uint16_t *crow = p.cfwd + row * n2 + 64 * (qc / 32) + 4 * gh;
         float dpr = 0.0f;
+        const float fi = alpha2 * pr[i] * beta;
         static_for<4>([&](auto jj) {
             constexpr int j = decltype(jj)::value;
             const bool ok = 32 * j < cols;
@@ -433,15 +457,11 @@ __device__ __forceinline__ void epilogue_dswiglu(const GroupedParams &p, f32x16 
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int v = 4 * q + u;
-                    const float ref = alpha2 * acc[i][j][v];
-                    const float in = beta * bf16_at(ci[q], u);
-                    const float gt = beta * bf16_at(cg[q], u);
-                    const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gt));
-                    const float sw = gt * sg;
-                    const float rp = ref * pr[i];
-                    ab[u] = rp * sw;
-                    ds[u] = rp * in * sg * fmaf(gt, 1.0f - sg, 1.0f);
-                    dpr = fmaf(sw * in, ref, dpr);
+                    const DswigluTerms r = dswiglu_terms(acc[i][j][v], bf16_at(cg[q], u), bf16_at(ci[q], u), fi,
+                                                         beta, kx);
+                    ab[u] = r.ab;
+                    ds[u] = r.ds;
+                    dpr = fmaf(r.tx, acc[i][j][v], dpr);
                     mab = fmaxf(mab, fabsf(ab[u]));
                     mds = fmaxf(mds, fabsf(ds[u]));
                 }
@@ -451,7 +471,7 @@ __device__ __forceinline__ void epilogue_dswiglu(const GroupedParams &p, f32x16 
                     pack_quad<OT>(ds[0], ds[1], ds[2], ds[3]);
             }
         });
-        dpr = add_xor32(dpr);
+        dpr = add_xor32(dpr) * cdp;
         if (gh == 0 && cols > 0) atomicAdd(p.dprob + row, dpr);
         // Materialise both maxima per row block: otherwise the compiler sinks
         // their max chains into the amax branch at the end, keeping all 512
