@@ -77,6 +77,10 @@ CASES = [
     # E5M2 D codes (rcp_max 1/57344)
     dict(sizes=[256, 0, 512], n=160, k=256, fmt="e4m3", d="e5m2"),
     dict(sizes=[512, 256], n=256, k=384, fmt="e5m2", d="e5m2"),
+    # norm_const that is not a power of two (the kernel carries it inside the
+    # values and divides by the E8M0 scale alone)
+    dict(sizes=[256, 0, 512], n=160, k=256, fmt="e4m3", nc=0.37),
+    dict(sizes=[512, 256], n=256, k=384, fmt="e4m3", d="e5m2", nc=3.0),
 ]
 
 
@@ -86,6 +90,8 @@ def test_grouped_dswiglu_matches_oracle(case):
     off = np.cumsum(case["sizes"]).astype(np.int32)
     L = len(case["sizes"])
     p = W.grouped_dswiglu_problem(0, L, case["n"], case["k"], case["fmt"], seed=6, offsets=off, extra_rows=256)
+    nc = case.get("nc", 1.0)
+    p.t["norm_const"] = torch.full((1,), nc)
     s = p.sizes
     m, n, k = s["m"], s["n"], s["k"]
     d_fmt = case.get("d", "e4m3")
@@ -95,7 +101,7 @@ def test_grouped_dswiglu_matches_oracle(case):
                           p.t["prob"], O.bits16(p.t["c"]), m, n, k, L, case["fmt"], 0, valid)
     bd, b_dp = bounds(p, r, 0, valid)
     rs, cs = gather_scales(sfd_row, sfd_col, 0, valid, m, 2 * n)
-    res = check_mx_outputs(r["d"], bd, d[:valid].cpu().numpy(), rs, d_col[:valid].cpu().numpy(), cs, 1.0,
+    res = check_mx_outputs(r["d"], bd, d[:valid].cpu().numpy(), rs, d_col[:valid].cpu().numpy(), cs, nc,
                            what="D", fmt=d_fmt)
     say(f"  {res}")
     g = dprob[:valid].cpu().double().numpy()
