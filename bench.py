@@ -38,7 +38,7 @@ def ceil_div(a, b):
 # ---------------------------------------------------------------------------
 # Workloads: each returns (step_fn, info) with inputs resident on the GPU.
 # ---------------------------------------------------------------------------
-def wl_moe_mxfp8_srelu(fp8_out=False, discrete=False, fmt="e4m3", d_fp8="e4m3"):
+def wl_moe_mxfp8_srelu(fp8_out=False, discrete=False, fmt="e4m3", d_fp8="e4m3", c_f32=False):
     import torch
     import block_scaled_gemm_02_amd as bsg
     import workloads as W
@@ -53,7 +53,8 @@ def wl_moe_mxfp8_srelu(fp8_out=False, discrete=False, fmt="e4m3", d_fp8="e4m3"):
         sfb_list = [t["sfb"][g * atom:(g + 1) * atom].clone() for g in range(L)]
         b_ptrs, sfb_ptrs = bsg.pointer_array(b_list), bsg.pointer_array(sfb_list)
         del t["b"], t["sfb"]
-    c = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    c_dt = torch.float32 if c_f32 else torch.bfloat16     # fp32 C with bf16 D: the mixed-type path
+    c = torch.empty(m, n, dtype=c_dt, device="cuda")
     if fp8_out:
         nb = n // 2 if d_fp8 == "e2m1" else n       # E2M1 codes: two per byte
         d = torch.empty(m, nb, dtype=torch.uint8, device="cuda")
@@ -72,12 +73,12 @@ def wl_moe_mxfp8_srelu(fp8_out=False, discrete=False, fmt="e4m3", d_fp8="e4m3"):
         if discrete:
             bsg.grouped_gemm_srelu_discrete(t["a"], b_ptrs, t["sfa"], sfb_ptrs, t["offsets"], t["alpha"],
                                             t["prob"], t["norm_const"], c, d, d_col, sfd_row, sfd_col,
-                                            amax, m, n, k, L, fmt, c_dtype=torch.bfloat16, d_dtype=dd,
+                                            amax, m, n, k, L, fmt, c_dtype=c_dt, d_dtype=dd,
                                             tanh_clamp_scale=32.0)
         else:
             bsg.grouped_gemm_srelu(t["a"], t["b"], t["sfa"], t["sfb"], t["offsets"], t["alpha"],
                                    t["prob"], t["norm_const"], c, d, d_col, sfd_row, sfd_col, amax,
-                                   m, n, k, L, fmt, c_dtype=torch.bfloat16, d_dtype=dd,
+                                   m, n, k, L, fmt, c_dtype=c_dt, d_dtype=dd,
                                    tanh_clamp_scale=32.0)
     step.keep = (b_list, sfb_list) if discrete else None
 
@@ -85,21 +86,21 @@ def wl_moe_mxfp8_srelu(fp8_out=False, discrete=False, fmt="e4m3", d_fp8="e4m3"):
     flops = 2.0 * valid_m * n * k
     ab_bytes = valid_m * k + L * n * k if fmt == "e4m3" else (valid_m * k + L * n * k) // 2
     sf_bytes = t["sfa"].numel() + (sum(x.numel() for x in sfb_list) if discrete else t["sfb"].numel())
-    # C bf16, then D (bf16), or D and D_col codes (1 byte each, E2M1 half a byte each)
-    out_bytes = valid_m * n * (2 + (2 if not fp8_out else (1 if d_fp8 == "e2m1" else 2)))
+    # C bf16 (or fp32), then D (bf16), or D and D_col codes (1 byte each, E2M1 half a byte each)
+    out_bytes = valid_m * n * ((4 if c_f32 else 2) + (2 if not fp8_out else (1 if d_fp8 == "e2m1" else 2)))
     alg_bytes = ab_bytes + sf_bytes + out_bytes
     name = ("moe_mxfp8_srelu" if fmt == "e4m3" else "moe_mxfp4_srelu") + \
         ({"e4m3": "_fp8d", "e5m2": "_e5m2d", "e2m1": "_mxfp4d"}[d_fp8] if fp8_out else "") + \
-        ("_discrete" if discrete else "")
+        ("_discrete" if discrete else "") + ("_c32" if c_f32 else "")
     info = dict(
         name=name, fmt=fmt, flops=flops, alg_bytes=alg_bytes, kernel="k_grouped",
         config={"workload": ("grouped MXFP8 (E4M3" if fmt == "e4m3" else "grouped MXFP4 (E2M1")
                 + ", E8M0 per 32 K) GEMM + prob-gated sReLU, tanh clamp s=32",
                 "experts": L, "n": n, "k": k, "valid_m": valid_m, "routed_rows": 28672,
                 "routing": "multinomial Zipf(1.1), padded to 256",
-                "outputs": "C bf16, D " + (d_fp8.upper() + " + SFD_row/SFD_col" if fp8_out else "bf16 + amax(L)"),
+                "outputs": ("C fp32" if c_f32 else "C bf16") + ", D " + (d_fp8.upper() + " + SFD_row/SFD_col" if fp8_out else "bf16 + amax(L)"),
                 "weights": "per-expert allocations (b_ptrs, sfb_ptrs)" if discrete else "one (N,K,L) tensor"},
-        cpu=None if (discrete or fmt != "e4m3") else (lambda: cpu_sample_srelu(p)))
+        cpu=None if (discrete or c_f32 or fmt != "e4m3") else (lambda: cpu_sample_srelu(p)))
     return step, info
 
 
@@ -349,6 +350,7 @@ WORKLOADS = {
     "proj_rope_w_in_out": lambda: wl_proj_rope(False, w_out_in=False),
     "proj_rope_mxfp8_w_in_out": lambda: wl_proj_rope(True, w_out_in=False),
     "moe_mxfp8_srelu": lambda: wl_moe_mxfp8_srelu(False),
+    "moe_mxfp8_srelu_c32": lambda: wl_moe_mxfp8_srelu(False, c_f32=True),
     "moe_mxfp8_srelu_fp8d": lambda: wl_moe_mxfp8_srelu(True),
     "moe_mxfp8_srelu_e5m2d": lambda: wl_moe_mxfp8_srelu(True, d_fp8="e5m2"),
     "moe_mxfp8_srelu_mxfp4d": lambda: wl_moe_mxfp8_srelu(True, d_fp8="e2m1"),
