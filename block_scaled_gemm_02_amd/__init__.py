@@ -59,6 +59,7 @@ def lib():
             "bsg_validate_grouped_gemm": [p] * 8 + [i64] * 4 + [i32] * 3,
             "bsg_validate_grouped_gemm_srelu": [p] * 14 + [i64] * 4 + [i32] * 4 + [f32],
             "bsg_validate_gemm_proj_rope_mxfp8": [p] * 10 + [i64] * 5 + [i32, i32],
+            "bsg_check_padded_offsets": [p, i64, i64, p],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -81,7 +82,7 @@ def symbols():
             "bsg_validate_grouped_gemm_srelu", "bsg_validate_gemm_proj_rope_mxfp8",
             "bsg_validate_grouped_gemm_dswiglu",
             "bsg_validate_grouped_gemm_discrete", "bsg_validate_grouped_gemm_srelu_discrete",
-            "bsg_status_string", "bsg_last_error", "bsg_version"]
+            "bsg_check_padded_offsets", "bsg_status_string", "bsg_last_error", "bsg_version"]
 
 
 def _ptr(t):
@@ -220,6 +221,16 @@ def gemm_amax(a, b, sfa, sfb, c, amax, m, n, k, l, ab_dtype="e4m3", c_dtype=None
     if validate_only:
         return lib().bsg_validate_gemm_amax(*args)
     _check(lib().gemm_amax(*args, _stream(stream)))
+
+
+def check_padded_offsets(padded_offsets, m, num_experts=None, stream=None):
+    """Opt-in debug check of the routing offsets' values on the device
+    (bsg_check_padded_offsets: multiples of 256 in [0, m], nondecreasing);
+    waits for the stream.  Raises BsgError naming the first violation."""
+    if num_experts is None:
+        num_experts = padded_offsets.numel()
+    _need(padded_offsets, "padded_offsets", 4 * num_experts, torch.int32)
+    _check(lib().bsg_check_padded_offsets(_ptr(padded_offsets), num_experts, m, _stream(stream)))
 
 
 def grouped_gemm(a, b, padded_offsets, alpha, prob, bias, c, d, m, n, k, num_experts,

@@ -107,6 +107,38 @@ const char *bsg_last_error(void) { return g_err; }
 
 int bsg_version(void) { return 100; }
 
+// Opt-in check of the routing offsets' values (see the header): one copy of
+// the num_experts ints to the host and a wait on the stream.
+int bsg_check_padded_offsets(const int32_t *padded_offsets, int64_t num_experts, int64_t m, void *stream)
+{
+    if (!padded_offsets) return fail(BSG_ERR_NULLPTR, "padded_offsets is NULL");
+    if (num_experts < 1 || num_experts > 1024)
+        return fail(BSG_ERR_SHAPE, "num_experts=%lld must be in [1, 1024]", (long long)num_experts);
+    if (m < 0 || m % 256) return fail(BSG_ERR_SHAPE, "m=%lld must be a non-negative multiple of 256", (long long)m);
+    if (int r = check_device()) return r;
+    int32_t host[1024];
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(host, padded_offsets, (size_t)num_experts * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(BSG_ERR_LAUNCH, "copying padded_offsets failed: %s", hipGetErrorString(e));
+    int64_t prev = 0;
+    for (int64_t g = 0; g < num_experts; ++g) {
+        const int64_t v = host[g];
+        if (v < 0) return fail(BSG_ERR_SHAPE, "padded_offsets[%lld]=%lld is negative", (long long)g, (long long)v);
+        if (v % 256)
+            return fail(BSG_ERR_SHAPE, "padded_offsets[%lld]=%lld is not a multiple of 256", (long long)g,
+                        (long long)v);
+        if (v < prev)
+            return fail(BSG_ERR_SHAPE, "padded_offsets[%lld]=%lld is below padded_offsets[%lld]=%lld", (long long)g,
+                        (long long)v, (long long)(g - 1), (long long)prev);
+        if (v > m)
+            return fail(BSG_ERR_SHAPE, "padded_offsets[%lld]=%lld exceeds m=%lld", (long long)g, (long long)v,
+                        (long long)m);
+        prev = v;
+    }
+    return BSG_OK;
+}
+
 // ---------------------------------------------------------------------------
 // gemm_amax
 // ---------------------------------------------------------------------------

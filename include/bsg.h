@@ -358,6 +358,19 @@ int bsg_validate_gemm_proj_rope_mxfp8(const void *x, const void *w, const uint8_
                                       int64_t head_dim, int64_t qk_rope, int in_dtype,
                                       int w_out_in);
 
+/* Opt-in debug check of the routing offsets that the grouped entry points
+ * take on the device without reading them ("Grouped GEMM + dSwiGLU (SM100)",
+ * JAX execution: the offsets are the caller's responsibility).  Copies the
+ * num_experts int32 values of padded_offsets (a device pointer) to the host
+ * on `stream`, waits for the stream, and checks the contract the kernels
+ * assume: every value a multiple of 256 in [0, m], nondecreasing ("Grouped
+ * GEMM (SM100 BF16)", Tensors and layouts: each expert's rows padded to 256).
+ * Returns BSG_OK, SHAPE naming the first violation (bsg_last_error), or
+ * NULLPTR / DEVICE / LAUNCH.  Synchronises the stream: for debugging, not
+ * for the hot path. */
+int bsg_check_padded_offsets(const int32_t *padded_offsets, int64_t num_experts, int64_t m,
+                             void *stream);
+
 /* Static text for a status code. */
 const char *bsg_status_string(int status);
 /* Thread-local message for the most recent non-zero return on this thread. */

@@ -235,3 +235,16 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(bsg.BsgError) as e:
         va(a=a)
     assert e.value.status == 6
+
+
+def test_padded_offsets_check_host_arguments():
+    """bsg_check_padded_offsets rejects a null pointer, an expert count out of
+    [1, 1024] and an M that is not a multiple of 256 before it touches the
+    device (the fake address is never read)."""
+    L = bsg.lib()
+    assert L.bsg_check_padded_offsets(None, 4, 512, None) == NULLPTR
+    assert L.bsg_check_padded_offsets(P, 0, 512, None) == SHAPE
+    assert L.bsg_check_padded_offsets(P, 1025, 512, None) == SHAPE
+    assert L.bsg_check_padded_offsets(P, 4, 300, None) == SHAPE
+    assert L.bsg_check_padded_offsets(P, 4, -256, None) == SHAPE
+    assert b"multiple of 256" in L.bsg_last_error()

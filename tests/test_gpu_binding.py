@@ -52,3 +52,25 @@ def test_binding_refuses_mismatched_tensors():
                      l=1) == SHAPE
     assert status_of(bsg.gemm_amax, a=a, b=a, sfa=sf, sfb=sf, c=c.half(), amax=amax, m=m, n=n, k=k,
                      l=1, c_dtype=torch.float32) == DTYPE
+
+
+@pytest.mark.parametrize("offsets,m,status,words", [
+    ([256, 256, 768, 1024], 1024, 0, ""),
+    ([0, 0], 0, 0, ""),
+    ([256, 300, 512], 512, SHAPE, "not a multiple of 256"),
+    ([512, 256, 768], 768, SHAPE, "is below"),
+    ([256, 768], 512, SHAPE, "exceeds m"),
+    ([-256, 256], 512, SHAPE, "negative"),
+])
+def test_check_padded_offsets(offsets, m, status, words):
+    """The opt-in offsets check reads the device values and names the first
+    value that breaks the kernels' contract (multiples of 256 in [0, m],
+    nondecreasing)."""
+    print(f"check_padded_offsets {offsets} m={m}", flush=True)
+    t = torch.tensor(offsets, dtype=torch.int32, device="cuda")
+    if status == 0:
+        bsg.check_padded_offsets(t, m)
+    else:
+        with pytest.raises(bsg.BsgError) as e:
+            bsg.check_padded_offsets(t, m)
+        assert e.value.status == status and words in str(e.value), str(e.value)
