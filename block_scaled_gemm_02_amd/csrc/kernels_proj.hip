@@ -222,6 +222,9 @@ __global__ void __launch_bounds__(1024 / MI) k_proj_rope(ProjParams p)
     // LDS region (half a pair slot; the K loop is over) and stored as whole
     // 96-byte row segments; scale bytes are written directly.
     typedef StageGeom<1, 3> G;
+    // row codes, column codes and the 32-float exchange fit the wave's region
+    static_assert(2 * 32 * G::RBP + 32 * 4 <= (MI == 2 ? (Ring<F>::kWaveStage / 2 & ~15) : Ring<F>::kWaveStage),
+                  "projection staging exceeds the wave's LDS region");
     uint8_t *stage = MI == 2 ? wave_stage8(ring, __builtin_amdgcn_readfirstlane(wall))
                              : wave_stage(ring, __builtin_amdgcn_readfirstlane(w));
     uint8_t *sr = stage, *sc = stage + 32 * G::RBP;
