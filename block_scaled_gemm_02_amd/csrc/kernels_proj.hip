@@ -21,7 +21,7 @@
 #include "launch.hpp"
 
 // Waves per workgroup: 8 (BSG_PROJ_MI 2, two waves of 64 tokens per SIMD)
-// or 4 (BSG_PROJ_MI 4).  Eight waves run 3-4% faster on the DeepSeek-V3
+// or 4 (BSG_PROJ_MI 4).  Eight waves run 2.5-4.5% faster on the DeepSeek-V3
 // shape: the K loop takes the same time, and the two waves of a SIMD cover
 // each other's epilogue waits.
 #ifndef BSG_PROJ_MI
@@ -219,8 +219,9 @@ __global__ void __launch_bounds__(1024 / MI) k_proj_rope(ProjParams p)
 
     // ---- dual MXFP8 quantisation (norm_const 1) ----
     // One 32-token block at a time: both code arrays are staged in the wave's
-    // LDS region (half a pair slot; the K loop is over) and stored as whole
-    // 96-byte row segments; scale bytes are written directly.
+    // LDS region (half a pair slot with four waves, a quarter with eight; the
+    // K loop is over) and stored as whole 96-byte row segments; scale bytes
+    // are written directly.
     typedef StageGeom<1, 3> G;
     // row codes, column codes and the 32-float exchange fit the wave's region
     static_assert(2 * 32 * G::RBP + 32 * 4 <= (MI == 2 ? (Ring<F>::kWaveStage / 2 & ~15) : Ring<F>::kWaveStage),
